@@ -1,0 +1,139 @@
+"""CPU oracle for paged-KV attention (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The product library under
+``paged_kv_attention_04_amd`` never imports it, and it imports nothing from
+there: the two share no code.  The arithmetic lives in ``pa_oracle.c``
+(plain double-precision loops, see its header for the definition and the
+passages of the pages it follows); this file only compiles it with gcc and
+marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_BUILD = os.path.join(_HERE, "_build")
+_LIB = os.path.join(_BUILD, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP) into oracle/_build/liboracle.so."""
+    os.makedirs(_BUILD, exist_ok=True)
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.oracle_append.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32]
+    lib.oracle_append.restype = ctypes.c_int
+    lib.oracle_attention.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f64,
+                                     P, P, P, P, P, P]
+    lib.oracle_attention.restype = ctypes.c_int
+    lib.oracle_double_to_bf16.argtypes = [f64]
+    lib.oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16_array.argtypes = [P, P, i64]
+    lib.oracle_round_bf16_array.restype = None
+    lib.oracle_slot.argtypes = [P, i64, i32]
+    lib.oracle_slot.restype = i64
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def round_bf16(x) -> np.ndarray:
+    """Double -> bf16 bit patterns, round to nearest even (one rounding step)."""
+    x = _c(np.atleast_1d(x), np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_bf16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def slot(block_table_row, pos: int, block_size: int) -> int:
+    bt = _c(block_table_row, np.int32)
+    return int(_load().oracle_slot(_ptr(bt), int(pos), int(block_size)))
+
+
+def append(k_pool, v_pool, k_new, v_new, slot_mapping, num_kv_heads, head_dim, block_size, num_blocks,
+           in_place: bool = False):
+    """Scatter new K/V rows into (copies of) the pools; returns (k_pool, v_pool)."""
+    kp = k_pool if in_place else np.array(k_pool, dtype=np.uint16, copy=True)
+    vp = v_pool if in_place else np.array(v_pool, dtype=np.uint16, copy=True)
+    assert kp.flags.c_contiguous and vp.flags.c_contiguous
+    kn, vn = _c(k_new, np.uint16), _c(v_new, np.uint16)
+    sm = _c(slot_mapping, np.int32)
+    rc = _load().oracle_append(_ptr(kp), _ptr(vp), _ptr(kn), _ptr(vn), _ptr(sm), int(sm.size),
+                               int(num_kv_heads), int(head_dim), int(block_size), int(num_blocks))
+    if rc != 0:
+        raise ValueError(f"oracle_append failed with code {rc}")
+    return kp, vp
+
+
+def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_kv_heads, head_dim,
+              block_size, num_blocks, scale, row_select=None, want_f64: bool = False):
+    """Returns dict(out=bf16 bits [total_q][Hq][D], lse=float32 [total_q][Hq], pairs=int,
+    and out_f64 / lse_f64 when ``want_f64``).  Rows not in ``row_select`` are left as zero."""
+    qa = _c(q, np.uint16)
+    kp, vp = _c(k_pool, np.uint16), _c(v_pool, np.uint16)
+    bt = _c(block_tables, np.int32)
+    qo, kv = _c(qo_len, np.int32), _c(kv_len, np.int32)
+    R = int(qo.size)
+    total_q = int(qo.sum())
+    out = np.zeros((total_q, num_q_heads, head_dim), np.uint16)
+    lse = np.zeros((total_q, num_q_heads), np.float32)
+    out64 = np.zeros((total_q, num_q_heads, head_dim), np.float64) if want_f64 else None
+    lse64 = np.zeros((total_q, num_q_heads), np.float64) if want_f64 else None
+    sel = None if row_select is None else _c(row_select, np.uint8)
+    pairs = ctypes.c_int64(0)
+    rc = _load().oracle_attention(_ptr(qa), _ptr(kp), _ptr(vp), _ptr(bt), int(bt.shape[1]), _ptr(qo), _ptr(kv),
+                                  R, int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+                                  int(num_blocks), float(scale), _ptr(sel), _ptr(out), _ptr(lse),
+                                  _ptr(out64), _ptr(lse64), ctypes.cast(ctypes.pointer(pairs), ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError(f"oracle_attention failed with code {rc}")
+    res = dict(out=out, lse=lse, pairs=int(pairs.value))
+    if want_f64:
+        res["out_f64"] = out64
+        res["lse_f64"] = lse64
+    return res
+
+
+def run_workload(wl, row_select=None, want_f64: bool = False):
+    """Append the workload's new tokens, then attend; returns (k_pool, v_pool, result)."""
+    kp, vp = append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
+                    wl.head_dim, wl.block_size, wl.num_blocks)
+    res = attention(wl.q, kp, vp, wl.block_tables, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
+                    wl.head_dim, wl.block_size, wl.num_blocks, wl.scale, row_select=row_select,
+                    want_f64=want_f64)
+    return kp, vp, res

@@ -1,0 +1,263 @@
+/*
+ * Plain CPU oracle for paged-KV attention over a mixed decode / chunked-prefill
+ * batch.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU baseline call it; the product library never does.  It shares
+ * no code, header or table with the GPU library.
+ *
+ * It is the plain definition, written out slowly in double precision:
+ *
+ *   append     For every new token t with slot s = slot_mapping[t] >= 0, copy its
+ *              K and V rows for every KV head into pool[s / B][head][s % B][:].
+ *              Blocks of B tokens, a per-request block table from logical to
+ *              physical block, and new tokens written into the slot that the
+ *              table gives (AI-infra book ch. 8 "Inference optimisation",
+ *              section 8.3.1 and fig. 8-10; the Perplexity blog on prefill /
+ *              decode disaggregation orders the per-layer append before attention).
+ *
+ *   attention  For request r, new token i in [0, qo_len) and query head h:
+ *                p    = kv_len - qo_len + i        (absolute position of the token)
+ *                kvh  = h / (Hq / Hkv)             (grouped-query attention: each KV
+ *                                                   head serves a contiguous group)
+ *                s_j  = scale * sum_c q[c] * K_j[c]   for j = 0..p, K_j read through the
+ *                                                   block table: K_pool[bt[r][j/B]][kvh][j%B]
+ *                LSE  = ln sum_j exp(s_j)          (natural log)
+ *                o[c] = sum_j exp(s_j - LSE) * V_j[c]
+ *              The i-th new token of a chunk at context h sees h + i + 1 keys, i.e.
+ *              itself and everything before it (book section 8.2.3, the N_pair sum
+ *              and figs. 8-8 / 8-9).  The output is rounded to bf16 (nearest even),
+ *              the LSE is stored as float.
+ *
+ * Everything is accumulated in double; the scores are kept and exponentiated
+ * in a second pass (max subtracted first), which is mathematically the same
+ * as any one-pass or split form of softmax.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_BAD_BLOCK 2
+#define ORACLE_NO_MEMORY 3
+
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 value, ties to even, in one rounding step.
+ * bf16 keeps 8 significant bits; a finite x with |x| = m * 2^e (m in [0.5, 1))
+ * lies between two neighbours that are multiples of 2^(e-8) (normal range) or
+ * of 2^-133 (subnormal range). */
+uint16_t oracle_double_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    int qexp = (e > -125 ? e : -125) - 8;
+    double quantum = ldexp(1.0, qexp);
+    double lo = floor(a / quantum);        /* exact: a / quantum scales by a power of two */
+    double below = lo * quantum, above = (lo + 1.0) * quantum;
+    double dlo = a - below, dhi = above - a;
+    double r;
+    if (dlo < dhi)
+        r = below;
+    else if (dhi < dlo)
+        r = above;
+    else
+        r = (fmod(lo, 2.0) == 0.0) ? below : above;
+    /* largest finite bf16 is (2 - 2^-7) * 2^127; anything that rounds past it is infinite */
+    if (r >= ldexp(1.0, 128))
+        return sign | 0x7F80;
+    float f = (float)r;                    /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)((u >> 16) & 0x7FFF);
+}
+
+double oracle_bf16_to_double(uint16_t b) { return bf16_to_double(b); }
+
+/* Pool slot of logical position pos of one request: bt_row[pos / B] * B + pos % B. */
+int64_t oracle_slot(const int32_t* bt_row, int64_t pos, int32_t block_size)
+{
+    return (int64_t)bt_row[pos / block_size] * block_size + pos % block_size;
+}
+
+/* append: pools are [num_blocks][Hkv][B][D] bf16; k_new / v_new are [n][Hkv][D]. */
+int oracle_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new, const uint16_t* v_new,
+                  const int32_t* slot_mapping, int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t num_blocks)
+{
+    if (!k_pool || !v_pool || !k_new || !v_new || (!slot_mapping && n_tokens > 0) || n_tokens < 0)
+        return ORACLE_BAD_ARG;
+    for (int32_t t = 0; t < n_tokens; ++t) {
+        int64_t s = slot_mapping[t];
+        if (s < 0)
+            continue;                      /* negative slot: token not cached */
+        int64_t blk = s / block_size, off = s % block_size;
+        if (blk >= num_blocks)
+            return ORACLE_BAD_BLOCK;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            size_t dst = (((size_t)blk * num_kv_heads + h) * block_size + off) * head_dim;
+            size_t src = ((size_t)t * num_kv_heads + h) * head_dim;
+            memcpy(k_pool + dst, k_new + src, sizeof(uint16_t) * head_dim);
+            memcpy(v_pool + dst, v_new + src, sizeof(uint16_t) * head_dim);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * attention.  q: [total_q][Hq][D] bf16 with rows of request r at qo_indptr[r]..;
+ * out: same shape bf16; lse: [total_q][Hq] float.  block_tables: [R][max_blocks].
+ * row_select (may be NULL): if given, only requests with row_select[r] != 0 are
+ * computed and the other rows of the outputs are left untouched.  out_f64 / lse_f64
+ * (may be NULL) receive the same results before rounding, for tests that need more
+ * than bf16 resolution.  pair_count (may be NULL) receives the number of
+ * (query, key) pairs visited for one head, summed over the computed rows: an
+ * instrument for the causal mask.
+ */
+int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
+                     const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale,
+                     const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
+                     double* lse_f64, int64_t* pair_count)
+{
+    if (!q || !k_pool || !v_pool || !block_tables || !qo_len || !kv_len)
+        return ORACLE_BAD_ARG;
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0)
+        return ORACLE_BAD_ARG;
+    const int32_t group = num_q_heads / num_kv_heads;
+
+    /* Row r's first query row is the sum of the earlier qo_len. */
+    int64_t* first_row = (int64_t*)malloc(sizeof(int64_t) * (size_t)(num_reqs + 1));
+    if (!first_row)
+        return ORACLE_NO_MEMORY;
+    first_row[0] = 0;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        if (qo_len[r] < 1 || kv_len[r] < qo_len[r] || (kv_len[r] + block_size - 1) / block_size > max_blocks) {
+            free(first_row);
+            return ORACLE_BAD_ARG;
+        }
+        first_row[r + 1] = first_row[r] + qo_len[r];
+    }
+    /* Every table entry that a row reads must name a pool block. */
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        int32_t nb = (kv_len[r] + block_size - 1) / block_size;
+        for (int32_t b = 0; b < nb; ++b) {
+            int32_t phys = block_tables[(size_t)r * max_blocks + b];
+            if (phys < 0 || phys >= num_blocks) {
+                free(first_row);
+                return ORACLE_BAD_BLOCK;
+            }
+        }
+    }
+
+    /* Work items: (request, new token, query head). */
+    int64_t total = first_row[num_reqs] * num_q_heads;
+    int64_t pairs = 0;
+    int status = ORACLE_OK;
+
+#pragma omp parallel reduction(+ : pairs)
+    {
+        int32_t max_kv = 0;
+        for (int32_t r = 0; r < num_reqs; ++r)
+            if (kv_len[r] > max_kv)
+                max_kv = kv_len[r];
+        double* s = (double*)malloc(sizeof(double) * (size_t)(max_kv > 0 ? max_kv : 1));
+        double* acc = (double*)malloc(sizeof(double) * (size_t)head_dim);
+        double* qd = (double*)malloc(sizeof(double) * (size_t)head_dim);
+        if (!s || !acc || !qd) {
+#pragma omp atomic write
+            status = ORACLE_NO_MEMORY;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t w = 0; w < total; ++w) {
+                int64_t row = w / num_q_heads;
+                int32_t h = (int32_t)(w % num_q_heads);
+                int32_t r = 0;                         /* request owning this query row */
+                while (first_row[r + 1] <= row)
+                    ++r;
+                if (row_select && !row_select[r])
+                    continue;
+                int32_t i = (int32_t)(row - first_row[r]);
+                int32_t kvh = h / group;
+                int64_t p = (int64_t)kv_len[r] - qo_len[r] + i;   /* keys 0..p are visible */
+                const int32_t* bt = block_tables + (size_t)r * max_blocks;
+                const uint16_t* qrow = q + ((size_t)row * num_q_heads + h) * head_dim;
+                for (int32_t c = 0; c < head_dim; ++c)
+                    qd[c] = bf16_to_double(qrow[c]);
+
+                double m = -INFINITY;
+                for (int64_t j = 0; j <= p; ++j) {
+                    size_t base = (((size_t)bt[j / block_size] * num_kv_heads + kvh) * block_size
+                                   + (size_t)(j % block_size)) * head_dim;
+                    double dot = 0.0;
+                    for (int32_t c = 0; c < head_dim; ++c)
+                        dot += qd[c] * bf16_to_double(k_pool[base + c]);
+                    s[j] = scale * dot;
+                    if (s[j] > m)
+                        m = s[j];
+                }
+                pairs += p + 1;
+
+                double l = 0.0;
+                for (int32_t c = 0; c < head_dim; ++c)
+                    acc[c] = 0.0;
+                for (int64_t j = 0; j <= p; ++j) {
+                    double e = exp(s[j] - m);
+                    l += e;
+                    size_t base = (((size_t)bt[j / block_size] * num_kv_heads + kvh) * block_size
+                                   + (size_t)(j % block_size)) * head_dim;
+                    for (int32_t c = 0; c < head_dim; ++c)
+                        acc[c] += e * bf16_to_double(v_pool[base + c]);
+                }
+                size_t orow = ((size_t)row * num_q_heads + h) * head_dim;
+                for (int32_t c = 0; c < head_dim; ++c) {
+                    if (out)
+                        out[orow + c] = oracle_double_to_bf16(acc[c] / l);
+                    if (out_f64)
+                        out_f64[orow + c] = acc[c] / l;
+                }
+                if (lse)
+                    lse[(size_t)row * num_q_heads + h] = (float)(m + log(l));
+                if (lse_f64)
+                    lse_f64[(size_t)row * num_q_heads + h] = m + log(l);
+            }
+        }
+        free(s);
+        free(acc);
+        free(qd);
+    }
+    free(first_row);
+    if (pair_count)
+        *pair_count = pairs / num_q_heads;
+    return status;
+}
+
+/* Element-wise oracle_double_to_bf16 over an array (for the rounding tests). */
+void oracle_round_bf16_array(const double* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_double_to_bf16(x[i]);
+}
+
+/* Threads the attention loop may use (OpenMP's current maximum; 1 without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif

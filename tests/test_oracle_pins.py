@@ -1,0 +1,412 @@
+"""Pins for the CPU oracle: checks against what the pages print and what the
+mathematics fixes, never against the oracle's own formula retyped.
+
+Page A = AI-infra book ch. 8 "Inference optimisation"; page B = serving tutorial,
+section "PagedAttention: KV cache in pages".  Printed values live in
+tests/golden/pages_worked_examples.json with their citations.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from synthetic import bf16_bits_to_f32, f32_to_bf16_bits
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_worked_examples.json")))
+rng = np.random.default_rng(12345)
+
+
+def _bf16(shape, scale=1.0, gen=None):
+    g = gen or rng
+    return f32_to_bf16_bits(g.standard_normal(shape).astype(np.float32) * np.float32(scale))
+
+
+def _contiguous_case(Hq, Hkv, D, qo, kv, B=16, seed=0, scale=None):
+    """A single request whose blocks are physical blocks 0..n-1 in order (no paging),
+    so that dense attention over the first kv positions is the reference."""
+    g = np.random.default_rng(seed)
+    nb = -(-kv // B)
+    kp = np.full((nb + 1, Hkv, B, D), synthetic.BF16_NAN, np.uint16)   # one spare poisoned block
+    kd, vd = _bf16((kv, Hkv, D), gen=g), _bf16((kv, Hkv, D), gen=g)
+    vp = kp.copy()
+    for j in range(kv):
+        kp[j // B, :, j % B] = kd[j]
+        vp[j // B, :, j % B] = vd[j]
+    q = _bf16((qo, Hq, D), gen=g)
+    bt = np.arange(nb, dtype=np.int32)[None, :]
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    return dict(q=q, kd=kd, vd=vd, kp=kp, vp=vp, bt=bt, scale=sc, nblocks=nb + 1)
+
+
+def _run(c, Hq, Hkv, D, qo, kv, B=16, want_f64=True):
+    return oracle.attention(c["q"], c["kp"], c["vp"], c["bt"], [qo], [kv], Hq, Hkv, D, B, c["nblocks"],
+                            c["scale"], want_f64=want_f64)
+
+
+# ---------------------------------------------------------------- geometry / capacity pins
+
+def test_kv_bytes_per_token_closed_form():
+    """k = 2 x 36 x 8 x 128 x 2 = 147,456 bytes (page A, section 8.1.2), measured as the
+    bytes one oracle append changes in a one-layer pool, times the layer count."""
+    g = GOLD["kv_bytes_per_token"]
+    geo = synthetic.QWEN3_8B
+    assert (geo["num_layers"], geo["num_kv_heads"], geo["head_dim"], geo["dtype_bytes"]) == \
+        (g["layers"], g["kv_heads"], g["head_dim"], g["bytes"])
+    Hkv, D, B = geo["num_kv_heads"], geo["head_dim"], 16
+    kp = np.zeros((4, Hkv, B, D), np.uint16)
+    vp = np.zeros_like(kp)
+    kn = np.full((1, Hkv, D), 0xFFFF, np.uint16)
+    k2, v2 = oracle.append(kp, vp, kn, kn, [2 * B + 5], Hkv, D, B, 4)
+    changed = int((k2 != kp).sum() + (v2 != vp).sum()) * geo["dtype_bytes"]
+    assert changed == 4096
+    assert changed * geo["num_layers"] == g["value"] == 147456
+
+
+def test_pool_blocks_for_12gib():
+    # 12 GiB / (36 layers x 16 tokens x 4096 B per token-layer) blocks per layer
+    assert synthetic.POOL_BLOCKS_12GIB == 5461
+    assert synthetic.POOL_BLOCKS_12GIB * 16 == 87376
+
+
+def test_capacity_table():
+    """Page A, section 8.1.2 table and section 8.3.2: allocation in 16-token blocks at
+    144 KiB per token; shared 6144-token prefix stored once."""
+    c = GOLD["capacity"]
+    kib = GOLD["kv_bytes_per_token"]["value"] // 1024
+    nb = lambda L: -(-L // 16)
+    assert c["short_in"] + c["out"] - 1 == c["short_tokens"]
+    assert nb(c["short_tokens"]) * 16 == c["short_alloc_tokens"]
+    assert nb(c["long_tokens"]) * 16 == c["long_alloc_tokens"]
+    assert c["short_in"] * kib // 1024 == c["short_mib_after_prefill"]
+    assert c["long_in"] * kib // 1024 == c["long_mib_after_prefill"]
+    assert c["short_alloc_tokens"] * kib // 1024 == c["short_mib"]
+    assert c["long_alloc_tokens"] * kib // 1024 == c["long_mib"]
+    assert c["pool_mib"] // c["short_mib"] == c["fit_short"]
+    assert c["pool_mib"] // c["long_mib"] == c["fit_long"]
+    # Shared prefix through the harness allocator: 16 long requests whose first 384
+    # blocks alias one set of physical blocks.
+    prefix_blocks = c["prefix_tokens"] // 16
+    bt = synthetic.place_blocks(np.random.default_rng(0), 6000, [nb(c["long_tokens"])] * 16, prefix_blocks)
+    unique = len(set(bt.ravel().tolist()) - {-1})
+    assert prefix_blocks * 16 * kib // 1024 == c["prefix_mib"]
+    assert unique * 16 * kib // 1024 == c["shared_total_mib_16"]
+    per_req = (nb(c["long_tokens"]) - prefix_blocks) * 16 * kib // 1024
+    assert (c["pool_mib"] - c["prefix_mib"]) // per_req == c["fit_long_shared"]
+
+
+def test_paging_example_and_sharing():
+    """Page A, section 8.3.1: lengths 9, 13, 5, 15 in 4-token pages -> 52 slots (waste 22 -> 10);
+    A and B sharing their first 8 tokens -> 44 slots."""
+    e = GOLD["paging_example"]
+    p = e["page"]
+    nbs = [-(-L // p) for L in e["lengths"]]
+    bt = synthetic.place_blocks(np.random.default_rng(1), 64, nbs)
+    assert len(set(bt.ravel().tolist()) - {-1}) * p == e["paged_slots"]
+    assert e["max_len"] * len(e["lengths"]) - sum(e["lengths"]) == e["waste_whole"]
+    assert e["paged_slots"] - sum(e["lengths"]) == e["waste_paged"]
+    # only A and B share: alias their first two blocks
+    shared = e["shared_tokens_AB"] // p
+    btab = synthetic.place_blocks(np.random.default_rng(2), 64, nbs[:2], shared)
+    btcd = synthetic.place_blocks(np.random.default_rng(3), 64, nbs[2:])
+    used = len(set(btab.ravel().tolist()) - {-1}) + len(set(btcd.ravel().tolist()) - {-1})
+    assert used * p == e["paged_slots_shared"]
+    assert e["reserved_whole"] == e["max_len"] * 4
+
+
+def test_four_branches():
+    """Page A, section 8.3.2: 4 x (95 + 9) = 416 references to 95 + 4 x 9 = 131 physical blocks."""
+    b = GOLD["branches"]
+    bt = synthetic.place_blocks(np.random.default_rng(4), 1000, [b["shared_blocks"] + b["own_blocks"]] * b["branches"],
+                                b["shared_blocks"])
+    assert int((bt >= 0).sum()) == b["references"]
+    assert len(set(bt.ravel().tolist()) - {-1}) == b["physical"]
+
+
+# ---------------------------------------------------------------- indexing pins
+
+def test_tutorial_request_a_slots():
+    """Page B diagram: request A has 40 tokens in blocks 7, 1, 3 (last one 8 of 16 used);
+    so token 39 is slot 3*16 + 7 and tokens 0..15 live in block 7, which B also uses."""
+    e = GOLD["tutorial_request_A"]
+    bt = np.array(e["block_table"], np.int32)
+    B = e["block_size"]
+    slots = [oracle.slot(bt, p, B) for p in range(e["tokens"])]
+    assert slots[:16] == list(range(7 * 16, 8 * 16))
+    assert slots[16:32] == list(range(16, 32))
+    assert slots[32:] == list(range(48, 48 + e["last_block_used"]))
+    assert slots[-1] == 55
+    assert -(-e["tokens"] // B) == len(bt)
+    # oracle append of token 39 lands in physical block 3 at offset 7, nothing else changes
+    kp = np.zeros((8, 2, B, 4), np.uint16)
+    kn = np.arange(8, dtype=np.uint16).reshape(1, 2, 4) + 1
+    k2, _ = oracle.append(kp, kp, kn, kn, [slots[-1]], 2, 4, B, 8)
+    assert np.array_equal(k2[3, :, 7], kn[0])
+    k2[3, :, 7] = 0
+    assert not k2.any()
+
+
+def test_append_skips_negative_slots_and_keeps_bytes():
+    B, Hkv, D, nb = 16, 2, 8, 6
+    kp = _bf16((nb, Hkv, B, D))
+    vp = _bf16((nb, Hkv, B, D))
+    kn, vn = _bf16((3, Hkv, D)), _bf16((3, Hkv, D))
+    k2, v2 = oracle.append(kp, vp, kn, vn, [5, -1, 4 * B + 15], Hkv, D, B, nb)
+    assert np.array_equal(k2[0, :, 5], kn[0]) and np.array_equal(v2[4, :, 15], vn[2])
+    mask = np.ones(kp.shape, bool)
+    mask[0, :, 5] = False
+    mask[4, :, 15] = False
+    assert np.array_equal(k2[mask], kp[mask]) and np.array_equal(v2[mask], vp[mask])
+    with pytest.raises(ValueError):
+        oracle.append(kp, vp, kn, vn, [nb * B], Hkv, D, B, nb)   # slot past the pool
+
+
+def test_generator_chunks_consistent_with_oracle_append():
+    one, chunks = synthetic.prompt_chunks(seed=9, prompt_len=96, chunk=32, num_q_heads=4, num_kv_heads=2,
+                                          num_blocks=16)
+    for a, b in zip(chunks[:-1], chunks[1:]):
+        kp, vp = oracle.append(a.k_pool, a.v_pool, a.k_new, a.v_new, a.slot_mapping, 2, 128, 16, 16)
+        assert np.array_equal(kp, b.k_pool) and np.array_equal(vp, b.v_pool)
+
+
+# ---------------------------------------------------------------- causal-mask pins
+
+@pytest.mark.parametrize("case", GOLD["causal_pairs"], ids=lambda c: f"c{c['c']}_h{c['h']}")
+def test_causal_pair_count(case):
+    """N_pair = ch + c(c+1)/2 (page A, section 8.2.3), counted by the oracle's own loop."""
+    c, h = case["c"], case["h"]
+    D = 8
+    kv = c + h
+    nb = -(-kv // 16)
+    q = np.zeros((c, 1, D), np.uint16)
+    kp = np.zeros((nb, 1, 16, D), np.uint16)
+    bt = np.arange(nb, dtype=np.int32)[None]
+    res = oracle.attention(q, kp, kp, bt, [c], [kv], 1, 1, D, 16, nb, 1.0)
+    assert res["pairs"] == case["pairs"]
+
+
+def test_chunked_pairs_sum_to_prompt_triangle():
+    # four 512-token chunks of a 2048 prompt visit 2048*2049/2 pairs, as one shot does
+    D, total = 4, 0
+    for k in range(4):
+        c, h = 512, 512 * k
+        nb = (c + h) // 16
+        res = oracle.attention(np.zeros((c, 1, D), np.uint16), np.zeros((nb, 1, 16, D), np.uint16),
+                               np.zeros((nb, 1, 16, D), np.uint16), np.arange(nb, dtype=np.int32)[None],
+                               [c], [c + h], 1, 1, D, 16, nb, 1.0)
+        total += res["pairs"]
+    assert total == 2048 * 2049 // 2 == 2098176
+
+
+# ---------------------------------------------------------------- softmax / output pins
+
+@pytest.mark.parametrize("Hq,Hkv,qo,kv", [(8, 2, 1, 17), (8, 2, 5, 40), (4, 4, 33, 33), (6, 3, 7, 70), (8, 1, 16, 16)])
+def test_matches_torch_sdpa_dense(Hq, Hkv, qo, kv):
+    """Brute force: with the blocks laid out in order, paged attention is dense scaled
+    dot-product attention with a bottom-right causal mask and KV heads repeated over
+    contiguous groups of query heads; torch's SDPA in float64 is the reference, and
+    scipy's logsumexp of the masked scores pins the LSE."""
+    from scipy.special import logsumexp
+    D = 128
+    c = _contiguous_case(Hq, Hkv, D, qo, kv, seed=Hq * 100 + kv)
+    res = _run(c, Hq, Hkv, D, qo, kv)
+    q = torch.from_numpy(bf16_bits_to_f32(c["q"]).astype(np.float64)).permute(1, 0, 2)      # [Hq][qo][D]
+    k = torch.from_numpy(bf16_bits_to_f32(c["kd"]).astype(np.float64)).permute(1, 0, 2)     # [Hkv][kv][D]
+    v = torch.from_numpy(bf16_bits_to_f32(c["vd"]).astype(np.float64)).permute(1, 0, 2)
+    g = Hq // Hkv
+    k = k.repeat_interleave(g, dim=0)
+    v = v.repeat_interleave(g, dim=0)
+    mask = torch.ones(qo, kv, dtype=torch.bool).tril(diagonal=kv - qo)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=c["scale"])
+    got = torch.from_numpy(res["out_f64"]).permute(1, 0, 2)
+    assert torch.allclose(got, ref, rtol=0, atol=1e-12)
+    scores = (q @ k.transpose(1, 2)).numpy() * c["scale"]
+    scores = np.where(mask.numpy()[None], scores, -np.inf)
+    lse_ref = logsumexp(scores, axis=-1).T                                                   # [qo][Hq]
+    assert np.allclose(res["lse_f64"], lse_ref, rtol=0, atol=1e-12)
+    # the bf16 output is the double output rounded to nearest even
+    assert np.array_equal(res["out"], oracle.round_bf16(res["out_f64"].ravel()).reshape(res["out"].shape))
+    assert np.array_equal(res["lse"], res["lse_f64"].astype(np.float32))
+
+
+def test_single_key_gives_v_and_scaled_dot():
+    """kv_len = 1: the softmax weight is 1, so O = V exactly and LSE = scale * q.k."""
+    Hq, Hkv, D = 4, 2, 128
+    c = _contiguous_case(Hq, Hkv, D, 1, 1, seed=3)
+    res = _run(c, Hq, Hkv, D, 1, 1)
+    for h in range(Hq):
+        kvh = h // (Hq // Hkv)
+        assert np.array_equal(res["out"][0, h], c["vd"][0, kvh])
+        qk = float(np.dot(bf16_bits_to_f32(c["q"][0, h]).astype(np.float64),
+                          bf16_bits_to_f32(c["kd"][0, kvh]).astype(np.float64)))
+        assert abs(res["lse_f64"][0, h] - c["scale"] * qk) < 1e-12
+
+
+def test_identical_keys_give_mean_v():
+    """All keys equal: uniform weights, O = mean(V) and LSE = scale*q.k + ln(n)."""
+    Hq, Hkv, D, n = 2, 1, 128, 37
+    c = _contiguous_case(Hq, Hkv, D, 1, n, seed=4)
+    for j in range(n):
+        c["kp"][j // 16, :, j % 16] = c["kd"][0]
+    res = _run(c, Hq, Hkv, D, 1, n)
+    mean_v = bf16_bits_to_f32(c["vd"]).astype(np.float64).mean(axis=0)          # [Hkv][D]
+    for h in range(Hq):
+        assert np.allclose(res["out_f64"][0, h], mean_v[0], rtol=0, atol=1e-13)
+        qk = float(np.dot(bf16_bits_to_f32(c["q"][0, h]).astype(np.float64),
+                          bf16_bits_to_f32(c["kd"][0, 0]).astype(np.float64)))
+        assert abs(res["lse_f64"][0, h] - (c["scale"] * qk + math.log(n))) < 1e-12
+
+
+def test_zero_scale_gives_mean_v():
+    Hq, Hkv, D, n = 4, 2, 128, 50
+    c = _contiguous_case(Hq, Hkv, D, 1, n, seed=5, scale=0.0)
+    res = _run(c, Hq, Hkv, D, 1, n)
+    mean_v = bf16_bits_to_f32(c["vd"]).astype(np.float64).mean(axis=0)
+    for h in range(Hq):
+        assert np.allclose(res["out_f64"][0, h], mean_v[h // 2], rtol=0, atol=1e-13)
+        assert abs(res["lse_f64"][0, h] - math.log(n)) < 1e-12
+
+
+def test_dominant_key_selects_its_value():
+    """One key aligned with q and far larger than the rest takes all the weight."""
+    Hq, Hkv, D, n = 1, 1, 128, 40
+    c = _contiguous_case(Hq, Hkv, D, 1, n, seed=6)
+    j0 = 23
+    c["kp"][j0 // 16, 0, j0 % 16] = f32_to_bf16_bits(bf16_bits_to_f32(c["q"][0, 0]) * np.float32(4.0))
+    res = _run(c, Hq, Hkv, D, 1, n)
+    v0 = bf16_bits_to_f32(c["vp"][j0 // 16, 0, j0 % 16]).astype(np.float64)
+    assert np.allclose(res["out_f64"][0, 0], v0, atol=1e-6)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_fig_8_10_block_table_equals_contiguous():
+    """Page A fig. 8-10: logical blocks 0,1,2 in physical blocks 2,0,3 (block 1 free).
+    Reading through the table gives the same result as reading the blocks in order;
+    the free block holds NaN and is never read."""
+    f = GOLD["fig_8_10"]
+    Hq, Hkv, D, qo, kv = 4, 2, 128, 3, 40
+    c = _contiguous_case(Hq, Hkv, D, qo, kv, seed=7)
+    ref = _run(c, Hq, Hkv, D, qo, kv)
+    kp = np.full((4, Hkv, 16, D), synthetic.BF16_NAN, np.uint16)
+    vp = kp.copy()
+    for logical, phys in enumerate(f["block_table"]):
+        kp[phys] = c["kp"][logical]
+        vp[phys] = c["vp"][logical]
+    got = oracle.attention(c["q"], kp, vp, np.array([f["block_table"]], np.int32), [qo], [kv], Hq, Hkv, D, 16, 4,
+                           c["scale"])
+    assert f["free_block"] not in f["block_table"]
+    assert np.array_equal(got["out"], ref["out"]) and np.array_equal(got["lse"], ref["lse"])
+
+
+def test_block_permutation_invariance():
+    wl = synthetic.config_tiny(seed=11)
+    _, _, ref = oracle.run_workload(wl)
+    perm = np.random.default_rng(5).permutation(wl.num_blocks).astype(np.int32)   # old -> new id
+    kp = np.empty_like(wl.k_pool)
+    vp = np.empty_like(wl.v_pool)
+    kp[perm] = wl.k_pool
+    vp[perm] = wl.v_pool
+    bt = np.where(wl.block_tables >= 0, perm[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
+    sm = (perm[wl.slot_mapping // 16] * 16 + wl.slot_mapping % 16).astype(np.int32)
+    k2, v2 = oracle.append(kp, vp, wl.k_new, wl.v_new, sm, wl.num_kv_heads, 128, 16, wl.num_blocks)
+    got = oracle.attention(wl.q, k2, v2, bt, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads, 128, 16,
+                           wl.num_blocks, wl.scale)
+    assert np.array_equal(got["out"], ref["out"]) and np.array_equal(got["lse"], ref["lse"])
+
+
+def test_shared_prefix_equals_duplicated_blocks():
+    """Page A section 8.3.2 (note on the four-branch run: shared branches give the same
+    outputs): aliasing prefix blocks equals storing a private copy per request."""
+    wl = synthetic.build("shared", 21, 8, 2, qo_len=[1, 1, 3], kv_len=[70, 90, 67], num_blocks=64,
+                         shared_prefix_blocks=3)
+    _, _, ref = oracle.run_workload(wl)
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    bt = wl.block_tables.copy()
+    free = sorted(set(range(wl.num_blocks)) - set(bt.ravel().tolist()))
+    for r in range(1, wl.num_reqs):            # give requests 1.. their own copy of the prefix
+        for b in range(3):
+            new = free.pop()
+            kp[new], vp[new] = kp[bt[r, b]], vp[bt[r, b]]
+            bt[r, b] = new
+    assert len(set(bt[:, :3].ravel().tolist())) == 3 * wl.num_reqs
+    k2, v2 = oracle.append(kp, vp, wl.k_new, wl.v_new, wl.slot_mapping, 2, 128, 16, 64)
+    got = oracle.attention(wl.q, k2, v2, bt, wl.qo_len, wl.kv_len, 8, 2, 128, 16, 64, wl.scale)
+    assert np.array_equal(got["out"], ref["out"]) and np.array_equal(got["lse"], ref["lse"])
+
+
+def test_shared_block_rows_coincide():
+    """Page B diagram: B's table is [7], A's is [7, 1, 3].  The same prompt in block 7 gives B
+    exactly A's first 16 outputs."""
+    Hq, Hkv, D = 4, 2, 128
+    g = np.random.default_rng(8)
+    kp, vp = _bf16((8, Hkv, 16, D), gen=g), _bf16((8, Hkv, 16, D), gen=g)
+    qa = _bf16((40, Hq, D), gen=g)
+    q = np.concatenate([qa, qa[:16]])
+    bt = np.array([[7, 1, 3], [7, -1, -1]], np.int32)
+    res = oracle.attention(q, kp, vp, bt, [40, 16], [40, 16], Hq, Hkv, D, 16, 8, 1 / math.sqrt(D))
+    assert np.array_equal(res["out"][40:], res["out"][:16])
+    assert np.array_equal(res["lse"][40:], res["lse"][:16])
+
+
+def test_chunked_prefill_equals_one_shot():
+    """Page A section 8.2.3: a prompt processed in chunks attends exactly as in one shot."""
+    one, chunks = synthetic.prompt_chunks(seed=10, prompt_len=200, chunk=64, num_q_heads=8, num_kv_heads=2,
+                                          num_blocks=32)
+    _, _, ref = oracle.run_workload(one)
+    outs, lses = [], []
+    for wl in chunks:
+        _, _, r = oracle.run_workload(wl)
+        outs.append(r["out"])
+        lses.append(r["lse"])
+    assert np.array_equal(np.concatenate(outs), ref["out"])
+    assert np.array_equal(np.concatenate(lses), ref["lse"])
+
+
+def test_poisoned_slots_never_read():
+    wl = synthetic.config_tiny(seed=12)
+    assert np.isnan(bf16_bits_to_f32(wl.k_pool)).any()
+    _, _, res = oracle.run_workload(wl)
+    assert not np.isnan(bf16_bits_to_f32(res["out"])).any()
+    assert np.isfinite(res["lse"]).all()
+
+
+def test_row_select_computes_only_selected():
+    wl = synthetic.config_tiny(seed=13)
+    _, _, full = oracle.run_workload(wl)
+    sel = np.array([0, 1, 0, 1], np.uint8)
+    _, _, part = oracle.run_workload(wl, row_select=sel)
+    assert np.array_equal(part["out"][[1, 3]], full["out"][[1, 3]])
+    assert not part["out"][[0, 2]].any()
+    assert part["pairs"] == int(wl.kv_len[1] + wl.kv_len[3])
+
+
+# ---------------------------------------------------------------- rounding pin
+
+def test_round_bf16_matches_torch_on_float32_values():
+    """For values exactly representable in float32, torch's float32 -> bfloat16 cast is a
+    single round-to-nearest-even; the oracle's double -> bf16 must agree bit for bit."""
+    g = np.random.default_rng(99)
+    x = np.concatenate([g.standard_normal(20000), g.standard_normal(2000) * 1e-38, g.standard_normal(2000) * 1e30,
+                        np.ldexp(1.0, np.arange(-140, 128)).astype(np.float64)]).astype(np.float32)
+    bits = x.view(np.uint32)
+    ties = ((bits & 0xFFFF0000) | 0x8000).view(np.float32)                          # exact halfway cases
+    x = np.concatenate([x, ties, -ties]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_round_bf16_double_only_cases():
+    # 1 + 2^-8 is a tie -> even (1.0); a hair above rounds up; 1 + 3*2^-8 ties up to even
+    assert oracle.round_bf16(1 + 2.0 ** -8)[0] == 0x3F80
+    assert oracle.round_bf16(1 + 2.0 ** -8 + 2.0 ** -40)[0] == 0x3F81
+    assert oracle.round_bf16(1 + 3 * 2.0 ** -8)[0] == 0x3F82
+    assert oracle.round_bf16(-0.0)[0] == 0x8000
+    assert oracle.round_bf16(2.0 ** -133)[0] == 0x0001
+    assert oracle.round_bf16(2.0 ** 128)[0] == 0x7F80
+    assert oracle.round_bf16(float("nan"))[0] == 0x7FC0
