@@ -1,0 +1,227 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the path over one layer's batch: pa_plan (host) ->
+pa_append_kv -> pa_attention_batch.  The headline workload is the Qwen3-8B
+single-layer decode step (32 requests, kv_len = 2048 + U[0,255], 32 query / 8 KV
+heads, head_dim 128, 16-token blocks, bf16); its value is algorithmic HBM bytes per
+second.  The mixed continuous batch (one 512-token prefill chunk at offset 4096 plus
+31 decode rows, 543 new tokens) is timed the same way and reported in tokens/s.
+
+Each step reads a different copy of the KV pools (the copies stand for different
+layers), so no step finds the previous step's KV in the 256 MB last-level cache.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-step attention HBM GB/s (% of peak) + mixed-batch tokens/s, Qwen3-8B layer"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+TOKEN_LAYER_BYTES = 2 * 8 * 128 * 2        # K + V of one token in one layer, all 8 KV heads
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes the method itself must move for one layer step (shared blocks once)."""
+    B = wl.block_size
+    table = sum(-(-int(L) // B) * 4 for L in wl.kv_len)
+    # unique token slots read: a block shared by several rows counts once, with the
+    # largest number of its tokens any row reads
+    slots = {}
+    for r in range(wl.num_reqs):
+        nb = -(-int(wl.kv_len[r]) // B)
+        for b in range(nb):
+            blk = int(wl.block_tables[r, b])
+            n = min(B, int(wl.kv_len[r]) - b * B)
+            slots[blk] = max(slots.get(blk, 0), n)
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * 2
+    kv_unique = sum(slots.values()) * per_tok
+    kv_logical = int(wl.kv_len.sum()) * per_tok
+    q = wl.total_q * wl.num_q_heads * wl.head_dim * 2
+    o = q
+    lse = wl.total_q * wl.num_q_heads * 4
+    meta = table + 8 * wl.num_reqs
+    append = wl.total_q * per_tok * 2 + wl.total_q * 4
+    return dict(kv_unique=kv_unique, kv_logical=kv_logical, attention=kv_unique + q + o + lse + meta,
+                append=append, step=kv_unique + q + o + lse + meta + append)
+
+
+def prefill_flops(wl) -> int:
+    """4 * head_dim * Hq FLOPs per visible (query, key) pair of the prefill rows."""
+    pairs = 0
+    for r in range(wl.num_reqs):
+        c, kv = int(wl.qo_len[r]), int(wl.kv_len[r])
+        if c > 1:
+            h = kv - c
+            pairs += c * h + c * (c + 1) // 2
+    return pairs * 4 * wl.head_dim * wl.num_q_heads
+
+
+class Stepper:
+    """Device copies of a workload, with `copies` KV-pool replicas rotated per step."""
+
+    def __init__(self, wl, copies: int, device="cuda"):
+        import torch
+
+        import paged_kv_attention_04_amd as pa
+
+        self.pa, self.wl = pa, wl
+        self.g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+        self.num_cus = pa.num_cus(0)
+        kp, vp = pa.to_device(wl.k_pool, device), pa.to_device(wl.v_pool, device)
+        self.pools = [(kp, vp)] + [(kp.clone(), vp.clone()) for _ in range(copies - 1)]
+        self.q = pa.to_device(wl.q, device)
+        self.bt = pa.to_device(wl.block_tables, device)
+        self.qo_indptr = pa.to_device(wl.qo_indptr, device)
+        self.kv = pa.to_device(wl.kv_len, device)
+        self.sm = pa.to_device(wl.slot_mapping, device)
+        self.kn, self.vn = pa.to_device(wl.k_new, device), pa.to_device(wl.v_new, device)
+        self.out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device=device)
+        self.lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=device)
+        self.plan = pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
+        self.ws = pa.workspace_for(self.plan, device)
+        self.i = 0
+
+    def step(self, attention_only: bool = False):
+        pa, wl = self.pa, self.wl
+        kp, vp = self.pools[self.i % len(self.pools)]
+        self.i += 1
+        if not attention_only:
+            self.plan = pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
+            pa.pa_append_kv(self.g, kp, vp, self.kn, self.vn, self.sm)
+        pa.pa_attention_batch(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
+                              self.lse, self.ws)
+
+
+def time_steps(stepper, steps: int, warmup: int, attention_only: bool = False) -> float:
+    """Seconds per step over exactly `steps` steps, bracketed by synchronisations."""
+    import torch
+    for _ in range(warmup):
+        stepper.step(attention_only)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        stepper.step(attention_only)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def event_time(stepper, reps: int) -> float:
+    """Average device time of one pa_attention_batch call, from HIP events recorded on
+    the stream the kernels run on."""
+    import torch
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record(stream)
+        stepper.step(attention_only=True)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
+
+
+def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
+    """The oracle, as it stands, on the host cores: whole decode steps repeated until
+    `min_seconds` have passed; reported in the same unit as the GPU value."""
+    import oracle
+
+    kp, vp = oracle.append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
+                           wl.head_dim, wl.block_size, wl.num_blocks)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.attention(wl.q, kp, vp, wl.block_tables, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
+                         wl.head_dim, wl.block_size, wl.num_blocks, wl.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    ab = algorithmic_bytes(wl)
+    return {"value": round(ab["attention"] * reps / el / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full attention passes of the decode-step workload (32 requests, "
+                      f"{int(wl.kv_len.sum())} KV tokens), fp64 C oracle, {el:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=8, help="KV pool replicas rotated over the steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_attention_04_amd as pa
+    import synthetic
+
+    torch.cuda.set_device(0)
+    pa.lib()
+
+    # headline: Qwen3-8B single-layer decode step
+    wl = synthetic.config_decode(poison=False)
+    ab = algorithmic_bytes(wl)
+    st = Stepper(wl, args.copies)
+    sec = time_steps(st, args.steps, args.warmup)
+    t_attn = event_time(st, max(args.steps, 50))
+    value = ab["step"] / sec / 1e9
+    achieved = ab["attention"] / t_attn / 1e9
+
+    # mixed continuous batch: tokens per second of a whole step
+    wm = synthetic.config_mixed(poison=False)
+    sm = Stepper(wm, args.copies)
+    sec_m = time_steps(sm, args.steps, args.warmup)
+    t_m = event_time(sm, max(args.steps, 50))
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_decode_step: 32 requests, kv_len 2048+U[0,255], 32 q / 8 kv heads, "
+                               "head_dim 128, 16-token blocks, bf16 KV pool of 5461 blocks, 1 layer",
+                   "kv_bytes_unique": ab["kv_unique"], "step_bytes": ab["step"],
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "plan": {"split_blocks": st.plan.split_blocks, "max_splits": st.plan.max_splits,
+                            "decode_items": st.plan.decode_items}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_attention_batch (decode split kernel + split merge)",
+                     "avg_us": round(t_attn * 1e6, 3)},
+        "mixed_batch": {"tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
+                        "attention_us": round(t_m * 1e6, 3), "new_tokens": wm.total_q,
+                        "prefill_tflops_if_alone": None,
+                        "prefill_flops": prefill_flops(wm)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(synthetic.config_decode(poison=False), args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

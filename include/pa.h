@@ -1,0 +1,186 @@
+/*
+ * pa.h -- paged-KV attention for a continuous batch that mixes decode rows
+ * (qo_len = 1) with chunked-prefill rows (qo_len = chunk, causal), on AMD
+ * Instinct MI355X (gfx950).  Plain C ABI: host or device pointers and sizes,
+ * no framework types.
+ *
+ * Vocabulary, from the pages this library implements:
+ *   - KV is stored in fixed-size blocks of `block_size` tokens; each request has
+ *     a block table mapping logical block -> physical block, and a physical
+ *     block may sit anywhere in the pool (AI-infra book ch. 8 "Inference
+ *     optimisation", section 8.3.1 and fig. 8-10; serving tutorial, section
+ *     "PagedAttention: KV cache in pages", which also gives 16-token blocks).
+ *   - Several block tables may point at the same physical blocks (a shared
+ *     prefix is stored once: book section 8.3.1 fig. 8-13 and section 8.3.2).
+ *   - qo_len is a row's number of new (query) tokens and kv_len the number of
+ *     KV entries it attends over; decode rows have qo_len = 1 (Perplexity blog
+ *     on disaggregated prefill and decode, section on prefill vs decode).
+ *   - A chunk of c new tokens at context h attends causally: the i-th new
+ *     token (0-based) sees keys 0 .. h + i (book section 8.2.3, N_pair sum).
+ *   - Inside a block the pool is laid out head-major ("HND"): one KV head's
+ *     block_size x head_dim rows are contiguous (Perplexity blog, paragraph on
+ *     NHD vs HND page layout).
+ *
+ * Layouts (bf16 = 16-bit brain float, stored as its bit pattern):
+ *   k_pool, v_pool  bf16 [num_blocks][num_kv_heads][block_size][head_dim]
+ *   q, out          bf16 [total_q][num_q_heads][head_dim]; the rows of request r
+ *                   are qo_indptr[r] .. qo_indptr[r+1]-1, in token order
+ *   lse             float [total_q][num_q_heads], natural log of the softmax
+ *                   denominator sum_j exp(scale * q.k_j)
+ *   block_tables    int32 [num_reqs][max_blocks_per_req]; entries past
+ *                   ceil(kv_len / block_size) are never read
+ *   k_new, v_new    bf16 [n_tokens][num_kv_heads][head_dim]
+ *   slot_mapping    int32 [n_tokens]: block_id * block_size + offset, < 0 = skip
+ *
+ * Semantics (per request r, new token i, query head h):
+ *   kvh = h / (num_q_heads / num_kv_heads)   (grouped-query attention, contiguous groups)
+ *   p   = kv_len[r] - qo_len[r] + i           (position of the token; keys 0..p visible)
+ *   out = sum_j softmax_j(scale * q.k_j) v_j  over j = 0..p, with k_j, v_j read at
+ *         pool[block_tables[r][j / block_size]][kvh][j % block_size]
+ * kv_len counts the tokens after this step's append, so a row sees its own new
+ * token: call pa_append_kv before pa_attention_batch on the same stream.
+ *
+ * Ownership and ordering: the caller allocates and owns every buffer (device
+ * memory for everything the kernels touch, host memory for plans and the
+ * validators' inputs).  The library allocates no device memory and keeps no
+ * global state.  Every device call is asynchronous on `stream` (a hipStream_t;
+ * NULL means the null stream).  A block may be freed or rewritten only after the
+ * stream work that reads it has completed (book section 8.3.2: release needs the
+ * last reference gone *and* the device done with the block); an append must
+ * never target a block that another request's table still reads (copy-on-write
+ * is the caller's job, book section 8.3.2 fig. 8-15).
+ *
+ * Errors: every entry point returns a pa_status and never aborts.  Cheap checks
+ * (null pointers, supported geometry, plan / workspace consistency) run before
+ * any launch.  Content checks that need a scan of host copies (block ids in
+ * range, 1 <= qo_len <= kv_len, slots in range and not repeated) are in
+ * pa_validate_batch / pa_validate_append.  The kernels bound-check what they read
+ * and write: a block id outside the pool or a row whose lengths disagree with the
+ * plan is not read and that row's output is set to NaN; an out-of-range slot is
+ * not written.  A failed launch maps to PA_ERR_HIP.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+    PA_ERR_SHAPE = -2,       /* lengths inconsistent (qo_len < 1, kv_len < qo_len, ...) */
+    PA_ERR_RANGE = -3,       /* a block id or slot outside the pool, a repeated slot */
+    PA_ERR_WORKSPACE = -4,   /* workspace too small for the plan                   */
+    PA_ERR_UNSUPPORTED = -5, /* geometry the kernels are not built for             */
+    PA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed         */
+} pa_status;
+
+/* One layer's attention geometry and pool size. */
+typedef struct pa_geometry {
+    int32_t num_q_heads;   /* query heads (32 for Qwen3-8B)                                   */
+    int32_t num_kv_heads;  /* KV heads (8 for Qwen3-8B); num_q_heads / num_kv_heads must be 4  */
+    int32_t head_dim;      /* must be 128                                                      */
+    int32_t block_size;    /* tokens per block; must be 16                                     */
+    int32_t num_blocks;    /* physical blocks in each of the K and V pools                     */
+    float scale;           /* score scale, normally 1 / sqrt(head_dim)                         */
+} pa_geometry;
+
+/* Most rows with qo_len > 1 that one plan can hold. */
+#define PA_MAX_PREFILL_ROWS 128
+
+/*
+ * The host-side work plan for one batch.  A pure function of the host copies of
+ * qo_len / kv_len, the geometry and the CU count; it can be reused for every
+ * layer of a step (all layers share the lengths).  Plain data: copy it freely.
+ */
+typedef struct pa_plan_t {
+    int32_t num_q_heads, num_kv_heads;   /* geometry the plan was made for                    */
+    int32_t num_reqs;                    /* rows of the batch                                 */
+    int32_t total_q;                     /* sum of qo_len                                     */
+    int32_t num_decode_rows;             /* rows with qo_len == 1                             */
+    int32_t num_prefill_rows;            /* rows with qo_len > 1                              */
+    int32_t split_blocks;                /* KV blocks per decode split                        */
+    int32_t max_splits;                  /* largest split count of any decode row             */
+    int32_t decode_items;                /* (row, KV head, split) work items                  */
+    int32_t prefill_tiles;               /* query tiles over all prefill rows                 */
+    int32_t prefill_req[PA_MAX_PREFILL_ROWS];       /* request index of each prefill row      */
+    int32_t prefill_tile_start[PA_MAX_PREFILL_ROWS + 1]; /* prefix sums of tiles per row      */
+    uint64_t workspace_bytes;            /* device workspace pa_attention_batch needs         */
+} pa_plan_t;
+
+/*
+ * Build the plan.  qo_len_host / kv_len_host: host int32 [num_reqs].  num_cus: the
+ * device's compute-unit count (256 on MI355X; see pa_query_num_cus).
+ * split_blocks: 0 picks the split length automatically so that the decode work
+ * items fill the CUs several times over (the pages motivate splitting attention
+ * over kv_len as well as over requests when a batch has few tokens: Perplexity
+ * blog, section on prefill vs decode); > 0 forces that many blocks per split
+ * (clamped to 1 .. 64).  Errors: PA_ERR_NULL, PA_ERR_SHAPE (qo_len < 1 or
+ * kv_len < qo_len), PA_ERR_UNSUPPORTED (geometry, or more than
+ * PA_MAX_PREFILL_ROWS prefill rows).
+ */
+pa_status pa_plan(const pa_geometry* geometry, int32_t num_reqs, const int32_t* qo_len_host,
+                  const int32_t* kv_len_host, int32_t num_cus, int32_t split_blocks, pa_plan_t* plan);
+
+/*
+ * Write this step's new K/V rows into the pools through the slot mapping
+ * (book section 8.3.1: a token's KV goes to a slot of the block its table
+ * names; Perplexity blog: the per-layer append happens before attention).
+ * Device pointers: k_pool, v_pool (written in place), k_new, v_new, slot_mapping.
+ * Slots < 0 are skipped; slots >= num_blocks * block_size are not written.
+ * Repeated slots are invalid (pa_validate_append reports them); which write wins
+ * is then unspecified.  Errors: PA_ERR_NULL, PA_ERR_UNSUPPORTED, PA_ERR_SHAPE
+ * (n_tokens < 0), PA_ERR_HIP.
+ */
+pa_status pa_append_kv(const pa_geometry* geometry, void* k_pool, void* v_pool, const void* k_new,
+                       const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, void* stream);
+
+/*
+ * Attention for the whole mixed batch (decode rows and chunked-prefill rows).
+ * plan: host pointer to a plan built from the same lengths.  Device pointers: q,
+ * k_pool, v_pool, block_tables, qo_indptr (int32 [num_reqs + 1], prefix sums of
+ * qo_len), kv_len (int32 [num_reqs]), out, lse, workspace (at least
+ * plan->workspace_bytes bytes, 256-byte aligned; may be NULL when that is 0).
+ * Errors: PA_ERR_NULL, PA_ERR_UNSUPPORTED (geometry differs from the plan's),
+ * PA_ERR_WORKSPACE, PA_ERR_HIP.
+ */
+pa_status pa_attention_batch(const pa_geometry* geometry, const pa_plan_t* plan, const void* q,
+                             const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                             int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side content checks on host copies of a batch's arguments: 1 <= qo_len <=
+ * kv_len, ceil(kv_len / block_size) <= max_blocks_per_req, and every table entry
+ * a row reads names a block in [0, num_blocks).  Returns PA_OK, PA_ERR_NULL,
+ * PA_ERR_SHAPE or PA_ERR_RANGE; *bad_index (may be NULL) receives the offending
+ * request index.
+ */
+pa_status pa_validate_batch(const pa_geometry* geometry, int32_t num_reqs, const int32_t* qo_len_host,
+                            const int32_t* kv_len_host, const int32_t* block_tables_host,
+                            int32_t max_blocks_per_req, int32_t* bad_index);
+
+/*
+ * Host-side check of a slot mapping: every slot is < 0 or below
+ * num_blocks * block_size, and no non-negative slot repeats.  Returns PA_OK,
+ * PA_ERR_NULL, PA_ERR_SHAPE or PA_ERR_RANGE; *bad_index (may be NULL) receives
+ * the offending token index.
+ */
+pa_status pa_validate_append(const pa_geometry* geometry, const int32_t* slot_mapping_host, int32_t n_tokens,
+                             int32_t* bad_index);
+
+/* Compute-unit count of a HIP device (for pa_plan).  PA_ERR_HIP on failure. */
+pa_status pa_query_num_cus(int32_t device, int32_t* num_cus);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

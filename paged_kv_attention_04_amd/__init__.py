@@ -1,0 +1,239 @@
+"""Python binding for libpa.so: paged-KV attention for mixed decode / chunked-prefill
+batches on MI355X.
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream.  The entry points keep the
+C names (``pa_plan``, ``pa_append_kv``, ``pa_attention_batch``); see include/pa.h for
+argument meaning, layouts, ownership and errors.  If the library has not been built
+the binding raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libpa.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
+
+PA_MAX_PREFILL_ROWS = 128
+HEAD_DIM = 128
+BLOCK_SIZE = 16
+
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_RANGE", -4: "PA_ERR_WORKSPACE",
+          -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_HIP"}
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, code: int, extra: str = ""):
+        self.code = code
+        text = lib().pa_status_string(code).decode() if _lib is not None else ""
+        super().__init__(f"{fn} -> {STATUS.get(code, code)} ({text}){extra}")
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+    @classmethod
+    def make(cls, num_q_heads: int, num_kv_heads: int, num_blocks: int, scale: Optional[float] = None,
+             head_dim: int = HEAD_DIM, block_size: int = BLOCK_SIZE) -> "Geometry":
+        return cls(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                   head_dim ** -0.5 if scale is None else scale)
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("num_reqs", ctypes.c_int32),
+                ("total_q", ctypes.c_int32), ("num_decode_rows", ctypes.c_int32),
+                ("num_prefill_rows", ctypes.c_int32), ("split_blocks", ctypes.c_int32),
+                ("max_splits", ctypes.c_int32), ("decode_items", ctypes.c_int32), ("prefill_tiles", ctypes.c_int32),
+                ("prefill_req", ctypes.c_int32 * PA_MAX_PREFILL_ROWS),
+                ("prefill_tile_start", ctypes.c_int32 * (PA_MAX_PREFILL_ROWS + 1)),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpa.so (built in-tree by build.build_library); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python -m paged_kv_attention_04_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    G, PL = ctypes.POINTER(Geometry), ctypes.POINTER(Plan)
+    L.pa_plan.argtypes = [G, i32, P, P, i32, i32, PL]
+    L.pa_append_kv.argtypes = [G, P, P, P, P, P, i32, P]
+    L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
+    L.pa_validate_batch.argtypes = [G, i32, P, P, P, i32, P]
+    L.pa_validate_append.argtypes = [G, P, i32, P]
+    L.pa_query_num_cus.argtypes = [i32, P]
+    for fn in ("pa_plan", "pa_append_kv", "pa_attention_batch", "pa_validate_batch", "pa_validate_append",
+               "pa_query_num_cus"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def header_functions() -> list:
+    """Names of the functions include/pa.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(pa_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise PaError(fn, code)
+
+
+def _np_ptr(a):
+    import numpy as np
+    assert isinstance(a, np.ndarray) and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dev_ptr(t, dtype=None, name="tensor"):
+    import torch
+    if t is None:
+        return None
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype not in dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def num_cus(device: int = 0) -> int:
+    v = ctypes.c_int32(0)
+    _check("pa_query_num_cus", lib().pa_query_num_cus(device, ctypes.byref(v)))
+    return int(v.value)
+
+
+def pa_plan(geometry: Geometry, qo_len, kv_len, num_cus: int = 256, split_blocks: int = 0) -> Plan:
+    """Host planner; qo_len / kv_len are host int32 sequences."""
+    import numpy as np
+    qo = np.ascontiguousarray(qo_len, dtype=np.int32)
+    kv = np.ascontiguousarray(kv_len, dtype=np.int32)
+    if qo.shape != kv.shape:
+        raise ValueError("qo_len and kv_len differ in length")
+    plan = Plan()
+    _check("pa_plan", lib().pa_plan(ctypes.byref(geometry), int(qo.size), _np_ptr(qo), _np_ptr(kv), int(num_cus),
+                                    int(split_blocks), ctypes.byref(plan)))
+    return plan
+
+
+
+
+def _bf16_types():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def pa_append_kv(geometry: Geometry, k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
+    import torch
+    n = int(slot_mapping.numel())
+    if n == 0:
+        return
+    bf = _bf16_types()
+    _check("pa_append_kv", lib().pa_append_kv(
+        ctypes.byref(geometry), _dev_ptr(k_pool, bf, "k_pool"), _dev_ptr(v_pool, bf, "v_pool"),
+        _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"),
+        _dev_ptr(slot_mapping, (torch.int32,), "slot_mapping"), n, _stream_handle(stream)))
+
+
+def pa_attention_batch(geometry: Geometry, plan: Plan, q, k_pool, v_pool, block_tables, qo_indptr, kv_len, out, lse,
+                       workspace=None, stream=None) -> None:
+    import torch
+    bf = _bf16_types()
+    i32 = (torch.int32,)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_attention_batch", lib().pa_attention_batch(
+        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(k_pool, bf, "k_pool"),
+        _dev_ptr(v_pool, bf, "v_pool"), _dev_ptr(block_tables, i32, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"), _dev_ptr(out, bf, "out"),
+        _dev_ptr(lse, (torch.float32,), "lse"), _dev_ptr(workspace, None, "workspace"), ws_bytes,
+        _stream_handle(stream)))
+
+
+def pa_validate_batch(geometry: Geometry, qo_len, kv_len, block_tables):
+    """Host check; returns (status_code, bad_request_index)."""
+    import numpy as np
+    qo = np.ascontiguousarray(qo_len, dtype=np.int32)
+    kv = np.ascontiguousarray(kv_len, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    bad = ctypes.c_int32(-1)
+    rc = lib().pa_validate_batch(ctypes.byref(geometry), int(qo.size), _np_ptr(qo), _np_ptr(kv), _np_ptr(bt),
+                                 int(bt.shape[1]) if bt.ndim == 2 else 0, ctypes.byref(bad))
+    return rc, int(bad.value)
+
+
+def pa_validate_append(geometry: Geometry, slot_mapping):
+    """Host check; returns (status_code, bad_token_index)."""
+    import numpy as np
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    bad = ctypes.c_int32(-1)
+    rc = lib().pa_validate_append(ctypes.byref(geometry), _np_ptr(sm), int(sm.size), ctypes.byref(bad))
+    return rc, int(bad.value)
+
+
+def workspace_for(plan: Plan, device="cuda"):
+    """A workspace tensor of the size the plan asks for (None if it needs none)."""
+    import torch
+    if plan.workspace_bytes == 0:
+        return None
+    return torch.empty(int(plan.workspace_bytes), dtype=torch.uint8, device=device)
+
+
+def to_device(arr, device="cuda"):
+    """numpy array -> device tensor (bf16 bit patterns stay uint16-shaped as int16)."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", validate: bool = True):
+    """Upload a workload (see synthetic.Workload for the fields), append its new tokens,
+    plan and run attention; returns host numpy (k_pool, v_pool, out, lse)."""
+    import numpy as np
+    import torch
+    g = Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale, wl.head_dim, wl.block_size)
+    if validate:
+        rc, bad = pa_validate_batch(g, wl.qo_len, wl.kv_len, wl.block_tables)
+        if rc:
+            raise PaError("pa_validate_batch", rc, f" at request {bad}")
+        rc, bad = pa_validate_append(g, wl.slot_mapping)
+        if rc:
+            raise PaError("pa_validate_append", rc, f" at token {bad}")
+    plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks)
+    kp, vp = to_device(wl.k_pool, device), to_device(wl.v_pool, device)
+    q = to_device(wl.q, device)
+    bt = to_device(wl.block_tables, device)
+    qo_indptr = to_device(wl.qo_indptr, device)
+    kv = to_device(wl.kv_len, device)
+    sm = to_device(wl.slot_mapping, device)
+    kn, vn = to_device(wl.k_new, device), to_device(wl.v_new, device)
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device=device)
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=device)
+    ws = workspace_for(plan, device)
+    pa_append_kv(g, kp, vp, kn, vn, sm)
+    pa_attention_batch(g, plan, q, kp, vp, bt, qo_indptr, kv, out, lse, ws)
+    torch.cuda.synchronize()
+    return (kp.cpu().numpy().view(np.uint16), vp.cpu().numpy().view(np.uint16),
+            out.cpu().numpy().view(np.uint16), lse.cpu().numpy())

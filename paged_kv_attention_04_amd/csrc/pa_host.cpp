@@ -1,0 +1,155 @@
+// Host side of the library: the work planner, the content validators and the
+// status strings.  No device code and no HIP calls.
+#include <string.h>
+
+#include <algorithm>
+#include <unordered_set>
+
+#include "pa_internal.h"
+
+namespace {
+
+// Decode work items per CU the automatic split aims for.  Each item is one
+// wavefront; several per CU keep enough KV loads in flight to cover HBM latency.
+constexpr int kItemsPerCu = 8;
+// Shortest automatic split: a split also costs one partial write and one merge read
+// of Hq * (head_dim + 1) floats, so very short splits waste bandwidth.
+constexpr int kMinAutoSplitBlocks = 4;
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+}  // namespace
+
+extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32_t* qo_len,
+                             const int32_t* kv_len, int32_t num_cus, int32_t split_blocks, pa_plan_t* plan)
+{
+    if (!g || !plan || (num_reqs > 0 && (!qo_len || !kv_len)))
+        return PA_ERR_NULL;
+    if (!pa::geometry_supported(g))
+        return PA_ERR_UNSUPPORTED;
+    if (num_reqs < 0)
+        return PA_ERR_SHAPE;
+    memset(plan, 0, sizeof(*plan));
+    plan->num_q_heads = g->num_q_heads;
+    plan->num_kv_heads = g->num_kv_heads;
+    plan->num_reqs = num_reqs;
+
+    int64_t decode_blocks = 0, total_q = 0;
+    int32_t max_decode_blocks = 0;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        if (qo_len[r] < 1 || kv_len[r] < qo_len[r])
+            return PA_ERR_SHAPE;
+        total_q += qo_len[r];
+        if (qo_len[r] == 1) {
+            int32_t nb = ceil_div(kv_len[r], pa::kBlock);
+            decode_blocks += nb;
+            max_decode_blocks = std::max(max_decode_blocks, nb);
+            plan->num_decode_rows++;
+        } else {
+            if (plan->num_prefill_rows >= PA_MAX_PREFILL_ROWS)
+                return PA_ERR_UNSUPPORTED;
+            int32_t i = plan->num_prefill_rows++;
+            plan->prefill_req[i] = r;
+            plan->prefill_tile_start[i + 1] = plan->prefill_tile_start[i] + ceil_div(qo_len[r], pa::kPrefillQ);
+        }
+    }
+    if (total_q > INT32_MAX)
+        return PA_ERR_SHAPE;
+    plan->total_q = (int32_t)total_q;
+    plan->prefill_tiles = plan->prefill_tile_start[plan->num_prefill_rows];
+
+    // Split length: split the decode rows' KV over enough (row, KV head, split) items
+    // to give every CU several wavefronts, on whole blocks.
+    int32_t sb;
+    if (split_blocks > 0) {
+        sb = std::min(split_blocks, pa::kMaxSplitBlocks);
+    } else {
+        int64_t target = (int64_t)std::max(num_cus, 1) * kItemsPerCu;
+        int64_t work = decode_blocks * g->num_kv_heads;
+        int64_t want = std::max<int64_t>(1, (work + target - 1) / target);
+        sb = (int32_t)std::min<int64_t>(std::max<int64_t>(want, kMinAutoSplitBlocks), pa::kMaxSplitBlocks);
+        sb = std::min(sb, std::max(max_decode_blocks, 1));
+    }
+    plan->split_blocks = sb;
+    int64_t items = 0;
+    int32_t max_splits = 0;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        if (qo_len[r] != 1)
+            continue;
+        int32_t s = ceil_div(ceil_div(kv_len[r], pa::kBlock), sb);
+        max_splits = std::max(max_splits, s);
+        items += (int64_t)s * g->num_kv_heads;
+    }
+    plan->max_splits = max_splits;
+    plan->decode_items = (int32_t)std::min<int64_t>(items, INT32_MAX);
+    plan->workspace_bytes = pa::workspace_layout(num_reqs, max_splits, g->num_q_heads).total;
+    return PA_OK;
+}
+
+extern "C" pa_status pa_validate_batch(const pa_geometry* g, int32_t num_reqs, const int32_t* qo_len,
+                                       const int32_t* kv_len, const int32_t* block_tables,
+                                       int32_t max_blocks_per_req, int32_t* bad_index)
+{
+    if (bad_index)
+        *bad_index = -1;
+    if (!g || (num_reqs > 0 && (!qo_len || !kv_len || !block_tables)))
+        return PA_ERR_NULL;
+    if (num_reqs < 0 || max_blocks_per_req < 0 || g->block_size <= 0)
+        return PA_ERR_SHAPE;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        if (qo_len[r] < 1 || kv_len[r] < qo_len[r] || ceil_div(kv_len[r], g->block_size) > max_blocks_per_req) {
+            if (bad_index)
+                *bad_index = r;
+            return PA_ERR_SHAPE;
+        }
+        int32_t nb = ceil_div(kv_len[r], g->block_size);
+        const int32_t* row = block_tables + (size_t)r * max_blocks_per_req;
+        for (int32_t b = 0; b < nb; ++b) {
+            if (row[b] < 0 || row[b] >= g->num_blocks) {
+                if (bad_index)
+                    *bad_index = r;
+                return PA_ERR_RANGE;
+            }
+        }
+    }
+    return PA_OK;
+}
+
+extern "C" pa_status pa_validate_append(const pa_geometry* g, const int32_t* slot_mapping, int32_t n_tokens,
+                                        int32_t* bad_index)
+{
+    if (bad_index)
+        *bad_index = -1;
+    if (!g || (n_tokens > 0 && !slot_mapping))
+        return PA_ERR_NULL;
+    if (n_tokens < 0)
+        return PA_ERR_SHAPE;
+    const int64_t num_slots = (int64_t)g->num_blocks * g->block_size;
+    std::unordered_set<int32_t> seen;
+    seen.reserve((size_t)n_tokens * 2);
+    for (int32_t t = 0; t < n_tokens; ++t) {
+        int32_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        if (s >= num_slots || !seen.insert(s).second) {
+            if (bad_index)
+                *bad_index = t;
+            return PA_ERR_RANGE;
+        }
+    }
+    return PA_OK;
+}
+
+extern "C" const char* pa_status_string(pa_status s)
+{
+    switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent lengths (need 1 <= qo_len <= kv_len and enough table entries)";
+    case PA_ERR_RANGE: return "block id or slot outside the pool, or a repeated slot";
+    case PA_ERR_WORKSPACE: return "workspace smaller than the plan needs";
+    case PA_ERR_UNSUPPORTED: return "unsupported geometry (need head_dim 128, block_size 16, 4 query heads per KV head)";
+    case PA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}

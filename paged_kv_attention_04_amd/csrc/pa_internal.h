@@ -1,0 +1,43 @@
+// Internal constants and helpers shared by the host planner and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+constexpr int kHeadDim = 128;   // head dimension the kernels are built for
+constexpr int kBlock = 16;      // tokens per KV block
+constexpr int kGroup = 4;       // query heads per KV head (grouped-query attention)
+constexpr int kMaxSplitBlocks = 64;   // one block id per lane of a wavefront
+constexpr int kPrefillQ = 16;   // new tokens per prefill tile (x kGroup heads = 64 MFMA rows)
+
+inline bool geometry_supported(const pa_geometry* g)
+{
+    return g->head_dim == kHeadDim && g->block_size == kBlock && g->num_kv_heads > 0 &&
+           g->num_q_heads == g->num_kv_heads * kGroup && g->num_blocks > 0;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Split partials: normalised FP32 output [num_reqs][max_splits][Hq][head_dim], then the
+// per-split log2-sum-exp [num_reqs][max_splits][Hq].
+struct WorkspaceLayout {
+    size_t part_o = 0, part_lse = 0, total = 0;
+};
+
+inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, int32_t num_q_heads)
+{
+    WorkspaceLayout w;
+    if (max_splits <= 1 || num_reqs <= 0)
+        return w;
+    size_t n = (size_t)num_reqs * (size_t)max_splits * (size_t)num_q_heads;
+    w.part_o = 0;
+    w.part_lse = align256(n * kHeadDim * sizeof(float));
+    w.total = align256(w.part_lse + n * sizeof(float));
+    return w;
+}
+
+}  // namespace pa

@@ -1,0 +1,765 @@
+// HIP kernels for gfx950 (MI355X) and the device-side C entry points.
+//
+//   pa_append_scatter   new K/V rows -> pool slots named by the slot mapping
+//   pa_decode_split     one wavefront per (decode row, KV head, KV split): block-table
+//                       gather, 4 KiB K tiles staged in LDS, QK^T with bf16 dot2,
+//                       online softmax in FP32, PV accumulation in FP32
+//   pa_merge_splits     log-sum-exp merge of the splits of each (row, query head)
+//   pa_prefill_tile     chunked-prefill rows: one workgroup per (row, KV head, 16 new
+//                       tokens x 4 query heads); S^T = K Q^T and O^T = V^T P^T on BF16
+//                       MFMA with FP32 accumulation, causal mask, online softmax
+//
+// Pool layout: [block][kv_head][token-in-block][dim] (head-major inside a block), so one
+// (block, KV head) tile is 16 x 128 bf16 = 4 KiB of contiguous memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+using pa::kBlock;
+using pa::kGroup;
+using pa::kHeadDim;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.44269504088896341f;
+// Lazy rescaling threshold in log2 units: the running maximum is only raised when a
+// score exceeds it by more than this, so unnormalised weights stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Round two floats to bf16 (nearest even) and pack them, low half first.
+__device__ inline uint32_t pack_bf16(float a, float b)
+{
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int kCtrl>
+__device__ inline float dpp(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+
+__device__ inline float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ inline float readlane_f(float x, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// ------------------------------------------------------------------------------ append
+
+// One thread moves one 16-byte chunk of K and the matching chunk of V.
+__global__ __launch_bounds__(256) void pa_append_scatter(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+                                                         const uint16_t* __restrict__ k_new,
+                                                         const uint16_t* __restrict__ v_new,
+                                                         const int32_t* __restrict__ slot_mapping, int32_t n_tokens,
+                                                         int32_t num_kv_heads, int64_t num_slots)
+{
+    constexpr int kChunks = kHeadDim * 2 / 16;   // 16-byte chunks per (token, head) row
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_token = (int64_t)num_kv_heads * kChunks;
+    if (idx >= (int64_t)n_tokens * per_token)
+        return;
+    const int32_t t = (int32_t)(idx / per_token);
+    const int32_t rem = (int32_t)(idx - (int64_t)t * per_token);
+    const int32_t h = rem / kChunks, c = rem % kChunks;
+    const int32_t slot = slot_mapping[t];
+    if (slot < 0 || (int64_t)slot >= num_slots)
+        return;
+    const int64_t blk = slot / kBlock, off = slot % kBlock;
+    const int64_t dst = ((blk * num_kv_heads + h) * kBlock + off) * kHeadDim / 8 + c;   // in 16-byte units
+    const int64_t src = ((int64_t)t * num_kv_heads + h) * kHeadDim / 8 + c;
+    reinterpret_cast<u32x4*>(k_pool)[dst] = reinterpret_cast<const u32x4*>(k_new)[src];
+    reinterpret_cast<u32x4*>(v_pool)[dst] = reinterpret_cast<const u32x4*>(v_new)[src];
+}
+
+// ------------------------------------------------------------------------------ decode
+
+struct DecodeParams {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* block_tables;
+    const int32_t* qo_indptr;
+    const int32_t* kv_len;
+    uint16_t* out;
+    float* lse;
+    float* part_o;
+    float* part_lse;
+    int32_t max_blocks;
+    int32_t num_reqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t split_blocks;
+    int32_t max_splits;
+    float scale_log2;   // score scale times log2(e): softmax runs in base 2
+};
+
+// A (block, KV head) tile is 16 tokens x 256 bytes.  Lane l moves bytes l*16 + i*1024
+// (i = 0..3): token l/16 + 4i, 16-byte chunk l%16 -- four fully coalesced 1 KiB loads.
+__device__ inline void load_tile(u32x4 (&r)[4], const uint16_t* tile, int lane)
+{
+    const u32x4* p = reinterpret_cast<const u32x4*>(tile) + lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = p[64 * i];
+}
+
+// LDS slot of (token, 16-byte chunk) in the staged K tile.  The chunk index is XORed
+// with 4 * (token % 4) so that both the coalesced writes (16 lanes = one token) and
+// the QK reads (16 lanes = 4 tokens x 4 chunks) touch 16 distinct 16-byte bank groups.
+__device__ inline int k_slot(int token, int chunk) { return token * 16 + (chunk ^ ((token & 3) << 2)); }
+
+// NaN results for a group whose inputs failed a bound check.  `final` writes the row's
+// output directly (the merge kernel skips such rows); otherwise this split's partial is
+// NaN and the merge turns the row into NaN.
+__device__ void decode_write_nan(const DecodeParams& p, int64_t part_index, int q_row, int head0, bool final,
+                                 int lane)
+{
+    const float nan = __builtin_nanf("");
+    if (final) {
+        for (int i = lane; i < kGroup * kHeadDim; i += 64)
+            p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + i] = 0x7FC0;
+        if (lane < kGroup)
+            p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = nan;
+    } else {
+        for (int i = lane; i < kGroup * kHeadDim; i += 64)
+            p.part_o[part_index * kHeadDim + i] = nan;
+        if (lane < kGroup)
+            p.part_lse[part_index + lane] = nan;
+    }
+}
+
+// Grid: max_splits * num_reqs * num_kv_heads wavefronts, KV head fastest so that the
+// eight XCDs (which take workgroups round-robin) each see one KV head of every row.
+__global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
+{
+    __shared__ u32x4 k_lds[kBlock * 16];
+    __shared__ float p_lds[kBlock * kGroup];
+
+    const int lane = threadIdx.x;
+    const int kvh = blockIdx.x % p.num_kv_heads;
+    const int rest = blockIdx.x / p.num_kv_heads;
+    const int r = rest % p.num_reqs;
+    const int split = rest / p.num_reqs;
+    const int q_row = p.qo_indptr[r];
+    if (p.qo_indptr[r + 1] - q_row != 1)
+        return;                                       // not a decode row
+    const int kvlen = p.kv_len[r];
+    const int nblk = (kvlen + kBlock - 1) / kBlock;
+    const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
+    const int head0 = kvh * kGroup;
+    if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits) {   // lengths disagree with the plan
+        if (split == 0)
+            decode_write_nan(p, 0, q_row, head0, true, lane);
+        return;
+    }
+    if (split >= nsplit)
+        return;
+    const int64_t part_index = ((int64_t)r * p.max_splits + split) * p.num_q_heads + head0;
+
+    const int b0 = split * p.split_blocks;
+    const int nb = min(nblk - b0, p.split_blocks);
+    int my_blk = 0;
+    bool bad = false;
+    if (lane < nb) {
+        my_blk = p.block_tables[(int64_t)r * p.max_blocks + b0 + lane];
+        bad = my_blk < 0 || my_blk >= p.num_blocks;
+    }
+    if (__any(bad)) {                                 // a block id outside the pool
+        decode_write_nan(p, part_index, q_row, head0, nsplit == 1, lane);
+        return;
+    }
+
+    // QK role: lane = 4 * token + quarter; the quarter owns 16-byte chunks quarter + 4k.
+    const int t = lane >> 2, qd = lane & 3;
+    // PV role: lane = 16 * token_group + chunk; tokens token_group + 4i, dims 8*chunk..+8.
+    const int chunk = lane & 15, tg = lane >> 4;
+
+    u32x4 qv[kGroup][4];
+    {
+        const uint16_t* qb = p.q + ((int64_t)q_row * p.num_q_heads + head0) * kHeadDim;
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                qv[h][k] = *reinterpret_cast<const u32x4*>(qb + h * kHeadDim + (qd + 4 * k) * 8);
+    }
+
+    float m = -INFINITY;   // running max (base 2) of this lane's head qd, same in all lanes of that head
+    float lsum = 0.f;      // this lane's share of the softmax denominator of head qd
+    float acc[kGroup][8];
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[h][e] = 0.f;
+
+    const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
+    const int64_t kvh_off = (int64_t)kvh * tile_elems;
+    const int64_t blk_stride = (int64_t)p.num_kv_heads * tile_elems;
+
+    u32x4 kr[4], vr[4];
+    {
+        const int blk = __builtin_amdgcn_readlane(my_blk, 0);
+        load_tile(kr, p.k_pool + blk * blk_stride + kvh_off, lane);
+        load_tile(vr, p.v_pool + blk * blk_stride + kvh_off, lane);
+    }
+    for (int j = 0; j < nb; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            k_lds[k_slot(tg + 4 * i, chunk)] = kr[i];
+        u32x4 kn[4], vn[4];
+        if (j + 1 < nb) {
+            const int blk = __builtin_amdgcn_readlane(my_blk, j + 1);
+            load_tile(kn, p.k_pool + blk * blk_stride + kvh_off, lane);
+            load_tile(vn, p.v_pool + blk * blk_stride + kvh_off, lane);
+        }
+        __syncthreads();
+
+        // scores of token t for the four heads, partial over this lane's 32 dims
+        float s[kGroup] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const u32x4 kk = k_lds[k_slot(t, qd + 4 * k)];
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h) {
+                s[h] = dot2_bf16(qv[h][k].x, kk.x, s[h]);
+                s[h] = dot2_bf16(qv[h][k].y, kk.y, s[h]);
+                s[h] = dot2_bf16(qv[h][k].z, kk.z, s[h]);
+                s[h] = dot2_bf16(qv[h][k].w, kk.w, s[h]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+            s[h] += dpp<kQuadXor1>(s[h]);
+            s[h] += dpp<kQuadXor2>(s[h]);
+        }
+        // lane (t, qd) now owns the score of token t for head qd
+        float x = (qd == 0 ? s[0] : qd == 1 ? s[1] : qd == 2 ? s[2] : s[3]) * p.scale_log2;
+        const int pos0 = (b0 + j) * kBlock;
+        if (pos0 + t >= kvlen)
+            x = -INFINITY;
+        if (__any(x > m + kRescaleSlack)) {
+            float mx = fmaxf(m, x);
+            mx = fmaxf(mx, shfl_xor(mx, 4));
+            mx = fmaxf(mx, shfl_xor(mx, 8));
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mx);
+            m = mx;
+            lsum *= alpha;
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h) {
+                const float a = readlane_f(alpha, h);   // lane h is (token 0, head h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[h][e] *= a;
+            }
+        }
+        const float pr = fast_exp2(x - m);
+        lsum += pr;
+        p_lds[lane] = pr;                              // [token][head]
+        __syncthreads();
+
+        const int valid = kvlen - pos0;                // tokens of this block that exist
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = tg + 4 * i;
+            const f32x4 pp = *reinterpret_cast<const f32x4*>(&p_lds[tok * kGroup]);
+            u32x4 v = vr[i];
+            if (valid < kBlock && tok >= valid)
+                v = u32x4{0u, 0u, 0u, 0u};            // slots past kv_len may hold anything
+            const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                                 bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc[0][e] = fmaf(pp.x, vf[e], acc[0][e]);
+                acc[1][e] = fmaf(pp.y, vf[e], acc[1][e]);
+                acc[2][e] = fmaf(pp.z, vf[e], acc[2][e]);
+                acc[3][e] = fmaf(pp.w, vf[e], acc[3][e]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kr[i] = kn[i];
+            vr[i] = vn[i];
+        }
+        __syncthreads();
+    }
+
+    // denominators: sum the 16 tokens' shares of each head
+    float ltot = lsum;
+    ltot += shfl_xor(ltot, 4);
+    ltot += shfl_xor(ltot, 8);
+    ltot += shfl_xor(ltot, 16);
+    ltot += shfl_xor(ltot, 32);
+    // numerators: sum the four token groups
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[h][e] += shfl_xor(acc[h][e], 16);
+            acc[h][e] += shfl_xor(acc[h][e], 32);
+        }
+
+    if (nsplit == 1) {
+        if (lane < 16) {
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h) {
+                const float inv = 1.f / readlane_f(ltot, h);
+                u32x4 o;
+                o.x = pack_bf16(acc[h][0] * inv, acc[h][1] * inv);
+                o.y = pack_bf16(acc[h][2] * inv, acc[h][3] * inv);
+                o.z = pack_bf16(acc[h][4] * inv, acc[h][5] * inv);
+                o.w = pack_bf16(acc[h][6] * inv, acc[h][7] * inv);
+                *reinterpret_cast<u32x4*>(p.out + ((int64_t)q_row * p.num_q_heads + head0 + h) * kHeadDim + chunk * 8) = o;
+            }
+        }
+        if (lane < kGroup)
+            p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = (m + fast_log2(ltot)) * kLn2;
+    } else {
+        const int64_t pi = part_index;
+        if (lane < 16) {
+#pragma unroll
+            for (int h = 0; h < kGroup; ++h) {
+                const float inv = 1.f / readlane_f(ltot, h);
+                f32x4* dst = reinterpret_cast<f32x4*>(p.part_o + (pi + h) * kHeadDim + chunk * 8);
+                dst[0] = f32x4{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
+                dst[1] = f32x4{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
+            }
+        }
+        if (lane < kGroup)
+            p.part_lse[pi + lane] = m + fast_log2(ltot);   // base 2
+    }
+}
+
+// ------------------------------------------------------------------------------ merge
+
+// One wavefront per (row, query head); each lane owns two dims.
+// L = max_s L_s;  w_s = 2^(L_s - L);  O = sum_s w_s O_s / sum_s w_s;  LSE = L + log2(sum_s w_s).
+__global__ __launch_bounds__(64) void pa_merge_splits(DecodeParams p)
+{
+    const int lane = threadIdx.x;
+    const int r = blockIdx.x / p.num_q_heads;
+    const int h = blockIdx.x % p.num_q_heads;
+    const int q_row = p.qo_indptr[r];
+    if (p.qo_indptr[r + 1] - q_row != 1)
+        return;
+    const int kvlen = p.kv_len[r];
+    const int nblk = (kvlen + kBlock - 1) / kBlock;
+    const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
+    if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits || nsplit <= 1)
+        return;
+    const int64_t base = (int64_t)r * p.max_splits * p.num_q_heads + h;
+    float L = -INFINITY;
+    bool nan = false;
+    for (int s = 0; s < nsplit; ++s) {
+        const float ls = p.part_lse[base + (int64_t)s * p.num_q_heads];
+        nan |= (ls != ls);
+        L = fmaxf(L, ls);
+    }
+    float wsum = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const int64_t pi = base + (int64_t)s * p.num_q_heads;
+        const float w = fast_exp2(p.part_lse[pi] - L);
+        const float2 v = reinterpret_cast<const float2*>(p.part_o + pi * kHeadDim)[lane];
+        wsum += w;
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+    }
+    const float inv = nan ? __builtin_nanf("") : 1.f / wsum;
+    reinterpret_cast<uint32_t*>(p.out + ((int64_t)q_row * p.num_q_heads + h) * kHeadDim)[lane] =
+        pack_bf16(o0 * inv, o1 * inv);
+    if (lane == 0)
+        p.lse[(int64_t)q_row * p.num_q_heads + h] = nan ? __builtin_nanf("") : (L + fast_log2(wsum)) * kLn2;
+}
+
+// ------------------------------------------------------------------------------ prefill
+
+struct PrefillParams {
+    const uint16_t* q;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* block_tables;
+    const int32_t* qo_indptr;
+    const int32_t* kv_len;
+    uint16_t* out;
+    float* lse;
+    int32_t max_blocks;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t num_prefill_rows;
+    float scale_log2;
+    int32_t prefill_req[PA_MAX_PREFILL_ROWS];
+    int32_t tile_start[PA_MAX_PREFILL_ROWS + 1];
+};
+
+constexpr int kKeyTile = 64;               // keys per step (four 16-token blocks)
+constexpr int kKStride = kHeadDim + 8;     // K tile row stride in LDS, bf16 units (272 bytes)
+constexpr int kVtStride = kKeyTile + 8;    // V^T tile row stride in LDS, bf16 units (144 bytes)
+
+// Workgroup of four wavefronts per (prefill row, KV head, tile of 16 new tokens).  The
+// tile's 64 MFMA rows are (token, head) pairs, row = 4 * token + head, so the four query
+// heads of a group share every K / V tile.  Wavefront w owns tokens 4w .. 4w+3.
+//
+// MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][k-slice l/16] and
+// B[k-slice l/16][l%16] (8 bf16 each) and receives D[4*(l/16) + e][l%16], e = 0..3.
+//   S^T (keys x rows) = K (keys x dims) . Q^T (dims x rows)          contraction over dims
+//   O^T (dims x rows) += V^T (dims x keys) . P^T (keys x rows)       contraction over keys
+// Each lane's S^T values all belong to one row (l%16), so the softmax statistics and the
+// rescaling of O^T stay lane-local except for one exchange across the four k-slices.
+// In the PV product lane l's eight keys are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of
+// a 32-key slice: exactly the S^T values it already holds; V^T is read with the same key
+// order, and a contraction does not care how its index is permuted.
+__global__ __launch_bounds__(256) void pa_prefill_tile(PrefillParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeyTile * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kHeadDim * kVtStride];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int kvh = blockIdx.x % p.num_kv_heads;
+    const int tile = blockIdx.x / p.num_kv_heads;
+    int pr = 0;
+    while (pr + 1 < p.num_prefill_rows && p.tile_start[pr + 1] <= tile)
+        ++pr;
+    const int r = p.prefill_req[pr];
+    const int qt = tile - p.tile_start[pr];
+    const int q0 = p.qo_indptr[r];
+    const int qlen = p.qo_indptr[r + 1] - q0;
+    const int kvlen = p.kv_len[r];
+    const int head0 = kvh * kGroup;
+    if (qt * pa::kPrefillQ >= qlen)
+        return;
+    const int ctx = kvlen - qlen;               // tokens before this chunk
+    const int nblk_row = (kvlen + kBlock - 1) / kBlock;
+    const bool bad_row = qlen < 2 || ctx < 0 || nblk_row > p.max_blocks;
+    // keys any token of this tile can see: 0 .. ctx + last token of the tile
+    const int kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * pa::kPrefillQ));
+    const int nsteps = (kv_hi + kKeyTile - 1) / kKeyTile;
+
+    const int row = lane & 15, kslice = lane >> 4;
+    const int tok_local = qt * pa::kPrefillQ + 4 * wave + (row >> 2);   // token index within the chunk
+    const int head = head0 + (row & 3);
+    const bool row_valid = tok_local < qlen;
+    const int qpos = ctx + tok_local;                                   // absolute position
+
+    // Q^T operand: row `row`, dims 32*ks + 8*kslice .. +8
+    bf16x8 qop[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (row_valid)
+            v = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)(q0 + tok_local) * p.num_q_heads + head) * kHeadDim +
+                                                 ks * 32 + kslice * 8);
+        qop[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+
+    const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
+    const int64_t kvh_off = (int64_t)kvh * tile_elems;
+    const int64_t blk_stride = (int64_t)p.num_kv_heads * tile_elems;
+    const int32_t* bt = p.block_tables + (int64_t)r * p.max_blocks;
+    bool bad = bad_row;
+
+    // Staging assignments.  K: chunk id = tid + 256 i -> key (tid>>4) + 16 i, 16-byte chunk tid&15.
+    // V: key quad kq = tid&15 (keys 4kq..4kq+3), chunk c16 = tid>>4; transposed on the way into LDS.
+    const int k_key = tid >> 4, k_chunk = tid & 15;
+    const int v_kq = tid & 15, v_chunk = tid >> 4;
+    u32x4 kst[4], vst[4];
+    auto load_step = [&](int step) {
+        const int key0 = step * kKeyTile;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = key0 + k_key + 16 * i;
+            kst[i] = u32x4{0u, 0u, 0u, 0u};
+            if (key < kv_hi) {
+                const int blk = bt[key / kBlock];
+                if (blk >= 0 && blk < p.num_blocks)
+                    kst[i] = *reinterpret_cast<const u32x4*>(p.k_pool + blk * blk_stride + kvh_off +
+                                                             (key % kBlock) * kHeadDim + k_chunk * 8);
+                else
+                    bad = true;
+            }
+        }
+        const int vkey0 = key0 + 4 * v_kq;
+        int vblk = -1;
+        if (vkey0 < kv_hi) {
+            vblk = bt[vkey0 / kBlock];
+            if (vblk < 0 || vblk >= p.num_blocks) {
+                bad = true;
+                vblk = -1;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            vst[i] = u32x4{0u, 0u, 0u, 0u};
+            if (vblk >= 0 && vkey0 + i < kv_hi)
+                vst[i] = *reinterpret_cast<const u32x4*>(p.v_pool + vblk * blk_stride + kvh_off +
+                                                         ((vkey0 + i) % kBlock) * kHeadDim + v_chunk * 8);
+        }
+    };
+    auto store_step = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4*>(&k_lds[(k_key + 16 * i) * kKStride + k_chunk * 8]) = kst[i];
+        // V^T row d holds keys in order; keys 4kq..4kq+3 of dims 8*c16 .. 8*c16+7
+        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vst[0]);
+        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vst[1]);
+        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vst[2]);
+        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vst[3]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            // dims 2w (low halves) and 2w+1 (high halves)
+            const u32x2 lo = u32x2{(v0[w] & 0xffffu) | (v1[w] << 16), (v2[w] & 0xffffu) | (v3[w] << 16)};
+            const u32x2 hi = u32x2{(v0[w] >> 16) | (v1[w] & 0xffff0000u), (v2[w] >> 16) | (v3[w] & 0xffff0000u)};
+            *reinterpret_cast<u32x2*>(&vt_lds[(v_chunk * 8 + 2 * w) * kVtStride + 4 * v_kq]) = lo;
+            *reinterpret_cast<u32x2*>(&vt_lds[(v_chunk * 8 + 2 * w + 1) * kVtStride + 4 * v_kq]) = hi;
+        }
+    };
+
+    f32x4 oacc[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+        oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    if (nsteps > 0)
+        load_step(0);
+    for (int step = 0; step < nsteps; ++step) {
+        __syncthreads();
+        store_step();
+        __syncthreads();
+        if (step + 1 < nsteps)
+            load_step(step + 1);
+
+        // S^T for the four 16-key blocks of this step
+        f32x4 sacc[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(&k_lds[(kb * 16 + row) * kKStride + ks * 32 + kslice * 8]));
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], sacc[kb], 0, 0, 0);
+            }
+        }
+        // lane holds S^T[key = key0 + 16 kb + 4 kslice + e][row]
+        const int key0 = step * kKeyTile;
+        float x[4][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = key0 + 16 * kb + 4 * kslice + e;
+                float v = sacc[kb][e] * p.scale_log2;
+                if (key > qpos || key >= kv_hi)
+                    v = -INFINITY;
+                x[kb][e] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+        const float mnew = fmaxf(m, tmax);
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+        m = mnew;
+        float psum = 0.f;
+        uint32_t pk[4][2];   // P^T operand halves, bf16 pairs
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float pe[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pe[e] = (mnew == -INFINITY) ? 0.f : fast_exp2(x[kb][e] - mnew);
+                psum += pe[e];
+            }
+            pk[kb][0] = pack_bf16(pe[0], pe[1]);
+            pk[kb][1] = pack_bf16(pe[2], pe[3]);
+        }
+        lsum = lsum * alpha + psum;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            oacc[db] *= alpha;
+
+        // O^T += V^T P^T over two 32-key slices
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const bf16x8 b = __builtin_bit_cast(
+                bf16x8, u32x4{pk[2 * ks2][0], pk[2 * ks2][1], pk[2 * ks2 + 1][0], pk[2 * ks2 + 1][1]});
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const uint16_t* vrow = &vt_lds[(db * 16 + row) * kVtStride + 32 * ks2 + 4 * kslice];
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[db], 0, 0, 0);
+            }
+        }
+    }
+
+    float ltot = lsum;
+    ltot += shfl_xor(ltot, 16);
+    ltot += shfl_xor(ltot, 32);
+    bad = __syncthreads_or(bad);
+    if (!row_valid)
+        return;
+    const float nan = __builtin_nanf("");
+    const float inv = bad ? nan : 1.f / ltot;
+    uint16_t* orow = p.out + ((int64_t)(q0 + tok_local) * p.num_q_heads + head) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        const u32x2 o = u32x2{pack_bf16(oacc[db][0] * inv, oacc[db][1] * inv), pack_bf16(oacc[db][2] * inv, oacc[db][3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * kslice) = o;
+    }
+    if (kslice == 0)
+        p.lse[(int64_t)(q0 + tok_local) * p.num_q_heads + head] = bad ? nan : (m + fast_log2(ltot)) * kLn2;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+// ------------------------------------------------------------------------------ C entry points
+
+extern "C" pa_status pa_append_kv(const pa_geometry* g, void* k_pool, void* v_pool, const void* k_new,
+                                  const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, void* stream)
+{
+    if (!g)
+        return PA_ERR_NULL;
+    if (!pa::geometry_supported(g))
+        return PA_ERR_UNSUPPORTED;
+    if (n_tokens < 0)
+        return PA_ERR_SHAPE;
+    if (n_tokens == 0)
+        return PA_OK;
+    if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
+        return PA_ERR_NULL;
+    const int64_t threads = (int64_t)n_tokens * g->num_kv_heads * (kHeadDim * 2 / 16);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX)
+        return PA_ERR_SHAPE;
+    hipLaunchKernelGGL(pa_append_scatter, dim3((uint32_t)blocks), dim3(256), 0, as_stream(stream),
+                       static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
+                       n_tokens, g->num_kv_heads, (int64_t)g->num_blocks * kBlock);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* plan, const void* q,
+                                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                        int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
+        return PA_ERR_UNSUPPORTED;
+    if (plan->num_reqs == 0 || plan->total_q == 0)
+        return PA_OK;
+    if (!q || !k_pool || !v_pool || !block_tables || !qo_indptr || !kv_len || !out || !lse)
+        return PA_ERR_NULL;
+    if (max_blocks_per_req < 1 || plan->num_prefill_rows > PA_MAX_PREFILL_ROWS)
+        return PA_ERR_SHAPE;
+    const pa::WorkspaceLayout ws = pa::workspace_layout(plan->num_reqs, plan->max_splits, g->num_q_heads);
+    if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))
+        return PA_ERR_WORKSPACE;
+    hipStream_t st = as_stream(stream);
+    const float scale_log2 = g->scale * kLog2e;
+
+    if (plan->num_prefill_rows > 0 && plan->prefill_tiles > 0) {
+        PrefillParams pp;
+        pp.q = static_cast<const uint16_t*>(q);
+        pp.k_pool = static_cast<const uint16_t*>(k_pool);
+        pp.v_pool = static_cast<const uint16_t*>(v_pool);
+        pp.block_tables = block_tables;
+        pp.qo_indptr = qo_indptr;
+        pp.kv_len = kv_len;
+        pp.out = static_cast<uint16_t*>(out);
+        pp.lse = lse;
+        pp.max_blocks = max_blocks_per_req;
+        pp.num_q_heads = g->num_q_heads;
+        pp.num_kv_heads = g->num_kv_heads;
+        pp.num_blocks = g->num_blocks;
+        pp.num_prefill_rows = plan->num_prefill_rows;
+        pp.scale_log2 = scale_log2;
+        for (int i = 0; i < PA_MAX_PREFILL_ROWS; ++i)
+            pp.prefill_req[i] = i < plan->num_prefill_rows ? plan->prefill_req[i] : 0;
+        for (int i = 0; i <= PA_MAX_PREFILL_ROWS; ++i)
+            pp.tile_start[i] = i <= plan->num_prefill_rows ? plan->prefill_tile_start[i] : plan->prefill_tiles;
+        const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads;
+        hipLaunchKernelGGL(pa_prefill_tile, dim3((uint32_t)grid), dim3(256), 0, st, pp);
+        if (hipGetLastError() != hipSuccess)
+            return PA_ERR_HIP;
+    }
+    if (plan->num_decode_rows > 0 && plan->max_splits > 0) {
+        DecodeParams dp;
+        dp.q = static_cast<const uint16_t*>(q);
+        dp.k_pool = static_cast<const uint16_t*>(k_pool);
+        dp.v_pool = static_cast<const uint16_t*>(v_pool);
+        dp.block_tables = block_tables;
+        dp.qo_indptr = qo_indptr;
+        dp.kv_len = kv_len;
+        dp.out = static_cast<uint16_t*>(out);
+        dp.lse = lse;
+        dp.part_o = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_o) : nullptr;
+        dp.part_lse = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_lse) : nullptr;
+        dp.max_blocks = max_blocks_per_req;
+        dp.num_reqs = plan->num_reqs;
+        dp.num_q_heads = g->num_q_heads;
+        dp.num_kv_heads = g->num_kv_heads;
+        dp.num_blocks = g->num_blocks;
+        dp.split_blocks = plan->split_blocks;
+        dp.max_splits = plan->max_splits;
+        dp.scale_log2 = scale_log2;
+        const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * g->num_kv_heads;
+        if (grid > INT32_MAX)
+            return PA_ERR_SHAPE;
+        hipLaunchKernelGGL(pa_decode_split, dim3((uint32_t)grid), dim3(64), 0, st, dp);
+        if (hipGetLastError() != hipSuccess)
+            return PA_ERR_HIP;
+        if (plan->max_splits > 1) {
+            hipLaunchKernelGGL(pa_merge_splits, dim3((uint32_t)((int64_t)plan->num_reqs * g->num_q_heads)), dim3(64), 0,
+                               st, dp);
+            if (hipGetLastError() != hipSuccess)
+                return PA_ERR_HIP;
+        }
+    }
+    return PA_OK;
+}
+
+extern "C" pa_status pa_query_num_cus(int32_t device, int32_t* num_cus)
+{
+    if (!num_cus)
+        return PA_ERR_NULL;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return PA_ERR_HIP;
+    *num_cus = v;
+    return PA_OK;
+}

@@ -1,0 +1,185 @@
+"""CPU-side checks of the C-ABI library: it loads, exports what include/pa.h declares,
+and its host functions (planner, validators, status strings, argument checks) behave.
+No kernel is launched here."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_04_amd as pa
+import synthetic
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.lib()
+
+
+def qwen(num_blocks=5461):
+    return pa.Geometry.make(32, 8, num_blocks)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = pa.header_functions()
+    assert set(names) >= {"pa_plan", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
+                          "pa_validate_append", "pa_query_num_cus", "pa_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_sizes_match_header():
+    # int32 x 10 + 128 + 129 int32, then a uint64 at an 8-byte boundary
+    assert ctypes.sizeof(pa.Geometry) == 24
+    assert ctypes.sizeof(pa.Plan) == 8 * ((4 * (10 + 128 + 129) + 7) // 8) + 8
+
+
+def test_status_strings(lib):
+    for code in pa.STATUS:
+        assert lib.pa_status_string(code)
+    assert lib.pa_status_string(12345) == b"unknown status"
+
+
+def _split_ranges(plan, kv):
+    nb = -(-int(kv) // 16)
+    s = plan.split_blocks
+    return [(b, min(nb, b + s)) for b in range(0, nb, s)]
+
+
+@pytest.mark.parametrize("wl_fn", [synthetic.config_tiny, synthetic.config_decode, synthetic.config_mixed])
+def test_plan_splits_tile_each_row_once(wl_fn):
+    wl = wl_fn(poison=False) if wl_fn is not synthetic.config_tiny else wl_fn()
+    g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256)
+    assert plan.num_reqs == wl.num_reqs and plan.total_q == wl.total_q
+    items = 0
+    for r in range(wl.num_reqs):
+        if wl.qo_len[r] != 1:
+            continue
+        ranges = _split_ranges(plan, wl.kv_len[r])
+        covered = [b for lo, hi in ranges for b in range(lo, hi)]
+        assert covered == list(range(-(-int(wl.kv_len[r]) // 16)))     # contiguous, once, block aligned
+        assert all(hi > lo for lo, hi in ranges)                          # no empty split
+        assert len(ranges) <= plan.max_splits
+        items += len(ranges) * wl.num_kv_heads
+    assert items == plan.decode_items
+    assert 1 <= plan.split_blocks <= 64
+
+
+def test_plan_is_pure_and_fills_cus():
+    wl = synthetic.config_decode(poison=False)
+    g = qwen()
+    a = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256)
+    b = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256)
+    assert bytes(a) == bytes(b)
+    assert a.decode_items >= 256 * 4                                    # several wavefronts per CU
+    # batch 1 at 2K: splits stay >= 4 blocks but still spread over many CUs
+    one = pa.pa_plan(g, [1], [2049], 256)
+    assert one.split_blocks >= 4 and one.decode_items >= 8 * 16
+
+
+def test_plan_prefill_rows_and_workspace():
+    g = qwen()
+    qo = [512] + [1] * 31
+    kv = [4608] + [2048 + i for i in range(31)]
+    plan = pa.pa_plan(g, qo, kv, 256)
+    assert plan.num_prefill_rows == 1 and plan.num_decode_rows == 31
+    assert plan.prefill_req[0] == 0 and plan.prefill_tiles == 512 // 16
+    assert plan.prefill_tile_start[1] == 32
+    if plan.max_splits > 1:
+        n = 32 * plan.max_splits * 32
+        assert plan.workspace_bytes >= n * 129 * 4
+    # forced split of 1 block and one large split
+    p1 = pa.pa_plan(g, qo, kv, 256, split_blocks=1)
+    assert p1.split_blocks == 1 and p1.max_splits == -(-2078 // 16)
+    p64 = pa.pa_plan(g, [1], [100], 256, split_blocks=1000)
+    assert p64.split_blocks == 64 and p64.max_splits == 1 and p64.workspace_bytes == 0
+
+
+def test_plan_errors():
+    g = qwen()
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(g, [2], [1])
+    assert e.value.code == -2
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(g, [0], [5])
+    assert e.value.code == -2
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(pa.Geometry.make(32, 16, 10), [1], [5])              # 2 query heads per KV head
+    assert e.value.code == -5
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(pa.Geometry.make(32, 8, 10, head_dim=64), [1], [5])
+    assert e.value.code == -5
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(g, [2] * 129, [2] * 129)                              # too many prefill rows
+    assert e.value.code == -5
+    empty = pa.pa_plan(g, [], [])
+    assert empty.num_reqs == 0 and empty.workspace_bytes == 0
+
+
+def test_validate_batch():
+    wl = synthetic.config_tiny()
+    g = pa.Geometry.make(8, 2, 64)
+    assert pa.pa_validate_batch(g, wl.qo_len, wl.kv_len, wl.block_tables) == (0, -1)
+    bt = wl.block_tables.copy()
+    bt[2, 3] = 64                                                        # past the pool
+    assert pa.pa_validate_batch(g, wl.qo_len, wl.kv_len, bt) == (-3, 2)
+    bt = wl.block_tables.copy()
+    bt[1, 0] = -1
+    assert pa.pa_validate_batch(g, wl.qo_len, wl.kv_len, bt) == (-3, 1)
+    # entries past ceil(kv_len/16) are not read, so -1 there is fine
+    assert wl.block_tables[0, 5] == -1
+    kv = wl.kv_len.copy()
+    kv[3] = 0
+    assert pa.pa_validate_batch(g, wl.qo_len, kv, wl.block_tables) == (-2, 3)
+    kv = wl.kv_len.copy()
+    kv[0] = 16 * wl.block_tables.shape[1] + 1                            # more blocks than the table has
+    assert pa.pa_validate_batch(g, wl.qo_len, kv, wl.block_tables) == (-2, 0)
+
+
+def test_validate_append():
+    g = pa.Geometry.make(8, 2, 4)
+    assert pa.pa_validate_append(g, [0, 5, -1, 63, -7]) == (0, -1)
+    assert pa.pa_validate_append(g, [0, 64]) == (-3, 1)
+    assert pa.pa_validate_append(g, [3, 9, 3]) == (-3, 2)
+
+
+def test_entry_points_reject_bad_arguments_before_launch(lib):
+    g = qwen()
+    plan = pa.pa_plan(g, [1], [100])
+    # NULL pointers for a non-empty batch
+    rc = lib.pa_attention_batch(ctypes.byref(g), ctypes.byref(plan), None, None, None, None, 7, None, None, None,
+                                None, None, 0, None)
+    assert rc == -1
+    # geometry differs from the plan's
+    g2 = pa.Geometry.make(16, 4, 5461)
+    one = ctypes.c_void_p(16)
+    rc = lib.pa_attention_batch(ctypes.byref(g2), ctypes.byref(plan), one, one, one, one, 7, one, one, one, one,
+                                None, 0, None)
+    assert rc == -5
+    # a plan that needs a workspace, given none
+    big = pa.pa_plan(g, [1] * 4, [8000] * 4)
+    assert big.workspace_bytes > 0
+    rc = lib.pa_attention_batch(ctypes.byref(g), ctypes.byref(big), one, one, one, one, 600, one, one, one, one,
+                                None, 0, None)
+    assert rc == -4
+    # append: unsupported geometry, negative count, NULL pools
+    rc = lib.pa_append_kv(ctypes.byref(pa.Geometry.make(32, 8, 10, head_dim=64)), one, one, one, one, one, 1, None)
+    assert rc == -5
+    assert lib.pa_append_kv(ctypes.byref(g), one, one, one, one, one, -1, None) == -2
+    assert lib.pa_append_kv(ctypes.byref(g), None, one, one, one, one, 1, None) == -1
+    assert lib.pa_append_kv(ctypes.byref(g), None, None, None, None, None, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(pa, "_lib", None)
+    monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        pa.lib()
+
+
+def test_product_path_does_not_import_oracle():
+    import subprocess
+    import sys
+    code = ("import sys, paged_kv_attention_04_amd as pa; pa.lib(); "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'")
+    subprocess.check_call([sys.executable, "-c", code], cwd=pa.os.path.dirname(pa._PKG))

@@ -1,0 +1,176 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element
+on the same seeded inputs.
+
+Bars: pa_append_kv is bit-exact over the whole pool (untouched and poisoned slots
+included); attention outputs agree within max |err| <= 2e-2 on the bf16 output and
+<= 1e-3 on the fp32 LSE.  Pool slots that hold no token are NaN, so any read of them
+would show up as NaN in the output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from synthetic import bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-2
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_attention_04_amd as pa
+    pa.lib()
+    yield
+
+
+def _run_gpu(wl, split_blocks=0):
+    import paged_kv_attention_04_amd as pa
+    return pa.run_workload(wl, split_blocks=split_blocks)
+
+
+def _errors(out, lse, ref, rows=None):
+    got, want = bf16_bits_to_f32(out), bf16_bits_to_f32(ref["out"])
+    l_got, l_want = lse, ref["lse"]
+    if rows is not None:
+        got, want, l_got, l_want = got[rows], want[rows], l_got[rows], l_want[rows]
+    assert not np.isnan(got).any(), "NaN in GPU output"
+    return float(np.max(np.abs(got - want))), float(np.max(np.abs(l_got - l_want)))
+
+
+def check(wl, split_blocks=0, label=""):
+    print(f"[gpu] {wl.name} {label} R={wl.num_reqs} total_q={wl.total_q} split={split_blocks}", flush=True)
+    kp, vp, out, lse = _run_gpu(wl, split_blocks)
+    okp, ovp, ref = oracle.run_workload(wl)
+    assert np.array_equal(kp, okp) and np.array_equal(vp, ovp), "append is not bit-exact"
+    eo, el = _errors(out, lse, ref)
+    dec = np.concatenate([np.arange(a, b) for a, b, q in zip(wl.qo_indptr[:-1], wl.qo_indptr[1:], wl.qo_len) if q == 1]
+                         or [np.zeros(0, int)]).astype(int)
+    pre = np.setdiff1d(np.arange(wl.total_q), dec)
+    parts = []
+    if dec.size:
+        parts.append("decode %.2e/%.2e" % _errors(out, lse, ref, dec))
+    if pre.size:
+        parts.append("prefill %.2e/%.2e" % _errors(out, lse, ref, pre))
+    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e} ({', '.join(parts)})", flush=True)
+    assert eo <= TOL_O, f"output error {eo}"
+    assert el <= TOL_LSE, f"LSE error {el}"
+    return out, lse
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_tiny_decode():
+    check(synthetic.config_tiny())
+
+
+def test_tiny_decode_q_times_8():
+    """Large scores force many online-softmax rescales."""
+    check(synthetic.config_tiny(seed=31, q_scale=8.0), label="q*8")
+
+
+def test_qwen3_decode_step():
+    check(synthetic.config_decode())
+
+
+def test_shared_prefix_decode():
+    check(synthetic.config_shared_prefix())
+
+
+def test_mixed_batch():
+    check(synthetic.config_mixed())
+
+
+@pytest.mark.parametrize("batch,long_only", [(1, False), (1, True), (8, False), (32, False), (64, False)])
+def test_sweep_decode_layer(batch, long_only):
+    check(synthetic.config_sweep_decode(batch, layer=batch % 36, long_only=long_only))
+
+
+def test_prompt_chunks_match_oracle_and_one_shot():
+    one, chunks = synthetic.prompt_chunks(seed=5, prompt_len=2048, chunk=512, num_blocks=256)
+    o_one, l_one = check(one, label="one-shot")
+    outs, lses = [], []
+    for wl in chunks:
+        o, l = check(wl, label="chunk")
+        outs.append(o)
+        lses.append(l)
+    o_ch, l_ch = np.concatenate(outs), np.concatenate(lses)
+    d_o = float(np.max(np.abs(bf16_bits_to_f32(o_ch) - bf16_bits_to_f32(o_one))))
+    d_l = float(np.max(np.abs(l_ch - l_one)))
+    print(f"[gpu]   chunked vs one-shot: {d_o:.3e} / {d_l:.3e}", flush=True)
+    assert d_o <= TOL_O and d_l <= TOL_LSE
+
+
+# ------------------------------------------------------------------ planner-independent results
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 64])
+def test_split_sweep(split):
+    check(synthetic.config_tiny(seed=41), split_blocks=split)
+    check(synthetic.build("split_sweep", 42, 32, 8, qo_len=[1] * 6 + [20], kv_len=[1, 16, 17, 700, 1025, 3000, 300],
+                          num_blocks=512), split_blocks=split)
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+def _permuted(wl, seed):
+    perm = np.random.default_rng(seed).permutation(wl.num_blocks).astype(np.int32)
+    kp = np.empty_like(wl.k_pool)
+    vp = np.empty_like(wl.v_pool)
+    kp[perm] = wl.k_pool
+    vp[perm] = wl.v_pool
+    bt = np.where(wl.block_tables >= 0, perm[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
+    sm = (perm[wl.slot_mapping // 16] * 16 + wl.slot_mapping % 16).astype(np.int32)
+    import dataclasses
+    return dataclasses.replace(wl, k_pool=kp, v_pool=vp, block_tables=bt, slot_mapping=sm, name=wl.name + "_perm")
+
+
+@pytest.mark.parametrize("make", [synthetic.config_tiny, lambda: synthetic.build(
+    "perm_mixed", 51, 32, 8, qo_len=[1, 70, 1, 3], kv_len=[300, 1000, 45, 3], num_blocks=300)])
+def test_block_permutation_is_bit_exact(make):
+    """Reduction order depends only on logical positions and the plan, never on where the
+    blocks sit, so relabelling physical blocks leaves every output bit unchanged."""
+    wl = make()
+    _, _, out_a, lse_a = _run_gpu(wl)
+    _, _, out_b, lse_b = _run_gpu(_permuted(wl, 3))
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+
+
+def test_shared_prefix_equals_duplicated_blocks_bit_exact():
+    wl = synthetic.build("shared_gpu", 61, 32, 8, qo_len=[1, 1, 1, 40], kv_len=[600, 700, 513, 900], num_blocks=400,
+                         shared_prefix_blocks=32)
+    _, _, out_a, lse_a = _run_gpu(wl)
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    bt = wl.block_tables.copy()
+    free = sorted(set(range(wl.num_blocks)) - set(bt.ravel().tolist()))
+    for r in range(1, wl.num_reqs):
+        for b in range(32):
+            new = free.pop()
+            kp[new], vp[new] = kp[bt[r, b]], vp[bt[r, b]]
+            bt[r, b] = new
+    import dataclasses
+    dup = dataclasses.replace(wl, k_pool=kp, v_pool=vp, block_tables=bt)
+    _, _, out_b, lse_b = _run_gpu(dup)
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+    check(wl, label="shared vs oracle")
+
+
+# ------------------------------------------------------------------ edge shapes
+
+@pytest.mark.parametrize("qo,kv", [
+    ([1], [1]),                                  # a single key: O = V
+    ([1, 1], [16, 32]),                          # whole blocks, no tail
+    ([2], [2]),                                  # smallest prefill row, no context
+    ([17], [17]),                                # ragged prefill tile
+    ([33, 1], [1000, 1]),                        # prefill at an offset + single-key decode
+    ([16], [16 * 64 + 1]),                       # context spanning many key tiles
+    ([1], [16 * 64 * 3 + 5]),                    # several 64-block splits
+    ([5, 1, 8, 1], [5, 2000, 200, 17]),          # short speculative-style rows mixed with decode
+])
+def test_edge_shapes(qo, kv):
+    need = sum(-(-k // 16) for k in kv)
+    check(synthetic.build("edge", 71 + len(qo), 8, 2, qo_len=qo, kv_len=kv, num_blocks=need + 3))
