@@ -120,8 +120,8 @@ typedef struct pa_plan_t {
  * over kv_len as well as over requests when a batch has few tokens: Perplexity
  * blog, section on prefill vs decode); > 0 forces that many blocks per split
  * (clamped to 1 .. 64).  Errors: PA_ERR_NULL, PA_ERR_SHAPE (qo_len < 1 or
- * kv_len < qo_len), PA_ERR_UNSUPPORTED (geometry, or more than
- * PA_MAX_PREFILL_ROWS prefill rows).
+ * kv_len < qo_len), PA_ERR_UNSUPPORTED (geometry, more than PA_MAX_PREFILL_ROWS
+ * prefill rows, or split decode rows with num_reqs * num_kv_heads > 16384).
  */
 pa_status pa_plan(const pa_geometry* geometry, int32_t num_reqs, const int32_t* qo_len_host,
                   const int32_t* kv_len_host, int32_t num_cus, int32_t split_blocks, pa_plan_t* plan);
@@ -145,6 +145,10 @@ pa_status pa_append_kv(const pa_geometry* geometry, void* k_pool, void* v_pool, 
  * k_pool, v_pool, block_tables, qo_indptr (int32 [num_reqs + 1], prefix sums of
  * qo_len), kv_len (int32 [num_reqs]), out, lse, workspace (at least
  * plan->workspace_bytes bytes, 256-byte aligned; may be NULL when that is 0).
+ * The workspace holds split partials and, in its first 64 KiB, one completion
+ * counter per (row, KV head): allocate it zeroed once; every call leaves the
+ * counters zero again, so the buffer can be reused by later calls (of any plan) on
+ * the same stream.  Two calls that run concurrently must not share a workspace.
  * Errors: PA_ERR_NULL, PA_ERR_UNSUPPORTED (geometry differs from the plan's),
  * PA_ERR_WORKSPACE, PA_ERR_HIP.
  */

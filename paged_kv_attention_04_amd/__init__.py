@@ -191,11 +191,12 @@ def pa_validate_append(geometry: Geometry, slot_mapping):
 
 
 def workspace_for(plan: Plan, device="cuda"):
-    """A workspace tensor of the size the plan asks for (None if it needs none)."""
+    """A zeroed workspace of the size the plan asks for (None if it needs none).  Its
+    completion counters must start at zero; the library leaves them zero after each call."""
     import torch
     if plan.workspace_bytes == 0:
         return None
-    return torch.empty(int(plan.workspace_bytes), dtype=torch.uint8, device=device)
+    return torch.zeros(int(plan.workspace_bytes), dtype=torch.uint8, device=device)
 
 
 def to_device(arr, device="cuda"):

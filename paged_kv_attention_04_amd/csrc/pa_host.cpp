@@ -80,6 +80,8 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
         max_splits = std::max(max_splits, s);
         items += (int64_t)s * g->num_kv_heads;
     }
+    if (max_splits > 1 && (int64_t)num_reqs * g->num_kv_heads > pa::kMaxCounters)
+        return PA_ERR_UNSUPPORTED;   // more (row, KV head) completion counters than the workspace holds
     plan->max_splits = max_splits;
     plan->decode_items = (int32_t)std::min<int64_t>(items, INT32_MAX);
     plan->workspace_bytes = pa::workspace_layout(num_reqs, max_splits, g->num_q_heads).total;

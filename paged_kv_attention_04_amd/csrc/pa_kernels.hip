@@ -2,9 +2,9 @@
 //
 //   pa_append_scatter   new K/V rows -> pool slots named by the slot mapping
 //   pa_decode_split     one wavefront per (decode row, KV head, KV split): block-table
-//                       gather, 4 KiB K tiles staged in LDS, QK^T with bf16 dot2,
-//                       online softmax in FP32, PV accumulation in FP32
-//   pa_merge_splits     log-sum-exp merge of the splits of each (row, query head)
+//                       gather with several blocks of loads in flight, QK^T with bf16
+//                       dot2, online softmax in FP32, PV accumulation in FP32, and the
+//                       log-sum-exp merge of the splits done by the last split to finish
 //   pa_prefill_tile     chunked-prefill rows: one workgroup per (row, KV head, 16 new
 //                       tokens x 4 query heads); S^T = K Q^T and O^T = V^T P^T on BF16
 //                       MFMA with FP32 accumulation, causal mask, online softmax
@@ -57,11 +57,16 @@ __device__ inline float dpp(float x)
 }
 constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;   // lane i <-> 7 - i inside each half-row
 
 __device__ inline float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Relaxed agent-scope accesses: coherent across the XCDs without cache maintenance.
+__device__ inline void store_agent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline float load_agent(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 __device__ inline float readlane_f(float x, int lane)
 {
@@ -106,6 +111,7 @@ struct DecodeParams {
     const int32_t* kv_len;
     uint16_t* out;
     float* lse;
+    uint32_t* counters;   // one per (row, KV head): splits finished so far
     float* part_o;
     float* part_lse;
     int32_t max_blocks;
@@ -118,46 +124,70 @@ struct DecodeParams {
     float scale_log2;   // score scale times log2(e): softmax runs in base 2
 };
 
-// A (block, KV head) tile is 16 tokens x 256 bytes.  Lane l moves bytes l*16 + i*1024
-// (i = 0..3): token l/16 + 4i, 16-byte chunk l%16 -- four fully coalesced 1 KiB loads.
-__device__ inline void load_tile(u32x4 (&r)[4], const uint16_t* tile, int lane)
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 3
+#endif
+// KV blocks whose loads are in flight while a block is being processed.
+constexpr int kDecodeDepth = PA_DECODE_DEPTH;
+
+// One (block, KV head) tile is 16 tokens x 256 bytes, read by four 16-byte loads per lane.
+// K: lane = 8 * t8 + c8 reads tokens t8 and t8 + 8, 16-byte chunks c8 and c8 + 8; each load
+//    instruction covers eight whole 128-byte lines (one half-row of each of 8 tokens).
+//    k[0] = (t8, c8), k[1] = (t8, c8 + 8), k[2] = (t8 + 8, c8), k[3] = (t8 + 8, c8 + 8).
+// V: lane = 16 * tg + c16 reads tokens tg + 4i, chunk c16: four contiguous 1 KiB loads.
+struct KvStage {
+    u32x4 k[4];
+    u32x4 v[4];
+};
+
+__device__ inline void load_stage(KvStage& s, const uint16_t* ktile, const uint16_t* vtile, int lane)
 {
-    const u32x4* p = reinterpret_cast<const u32x4*>(tile) + lane;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(ktile);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vtile) + lane;
+    const int t8 = lane >> 3, c8 = lane & 7;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        r[i] = p[64 * i];
+        s.k[i] = kp[(t8 + 8 * (i >> 1)) * 16 + c8 + 8 * (i & 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s.v[i] = vp[64 * i];
 }
 
-// LDS slot of (token, 16-byte chunk) in the staged K tile.  The chunk index is XORed
-// with 4 * (token % 4) so that both the coalesced writes (16 lanes = one token) and
-// the QK reads (16 lanes = 4 tokens x 4 chunks) touch 16 distinct 16-byte bank groups.
-__device__ inline int k_slot(int token, int chunk) { return token * 16 + (chunk ^ ((token & 3) << 2)); }
-
-// NaN results for a group whose inputs failed a bound check.  `final` writes the row's
-// output directly (the merge kernel skips such rows); otherwise this split's partial is
-// NaN and the merge turns the row into NaN.
-__device__ void decode_write_nan(const DecodeParams& p, int64_t part_index, int q_row, int head0, bool final,
-                                 int lane)
+__device__ inline float dot16(const u32x4& q, const u32x4& k, float acc)
 {
-    const float nan = __builtin_nanf("");
-    if (final) {
-        for (int i = lane; i < kGroup * kHeadDim; i += 64)
-            p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + i] = 0x7FC0;
-        if (lane < kGroup)
-            p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = nan;
-    } else {
-        for (int i = lane; i < kGroup * kHeadDim; i += 64)
-            p.part_o[part_index * kHeadDim + i] = nan;
-        if (lane < kGroup)
-            p.part_lse[part_index + lane] = nan;
-    }
+    acc = dot2_bf16(q.x, k.x, acc);
+    acc = dot2_bf16(q.y, k.y, acc);
+    acc = dot2_bf16(q.z, k.z, acc);
+    return dot2_bf16(q.w, k.w, acc);
 }
 
-// Grid: max_splits * num_reqs * num_kv_heads wavefronts, KV head fastest so that the
-// eight XCDs (which take workgroups round-robin) each see one KV head of every row.
+// Sum over the eight lanes of a half-row (lanes 8a .. 8a+7): two quad butterflies, then
+// the half-row mirror (lane i <-> 7 - i) adds the other quad.
+__device__ inline float sum8(float v)
+{
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kRowHalfMirror>(v);
+    return v;
+}
+
+// Grid: max_splits * num_reqs * num_kv_heads single-wavefront workgroups, KV head fastest:
+// workgroups go round-robin to the eight XCDs, so with eight KV heads every split of one
+// (row, KV head) runs on the same XCD and reads its shared-prefix blocks from one L2.
+//
+// Each wavefront streams its split's blocks with kDecodeDepth blocks of loads in flight.
+// Per block: scores of 16 tokens x 4 heads (bf16 dot2, FP32 accumulation, reduced over
+// 8 lanes), then the online softmax with one (token, head) pair per lane, then the
+// weights go through LDS to the PV layout, where each lane accumulates 4 heads x 8 dims
+// over its 4 tokens.  The running maximum is raised lazily (only when a score passes it
+// by kRescaleSlack), which keeps exact results and skips most rescales.
+//
+// With one split the wavefront writes the final output.  Otherwise it writes a normalised
+// partial and its log2-sum-exp, and the last split of the (row, KV head) to finish -- found
+// with an agent-scope counter that it then resets -- merges all of them:
+//   L = max_s L_s,  w_s = 2^(L_s - L),  O = sum_s w_s O_s / sum_s w_s,  LSE = L + log2 sum_s w_s.
 __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
 {
-    __shared__ u32x4 k_lds[kBlock * 16];
     __shared__ float p_lds[kBlock * kGroup];
 
     const int lane = threadIdx.x;
@@ -172,14 +202,18 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
     const int nblk = (kvlen + kBlock - 1) / kBlock;
     const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
     const int head0 = kvh * kGroup;
+    const float nan = __builtin_nanf("");
     if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits) {   // lengths disagree with the plan
-        if (split == 0)
-            decode_write_nan(p, 0, q_row, head0, true, lane);
+        if (split == 0) {
+            for (int i = lane; i < kGroup * kHeadDim; i += 64)
+                p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + i] = 0x7FC0;
+            if (lane < kGroup)
+                p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = nan;
+        }
         return;
     }
     if (split >= nsplit)
         return;
-    const int64_t part_index = ((int64_t)r * p.max_splits + split) * p.num_q_heads + head0;
 
     const int b0 = split * p.split_blocks;
     const int nb = min(nblk - b0, p.split_blocks);
@@ -189,28 +223,24 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
         my_blk = p.block_tables[(int64_t)r * p.max_blocks + b0 + lane];
         bad = my_blk < 0 || my_blk >= p.num_blocks;
     }
-    if (__any(bad)) {                                 // a block id outside the pool
-        decode_write_nan(p, part_index, q_row, head0, nsplit == 1, lane);
-        return;
-    }
+    bad = __any(bad);                                 // a block id outside the pool: no reads
 
-    // QK role: lane = 4 * token + quarter; the quarter owns 16-byte chunks quarter + 4k.
-    const int t = lane >> 2, qd = lane & 3;
-    // PV role: lane = 16 * token_group + chunk; tokens token_group + 4i, dims 8*chunk..+8.
-    const int chunk = lane & 15, tg = lane >> 4;
+    const int t8 = lane >> 3, c8 = lane & 7;          // score role
+    const int ts = t8 + 8 * (c8 >> 2), hs = c8 & 3;   // softmax role: token ts, head hs
+    const int c16 = lane & 15, tg = lane >> 4;        // PV role
 
-    u32x4 qv[kGroup][4];
+    u32x4 qv[kGroup][2];
     {
-        const uint16_t* qb = p.q + ((int64_t)q_row * p.num_q_heads + head0) * kHeadDim;
+        const u32x4* qb = reinterpret_cast<const u32x4*>(p.q + ((int64_t)q_row * p.num_q_heads + head0) * kHeadDim);
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                qv[h][k] = *reinterpret_cast<const u32x4*>(qb + h * kHeadDim + (qd + 4 * k) * 8);
+        for (int h = 0; h < kGroup; ++h) {
+            qv[h][0] = qb[h * 16 + c8];
+            qv[h][1] = qb[h * 16 + c8 + 8];
+        }
     }
 
-    float m = -INFINITY;   // running max (base 2) of this lane's head qd, same in all lanes of that head
-    float lsum = 0.f;      // this lane's share of the softmax denominator of head qd
+    float m = -INFINITY;   // running max (base 2) of head hs, equal in every lane of that head
+    float lsum = 0.f;      // this lane's share of head hs's softmax denominator
     float acc[kGroup][8];
 #pragma unroll
     for (int h = 0; h < kGroup; ++h)
@@ -221,47 +251,25 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
     const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
     const int64_t kvh_off = (int64_t)kvh * tile_elems;
     const int64_t blk_stride = (int64_t)p.num_kv_heads * tile_elems;
+    auto issue = [&](KvStage& s, int j) {
+        const int64_t off = (int64_t)__builtin_amdgcn_readlane(my_blk, j) * blk_stride + kvh_off;
+        load_stage(s, p.k_pool + off, p.v_pool + off, lane);
+    };
 
-    u32x4 kr[4], vr[4];
-    {
-        const int blk = __builtin_amdgcn_readlane(my_blk, 0);
-        load_tile(kr, p.k_pool + blk * blk_stride + kvh_off, lane);
-        load_tile(vr, p.v_pool + blk * blk_stride + kvh_off, lane);
-    }
-    for (int j = 0; j < nb; ++j) {
+    auto process = [&](const KvStage& s, int j) {
+        // scores: s[tt][h] for tokens t8 + 8 tt, partial over this lane's 16 dims
+        float sc[2][kGroup];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            k_lds[k_slot(tg + 4 * i, chunk)] = kr[i];
-        u32x4 kn[4], vn[4];
-        if (j + 1 < nb) {
-            const int blk = __builtin_amdgcn_readlane(my_blk, j + 1);
-            load_tile(kn, p.k_pool + blk * blk_stride + kvh_off, lane);
-            load_tile(vn, p.v_pool + blk * blk_stride + kvh_off, lane);
-        }
-        __syncthreads();
-
-        // scores of token t for the four heads, partial over this lane's 32 dims
-        float s[kGroup] = {0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const u32x4 kk = k_lds[k_slot(t, qd + 4 * k)];
-#pragma unroll
-            for (int h = 0; h < kGroup; ++h) {
-                s[h] = dot2_bf16(qv[h][k].x, kk.x, s[h]);
-                s[h] = dot2_bf16(qv[h][k].y, kk.y, s[h]);
-                s[h] = dot2_bf16(qv[h][k].z, kk.z, s[h]);
-                s[h] = dot2_bf16(qv[h][k].w, kk.w, s[h]);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h) {
-            s[h] += dpp<kQuadXor1>(s[h]);
-            s[h] += dpp<kQuadXor2>(s[h]);
-        }
-        // lane (t, qd) now owns the score of token t for head qd
-        float x = (qd == 0 ? s[0] : qd == 1 ? s[1] : qd == 2 ? s[2] : s[3]) * p.scale_log2;
+            for (int h = 0; h < kGroup; ++h)
+                sc[tt][h] = sum8(dot16(qv[h][1], s.k[2 * tt + 1], dot16(qv[h][0], s.k[2 * tt], 0.f)));
+        const int sel = c8 >> 2;
+        float x = sel == 0 ? (hs == 0 ? sc[0][0] : hs == 1 ? sc[0][1] : hs == 2 ? sc[0][2] : sc[0][3])
+                           : (hs == 0 ? sc[1][0] : hs == 1 ? sc[1][1] : hs == 2 ? sc[1][2] : sc[1][3]);
+        x *= p.scale_log2;
         const int pos0 = (b0 + j) * kBlock;
-        if (pos0 + t >= kvlen)
+        if (pos0 + ts >= kvlen)
             x = -INFINITY;
         if (__any(x > m + kRescaleSlack)) {
             float mx = fmaxf(m, x);
@@ -274,7 +282,7 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
             lsum *= alpha;
 #pragma unroll
             for (int h = 0; h < kGroup; ++h) {
-                const float a = readlane_f(alpha, h);   // lane h is (token 0, head h)
+                const float a = readlane_f(alpha, h);   // lane h holds head h (t8 = 0, c8 = h)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     acc[h][e] *= a;
@@ -282,15 +290,14 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
         }
         const float pr = fast_exp2(x - m);
         lsum += pr;
-        p_lds[lane] = pr;                              // [token][head]
+        p_lds[ts * kGroup + hs] = pr;                 // [token][head]
         __syncthreads();
-
-        const int valid = kvlen - pos0;                // tokens of this block that exist
+        const int valid = kvlen - pos0;               // tokens of this block that exist
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tok = tg + 4 * i;
             const f32x4 pp = *reinterpret_cast<const f32x4*>(&p_lds[tok * kGroup]);
-            u32x4 v = vr[i];
+            u32x4 v = s.v[i];
             if (valid < kBlock && tok >= valid)
                 v = u32x4{0u, 0u, 0u, 0u};            // slots past kv_len may hold anything
             const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
@@ -303,15 +310,29 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
                 acc[3][e] = fmaf(pp.w, vf[e], acc[3][e]);
             }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kr[i] = kn[i];
-            vr[i] = vn[i];
-        }
         __syncthreads();
+    };
+
+    if (!bad) {
+        KvStage st[kDecodeDepth + 1];
+#pragma unroll
+        for (int d = 0; d < kDecodeDepth; ++d)
+            if (d < nb)
+                issue(st[d], d);
+        for (int j0 = 0; j0 < nb; j0 += kDecodeDepth + 1) {
+#pragma unroll
+            for (int u = 0; u <= kDecodeDepth; ++u) {
+                const int j = j0 + u;
+                if (j >= nb)
+                    break;
+                if (j + kDecodeDepth < nb)
+                    issue(st[(u + kDecodeDepth) % (kDecodeDepth + 1)], j + kDecodeDepth);
+                process(st[u], j);
+            }
+        }
     }
 
-    // denominators: sum the 16 tokens' shares of each head
+    // denominators: sum the 16 tokens' shares of each head (lanes with equal hs)
     float ltot = lsum;
     ltot += shfl_xor(ltot, 4);
     ltot += shfl_xor(ltot, 8);
@@ -325,77 +346,88 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
             acc[h][e] += shfl_xor(acc[h][e], 16);
             acc[h][e] += shfl_xor(acc[h][e], 32);
         }
+    float inv[kGroup];
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h)
+        inv[h] = bad ? nan : 1.f / readlane_f(ltot, h);
+    const float my_lse2 = bad ? nan : m + fast_log2(ltot);   // lanes 0..3: head = lane
 
     if (nsplit == 1) {
         if (lane < 16) {
 #pragma unroll
             for (int h = 0; h < kGroup; ++h) {
-                const float inv = 1.f / readlane_f(ltot, h);
                 u32x4 o;
-                o.x = pack_bf16(acc[h][0] * inv, acc[h][1] * inv);
-                o.y = pack_bf16(acc[h][2] * inv, acc[h][3] * inv);
-                o.z = pack_bf16(acc[h][4] * inv, acc[h][5] * inv);
-                o.w = pack_bf16(acc[h][6] * inv, acc[h][7] * inv);
-                *reinterpret_cast<u32x4*>(p.out + ((int64_t)q_row * p.num_q_heads + head0 + h) * kHeadDim + chunk * 8) = o;
+                o.x = pack_bf16(acc[h][0] * inv[h], acc[h][1] * inv[h]);
+                o.y = pack_bf16(acc[h][2] * inv[h], acc[h][3] * inv[h]);
+                o.z = pack_bf16(acc[h][4] * inv[h], acc[h][5] * inv[h]);
+                o.w = pack_bf16(acc[h][6] * inv[h], acc[h][7] * inv[h]);
+                *reinterpret_cast<u32x4*>(p.out + ((int64_t)q_row * p.num_q_heads + head0 + h) * kHeadDim + c16 * 8) = o;
             }
         }
         if (lane < kGroup)
-            p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = (m + fast_log2(ltot)) * kLn2;
-    } else {
-        const int64_t pi = part_index;
-        if (lane < 16) {
-#pragma unroll
-            for (int h = 0; h < kGroup; ++h) {
-                const float inv = 1.f / readlane_f(ltot, h);
-                f32x4* dst = reinterpret_cast<f32x4*>(p.part_o + (pi + h) * kHeadDim + chunk * 8);
-                dst[0] = f32x4{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
-                dst[1] = f32x4{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
-            }
-        }
-        if (lane < kGroup)
-            p.part_lse[pi + lane] = m + fast_log2(ltot);   // base 2
+            p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = my_lse2 * kLn2;
+        return;
     }
-}
 
-// ------------------------------------------------------------------------------ merge
+    // Partials are written with agent-scope stores (coherent across the XCDs' separate L2
+    // caches) and the wave waits until they have completed before it counts itself in; the
+    // last split reads them back with agent-scope loads.  This needs no L2 writeback or
+    // invalidation, which a full device fence would do for every split.
+    const int64_t split_stride = p.num_q_heads;                        // partial index step per split
+    const int64_t base = (int64_t)r * p.max_splits * p.num_q_heads + head0;
+    const int64_t mine = base + (int64_t)split * split_stride;
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+            float* dst = p.part_o + (mine + h) * kHeadDim + c16 * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                store_agent(dst + e, acc[h][e] * inv[h]);
+        }
+    }
+    if (lane < kGroup)
+        store_agent(p.part_lse + mine + lane, my_lse2);
+    __builtin_amdgcn_s_waitcnt(0);
 
-// One wavefront per (row, query head); each lane owns two dims.
-// L = max_s L_s;  w_s = 2^(L_s - L);  O = sum_s w_s O_s / sum_s w_s;  LSE = L + log2(sum_s w_s).
-__global__ __launch_bounds__(64) void pa_merge_splits(DecodeParams p)
-{
-    const int lane = threadIdx.x;
-    const int r = blockIdx.x / p.num_q_heads;
-    const int h = blockIdx.x % p.num_q_heads;
-    const int q_row = p.qo_indptr[r];
-    if (p.qo_indptr[r + 1] - q_row != 1)
+    uint32_t* counter = p.counters + (int64_t)r * p.num_kv_heads + kvh;
+    uint32_t done = 0;
+    if (lane == 0)
+        done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __builtin_amdgcn_readfirstlane(done);
+    if (done != (uint32_t)(nsplit - 1))
         return;
-    const int kvlen = p.kv_len[r];
-    const int nblk = (kvlen + kBlock - 1) / kBlock;
-    const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
-    if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits || nsplit <= 1)
-        return;
-    const int64_t base = (int64_t)r * p.max_splits * p.num_q_heads + h;
+    if (lane == 0)
+        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+
+    // merge: lane -> head h = lane / 16, dims 8 * (lane % 16) .. + 8
+    const int h = lane >> 4;
     float L = -INFINITY;
-    bool nan = false;
+    bool any_nan = false;
     for (int s = 0; s < nsplit; ++s) {
-        const float ls = p.part_lse[base + (int64_t)s * p.num_q_heads];
-        nan |= (ls != ls);
+        const float ls = load_agent(p.part_lse + base + s * split_stride + h);
+        any_nan |= (ls != ls);
         L = fmaxf(L, ls);
     }
-    float wsum = 0.f, o0 = 0.f, o1 = 0.f;
+    float wsum = 0.f;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nsplit; ++s) {
-        const int64_t pi = base + (int64_t)s * p.num_q_heads;
-        const float w = fast_exp2(p.part_lse[pi] - L);
-        const float2 v = reinterpret_cast<const float2*>(p.part_o + pi * kHeadDim)[lane];
+        const int64_t pi = base + s * split_stride + h;
+        const float w = fast_exp2(load_agent(p.part_lse + pi) - L);
+        const float* src = p.part_o + pi * kHeadDim + c16 * 8;
         wsum += w;
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            o[e] = fmaf(w, load_agent(src + e), o[e]);
     }
-    const float inv = nan ? __builtin_nanf("") : 1.f / wsum;
-    reinterpret_cast<uint32_t*>(p.out + ((int64_t)q_row * p.num_q_heads + h) * kHeadDim)[lane] =
-        pack_bf16(o0 * inv, o1 * inv);
-    if (lane == 0)
-        p.lse[(int64_t)q_row * p.num_q_heads + h] = nan ? __builtin_nanf("") : (L + fast_log2(wsum)) * kLn2;
+    const float winv = any_nan ? nan : 1.f / wsum;
+    u32x4 ov;
+    ov.x = pack_bf16(o[0] * winv, o[1] * winv);
+    ov.y = pack_bf16(o[2] * winv, o[3] * winv);
+    ov.z = pack_bf16(o[4] * winv, o[5] * winv);
+    ov.w = pack_bf16(o[6] * winv, o[7] * winv);
+    *reinterpret_cast<u32x4*>(p.out + ((int64_t)q_row * p.num_q_heads + head0 + h) * kHeadDim + c16 * 8) = ov;
+    if (c16 == 0)
+        p.lse[(int64_t)q_row * p.num_q_heads + head0 + h] = any_nan ? nan : (L + fast_log2(wsum)) * kLn2;
 }
 
 // ------------------------------------------------------------------------------ prefill
@@ -488,50 +520,59 @@ __global__ __launch_bounds__(256) void pa_prefill_tile(PrefillParams p)
 
     // Staging assignments.  K: chunk id = tid + 256 i -> key (tid>>4) + 16 i, 16-byte chunk tid&15.
     // V: key quad kq = tid&15 (keys 4kq..4kq+3), chunk c16 = tid>>4; transposed on the way into LDS.
+    // Step s covers logical blocks 4s .. 4s+3 of the row; their ids are read two steps ahead
+    // and the K / V data one to two steps ahead, so neither waits on the other.
     const int k_key = tid >> 4, k_chunk = tid & 15;
     const int v_kq = tid & 15, v_chunk = tid >> 4;
-    u32x4 kst[4], vst[4];
-    auto load_step = [&](int step) {
+    struct Stage {
+        u32x4 k[4];
+        u32x4 v[4];
+    };
+    auto load_ids = [&](int step, int (&ids)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = 4 * step + i;
+            ids[i] = (b * kBlock < kv_hi) ? bt[b] : 0;
+        }
+    };
+    auto load_step = [&](Stage& stg, int step, const int (&ids)[4]) {
         const int key0 = step * kKeyTile;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = key0 + k_key + 16 * i;
-            kst[i] = u32x4{0u, 0u, 0u, 0u};
+            const int blk = ids[i];
+            stg.k[i] = u32x4{0u, 0u, 0u, 0u};
             if (key < kv_hi) {
-                const int blk = bt[key / kBlock];
                 if (blk >= 0 && blk < p.num_blocks)
-                    kst[i] = *reinterpret_cast<const u32x4*>(p.k_pool + blk * blk_stride + kvh_off +
-                                                             (key % kBlock) * kHeadDim + k_chunk * 8);
+                    stg.k[i] = *reinterpret_cast<const u32x4*>(p.k_pool + blk * blk_stride + kvh_off +
+                                                               k_key * kHeadDim + k_chunk * 8);
                 else
                     bad = true;
             }
         }
         const int vkey0 = key0 + 4 * v_kq;
-        int vblk = -1;
-        if (vkey0 < kv_hi) {
-            vblk = bt[vkey0 / kBlock];
-            if (vblk < 0 || vblk >= p.num_blocks) {
-                bad = true;
-                vblk = -1;
-            }
-        }
+        const int q4 = v_kq >> 2;
+        const int vblk = q4 == 0 ? ids[0] : q4 == 1 ? ids[1] : q4 == 2 ? ids[2] : ids[3];
+        const bool vok = vblk >= 0 && vblk < p.num_blocks;
+        if (vkey0 < kv_hi && !vok)
+            bad = true;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            vst[i] = u32x4{0u, 0u, 0u, 0u};
-            if (vblk >= 0 && vkey0 + i < kv_hi)
-                vst[i] = *reinterpret_cast<const u32x4*>(p.v_pool + vblk * blk_stride + kvh_off +
-                                                         ((vkey0 + i) % kBlock) * kHeadDim + v_chunk * 8);
+            stg.v[i] = u32x4{0u, 0u, 0u, 0u};
+            if (vok && vkey0 + i < kv_hi)
+                stg.v[i] = *reinterpret_cast<const u32x4*>(p.v_pool + vblk * blk_stride + kvh_off +
+                                                           ((vkey0 + i) % kBlock) * kHeadDim + v_chunk * 8);
         }
     };
-    auto store_step = [&]() {
+    auto store_step = [&](const Stage& stg) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(&k_lds[(k_key + 16 * i) * kKStride + k_chunk * 8]) = kst[i];
+            *reinterpret_cast<u32x4*>(&k_lds[(k_key + 16 * i) * kKStride + k_chunk * 8]) = stg.k[i];
         // V^T row d holds keys in order; keys 4kq..4kq+3 of dims 8*c16 .. 8*c16+7
-        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vst[0]);
-        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vst[1]);
-        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vst[2]);
-        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vst[3]);
+        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&stg.v[0]);
+        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&stg.v[1]);
+        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&stg.v[2]);
+        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&stg.v[3]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             // dims 2w (low halves) and 2w+1 (high halves)
@@ -548,77 +589,94 @@ __global__ __launch_bounds__(256) void pa_prefill_tile(PrefillParams p)
         oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
 
-    if (nsteps > 0)
-        load_step(0);
-    for (int step = 0; step < nsteps; ++step) {
-        __syncthreads();
-        store_step();
-        __syncthreads();
-        if (step + 1 < nsteps)
-            load_step(step + 1);
+    Stage stg[2];
+    int idb[2][4];
+    {
+        int ids0[4], ids1[4];
+        load_ids(0, ids0);
+        load_ids(1, ids1);
+        if (nsteps > 0)
+            load_step(stg[0], 0, ids0);
+        if (nsteps > 1)
+            load_step(stg[1], 1, ids1);
+        load_ids(2, idb[0]);
+    }
+    for (int s0 = 0; s0 < nsteps; s0 += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int step = s0 + u;
+            if (step >= nsteps)
+                break;
+            __syncthreads();
+            store_step(stg[u]);
+            __syncthreads();
+            if (step + 2 < nsteps)
+                load_step(stg[u], step + 2, idb[u]);
+            load_ids(step + 3, idb[u ^ 1]);
 
-        // S^T for the four 16-key blocks of this step
-        f32x4 sacc[4];
+            // S^T for the four 16-key blocks of this step
+            f32x4 sacc[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < 4; ++kb) {
+                sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(&k_lds[(kb * 16 + row) * kKStride + ks * 32 + kslice * 8]));
-                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], sacc[kb], 0, 0, 0);
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4*>(&k_lds[(kb * 16 + row) * kKStride + ks * 32 + kslice * 8]));
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], sacc[kb], 0, 0, 0);
+                }
             }
-        }
-        // lane holds S^T[key = key0 + 16 kb + 4 kslice + e][row]
-        const int key0 = step * kKeyTile;
-        float x[4][4];
-        float tmax = -INFINITY;
+            // lane holds S^T[key = key0 + 16 kb + 4 kslice + e][row]
+            const int key0 = step * kKeyTile;
+            float x[4][4];
+            float tmax = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = key0 + 16 * kb + 4 * kslice + e;
-                float v = sacc[kb][e] * p.scale_log2;
-                if (key > qpos || key >= kv_hi)
-                    v = -INFINITY;
-                x[kb][e] = v;
-                tmax = fmaxf(tmax, v);
+                for (int e = 0; e < 4; ++e) {
+                    const int key = key0 + 16 * kb + 4 * kslice + e;
+                    float v = sacc[kb][e] * p.scale_log2;
+                    if (key > qpos || key >= kv_hi)
+                        v = -INFINITY;
+                    x[kb][e] = v;
+                    tmax = fmaxf(tmax, v);
+                }
+            tmax = fmaxf(tmax, shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, shfl_xor(tmax, 32));
+            const float mnew = fmaxf(m, tmax);
+            const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+            m = mnew;
+            float psum = 0.f;
+            uint32_t pk[4][2];   // P^T operand halves, bf16 pairs
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float pe[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pe[e] = (mnew == -INFINITY) ? 0.f : fast_exp2(x[kb][e] - mnew);
+                    psum += pe[e];
+                }
+                pk[kb][0] = pack_bf16(pe[0], pe[1]);
+                pk[kb][1] = pack_bf16(pe[2], pe[3]);
             }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m, tmax);
-        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-        m = mnew;
-        float psum = 0.f;
-        uint32_t pk[4][2];   // P^T operand halves, bf16 pairs
+            lsum = lsum * alpha + psum;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            float pe[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pe[e] = (mnew == -INFINITY) ? 0.f : fast_exp2(x[kb][e] - mnew);
-                psum += pe[e];
-            }
-            pk[kb][0] = pack_bf16(pe[0], pe[1]);
-            pk[kb][1] = pack_bf16(pe[2], pe[3]);
-        }
-        lsum = lsum * alpha + psum;
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-            oacc[db] *= alpha;
+            for (int db = 0; db < 8; ++db)
+                oacc[db] *= alpha;
 
-        // O^T += V^T P^T over two 32-key slices
+            // O^T += V^T P^T over two 32-key slices
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-            const bf16x8 b = __builtin_bit_cast(
-                bf16x8, u32x4{pk[2 * ks2][0], pk[2 * ks2][1], pk[2 * ks2 + 1][0], pk[2 * ks2 + 1][1]});
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                const bf16x8 b = __builtin_bit_cast(
+                    bf16x8, u32x4{pk[2 * ks2][0], pk[2 * ks2][1], pk[2 * ks2 + 1][0], pk[2 * ks2 + 1][1]});
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const uint16_t* vrow = &vt_lds[(db * 16 + row) * kVtStride + 32 * ks2 + 4 * kslice];
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[db], 0, 0, 0);
+                for (int db = 0; db < 8; ++db) {
+                    const uint16_t* vrow = &vt_lds[(db * 16 + row) * kVtStride + 32 * ks2 + 4 * kslice];
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[db], 0, 0, 0);
+                }
             }
         }
     }
@@ -689,6 +747,8 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
     const pa::WorkspaceLayout ws = pa::workspace_layout(plan->num_reqs, plan->max_splits, g->num_q_heads);
     if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))
         return PA_ERR_WORKSPACE;
+    if (ws.total > 0 && (int64_t)plan->num_reqs * g->num_kv_heads > pa::kMaxCounters)
+        return PA_ERR_UNSUPPORTED;
     hipStream_t st = as_stream(stream);
     const float scale_log2 = g->scale * kLog2e;
 
@@ -727,6 +787,7 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         dp.kv_len = kv_len;
         dp.out = static_cast<uint16_t*>(out);
         dp.lse = lse;
+        dp.counters = ws.total ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ws.counters) : nullptr;
         dp.part_o = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_o) : nullptr;
         dp.part_lse = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_lse) : nullptr;
         dp.max_blocks = max_blocks_per_req;
@@ -743,12 +804,6 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         hipLaunchKernelGGL(pa_decode_split, dim3((uint32_t)grid), dim3(64), 0, st, dp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
-        if (plan->max_splits > 1) {
-            hipLaunchKernelGGL(pa_merge_splits, dim3((uint32_t)((int64_t)plan->num_reqs * g->num_q_heads)), dim3(64), 0,
-                               st, dp);
-            if (hipGetLastError() != hipSuccess)
-                return PA_ERR_HIP;
-        }
     }
     return PA_OK;
 }
