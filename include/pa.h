@@ -103,9 +103,9 @@ typedef struct pa_plan_t {
     int32_t total_q;                     /* sum of qo_len                                     */
     int32_t num_decode_rows;             /* rows with qo_len == 1                             */
     int32_t num_prefill_rows;            /* rows with qo_len > 1                              */
-    int32_t split_blocks;                /* KV blocks per decode split                        */
+    int32_t split_blocks;                /* KV blocks per decode split (one workgroup each)   */
     int32_t max_splits;                  /* largest split count of any decode row             */
-    int32_t decode_items;                /* (row, KV head, split) work items                  */
+    int32_t decode_items;                /* (row, KV head, split) decode workgroups           */
     int32_t prefill_tiles;               /* query tiles over all prefill rows                 */
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];       /* request index of each prefill row      */
     int32_t prefill_tile_start[PA_MAX_PREFILL_ROWS + 1]; /* prefix sums of tiles per row      */
@@ -115,11 +115,11 @@ typedef struct pa_plan_t {
 /*
  * Build the plan.  qo_len_host / kv_len_host: host int32 [num_reqs].  num_cus: the
  * device's compute-unit count (256 on MI355X; see pa_query_num_cus).
- * split_blocks: 0 picks the split length automatically so that the decode work
- * items fill the CUs several times over (the pages motivate splitting attention
- * over kv_len as well as over requests when a batch has few tokens: Perplexity
- * blog, section on prefill vs decode); > 0 forces that many blocks per split
- * (clamped to 1 .. 64).  Errors: PA_ERR_NULL, PA_ERR_SHAPE (qo_len < 1 or
+ * split_blocks: 0 picks the split length automatically: a decode row is split
+ * over kv_len only when its (row, KV head) pairs alone would leave CUs idle (the
+ * pages motivate splitting attention over kv_len as well as over requests when a
+ * batch has few tokens: Perplexity blog, section on prefill vs decode); > 0
+ * forces that many blocks per split (clamped to 1 .. 512).  Errors: PA_ERR_NULL, PA_ERR_SHAPE (qo_len < 1 or
  * kv_len < qo_len), PA_ERR_UNSUPPORTED (geometry, more than PA_MAX_PREFILL_ROWS
  * prefill rows, or split decode rows with num_reqs * num_kv_heads > 16384).
  */

@@ -9,12 +9,14 @@
 
 namespace {
 
-// Decode work items per CU the automatic split aims for.  Each item is one
-// wavefront; several per CU keep enough KV loads in flight to cover HBM latency.
-constexpr int kItemsPerCu = 8;
-// Shortest automatic split: a split also costs one partial write and one merge read
-// of Hq * (head_dim + 1) floats, so very short splits waste bandwidth.
-constexpr int kMinAutoSplitBlocks = 4;
+// Decode workgroups (of pa::kDecodeWaves wavefronts each) per CU the automatic split aims
+// for: one workgroup fills a CU with two wavefronts per SIMD.
+constexpr int kWorkgroupsPerCu = 1;
+// Shortest automatic split: each split also costs a partial write and a merge read of
+// Hq * (head_dim + 1) floats, so very short splits waste bandwidth.
+constexpr int kMinAutoSplitBlocks = 8;
+// Fixed cost of one decode workgroup (start-up latency, merge), in block-times.
+constexpr int kWorkgroupOverheadBlocks = 4;
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
@@ -64,11 +66,30 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
     if (split_blocks > 0) {
         sb = std::min(split_blocks, pa::kMaxSplitBlocks);
     } else {
-        int64_t target = (int64_t)std::max(num_cus, 1) * kItemsPerCu;
-        int64_t work = decode_blocks * g->num_kv_heads;
-        int64_t want = std::max<int64_t>(1, (work + target - 1) / target);
-        sb = (int32_t)std::min<int64_t>(std::max<int64_t>(want, kMinAutoSplitBlocks), pa::kMaxSplitBlocks);
-        sb = std::min(sb, std::max(max_decode_blocks, 1));
+        // Candidate split lengths divide the longest row evenly; each is scored by the
+        // estimated makespan in block-times: rounds of resident workgroups (one per CU)
+        // times the blocks one workgroup streams plus its fixed cost.  Ties go to the
+        // longer split, which needs fewer partials.
+        const int64_t target = (int64_t)std::max(num_cus, 1) * kWorkgroupsPerCu;
+        const int32_t longest = std::max(max_decode_blocks, 1);
+        int64_t best_cost = INT64_MAX;
+        sb = std::min(longest, pa::kMaxSplitBlocks);
+        for (int32_t parts = 1; parts <= 256; ++parts) {
+            const int32_t cand = ceil_div(longest, parts);
+            if (cand > pa::kMaxSplitBlocks)
+                continue;
+            if (cand < kMinAutoSplitBlocks && parts > 1)
+                break;
+            int64_t wgs = 0;
+            for (int32_t r = 0; r < num_reqs; ++r)
+                if (qo_len[r] == 1)
+                    wgs += (int64_t)ceil_div(ceil_div(kv_len[r], pa::kBlock), cand) * g->num_kv_heads;
+            const int64_t cost = (wgs + target - 1) / target * (cand + kWorkgroupOverheadBlocks);
+            if (cost < best_cost) {
+                best_cost = cost;
+                sb = cand;
+            }
+        }
     }
     plan->split_blocks = sb;
     int64_t items = 0;

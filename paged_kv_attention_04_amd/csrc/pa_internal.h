@@ -11,7 +11,8 @@ namespace pa {
 constexpr int kHeadDim = 128;   // head dimension the kernels are built for
 constexpr int kBlock = 16;      // tokens per KV block
 constexpr int kGroup = 4;       // query heads per KV head (grouped-query attention)
-constexpr int kMaxSplitBlocks = 64;   // one block id per lane of a wavefront
+constexpr int kDecodeWaves = 8;       // wavefronts per decode workgroup
+constexpr int kMaxSplitBlocks = 64 * kDecodeWaves;   // one block id per lane of each wavefront
 constexpr int kPrefillQ = 16;   // new tokens per prefill tile (x kGroup heads = 64 MFMA rows)
 
 inline bool geometry_supported(const pa_geometry* g)

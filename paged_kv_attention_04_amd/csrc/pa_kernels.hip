@@ -125,10 +125,11 @@ struct DecodeParams {
 };
 
 #ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 3
+#define PA_DECODE_DEPTH 1
 #endif
 // KV blocks whose loads are in flight while a block is being processed.
 constexpr int kDecodeDepth = PA_DECODE_DEPTH;
+constexpr int kDecodeWaves = pa::kDecodeWaves;
 
 // One (block, KV head) tile is 16 tokens x 256 bytes, read by four 16-byte loads per lane.
 // K: lane = 8 * t8 + c8 reads tokens t8 and t8 + 8, 16-byte chunks c8 and c8 + 8; each load
@@ -161,36 +162,69 @@ __device__ inline float dot16(const u32x4& q, const u32x4& k, float acc)
     return dot2_bf16(q.w, k.w, acc);
 }
 
-// Sum over the eight lanes of a half-row (lanes 8a .. 8a+7): two quad butterflies, then
-// the half-row mirror (lane i <-> 7 - i) adds the other quad.
-__device__ inline float sum8(float v)
+// Reduce-scatter over the eight lanes of a half-row: lane c (0..7) holds eight partial
+// sums v[0..7] and returns the full sum of v[c] over the eight lanes.  Three halving
+// steps pair lanes that differ in one bit of c: the half-row mirror (c <-> 7 - c, bit 2),
+// then quad xor 2 (bit 1), then quad xor 1 (bit 0); at each step a lane keeps the half of
+// its values that its bit selects and adds the partner's copy of that half.
+__device__ inline float reduce_scatter8(const float (&v)[8], int c)
 {
-    v += dpp<kQuadXor1>(v);
-    v += dpp<kQuadXor2>(v);
-    v += dpp<kRowHalfMirror>(v);
-    return v;
+    const bool b2 = c & 4, b1 = c & 2, b0 = c & 1;
+    float k4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float keep = b2 ? v[4 + i] : v[i];
+        const float send = b2 ? v[i] : v[4 + i];
+        k4[i] = keep + dpp<kRowHalfMirror>(send);
+    }
+    float k2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = b1 ? k4[2 + i] : k4[i];
+        const float send = b1 ? k4[i] : k4[2 + i];
+        k2[i] = keep + dpp<kQuadXor2>(send);
+    }
+    const float keep = b0 ? k2[1] : k2[0];
+    const float send = b0 ? k2[0] : k2[1];
+    return keep + dpp<kQuadXor1>(send);
 }
 
-// Grid: max_splits * num_reqs * num_kv_heads single-wavefront workgroups, KV head fastest:
-// workgroups go round-robin to the eight XCDs, so with eight KV heads every split of one
-// (row, KV head) runs on the same XCD and reads its shared-prefix blocks from one L2.
-//
-// Each wavefront streams its split's blocks with kDecodeDepth blocks of loads in flight.
-// Per block: scores of 16 tokens x 4 heads (bf16 dot2, FP32 accumulation, reduced over
-// 8 lanes), then the online softmax with one (token, head) pair per lane, then the
-// weights go through LDS to the PV layout, where each lane accumulates 4 heads x 8 dims
-// over its 4 tokens.  The running maximum is raised lazily (only when a score passes it
-// by kRescaleSlack), which keeps exact results and skips most rescales.
-//
-// With one split the wavefront writes the final output.  Otherwise it writes a normalised
-// partial and its log2-sum-exp, and the last split of the (row, KV head) to finish -- found
-// with an agent-scope counter that it then resets -- merges all of them:
-//   L = max_s L_s,  w_s = 2^(L_s - L),  O = sum_s w_s O_s / sum_s w_s,  LSE = L + log2 sum_s w_s.
-__global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
+// Orders this wavefront's LDS accesses around a cross-lane exchange.  LDS executes one
+// wavefront's instructions in order, so only the compiler has to be kept from moving them.
+__device__ inline void wave_lds_sync()
 {
-    __shared__ float p_lds[kBlock * kGroup];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    const int lane = threadIdx.x;
+// Grid: max_splits * num_reqs * num_kv_heads workgroups of kDecodeWaves wavefronts, KV
+// head fastest: workgroups go round-robin to the eight XCDs, so with eight KV heads each
+// XCD serves one KV head of every row and reads that head's shared-prefix blocks from
+// one L2.
+//
+// A workgroup owns one (row, KV head, split); its blocks are cut into kDecodeWaves
+// contiguous runs, one per wavefront.  Each wavefront streams its run with kDecodeDepth
+// blocks of loads in flight.  Per block: scores of 16 tokens x 4 heads (bf16 dot2, FP32
+// accumulation, reduced over 8 lanes), the online softmax with one (token, head) pair per
+// lane, and PV, where each lane accumulates 4 heads x 8 dims over its 4 tokens after the
+// weights pass through LDS.  The running maximum is raised lazily (only when a score
+// passes it by kRescaleSlack), which keeps exact results and skips most rescales.
+//
+// The wavefronts' results are merged through LDS with the log-sum-exp rule
+//   L = max_w L_w,  c_w = 2^(L_w - L),  O = sum_w c_w O_w / sum_w c_w,  LSE = L + log2 sum_w c_w.
+// With one split per row the workgroup writes the final output.  Otherwise it writes a
+// partial, and the last split of the (row, KV head) to finish -- found with an agent-scope
+// counter that it then resets -- merges the partials by the same rule.
+__global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParams p)
+{
+    __shared__ float p_lds[kDecodeWaves][kBlock * kGroup];
+    __shared__ float o_lds[kDecodeWaves][kGroup * kHeadDim];
+    __shared__ float l_lds[kDecodeWaves][kGroup];
+    __shared__ uint32_t last_lds;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int kvh = blockIdx.x % p.num_kv_heads;
     const int rest = blockIdx.x / p.num_kv_heads;
     const int r = rest % p.num_reqs;
@@ -203,27 +237,32 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
     const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
     const int head0 = kvh * kGroup;
     const float nan = __builtin_nanf("");
-    if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits) {   // lengths disagree with the plan
-        if (split == 0) {
-            for (int i = lane; i < kGroup * kHeadDim; i += 64)
+    if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits ||
+        p.split_blocks > pa::kMaxSplitBlocks) {       // lengths disagree with the plan
+        if (split == 0)
+            for (int i = tid; i < kGroup * kHeadDim; i += 64 * kDecodeWaves) {
                 p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + i] = 0x7FC0;
-            if (lane < kGroup)
-                p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = nan;
-        }
+                if (i < kGroup)
+                    p.lse[(int64_t)q_row * p.num_q_heads + head0 + i] = nan;
+            }
         return;
     }
     if (split >= nsplit)
         return;
 
-    const int b0 = split * p.split_blocks;
-    const int nb = min(nblk - b0, p.split_blocks);
+    // this wavefront's run of blocks
+    const int g0 = split * p.split_blocks;
+    const int gnb = min(nblk - g0, p.split_blocks);
+    const int per = (gnb + kDecodeWaves - 1) / kDecodeWaves;          // <= 64
+    const int b0 = g0 + wave * per;
+    const int nb = max(0, min(per, g0 + gnb - b0));
     int my_blk = 0;
     bool bad = false;
     if (lane < nb) {
         my_blk = p.block_tables[(int64_t)r * p.max_blocks + b0 + lane];
         bad = my_blk < 0 || my_blk >= p.num_blocks;
     }
-    bad = __any(bad);                                 // a block id outside the pool: no reads
+    bad = __syncthreads_or(bad);                      // a block id outside the pool: no reads
 
     const int t8 = lane >> 3, c8 = lane & 7;          // score role
     const int ts = t8 + 8 * (c8 >> 2), hs = c8 & 3;   // softmax role: token ts, head hs
@@ -251,22 +290,23 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
     const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
     const int64_t kvh_off = (int64_t)kvh * tile_elems;
     const int64_t blk_stride = (int64_t)p.num_kv_heads * tile_elems;
-    auto issue = [&](KvStage& s, int j) {
+    float* pw = p_lds[wave];
+    auto issue = [&](KvStage& st, int j) {
         const int64_t off = (int64_t)__builtin_amdgcn_readlane(my_blk, j) * blk_stride + kvh_off;
-        load_stage(s, p.k_pool + off, p.v_pool + off, lane);
+        load_stage(st, p.k_pool + off, p.v_pool + off, lane);
     };
 
-    auto process = [&](const KvStage& s, int j) {
-        // scores: s[tt][h] for tokens t8 + 8 tt, partial over this lane's 16 dims
-        float sc[2][kGroup];
+    auto process = [&](const KvStage& st, int j) {
+        // scores of tokens t8 + 8 tt for the four heads, partial over this lane's 16 dims,
+        // index 4 tt + h; the reduce-scatter leaves lane c8 with the full score of token
+        // ts = t8 + 8 (c8 / 4), head hs = c8 % 4
+        float sc[2 * kGroup];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int h = 0; h < kGroup; ++h)
-                sc[tt][h] = sum8(dot16(qv[h][1], s.k[2 * tt + 1], dot16(qv[h][0], s.k[2 * tt], 0.f)));
-        const int sel = c8 >> 2;
-        float x = sel == 0 ? (hs == 0 ? sc[0][0] : hs == 1 ? sc[0][1] : hs == 2 ? sc[0][2] : sc[0][3])
-                           : (hs == 0 ? sc[1][0] : hs == 1 ? sc[1][1] : hs == 2 ? sc[1][2] : sc[1][3]);
+                sc[tt * kGroup + h] = dot16(qv[h][1], st.k[2 * tt + 1], dot16(qv[h][0], st.k[2 * tt], 0.f));
+        float x = reduce_scatter8(sc, c8);
         x *= p.scale_log2;
         const int pos0 = (b0 + j) * kBlock;
         if (pos0 + ts >= kvlen)
@@ -288,57 +328,82 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
                     acc[h][e] *= a;
             }
         }
+        // The softmax statistics stay FP32; the weights enter PV as bf16, as in the MFMA
+        // prefill path (relative error <= 2^-9 per weight in the numerator only).
         const float pr = fast_exp2(x - m);
         lsum += pr;
-        p_lds[ts * kGroup + hs] = pr;                 // [token][head]
-        __syncthreads();
+        pw[ts * kGroup + hs] = pr;                    // [token][head]
+        wave_lds_sync();
+        // PV on bf16 dot2: tokens are taken in pairs (tg, tg + 4) and (tg + 8, tg + 12);
+        // a pair's V values for one dim and the pair's weights for one head are packed
+        // into bf16x2 operands.
+        u32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = st.v[i];
         const int valid = kvlen - pos0;               // tokens of this block that exist
+        if (valid < kBlock) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tok = tg + 4 * i;
-            const f32x4 pp = *reinterpret_cast<const f32x4*>(&p_lds[tok * kGroup]);
-            u32x4 v = s.v[i];
-            if (valid < kBlock && tok >= valid)
-                v = u32x4{0u, 0u, 0u, 0u};            // slots past kv_len may hold anything
-            const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                                 bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+            for (int i = 0; i < 4; ++i)
+                if (tg + 4 * i >= valid)
+                    v[i] = u32x4{0u, 0u, 0u, 0u};     // slots past kv_len may hold anything
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                acc[0][e] = fmaf(pp.x, vf[e], acc[0][e]);
-                acc[1][e] = fmaf(pp.y, vf[e], acc[1][e]);
-                acc[2][e] = fmaf(pp.z, vf[e], acc[2][e]);
-                acc[3][e] = fmaf(pp.w, vf[e], acc[3][e]);
+        for (int pair = 0; pair < 2; ++pair) {
+            const f32x4 pa = *reinterpret_cast<const f32x4*>(&pw[(tg + 8 * pair) * kGroup]);
+            const f32x4 pb = *reinterpret_cast<const f32x4*>(&pw[(tg + 8 * pair + 4) * kGroup]);
+            const uint32_t pk[kGroup] = {pack_bf16(pa.x, pb.x), pack_bf16(pa.y, pb.y), pack_bf16(pa.z, pb.z),
+                                         pack_bf16(pa.w, pb.w)};
+            const u32x4& va = v[2 * pair];
+            const u32x4& vb = v[2 * pair + 1];
+            const uint32_t wa[4] = {va.x, va.y, va.z, va.w};
+            const uint32_t wb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t lo = __builtin_amdgcn_perm(wb[w], wa[w], 0x05040100u);   // dim 2w of both tokens
+                const uint32_t hi = __builtin_amdgcn_perm(wb[w], wa[w], 0x07060302u);   // dim 2w + 1
+#pragma unroll
+                for (int h = 0; h < kGroup; ++h) {
+                    acc[h][2 * w] = dot2_bf16(pk[h], lo, acc[h][2 * w]);
+                    acc[h][2 * w + 1] = dot2_bf16(pk[h], hi, acc[h][2 * w + 1]);
+                }
             }
         }
-        __syncthreads();
+        wave_lds_sync();
     };
 
-    if (!bad) {
+    if (!bad && nb > 0) {
+        // Loads for block j + kDecodeDepth are issued before block j is processed.  Past the
+        // end of the run the last block is fetched again (an L2 hit), so every iteration
+        // issues the same loads, and the stages that are in flight at the top of the
+        // steady-state loop are the same on entry and on every trip: the compiler can then
+        // wait for exactly the oldest stage.
         KvStage st[kDecodeDepth + 1];
 #pragma unroll
         for (int d = 0; d < kDecodeDepth; ++d)
-            if (d < nb)
-                issue(st[d], d);
-        for (int j0 = 0; j0 < nb; j0 += kDecodeDepth + 1) {
+            issue(st[d], min(d, nb - 1));
+        int j0 = 0;
+        for (; j0 + kDecodeDepth + 1 <= nb; j0 += kDecodeDepth + 1) {
 #pragma unroll
             for (int u = 0; u <= kDecodeDepth; ++u) {
-                const int j = j0 + u;
-                if (j >= nb)
-                    break;
-                if (j + kDecodeDepth < nb)
-                    issue(st[(u + kDecodeDepth) % (kDecodeDepth + 1)], j + kDecodeDepth);
-                process(st[u], j);
+                issue(st[(u + kDecodeDepth) % (kDecodeDepth + 1)], min(j0 + u + kDecodeDepth, nb - 1));
+                process(st[u], j0 + u);
             }
         }
+        // the last nb - j0 < kDecodeDepth + 1 blocks are already in flight
+#pragma unroll
+        for (int u = 0; u < kDecodeDepth; ++u)
+            if (j0 + u < nb)
+                process(st[u], j0 + u);
     }
 
-    // denominators: sum the 16 tokens' shares of each head (lanes with equal hs)
+    // this wavefront's totals: denominators over its 16 token slots, numerators over its
+    // four token groups
     float ltot = lsum;
     ltot += shfl_xor(ltot, 4);
     ltot += shfl_xor(ltot, 8);
     ltot += shfl_xor(ltot, 16);
     ltot += shfl_xor(ltot, 32);
-    // numerators: sum the four token groups
 #pragma unroll
     for (int h = 0; h < kGroup; ++h)
 #pragma unroll
@@ -346,88 +411,105 @@ __global__ __launch_bounds__(64) void pa_decode_split(DecodeParams p)
             acc[h][e] += shfl_xor(acc[h][e], 16);
             acc[h][e] += shfl_xor(acc[h][e], 32);
         }
-    float inv[kGroup];
+    const bool empty = nb == 0 || bad;
+    if (lane < 16) {
 #pragma unroll
-    for (int h = 0; h < kGroup; ++h)
-        inv[h] = bad ? nan : 1.f / readlane_f(ltot, h);
-    const float my_lse2 = bad ? nan : m + fast_log2(ltot);   // lanes 0..3: head = lane
-
-    if (nsplit == 1) {
-        if (lane < 16) {
-#pragma unroll
-            for (int h = 0; h < kGroup; ++h) {
-                u32x4 o;
-                o.x = pack_bf16(acc[h][0] * inv[h], acc[h][1] * inv[h]);
-                o.y = pack_bf16(acc[h][2] * inv[h], acc[h][3] * inv[h]);
-                o.z = pack_bf16(acc[h][4] * inv[h], acc[h][5] * inv[h]);
-                o.w = pack_bf16(acc[h][6] * inv[h], acc[h][7] * inv[h]);
-                *reinterpret_cast<u32x4*>(p.out + ((int64_t)q_row * p.num_q_heads + head0 + h) * kHeadDim + c16 * 8) = o;
-            }
+        for (int h = 0; h < kGroup; ++h) {
+            const float inv = empty ? 0.f : 1.f / readlane_f(ltot, h);
+            f32x4* dst = reinterpret_cast<f32x4*>(&o_lds[wave][h * kHeadDim + c16 * 8]);
+            dst[0] = f32x4{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
+            dst[1] = f32x4{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
         }
-        if (lane < kGroup)
-            p.lse[(int64_t)q_row * p.num_q_heads + head0 + lane] = my_lse2 * kLn2;
+    }
+    if (lane < kGroup)
+        l_lds[wave][lane] = empty ? -INFINITY : m + fast_log2(ltot);   // lane = head (t8 = 0, c8 = head)
+    __syncthreads();
+
+    // merge the wavefronts: thread -> (head h, dim d); 512 outputs, kDecodeWaves * 64 threads
+    float res[kGroup * kHeadDim / (64 * kDecodeWaves)];
+    float res_lse[kGroup * kHeadDim / (64 * kDecodeWaves)];
+    constexpr int kPerThread = kGroup * kHeadDim / (64 * kDecodeWaves);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int idx = tid + k * 64 * kDecodeWaves;
+        const int h = idx / kHeadDim;
+        float L = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kDecodeWaves; ++w)
+            L = fmaxf(L, l_lds[w][h]);
+        float wsum = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecodeWaves; ++w) {
+            const float c = (l_lds[w][h] == -INFINITY) ? 0.f : fast_exp2(l_lds[w][h] - L);
+            wsum += c;
+            o = fmaf(c, o_lds[w][idx], o);
+        }
+        res[k] = bad ? nan : o / wsum;
+        res_lse[k] = bad ? nan : L + fast_log2(wsum);
+    }
+
+    const int64_t out_base = ((int64_t)q_row * p.num_q_heads + head0) * kHeadDim;
+    if (nsplit == 1) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int idx = tid + k * 64 * kDecodeWaves;
+            p.out[out_base + idx] = __builtin_bit_cast(uint16_t, (__bf16)res[k]);
+            if ((idx & (kHeadDim - 1)) == 0)
+                p.lse[(int64_t)q_row * p.num_q_heads + head0 + idx / kHeadDim] = res_lse[k] * kLn2;
+        }
         return;
     }
 
     // Partials are written with agent-scope stores (coherent across the XCDs' separate L2
-    // caches) and the wave waits until they have completed before it counts itself in; the
-    // last split reads them back with agent-scope loads.  This needs no L2 writeback or
-    // invalidation, which a full device fence would do for every split.
+    // caches) and every thread waits until its stores have completed before the
+    // workgroup counts itself in; the last split reads them with agent-scope loads.  This
+    // needs no L2 writeback or invalidation, which a device fence would do for every split.
     const int64_t split_stride = p.num_q_heads;                        // partial index step per split
     const int64_t base = (int64_t)r * p.max_splits * p.num_q_heads + head0;
     const int64_t mine = base + (int64_t)split * split_stride;
-    if (lane < 16) {
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h) {
-            float* dst = p.part_o + (mine + h) * kHeadDim + c16 * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                store_agent(dst + e, acc[h][e] * inv[h]);
-        }
+    for (int k = 0; k < kPerThread; ++k) {
+        const int idx = tid + k * 64 * kDecodeWaves;
+        store_agent(p.part_o + mine * kHeadDim + idx, res[k]);
+        if ((idx & (kHeadDim - 1)) == 0)
+            store_agent(p.part_lse + mine + idx / kHeadDim, res_lse[k]);
     }
-    if (lane < kGroup)
-        store_agent(p.part_lse + mine + lane, my_lse2);
     __builtin_amdgcn_s_waitcnt(0);
-
+    __syncthreads();
     uint32_t* counter = p.counters + (int64_t)r * p.num_kv_heads + kvh;
-    uint32_t done = 0;
-    if (lane == 0)
-        done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    done = __builtin_amdgcn_readfirstlane(done);
-    if (done != (uint32_t)(nsplit - 1))
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = done == (uint32_t)(nsplit - 1);
+        if (last)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+        last_lds = last;
+    }
+    __syncthreads();
+    if (!last_lds)
         return;
-    if (lane == 0)
-        __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
 
-    // merge: lane -> head h = lane / 16, dims 8 * (lane % 16) .. + 8
-    const int h = lane >> 4;
-    float L = -INFINITY;
-    bool any_nan = false;
-    for (int s = 0; s < nsplit; ++s) {
-        const float ls = load_agent(p.part_lse + base + s * split_stride + h);
-        any_nan |= (ls != ls);
-        L = fmaxf(L, ls);
-    }
-    float wsum = 0.f;
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-        const int64_t pi = base + s * split_stride + h;
-        const float w = fast_exp2(load_agent(p.part_lse + pi) - L);
-        const float* src = p.part_o + pi * kHeadDim + c16 * 8;
-        wsum += w;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            o[e] = fmaf(w, load_agent(src + e), o[e]);
+    for (int k = 0; k < kPerThread; ++k) {
+        const int idx = tid + k * 64 * kDecodeWaves;
+        const int h = idx / kHeadDim;
+        float L = -INFINITY;
+        bool any_nan = false;
+        for (int s = 0; s < nsplit; ++s) {
+            const float ls = load_agent(p.part_lse + base + s * split_stride + h);
+            any_nan |= (ls != ls);
+            L = fmaxf(L, ls);
+        }
+        float wsum = 0.f, o = 0.f;
+        for (int s = 0; s < nsplit; ++s) {
+            const int64_t pi = base + s * split_stride + h;
+            const float c = fast_exp2(load_agent(p.part_lse + pi) - L);
+            wsum += c;
+            o = fmaf(c, load_agent(p.part_o + pi * kHeadDim + (idx & (kHeadDim - 1))), o);
+        }
+        p.out[out_base + idx] = __builtin_bit_cast(uint16_t, (__bf16)(any_nan ? nan : o / wsum));
+        if ((idx & (kHeadDim - 1)) == 0)
+            p.lse[(int64_t)q_row * p.num_q_heads + head0 + h] = any_nan ? nan : (L + fast_log2(wsum)) * kLn2;
     }
-    const float winv = any_nan ? nan : 1.f / wsum;
-    u32x4 ov;
-    ov.x = pack_bf16(o[0] * winv, o[1] * winv);
-    ov.y = pack_bf16(o[2] * winv, o[3] * winv);
-    ov.z = pack_bf16(o[4] * winv, o[5] * winv);
-    ov.w = pack_bf16(o[6] * winv, o[7] * winv);
-    *reinterpret_cast<u32x4*>(p.out + ((int64_t)q_row * p.num_q_heads + head0 + h) * kHeadDim + c16 * 8) = ov;
-    if (c16 == 0)
-        p.lse[(int64_t)q_row * p.num_q_heads + head0 + h] = any_nan ? nan : (L + fast_log2(wsum)) * kLn2;
 }
 
 // ------------------------------------------------------------------------------ prefill
@@ -801,7 +883,7 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * g->num_kv_heads;
         if (grid > INT32_MAX)
             return PA_ERR_SHAPE;
-        hipLaunchKernelGGL(pa_decode_split, dim3((uint32_t)grid), dim3(64), 0, st, dp);
+        hipLaunchKernelGGL(pa_decode_split, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }

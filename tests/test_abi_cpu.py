@@ -62,7 +62,7 @@ def test_plan_splits_tile_each_row_once(wl_fn):
         assert len(ranges) <= plan.max_splits
         items += len(ranges) * wl.num_kv_heads
     assert items == plan.decode_items
-    assert 1 <= plan.split_blocks <= 64
+    assert 1 <= plan.split_blocks <= 512
 
 
 def test_plan_is_pure_and_fills_cus():
@@ -71,10 +71,15 @@ def test_plan_is_pure_and_fills_cus():
     a = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256)
     b = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256)
     assert bytes(a) == bytes(b)
-    assert a.decode_items >= 256 * 4                                    # several wavefronts per CU
-    # batch 1 at 2K: splits stay >= 4 blocks but still spread over many CUs
+    assert a.decode_items >= 256                                        # a workgroup per CU
+    assert a.max_splits == 1                                            # 32 x 8 pairs fill the CUs unsplit
+    # fewer (row, KV head) pairs than CUs: rows are split over kv_len
+    sp = synthetic.config_shared_prefix(poison=False)
+    b = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
+    assert b.max_splits == 2 and b.decode_items == 256
+    # batch 1 at 2K: splits stay >= 8 blocks but still spread over many CUs
     one = pa.pa_plan(g, [1], [2049], 256)
-    assert one.split_blocks >= 4 and one.decode_items >= 8 * 16
+    assert one.split_blocks >= 8 and one.decode_items >= 8 * 16
 
 
 def test_plan_prefill_rows_and_workspace():
@@ -91,8 +96,11 @@ def test_plan_prefill_rows_and_workspace():
     # forced split of 1 block and one large split
     p1 = pa.pa_plan(g, qo, kv, 256, split_blocks=1)
     assert p1.split_blocks == 1 and p1.max_splits == -(-2078 // 16)
-    p64 = pa.pa_plan(g, [1], [100], 256, split_blocks=1000)
-    assert p64.split_blocks == 64 and p64.max_splits == 1 and p64.workspace_bytes == 0
+    p512 = pa.pa_plan(g, [1], [100], 256, split_blocks=1000)
+    assert p512.split_blocks == 512 and p512.max_splits == 1 and p512.workspace_bytes == 0
+    # rows longer than 512 blocks are always split
+    long = pa.pa_plan(g, [1] * 64, [20000] * 64, 256)
+    assert long.split_blocks <= 512 and long.max_splits == 3 and long.split_blocks * 3 >= 1250
 
 
 def test_plan_errors():
