@@ -6,8 +6,9 @@
 //                       dot2, online softmax in FP32, PV accumulation in FP32, and the
 //                       log-sum-exp merge of the splits done by the last split to finish
 //   pa_prefill_tile     chunked-prefill rows: one workgroup per (row, KV head, 16 new
-//                       tokens x 4 query heads); S^T = K Q^T and O^T = V^T P^T on BF16
-//                       MFMA with FP32 accumulation, causal mask, online softmax
+//                       tokens x 4 query heads); K / V copied straight into LDS,
+//                       S^T = K Q^T and O^T = V^T P^T on BF16 MFMA with FP32
+//                       accumulation, causal mask, online softmax
 //
 // Pool layout: [block][kv_head][token-in-block][dim] (head-major inside a block), so one
 // (block, KV head) tile is 16 x 128 bf16 = 4 KiB of contiguous memory.
@@ -533,30 +534,141 @@ struct PrefillParams {
     int32_t tile_start[PA_MAX_PREFILL_ROWS + 1];
 };
 
-constexpr int kKeyTile = 64;               // keys per step (four 16-token blocks)
-constexpr int kKStride = kHeadDim + 8;     // K tile row stride in LDS, bf16 units (272 bytes)
-constexpr int kVtStride = kKeyTile + 8;    // V^T tile row stride in LDS, bf16 units (144 bytes)
+constexpr int kPfKeys = 128;               // keys per step: eight 16-token blocks
+constexpr int kPfWaves = 8;                // 2 row groups x 4 key quarters
+constexpr int kPfRows = pa::kPrefillQ * kGroup;   // 64 MFMA rows: (token, head) pairs
+constexpr int kTileChunks = kPfKeys * kHeadDim * 2 / 16;   // 16-byte chunks in one K or V tile
 
-// Workgroup of four wavefronts per (prefill row, KV head, tile of 16 new tokens).  The
+// Swizzle of the 16-byte chunk index inside a staged K / V tile row (one key, 256 bytes).
+// A bijection of the low four bits of the key: the S^T operand reads (16 consecutive keys,
+// one chunk) and the transposed V reads (8 consecutive keys, two adjacent chunks) then hit
+// distinct LDS banks.
+__device__ inline int pf_swz(int key) { return ((key & 7) << 1) | ((key >> 3) & 1); }
+
+// s_waitcnt for vector memory only (expcnt and lgkmcnt left at their maxima).
+template <int kVm>
+__device__ inline void wait_vmcnt()
+{
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read: within each group of 16 lanes, if lane m points at four consecutive
+// bf16 values (row m of a 16 x 4 tile), lane i receives the values at [4k + i/4][i%4],
+// k = 0..3.
+__device__ inline uint2 lds_read_tr16(const void* p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<void*>(p)));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// One 32-key step of a prefill wavefront (two row blocks of 16 rows): S^T = K Q^T, the
+// online softmax, O^T += V^T P^T.  The running maximum is raised lazily: a lane compares
+// its own scores with the row's running maximum plus kRescaleSlack, and only when some
+// lane's score passes it does the wavefront take the row maxima across its lanes and
+// rescale O and the denominators; otherwise no cross-lane exchange is needed.
+__device__ __forceinline__ void pf_step(const bf16x8 (&kop)[2][4], const bf16x8 (&qop)[2][4], const bf16x8 (&vop)[8],
+                                        f32x4 (&oacc)[2][8], float (&m)[2], float (&lsum)[2], bool need_mask, int key0,
+                                        int kslice, const int (&qpos)[2], int kv_hi, float scale_log2)
+{
+    f32x4 sacc[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sacc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                sacc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][ks], qop[rb][ks], sacc[rb][kb], 0, 0, 0);
+        }
+    float x[2][8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[rb][4 * kb + e] = sacc[rb][kb][e];
+    if (need_mask) {                              // wavefront-uniform: diagonal and tail steps only
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int key = key0 + 16 * (i >> 2) + 4 * kslice + (i & 3);
+                x[rb][i] = (key > qpos[rb] || key >= kv_hi) ? -INFINITY : x[rb][i];
+            }
+    }
+    float lmax[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+        lmax[rb] = fmaxf(fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3])),
+                         fmaxf(fmaxf(x[rb][4], x[rb][5]), fmaxf(x[rb][6], x[rb][7]))) * scale_log2;
+    if (__any(lmax[0] > m[0] + kRescaleSlack || lmax[1] > m[1] + kRescaleSlack)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float t = fmaxf(lmax[rb], shfl_xor(lmax[rb], 16));
+            t = fmaxf(t, shfl_xor(t, 32));
+            if (t > m[rb] + kRescaleSlack) {
+                const float alpha = (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - t);
+                m[rb] = t;
+                lsum[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    oacc[rb][db] *= alpha;
+            }
+        }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        // with no visible key yet every score is -inf and any finite offset gives 0
+        const float neg_m = (m[rb] == -INFINITY) ? 0.f : -m[rb];
+        float pe[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            pe[i] = fast_exp2(fmaf(x[rb][i], scale_log2, neg_m));
+        lsum[rb] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+        pb[rb] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16(pe[0], pe[1]), pack_bf16(pe[2], pe[3]),
+                                                  pack_bf16(pe[4], pe[5]), pack_bf16(pe[6], pe[7])});
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[0], oacc[0][db], 0, 0, 0);
+        oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[1], oacc[1][db], 0, 0, 0);
+    }
+}
+
+// Workgroup of eight wavefronts per (prefill row, KV head, tile of 16 new tokens).  The
 // tile's 64 MFMA rows are (token, head) pairs, row = 4 * token + head, so the four query
-// heads of a group share every K / V tile.  Wavefront w owns tokens 4w .. 4w+3.
+// heads of a group share every K / V tile.  Wavefront w owns rows 32 (w % 2) .. +32 and
+// keys 32 (w / 2) .. +32 of every 128-key step; the four key quarters of a row are merged
+// through LDS at the end by the log-sum-exp rule.
+//
+// K / V staging: all eight wavefronts copy one step's eight blocks (one block each, K and
+// V, 8 KiB) straight from the pool into LDS with global_load_lds_dwordx4, double-buffered:
+// the copy of step s + 1 runs while step s is computed.  Slots past kv_len are filled
+// from a valid slot of the same block, so every staged value is finite.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][k-slice l/16] and
 // B[k-slice l/16][l%16] (8 bf16 each) and receives D[4*(l/16) + e][l%16], e = 0..3.
 //   S^T (keys x rows) = K (keys x dims) . Q^T (dims x rows)          contraction over dims
 //   O^T (dims x rows) += V^T (dims x keys) . P^T (keys x rows)       contraction over keys
-// Each lane's S^T values all belong to one row (l%16), so the softmax statistics and the
-// rescaling of O^T stay lane-local except for one exchange across the four k-slices.
-// In the PV product lane l's eight keys are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of
-// a 32-key slice: exactly the S^T values it already holds; V^T is read with the same key
-// order, and a contraction does not care how its index is permuted.
-__global__ __launch_bounds__(256) void pa_prefill_tile(PrefillParams p)
+// Each lane's S^T values all belong to one row, so softmax statistics and the rescaling of
+// O^T stay lane-local except for one exchange across the four k-slices.  In PV lane l's
+// eight keys are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of its 32-key quarter: exactly
+// the S^T values it holds; the V^T operand is read with the same key order by two
+// transposed LDS reads, and a contraction does not care how its index is permuted.
+__global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeyTile * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kHeadDim * kVtStride];
+    __shared__ __attribute__((aligned(1024))) u32x4 tiles[2][2][kTileChunks];   // [buffer][K, V]
+    __shared__ float m_part[4][kPfRows];
+    __shared__ float l_part[4][kPfRows];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int rg = wave & 1, kq = wave >> 1;
     const int kvh = blockIdx.x % p.num_kv_heads;
     const int tile = blockIdx.x / p.num_kv_heads;
     int pr = 0;
@@ -575,23 +687,28 @@ __global__ __launch_bounds__(256) void pa_prefill_tile(PrefillParams p)
     const bool bad_row = qlen < 2 || ctx < 0 || nblk_row > p.max_blocks;
     // keys any token of this tile can see: 0 .. ctx + last token of the tile
     const int kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * pa::kPrefillQ));
-    const int nsteps = (kv_hi + kKeyTile - 1) / kKeyTile;
+    const int nsteps = (kv_hi + kPfKeys - 1) / kPfKeys;
 
-    const int row = lane & 15, kslice = lane >> 4;
-    const int tok_local = qt * pa::kPrefillQ + 4 * wave + (row >> 2);   // token index within the chunk
-    const int head = head0 + (row & 3);
-    const bool row_valid = tok_local < qlen;
-    const int qpos = ctx + tok_local;                                   // absolute position
-
-    // Q^T operand: row `row`, dims 32*ks + 8*kslice .. +8
-    bf16x8 qop[4];
+    const int row16 = lane & 15, kslice = lane >> 4;
+    const int qpos_first = ctx + qt * pa::kPrefillQ + 8 * rg;   // smallest position of this wavefront's rows
+    // this lane's two rows (row blocks rb = 0, 1)
+    int tok_local[2], qpos[2];
+    bf16x8 qop[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (row_valid)
-            v = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)(q0 + tok_local) * p.num_q_heads + head) * kHeadDim +
-                                                 ks * 32 + kslice * 8);
-        qop[ks] = __builtin_bit_cast(bf16x8, v);
+    for (int rb = 0; rb < 2; ++rb) {
+        const int rho = 32 * rg + 16 * rb + row16;
+        tok_local[rb] = qt * pa::kPrefillQ + (rho >> 2);
+        qpos[rb] = ctx + tok_local[rb];
+        const bool ok = tok_local[rb] < qlen;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (ok)
+                v = *reinterpret_cast<const u32x4*>(
+                    p.q + ((int64_t)(q0 + tok_local[rb]) * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + ks * 32 +
+                    kslice * 8);
+            qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
+        }
     }
 
     const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
@@ -600,185 +717,153 @@ __global__ __launch_bounds__(256) void pa_prefill_tile(PrefillParams p)
     const int32_t* bt = p.block_tables + (int64_t)r * p.max_blocks;
     bool bad = bad_row;
 
-    // Staging assignments.  K: chunk id = tid + 256 i -> key (tid>>4) + 16 i, 16-byte chunk tid&15.
-    // V: key quad kq = tid&15 (keys 4kq..4kq+3), chunk c16 = tid>>4; transposed on the way into LDS.
-    // Step s covers logical blocks 4s .. 4s+3 of the row; their ids are read two steps ahead
-    // and the K / V data one to two steps ahead, so neither waits on the other.
-    const int k_key = tid >> 4, k_chunk = tid & 15;
-    const int v_kq = tid & 15, v_chunk = tid >> 4;
-    struct Stage {
-        u32x4 k[4];
-        u32x4 v[4];
+    // Table entry of block `wave` of step s (the row's first block if the step runs past
+    // the row).  It is range-checked only where it is used, one step later, so that the
+    // load does not hold up the copies issued just before it.
+    auto table_entry = [&](int s) {
+        const int b = s * (kPfKeys / kBlock) + wave;
+        return bt[b < nblk_row ? b : 0];
     };
-    auto load_ids = [&](int step, int (&ids)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int b = 4 * step + i;
-            ids[i] = (b * kBlock < kv_hi) ? bt[b] : 0;
-        }
-    };
-    auto load_step = [&](Stage& stg, int step, const int (&ids)[4]) {
-        const int key0 = step * kKeyTile;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = key0 + k_key + 16 * i;
-            const int blk = ids[i];
-            stg.k[i] = u32x4{0u, 0u, 0u, 0u};
-            if (key < kv_hi) {
-                if (blk >= 0 && blk < p.num_blocks)
-                    stg.k[i] = *reinterpret_cast<const u32x4*>(p.k_pool + blk * blk_stride + kvh_off +
-                                                               k_key * kHeadDim + k_chunk * 8);
-                else
-                    bad = true;
-            }
-        }
-        const int vkey0 = key0 + 4 * v_kq;
-        const int q4 = v_kq >> 2;
-        const int vblk = q4 == 0 ? ids[0] : q4 == 1 ? ids[1] : q4 == 2 ? ids[2] : ids[3];
-        const bool vok = vblk >= 0 && vblk < p.num_blocks;
-        if (vkey0 < kv_hi && !vok)
+    auto checked = [&](int id) {
+        if (id < 0 || id >= p.num_blocks) {
             bad = true;
+            id = 0;
+        }
+        return id;
+    };
+    // Wavefront w copies block w of step s: 16 keys = four 1 KiB LDS rows-of-four, for K and V.
+    auto stage = [&](int s, int buf, int id) {
+        const int key_in_blk = lane >> 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            stg.v[i] = u32x4{0u, 0u, 0u, 0u};
-            if (vok && vkey0 + i < kv_hi)
-                stg.v[i] = *reinterpret_cast<const u32x4*>(p.v_pool + vblk * blk_stride + kvh_off +
-                                                           ((vkey0 + i) % kBlock) * kHeadDim + v_chunk * 8);
-        }
-    };
-    auto store_step = [&](const Stage& stg) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(&k_lds[(k_key + 16 * i) * kKStride + k_chunk * 8]) = stg.k[i];
-        // V^T row d holds keys in order; keys 4kq..4kq+3 of dims 8*c16 .. 8*c16+7
-        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&stg.v[0]);
-        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&stg.v[1]);
-        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&stg.v[2]);
-        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&stg.v[3]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // dims 2w (low halves) and 2w+1 (high halves)
-            const u32x2 lo = u32x2{(v0[w] & 0xffffu) | (v1[w] << 16), (v2[w] & 0xffffu) | (v3[w] << 16)};
-            const u32x2 hi = u32x2{(v0[w] >> 16) | (v1[w] & 0xffff0000u), (v2[w] >> 16) | (v3[w] & 0xffff0000u)};
-            *reinterpret_cast<u32x2*>(&vt_lds[(v_chunk * 8 + 2 * w) * kVtStride + 4 * v_kq]) = lo;
-            *reinterpret_cast<u32x2*>(&vt_lds[(v_chunk * 8 + 2 * w + 1) * kVtStride + 4 * v_kq]) = hi;
+            const int row = 16 * wave + 4 * i + key_in_blk;            // key within the step
+            const int tok = 4 * i + key_in_blk;                         // token within the block
+            const int key = s * kPfKeys + row;
+            const int src_tok = key < kvlen ? tok : 0;
+            const int chunk = (lane & 15) ^ pf_swz(row);
+            const int64_t off = id * blk_stride + kvh_off + src_tok * kHeadDim + chunk * 8;
+            __builtin_amdgcn_global_load_lds(p.k_pool + off,
+                                             (__attribute__((address_space(3))) void*)&tiles[buf][0][(16 * wave + 4 * i) * 16],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(p.v_pool + off,
+                                             (__attribute__((address_space(3))) void*)&tiles[buf][1][(16 * wave + 4 * i) * 16],
+                                             16, 0, 0);
         }
     };
 
-    f32x4 oacc[8];
+    f32x4 oacc[2][8];
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-        oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lsum = 0.f;
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
-    Stage stg[2];
-    int idb[2][4];
-    {
-        int ids0[4], ids1[4];
-        load_ids(0, ids0);
-        load_ids(1, ids1);
-        if (nsteps > 0)
-            load_step(stg[0], 0, ids0);
-        if (nsteps > 1)
-            load_step(stg[1], 1, ids1);
-        load_ids(2, idb[0]);
-    }
-    for (int s0 = 0; s0 < nsteps; s0 += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int step = s0 + u;
-            if (step >= nsteps)
-                break;
-            __syncthreads();
-            store_step(stg[u]);
-            __syncthreads();
-            if (step + 2 < nsteps)
-                load_step(stg[u], step + 2, idb[u]);
-            load_ids(step + 3, idb[u ^ 1]);
+    // Workgroups of neighbouring query tiles start their key loop one step apart, so at
+    // any time each K / V step is fetched from memory by one workgroup and found in the
+    // XCD's L2 by the others (all tiles of one KV head run on one XCD).
+    const int rot = nsteps > 0 ? qt % nsteps : 0;
+    auto step_at = [&](int i) { return i + rot < nsteps ? i + rot : i + rot - nsteps; };
+    int next_id = 0;
+    if (nsteps > 0)
+        stage(step_at(0), 0, checked(table_entry(step_at(0))));
+    if (nsteps > 1)
+        next_id = table_entry(step_at(1));
+    for (int it = 0; it < nsteps; ++it) {
+        const int s = step_at(it);
+        const int buf = it & 1;
+        wait_vmcnt<0>();                       // this wavefront's copies of this step have landed
+        __builtin_amdgcn_s_barrier();          // everyone's have, and the previous step is finished
+        const u32x4* kt = tiles[buf][0];
+        const char* vt = reinterpret_cast<const char*>(tiles[buf][1]);
 
-            // S^T for the four 16-key blocks of this step
-            f32x4 sacc[4];
+        // All of this step's LDS operands are read before the next copy is issued, so no
+        // LDS read is ever outstanding next to a copy into the other buffer.
+        bf16x8 kop[2][4];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4*>(&k_lds[(kb * 16 + row) * kKStride + ks * 32 + kslice * 8]));
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[ks], sacc[kb], 0, 0, 0);
-                }
+            for (int ks = 0; ks < 4; ++ks) {
+                const int key = 32 * kq + 16 * kb + row16;
+                kop[kb][ks] = __builtin_bit_cast(bf16x8, kt[key * 16 + ((ks * 4 + kslice) ^ pf_swz(key))]);
             }
-            // lane holds S^T[key = key0 + 16 kb + 4 kslice + e][row]
-            const int key0 = step * kKeyTile;
-            float x[4][4];
-            float tmax = -INFINITY;
+        bf16x8 vop[8];
+        {
+            const int i16 = lane & 15;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = key0 + 16 * kb + 4 * kslice + e;
-                    float v = sacc[kb][e] * p.scale_log2;
-                    if (key > qpos || key >= kv_hi)
-                        v = -INFINITY;
-                    x[kb][e] = v;
-                    tmax = fmaxf(tmax, v);
-                }
-            tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-            const float mnew = fmaxf(m, tmax);
-            const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
-            m = mnew;
-            float psum = 0.f;
-            uint32_t pk[4][2];   // P^T operand halves, bf16 pairs
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                float pe[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pe[e] = (mnew == -INFINITY) ? 0.f : fast_exp2(x[kb][e] - mnew);
-                    psum += pe[e];
-                }
-                pk[kb][0] = pack_bf16(pe[0], pe[1]);
-                pk[kb][1] = pack_bf16(pe[2], pe[3]);
-            }
-            lsum = lsum * alpha + psum;
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-                oacc[db] *= alpha;
-
-            // O^T += V^T P^T over two 32-key slices
-#pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) {
-                const bf16x8 b = __builtin_bit_cast(
-                    bf16x8, u32x4{pk[2 * ks2][0], pk[2 * ks2][1], pk[2 * ks2 + 1][0], pk[2 * ks2 + 1][1]});
-#pragma unroll
-                for (int db = 0; db < 8; ++db) {
-                    const uint16_t* vrow = &vt_lds[(db * 16 + row) * kVtStride + 32 * ks2 + 4 * kslice];
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                    oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[db], 0, 0, 0);
-                }
+            for (int db = 0; db < 8; ++db) {
+                // source lane i16 of group kslice points at key 4 kslice + i16/4 (+16), dims
+                // 16 db + 4 (i16 % 4) .. +4; lane (kslice, i16) receives dim 16 db + i16 of
+                // keys 4 kslice + 0..3 (+16)
+                const int c = 2 * db + ((i16 & 3) >> 1);
+                const int k_lo = 32 * kq + 4 * kslice + (i16 >> 2);
+                const int k_hi = k_lo + 16;
+                const uint2 lo = lds_read_tr16(vt + k_lo * 256 + ((c ^ pf_swz(k_lo)) << 4) + ((i16 & 1) << 3));
+                const uint2 hi = lds_read_tr16(vt + k_hi * 256 + ((c ^ pf_swz(k_hi)) << 4) + ((i16 & 1) << 3));
+                vop[db] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
             }
         }
+        if (it + 1 < nsteps) {
+            stage(step_at(it + 1), buf ^ 1, checked(next_id));
+            if (it + 2 < nsteps)
+                next_id = table_entry(step_at(it + 2));
+        }
+
+        const int key0 = s * kPfKeys + 32 * kq;
+        // wavefront-uniform: the wavefront's first row has the smallest position
+        const bool need_mask = key0 + 31 >= kv_hi || key0 + 31 > qpos_first;
+        pf_step(kop, qop, vop, oacc, m, lsum, need_mask, key0, kslice, qpos, kv_hi, p.scale_log2);
     }
 
-    float ltot = lsum;
-    ltot += shfl_xor(ltot, 16);
-    ltot += shfl_xor(ltot, 32);
+    // merge the four key quarters of every row through LDS (the tile buffers are free now)
+    __syncthreads();
+    float* o_part = reinterpret_cast<float*>(&tiles[0][0][0]);   // [4][64 rows][128 dims] = 128 KiB
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int rho = 32 * rg + 16 * rb + row16;
+        float ltot = lsum[rb];
+        ltot += shfl_xor(ltot, 16);
+        ltot += shfl_xor(ltot, 32);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            *reinterpret_cast<f32x4*>(&o_part[(kq * kPfRows + rho) * kHeadDim + db * 16 + 4 * kslice]) = oacc[rb][db];
+        if (kslice == 0) {
+            m_part[kq][rho] = m[rb];
+            l_part[kq][rho] = ltot;
+        }
+    }
     bad = __syncthreads_or(bad);
-    if (!row_valid)
-        return;
-    const float nan = __builtin_nanf("");
-    const float inv = bad ? nan : 1.f / ltot;
-    uint16_t* orow = p.out + ((int64_t)(q0 + tok_local) * p.num_q_heads + head) * kHeadDim;
+
+    {
+        const int rho = tid >> 3, d0 = (tid & 7) * 16;
+        const int tl = qt * pa::kPrefillQ + (rho >> 2);
+        if (tl < qlen) {
+            float M = -INFINITY;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-        const u32x2 o = u32x2{pack_bf16(oacc[db][0] * inv, oacc[db][1] * inv), pack_bf16(oacc[db][2] * inv, oacc[db][3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + db * 16 + 4 * kslice) = o;
+            for (int k = 0; k < 4; ++k)
+                M = fmaxf(M, m_part[k][rho]);
+            float w[4], L = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                w[k] = (m_part[k][rho] == -INFINITY) ? 0.f : fast_exp2(m_part[k][rho] - M);
+                L += w[k] * l_part[k][rho];
+            }
+            const float inv = bad ? __builtin_nanf("") : 1.f / L;
+            uint16_t* orow = p.out + ((int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + d0;
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    o += w[k] * *reinterpret_cast<const f32x4*>(&o_part[(k * kPfRows + rho) * kHeadDim + d0 + 4 * c4]);
+                *reinterpret_cast<u32x2*>(orow + 4 * c4) =
+                    u32x2{pack_bf16(o[0] * inv, o[1] * inv), pack_bf16(o[2] * inv, o[3] * inv)};
+            }
+            if ((tid & 7) == 0)
+                p.lse[(int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3)] =
+                    bad ? __builtin_nanf("") : (M + fast_log2(L)) * kLn2;
+        }
     }
-    if (kslice == 0)
-        p.lse[(int64_t)(q0 + tok_local) * p.num_q_heads + head] = bad ? nan : (m + fast_log2(ltot)) * kLn2;
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -855,7 +940,7 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         for (int i = 0; i <= PA_MAX_PREFILL_ROWS; ++i)
             pp.tile_start[i] = i <= plan->num_prefill_rows ? plan->prefill_tile_start[i] : plan->prefill_tiles;
         const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads;
-        hipLaunchKernelGGL(pa_prefill_tile, dim3((uint32_t)grid), dim3(256), 0, st, pp);
+        hipLaunchKernelGGL(pa_prefill_tile, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
