@@ -4,17 +4,22 @@ A step is one pass of the path over one layer's batch: pa_plan (host) ->
 pa_append_kv -> pa_attention_batch.  The headline workload is the Qwen3-8B
 single-layer decode step (32 requests, kv_len = 2048 + U[0,255], 32 query / 8 KV
 heads, head_dim 128, 16-token blocks, bf16); its value is algorithmic HBM bytes per
-second.  The mixed continuous batch (one 512-token prefill chunk at offset 4096 plus
-31 decode rows, 543 new tokens) is timed the same way and reported in tokens/s.
+second of the whole step.  The mixed continuous batch (one 512-token prefill chunk at
+offset 4096 plus 31 decode rows, 543 new tokens) is timed the same way and reported
+in tokens/s, and the prefill chunk alone is reported against the bf16 MFMA peak.
 
 Each step reads a different copy of the KV pools (the copies stand for different
 layers), so no step finds the previous step's KV in the 256 MB last-level cache.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --kernel-only decode|mixed|prefill   # attention launches only, for rocprofv3
+    python bench.py --summarize DIR [--title T]          # rocprofv3 CSV output -> profile text
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,17 +31,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode-step attention HBM GB/s (% of peak) + mixed-batch tokens/s, Qwen3-8B layer"
-HBM_PEAK_GBS = 8000.0
-BF16_MFMA_PEAK_TFLOPS = 2500.0
-TOKEN_LAYER_BYTES = 2 * 8 * 128 * 2        # K + V of one token in one layer, all 8 KV heads
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_attention_04_amd", "csrc", "pa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.json")
+CALIBRATION_COPY_BYTES = 256 << 20
 
 
 def algorithmic_bytes(wl) -> dict:
-    """Bytes the method itself must move for one layer step (shared blocks once)."""
+    """Bytes the method itself must move for one layer step: every KV slot read once
+    (a block shared by several rows counts once), Q, O, LSE, table entries and lengths,
+    and the appended K / V rows (read from the new-token buffers, written to the pool)."""
     B = wl.block_size
     table = sum(-(-int(L) // B) * 4 for L in wl.kv_len)
-    # unique token slots read: a block shared by several rows counts once, with the
-    # largest number of its tokens any row reads
     slots = {}
     for r in range(wl.num_reqs):
         nb = -(-int(wl.kv_len[r]) // B)
@@ -65,6 +72,12 @@ def prefill_flops(wl) -> int:
             h = kv - c
             pairs += c * h + c * (c + 1) // 2
     return pairs * 4 * wl.head_dim * wl.num_q_heads
+
+
+def prefill_only_workload(poison=False):
+    import synthetic
+    return synthetic.build("prefill_512_at_4096", 4, 32, 8, qo_len=[512], kv_len=[4608],
+                           num_blocks=synthetic.POOL_BLOCKS_12GIB, poison=poison)
 
 
 class Stepper:
@@ -118,7 +131,7 @@ def time_steps(stepper, steps: int, warmup: int, attention_only: bool = False) -
 
 def event_time(stepper, reps: int) -> float:
     """Average device time of one pa_attention_batch call, from HIP events recorded on
-    the stream the kernels run on."""
+    the stream its kernels are launched on (the current stream)."""
     import torch
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
@@ -131,9 +144,25 @@ def event_time(stepper, reps: int) -> float:
     return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
 
 
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch", {}).get("total")
+
+
 def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
-    """The oracle, as it stands, on the host cores: whole decode steps repeated until
-    `min_seconds` have passed; reported in the same unit as the GPU value."""
+    """The oracle, as it stands, on the host cores: whole attention passes over the
+    decode-step workload repeated until `min_seconds` have passed; same unit as value."""
     import oracle
 
     kp, vp = oracle.append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
@@ -154,6 +183,86 @@ def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
                       f"{int(wl.kv_len.sum())} KV tokens), fp64 C oracle, {el:.1f} s"}
 
 
+def kernel_only(which: str, reps: int):
+    """Attention launches only (plus one calibration copy of known size), for counters."""
+    import torch
+
+    import paged_kv_attention_04_amd as pa
+    import synthetic
+
+    torch.cuda.set_device(0)
+    pa.lib()
+    wl = {"decode": lambda: synthetic.config_decode(poison=False),
+          "mixed": lambda: synthetic.config_mixed(poison=False),
+          "prefill": prefill_only_workload}[which]()
+    st = Stepper(wl, 4)
+    src = torch.empty(CALIBRATION_COPY_BYTES // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)                                           # calibration: reads and writes 256 MiB
+    for _ in range(reps):
+        st.step(attention_only=True)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_only": which, "launches": reps, "attention_bytes": algorithmic_bytes(wl)["attention"],
+                      "calibration_copy_bytes": CALIBRATION_COPY_BYTES}), flush=True)
+
+
+def summarize(directory: str, title: str):
+    """Turn rocprofv3 CSV output (kernel trace and / or counter collection) into text."""
+    import csv
+    from collections import defaultdict
+    lines = [f"### {title}", ""]
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)):
+        lines += ["| kernel | calls | avg us | min us | max us | total us |", "|---|---|---|---|---|---|"]
+        for r in csv.DictReader(open(f)):
+            name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
+                         f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['TotalDurationNs']) / 1e3:.1f} |")
+        lines.append("")
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
+        agg = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            agg[(name, r["Counter_Name"])].append(float(r["Counter_Value"]))
+        lines += ["| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+        for (name, c), v in sorted(agg.items()):
+            lines.append(f"| {name} | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+        lines.append("")
+    print("\n".join(lines))
+
+
+def write_traffic(fetch_dir: str, write_dir: str):
+    """HBM bytes per decode launch from two counter runs of `--kernel-only decode`
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the calibration copy of known size; written next to the kernel-source hash."""
+    import csv
+
+    def per_kernel(directory, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = "decode" if "pa_decode_split" in r["Kernel_Name"] else (
+                    "copy" if "pa_" not in r["Kernel_Name"] else "other")
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return vals
+
+    f, w = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    kib_true = CALIBRATION_COPY_BYTES / 1024
+    read_scale = kib_true / max(f["copy"])       # the largest non-library dispatch is the 256 MiB copy
+    write_scale = kib_true / max(w["copy"])
+    read = float(np.mean(f["decode"])) * 1024 * read_scale
+    write = float(np.mean(w["decode"])) * 1024 * write_scale
+    out = {"kernel": "pa_decode_split", "workload": "qwen3_8b_decode_step",
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "fetch_kib_per_dispatch": float(np.mean(f["decode"])), "write_kib_per_dispatch": float(np.mean(w["decode"])),
+           "calibration": {"copy_bytes": CALIBRATION_COPY_BYTES, "fetch_kib": max(f["copy"]), "write_kib": max(w["copy"]),
+                           "read_scale": read_scale, "write_scale": write_scale},
+           "bytes_per_launch": {"read": round(read), "write": round(write), "total": round(read + write)}}
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,10 +271,24 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=8, help="KV pool replicas rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-only", choices=["decode", "mixed", "prefill"])
+    ap.add_argument("--reps", type=int, default=20)
+    ap.add_argument("--summarize")
+    ap.add_argument("--title", default="rocprofv3 summary")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args(argv)
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
+    if args.summarize:
+        summarize(args.summarize, args.title)
+        return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this path has no multi-GPU mode (--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: this path has no multi-GPU mode (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+    if args.kernel_only:
+        kernel_only(args.kernel_only, args.reps)
+        return
 
     import torch
 
@@ -175,7 +298,7 @@ def main(argv=None):
     torch.cuda.set_device(0)
     pa.lib()
 
-    # headline: Qwen3-8B single-layer decode step
+    # headline: Qwen3-8B single-layer decode step (plan + append + attention)
     wl = synthetic.config_decode(poison=False)
     ab = algorithmic_bytes(wl)
     st = Stepper(wl, args.copies)
@@ -189,6 +312,15 @@ def main(argv=None):
     sm = Stepper(wm, args.copies)
     sec_m = time_steps(sm, args.steps, args.warmup)
     t_m = event_time(sm, max(args.steps, 50))
+    del sm
+
+    # the prefill chunk alone, against the bf16 matrix peak
+    wp = prefill_only_workload()
+    sp = Stepper(wp, 2)
+    time_steps(sp, 10, 5, attention_only=True)
+    t_p = event_time(sp, max(args.steps // 2, 30))
+    del sp
+    pflops = prefill_flops(wp)
 
     line = {
         "metric": METRIC,
@@ -204,19 +336,22 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "qwen3_8b_decode_step: 32 requests, kv_len 2048+U[0,255], 32 q / 8 kv heads, "
-                               "head_dim 128, 16-token blocks, bf16 KV pool of 5461 blocks, 1 layer",
+                               "head_dim 128, 16-token blocks, bf16 KV pool of 5461 blocks, 1 layer; "
+                               "step = pa_plan + pa_append_kv + pa_attention_batch",
                    "kv_bytes_unique": ab["kv_unique"], "step_bytes": ab["step"],
                    "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "plan": {"split_blocks": st.plan.split_blocks, "max_splits": st.plan.max_splits,
-                            "decode_items": st.plan.decode_items}},
+                            "decode_workgroups": st.plan.decode_items}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pa_attention_batch (decode split kernel + split merge)",
-                     "avg_us": round(t_attn * 1e6, 3)},
-        "mixed_batch": {"tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
-                        "attention_us": round(t_m * 1e6, 3), "new_tokens": wm.total_q,
-                        "prefill_tflops_if_alone": None,
-                        "prefill_flops": prefill_flops(wm)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "pa_decode_split (the only kernel pa_attention_batch launches for this batch)",
+                     "avg_us": round(t_attn * 1e6, 3), "bytes_per_launch": ab["attention"]},
+        "mixed_batch": {"workload": "1 prefill row (512 tokens at offset 4096) + 31 decode rows, 543 new tokens",
+                        "tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
+                        "attention_us": round(t_m * 1e6, 3)},
+        "prefill_chunk": {"workload": "512 new tokens at kv offset 4096, 32 q / 8 kv heads, causal",
+                          "us": round(t_p * 1e6, 3), "tflops": round(pflops / t_p / 1e12, 1),
+                          "frac_of_bf16_mfma_peak": round(pflops / t_p / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(synthetic.config_decode(poison=False), args.cpu_seconds)
