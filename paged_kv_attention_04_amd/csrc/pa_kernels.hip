@@ -230,14 +230,45 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     const int rest = blockIdx.x / p.num_kv_heads;
     const int r = rest % p.num_reqs;
     const int split = rest / p.num_reqs;
-    const int q_row = p.qo_indptr[r];
-    if (p.qo_indptr[r + 1] - q_row != 1)
-        return;                                       // not a decode row
-    const int kvlen = p.kv_len[r];
-    const int nblk = (kvlen + kBlock - 1) / kBlock;
-    const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
     const int head0 = kvh * kGroup;
     const float nan = __builtin_nanf("");
+
+    // Wavefront w takes blocks g0 + w, g0 + w + 8, ... of the split.  Their table entries
+    // (lane i holds entry i) and the first kDecodeDepth blocks' K / V are requested before
+    // the row's lengths arrive, so the start-up waits for one memory round trip less.  The
+    // early requests are bounded by the table row and the pool; entries past the row's
+    // last block are never used.
+    const int g0 = split * p.split_blocks;
+    const int bidx = g0 + wave + kDecodeWaves * lane;
+    int my_blk = 0;
+    if (lane * kDecodeWaves < p.split_blocks && bidx < p.max_blocks)
+        my_blk = p.block_tables[(int64_t)r * p.max_blocks + bidx];
+    const int q_row = p.qo_indptr[r];
+    const int q_end = p.qo_indptr[r + 1];
+    const int kvlen = p.kv_len[r];
+
+    const int t8 = lane >> 3, c8 = lane & 7;          // score role
+    const int ts = t8 + 8 * (c8 >> 2), hs = c8 & 3;   // softmax role: token ts, head hs
+    const int c16 = lane & 15, tg = lane >> 4;        // PV role
+
+    const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
+    const int64_t kvh_off = (int64_t)kvh * tile_elems;
+    const int64_t blk_stride = (int64_t)p.num_kv_heads * tile_elems;
+    auto issue = [&](KvStage& st, int j) {
+        int id = __builtin_amdgcn_readlane(my_blk, j);
+        id = (id >= 0 && id < p.num_blocks) ? id : 0;
+        const int64_t off = (int64_t)id * blk_stride + kvh_off;
+        load_stage(st, p.k_pool + off, p.v_pool + off, lane);
+    };
+    KvStage st[kDecodeDepth + 1];
+#pragma unroll
+    for (int d = 0; d < kDecodeDepth; ++d)
+        issue(st[d], d);
+
+    if (q_end - q_row != 1)
+        return;                                       // not a decode row
+    const int nblk = (kvlen + kBlock - 1) / kBlock;
+    const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
     if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits ||
         p.split_blocks > pa::kMaxSplitBlocks) {       // lengths disagree with the plan
         if (split == 0)
@@ -250,24 +281,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     }
     if (split >= nsplit)
         return;
-
-    // this wavefront's run of blocks
-    const int g0 = split * p.split_blocks;
-    const int gnb = min(nblk - g0, p.split_blocks);
-    const int per = (gnb + kDecodeWaves - 1) / kDecodeWaves;          // <= 64
-    const int b0 = g0 + wave * per;
-    const int nb = max(0, min(per, g0 + gnb - b0));
-    int my_blk = 0;
-    bool bad = false;
-    if (lane < nb) {
-        my_blk = p.block_tables[(int64_t)r * p.max_blocks + b0 + lane];
-        bad = my_blk < 0 || my_blk >= p.num_blocks;
-    }
-    bad = __syncthreads_or(bad);                      // a block id outside the pool: no reads
-
-    const int t8 = lane >> 3, c8 = lane & 7;          // score role
-    const int ts = t8 + 8 * (c8 >> 2), hs = c8 & 3;   // softmax role: token ts, head hs
-    const int c16 = lane & 15, tg = lane >> 4;        // PV role
+    const int g_end = min(nblk, g0 + p.split_blocks);
+    const int nb = g_end > g0 + wave ? (g_end - g0 - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+    bool bad = lane < nb && (my_blk < 0 || my_blk >= p.num_blocks);
+    bad = __syncthreads_or(bad);                      // a block id outside the pool: its data is not used
 
     u32x4 qv[kGroup][2];
     {
@@ -288,14 +305,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
         for (int e = 0; e < 8; ++e)
             acc[h][e] = 0.f;
 
-    const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
-    const int64_t kvh_off = (int64_t)kvh * tile_elems;
-    const int64_t blk_stride = (int64_t)p.num_kv_heads * tile_elems;
     float* pw = p_lds[wave];
-    auto issue = [&](KvStage& st, int j) {
-        const int64_t off = (int64_t)__builtin_amdgcn_readlane(my_blk, j) * blk_stride + kvh_off;
-        load_stage(st, p.k_pool + off, p.v_pool + off, lane);
-    };
 
     auto process = [&](const KvStage& st, int j) {
         // scores of tokens t8 + 8 tt for the four heads, partial over this lane's 16 dims,
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
                 sc[tt * kGroup + h] = dot16(qv[h][1], st.k[2 * tt + 1], dot16(qv[h][0], st.k[2 * tt], 0.f));
         float x = reduce_scatter8(sc, c8);
         x *= p.scale_log2;
-        const int pos0 = (b0 + j) * kBlock;
+        const int pos0 = (g0 + wave + kDecodeWaves * j) * kBlock;
         if (pos0 + ts >= kvlen)
             x = -INFINITY;
         if (__any(x > m + kRescaleSlack)) {
@@ -374,15 +384,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     };
 
     if (!bad && nb > 0) {
-        // Loads for block j + kDecodeDepth are issued before block j is processed.  Past the
-        // end of the run the last block is fetched again (an L2 hit), so every iteration
-        // issues the same loads, and the stages that are in flight at the top of the
-        // steady-state loop are the same on entry and on every trip: the compiler can then
-        // wait for exactly the oldest stage.
-        KvStage st[kDecodeDepth + 1];
-#pragma unroll
-        for (int d = 0; d < kDecodeDepth; ++d)
-            issue(st[d], min(d, nb - 1));
+        // Loads for block j + kDecodeDepth are issued before block j is processed (the first
+        // kDecodeDepth were issued above).  Past the end of the run the last block is
+        // fetched again (an L2 hit), so every iteration issues the same loads, and the stages
+        // in flight at the top of the steady-state loop are the same on entry and on every
+        // trip: the compiler can then wait for exactly the oldest stage.
         int j0 = 0;
         for (; j0 + kDecodeDepth + 1 <= nb; j0 += kDecodeDepth + 1) {
 #pragma unroll
