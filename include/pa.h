@@ -106,7 +106,8 @@ typedef struct pa_plan_t {
     int32_t split_blocks;                /* KV blocks per decode split (one workgroup each)   */
     int32_t max_splits;                  /* largest split count of any decode row             */
     int32_t decode_items;                /* (row, KV head, split) decode workgroups           */
-    int32_t prefill_tiles;               /* query tiles over all prefill rows                 */
+    int32_t prefill_tiles;               /* 32-token query tiles over all prefill rows        */
+    int32_t prefill_splits;              /* key splits per prefill tile (one workgroup each)  */
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];       /* request index of each prefill row      */
     int32_t prefill_tile_start[PA_MAX_PREFILL_ROWS + 1]; /* prefix sums of tiles per row      */
     uint64_t workspace_bytes;            /* device workspace pa_attention_batch needs         */
@@ -115,16 +116,22 @@ typedef struct pa_plan_t {
 /*
  * Build the plan.  qo_len_host / kv_len_host: host int32 [num_reqs].  num_cus: the
  * device's compute-unit count (256 on MI355X; see pa_query_num_cus).
- * split_blocks: 0 picks the split length automatically: a decode row is split
- * over kv_len only when its (row, KV head) pairs alone would leave CUs idle (the
- * pages motivate splitting attention over kv_len as well as over requests when a
- * batch has few tokens: Perplexity blog, section on prefill vs decode); > 0
- * forces that many blocks per split (clamped to 1 .. 512).  Errors: PA_ERR_NULL, PA_ERR_SHAPE (qo_len < 1 or
- * kv_len < qo_len), PA_ERR_UNSUPPORTED (geometry, more than PA_MAX_PREFILL_ROWS
- * prefill rows, or split decode rows with num_reqs * num_kv_heads > 16384).
+ * split_blocks: 0 picks the decode split length automatically: a decode row is
+ * split over kv_len only when its (row, KV head) pairs alone would leave CUs idle
+ * (the pages motivate splitting attention over kv_len as well as over requests when
+ * a batch has few tokens: Perplexity blog, section on prefill vs decode); > 0 forces
+ * that many blocks per split (clamped to 1 .. 512).
+ * prefill_splits: 0 picks how many contiguous key ranges each 32-token prefill tile
+ * is cut into (one workgroup per range, merged by the last one to finish) so that
+ * the tiles fill the CUs; > 0 forces that count (1 .. 64; ranges may then be empty).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE (qo_len < 1, kv_len < qo_len, prefill_splits
+ * out of range), PA_ERR_UNSUPPORTED (geometry, more than PA_MAX_PREFILL_ROWS prefill
+ * rows, or split work needing more than 16384 completion counters: one per
+ * (request, KV head) plus one per (prefill tile, KV head)).
  */
 pa_status pa_plan(const pa_geometry* geometry, int32_t num_reqs, const int32_t* qo_len_host,
-                  const int32_t* kv_len_host, int32_t num_cus, int32_t split_blocks, pa_plan_t* plan);
+                  const int32_t* kv_len_host, int32_t num_cus, int32_t split_blocks, int32_t prefill_splits,
+                  pa_plan_t* plan);
 
 /*
  * Write this step's new K/V rows into the pools through the slot mapping
@@ -145,10 +152,11 @@ pa_status pa_append_kv(const pa_geometry* geometry, void* k_pool, void* v_pool, 
  * k_pool, v_pool, block_tables, qo_indptr (int32 [num_reqs + 1], prefix sums of
  * qo_len), kv_len (int32 [num_reqs]), out, lse, workspace (at least
  * plan->workspace_bytes bytes, 256-byte aligned; may be NULL when that is 0).
- * The workspace holds split partials and, in its first 64 KiB, one completion
- * counter per (row, KV head): allocate it zeroed once; every call leaves the
- * counters zero again, so the buffer can be reused by later calls (of any plan) on
- * the same stream.  Two calls that run concurrently must not share a workspace.
+ * The workspace holds split partials and, in its first 64 KiB, the completion
+ * counters of split work (one per (row, KV head) and one per (prefill tile, KV
+ * head)): allocate it zeroed once; every call leaves the counters zero again, so
+ * the buffer can be reused by later calls (of any plan) on the same stream.  Two
+ * calls that run concurrently must not share a workspace.
  * Errors: PA_ERR_NULL, PA_ERR_UNSUPPORTED (geometry differs from the plan's),
  * PA_ERR_WORKSPACE, PA_ERR_HIP.
  */

@@ -49,6 +49,7 @@ class Plan(ctypes.Structure):
                 ("total_q", ctypes.c_int32), ("num_decode_rows", ctypes.c_int32),
                 ("num_prefill_rows", ctypes.c_int32), ("split_blocks", ctypes.c_int32),
                 ("max_splits", ctypes.c_int32), ("decode_items", ctypes.c_int32), ("prefill_tiles", ctypes.c_int32),
+                ("prefill_splits", ctypes.c_int32),
                 ("prefill_req", ctypes.c_int32 * PA_MAX_PREFILL_ROWS),
                 ("prefill_tile_start", ctypes.c_int32 * (PA_MAX_PREFILL_ROWS + 1)),
                 ("workspace_bytes", ctypes.c_uint64)]
@@ -68,7 +69,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     G, PL = ctypes.POINTER(Geometry), ctypes.POINTER(Plan)
-    L.pa_plan.argtypes = [G, i32, P, P, i32, i32, PL]
+    L.pa_plan.argtypes = [G, i32, P, P, i32, i32, i32, PL]
     L.pa_append_kv.argtypes = [G, P, P, P, P, P, i32, P]
     L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_validate_batch.argtypes = [G, i32, P, P, P, i32, P]
@@ -123,8 +124,9 @@ def num_cus(device: int = 0) -> int:
     return int(v.value)
 
 
-def pa_plan(geometry: Geometry, qo_len, kv_len, num_cus: int = 256, split_blocks: int = 0) -> Plan:
-    """Host planner; qo_len / kv_len are host int32 sequences."""
+def pa_plan(geometry: Geometry, qo_len, kv_len, num_cus: int = 256, split_blocks: int = 0,
+            prefill_splits: int = 0) -> Plan:
+    """Host planner; qo_len / kv_len are host int32 sequences; 0 picks a split automatically."""
     import numpy as np
     qo = np.ascontiguousarray(qo_len, dtype=np.int32)
     kv = np.ascontiguousarray(kv_len, dtype=np.int32)
@@ -132,7 +134,7 @@ def pa_plan(geometry: Geometry, qo_len, kv_len, num_cus: int = 256, split_blocks
         raise ValueError("qo_len and kv_len differ in length")
     plan = Plan()
     _check("pa_plan", lib().pa_plan(ctypes.byref(geometry), int(qo.size), _np_ptr(qo), _np_ptr(kv), int(num_cus),
-                                    int(split_blocks), ctypes.byref(plan)))
+                                    int(split_blocks), int(prefill_splits), ctypes.byref(plan)))
     return plan
 
 
@@ -209,7 +211,8 @@ def to_device(arr, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
-def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", validate: bool = True):
+def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", validate: bool = True,
+                 prefill_splits: int = 0):
     """Upload a workload (see synthetic.Workload for the fields), append its new tokens,
     plan and run attention; returns host numpy (k_pool, v_pool, out, lse)."""
     import numpy as np
@@ -222,7 +225,7 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
         rc, bad = pa_validate_append(g, wl.slot_mapping)
         if rc:
             raise PaError("pa_validate_append", rc, f" at token {bad}")
-    plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks)
+    plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks, prefill_splits)
     kp, vp = to_device(wl.k_pool, device), to_device(wl.v_pool, device)
     q = to_device(wl.q, device)
     bt = to_device(wl.block_tables, device)

@@ -17,19 +17,26 @@ constexpr int kWorkgroupsPerCu = 1;
 constexpr int kMinAutoSplitBlocks = 8;
 // Fixed cost of one decode workgroup (start-up latency, merge), in block-times.
 constexpr int kWorkgroupOverheadBlocks = 4;
+// Prefill workgroup costs in 128-key step times: start-up and output of any workgroup,
+// and the partial write plus merge read that a split tile adds.
+constexpr int kPrefillOverheadSteps = 2;
+constexpr int kPrefillMergeSteps = 1;
+// Shortest automatic prefill split, in steps.
+constexpr int kMinAutoPrefillSplitSteps = 4;
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
 }  // namespace
 
 extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32_t* qo_len,
-                             const int32_t* kv_len, int32_t num_cus, int32_t split_blocks, pa_plan_t* plan)
+                             const int32_t* kv_len, int32_t num_cus, int32_t split_blocks, int32_t prefill_splits,
+                             pa_plan_t* plan)
 {
     if (!g || !plan || (num_reqs > 0 && (!qo_len || !kv_len)))
         return PA_ERR_NULL;
     if (!pa::geometry_supported(g))
         return PA_ERR_UNSUPPORTED;
-    if (num_reqs < 0)
+    if (num_reqs < 0 || prefill_splits < 0 || prefill_splits > pa::kMaxPrefillSplits)
         return PA_ERR_SHAPE;
     memset(plan, 0, sizeof(*plan));
     plan->num_q_heads = g->num_q_heads;
@@ -37,7 +44,7 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
     plan->num_reqs = num_reqs;
 
     int64_t decode_blocks = 0, total_q = 0;
-    int32_t max_decode_blocks = 0;
+    int32_t max_decode_blocks = 0, max_prefill_steps = 0;
     for (int32_t r = 0; r < num_reqs; ++r) {
         if (qo_len[r] < 1 || kv_len[r] < qo_len[r])
             return PA_ERR_SHAPE;
@@ -53,6 +60,7 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
             int32_t i = plan->num_prefill_rows++;
             plan->prefill_req[i] = r;
             plan->prefill_tile_start[i + 1] = plan->prefill_tile_start[i] + ceil_div(qo_len[r], pa::kPrefillQ);
+            max_prefill_steps = std::max(max_prefill_steps, ceil_div(kv_len[r], pa::kPrefillKeys));
         }
     }
     if (total_q > INT32_MAX)
@@ -101,11 +109,44 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
         max_splits = std::max(max_splits, s);
         items += (int64_t)s * g->num_kv_heads;
     }
-    if (max_splits > 1 && (int64_t)num_reqs * g->num_kv_heads > pa::kMaxCounters)
-        return PA_ERR_UNSUPPORTED;   // more (row, KV head) completion counters than the workspace holds
     plan->max_splits = max_splits;
     plan->decode_items = (int32_t)std::min<int64_t>(items, INT32_MAX);
-    plan->workspace_bytes = pa::workspace_layout(num_reqs, max_splits, g->num_q_heads).total;
+
+    // Prefill key splits: a tile's causal key range is cut into contiguous step ranges,
+    // one workgroup each, when the (tile, KV head) pairs alone would leave CUs idle.
+    // Candidates are scored like the decode splits: rounds of resident workgroups times
+    // the steps of the longest range plus the fixed and merge costs.
+    int32_t ps = 1;
+    if (plan->prefill_tiles > 0) {
+        if (prefill_splits > 0) {
+            ps = prefill_splits;
+        } else {
+            const int64_t base = (int64_t)plan->prefill_tiles * g->num_kv_heads;
+            const int64_t cus = std::max(num_cus, 1);
+            int64_t best_cost = INT64_MAX;
+            for (int32_t cand = 1; cand <= pa::kMaxPrefillSplits; ++cand) {
+                const int32_t steps = ceil_div(std::max(max_prefill_steps, 1), cand);
+                if (cand > 1 && steps < kMinAutoPrefillSplitSteps)
+                    break;
+                const int64_t rounds = (base * cand + cus - 1) / cus;
+                const int64_t cost =
+                    rounds * (steps + kPrefillOverheadSteps + (cand > 1 ? kPrefillMergeSteps : 0));
+                if (cost < best_cost) {
+                    best_cost = cost;
+                    ps = cand;
+                }
+            }
+            // fall back to unsplit tiles when the counters would not fit
+            if (ps > 1 && (int64_t)num_reqs * g->num_kv_heads + base > pa::kMaxCounters)
+                ps = 1;
+        }
+    }
+    plan->prefill_splits = plan->prefill_tiles > 0 ? ps : 0;
+    const pa::WorkspaceLayout ws = pa::workspace_layout(num_reqs, max_splits, g->num_q_heads, g->num_kv_heads,
+                                                        plan->prefill_tiles, plan->prefill_splits);
+    if (ws.counters_used > pa::kMaxCounters)
+        return PA_ERR_UNSUPPORTED;   // more completion counters than the workspace holds
+    plan->workspace_bytes = ws.total;
     return PA_OK;
 }
 

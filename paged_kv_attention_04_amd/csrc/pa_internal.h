@@ -13,7 +13,9 @@ constexpr int kBlock = 16;      // tokens per KV block
 constexpr int kGroup = 4;       // query heads per KV head (grouped-query attention)
 constexpr int kDecodeWaves = 8;       // wavefronts per decode workgroup
 constexpr int kMaxSplitBlocks = 64 * kDecodeWaves;   // one block id per lane of each wavefront
-constexpr int kPrefillQ = 16;   // new tokens per prefill tile (x kGroup heads = 64 MFMA rows)
+constexpr int kPrefillQ = 32;   // new tokens per prefill tile (x kGroup heads = 128 MFMA rows)
+constexpr int kPrefillKeys = 128;     // keys per prefill step (eight blocks)
+constexpr int kMaxPrefillSplits = 64; // most key splits of one prefill tile
 
 inline bool geometry_supported(const pa_geometry* g)
 {
@@ -23,29 +25,54 @@ inline bool geometry_supported(const pa_geometry* g)
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace of a batch whose decode rows are split:
-//   [0, 64 KiB)   uint32 completion counters, one per (row, KV head); zero before the
-//                 first use of the buffer, and every call leaves them zero again
-//   part_o        normalised FP32 split outputs [num_reqs][max_splits][Hq][head_dim]
+// Workspace of a batch whose decode rows or prefill tiles are split:
+//   [0, 64 KiB)   uint32 completion counters: decode (row, KV head) pairs at r * Hkv + kvh,
+//                 prefill (tile, KV head) pairs after them at num_reqs * Hkv + tile * Hkv + kvh;
+//                 zero before the first use of the buffer, and every call leaves them zero
+//   part_o        normalised FP32 decode split outputs [num_reqs][max_splits][Hq][head_dim]
 //   part_lse      per-split log2-sum-exp [num_reqs][max_splits][Hq]
+//   pf_part_o     normalised FP32 prefill split outputs, 128 x 128 floats per (tile, KV head,
+//                 split), in the order the prefill kernel's lanes hold them
+//   pf_part_lse   their log2-sum-exp, 512 floats per (tile, KV head, split), also in lane order
 // The counters sit at a fixed place so that no call's partials ever land on them.
 constexpr size_t kCounterBytes = 64 * 1024;
 constexpr int64_t kMaxCounters = kCounterBytes / sizeof(uint32_t);
+constexpr int64_t kPrefillPartFloats = (int64_t)kPrefillQ * kGroup * kHeadDim;
+// one log2-sum-exp per lane of each row group's two row blocks: 4 x 2 x 64 (each row's
+// value is held by its four k-slice lanes)
+constexpr int64_t kPrefillPartLseFloats = 4 * 2 * 64;
 
 struct WorkspaceLayout {
-    size_t counters = 0, part_o = 0, part_lse = 0, total = 0;
+    size_t counters = 0, part_o = 0, part_lse = 0, pf_part_o = 0, pf_part_lse = 0, total = 0;
+    int64_t pf_counter_base = 0;   // index of the first prefill counter
+    int64_t counters_used = 0;     // counters the layout needs
 };
 
-inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, int32_t num_q_heads)
+inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t prefill_tiles, int32_t prefill_splits)
 {
     WorkspaceLayout w;
-    if (max_splits <= 1 || num_reqs <= 0)
+    const bool decode = max_splits > 1 && num_reqs > 0;
+    const bool prefill = prefill_splits > 1 && prefill_tiles > 0;
+    if (!decode && !prefill)
         return w;
-    size_t n = (size_t)num_reqs * (size_t)max_splits * (size_t)num_q_heads;
-    w.counters = 0;
-    w.part_o = kCounterBytes;
-    w.part_lse = align256(w.part_o + n * kHeadDim * sizeof(float));
-    w.total = align256(w.part_lse + n * sizeof(float));
+    w.pf_counter_base = (int64_t)num_reqs * num_kv_heads;
+    w.counters_used = prefill ? w.pf_counter_base + (int64_t)prefill_tiles * num_kv_heads
+                              : (int64_t)num_reqs * num_kv_heads;
+    size_t at = kCounterBytes;
+    if (decode) {
+        const size_t n = (size_t)num_reqs * (size_t)max_splits * (size_t)num_q_heads;
+        w.part_o = at;
+        w.part_lse = align256(w.part_o + n * kHeadDim * sizeof(float));
+        at = align256(w.part_lse + n * sizeof(float));
+    }
+    if (prefill) {
+        const size_t n = (size_t)prefill_tiles * (size_t)num_kv_heads * (size_t)prefill_splits;
+        w.pf_part_o = at;
+        w.pf_part_lse = align256(w.pf_part_o + n * (size_t)kPrefillPartFloats * sizeof(float));
+        at = align256(w.pf_part_lse + n * (size_t)kPrefillPartLseFloats * sizeof(float));
+    }
+    w.total = at;
     return w;
 }
 

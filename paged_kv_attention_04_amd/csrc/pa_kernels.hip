@@ -16,6 +16,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace {
@@ -530,19 +532,24 @@ struct PrefillParams {
     const int32_t* kv_len;
     uint16_t* out;
     float* lse;
+    uint32_t* counters;         // one per (tile, KV head); used when splits > 1
+    float* part_o;              // split partials, kPfRows * kHeadDim floats per (tile, KV head, split)
+    float* part_lse;            // 4 x 2 x 64 floats (lane order) per (tile, KV head, split)
     int32_t max_blocks;
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t num_blocks;
     int32_t num_prefill_rows;
+    int32_t splits;             // key splits per tile
     float scale_log2;
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];
     int32_t tile_start[PA_MAX_PREFILL_ROWS + 1];
 };
 
-constexpr int kPfKeys = 128;               // keys per step: eight 16-token blocks
-constexpr int kPfWaves = 8;                // 2 row groups x 4 key quarters
-constexpr int kPfRows = pa::kPrefillQ * kGroup;   // 64 MFMA rows: (token, head) pairs
+constexpr int kPfKeys = pa::kPrefillKeys;  // keys per step: eight 16-token blocks
+constexpr int kPfWaves = 8;                // 4 row groups x 2 key halves
+constexpr int kPfRows = pa::kPrefillQ * kGroup;   // 128 MFMA rows: (token, head) pairs
+constexpr int kPfAcc = 16;                 // f32x4 O^T accumulators per lane: 2 row blocks x 8 dim blocks
 constexpr int kTileChunks = kPfKeys * kHeadDim * 2 / 16;   // 16-byte chunks in one K or V tile
 
 // Swizzle of the 16-byte chunk index inside a staged K / V tile row (one key, 256 bytes).
@@ -570,48 +577,122 @@ __device__ inline uint2 lds_read_tr16(const void* p)
     return __builtin_bit_cast(uint2, v);
 }
 
-// One 32-key step of a prefill wavefront (two row blocks of 16 rows): S^T = K Q^T, the
-// online softmax, O^T += V^T P^T.  The running maximum is raised lazily: a lane compares
-// its own scores with the row's running maximum plus kRescaleSlack, and only when some
-// lane's score passes it does the wavefront take the row maxima across its lanes and
-// rescale O and the denominators; otherwise no cross-lane exchange is needed.
-__device__ __forceinline__ void pf_step(const bf16x8 (&kop)[2][4], const bf16x8 (&qop)[2][4], const bf16x8 (&vop)[8],
-                                        f32x4 (&oacc)[2][8], float (&m)[2], float (&lsum)[2], bool need_mask, int key0,
-                                        int kslice, const int (&qpos)[2], int kv_hi, float scale_log2)
+// Largest of three floats, NaN-propagating (v_maximum3_f32); the scores are never NaN on
+// a valid row, and fmaxf would add a canonicalising instruction per input.
+__device__ inline float max3f(float a, float b, float c)
 {
-    f32x4 sacc[2][2];
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+static_assert(4 * kPfAcc * 4 * 64 == pa::kPrefillPartFloats, "prefill partial size differs from the workspace's");
+static_assert(4 * 2 * 64 == pa::kPrefillPartLseFloats, "prefill partial LSE size differs from the workspace's");
+
+template <int N>
+struct BufSel {
+    static constexpr int value = N;
+};
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x2;
+constexpr int kSchedMfma = 0x8;
+constexpr int kSchedVmemRead = 0x20;
+constexpr int kSchedDsRead = 0x100;
+
+// exp2 of eight scores (a 32-key chunk of one row block) against the running maximum,
+// packed as that chunk's P^T operand; returns their sum.  Chunk c's operand holds this
+// lane's keys 32 c + 4 kslice + 0..3 and 32 c + 16 + 4 kslice + 0..3, i.e. x[8 c .. 8 c + 7].
+__device__ __forceinline__ float pf_exp8(const float* x, float neg_m, float scale_log2, bf16x8& pb)
+{
+    float pe[8];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int i = 0; i < 8; ++i)
+        pe[i] = fast_exp2(fmaf(x[i], scale_log2, neg_m));
+    pb = __builtin_bit_cast(bf16x8, u32x4{pack_bf16(pe[0], pe[1]), pack_bf16(pe[2], pe[3]), pack_bf16(pe[4], pe[5]),
+                                          pack_bf16(pe[6], pe[7])});
+    return ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+}
+
+// Transposed V operand of 32-key chunk c: v_addr[db] is this lane's byte offset for dim
+// block db; the chunk adds 8 KiB and its upper 16 keys another 4 KiB.
+__device__ __forceinline__ void pf_read_v(const char* vt, const int (&v_addr)[8], int c, bf16x8 (&vop)[8])
+{
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+    for (int db = 0; db < 8; ++db) {
+        const uint2 lo = lds_read_tr16(vt + v_addr[db] + c * 8192);
+        const uint2 hi = lds_read_tr16(vt + v_addr[db] + c * 8192 + 4096);
+        vop[db] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
+}
+
+// One 64-key half step of a prefill wavefront (two row blocks rb of 16 rows): S^T = K Q^T,
+// the online softmax, O^T += V^T P^T.  The running maximum is raised lazily: a lane
+// compares its own scores with the row's running maximum plus kRescaleSlack, and only
+// when some lane's score passes it does the wavefront take the row maxima across its
+// lanes and rescale O and the denominators; otherwise no cross-lane exchange is needed.
+//
+// Instruction order within the step (fixed with scheduling-group barriers): the S^T
+// products go out interleaved with the transposed reads of V's first 32-key chunk; after
+// the maxima and the rescale test come the first chunk's exponentials (both row blocks),
+// the first chunk's PV products interleaved with the second chunk's V reads and
+// exponentials, and the second chunk's PV products with the denominator sums.
+// The matrix unit thus stays busy while the wavefront works through the softmax.
+// kMask: the step holds keys past some row's position or past kv_hi.
+template <bool kMask>
+__device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* vt, const int (&v_addr)[8],
+                                        const bf16x8 (&qop)[2][4], f32x4 (&oacc)[2][8], float (&m)[2],
+                                        float (&lsum)[2], int key0, int kslice, const int (&qpos)[2], int kv_hi,
+                                        float scale_log2)
+{
+    bf16x8 v0[8];
+    pf_read_v(vt, v_addr, 0, v0);
+    // key block by key block, so that each K operand is dead once both row blocks used it
+    f32x4 sacc[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
             sacc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 sacc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][ks], qop[rb][ks], sacc[rb][kb], 0, 0, 0);
         }
-    float x[2][8];
+    // x[rb][4 kb + e] is the score of key key0 + 16 kb + 4 kslice + e for this lane's row
+    float x[2][16];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 x[rb][4 * kb + e] = sacc[rb][kb][e];
-    if (need_mask) {                              // wavefront-uniform: diagonal and tail steps only
+    if constexpr (kMask) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 16; ++i) {
                 const int key = key0 + 16 * (i >> 2) + 4 * kslice + (i & 3);
                 x[rb][i] = (key > qpos[rb] || key >= kv_hi) ? -INFINITY : x[rb][i];
             }
     }
     float lmax[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-        lmax[rb] = fmaxf(fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3])),
-                         fmaxf(fmaxf(x[rb][4], x[rb][5]), fmaxf(x[rb][6], x[rb][7]))) * scale_log2;
-    if (__any(lmax[0] > m[0] + kRescaleSlack || lmax[1] > m[1] + kRescaleSlack)) {
+    for (int rb = 0; rb < 2; ++rb) {
+        const float a = max3f(x[rb][0], x[rb][1], x[rb][2]);
+        const float b = max3f(x[rb][3], x[rb][4], x[rb][5]);
+        const float c = max3f(x[rb][6], x[rb][7], x[rb][8]);
+        const float d = max3f(x[rb][9], x[rb][10], x[rb][11]);
+        const float e = max3f(x[rb][12], x[rb][13], x[rb][14]);
+        lmax[rb] = max3f(max3f(a, b, c), max3f(d, e, x[rb][15]), -INFINITY) * scale_log2;
+    }
+    const bool raise = lmax[0] > m[0] + kRescaleSlack || lmax[1] > m[1] + kRescaleSlack;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 16, 0);     // K operand reads
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 9, 0);    // next step's copies
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    if (__any(raise)) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             float t = fmaxf(lmax[rb], shfl_xor(lmax[rb], 16));
@@ -626,36 +707,60 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[2][4], const bf16x8 
             }
         }
     }
-    bf16x8 pb[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        // with no visible key yet every score is -inf and any finite offset gives 0
-        const float neg_m = (m[rb] == -INFINITY) ? 0.f : -m[rb];
-        float pe[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            pe[i] = fast_exp2(fmaf(x[rb][i], scale_log2, neg_m));
-        lsum[rb] += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-        pb[rb] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16(pe[0], pe[1]), pack_bf16(pe[2], pe[3]),
-                                                  pack_bf16(pe[4], pe[5]), pack_bf16(pe[6], pe[7])});
-    }
+    // with no visible key yet every score is -inf and any finite offset gives 0
+    const float nm0 = (m[0] == -INFINITY) ? 0.f : -m[0];
+    const float nm1 = (m[1] == -INFINITY) ? 0.f : -m[1];
+    bf16x8 p00, p10, p01, p11;                                       // p<rb><chunk>
+    float s0 = pf_exp8(&x[0][0], nm0, scale_log2, p00);
+    float s1 = pf_exp8(&x[1][0], nm1, scale_log2, p10);
+    bf16x8 v1[8];
+    pf_read_v(vt, v_addr, 1, v1);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-        oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[0], oacc[0][db], 0, 0, 0);
-        oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[db], pb[1], oacc[1][db], 0, 0, 0);
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0[db], p00, oacc[0][db], 0, 0, 0);
+        oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0[db], p10, oacc[1][db], 0, 0, 0);
+    }
+    s0 += pf_exp8(&x[0][8], nm0, scale_log2, p01);
+    s1 += pf_exp8(&x[1][8], nm1, scale_log2, p11);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1[db], p01, oacc[0][db], 0, 0, 0);
+        oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1[db], p11, oacc[1][db], 0, 0, 0);
+    }
+    lsum[0] += s0;
+    lsum[1] += s1;
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 24, 0);       // first chunk's exponentials
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {                                   // with the second chunk's V reads
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
     }
 }
 
-// Workgroup of eight wavefronts per (prefill row, KV head, tile of 16 new tokens).  The
-// tile's 64 MFMA rows are (token, head) pairs, row = 4 * token + head, so the four query
-// heads of a group share every K / V tile.  Wavefront w owns rows 32 (w % 2) .. +32 and
-// keys 32 (w / 2) .. +32 of every 128-key step; the four key quarters of a row are merged
-// through LDS at the end by the log-sum-exp rule.
+// Workgroup of eight wavefronts per (prefill row, 32-token query tile, KV head, key split).
+// The tile's 128 MFMA rows are (token, head) pairs, row = 4 * token + head, so the four
+// query heads of a group share every K / V tile.  Wavefront w owns rows 32 (w % 4) .. +32
+// and keys 64 (w / 4) .. +64 of every 128-key step; the two wavefronts that share a SIMD
+// hold the same rows.  Their two key halves are merged through LDS at the end, lane by
+// lane, by the log-sum-exp rule.
+//
+// Key splits: the tile's causal key range, ceil(kv_hi / 128) steps, is cut into `splits`
+// contiguous step ranges, one workgroup each.  With one split the workgroup writes the
+// output; otherwise each writes its normalised partial and log2-sum-exp to the workspace
+// with agent-scope stores and counts itself in, and the last one merges all partials.
 //
 // K / V staging: all eight wavefronts copy one step's eight blocks (one block each, K and
-// V, 8 KiB) straight from the pool into LDS with global_load_lds_dwordx4, double-buffered:
-// the copy of step s + 1 runs while step s is computed.  Slots past kv_len are filled
-// from a valid slot of the same block, so every staged value is finite.
+// V, 8 KiB) straight from the pool into LDS with global_load_lds_dwordx4, double-buffered
+// in two named buffer pairs: the copy of step s + 1 is issued right after the K operand
+// reads of step s, and since it targets the other pair, the transposed V reads of step s
+// need not wait for it.  Slots past kv_len are filled from a valid slot of the same
+// block, so every staged value is finite.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][k-slice l/16] and
 // B[k-slice l/16][l%16] (8 bf16 each) and receives D[4*(l/16) + e][l%16], e = 0..3.
@@ -663,20 +768,26 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[2][4], const bf16x8 
 //   O^T (dims x rows) += V^T (dims x keys) . P^T (keys x rows)       contraction over keys
 // Each lane's S^T values all belong to one row, so softmax statistics and the rescaling of
 // O^T stay lane-local except for one exchange across the four k-slices.  In PV lane l's
-// eight keys are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of its 32-key quarter: exactly
-// the S^T values it holds; the V^T operand is read with the same key order by two
+// eight keys of chunk c are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of the chunk:
+// exactly S^T values it holds; the V^T operand is read with the same key order by two
 // transposed LDS reads, and a contraction does not care how its index is permuted.
 __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
 {
-    __shared__ __attribute__((aligned(1024))) u32x4 tiles[2][2][kTileChunks];   // [buffer][K, V]
-    __shared__ float m_part[4][kPfRows];
-    __shared__ float l_part[4][kPfRows];
+    __shared__ __attribute__((aligned(1024))) u32x4 k_tile0[kTileChunks];
+    __shared__ __attribute__((aligned(1024))) u32x4 v_tile0[kTileChunks];
+    __shared__ __attribute__((aligned(1024))) u32x4 k_tile1[kTileChunks];
+    __shared__ __attribute__((aligned(1024))) u32x4 v_tile1[kTileChunks];
+    __shared__ float x_m[4][2][64];     // key-half merge: running maxima of the kh = 1 wavefronts
+    __shared__ float x_l[4][2][64];     // and their lane-partial denominators
+    __shared__ int last_lds;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int rg = wave & 1, kq = wave >> 1;
+    const int rg = wave & 3, kh = wave >> 2;
     const int kvh = blockIdx.x % p.num_kv_heads;
-    const int tile = blockIdx.x / p.num_kv_heads;
+    const int rest = blockIdx.x / p.num_kv_heads;
+    const int split = rest % p.splits;
+    const int tile = rest / p.splits;
     int pr = 0;
     while (pr + 1 < p.num_prefill_rows && p.tile_start[pr + 1] <= tile)
         ++pr;
@@ -686,33 +797,33 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     const int qlen = p.qo_indptr[r + 1] - q0;
     const int kvlen = p.kv_len[r];
     const int head0 = kvh * kGroup;
-    if (qt * pa::kPrefillQ >= qlen)
+    if (qt * pa::kPrefillQ >= qlen)             // the same for every split of the tile
         return;
     const int ctx = kvlen - qlen;               // tokens before this chunk
     const int nblk_row = (kvlen + kBlock - 1) / kBlock;
     const bool bad_row = qlen < 2 || ctx < 0 || nblk_row > p.max_blocks;
     // keys any token of this tile can see: 0 .. ctx + last token of the tile
     const int kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * pa::kPrefillQ));
-    const int nsteps = (kv_hi + kPfKeys - 1) / kPfKeys;
+    const int nsteps_tile = (kv_hi + kPfKeys - 1) / kPfKeys;
+    const int s_begin = split * nsteps_tile / p.splits;
+    const int nsteps = (split + 1) * nsteps_tile / p.splits - s_begin;
 
     const int row16 = lane & 15, kslice = lane >> 4;
-    const int qpos_first = ctx + qt * pa::kPrefillQ + 8 * rg;   // smallest position of this wavefront's rows
     // this lane's two rows (row blocks rb = 0, 1)
-    int tok_local[2], qpos[2];
+    int qpos[2];
     bf16x8 qop[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int rho = 32 * rg + 16 * rb + row16;
-        tok_local[rb] = qt * pa::kPrefillQ + (rho >> 2);
-        qpos[rb] = ctx + tok_local[rb];
-        const bool ok = tok_local[rb] < qlen;
+        const int tl = qt * pa::kPrefillQ + (rho >> 2);
+        qpos[rb] = ctx + tl;
+        const bool ok = tl < qlen;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
             if (ok)
                 v = *reinterpret_cast<const u32x4*>(
-                    p.q + ((int64_t)(q0 + tok_local[rb]) * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + ks * 32 +
-                    kslice * 8);
+                    p.q + ((int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + ks * 32 + kslice * 8);
             qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -726,36 +837,62 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     // Table entry of block `wave` of step s (the row's first block if the step runs past
     // the row).  It is range-checked only where it is used, one step later, so that the
     // load does not hold up the copies issued just before it.
-    auto table_entry = [&](int s) {
+    auto table_entry = [&](int s) __attribute__((always_inline)) {
         const int b = s * (kPfKeys / kBlock) + wave;
         return bt[b < nblk_row ? b : 0];
     };
-    auto checked = [&](int id) {
+    auto checked = [&](int id) __attribute__((always_inline)) {
         if (id < 0 || id >= p.num_blocks) {
             bad = true;
             id = 0;
         }
         return id;
     };
-    // Wavefront w copies block w of step s: 16 keys = four 1 KiB LDS rows-of-four, for K and V.
-    auto stage = [&](int s, int buf, int id) {
-        const int key_in_blk = lane >> 4;
+    // Wavefront w copies block w of step s: 16 keys = four 1 KiB LDS rows-of-four, for K
+    // and V.  Copy i of lane l moves 16 bytes of token 4 i + l / 16 of the block (element
+    // offset cp_off[i]); in the row's last step, slots past kv_len take token 0's bytes
+    // (cp_tail[i]), so that every staged value is finite.
+    int cp_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = 4 * i + (lane >> 4);
+        const int chunk = (lane & 15) ^ pf_swz(tok);      // pf_swz sees only the key's low four bits
+        cp_off[i] = tok * kHeadDim + chunk * 8;            // token 0's offset is cp_off[i] % kHeadDim
+    }
+    auto stage = [&](auto sel, int s, int id) __attribute__((always_inline)) {
+        u32x4* kd = decltype(sel)::value == 0 ? k_tile0 : k_tile1;
+        u32x4* vd = decltype(sel)::value == 0 ? v_tile0 : v_tile1;
+        const int64_t base = (int64_t)id * blk_stride + kvh_off;
+        const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * wave + 4 * i + key_in_blk;            // key within the step
-            const int tok = 4 * i + key_in_blk;                         // token within the block
-            const int key = s * kPfKeys + row;
-            const int src_tok = key < kvlen ? tok : 0;
-            const int chunk = (lane & 15) ^ pf_swz(row);
-            const int64_t off = id * blk_stride + kvh_off + src_tok * kHeadDim + chunk * 8;
-            __builtin_amdgcn_global_load_lds(p.k_pool + off,
-                                             (__attribute__((address_space(3))) void*)&tiles[buf][0][(16 * wave + 4 * i) * 16],
+            const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
+            __builtin_amdgcn_global_load_lds(p.k_pool + base + off,
+                                             (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16],
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds(p.v_pool + off,
-                                             (__attribute__((address_space(3))) void*)&tiles[buf][1][(16 * wave + 4 * i) * 16],
+            __builtin_amdgcn_global_load_lds(p.v_pool + base + off,
+                                             (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16],
                                              16, 0, 0);
         }
     };
+    // LDS byte offsets of this lane's operand reads within a K or V tile.  K: key
+    // 64 kh + 16 kb + row16, chunk 4 ks + kslice (kb adds 4 KiB).  V: source lane i16 of
+    // group kslice points at key 4 kslice + i16/4 (+16) of chunk c, dims 16 db + 4 (i16 % 4)
+    // .. +4, and lane (kslice, i16) receives dim 16 db + i16 of keys 4 kslice + 0..3 (+16)
+    // (c adds 8 KiB, +16 keys 4 KiB).
+    int k_addr[4], v_addr[8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        k_addr[ks] = (64 * kh + row16) * 256 + (((ks * 4 + kslice) ^ pf_swz(row16)) << 4);
+    {
+        const int i16 = lane & 15;
+        const int k_lo = 64 * kh + 4 * kslice + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int cc = 2 * db + ((i16 & 3) >> 1);
+            v_addr[db] = k_lo * 256 + ((cc ^ pf_swz(k_lo)) << 4) + ((i16 & 1) << 3);
+        }
+    }
 
     f32x4 oacc[2][8];
 #pragma unroll
@@ -765,111 +902,203 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
             oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
-    // Workgroups of neighbouring query tiles start their key loop one step apart, so at
-    // any time each K / V step is fetched from memory by one workgroup and found in the
-    // XCD's L2 by the others (all tiles of one KV head run on one XCD).
-    const int rot = nsteps > 0 ? qt % nsteps : 0;
-    auto step_at = [&](int i) { return i + rot < nsteps ? i + rot : i + rot - nsteps; };
+    // Step order: the steps no row of the tile needs masked first, rotated so that
+    // workgroups of neighbouring query tiles start one step apart (at any time each K / V
+    // step is then fetched from memory by one workgroup and found in the XCD's L2 by the
+    // others: all tiles of one KV head run on one XCD), then the diagonal and tail steps.
+    const int qmin = ctx + qt * pa::kPrefillQ;              // smallest query position of the tile
+    const int s_masked = max(s_begin, min(s_begin + nsteps, (qmin + 1) / kPfKeys));
+    const int n_plain = s_masked - s_begin;
+    const int rot = n_plain > 0 ? qt % n_plain : 0;
+    auto step_at = [&](int i) __attribute__((always_inline)) {
+        i = min(i, nsteps - 1);
+        return i >= n_plain ? s_begin + i : s_begin + (i + rot < n_plain ? i + rot : i + rot - n_plain);
+    };
     int next_id = 0;
-    if (nsteps > 0)
-        stage(step_at(0), 0, checked(table_entry(step_at(0))));
-    if (nsteps > 1)
+    if (nsteps > 0) {
+        stage(BufSel<0>{}, step_at(0), checked(table_entry(step_at(0))));
         next_id = table_entry(step_at(1));
-    for (int it = 0; it < nsteps; ++it) {
-        const int s = step_at(it);
-        const int buf = it & 1;
-        wait_vmcnt<0>();                       // this wavefront's copies of this step have landed
-        __builtin_amdgcn_s_barrier();          // everyone's have, and the previous step is finished
-        const u32x4* kt = tiles[buf][0];
-        const char* vt = reinterpret_cast<const char*>(tiles[buf][1]);
-
-        // All of this step's LDS operands are read before the next copy is issued, so no
-        // LDS read is ever outstanding next to a copy into the other buffer.
-        bf16x8 kop[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int key = 32 * kq + 16 * kb + row16;
-                kop[kb][ks] = __builtin_bit_cast(bf16x8, kt[key * 16 + ((ks * 4 + kslice) ^ pf_swz(key))]);
-            }
-        bf16x8 vop[8];
-        {
-            const int i16 = lane & 15;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                // source lane i16 of group kslice points at key 4 kslice + i16/4 (+16), dims
-                // 16 db + 4 (i16 % 4) .. +4; lane (kslice, i16) receives dim 16 db + i16 of
-                // keys 4 kslice + 0..3 (+16)
-                const int c = 2 * db + ((i16 & 3) >> 1);
-                const int k_lo = 32 * kq + 4 * kslice + (i16 >> 2);
-                const int k_hi = k_lo + 16;
-                const uint2 lo = lds_read_tr16(vt + k_lo * 256 + ((c ^ pf_swz(k_lo)) << 4) + ((i16 & 1) << 3));
-                const uint2 hi = lds_read_tr16(vt + k_hi * 256 + ((c ^ pf_swz(k_hi)) << 4) + ((i16 & 1) << 3));
-                vop[db] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-            }
-        }
-        if (it + 1 < nsteps) {
-            stage(step_at(it + 1), buf ^ 1, checked(next_id));
-            if (it + 2 < nsteps)
-                next_id = table_entry(step_at(it + 2));
-        }
-
-        const int key0 = s * kPfKeys + 32 * kq;
-        // wavefront-uniform: the wavefront's first row has the smallest position
-        const bool need_mask = key0 + 31 >= kv_hi || key0 + 31 > qpos_first;
-        pf_step(kop, qop, vop, oacc, m, lsum, need_mask, key0, kslice, qpos, kv_hi, p.scale_log2);
     }
 
-    // merge the four key quarters of every row through LDS (the tile buffers are free now)
+    auto do_step = [&](auto sel, auto msk, int it) __attribute__((always_inline)) {
+        constexpr int B = decltype(sel)::value;
+        const char* kt = reinterpret_cast<const char*>(B == 0 ? k_tile0 : k_tile1);
+        const char* vt = reinterpret_cast<const char*>(B == 0 ? v_tile0 : v_tile1);
+        const int s = step_at(it);
+        // This wavefront's copies of this step have landed and its LDS reads of the previous
+        // step have returned; after the barrier everyone's have.  The memory clobber keeps
+        // the compiler from moving any memory access across; register-only work of the
+        // previous step may still drift past it.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        bf16x8 kop[4][4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kop[kb][ks] = *reinterpret_cast<const bf16x8*>(kt + k_addr[ks] + kb * 4096);
+        // Next step's copy (the last step repeats its own; nothing reads that copy) into
+        // the other buffer pair, which every wavefront finished reading in the previous
+        // step.  Its table entry was loaded one step ago and has landed; the empty asm
+        // keeps it in a vector register until here, since moving it to a scalar one at
+        // its load would make the load wait for all of this wavefront's copies.
+        {
+            int id = next_id;
+            asm volatile("" : "+v"(id));
+            stage(BufSel<B ^ 1>{}, step_at(it + 1), checked(__builtin_amdgcn_readfirstlane(id)));
+            next_id = table_entry(step_at(it + 2));
+        }
+        pf_step<decltype(msk)::value>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + 64 * kh, kslice, qpos, kv_hi,
+                                      p.scale_log2);
+    };
+    // Steps alternate between the two buffer pairs; each loop is unrolled by two so that
+    // every LDS access names its buffer statically.
+    auto run = [&](auto msk, int it, int it_end) __attribute__((always_inline)) {
+        if (it < it_end && (it & 1)) {
+            do_step(BufSel<1>{}, msk, it);
+            ++it;
+        }
+        for (; it + 1 < it_end; it += 2) {
+            do_step(BufSel<0>{}, msk, it);
+            do_step(BufSel<1>{}, msk, it + 1);
+        }
+        if (it < it_end)
+            do_step(BufSel<0>{}, msk, it);
+    };
+    run(std::integral_constant<bool, false>{}, 0, n_plain);
+    run(std::integral_constant<bool, true>{}, n_plain, nsteps);
+    wait_vmcnt<0>();                           // the last step's spare copy
+
+    // merge the two key halves: the kh = 1 wavefronts hand (m, lane-partial l, O^T) to the
+    // kh = 0 wavefront with the same rows, in the lanes' own layout
     __syncthreads();
-    float* o_part = reinterpret_cast<float*>(&tiles[0][0][0]);   // [4][64 rows][128 dims] = 128 KiB
+    u32x4* xo = (rg < 2 ? k_tile0 : v_tile0) + (rg & 1) * (kPfAcc * 64);
+    if (kh == 1) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int rho = 32 * rg + 16 * rb + row16;
-        float ltot = lsum[rb];
-        ltot += shfl_xor(ltot, 16);
-        ltot += shfl_xor(ltot, 32);
+        for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-            *reinterpret_cast<f32x4*>(&o_part[(kq * kPfRows + rho) * kHeadDim + db * 16 + 4 * kslice]) = oacc[rb][db];
-        if (kslice == 0) {
-            m_part[kq][rho] = m[rb];
-            l_part[kq][rho] = ltot;
+            for (int db = 0; db < 8; ++db)
+                xo[(rb * 8 + db) * 64 + lane] = __builtin_bit_cast(u32x4, oacc[rb][db]);
+            x_m[rg][rb][lane] = m[rb];
+            x_l[rg][rb][lane] = lsum[rb];
         }
     }
     bad = __syncthreads_or(bad);
-
-    {
-        const int rho = tid >> 3, d0 = (tid & 7) * 16;
-        const int tl = qt * pa::kPrefillQ + (rho >> 2);
-        if (tl < qlen) {
-            float M = -INFINITY;
+    const float nan = __builtin_nanf("");
+    float lse2[2] = {-INFINITY, -INFINITY};     // log2-sum-exp of this workgroup's keys per row
+    if (kh == 0) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                M = fmaxf(M, m_part[k][rho]);
-            float w[4], L = 0.f;
+        for (int rb = 0; rb < 2; ++rb) {
+            const float m1 = x_m[rg][rb][lane], l1 = x_l[rg][rb][lane];
+            const float M = fmaxf(m[rb], m1);
+            const float w0 = (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - M);
+            const float w1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
+            float l = w0 * lsum[rb] + w1 * l1;
+            l += shfl_xor(l, 16);
+            l += shfl_xor(l, 32);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                w[k] = (m_part[k][rho] == -INFINITY) ? 0.f : fast_exp2(m_part[k][rho] - M);
-                L += w[k] * l_part[k][rho];
-            }
-            const float inv = bad ? __builtin_nanf("") : 1.f / L;
-            uint16_t* orow = p.out + ((int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + d0;
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    o += w[k] * *reinterpret_cast<const f32x4*>(&o_part[(k * kPfRows + rho) * kHeadDim + d0 + 4 * c4]);
-                *reinterpret_cast<u32x2*>(orow + 4 * c4) =
-                    u32x2{pack_bf16(o[0] * inv, o[1] * inv), pack_bf16(o[2] * inv, o[3] * inv)};
-            }
-            if ((tid & 7) == 0)
-                p.lse[(int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3)] =
-                    bad ? __builtin_nanf("") : (M + fast_log2(L)) * kLn2;
+            for (int db = 0; db < 8; ++db)
+                oacc[rb][db] = (w0 * oacc[rb][db] + w1 * __builtin_bit_cast(f32x4, xo[(rb * 8 + db) * 64 + lane])) * inv;
+            lse2[rb] = bad ? nan : (l > 0.f ? M + fast_log2(l) : -INFINITY);
         }
     }
+
+    // output: lane l holds O^T[16 db + 4 kslice + e][row row16] of row block rb
+    auto write_out = [&](const f32x4 (&o)[2][8], const float (&lse_row)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int rho = 32 * rg + 16 * rb + row16;
+            const int tl = qt * pa::kPrefillQ + (rho >> 2);
+            if (tl >= qlen)
+                continue;
+            const bool nan_row = lse_row[rb] != lse_row[rb];
+            const int64_t orow = ((int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3));
+            uint16_t* dst = p.out + orow * kHeadDim + 4 * kslice;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const f32x4 v = nan_row ? f32x4{nan, nan, nan, nan} : o[rb][db];
+                *reinterpret_cast<u32x2*>(dst + 16 * db) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+            }
+            if (kslice == 0)
+                p.lse[orow] = lse_row[rb] * kLn2;
+        }
+    };
+
+    if (p.splits == 1) {
+        if (kh == 0)
+            write_out(oacc, lse2);
+        return;
+    }
+
+    // Partials are written with agent-scope stores (coherent across the XCDs' separate L2
+    // caches) and every thread waits until its stores have completed before the
+    // workgroup counts itself in; the last split reads them with agent-scope loads.
+    const int64_t item0 = ((int64_t)tile * p.num_kv_heads + kvh) * p.splits;   // split 0 of this (tile, KV head)
+    auto part_o_at = [&](int sp) __attribute__((always_inline)) { return p.part_o + ((item0 + sp) * 4 + rg) * (kPfAcc * 4 * 64); };
+    auto part_lse_at = [&](int sp) __attribute__((always_inline)) { return p.part_lse + ((item0 + sp) * 4 + rg) * 128; };   // 2 x 64 per row group
+    if (kh == 0) {
+        float* po = part_o_at(split);
+#pragma unroll
+        for (int i = 0; i < kPfAcc; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                store_agent(po + (i * 4 + e) * 64 + lane, oacc[i >> 3][i & 7][e]);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            store_agent(part_lse_at(split) + rb * 64 + lane, lse2[rb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    uint32_t* counter = p.counters + (int64_t)tile * p.num_kv_heads + kvh;
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = done == (uint32_t)(p.splits - 1);
+        if (last)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+        last_lds = last;
+    }
+    __syncthreads();
+    if (!last_lds || kh != 0)
+        return;
+
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        float L = lse2[rb];
+        bool any_nan = lse2[rb] != lse2[rb];
+        for (int sp = 0; sp < p.splits; ++sp) {
+            const float ls = sp == split ? lse2[rb] : load_agent(part_lse_at(sp) + rb * 64 + lane);
+            any_nan |= ls != ls;
+            L = fmaxf(L, ls);
+        }
+        float wsum = 0.f;
+        f32x4 acc[8];
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < p.splits; ++sp) {
+            const float ls = sp == split ? lse2[rb] : load_agent(part_lse_at(sp) + rb * 64 + lane);
+            const float c = (ls == -INFINITY || any_nan) ? 0.f : fast_exp2(ls - L);
+            wsum += c;
+            if (sp == split) {
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    acc[db] += c * oacc[rb][db];
+            } else if (c != 0.f) {
+                const float* po = part_o_at(sp);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[db][e] += c * load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
+            }
+        }
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            oacc[rb][db] = acc[db] * inv;
+        lse2[rb] = any_nan ? nan : (wsum > 0.f ? L + fast_log2(wsum) : -INFINITY);
+    }
+    write_out(oacc, lse2);
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -917,11 +1146,15 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         return PA_ERR_NULL;
     if (max_blocks_per_req < 1 || plan->num_prefill_rows > PA_MAX_PREFILL_ROWS)
         return PA_ERR_SHAPE;
-    const pa::WorkspaceLayout ws = pa::workspace_layout(plan->num_reqs, plan->max_splits, g->num_q_heads);
+    if (plan->prefill_tiles > 0 && (plan->prefill_splits < 1 || plan->prefill_splits > pa::kMaxPrefillSplits))
+        return PA_ERR_SHAPE;
+    const pa::WorkspaceLayout ws = pa::workspace_layout(plan->num_reqs, plan->max_splits, g->num_q_heads,
+                                                        g->num_kv_heads, plan->prefill_tiles, plan->prefill_splits);
     if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))
         return PA_ERR_WORKSPACE;
-    if (ws.total > 0 && (int64_t)plan->num_reqs * g->num_kv_heads > pa::kMaxCounters)
+    if (ws.counters_used > pa::kMaxCounters)
         return PA_ERR_UNSUPPORTED;
+    char* wsp = static_cast<char*>(workspace);
     hipStream_t st = as_stream(stream);
     const float scale_log2 = g->scale * kLog2e;
 
@@ -940,12 +1173,19 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         pp.num_kv_heads = g->num_kv_heads;
         pp.num_blocks = g->num_blocks;
         pp.num_prefill_rows = plan->num_prefill_rows;
+        pp.splits = plan->prefill_splits;
+        const bool split = plan->prefill_splits > 1;
+        pp.counters = split ? reinterpret_cast<uint32_t*>(wsp + ws.counters) + ws.pf_counter_base : nullptr;
+        pp.part_o = split ? reinterpret_cast<float*>(wsp + ws.pf_part_o) : nullptr;
+        pp.part_lse = split ? reinterpret_cast<float*>(wsp + ws.pf_part_lse) : nullptr;
         pp.scale_log2 = scale_log2;
         for (int i = 0; i < PA_MAX_PREFILL_ROWS; ++i)
             pp.prefill_req[i] = i < plan->num_prefill_rows ? plan->prefill_req[i] : 0;
         for (int i = 0; i <= PA_MAX_PREFILL_ROWS; ++i)
             pp.tile_start[i] = i <= plan->num_prefill_rows ? plan->prefill_tile_start[i] : plan->prefill_tiles;
-        const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads;
+        const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads * plan->prefill_splits;
+        if (grid > INT32_MAX)
+            return PA_ERR_SHAPE;
         hipLaunchKernelGGL(pa_prefill_tile, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
@@ -960,9 +1200,10 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         dp.kv_len = kv_len;
         dp.out = static_cast<uint16_t*>(out);
         dp.lse = lse;
-        dp.counters = ws.total ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + ws.counters) : nullptr;
-        dp.part_o = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_o) : nullptr;
-        dp.part_lse = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_lse) : nullptr;
+        const bool split = plan->max_splits > 1;
+        dp.counters = split ? reinterpret_cast<uint32_t*>(wsp + ws.counters) : nullptr;
+        dp.part_o = split ? reinterpret_cast<float*>(wsp + ws.part_o) : nullptr;
+        dp.part_lse = split ? reinterpret_cast<float*>(wsp + ws.part_lse) : nullptr;
         dp.max_blocks = max_blocks_per_req;
         dp.num_reqs = plan->num_reqs;
         dp.num_q_heads = g->num_q_heads;

@@ -28,9 +28,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_struct_sizes_match_header():
-    # int32 x 10 + 128 + 129 int32, then a uint64 at an 8-byte boundary
+    # int32 x 11 + 128 + 129 int32, then a uint64 at an 8-byte boundary
     assert ctypes.sizeof(pa.Geometry) == 24
-    assert ctypes.sizeof(pa.Plan) == 8 * ((4 * (10 + 128 + 129) + 7) // 8) + 8
+    assert ctypes.sizeof(pa.Plan) == 8 * ((4 * (11 + 128 + 129) + 7) // 8) + 8
 
 
 def test_status_strings(lib):
@@ -88,11 +88,15 @@ def test_plan_prefill_rows_and_workspace():
     kv = [4608] + [2048 + i for i in range(31)]
     plan = pa.pa_plan(g, qo, kv, 256)
     assert plan.num_prefill_rows == 1 and plan.num_decode_rows == 31
-    assert plan.prefill_req[0] == 0 and plan.prefill_tiles == 512 // 16
-    assert plan.prefill_tile_start[1] == 32
+    assert plan.prefill_req[0] == 0 and plan.prefill_tiles == 512 // 32
+    assert plan.prefill_tile_start[1] == 16
+    # 16 tiles x 8 KV heads leave half the CUs idle: each tile's 36 key steps are split in two
+    assert plan.prefill_splits == 2
+    n_pf = 16 * 8 * 2
+    need = n_pf * 128 * 129 * 4
     if plan.max_splits > 1:
-        n = 32 * plan.max_splits * 32
-        assert plan.workspace_bytes >= n * 129 * 4
+        need += 32 * plan.max_splits * 32 * 129 * 4
+    assert plan.workspace_bytes >= need
     # forced split of 1 block and one large split
     p1 = pa.pa_plan(g, qo, kv, 256, split_blocks=1)
     assert p1.split_blocks == 1 and p1.max_splits == -(-2078 // 16)
@@ -101,6 +105,29 @@ def test_plan_prefill_rows_and_workspace():
     # rows longer than 512 blocks are always split
     long = pa.pa_plan(g, [1] * 64, [20000] * 64, 256)
     assert long.split_blocks <= 512 and long.max_splits == 3 and long.split_blocks * 3 >= 1250
+
+
+def test_plan_prefill_splits():
+    g = qwen()
+    # enough tiles to fill the CUs: no split and no workspace
+    big = pa.pa_plan(g, [2048] * 4, [2048] * 4, 256)
+    assert big.prefill_tiles == 4 * 64 and big.prefill_splits == 1 and big.workspace_bytes == 0
+    # short keys are never split below 4 steps per workgroup
+    short = pa.pa_plan(g, [64], [300], 256)
+    assert short.prefill_tiles == 2 and short.prefill_splits == 1
+    # one long chunk: split over many workgroups
+    one = pa.pa_plan(g, [256], [32768], 256)
+    assert one.prefill_tiles == 8 and one.prefill_splits > 1
+    assert 64 * one.prefill_splits <= 256 * 2
+    # forced counts, including more splits than steps
+    for s in (1, 3, 64):
+        f = pa.pa_plan(g, [40], [100], 256, prefill_splits=s)
+        assert f.prefill_splits == s and (f.workspace_bytes > 0) == (s > 1)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan(g, [40], [100], 256, prefill_splits=65)
+    assert e.value.code == -2
+    # decode-only batches carry no prefill split
+    assert pa.pa_plan(g, [1] * 8, [100] * 8, 256).prefill_splits == 0
 
 
 def test_plan_errors():

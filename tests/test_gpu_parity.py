@@ -29,9 +29,9 @@ def _gpu():
     yield
 
 
-def _run_gpu(wl, split_blocks=0):
+def _run_gpu(wl, split_blocks=0, prefill_splits=0):
     import paged_kv_attention_04_amd as pa
-    return pa.run_workload(wl, split_blocks=split_blocks)
+    return pa.run_workload(wl, split_blocks=split_blocks, prefill_splits=prefill_splits)
 
 
 def _errors(out, lse, ref, rows=None):
@@ -43,9 +43,10 @@ def _errors(out, lse, ref, rows=None):
     return float(np.max(np.abs(got - want))), float(np.max(np.abs(l_got - l_want)))
 
 
-def check(wl, split_blocks=0, label=""):
-    print(f"[gpu] {wl.name} {label} R={wl.num_reqs} total_q={wl.total_q} split={split_blocks}", flush=True)
-    kp, vp, out, lse = _run_gpu(wl, split_blocks)
+def check(wl, split_blocks=0, label="", prefill_splits=0):
+    print(f"[gpu] {wl.name} {label} R={wl.num_reqs} total_q={wl.total_q} split={split_blocks} "
+          f"prefill_splits={prefill_splits}", flush=True)
+    kp, vp, out, lse = _run_gpu(wl, split_blocks, prefill_splits)
     okp, ovp, ref = oracle.run_workload(wl)
     assert np.array_equal(kp, okp) and np.array_equal(vp, ovp), "append is not bit-exact"
     eo, el = _errors(out, lse, ref)
@@ -113,6 +114,18 @@ def test_split_sweep(split):
     check(synthetic.config_tiny(seed=41), split_blocks=split)
     check(synthetic.build("split_sweep", 42, 32, 8, qo_len=[1] * 6 + [20], kv_len=[1, 16, 17, 700, 1025, 3000, 300],
                           num_blocks=512), split_blocks=split)
+
+
+@pytest.mark.parametrize("psplit", [1, 2, 3, 5, 64])
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_prefill_split_sweep(psplit, q_scale):
+    """Forced key-split counts of the prefill tiles all match the oracle; 64 exceeds every
+    tile's step count, so some key ranges are empty.  Rows: a 77-token chunk after 1023
+    tokens (three tiles, the last ragged), a 33-token prompt from position 0 (a one-token
+    tail tile), a 2-token chunk, and a decode row."""
+    wl = synthetic.build("prefill_split", 61, 32, 8, qo_len=[77, 1, 33, 2], kv_len=[1100, 500, 33, 700],
+                         num_blocks=400, q_scale=q_scale)
+    check(wl, prefill_splits=psplit, label=f"q*{q_scale:g}")
 
 
 # ------------------------------------------------------------------ invariants on the GPU
