@@ -91,6 +91,9 @@ typedef struct pa_geometry {
 
 /* Most rows with qo_len > 1 that one plan can hold. */
 #define PA_MAX_PREFILL_ROWS 128
+/* Most shared-prefix (cascade) groups one plan can hold, and most requests per group. */
+#define PA_MAX_PREFIX_GROUPS 16
+#define PA_MAX_PREFIX_GROUP_REQS 32
 
 /*
  * The host-side work plan for one batch.  A pure function of the host copies of
@@ -110,6 +113,11 @@ typedef struct pa_plan_t {
     int32_t prefill_splits;              /* key splits per prefill tile (one workgroup each)  */
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];       /* request index of each prefill row      */
     int32_t prefill_tile_start[PA_MAX_PREFILL_ROWS + 1]; /* prefix sums of tiles per row      */
+    int32_t num_prefix_groups;           /* shared-prefix groups (pa_plan_shared_prefix)      */
+    int32_t prefix_splits;               /* key splits of each group's shared blocks          */
+    int32_t prefix_first_req[PA_MAX_PREFIX_GROUPS]; /* first request of each group            */
+    int32_t prefix_num_reqs[PA_MAX_PREFIX_GROUPS];  /* consecutive decode requests in it      */
+    int32_t prefix_blocks[PA_MAX_PREFIX_GROUPS];    /* leading blocks all of them share       */
     uint64_t workspace_bytes;            /* device workspace pa_attention_batch needs         */
 } pa_plan_t;
 
@@ -132,6 +140,28 @@ typedef struct pa_plan_t {
 pa_status pa_plan(const pa_geometry* geometry, int32_t num_reqs, const int32_t* qo_len_host,
                   const int32_t* kv_len_host, int32_t num_cus, int32_t split_blocks, int32_t prefill_splits,
                   pa_plan_t* plan);
+
+/*
+ * Add shared-prefix (cascade) groups to a plan built by pa_plan from the same lengths.
+ * A group is a run of at least two consecutive decode rows (qo_len == 1) whose block
+ * tables start with the same physical blocks: the pages keep one physical copy of a
+ * common prefix, referenced from every request's table (book section 8.3.2, shared
+ * blocks with reference counts; Hugging Face continuous-batching page, prefix caching).
+ * pa_attention_batch then reads each group's shared blocks once per KV head, for all
+ * of the group's query rows together, and merges that partial result with each row's
+ * private suffix by the log-sum-exp rule.  Only whole blocks that precede every row's
+ * last block are shared, and a run needs at least min_shared_blocks of them (0 picks
+ * 16).  block_tables_host: host int32 [num_reqs][max_blocks_per_req], the tables the
+ * batch will use (a device table that differs gives wrong results).  Runs longer than
+ * PA_MAX_PREFIX_GROUP_REQS are cut; at most PA_MAX_PREFIX_GROUPS groups are kept.
+ * Recomputes the decode splits over the private suffixes and the workspace size; a
+ * plan with no group found is left as it was.  Errors: PA_ERR_NULL, PA_ERR_SHAPE
+ * (lengths differ from the plan's), PA_ERR_UNSUPPORTED (completion counters, as for
+ * pa_plan).
+ */
+pa_status pa_plan_shared_prefix(const pa_geometry* geometry, const int32_t* qo_len_host, const int32_t* kv_len_host,
+                                const int32_t* block_tables_host, int32_t max_blocks_per_req, int32_t num_cus,
+                                int32_t min_shared_blocks, pa_plan_t* plan);
 
 /*
  * Write this step's new K/V rows into the pools through the slot mapping

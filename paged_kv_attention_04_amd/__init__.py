@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_PKG, "_build", "libpa.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 
 PA_MAX_PREFILL_ROWS = 128
+PA_MAX_PREFIX_GROUPS = 16
+PA_MAX_PREFIX_GROUP_REQS = 32
 HEAD_DIM = 128
 BLOCK_SIZE = 16
 
@@ -52,6 +54,10 @@ class Plan(ctypes.Structure):
                 ("prefill_splits", ctypes.c_int32),
                 ("prefill_req", ctypes.c_int32 * PA_MAX_PREFILL_ROWS),
                 ("prefill_tile_start", ctypes.c_int32 * (PA_MAX_PREFILL_ROWS + 1)),
+                ("num_prefix_groups", ctypes.c_int32), ("prefix_splits", ctypes.c_int32),
+                ("prefix_first_req", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
+                ("prefix_num_reqs", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
+                ("prefix_blocks", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
@@ -70,6 +76,7 @@ def lib():
     P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     G, PL = ctypes.POINTER(Geometry), ctypes.POINTER(Plan)
     L.pa_plan.argtypes = [G, i32, P, P, i32, i32, i32, PL]
+    L.pa_plan_shared_prefix.argtypes = [G, P, P, P, i32, i32, i32, PL]
     L.pa_append_kv.argtypes = [G, P, P, P, P, P, i32, P]
     L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_validate_batch.argtypes = [G, i32, P, P, P, i32, P]
@@ -138,6 +145,22 @@ def pa_plan(geometry: Geometry, qo_len, kv_len, num_cus: int = 256, split_blocks
     return plan
 
 
+
+
+def pa_plan_shared_prefix(geometry: Geometry, plan: Plan, qo_len, kv_len, block_tables, num_cus: int = 256,
+                          min_shared_blocks: int = 0) -> Plan:
+    """Add shared-prefix groups found in the host block tables to `plan` (in place; also
+    returned).  block_tables: host int32 [num_reqs][max_blocks]."""
+    import numpy as np
+    qo = np.ascontiguousarray(qo_len, dtype=np.int32)
+    kv = np.ascontiguousarray(kv_len, dtype=np.int32)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    if bt.ndim != 2 or bt.shape[0] != qo.size or qo.shape != kv.shape:
+        raise ValueError("block_tables must be [num_reqs][max_blocks] and match the lengths")
+    _check("pa_plan_shared_prefix", lib().pa_plan_shared_prefix(ctypes.byref(geometry), _np_ptr(qo), _np_ptr(kv),
+                                                                _np_ptr(bt), int(bt.shape[1]), int(num_cus),
+                                                                int(min_shared_blocks), ctypes.byref(plan)))
+    return plan
 
 
 def _bf16_types():
@@ -212,7 +235,7 @@ def to_device(arr, device="cuda"):
 
 
 def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", validate: bool = True,
-                 prefill_splits: int = 0):
+                 prefill_splits: int = 0, cascade: bool = False, min_shared_blocks: int = 0):
     """Upload a workload (see synthetic.Workload for the fields), append its new tokens,
     plan and run attention; returns host numpy (k_pool, v_pool, out, lse)."""
     import numpy as np
@@ -226,6 +249,8 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
         if rc:
             raise PaError("pa_validate_append", rc, f" at token {bad}")
     plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks, prefill_splits)
+    if cascade:
+        pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, num_cus, min_shared_blocks)
     kp, vp = to_device(wl.k_pool, device), to_device(wl.v_pool, device)
     q = to_device(wl.q, device)
     bt = to_device(wl.block_tables, device)

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <unordered_set>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -26,6 +27,74 @@ constexpr int kMinAutoPrefillSplitSteps = 4;
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
+// Blocks a decode row streams: its whole table, less the leading blocks a shared-prefix
+// group reads for it (skip[r], or none).
+int32_t decode_blocks(const int32_t* kv_len, const int32_t* skip, int32_t r)
+{
+    return ceil_div(kv_len[r], pa::kBlock) - (skip ? skip[r] : 0);
+}
+
+// Decode split length and the resulting split count and work-item count.  split_blocks
+// > 0 forces the length; otherwise candidate lengths divide the longest row evenly and
+// each is scored by the estimated makespan in block-times: rounds of resident workgroups
+// (one per CU) times the blocks one workgroup streams plus its fixed cost.  Ties go to
+// the longer split, which needs fewer partials.
+void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t* qo_len, const int32_t* kv_len,
+                          const int32_t* skip, int32_t num_cus, int32_t split_blocks, pa_plan_t* plan)
+{
+    int32_t longest = 1;
+    for (int32_t r = 0; r < num_reqs; ++r)
+        if (qo_len[r] == 1)
+            longest = std::max(longest, decode_blocks(kv_len, skip, r));
+    int32_t sb;
+    if (split_blocks > 0) {
+        sb = std::min(split_blocks, pa::kMaxSplitBlocks);
+    } else {
+        const int64_t target = (int64_t)std::max(num_cus, 1) * kWorkgroupsPerCu;
+        int64_t best_cost = INT64_MAX;
+        sb = std::min(longest, pa::kMaxSplitBlocks);
+        for (int32_t parts = 1; parts <= 256; ++parts) {
+            const int32_t cand = ceil_div(longest, parts);
+            if (cand > pa::kMaxSplitBlocks)
+                continue;
+            if (cand < kMinAutoSplitBlocks && parts > 1)
+                break;
+            int64_t wgs = 0;
+            for (int32_t r = 0; r < num_reqs; ++r)
+                if (qo_len[r] == 1)
+                    wgs += (int64_t)ceil_div(decode_blocks(kv_len, skip, r), cand) * g->num_kv_heads;
+            const int64_t cost = (wgs + target - 1) / target * (cand + kWorkgroupOverheadBlocks);
+            if (cost < best_cost) {
+                best_cost = cost;
+                sb = cand;
+            }
+        }
+    }
+    plan->split_blocks = sb;
+    int64_t items = 0;
+    int32_t max_splits = 0;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        if (qo_len[r] != 1)
+            continue;
+        const int32_t s = ceil_div(decode_blocks(kv_len, skip, r), sb);
+        max_splits = std::max(max_splits, s);
+        items += (int64_t)s * g->num_kv_heads;
+    }
+    plan->max_splits = max_splits;
+    plan->decode_items = (int32_t)std::min<int64_t>(items, INT32_MAX);
+}
+
+pa_status finish_workspace(const pa_geometry* g, pa_plan_t* plan)
+{
+    const pa::WorkspaceLayout ws =
+        pa::workspace_layout(plan->num_reqs, plan->max_splits, g->num_q_heads, g->num_kv_heads, plan->prefill_tiles,
+                             plan->prefill_splits, plan->num_prefix_groups > 0 ? plan->prefix_splits : 0);
+    if (ws.counters_used > pa::kMaxCounters)
+        return PA_ERR_UNSUPPORTED;   // more completion counters than the workspace holds
+    plan->workspace_bytes = ws.total;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32_t* qo_len,
@@ -43,16 +112,13 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
     plan->num_kv_heads = g->num_kv_heads;
     plan->num_reqs = num_reqs;
 
-    int64_t decode_blocks = 0, total_q = 0;
-    int32_t max_decode_blocks = 0, max_prefill_steps = 0;
+    int64_t total_q = 0;
+    int32_t max_prefill_steps = 0;
     for (int32_t r = 0; r < num_reqs; ++r) {
         if (qo_len[r] < 1 || kv_len[r] < qo_len[r])
             return PA_ERR_SHAPE;
         total_q += qo_len[r];
         if (qo_len[r] == 1) {
-            int32_t nb = ceil_div(kv_len[r], pa::kBlock);
-            decode_blocks += nb;
-            max_decode_blocks = std::max(max_decode_blocks, nb);
             plan->num_decode_rows++;
         } else {
             if (plan->num_prefill_rows >= PA_MAX_PREFILL_ROWS)
@@ -70,47 +136,7 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
 
     // Split length: split the decode rows' KV over enough (row, KV head, split) items
     // to give every CU several wavefronts, on whole blocks.
-    int32_t sb;
-    if (split_blocks > 0) {
-        sb = std::min(split_blocks, pa::kMaxSplitBlocks);
-    } else {
-        // Candidate split lengths divide the longest row evenly; each is scored by the
-        // estimated makespan in block-times: rounds of resident workgroups (one per CU)
-        // times the blocks one workgroup streams plus its fixed cost.  Ties go to the
-        // longer split, which needs fewer partials.
-        const int64_t target = (int64_t)std::max(num_cus, 1) * kWorkgroupsPerCu;
-        const int32_t longest = std::max(max_decode_blocks, 1);
-        int64_t best_cost = INT64_MAX;
-        sb = std::min(longest, pa::kMaxSplitBlocks);
-        for (int32_t parts = 1; parts <= 256; ++parts) {
-            const int32_t cand = ceil_div(longest, parts);
-            if (cand > pa::kMaxSplitBlocks)
-                continue;
-            if (cand < kMinAutoSplitBlocks && parts > 1)
-                break;
-            int64_t wgs = 0;
-            for (int32_t r = 0; r < num_reqs; ++r)
-                if (qo_len[r] == 1)
-                    wgs += (int64_t)ceil_div(ceil_div(kv_len[r], pa::kBlock), cand) * g->num_kv_heads;
-            const int64_t cost = (wgs + target - 1) / target * (cand + kWorkgroupOverheadBlocks);
-            if (cost < best_cost) {
-                best_cost = cost;
-                sb = cand;
-            }
-        }
-    }
-    plan->split_blocks = sb;
-    int64_t items = 0;
-    int32_t max_splits = 0;
-    for (int32_t r = 0; r < num_reqs; ++r) {
-        if (qo_len[r] != 1)
-            continue;
-        int32_t s = ceil_div(ceil_div(kv_len[r], pa::kBlock), sb);
-        max_splits = std::max(max_splits, s);
-        items += (int64_t)s * g->num_kv_heads;
-    }
-    plan->max_splits = max_splits;
-    plan->decode_items = (int32_t)std::min<int64_t>(items, INT32_MAX);
+    choose_decode_splits(g, num_reqs, qo_len, kv_len, nullptr, num_cus, split_blocks, plan);
 
     // Prefill key splits: a tile's causal key range is cut into contiguous step ranges,
     // one workgroup each, when the (tile, KV head) pairs alone would leave CUs idle.
@@ -142,11 +168,89 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
         }
     }
     plan->prefill_splits = plan->prefill_tiles > 0 ? ps : 0;
-    const pa::WorkspaceLayout ws = pa::workspace_layout(num_reqs, max_splits, g->num_q_heads, g->num_kv_heads,
-                                                        plan->prefill_tiles, plan->prefill_splits);
-    if (ws.counters_used > pa::kMaxCounters)
-        return PA_ERR_UNSUPPORTED;   // more completion counters than the workspace holds
-    plan->workspace_bytes = ws.total;
+    return finish_workspace(g, plan);
+}
+
+extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* qo_len, const int32_t* kv_len,
+                                           const int32_t* bt, int32_t max_blocks, int32_t num_cus,
+                                           int32_t min_shared_blocks, pa_plan_t* plan)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    const int32_t R = plan->num_reqs;
+    if (R > 0 && (!qo_len || !kv_len || !bt))
+        return PA_ERR_NULL;
+    if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
+        return PA_ERR_UNSUPPORTED;
+    if (max_blocks < 1 && R > 0)
+        return PA_ERR_SHAPE;
+    int64_t total_q = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        if (qo_len[r] < 1 || kv_len[r] < qo_len[r] || ceil_div(kv_len[r], pa::kBlock) > max_blocks)
+            return PA_ERR_SHAPE;
+        total_q += qo_len[r];
+    }
+    if (total_q != plan->total_q)
+        return PA_ERR_SHAPE;
+    const int32_t min_shared = min_shared_blocks > 0 ? min_shared_blocks : 16;
+    // Whole blocks of decode row r that may be shared: those before its last block.
+    auto shareable = [&](int32_t r) { return (kv_len[r] - 1) / pa::kBlock; };
+
+    // Greedy runs: from each decode row, extend over the following decode rows while
+    // the common leading part of their tables stays at least min_shared blocks long.
+    pa_plan_t out = *plan;
+    out.num_prefix_groups = 0;
+    int32_t max_prefix_blocks = 0;
+    for (int32_t r = 0; r < R && out.num_prefix_groups < PA_MAX_PREFIX_GROUPS;) {
+        if (qo_len[r] != 1 || shareable(r) < min_shared) {
+            ++r;
+            continue;
+        }
+        int32_t common = shareable(r), end = r + 1;
+        const int32_t* t0 = bt + (int64_t)r * max_blocks;
+        for (int32_t r2 = r + 1; r2 < R && r2 - r < PA_MAX_PREFIX_GROUP_REQS && qo_len[r2] == 1; ++r2) {
+            const int32_t* t2 = bt + (int64_t)r2 * max_blocks;
+            int32_t c = 0;
+            const int32_t lim = std::min(common, shareable(r2));
+            while (c < lim && t2[c] == t0[c])
+                ++c;
+            if (c < min_shared)
+                break;
+            common = c;
+            end = r2 + 1;
+        }
+        if (end - r >= 2) {
+            const int32_t i = out.num_prefix_groups++;
+            out.prefix_first_req[i] = r;
+            out.prefix_num_reqs[i] = end - r;
+            out.prefix_blocks[i] = common;
+            max_prefix_blocks = std::max(max_prefix_blocks, common);
+            r = end;
+        } else {
+            ++r;
+        }
+    }
+    if (out.num_prefix_groups == 0)
+        return PA_OK;
+
+    // Key splits of the shared blocks: enough (group, KV head, split) workgroups to fill
+    // the CUs, each at least two 128-key steps long.
+    const int32_t steps = ceil_div((int64_t)max_prefix_blocks * pa::kBlock, pa::kPrefillKeys);
+    const int64_t base = (int64_t)out.num_prefix_groups * g->num_kv_heads;
+    int32_t ps = (int32_t)std::max<int64_t>(1, std::max(num_cus, 1) / base);
+    ps = std::min(ps, std::max(1, steps / 2));
+    out.prefix_splits = std::min(ps, pa::kMaxPrefillSplits);
+
+    // Decode splits over the private suffixes.
+    std::vector<int32_t> skip(R, 0);
+    for (int32_t i = 0; i < out.num_prefix_groups; ++i)
+        for (int32_t k = 0; k < out.prefix_num_reqs[i]; ++k)
+            skip[out.prefix_first_req[i] + k] = out.prefix_blocks[i];
+    choose_decode_splits(g, R, qo_len, kv_len, skip.data(), num_cus, 0, &out);
+    const pa_status st = finish_workspace(g, &out);
+    if (st != PA_OK)
+        return st;
+    *plan = out;
     return PA_OK;
 }
 

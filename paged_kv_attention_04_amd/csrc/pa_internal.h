@@ -34,6 +34,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //   pf_part_o     normalised FP32 prefill split outputs, 128 x 128 floats per (tile, KV head,
 //                 split), in the order the prefill kernel's lanes hold them
 //   pf_part_lse   their log2-sum-exp, 512 floats per (tile, KV head, split), also in lane order
+//   px_part_o     normalised FP32 outputs over a row's shared-prefix blocks, per (request,
+//                 prefix split, query head): [num_reqs][prefix_splits][Hq][head_dim]
+//   px_part_lse   their log2-sum-exp [num_reqs][prefix_splits][Hq]
 // The counters sit at a fixed place so that no call's partials ever land on them.
 constexpr size_t kCounterBytes = 64 * 1024;
 constexpr int64_t kMaxCounters = kCounterBytes / sizeof(uint32_t);
@@ -43,22 +46,25 @@ constexpr int64_t kPrefillPartFloats = (int64_t)kPrefillQ * kGroup * kHeadDim;
 constexpr int64_t kPrefillPartLseFloats = 4 * 2 * 64;
 
 struct WorkspaceLayout {
-    size_t counters = 0, part_o = 0, part_lse = 0, pf_part_o = 0, pf_part_lse = 0, total = 0;
+    size_t counters = 0, part_o = 0, part_lse = 0, pf_part_o = 0, pf_part_lse = 0, px_part_o = 0, px_part_lse = 0,
+           total = 0;
     int64_t pf_counter_base = 0;   // index of the first prefill counter
     int64_t counters_used = 0;     // counters the layout needs
 };
 
 inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, int32_t num_q_heads,
-                                        int32_t num_kv_heads, int32_t prefill_tiles, int32_t prefill_splits)
+                                        int32_t num_kv_heads, int32_t prefill_tiles, int32_t prefill_splits,
+                                        int32_t prefix_splits = 0)
 {
     WorkspaceLayout w;
     const bool decode = max_splits > 1 && num_reqs > 0;
     const bool prefill = prefill_splits > 1 && prefill_tiles > 0;
-    if (!decode && !prefill)
+    const bool prefix = prefix_splits > 0 && num_reqs > 0;
+    if (!decode && !prefill && !prefix)
         return w;
     w.pf_counter_base = (int64_t)num_reqs * num_kv_heads;
     w.counters_used = prefill ? w.pf_counter_base + (int64_t)prefill_tiles * num_kv_heads
-                              : (int64_t)num_reqs * num_kv_heads;
+                              : decode ? (int64_t)num_reqs * num_kv_heads : 0;
     size_t at = kCounterBytes;
     if (decode) {
         const size_t n = (size_t)num_reqs * (size_t)max_splits * (size_t)num_q_heads;
@@ -71,6 +77,12 @@ inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, in
         w.pf_part_o = at;
         w.pf_part_lse = align256(w.pf_part_o + n * (size_t)kPrefillPartFloats * sizeof(float));
         at = align256(w.pf_part_lse + n * (size_t)kPrefillPartLseFloats * sizeof(float));
+    }
+    if (prefix) {
+        const size_t n = (size_t)num_reqs * (size_t)prefix_splits * (size_t)num_q_heads;
+        w.px_part_o = at;
+        w.px_part_lse = align256(w.px_part_o + n * kHeadDim * sizeof(float));
+        at = align256(w.px_part_lse + n * sizeof(float));
     }
     w.total = at;
     return w;

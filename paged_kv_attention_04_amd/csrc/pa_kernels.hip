@@ -13,6 +13,7 @@
 // Pool layout: [block][kv_head][token-in-block][dim] (head-major inside a block), so one
 // (block, KV head) tile is 16 x 128 bf16 = 4 KiB of contiguous memory.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -71,6 +72,50 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ inline void store_agent(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ inline float load_agent(const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
+// Running log-sum-exp merge of normalised partial results (o_s, lse_s in log2 units):
+// out = sum_s 2^lse_s o_s / sum_s 2^lse_s, with the weights taken relative to the largest
+// lse seen so far.  An empty partial (lse = -inf) adds nothing; a NaN lse poisons the
+// result.
+struct LseMerge {
+    float lmax = -INFINITY, wsum = 0.f, o = 0.f;
+    bool nan = false;
+    __device__ void add(float ls, float os)
+    {
+        nan |= ls != ls;
+        if (!(ls > -INFINITY))
+            return;
+        if (ls > lmax) {
+            const float a = lmax == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lmax - ls);
+            wsum *= a;
+            o *= a;
+            lmax = ls;
+        }
+        const float c = __builtin_amdgcn_exp2f(ls - lmax);
+        wsum += c;
+        o = fmaf(c, os, o);
+    }
+};
+
+// Adds partials s = 0 .. n - 1 to m, eight at a time: all loads of a group of eight are
+// issued before any is used, so n partials cost about n / 8 memory round trips.
+template <typename LoadLse, typename LoadO>
+__device__ inline void merge_partials(LseMerge& m, int n, LoadLse load_lse, LoadO load_o)
+{
+    for (int s0 = 0; s0 < n; s0 += 8) {
+        float ls[8], os[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = min(s0 + u, n - 1);
+            ls[u] = load_lse(s);
+            os[u] = load_o(s);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < n)
+                m.add(ls[u], os[u]);
+    }
+}
+
 __device__ inline float readlane_f(float x, int lane)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
@@ -125,6 +170,16 @@ struct DecodeParams {
     int32_t split_blocks;
     int32_t max_splits;
     float scale_log2;   // score scale times log2(e): softmax runs in base 2
+    // shared-prefix groups: rows first .. first + count - 1 skip their first `blocks`
+    // blocks, whose partial results (prefix_splits of them per row and head) an earlier
+    // launch left in px_part_o / px_part_lse
+    int32_t num_prefix_groups;
+    int32_t prefix_splits;
+    int32_t prefix_first[PA_MAX_PREFIX_GROUPS];
+    int32_t prefix_count[PA_MAX_PREFIX_GROUPS];
+    int32_t prefix_blocks[PA_MAX_PREFIX_GROUPS];
+    const float* px_part_o;
+    const float* px_part_lse;
 };
 
 #ifndef PA_DECODE_DEPTH
@@ -240,7 +295,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     // the row's lengths arrive, so the start-up waits for one memory round trip less.  The
     // early requests are bounded by the table row and the pool; entries past the row's
     // last block are never used.
-    const int g0 = split * p.split_blocks;
+    int skip = 0;                                     // blocks a shared-prefix group reads for this row
+    for (int gi = 0; gi < p.num_prefix_groups; ++gi)
+        if (r >= p.prefix_first[gi] && r < p.prefix_first[gi] + p.prefix_count[gi])
+            skip = p.prefix_blocks[gi];
+    const int g0 = skip + split * p.split_blocks;
     const int bidx = g0 + wave + kDecodeWaves * lane;
     int my_blk = 0;
     if (lane * kDecodeWaves < p.split_blocks && bidx < p.max_blocks)
@@ -270,8 +329,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     if (q_end - q_row != 1)
         return;                                       // not a decode row
     const int nblk = (kvlen + kBlock - 1) / kBlock;
-    const int nsplit = (nblk + p.split_blocks - 1) / p.split_blocks;
-    if (kvlen < 1 || nblk > p.max_blocks || nsplit > p.max_splits ||
+    const int nsplit = (nblk - skip + p.split_blocks - 1) / p.split_blocks;
+    if (kvlen < 1 || nblk > p.max_blocks || nblk <= skip || nsplit > p.max_splits ||
         p.split_blocks > pa::kMaxSplitBlocks) {       // lengths disagree with the plan
         if (split == 0)
             for (int i = tid; i < kGroup * kHeadDim; i += 64 * kDecodeWaves) {
@@ -458,7 +517,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     }
 
     const int64_t out_base = ((int64_t)q_row * p.num_q_heads + head0) * kHeadDim;
-    if (nsplit == 1) {
+    const bool prefix = skip > 0 && p.prefix_splits > 0;
+    if (nsplit == 1 && !prefix) {
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
             const int idx = tid + k * 64 * kDecodeWaves;
@@ -475,49 +535,52 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     // needs no L2 writeback or invalidation, which a device fence would do for every split.
     const int64_t split_stride = p.num_q_heads;                        // partial index step per split
     const int64_t base = (int64_t)r * p.max_splits * p.num_q_heads + head0;
-    const int64_t mine = base + (int64_t)split * split_stride;
+    if (nsplit > 1) {
+        const int64_t mine = base + (int64_t)split * split_stride;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const int idx = tid + k * 64 * kDecodeWaves;
-        store_agent(p.part_o + mine * kHeadDim + idx, res[k]);
-        if ((idx & (kHeadDim - 1)) == 0)
-            store_agent(p.part_lse + mine + idx / kHeadDim, res_lse[k]);
+        for (int k = 0; k < kPerThread; ++k) {
+            const int idx = tid + k * 64 * kDecodeWaves;
+            store_agent(p.part_o + mine * kHeadDim + idx, res[k]);
+            if ((idx & (kHeadDim - 1)) == 0)
+                store_agent(p.part_lse + mine + idx / kHeadDim, res_lse[k]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        uint32_t* counter = p.counters + (int64_t)r * p.num_kv_heads + kvh;
+        if (tid == 0) {
+            const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = done == (uint32_t)(nsplit - 1);
+            if (last)
+                __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+            last_lds = last;
+        }
+        __syncthreads();
+        if (!last_lds)
+            return;
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    uint32_t* counter = p.counters + (int64_t)r * p.num_kv_heads + kvh;
-    if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = done == (uint32_t)(nsplit - 1);
-        if (last)
-            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
-        last_lds = last;
-    }
-    __syncthreads();
-    if (!last_lds)
-        return;
 
+    // Merge the decode splits (this workgroup's own result when it is the only one) and,
+    // for a row of a shared-prefix group, the partials over its shared blocks, which an
+    // earlier launch wrote: plain loads see them.
+    const int64_t pbase = (int64_t)r * p.prefix_splits * p.num_q_heads + head0;
+    const int nprefix = prefix ? p.prefix_splits : 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int idx = tid + k * 64 * kDecodeWaves;
-        const int h = idx / kHeadDim;
-        float L = -INFINITY;
-        bool any_nan = false;
-        for (int s = 0; s < nsplit; ++s) {
-            const float ls = load_agent(p.part_lse + base + s * split_stride + h);
-            any_nan |= (ls != ls);
-            L = fmaxf(L, ls);
-        }
-        float wsum = 0.f, o = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const int64_t pi = base + s * split_stride + h;
-            const float c = fast_exp2(load_agent(p.part_lse + pi) - L);
-            wsum += c;
-            o = fmaf(c, load_agent(p.part_o + pi * kHeadDim + (idx & (kHeadDim - 1))), o);
-        }
-        p.out[out_base + idx] = __builtin_bit_cast(uint16_t, (__bf16)(any_nan ? nan : o / wsum));
-        if ((idx & (kHeadDim - 1)) == 0)
-            p.lse[(int64_t)q_row * p.num_q_heads + head0 + h] = any_nan ? nan : (L + fast_log2(wsum)) * kLn2;
+        const int h = idx / kHeadDim, d = idx & (kHeadDim - 1);
+        LseMerge mg;
+        if (nsplit == 1)
+            mg.add(res_lse[k], res[k]);
+        else
+            merge_partials(
+                mg, nsplit, [&](int s) { return load_agent(p.part_lse + base + s * split_stride + h); },
+                [&](int s) { return load_agent(p.part_o + (base + s * split_stride + h) * kHeadDim + d); });
+        merge_partials(
+            mg, nprefix, [&](int s) { return p.px_part_lse[pbase + s * p.num_q_heads + h]; },
+            [&](int s) { return p.px_part_o[(pbase + s * p.num_q_heads + h) * kHeadDim + d]; });
+        p.out[out_base + idx] = __builtin_bit_cast(uint16_t, (__bf16)(mg.nan ? nan : mg.o / mg.wsum));
+        if (d == 0)
+            p.lse[(int64_t)q_row * p.num_q_heads + head0 + h] = mg.nan ? nan : (mg.lmax + fast_log2(mg.wsum)) * kLn2;
     }
 }
 
@@ -544,6 +607,13 @@ struct PrefillParams {
     float scale_log2;
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];
     int32_t tile_start[PA_MAX_PREFILL_ROWS + 1];
+    // shared-prefix mode: one tile per group, its rows (request, head) of the group's
+    // decode requests, its keys the group's shared blocks
+    int32_t group_first[PA_MAX_PREFIX_GROUPS];
+    int32_t group_count[PA_MAX_PREFIX_GROUPS];
+    int32_t group_blocks[PA_MAX_PREFIX_GROUPS];
+    float* px_part_o;           // [num_reqs][splits][Hq][head_dim]
+    float* px_part_lse;         // [num_reqs][splits][Hq]
 };
 
 constexpr int kPfKeys = pa::kPrefillKeys;  // keys per step: eight 16-token blocks
@@ -771,6 +841,7 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* v
 // eight keys of chunk c are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of the chunk:
 // exactly S^T values it holds; the V^T operand is read with the same key order by two
 // transposed LDS reads, and a contraction does not care how its index is permuted.
+template <bool kCascade>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
 {
     __shared__ __attribute__((aligned(1024))) u32x4 k_tile0[kTileChunks];
@@ -788,22 +859,39 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     const int rest = blockIdx.x / p.num_kv_heads;
     const int split = rest % p.splits;
     const int tile = rest / p.splits;
-    int pr = 0;
-    while (pr + 1 < p.num_prefill_rows && p.tile_start[pr + 1] <= tile)
-        ++pr;
-    const int r = p.prefill_req[pr];
-    const int qt = tile - p.tile_start[pr];
-    const int q0 = p.qo_indptr[r];
-    const int qlen = p.qo_indptr[r + 1] - q0;
-    const int kvlen = p.kv_len[r];
     const int head0 = kvh * kGroup;
-    if (qt * pa::kPrefillQ >= qlen)             // the same for every split of the tile
-        return;
-    const int ctx = kvlen - qlen;               // tokens before this chunk
-    const int nblk_row = (kvlen + kBlock - 1) / kBlock;
-    const bool bad_row = qlen < 2 || ctx < 0 || nblk_row > p.max_blocks;
-    // keys any token of this tile can see: 0 .. ctx + last token of the tile
-    const int kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * pa::kPrefillQ));
+    int r, qt, q0, qlen, kvlen, ctx, nblk_row, kv_hi;
+    bool bad_row;
+    int grp_first = 0, grp_count = 0;
+    if constexpr (kCascade) {
+        // the group's requests are rows r .. r + grp_count - 1, each one decode token; the
+        // keys are the first group_blocks blocks of their (shared) tables, all of them
+        // before every one of the group's queries
+        grp_first = p.group_first[tile];
+        grp_count = p.group_count[tile];
+        r = grp_first;
+        qt = q0 = qlen = ctx = 0;
+        nblk_row = p.group_blocks[tile];
+        kvlen = nblk_row * kBlock;
+        bad_row = nblk_row < 1 || nblk_row > p.max_blocks || grp_count < 1 || grp_count > PA_MAX_PREFIX_GROUP_REQS;
+        kv_hi = bad_row ? 0 : kvlen;
+    } else {
+        int pr = 0;
+        while (pr + 1 < p.num_prefill_rows && p.tile_start[pr + 1] <= tile)
+            ++pr;
+        r = p.prefill_req[pr];
+        qt = tile - p.tile_start[pr];
+        q0 = p.qo_indptr[r];
+        qlen = p.qo_indptr[r + 1] - q0;
+        kvlen = p.kv_len[r];
+        if (qt * pa::kPrefillQ >= qlen)         // the same for every split of the tile
+            return;
+        ctx = kvlen - qlen;                     // tokens before this chunk
+        nblk_row = (kvlen + kBlock - 1) / kBlock;
+        bad_row = qlen < 2 || ctx < 0 || nblk_row > p.max_blocks;
+        // keys any token of this tile can see: 0 .. ctx + last token of the tile
+        kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * pa::kPrefillQ));
+    }
     const int nsteps_tile = (kv_hi + kPfKeys - 1) / kPfKeys;
     const int s_begin = split * nsteps_tile / p.splits;
     const int nsteps = (split + 1) * nsteps_tile / p.splits - s_begin;
@@ -815,15 +903,25 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int rho = 32 * rg + 16 * rb + row16;
-        const int tl = qt * pa::kPrefillQ + (rho >> 2);
-        qpos[rb] = ctx + tl;
-        const bool ok = tl < qlen;
+        int qidx;
+        bool ok;
+        if constexpr (kCascade) {
+            const int slot = rho >> 2;          // the group's request slot
+            ok = slot < grp_count;
+            qidx = ok ? p.qo_indptr[grp_first + slot] : 0;
+            qpos[rb] = INT_MAX;                 // every shared key precedes the query
+        } else {
+            const int tl = qt * pa::kPrefillQ + (rho >> 2);
+            qpos[rb] = ctx + tl;
+            ok = tl < qlen;
+            qidx = q0 + tl;
+        }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
             if (ok)
                 v = *reinterpret_cast<const u32x4*>(
-                    p.q + ((int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + ks * 32 + kslice * 8);
+                    p.q + ((int64_t)qidx * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + ks * 32 + kslice * 8);
             qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -906,10 +1004,11 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     // workgroups of neighbouring query tiles start one step apart (at any time each K / V
     // step is then fetched from memory by one workgroup and found in the XCD's L2 by the
     // others: all tiles of one KV head run on one XCD), then the diagonal and tail steps.
-    const int qmin = ctx + qt * pa::kPrefillQ;              // smallest query position of the tile
+    // smallest query position of the tile (a shared prefix masks only past its end)
+    const int qmin = kCascade ? kv_hi - 1 : ctx + qt * pa::kPrefillQ;
     const int s_masked = max(s_begin, min(s_begin + nsteps, (qmin + 1) / kPfKeys));
     const int n_plain = s_masked - s_begin;
-    const int rot = n_plain > 0 ? qt % n_plain : 0;
+    const int rot = (!kCascade && n_plain > 0) ? qt % n_plain : 0;
     auto step_at = [&](int i) __attribute__((always_inline)) {
         i = min(i, nsteps - 1);
         return i >= n_plain ? s_begin + i : s_begin + (i + rot < n_plain ? i + rot : i + rot - n_plain);
@@ -1003,6 +1102,28 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
         }
     }
 
+    if constexpr (kCascade) {
+        // this split's normalised partial and log2-sum-exp per (request, query head), in
+        // the decode kernel's partial layout; a later launch merges them
+        if (kh == 0) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const int rho = 32 * rg + 16 * rb + row16;
+                if ((rho >> 2) >= grp_count)
+                    continue;
+                const int64_t pi =
+                    ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * p.num_q_heads + head0 + (rho & 3);
+                float* dst = p.px_part_o + pi * kHeadDim + 4 * kslice;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    *reinterpret_cast<f32x4*>(dst + 16 * db) = oacc[rb][db];
+                if (kslice == 0)
+                    p.px_part_lse[pi] = lse2[rb];
+            }
+        }
+        return;
+    }
+
     // output: lane l holds O^T[16 db + 4 kslice + e][row row16] of row block rb
     auto write_out = [&](const f32x4 (&o)[2][8], const float (&lse_row)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -1063,40 +1184,39 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        float L = lse2[rb];
-        bool any_nan = lse2[rb] != lse2[rb];
-        for (int sp = 0; sp < p.splits; ++sp) {
-            const float ls = sp == split ? lse2[rb] : load_agent(part_lse_at(sp) + rb * 64 + lane);
-            any_nan |= ls != ls;
-            L = fmaxf(L, ls);
-        }
-        float wsum = 0.f;
-        f32x4 acc[8];
+        // lanes hold 32 output values of the row block: merge each with its own running
+        // weights (the lse is the same for all of a row's values)
+        LseMerge mg[8][4];
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-            acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mg[db][e].add(lse2[rb], oacc[rb][db][e]);
         for (int sp = 0; sp < p.splits; ++sp) {
-            const float ls = sp == split ? lse2[rb] : load_agent(part_lse_at(sp) + rb * 64 + lane);
-            const float c = (ls == -INFINITY || any_nan) ? 0.f : fast_exp2(ls - L);
-            wsum += c;
-            if (sp == split) {
+            if (sp == split)
+                continue;
+            const float ls = load_agent(part_lse_at(sp) + rb * 64 + lane);
+            const float* po = part_o_at(sp);
+            float os[8][4];
 #pragma unroll
-                for (int db = 0; db < 8; ++db)
-                    acc[db] += c * oacc[rb][db];
-            } else if (c != 0.f) {
-                const float* po = part_o_at(sp);
+            for (int db = 0; db < 8; ++db)
 #pragma unroll
-                for (int db = 0; db < 8; ++db)
+                for (int e = 0; e < 4; ++e)
+                    os[db][e] = load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[db][e] += c * load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
-            }
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    mg[db][e].add(ls, os[db][e]);
         }
-        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+        const LseMerge& m0 = mg[0][0];
+        const float inv = m0.wsum > 0.f ? 1.f / m0.wsum : 0.f;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-            oacc[rb][db] = acc[db] * inv;
-        lse2[rb] = any_nan ? nan : (wsum > 0.f ? L + fast_log2(wsum) : -INFINITY);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                oacc[rb][db][e] = mg[db][e].o * inv;
+        lse2[rb] = m0.nan ? nan : (m0.wsum > 0.f ? m0.lmax + fast_log2(m0.wsum) : -INFINITY);
     }
     write_out(oacc, lse2);
 }
@@ -1148,8 +1268,19 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         return PA_ERR_SHAPE;
     if (plan->prefill_tiles > 0 && (plan->prefill_splits < 1 || plan->prefill_splits > pa::kMaxPrefillSplits))
         return PA_ERR_SHAPE;
-    const pa::WorkspaceLayout ws = pa::workspace_layout(plan->num_reqs, plan->max_splits, g->num_q_heads,
-                                                        g->num_kv_heads, plan->prefill_tiles, plan->prefill_splits);
+    const int ngroups = plan->num_prefix_groups;
+    if (ngroups < 0 || ngroups > PA_MAX_PREFIX_GROUPS ||
+        (ngroups > 0 && (plan->prefix_splits < 1 || plan->prefix_splits > pa::kMaxPrefillSplits)))
+        return PA_ERR_SHAPE;
+    for (int i = 0; i < ngroups; ++i)
+        if (plan->prefix_first_req[i] < 0 || plan->prefix_num_reqs[i] < 1 ||
+            plan->prefix_num_reqs[i] > PA_MAX_PREFIX_GROUP_REQS ||
+            plan->prefix_first_req[i] + plan->prefix_num_reqs[i] > plan->num_reqs || plan->prefix_blocks[i] < 1 ||
+            plan->prefix_blocks[i] > max_blocks_per_req)
+            return PA_ERR_SHAPE;
+    const pa::WorkspaceLayout ws =
+        pa::workspace_layout(plan->num_reqs, plan->max_splits, g->num_q_heads, g->num_kv_heads, plan->prefill_tiles,
+                             plan->prefill_splits, ngroups > 0 ? plan->prefix_splits : 0);
     if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || (reinterpret_cast<uintptr_t>(workspace) & 255)))
         return PA_ERR_WORKSPACE;
     if (ws.counters_used > pa::kMaxCounters)
@@ -1158,8 +1289,26 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
     hipStream_t st = as_stream(stream);
     const float scale_log2 = g->scale * kLog2e;
 
+    auto prefill_params = [&]() {
+        PrefillParams pp = {};
+        pp.q = static_cast<const uint16_t*>(q);
+        pp.k_pool = static_cast<const uint16_t*>(k_pool);
+        pp.v_pool = static_cast<const uint16_t*>(v_pool);
+        pp.block_tables = block_tables;
+        pp.qo_indptr = qo_indptr;
+        pp.kv_len = kv_len;
+        pp.out = static_cast<uint16_t*>(out);
+        pp.lse = lse;
+        pp.max_blocks = max_blocks_per_req;
+        pp.num_q_heads = g->num_q_heads;
+        pp.num_kv_heads = g->num_kv_heads;
+        pp.num_blocks = g->num_blocks;
+        pp.scale_log2 = scale_log2;
+        return pp;
+    };
+
     if (plan->num_prefill_rows > 0 && plan->prefill_tiles > 0) {
-        PrefillParams pp;
+        PrefillParams pp = prefill_params();
         pp.q = static_cast<const uint16_t*>(q);
         pp.k_pool = static_cast<const uint16_t*>(k_pool);
         pp.v_pool = static_cast<const uint16_t*>(v_pool);
@@ -1186,7 +1335,23 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads * plan->prefill_splits;
         if (grid > INT32_MAX)
             return PA_ERR_SHAPE;
-        hipLaunchKernelGGL(pa_prefill_tile, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        hipLaunchKernelGGL(pa_prefill_tile<false>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        if (hipGetLastError() != hipSuccess)
+            return PA_ERR_HIP;
+    }
+    if (ngroups > 0) {
+        // each group's shared blocks, once per KV head, for all of its query rows
+        PrefillParams pp = prefill_params();
+        pp.splits = plan->prefix_splits;
+        for (int i = 0; i < ngroups; ++i) {
+            pp.group_first[i] = plan->prefix_first_req[i];
+            pp.group_count[i] = plan->prefix_num_reqs[i];
+            pp.group_blocks[i] = plan->prefix_blocks[i];
+        }
+        pp.px_part_o = reinterpret_cast<float*>(wsp + ws.px_part_o);
+        pp.px_part_lse = reinterpret_cast<float*>(wsp + ws.px_part_lse);
+        const int64_t grid = (int64_t)ngroups * g->num_kv_heads * plan->prefix_splits;
+        hipLaunchKernelGGL(pa_prefill_tile<true>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
@@ -1212,6 +1377,15 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         dp.split_blocks = plan->split_blocks;
         dp.max_splits = plan->max_splits;
         dp.scale_log2 = scale_log2;
+        dp.num_prefix_groups = ngroups;
+        dp.prefix_splits = ngroups > 0 ? plan->prefix_splits : 0;
+        for (int i = 0; i < PA_MAX_PREFIX_GROUPS; ++i) {
+            dp.prefix_first[i] = i < ngroups ? plan->prefix_first_req[i] : 0;
+            dp.prefix_count[i] = i < ngroups ? plan->prefix_num_reqs[i] : 0;
+            dp.prefix_blocks[i] = i < ngroups ? plan->prefix_blocks[i] : 0;
+        }
+        dp.px_part_o = ngroups > 0 ? reinterpret_cast<const float*>(wsp + ws.px_part_o) : nullptr;
+        dp.px_part_lse = ngroups > 0 ? reinterpret_cast<const float*>(wsp + ws.px_part_lse) : nullptr;
         const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * g->num_kv_heads;
         if (grid > INT32_MAX)
             return PA_ERR_SHAPE;

@@ -28,9 +28,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_struct_sizes_match_header():
-    # int32 x 11 + 128 + 129 int32, then a uint64 at an 8-byte boundary
+    # int32 x 11 + 128 + 129, then 2 + 3 x 16 int32 of the prefix groups, then a uint64 at
+    # an 8-byte boundary
     assert ctypes.sizeof(pa.Geometry) == 24
-    assert ctypes.sizeof(pa.Plan) == 8 * ((4 * (11 + 128 + 129) + 7) // 8) + 8
+    assert ctypes.sizeof(pa.Plan) == 8 * ((4 * (11 + 128 + 129 + 2 + 3 * 16) + 7) // 8) + 8
 
 
 def test_status_strings(lib):
@@ -128,6 +129,83 @@ def test_plan_prefill_splits():
     assert e.value.code == -2
     # decode-only batches carry no prefill split
     assert pa.pa_plan(g, [1] * 8, [100] * 8, 256).prefill_splits == 0
+
+
+def _shared_tables(n_rows, shared, private, max_blocks, seed=0, split_at=None):
+    """Block tables where every row starts with the same `shared` blocks (rows from
+    split_at on use a different shared run) followed by private blocks."""
+    rng = np.random.default_rng(seed)
+    ids = rng.permutation(100000).astype(np.int32)
+    bt = np.full((n_rows, max_blocks), -1, np.int32)
+    nxt = 2 * shared
+    for r in range(n_rows):
+        base = 0 if split_at is None or r < split_at else shared
+        bt[r, :shared] = ids[base:base + shared]
+        bt[r, shared:shared + private[r]] = ids[nxt:nxt + private[r]]
+        nxt += private[r]
+    return bt
+
+
+def test_plan_shared_prefix_groups():
+    g = qwen(num_blocks=100000)
+    sp = synthetic.config_shared_prefix(poison=False)
+    plan = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
+    before = bytes(plan)
+    pa.pa_plan_shared_prefix(g, plan, sp.qo_len, sp.kv_len, sp.block_tables, 256)
+    assert plan.num_prefix_groups == 1
+    assert (plan.prefix_first_req[0], plan.prefix_num_reqs[0], plan.prefix_blocks[0]) == (0, 16, 384)
+    assert 1 <= plan.prefix_splits <= 64 and plan.prefix_splits * 2 <= 384 // 8
+    # decode splits now cover only the private suffixes (2048 + U[0,255] tokens)
+    assert plan.split_blocks * plan.max_splits >= -(-(int(sp.kv_len.max()) - 6144) // 16)
+    assert plan.split_blocks < 263
+    n = 16 * plan.prefix_splits * 32
+    assert plan.workspace_bytes >= n * 129 * 4
+    assert bytes(plan) != before
+    # no shared run: the plan is left as it was
+    dec = synthetic.config_decode(poison=False)
+    p2 = pa.pa_plan(g, dec.qo_len, dec.kv_len, 256)
+    b2 = bytes(p2)
+    pa.pa_plan_shared_prefix(g, p2, dec.qo_len, dec.kv_len, dec.block_tables, 256)
+    assert bytes(p2) == b2 and p2.num_prefix_groups == 0
+    # a run shorter than the minimum is not a group
+    p3 = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
+    pa.pa_plan_shared_prefix(g, p3, sp.qo_len, sp.kv_len, sp.block_tables, 256, min_shared_blocks=385)
+    assert p3.num_prefix_groups == 0
+
+
+def test_plan_shared_prefix_runs_and_limits():
+    g = qwen(num_blocks=100000)
+    # 40 rows sharing 20 blocks: cut into groups of at most 32 requests
+    qo = [1] * 40
+    priv = [3 + (r % 5) for r in range(40)]
+    kv = [16 * (20 + priv[r]) - r % 7 for r in range(40)]
+    bt = _shared_tables(40, 20, priv, 32)
+    plan = pa.pa_plan(g, qo, kv, 256)
+    pa.pa_plan_shared_prefix(g, plan, qo, kv, bt, 256)
+    assert plan.num_prefix_groups == 2
+    assert [plan.prefix_num_reqs[i] for i in range(2)] == [32, 8]
+    assert [plan.prefix_blocks[i] for i in range(2)] == [20, 20]
+    # a prefill row breaks a run; two different shared runs make two groups
+    qo = [1, 1, 1, 9, 1, 1, 1, 1]
+    priv = [4] * 8
+    kv = [16 * 24] * 8
+    bt = _shared_tables(8, 20, priv, 32, split_at=5)
+    plan = pa.pa_plan(g, qo, kv, 256)
+    pa.pa_plan_shared_prefix(g, plan, qo, kv, bt, 256)
+    groups = [(plan.prefix_first_req[i], plan.prefix_num_reqs[i]) for i in range(plan.num_prefix_groups)]
+    assert groups == [(0, 3), (5, 3)]
+    # a row whose kv_len ends inside the shared run shares only whole blocks before its last
+    qo = [1, 1]
+    kv = [16 * 24, 16 * 18 + 1]
+    bt = _shared_tables(2, 20, [4, 0], 32)
+    plan = pa.pa_plan(g, qo, kv, 256)
+    pa.pa_plan_shared_prefix(g, plan, qo, kv, bt, 256)
+    assert plan.num_prefix_groups == 1 and plan.prefix_blocks[0] == 18
+    # lengths whose total differs from the plan's are rejected and leave the plan alone
+    before = bytes(plan)
+    with pytest.raises(pa.PaError) as e:
+        pa.pa_plan_shared_prefix(g, plan, [1, 2], [16 * 24, 16 * 19], bt, 256)
+    assert e.value.code == -2 and bytes(plan) == before
 
 
 def test_plan_errors():

@@ -29,9 +29,10 @@ def _gpu():
     yield
 
 
-def _run_gpu(wl, split_blocks=0, prefill_splits=0):
+def _run_gpu(wl, split_blocks=0, prefill_splits=0, cascade=False, num_cus=256):
     import paged_kv_attention_04_amd as pa
-    return pa.run_workload(wl, split_blocks=split_blocks, prefill_splits=prefill_splits)
+    return pa.run_workload(wl, split_blocks=split_blocks, prefill_splits=prefill_splits, cascade=cascade,
+                           num_cus=num_cus)
 
 
 def _errors(out, lse, ref, rows=None):
@@ -43,10 +44,10 @@ def _errors(out, lse, ref, rows=None):
     return float(np.max(np.abs(got - want))), float(np.max(np.abs(l_got - l_want)))
 
 
-def check(wl, split_blocks=0, label="", prefill_splits=0):
+def check(wl, split_blocks=0, label="", prefill_splits=0, cascade=False, num_cus=256):
     print(f"[gpu] {wl.name} {label} R={wl.num_reqs} total_q={wl.total_q} split={split_blocks} "
-          f"prefill_splits={prefill_splits}", flush=True)
-    kp, vp, out, lse = _run_gpu(wl, split_blocks, prefill_splits)
+          f"prefill_splits={prefill_splits} cascade={cascade} num_cus={num_cus}", flush=True)
+    kp, vp, out, lse = _run_gpu(wl, split_blocks, prefill_splits, cascade, num_cus)
     okp, ovp, ref = oracle.run_workload(wl)
     assert np.array_equal(kp, okp) and np.array_equal(vp, ovp), "append is not bit-exact"
     eo, el = _errors(out, lse, ref)
@@ -81,6 +82,25 @@ def test_qwen3_decode_step():
 
 def test_shared_prefix_decode():
     check(synthetic.config_shared_prefix())
+
+
+def test_shared_prefix_decode_cascade():
+    """The 384 shared blocks read once per KV head for all 16 rows, merged with each
+    row's private suffix."""
+    check(synthetic.config_shared_prefix(), cascade=True, label="cascade")
+
+
+@pytest.mark.parametrize("num_cus", [8, 32, 256])
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_cascade_groups(num_cus, q_scale):
+    """Every row shares its first 70 blocks (1120 tokens: the shared range ends inside a
+    128-key step).  The prefill row in the middle splits the decode rows into two groups
+    (rows 0-4 and 6-8); num_cus 8 / 32 / 256 gives 1 / 2 / 4 key splits of the shared
+    blocks.  Row 3 holds exactly one token past the shared range."""
+    wl = synthetic.build("cascade_groups", 71, 32, 8, qo_len=[1, 1, 1, 1, 1, 20, 1, 1, 1],
+                         kv_len=[1125, 1300, 1500, 1121, 1700, 1250, 1136, 1400, 2000], num_blocks=700,
+                         shared_prefix_blocks=70, q_scale=q_scale)
+    check(wl, cascade=True, num_cus=num_cus, label=f"cascade q*{q_scale:g}")
 
 
 def test_mixed_batch():
