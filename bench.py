@@ -83,7 +83,7 @@ def prefill_only_workload(poison=False):
 class Stepper:
     """Device copies of a workload, with `copies` KV-pool replicas rotated per step."""
 
-    def __init__(self, wl, copies: int, device="cuda"):
+    def __init__(self, wl, copies: int, device="cuda", cascade: bool = False):
         import torch
 
         import paged_kv_attention_04_amd as pa
@@ -101,16 +101,24 @@ class Stepper:
         self.kn, self.vn = pa.to_device(wl.k_new, device), pa.to_device(wl.v_new, device)
         self.out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device=device)
         self.lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=device)
-        self.plan = pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
+        self.cascade = cascade
+        self.plan = self.make_plan()
         self.ws = pa.workspace_for(self.plan, device)
         self.i = 0
+
+    def make_plan(self):
+        wl = self.wl
+        plan = self.pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
+        if self.cascade:
+            self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus)
+        return plan
 
     def step(self, attention_only: bool = False):
         pa, wl = self.pa, self.wl
         kp, vp = self.pools[self.i % len(self.pools)]
         self.i += 1
         if not attention_only:
-            self.plan = pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
+            self.plan = self.make_plan()
             pa.pa_append_kv(self.g, kp, vp, self.kn, self.vn, self.sm)
         pa.pa_attention_batch(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
                               self.lse, self.ws)
@@ -194,8 +202,9 @@ def kernel_only(which: str, reps: int):
     pa.lib()
     wl = {"decode": lambda: synthetic.config_decode(poison=False),
           "mixed": lambda: synthetic.config_mixed(poison=False),
+          "shared": lambda: synthetic.config_shared_prefix(poison=False),
           "prefill": prefill_only_workload}[which]()
-    st = Stepper(wl, 4)
+    st = Stepper(wl, 4, cascade=which == "shared")
     src = torch.empty(CALIBRATION_COPY_BYTES // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)                                           # calibration: reads and writes 256 MiB
@@ -271,7 +280,7 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=8, help="KV pool replicas rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--kernel-only", choices=["decode", "mixed", "prefill"])
+    ap.add_argument("--kernel-only", choices=["decode", "mixed", "shared", "prefill"])
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--summarize")
     ap.add_argument("--title", default="rocprofv3 summary")
@@ -314,6 +323,21 @@ def main(argv=None):
     t_m = event_time(sm, max(args.steps, 50))
     del sm
 
+    # shared-prefix decode (16 requests share 6144 tokens), plain and with the cascade plan
+    ws3 = synthetic.config_shared_prefix(poison=False)
+    ab3 = algorithmic_bytes(ws3)
+    shared = {"workload": "16 requests, kv_len 8192+U[0,255], first 384 blocks (6144 tokens) shared",
+              "kv_bytes_unique": ab3["kv_unique"], "kv_bytes_logical": ab3["kv_logical"]}
+    for cascade in (False, True):
+        s3 = Stepper(ws3, 4, cascade=cascade)
+        time_steps(s3, 10, 5, attention_only=True)
+        t3 = event_time(s3, max(args.steps // 2, 50))
+        shared["cascade" if cascade else "plain"] = {
+            "attention_us": round(t3 * 1e6, 3), "unique_gbs": round(ab3["attention"] / t3 / 1e9, 1),
+            "frac_of_hbm_peak": round(ab3["attention"] / t3 / 1e9 / HBM_PEAK_GBS, 4),
+            "prefix_groups": s3.plan.num_prefix_groups, "prefix_splits": s3.plan.prefix_splits}
+        del s3
+
     # the prefill chunk alone, against the bf16 matrix peak
     wp = prefill_only_workload()
     sp = Stepper(wp, 2)
@@ -349,6 +373,7 @@ def main(argv=None):
         "mixed_batch": {"workload": "1 prefill row (512 tokens at offset 4096) + 31 decode rows, 543 new tokens",
                         "tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
                         "attention_us": round(t_m * 1e6, 3)},
+        "shared_prefix": shared,
         "prefill_chunk": {"workload": "512 new tokens at kv offset 4096, 32 q / 8 kv heads, causal",
                           "us": round(t_p * 1e6, 3), "tflops": round(pflops / t_p / 1e12, 1),
                           "frac_of_bf16_mfma_peak": round(pflops / t_p / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
