@@ -191,6 +191,119 @@ def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
                       f"{int(wl.kv_len.sum())} KV tokens), fp64 C oracle, {el:.1f} s"}
 
 
+SWEEP_LAYERS = 36
+
+
+class LayerStack:
+    """One workload's tables, lengths, slots, Q and new K/V, with a separate device KV
+    pool per layer (the same block ids index every layer's pool: a block is one page per
+    layer); pool values are random bf16 drawn on the device."""
+
+    def __init__(self, wl, layers: int = SWEEP_LAYERS, cascade: bool = False, device="cuda"):
+        import torch
+
+        import paged_kv_attention_04_amd as pa
+
+        self.pa, self.wl, self.layers = pa, wl, layers
+        self.g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+        self.num_cus = pa.num_cus(0)
+        shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+        gen = torch.Generator(device=device).manual_seed(5)
+        self.pools = [tuple(torch.randn(shape, generator=gen, dtype=torch.bfloat16, device=device).view(torch.int16)
+                            for _ in range(2)) for _ in range(layers)]
+        self.q = pa.to_device(wl.q, device)
+        self.bt = pa.to_device(wl.block_tables, device)
+        self.qo_indptr = pa.to_device(wl.qo_indptr, device)
+        self.kv = pa.to_device(wl.kv_len, device)
+        self.sm = pa.to_device(wl.slot_mapping, device)
+        self.kn, self.vn = pa.to_device(wl.k_new, device), pa.to_device(wl.v_new, device)
+        self.out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device=device)
+        self.lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=device)
+        self.cascade = cascade
+        self.plan = self.make_plan()
+        self.ws = pa.workspace_for(self.plan, device)
+
+    def make_plan(self):
+        wl = self.wl
+        plan = self.pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
+        if self.cascade:
+            self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus)
+        return plan
+
+    def step(self, replan: bool = True):
+        """One model step: the plan once, then per layer the append and the attention."""
+        pa = self.pa
+        if replan:
+            self.plan = self.make_plan()
+        for kp, vp in self.pools:
+            pa.pa_append_kv(self.g, kp, vp, self.kn, self.vn, self.sm)
+            pa.pa_attention_batch(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
+                                  self.lse, self.ws)
+
+
+def median_step_seconds(fn, steps: int, warmup: int) -> float:
+    """Median over `steps` runs of fn, each bracketed by HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+
+def sweep36(steps: int = 20, warmup: int = 5) -> dict:
+    """36-layer decode steps at batch 1 (short, long), 8, 32, 64, eager and replayed from a
+    captured graph, and a 2048-token prompt in four 512-token chunks over 36 layers."""
+    import torch
+
+    import synthetic
+
+    res = {"layers": SWEEP_LAYERS, "decode": []}
+    for batch, long_only in ((1, False), (1, True), (8, False), (32, False), (64, False)):
+        wl = synthetic.config_sweep_decode(batch, 0, long_only=long_only, poison=False, fill_pools=False)
+        ab = algorithmic_bytes(wl)
+        stack = LayerStack(wl, cascade=True)
+        t = median_step_seconds(stack.step, steps, warmup)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            stack.step(replan=False)                    # warm up on the capture stream's side
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            stack.step(replan=False)
+        tg = median_step_seconds(graph.replay, steps, warmup)
+        unique = ab["step"] * SWEEP_LAYERS
+        logical = (ab["kv_logical"] - ab["kv_unique"] + ab["step"]) * SWEEP_LAYERS
+        res["decode"].append({
+            "batch": batch, "context": "8192 (6144 shared)" if long_only else ("2048" if batch == 1 else "half 2048, half 8192 sharing 6144"),
+            "step_ms": round(t * 1e3, 4), "graph_step_ms": round(tg * 1e3, 4),
+            "unique_gb_per_step": round(unique / 1e9, 4), "unique_gbs": round(unique / tg / 1e9, 1),
+            "logical_gbs": round(logical / tg / 1e9, 1), "frac_of_hbm_peak": round(unique / tg / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(batch / tg, 1), "prefix_groups": stack.plan.num_prefix_groups})
+        del stack, graph
+        torch.cuda.empty_cache()
+    # 2048-token prompt, four 512-token chunks, 36 layers each
+    _, chunks = synthetic.prompt_chunks(seed=5, prompt_len=2048, chunk=512, num_blocks=256, poison=False)
+    stacks = [LayerStack(c) for c in chunks]
+    flops = sum(prefill_flops(c) for c in chunks) * SWEEP_LAYERS
+
+    def prompt():
+        for st in stacks:
+            st.step(replan=True)
+    t = median_step_seconds(prompt, max(steps // 2, 5), 2)
+    res["prefill_2k_in_4x512"] = {"ms": round(t * 1e3, 4), "tflops": round(flops / t / 1e12, 1),
+                                  "frac_of_bf16_mfma_peak": round(flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                  "tokens_per_s": round(2048 / t, 1)}
+    return res
+
+
 def kernel_only(which: str, reps: int):
     """Attention launches only (plus one calibration copy of known size), for counters."""
     import torch
@@ -279,6 +392,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=8, help="KV pool replicas rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 36-layer sweep")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-only", choices=["decode", "mixed", "shared", "prefill"])
     ap.add_argument("--reps", type=int, default=20)
@@ -378,6 +492,8 @@ def main(argv=None):
                           "us": round(t_p * 1e6, 3), "tflops": round(pflops / t_p / 1e12, 1),
                           "frac_of_bf16_mfma_peak": round(pflops / t_p / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
     }
+    if not args.no_sweep:
+        line["sweep_36_layers"] = sweep36()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(synthetic.config_decode(poison=False), args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -238,10 +238,13 @@ def config_mixed(seed: int = 4, poison: bool = True, num_blocks: int = POOL_BLOC
 
 
 def config_sweep_decode(batch: int, layer: int, seed: int = 5, poison: bool = True,
-                        num_blocks: Optional[int] = None, long_only: bool = False) -> Workload:
+                        num_blocks: Optional[int] = None, long_only: bool = False,
+                        fill_pools: bool = True) -> Workload:
     """One layer of the 36-layer decode sweep: half the rows have a 2048-token context and
     half an 8192-token context whose first 6144 tokens are a shared prefix; the step
-    appends one token per row (kv_len 2049 / 8193).  Batch 1 is short unless ``long_only``."""
+    appends one token per row (kv_len 2049 / 8193).  Batch 1 is short unless ``long_only``.
+    ``fill_pools=False`` leaves the pools empty (zero-size arrays): tables, lengths, slots,
+    Q and new K/V only, for callers that fill device pools themselves."""
     if batch == 1:
         kv = [8193] if long_only else [2049]
     else:
@@ -255,11 +258,11 @@ def config_sweep_decode(batch: int, layer: int, seed: int = 5, poison: bool = Tr
     need = nshort * 129 + (384 + nlong * (513 - 384) if nlong else 0)
     nblocks = num_blocks if num_blocks is not None else max(POOL_BLOCKS_12GIB, need)
     wl = _build_short_long(f"sweep_b{batch}_layer{layer}", [seed, layer, batch], kv, shared, nblocks,
-                           poison)
+                           poison, fill_pools)
     return wl
 
 
-def _build_short_long(name, seed_words, kv, shared_blocks, num_blocks, poison):
+def _build_short_long(name, seed_words, kv, shared_blocks, num_blocks, poison, fill_pools=True):
     """Placement where only the rows longer than the shared prefix alias it."""
     seed = int(np.random.SeedSequence(seed_words).generate_state(1)[0])
     s_len, s_place, s_k, s_v, s_new, s_q = _streams(seed)
@@ -280,10 +283,11 @@ def _build_short_long(name, seed_words, kv, shared_blocks, num_blocks, poison):
     if cur > num_blocks:
         raise ValueError("pool too small")
     fill = BF16_NAN if poison else np.uint16(0)
-    k_pool = np.full((num_blocks, Hkv, B, D), fill, np.uint16)
-    v_pool = np.full((num_blocks, Hkv, B, D), fill, np.uint16)
+    pool_shape = (num_blocks, Hkv, B, D) if fill_pools else (0, Hkv, B, D)
+    k_pool = np.full(pool_shape, fill, np.uint16)
+    v_pool = np.full(pool_shape, fill, np.uint16)
     filled = set()
-    for r in range(R):
+    for r in range(R if fill_pools else 0):
         ctx = int(kv[r]) - 1
         ncb = -(-ctx // B)
         kd = f32_to_bf16_bits(s_k.standard_normal((ncb, Hkv, B, D), dtype=np.float32))

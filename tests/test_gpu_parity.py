@@ -207,3 +207,53 @@ def test_shared_prefix_equals_duplicated_blocks_bit_exact():
 def test_edge_shapes(qo, kv):
     need = sum(-(-k // 16) for k in kv)
     check(synthetic.build("edge", 71 + len(qo), 8, 2, qo_len=qo, kv_len=kv, num_blocks=need + 3))
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_replay_matches_eager():
+    """The append and the attention captured into one graph and replayed several times,
+    with eager work and synchronisations between the replays: every replay gives the
+    eager result bit for bit (the split counters reset themselves; nothing is cleared
+    with a memset)."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    wl = synthetic.build("graph_mixed", 81, 32, 8, qo_len=[1, 40, 1, 1, 1], kv_len=[900, 1200, 1500, 2300, 1600],
+                         num_blocks=600, shared_prefix_blocks=40, poison=False)
+    g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256, split_blocks=20, prefill_splits=2)
+    pa.pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, 256)
+    assert plan.max_splits > 1 and plan.num_prefix_groups == 1 and plan.prefill_splits == 2
+    d = {k: pa.to_device(getattr(wl, k)) for k in ("k_pool", "v_pool", "q", "block_tables", "qo_indptr", "kv_len",
+                                                   "slot_mapping", "k_new", "v_new")}
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    ws = pa.workspace_for(plan)
+
+    def step():
+        pa.pa_append_kv(g, d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], d["slot_mapping"])
+        pa.pa_attention_batch(g, plan, d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["qo_indptr"],
+                              d["kv_len"], out, lse, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(4):
+        out.fill_(0)
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[gpu] graph replay {i}", flush=True)
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i} differs from the eager result"
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
