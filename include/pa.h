@@ -215,6 +215,28 @@ pa_status pa_validate_batch(const pa_geometry* geometry, int32_t num_reqs, const
 pa_status pa_validate_append(const pa_geometry* geometry, const int32_t* slot_mapping_host, int32_t n_tokens,
                              int32_t* bad_index);
 
+/*
+ * Copy whole blocks inside the pools: for i < n, the K and V tiles of every KV head of
+ * block src[i] are copied to block dst[i].  This is the copy-on-write step of a shared
+ * block that one request is about to write into: the request gets a private copy and
+ * its table is pointed at it (book section 8.3.2, copy-on-write of a shared tail
+ * block).  Device pointers: k_pool, v_pool (written in place), src_blocks, dst_blocks
+ * (int32 [n]).  Pairs with an id outside [0, num_blocks) are skipped.  A dst that is
+ * also a src, or a dst that repeats, is invalid (pa_validate_copy reports it); the
+ * result is then unspecified.  Errors: PA_ERR_NULL, PA_ERR_UNSUPPORTED, PA_ERR_SHAPE
+ * (n < 0), PA_ERR_HIP.
+ */
+pa_status pa_copy_blocks(const pa_geometry* geometry, void* k_pool, void* v_pool, const int32_t* src_blocks,
+                         const int32_t* dst_blocks, int32_t n, void* stream);
+
+/*
+ * Host-side check of a block-copy list: every id is in [0, num_blocks), no dst repeats
+ * and no dst is also a src.  Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE or PA_ERR_RANGE;
+ * *bad_index (may be NULL) receives the offending pair index.
+ */
+pa_status pa_validate_copy(const pa_geometry* geometry, const int32_t* src_blocks_host,
+                           const int32_t* dst_blocks_host, int32_t n, int32_t* bad_index);
+
 /* Compute-unit count of a HIP device (for pa_plan).  PA_ERR_HIP on failure. */
 pa_status pa_query_num_cus(int32_t device, int32_t* num_cus);
 

@@ -44,6 +44,7 @@ def _load():
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.oracle_append.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32]
+    lib.oracle_copy_blocks.argtypes = [P, P, P, P, i32, i32, i32, i32, i32]
     lib.oracle_append.restype = ctypes.c_int
     lib.oracle_attention.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f64,
                                      P, P, P, P, P, P]
@@ -97,6 +98,20 @@ def append(k_pool, v_pool, k_new, v_new, slot_mapping, num_kv_heads, head_dim, b
                                int(num_kv_heads), int(head_dim), int(block_size), int(num_blocks))
     if rc != 0:
         raise ValueError(f"oracle_append failed with code {rc}")
+    return kp, vp
+
+
+def copy_blocks(k_pool, v_pool, src, dst, num_kv_heads, head_dim, block_size, num_blocks):
+    """Copies of the pools with block src[i] copied to block dst[i]; returns (k_pool, v_pool)."""
+    kp = np.array(k_pool, dtype=np.uint16, copy=True)
+    vp = np.array(v_pool, dtype=np.uint16, copy=True)
+    s, d = _c(src, np.int32), _c(dst, np.int32)
+    if s.shape != d.shape:
+        raise ValueError("src and dst differ in length")
+    rc = _load().oracle_copy_blocks(_ptr(kp), _ptr(vp), _ptr(s), _ptr(d), int(s.size), int(num_kv_heads),
+                                    int(head_dim), int(block_size), int(num_blocks))
+    if rc != 0:
+        raise ValueError(f"oracle_copy_blocks failed with code {rc}")
     return kp, vp
 
 

@@ -119,6 +119,28 @@ int oracle_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new, con
 }
 
 /*
+ * block copy (book section 8.3.2, copy-on-write: the writer gets a private copy of a
+ * shared block): block src[i]'s tiles of every KV head, K and V, become block dst[i]'s.
+ * The pairs are applied in order; a valid list never writes a block it later reads.
+ */
+int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks)
+{
+    if (!k_pool || !v_pool || (n > 0 && (!src || !dst)) || n < 0)
+        return ORACLE_BAD_ARG;
+    const size_t block_elems = (size_t)num_kv_heads * block_size * head_dim;
+    for (int32_t i = 0; i < n; ++i) {
+        if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
+            continue;                      /* out-of-range pair: skipped */
+        memcpy(k_pool + (size_t)dst[i] * block_elems, k_pool + (size_t)src[i] * block_elems,
+               sizeof(uint16_t) * block_elems);
+        memcpy(v_pool + (size_t)dst[i] * block_elems, v_pool + (size_t)src[i] * block_elems,
+               sizeof(uint16_t) * block_elems);
+    }
+    return ORACLE_OK;
+}
+
+/*
  * attention.  q: [total_q][Hq][D] bf16 with rows of request r at qo_indptr[r]..;
  * out: same shape bf16; lse: [total_q][Hq] float.  block_tables: [R][max_blocks].
  * row_select (may be NULL): if given, only requests with row_select[r] != 0 are

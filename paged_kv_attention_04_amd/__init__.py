@@ -81,6 +81,8 @@ def lib():
     L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_validate_batch.argtypes = [G, i32, P, P, P, i32, P]
     L.pa_validate_append.argtypes = [G, P, i32, P]
+    L.pa_copy_blocks.argtypes = [G, P, P, P, P, i32, P]
+    L.pa_validate_copy.argtypes = [G, P, P, i32, P]
     L.pa_query_num_cus.argtypes = [i32, P]
     for fn in ("pa_plan", "pa_append_kv", "pa_attention_batch", "pa_validate_batch", "pa_validate_append",
                "pa_query_num_cus"):
@@ -212,6 +214,33 @@ def pa_validate_append(geometry: Geometry, slot_mapping):
     sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
     bad = ctypes.c_int32(-1)
     rc = lib().pa_validate_append(ctypes.byref(geometry), _np_ptr(sm), int(sm.size), ctypes.byref(bad))
+    return rc, int(bad.value)
+
+
+def pa_copy_blocks(geometry: Geometry, k_pool, v_pool, src_blocks, dst_blocks, stream=None) -> None:
+    """Device copy of whole blocks (all KV heads, K and V): block src[i] -> block dst[i]."""
+    import torch
+    n = int(src_blocks.numel())
+    if int(dst_blocks.numel()) != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    if n == 0:
+        return
+    bf, i32 = _bf16_types(), (torch.int32,)
+    _check("pa_copy_blocks", lib().pa_copy_blocks(
+        ctypes.byref(geometry), _dev_ptr(k_pool, bf, "k_pool"), _dev_ptr(v_pool, bf, "v_pool"),
+        _dev_ptr(src_blocks, i32, "src_blocks"), _dev_ptr(dst_blocks, i32, "dst_blocks"), n,
+        _stream_handle(stream)))
+
+
+def pa_validate_copy(geometry: Geometry, src_blocks, dst_blocks):
+    """(status, bad pair index) for a host block-copy list."""
+    import numpy as np
+    s = np.ascontiguousarray(src_blocks, dtype=np.int32)
+    d = np.ascontiguousarray(dst_blocks, dtype=np.int32)
+    if s.shape != d.shape:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    bad = ctypes.c_int32(-1)
+    rc = lib().pa_validate_copy(ctypes.byref(geometry), _np_ptr(s), _np_ptr(d), int(s.size), ctypes.byref(bad))
     return rc, int(bad.value)
 
 

@@ -283,6 +283,30 @@ extern "C" pa_status pa_validate_batch(const pa_geometry* g, int32_t num_reqs, c
     return PA_OK;
 }
 
+extern "C" pa_status pa_validate_copy(const pa_geometry* g, const int32_t* src, const int32_t* dst, int32_t n,
+                                      int32_t* bad_index)
+{
+    if (bad_index)
+        *bad_index = -1;
+    if (!g || (n > 0 && (!src || !dst)))
+        return PA_ERR_NULL;
+    if (n < 0)
+        return PA_ERR_SHAPE;
+    std::unordered_set<int32_t> dsts, srcs;
+    for (int32_t i = 0; i < n; ++i)
+        srcs.insert(src[i]);
+    for (int32_t i = 0; i < n; ++i) {
+        const bool bad = src[i] < 0 || src[i] >= g->num_blocks || dst[i] < 0 || dst[i] >= g->num_blocks ||
+                         !dsts.insert(dst[i]).second || srcs.count(dst[i]);
+        if (bad) {
+            if (bad_index)
+                *bad_index = i;
+            return PA_ERR_RANGE;
+        }
+    }
+    return PA_OK;
+}
+
 extern "C" pa_status pa_validate_append(const pa_geometry* g, const int32_t* slot_mapping, int32_t n_tokens,
                                         int32_t* bad_index)
 {

@@ -148,6 +148,31 @@ __global__ __launch_bounds__(256) void pa_append_scatter(uint16_t* __restrict__ 
     reinterpret_cast<u32x4*>(v_pool)[dst] = reinterpret_cast<const u32x4*>(v_new)[src];
 }
 
+// ------------------------------------------------------------------------------ block copy
+
+// One thread per 16 bytes of a (pair, pool, KV head) tile: pairs x 2 pools x Hkv x 256
+// threads; each 256 consecutive threads move one contiguous 4 KiB tile.
+__global__ __launch_bounds__(256) void pa_copy_scatter(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+                                                       const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                                                       int32_t n, int32_t num_kv_heads, int32_t num_blocks)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_pair = (int64_t)2 * num_kv_heads * 256;
+    const int64_t pair = t / per_pair;
+    if (pair >= n)
+        return;
+    const int32_t s = src[pair], d = dst[pair];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+        return;
+    const int64_t rem = t - pair * per_pair;
+    uint16_t* pool = (rem / ((int64_t)num_kv_heads * 256)) ? v_pool : k_pool;
+    const int64_t within = rem % ((int64_t)num_kv_heads * 256);    // chunk within one block's Hkv tiles
+    const int64_t blk_chunks = (int64_t)num_kv_heads * 256;         // 16-byte chunks per block (all KV heads)
+    const u32x4* from = reinterpret_cast<const u32x4*>(pool) + (int64_t)s * blk_chunks + within;
+    u32x4* to = reinterpret_cast<u32x4*>(pool) + (int64_t)d * blk_chunks + within;
+    *to = *from;
+}
+
 // ------------------------------------------------------------------------------ decode
 
 struct DecodeParams {
@@ -1248,6 +1273,29 @@ extern "C" pa_status pa_append_kv(const pa_geometry* g, void* k_pool, void* v_po
                        static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
                        n_tokens, g->num_kv_heads, (int64_t)g->num_blocks * kBlock);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" pa_status pa_copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
+                                    const int32_t* dst_blocks, int32_t n, void* stream)
+{
+    if (!g)
+        return PA_ERR_NULL;
+    if (!pa::geometry_supported(g))
+        return PA_ERR_UNSUPPORTED;
+    if (n < 0)
+        return PA_ERR_SHAPE;
+    if (n == 0)
+        return PA_OK;
+    if (!k_pool || !v_pool || !src_blocks || !dst_blocks)
+        return PA_ERR_NULL;
+    const int64_t threads = (int64_t)n * 2 * g->num_kv_heads * 256;
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX)
+        return PA_ERR_SHAPE;
+    hipLaunchKernelGGL(pa_copy_scatter, dim3((uint32_t)blocks), dim3(256), 0, as_stream(stream),
+                       static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), src_blocks, dst_blocks, n,
+                       g->num_kv_heads, g->num_blocks);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

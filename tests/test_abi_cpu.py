@@ -256,6 +256,18 @@ def test_validate_append():
     assert pa.pa_validate_append(g, [3, 9, 3]) == (-3, 2)
 
 
+def test_validate_copy():
+    g = pa.Geometry.make(8, 2, 12)
+    assert pa.pa_validate_copy(g, [3, 7, 3], [9, 1, 11]) == (0, -1)    # one source, several copies
+    assert pa.pa_validate_copy(g, [], []) == (0, -1)
+    assert pa.pa_validate_copy(g, [3, 12], [9, 1]) == (-3, 1)          # src out of range
+    assert pa.pa_validate_copy(g, [3, 4], [-1, 1]) == (-3, 0)          # dst out of range
+    assert pa.pa_validate_copy(g, [3, 4], [9, 9]) == (-3, 1)           # dst repeats
+    assert pa.pa_validate_copy(g, [3, 4], [9, 3]) == (-3, 1)           # dst is also a src
+    with pytest.raises(ValueError):
+        pa.pa_validate_copy(g, [1, 2], [3])
+
+
 def test_entry_points_reject_bad_arguments_before_launch(lib):
     g = qwen()
     plan = pa.pa_plan(g, [1], [100])
@@ -281,6 +293,13 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.pa_append_kv(ctypes.byref(g), one, one, one, one, one, -1, None) == -2
     assert lib.pa_append_kv(ctypes.byref(g), None, one, one, one, one, 1, None) == -1
     assert lib.pa_append_kv(ctypes.byref(g), None, None, None, None, None, 0, None) == 0
+    # block copy: the same checks
+    rc = lib.pa_copy_blocks(ctypes.byref(pa.Geometry.make(32, 8, 10, head_dim=64)), one, one, one, one, 1, None)
+    assert rc == -5
+    assert lib.pa_copy_blocks(ctypes.byref(g), one, one, one, one, -1, None) == -2
+    assert lib.pa_copy_blocks(ctypes.byref(g), one, None, one, one, 1, None) == -1
+    assert lib.pa_copy_blocks(None, one, one, one, one, 1, None) == -1
+    assert lib.pa_copy_blocks(ctypes.byref(g), None, None, None, None, 0, None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

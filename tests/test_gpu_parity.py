@@ -257,3 +257,107 @@ def test_graph_replay_matches_eager():
         step()                                   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+
+
+# ------------------------------------------------------------------ block copy (copy-on-write)
+
+def _geometry(wl):
+    import paged_kv_attention_04_amd as pa
+    return pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale, wl.head_dim, wl.block_size)
+
+
+@pytest.mark.parametrize("num_blocks,n_pairs", [(64, 1), (4096, 1500)])
+def test_copy_blocks_bit_exact(num_blocks, n_pairs):
+    """Whole pools compared bit for bit: copied blocks, every other block, and two
+    out-of-range pairs that must be skipped.  Pool words are random bit patterns."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    print(f"[gpu] copy_blocks num_blocks={num_blocks} pairs={n_pairs}", flush=True)
+    rng = np.random.default_rng(num_blocks + n_pairs)
+    Hkv, B, D = 8, 16, 128
+    kp = rng.integers(0, 2**16, (num_blocks, Hkv, B, D), dtype=np.uint16)
+    vp = rng.integers(0, 2**16, (num_blocks, Hkv, B, D), dtype=np.uint16)
+    perm = rng.permutation(num_blocks)
+    dst = perm[:n_pairs].astype(np.int32)
+    src = rng.choice(perm[n_pairs:], n_pairs).astype(np.int32)      # sources may repeat
+    src = np.concatenate([src, [-1, 3]]).astype(np.int32)
+    dst = np.concatenate([dst, [5, num_blocks]]).astype(np.int32)
+    wl_g = pa.Geometry.make(32, Hkv, num_blocks)
+    assert pa.pa_validate_copy(wl_g, src, dst)[0] == -3       # PA_ERR_RANGE
+    okp, ovp = oracle.copy_blocks(kp, vp, src, dst, Hkv, D, B, num_blocks)
+    dk, dv = pa.to_device(kp), pa.to_device(vp)
+    pa.pa_copy_blocks(wl_g, dk, dv, pa.to_device(src), pa.to_device(dst))
+    pa.pa_copy_blocks(wl_g, dk, dv, pa.to_device(src[:0]), pa.to_device(dst[:0]))    # empty list: no-op
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy().view(np.uint16), okp)
+    assert np.array_equal(dv.cpu().numpy().view(np.uint16), ovp)
+
+
+def _forked_workload(seed, n_fork, prompt):
+    """n_fork decode rows forked from one prompt of ``prompt`` tokens: every block is
+    shared, the last one partly filled, so each row's next token lands in one slot."""
+    nb = -(-prompt // 16)
+    assert prompt % 16, "the shared tail must be partly filled"
+    wl = synthetic.build("forked", seed, 32, 8, qo_len=[1] * n_fork, kv_len=[prompt + 1] * n_fork,
+                         num_blocks=nb + n_fork + 8, shared_prefix_blocks=nb)
+    assert len(set(wl.slot_mapping.tolist())) == 1
+    return wl
+
+
+def _copy_on_write(wl):
+    """Book section 8.3.2: every row but the first gets a private copy of the shared tail
+    block before it writes.  Returns (src, dst, new block tables, new slot mapping)."""
+    bt = wl.block_tables.copy()
+    used = set(bt[bt >= 0].ravel().tolist())
+    free = [b for b in range(wl.num_blocks) if b not in used]
+    tail = (int(wl.kv_len[0]) - 1) // wl.block_size
+    src, dst = [], []
+    for r in range(1, wl.num_reqs):
+        src.append(int(bt[r, tail]))
+        dst.append(free[r - 1])
+        bt[r, tail] = free[r - 1]
+    slots = np.array([synthetic.slot_of(bt[r], int(wl.kv_len[r]) - 1, wl.block_size) for r in range(wl.num_reqs)],
+                     dtype=np.int32)
+    return np.array(src, np.int32), np.array(dst, np.int32), bt, slots
+
+
+@pytest.mark.parametrize("cascade", [False, True])
+def test_copy_on_write_fork_step(cascade):
+    """Rows forked from one prompt: copy the shared tail, repoint the tables, append each
+    row's token and attend, all on the device; the oracle takes the same steps.  Pools
+    bit-exact, attention within the bars, and each row sees its own token."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    wl = _forked_workload(41, 8, 16 * 37 + 5)
+    src, dst, bt, slots = _copy_on_write(wl)
+    g = _geometry(wl)
+    assert pa.pa_validate_copy(g, src, dst) == (0, -1)
+    assert pa.pa_validate_append(g, slots) == (0, -1)
+    print(f"[gpu] copy-on-write fork rows={wl.num_reqs} kv={int(wl.kv_len[0])} cascade={cascade}", flush=True)
+    okp, ovp = oracle.copy_blocks(wl.k_pool, wl.v_pool, src, dst, wl.num_kv_heads, wl.head_dim, wl.block_size,
+                                  wl.num_blocks)
+    okp, ovp = oracle.append(okp, ovp, wl.k_new, wl.v_new, slots, wl.num_kv_heads, wl.head_dim, wl.block_size,
+                             wl.num_blocks)
+    ref = oracle.attention(wl.q, okp, ovp, bt, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                           wl.block_size, wl.num_blocks, wl.scale)
+
+    dk, dv = pa.to_device(wl.k_pool), pa.to_device(wl.v_pool)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len)
+    if cascade:
+        pa.pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, bt)
+        assert plan.num_prefix_groups == 1
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    pa.pa_copy_blocks(g, dk, dv, pa.to_device(src), pa.to_device(dst))
+    pa.pa_append_kv(g, dk, dv, pa.to_device(wl.k_new), pa.to_device(wl.v_new), pa.to_device(slots))
+    pa.pa_attention_batch(g, plan, pa.to_device(wl.q), dk, dv, pa.to_device(bt), pa.to_device(wl.qo_indptr),
+                          pa.to_device(wl.kv_len), out, lse, pa.workspace_for(plan))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy().view(np.uint16), okp)
+    assert np.array_equal(dv.cpu().numpy().view(np.uint16), ovp)
+    eo, el = _errors(out.cpu().numpy().view(np.uint16), lse.cpu().numpy(), ref)
+    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+    # the rows' outputs differ: each attended to its own newest token
+    o = bf16_bits_to_f32(out.cpu().numpy().view(np.uint16))
+    assert all(not np.array_equal(o[0], o[r]) for r in range(1, wl.num_reqs))

@@ -410,3 +410,77 @@ def test_round_bf16_double_only_cases():
     assert oracle.round_bf16(2.0 ** -133)[0] == 0x0001
     assert oracle.round_bf16(2.0 ** 128)[0] == 0x7F80
     assert oracle.round_bf16(float("nan"))[0] == 0x7FC0
+
+
+# ------------------------------------------------------------------ block copy (copy-on-write)
+
+def test_copy_blocks_moves_whole_blocks_only():
+    """Block src -> dst for every KV head, K and V; nothing else changes; an out-of-range
+    pair is skipped; the inputs are not modified (checked with numpy indexing)."""
+    rng = np.random.default_rng(3)
+    nb, Hkv, B, D = 12, 2, 16, 128
+    kp = rng.integers(0, 2**16, (nb, Hkv, B, D), dtype=np.uint16)
+    vp = rng.integers(0, 2**16, (nb, Hkv, B, D), dtype=np.uint16)
+    kp0, vp0 = kp.copy(), vp.copy()
+    src, dst = np.array([3, 7, 0, 5], np.int32), np.array([9, 1, 11, 99], np.int32)
+    k2, v2 = oracle.copy_blocks(kp, vp, src, dst, Hkv, D, B, nb)
+    ek, ev = kp0.copy(), vp0.copy()
+    for s_, d_ in zip(src[:3], dst[:3]):
+        ek[d_], ev[d_] = kp0[s_], vp0[s_]
+    assert np.array_equal(k2, ek) and np.array_equal(v2, ev)
+    assert np.array_equal(kp, kp0) and np.array_equal(vp, vp0)
+
+
+def _cow_workload():
+    # two decode rows share all three blocks; the third is partly filled (positions 32..38)
+    # and both rows' new token (position 39) maps to the same slot of it
+    wl = synthetic.build("cow", 9, 8, 2, qo_len=[1, 1], kv_len=[40, 40], num_blocks=16,
+                         shared_prefix_blocks=3, poison=False)
+    assert np.array_equal(wl.block_tables[0, :3], wl.block_tables[1, :3])
+    assert wl.slot_mapping[0] == wl.slot_mapping[1]
+    return wl
+
+
+def _attend(wl, kp, vp, bt):
+    return oracle.attention(wl.q, kp, vp, bt, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
+                            wl.head_dim, wl.block_size, wl.num_blocks, wl.scale)
+
+
+def _unshared_reference(wl):
+    """Each request owns private blocks holding the same context; each appends its own token."""
+    used = set(wl.block_tables[wl.block_tables >= 0].ravel().tolist())
+    spare = [b for b in range(wl.num_blocks) if b not in used]
+    kp, vp, bt = wl.k_pool.copy(), wl.v_pool.copy(), wl.block_tables.copy()
+    for r in range(2):
+        mine = spare[3 * r: 3 * r + 3]
+        kp[mine], vp[mine] = wl.k_pool[bt[r, :3]], wl.v_pool[bt[r, :3]]
+        bt[r, :3] = mine
+        s = synthetic.slot_of(bt[r], 39, wl.block_size)
+        kp[s // wl.block_size, :, s % wl.block_size] = wl.k_new[r]
+        vp[s // wl.block_size, :, s % wl.block_size] = wl.v_new[r]
+    return _attend(wl, kp, vp, bt)
+
+
+def test_copy_on_write_gives_each_branch_its_own_token():
+    """Book section 8.3.2: before a request writes into a physical block it shares, the
+    block is copied and that request's table is pointed at the copy.  After the copy and
+    both appends, each request's attention equals the one over a layout where nothing was
+    shared; appending without the copy makes the two requests' tokens collide."""
+    wl = _cow_workload()
+    ref = _unshared_reference(wl)
+    bt = wl.block_tables.copy()
+    used = set(bt[bt >= 0].ravel().tolist())
+    free = [b for b in range(wl.num_blocks) if b not in used][-1]
+    kp, vp = oracle.copy_blocks(wl.k_pool, wl.v_pool, [int(bt[1, 2])], [free], wl.num_kv_heads, wl.head_dim,
+                                wl.block_size, wl.num_blocks)
+    bt[1, 2] = free
+    slots = [synthetic.slot_of(bt[r], 39, wl.block_size) for r in range(2)]
+    kp, vp = oracle.append(kp, vp, wl.k_new, wl.v_new, slots, wl.num_kv_heads, wl.head_dim, wl.block_size,
+                           wl.num_blocks)
+    res = _attend(wl, kp, vp, bt)
+    assert np.array_equal(res["out"], ref["out"]) and np.array_equal(res["lse"], ref["lse"])
+    # without the copy the second append overwrites the first request's token
+    kp, vp = oracle.append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
+                           wl.head_dim, wl.block_size, wl.num_blocks)
+    bad = _attend(wl, kp, vp, wl.block_tables)
+    assert not np.array_equal(bad["out"][0], ref["out"][0])
