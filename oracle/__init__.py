@@ -55,6 +55,18 @@ def _load():
     lib.oracle_round_bf16_array.restype = None
     lib.oracle_slot.argtypes = [P, i64, i32]
     lib.oracle_slot.restype = i64
+    lib.oracle_attention_q8.argtypes = lib.oracle_attention.argtypes
+    lib.oracle_attention_q8.restype = ctypes.c_int
+    lib.oracle_append_q8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32]
+    lib.oracle_append_q8.restype = ctypes.c_int
+    lib.oracle_quantize_q8_rows.argtypes = [P, i64, i32, P, P]
+    lib.oracle_quantize_q8_rows.restype = ctypes.c_int
+    lib.oracle_q8_tile_bytes.argtypes = [i32, i32]
+    lib.oracle_q8_tile_bytes.restype = i64
+    lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+    lib.oracle_float_to_half.restype = ctypes.c_uint16
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = f64
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -115,12 +127,57 @@ def copy_blocks(k_pool, v_pool, src, dst, num_kv_heads, head_dim, block_size, nu
     return kp, vp
 
 
+def float_to_half(x: float) -> int:
+    """binary32 value -> binary16 bits, to nearest with ties to even."""
+    return int(_load().oracle_float_to_half(float(np.float32(x))))
+
+
+def half_to_double(h: int) -> float:
+    return float(_load().oracle_half_to_double(int(h)))
+
+
+def q8_tile_bytes(head_dim: int, block_size: int) -> int:
+    """Bytes of one q8_0 (block, KV head) tile: [B][D] int8 codes, then [B][D/32] binary16 scales."""
+    return int(_load().oracle_q8_tile_bytes(int(head_dim), int(block_size)))
+
+
+def quantize_q8_rows(x, head_dim: int):
+    """bf16 rows [..., D] -> (int8 codes [..., D], binary16 scale bits [..., D/32])."""
+    xa = _c(x, np.uint16)
+    n = xa.size // head_dim
+    codes = np.empty(xa.shape, np.int8)
+    scales = np.empty(xa.shape[:-1] + (head_dim // 32,), np.uint16)
+    rc = _load().oracle_quantize_q8_rows(_ptr(xa), n, int(head_dim), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_quantize_q8_rows failed with code {rc}")
+    return codes, scales
+
+
+def append_q8(k_pool, v_pool, k_new, v_new, slot_mapping, num_kv_heads, head_dim, block_size, num_blocks):
+    """Quantise new bf16 K/V rows into copies of q8_0 pools [num_blocks][Hkv][tile bytes]."""
+    kp = np.array(k_pool, dtype=np.uint8, copy=True)
+    vp = np.array(v_pool, dtype=np.uint8, copy=True)
+    kn, vn = _c(k_new, np.uint16), _c(v_new, np.uint16)
+    sm = _c(slot_mapping, np.int32)
+    rc = _load().oracle_append_q8(_ptr(kp), _ptr(vp), _ptr(kn), _ptr(vn), _ptr(sm), int(sm.size),
+                                  int(num_kv_heads), int(head_dim), int(block_size), int(num_blocks))
+    if rc != 0:
+        raise ValueError(f"oracle_append_q8 failed with code {rc}")
+    return kp, vp
+
+
 def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_kv_heads, head_dim,
-              block_size, num_blocks, scale, row_select=None, want_f64: bool = False):
+              block_size, num_blocks, scale, row_select=None, want_f64: bool = False, kv_format: str = "bf16"):
     """Returns dict(out=bf16 bits [total_q][Hq][D], lse=float32 [total_q][Hq], pairs=int,
-    and out_f64 / lse_f64 when ``want_f64``).  Rows not in ``row_select`` are left as zero."""
+    and out_f64 / lse_f64 when ``want_f64``).  Rows not in ``row_select`` are left as zero.
+    ``kv_format`` "q8_0" reads q8_0 pools [num_blocks][Hkv][tile bytes] (uint8)."""
     qa = _c(q, np.uint16)
-    kp, vp = _c(k_pool, np.uint16), _c(v_pool, np.uint16)
+    if kv_format == "q8_0":
+        kp, vp, fn = _c(k_pool, np.uint8), _c(v_pool, np.uint8), _load().oracle_attention_q8
+    elif kv_format == "bf16":
+        kp, vp, fn = _c(k_pool, np.uint16), _c(v_pool, np.uint16), _load().oracle_attention
+    else:
+        raise ValueError(f"unknown kv_format {kv_format}")
     bt = _c(block_tables, np.int32)
     qo, kv = _c(qo_len, np.int32), _c(kv_len, np.int32)
     R = int(qo.size)
@@ -131,7 +188,7 @@ def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_
     lse64 = np.zeros((total_q, num_q_heads), np.float64) if want_f64 else None
     sel = None if row_select is None else _c(row_select, np.uint8)
     pairs = ctypes.c_int64(0)
-    rc = _load().oracle_attention(_ptr(qa), _ptr(kp), _ptr(vp), _ptr(bt), int(bt.shape[1]), _ptr(qo), _ptr(kv),
+    rc = fn(_ptr(qa), _ptr(kp), _ptr(vp), _ptr(bt), int(bt.shape[1]), _ptr(qo), _ptr(kv),
                                   R, int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
                                   int(num_blocks), float(scale), _ptr(sel), _ptr(out), _ptr(lse),
                                   _ptr(out64), _ptr(lse64), ctypes.cast(ctypes.pointer(pairs), ctypes.c_void_p))
@@ -146,9 +203,11 @@ def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_
 
 def run_workload(wl, row_select=None, want_f64: bool = False):
     """Append the workload's new tokens, then attend; returns (k_pool, v_pool, result)."""
-    kp, vp = append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
-                    wl.head_dim, wl.block_size, wl.num_blocks)
+    fmt = getattr(wl, "kv_format", "bf16")
+    put = append_q8 if fmt == "q8_0" else append
+    kp, vp = put(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
+                 wl.head_dim, wl.block_size, wl.num_blocks)
     res = attention(wl.q, kp, vp, wl.block_tables, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
                     wl.head_dim, wl.block_size, wl.num_blocks, wl.scale, row_select=row_select,
-                    want_f64=want_f64)
+                    want_f64=want_f64, kv_format=fmt)
     return kp, vp, res

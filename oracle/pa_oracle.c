@@ -30,6 +30,20 @@
  * Everything is accumulated in double; the scores are kept and exponentiated
  * in a second pass (max subtracted first), which is mathematically the same
  * as any one-pass or split form of softmax.
+ *
+ *   q8_0 pool  (book section 8.4.2 and fig. 8-23: every 32 values share one 2-byte
+ *              scale and are stored as 8-bit codes, 34 bytes instead of 64.)  A group
+ *              is 32 consecutive dims of one token's row for one KV head.  One
+ *              (block, KV head) tile holds the codes of its B tokens, [B][D] int8,
+ *              followed by their scales, [B][D / 32] IEEE binary16.  The pages fix
+ *              neither the scale's type nor the rounding; the readings taken here:
+ *                d    = binary16(min(amax / 127, 65504)), amax = max |x| of the group,
+ *                       the division in binary32, the conversion to nearest (ties even)
+ *                code = clamp(rint(x / d), -127, 127) with x / d in binary32 and rint
+ *                       to nearest, ties even; code = 0 when d = 0
+ *                value represented = code * d
+ *              Append quantises each new row this way; attention is the definition
+ *              above applied to the represented values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -94,6 +108,128 @@ int64_t oracle_slot(const int32_t* bt_row, int64_t pos, int32_t block_size)
     return (int64_t)bt_row[pos / block_size] * block_size + pos % block_size;
 }
 
+/* IEEE binary16 -> double: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+static double half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                     /* zero and subnormals: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp(1.0 + f / 1024.0, e - 15);
+    return sign ? -v : v;
+}
+
+double oracle_half_to_double(uint16_t h) { return half_to_double(h); }
+
+/* binary32 -> binary16, to nearest with ties to even.  Normal results keep 11
+ * significant bits (quantum 2^(E-10) for |x| in [2^E, 2^(E+1))); below 2^-14 the
+ * quantum is 2^-24.  Everything is done in double, where these scalings are exact. */
+uint16_t oracle_float_to_half(float x)
+{
+    if (isnan(x))
+        return 0x7E00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isinf(a))
+        return sign | 0x7C00;
+    int e;
+    frexp(a, &e);                                  /* a = m * 2^e, m in [0.5, 1) */
+    int E = e - 1;                                 /* a in [2^E, 2^(E+1)) */
+    int qexp = (E < -14 ? -14 : E) - 10;
+    double units = nearbyint(a / ldexp(1.0, qexp));   /* default rounding: nearest, ties even */
+    double r = units * ldexp(1.0, qexp);
+    if (r > 65504.0)                               /* past the largest finite binary16 */
+        return sign | 0x7C00;
+    if (r < ldexp(1.0, -14))                       /* subnormal (or zero): fraction = r / 2^-24 */
+        return sign | (uint16_t)nearbyint(r / ldexp(1.0, -24));
+    int er;
+    frexp(r, &er);
+    int Er = er - 1;
+    uint16_t frac = (uint16_t)nearbyint((r / ldexp(1.0, Er) - 1.0) * 1024.0);
+    return sign | (uint16_t)((Er + 15) << 10) | frac;
+}
+
+/* One q8_0 group of 32 bf16 values -> 32 codes and the scale's binary16 bits. */
+static void quantize_q8_group(const uint16_t* x, int8_t* codes, uint16_t* scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        float v = fabsf((float)bf16_to_double(x[i]));
+        if (v > amax)
+            amax = v;
+    }
+    float d = amax / 127.0f;
+    if (d > 65504.0f)
+        d = 65504.0f;
+    *scale = oracle_float_to_half(d);
+    float dw = (float)half_to_double(*scale);
+    for (int i = 0; i < 32; ++i) {
+        float c = 0.0f;
+        if (dw != 0.0f) {
+            c = rintf((float)bf16_to_double(x[i]) / dw);
+            if (c > 127.0f)
+                c = 127.0f;
+            if (c < -127.0f)
+                c = -127.0f;
+        }
+        codes[i] = (int8_t)c;
+    }
+}
+
+/* q8_0 of n rows of head_dim bf16 values: codes [n][D], scales [n][D / 32]. */
+int oracle_quantize_q8_rows(const uint16_t* x, int64_t n, int32_t head_dim, int8_t* codes, uint16_t* scales)
+{
+    if (!x || !codes || !scales || head_dim % 32 != 0 || n < 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < n; ++r)
+        for (int32_t g = 0; g < head_dim / 32; ++g)
+            quantize_q8_group(x + r * head_dim + g * 32, codes + r * head_dim + g * 32,
+                              scales + r * (head_dim / 32) + g);
+    return ORACLE_OK;
+}
+
+/* Bytes of one q8_0 (block, KV head) tile. */
+int64_t oracle_q8_tile_bytes(int32_t head_dim, int32_t block_size)
+{
+    return (int64_t)block_size * head_dim + (int64_t)block_size * (head_dim / 32) * 2;
+}
+
+/* append into q8_0 pools [num_blocks][Hkv][tile bytes]; k_new / v_new are bf16 [n][Hkv][D]. */
+int oracle_append_q8(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_new, const uint16_t* v_new,
+                     const int32_t* slot_mapping, int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks)
+{
+    if (!k_pool || !v_pool || !k_new || !v_new || (!slot_mapping && n_tokens > 0) || n_tokens < 0 ||
+        head_dim % 32 != 0)
+        return ORACLE_BAD_ARG;
+    const int64_t tile = oracle_q8_tile_bytes(head_dim, block_size);
+    const int32_t groups = head_dim / 32;
+    for (int32_t t = 0; t < n_tokens; ++t) {
+        int64_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        int64_t blk = s / block_size, off = s % block_size;
+        if (blk >= num_blocks)
+            return ORACLE_BAD_BLOCK;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            size_t src = ((size_t)t * num_kv_heads + h) * head_dim;
+            for (int which = 0; which < 2; ++which) {
+                uint8_t* base = (which ? v_pool : k_pool) + ((size_t)blk * num_kv_heads + h) * tile;
+                const uint16_t* row = (which ? v_new : k_new) + src;
+                for (int32_t g = 0; g < groups; ++g) {
+                    uint16_t sc;
+                    quantize_q8_group(row + g * 32, (int8_t*)(base + off * head_dim + g * 32), &sc);
+                    memcpy(base + (size_t)block_size * head_dim + ((size_t)off * groups + g) * 2, &sc, 2);
+                }
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* append: pools are [num_blocks][Hkv][B][D] bf16; k_new / v_new are [n][Hkv][D]. */
 int oracle_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new, const uint16_t* v_new,
                   const int32_t* slot_mapping, int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
@@ -150,16 +286,42 @@ int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, c
  * (query, key) pairs visited for one head, summed over the computed rows: an
  * instrument for the causal mask.
  */
-int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                     const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
-                     const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
-                     int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale,
-                     const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
-                     double* lse_f64, int64_t* pair_count)
+enum { FMT_BF16 = 0, FMT_Q8_0 = 1 };
+
+/* The values of token `tok` of physical block `phys`, KV head kvh, as doubles. */
+static void load_row(int fmt, const void* pool, int32_t phys, int32_t kvh, int32_t tok, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, double* dst)
+{
+    if (fmt == FMT_BF16) {
+        const uint16_t* src = (const uint16_t*)pool +
+                              (((size_t)phys * num_kv_heads + kvh) * block_size + (size_t)tok) * head_dim;
+        for (int32_t c = 0; c < head_dim; ++c)
+            dst[c] = bf16_to_double(src[c]);
+    } else {
+        const uint8_t* tile = (const uint8_t*)pool +
+                              ((size_t)phys * num_kv_heads + kvh) * (size_t)oracle_q8_tile_bytes(head_dim, block_size);
+        const int8_t* codes = (const int8_t*)tile + (size_t)tok * head_dim;
+        const uint8_t* sc = tile + (size_t)block_size * head_dim + (size_t)tok * (head_dim / 32) * 2;
+        for (int32_t c = 0; c < head_dim; ++c) {
+            uint16_t h;
+            memcpy(&h, sc + (c / 32) * 2, 2);
+            dst[c] = (double)codes[c] * half_to_double(h);
+        }
+    }
+}
+
+static int attention_impl(int fmt, const uint16_t* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
+                          const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale,
+                          const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
+                          double* lse_f64, int64_t* pair_count)
 {
     if (!q || !k_pool || !v_pool || !block_tables || !qo_len || !kv_len)
         return ORACLE_BAD_ARG;
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 || block_size <= 0)
+        return ORACLE_BAD_ARG;
+    if (fmt == FMT_Q8_0 && head_dim % 32 != 0)
         return ORACLE_BAD_ARG;
     const int32_t group = num_q_heads / num_kv_heads;
 
@@ -201,7 +363,8 @@ int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
         double* s = (double*)malloc(sizeof(double) * (size_t)(max_kv > 0 ? max_kv : 1));
         double* acc = (double*)malloc(sizeof(double) * (size_t)head_dim);
         double* qd = (double*)malloc(sizeof(double) * (size_t)head_dim);
-        if (!s || !acc || !qd) {
+        double* kvrow = (double*)malloc(sizeof(double) * (size_t)head_dim);
+        if (!s || !acc || !qd || !kvrow) {
 #pragma omp atomic write
             status = ORACLE_NO_MEMORY;
         } else {
@@ -224,11 +387,11 @@ int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
 
                 double m = -INFINITY;
                 for (int64_t j = 0; j <= p; ++j) {
-                    size_t base = (((size_t)bt[j / block_size] * num_kv_heads + kvh) * block_size
-                                   + (size_t)(j % block_size)) * head_dim;
+                    load_row(fmt, k_pool, bt[j / block_size], kvh, (int32_t)(j % block_size), num_kv_heads,
+                             head_dim, block_size, kvrow);
                     double dot = 0.0;
                     for (int32_t c = 0; c < head_dim; ++c)
-                        dot += qd[c] * bf16_to_double(k_pool[base + c]);
+                        dot += qd[c] * kvrow[c];
                     s[j] = scale * dot;
                     if (s[j] > m)
                         m = s[j];
@@ -241,10 +404,10 @@ int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
                 for (int64_t j = 0; j <= p; ++j) {
                     double e = exp(s[j] - m);
                     l += e;
-                    size_t base = (((size_t)bt[j / block_size] * num_kv_heads + kvh) * block_size
-                                   + (size_t)(j % block_size)) * head_dim;
+                    load_row(fmt, v_pool, bt[j / block_size], kvh, (int32_t)(j % block_size), num_kv_heads,
+                             head_dim, block_size, kvrow);
                     for (int32_t c = 0; c < head_dim; ++c)
-                        acc[c] += e * bf16_to_double(v_pool[base + c]);
+                        acc[c] += e * kvrow[c];
                 }
                 size_t orow = ((size_t)row * num_q_heads + h) * head_dim;
                 for (int32_t c = 0; c < head_dim; ++c) {
@@ -262,11 +425,37 @@ int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
         free(s);
         free(acc);
         free(qd);
+        free(kvrow);
     }
     free(first_row);
     if (pair_count)
         *pair_count = pairs / num_q_heads;
     return status;
+}
+
+int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
+                     const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale,
+                     const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
+                     double* lse_f64, int64_t* pair_count)
+{
+    return attention_impl(FMT_BF16, q, k_pool, v_pool, block_tables, max_blocks, qo_len, kv_len, num_reqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, row_select, out, lse,
+                          out_f64, lse_f64, pair_count);
+}
+
+/* attention over q8_0 pools [num_blocks][Hkv][tile bytes]; everything else as above. */
+int oracle_attention_q8(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                        const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
+                        const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale,
+                        const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
+                        double* lse_f64, int64_t* pair_count)
+{
+    return attention_impl(FMT_Q8_0, q, k_pool, v_pool, block_tables, max_blocks, qo_len, kv_len, num_reqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, row_select, out, lse,
+                          out_f64, lse_f64, pair_count);
 }
 
 /* Element-wise oracle_double_to_bf16 over an array (for the rounding tests). */

@@ -84,6 +84,7 @@ class Workload:
     slot_mapping: np.ndarray
     shared_prefix_blocks: int = 0
     notes: dict = field(default_factory=dict)
+    kv_format: str = "bf16"      # "q8_0": pools are uint8 [num_blocks][num_kv_heads][q8_tile_bytes]
 
     @property
     def num_reqs(self) -> int:
@@ -193,6 +194,88 @@ def build(name: str, seed: int, num_q_heads: int, num_kv_heads: int, qo_len, kv_
                     qo_len=qo_len, kv_len=kv_len, block_tables=bt, q=q, k_pool=k_pool, v_pool=v_pool,
                     k_new=k_new, v_new=v_new, slot_mapping=slots,
                     shared_prefix_blocks=shared_prefix_blocks)
+
+
+def q8_tile_bytes(head_dim: int = 128, block_size: int = 16) -> int:
+    """q8_0 (block, KV head) tile: [B][D] int8 codes followed by [B][D/32] binary16 scales."""
+    return block_size * head_dim + block_size * (head_dim // 32) * 2
+
+
+HALF_NAN = np.uint16(0x7E00)
+
+
+def build_q8(name: str, seed: int, num_q_heads: int, num_kv_heads: int, qo_len, kv_len, num_blocks: int,
+             head_dim: int = 128, block_size: int = 16, shared_prefix_blocks: int = 0, poison: bool = True,
+             q_scale: float = 1.0) -> Workload:
+    """Like ``build`` with a q8_0 pool.  Context tokens already in the cache are drawn in the
+    storage format itself: codes round(N(0,1) * 42) clipped to [-127, 127] (about what
+    quantising N(0,1) data gives) and one binary16 scale per 32 dims from U[0.018, 0.03].
+    Slots that hold no context token keep random code bytes and NaN scales when ``poison``
+    is set.  The new tokens' K/V are bf16 N(0,1), to be quantised by the append."""
+    qo_len = np.asarray(qo_len, dtype=np.int32)
+    kv_len = np.asarray(kv_len, dtype=np.int32)
+    R = qo_len.shape[0]
+    if np.any(qo_len < 1) or np.any(kv_len < qo_len):
+        raise ValueError("need 1 <= qo_len <= kv_len")
+    s_len, s_place, s_k, s_v, s_new, s_q = _streams(seed)
+    B, D, Hkv, Hq = block_size, head_dim, num_kv_heads, num_q_heads
+    G = D // 32
+    nb = [-(-int(L) // B) for L in kv_len]
+    bt = place_blocks(s_place, num_blocks, nb, shared_prefix_blocks, None)
+    tile = q8_tile_bytes(D, B)
+    pools = []
+    for s_x in (s_k, s_v):
+        pool = np.zeros((num_blocks, Hkv, tile), np.uint8)
+        if poison:
+            pool[:, :, :B * D] = s_x.integers(0, 256, (num_blocks, Hkv, B * D), dtype=np.uint8)
+            pool[:, :, B * D:].view(np.uint16)[...] = HALF_NAN
+        pools.append(pool)
+    k_pool, v_pool = pools
+    filled = set()
+    for r in range(R):
+        ctx = int(kv_len[r] - qo_len[r])
+        for b in range(-(-ctx // B)):
+            phys = int(bt[r, b])
+            n = min(B, ctx - b * B)
+            if phys in filled:
+                continue
+            for pool, s_x in ((k_pool, s_k), (v_pool, s_v)):
+                codes = np.clip(np.rint(s_x.standard_normal((Hkv, n, D)) * 42.0), -127, 127).astype(np.int8)
+                scales = s_x.uniform(0.018, 0.03, (Hkv, n, G)).astype(np.float16).view(np.uint16)
+                cv = pool[phys, :, :B * D].reshape(Hkv, B, D).view(np.int8)
+                cv[:, :n, :] = codes
+                sv = pool[phys, :, B * D:].reshape(Hkv, B * G * 2).view(np.uint16).reshape(Hkv, B, G)
+                sv[:, :n, :] = scales
+            if n == B:
+                filled.add(phys)
+    n_new = int(qo_len.sum())
+    k_new = f32_to_bf16_bits(s_new.standard_normal((n_new, Hkv, D), dtype=np.float32))
+    v_new = f32_to_bf16_bits(s_new.standard_normal((n_new, Hkv, D), dtype=np.float32))
+    slots = np.empty(n_new, dtype=np.int32)
+    t = 0
+    for r in range(R):
+        for pos in range(int(kv_len[r] - qo_len[r]), int(kv_len[r])):
+            slots[t] = slot_of(bt[r], pos, B)
+            t += 1
+    q = f32_to_bf16_bits(s_q.standard_normal((n_new, Hq, D), dtype=np.float32) * np.float32(q_scale))
+    return Workload(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
+                    num_blocks=num_blocks, scale=1.0 / np.sqrt(D), qo_len=qo_len, kv_len=kv_len,
+                    block_tables=bt, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
+                    slot_mapping=slots, shared_prefix_blocks=shared_prefix_blocks, kv_format="q8_0")
+
+
+def config_tiny_q8(seed: int = 11, poison: bool = True, q_scale: float = 1.0) -> Workload:
+    """The tiny decode case (4 rows, kv_len 17 / 64 / 100 / 250, 8 q / 2 kv heads) on a q8_0 pool."""
+    return build_q8("tiny_decode_q8", seed, 8, 2, qo_len=[1, 1, 1, 1], kv_len=[17, 64, 100, 250],
+                    num_blocks=64, poison=poison, q_scale=q_scale)
+
+
+def config_decode_q8(seed: int = 12, num_reqs: int = 32, poison: bool = True) -> Workload:
+    """The Qwen3-8B decode step (32 rows, kv_len 2048 + U[0,255]) on a q8_0 pool of as many
+    blocks as the bf16 one."""
+    kv = 2048 + _uniform_extra(seed, num_reqs)
+    return build_q8("qwen3_8b_decode_step_q8", seed, 32, 8, qo_len=[1] * num_reqs, kv_len=kv,
+                    num_blocks=POOL_BLOCKS_12GIB, poison=poison)
 
 
 # Qwen3-8B attention geometry (book section 8.1.2: 36 layers, 8 KV heads of size 128, bf16).

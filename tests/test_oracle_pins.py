@@ -484,3 +484,126 @@ def test_copy_on_write_gives_each_branch_its_own_token():
                            wl.head_dim, wl.block_size, wl.num_blocks)
     bad = _attend(wl, kp, vp, wl.block_tables)
     assert not np.array_equal(bad["out"][0], ref["out"][0])
+
+
+# ------------------------------------------------------------------ q8_0 KV pool
+
+QWEN_KV_BYTES_PER_TOKEN_BF16 = 2 * 36 * 8 * 128 * 2      # K and V, 36 layers, 8 KV heads, d = 128, bf16
+
+
+def test_q8_bytes_reproduce_the_pages_figures():
+    """Book section 8.4.2 / fig. 8-23: a q8_0 group is 34 bytes against 64 for bf16.  The
+    long request (8192 + 256 tokens, 1188 MiB in bf16) takes 631.125 MiB; an 8K context
+    saves 540 MiB; 16 long requests take about 9.86 GiB."""
+    tile = oracle.q8_tile_bytes(128, 16)
+    assert tile == 2176 and synthetic.q8_tile_bytes(128, 16) == tile
+    per_token_q8 = 2 * 36 * 8 * tile // 16
+    assert per_token_q8 * 64 == QWEN_KV_BYTES_PER_TOKEN_BF16 * 34
+    MiB = 2**20
+    assert 8448 * QWEN_KV_BYTES_PER_TOKEN_BF16 == 1188 * MiB
+    assert 8448 * per_token_q8 == 631.125 * MiB
+    assert 8192 * QWEN_KV_BYTES_PER_TOKEN_BF16 - 8192 * per_token_q8 == 540 * MiB
+    assert round(16 * 8448 * per_token_q8 / 2**30, 2) == 9.86
+
+
+def test_float_to_half_matches_numpy():
+    """binary32 -> binary16 to nearest even, against numpy's conversion: random finite bit
+    patterns over the whole range, every tie between neighbouring halves, subnormals and
+    the overflow edge."""
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2**32, 20000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    halves = np.arange(0, 0x7C00, 7, dtype=np.uint16).view(np.float16).astype(np.float32)
+    ties = ((halves[:-1].astype(np.float64) + halves[1:].astype(np.float64)) / 2).astype(np.float32)
+    edge = np.array([65504, 65519.996, 65520, 65536, 2.0**-24, 2.0**-25, 3 * 2.0**-26, 2.0**-14,
+                     2.0**-14 - 2.0**-25, -0.0, 1e-30], np.float32)
+    allv = np.concatenate([vals[:4000], ties, edge, -ties[:200]])
+    with np.errstate(over="ignore"):
+        want = allv.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.float_to_half(v) for v in allv], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_half_to_double_matches_numpy():
+    h = np.arange(0, 2**16, dtype=np.uint32).astype(np.uint16)
+    f = h.view(np.float16).astype(np.float64)
+    for i in range(0, 2**16, 37):
+        g = oracle.half_to_double(int(h[i]))
+        assert (np.isnan(g) and np.isnan(f[i])) or g == f[i]
+
+
+def test_q8_quantise_recovers_exact_groups():
+    """A group whose values are integers c times 2^-5 with max |c| = 127 has scale exactly
+    2^-5 and codes exactly c."""
+    rng = np.random.default_rng(6)
+    c = rng.integers(-127, 128, (50, 128))
+    c[:, ::32] = np.where(rng.random((50, 4)) < 0.5, 127, -127)
+    x = f32_to_bf16_bits((c * 2.0**-5).astype(np.float32))
+    codes, scales = oracle.quantize_q8_rows(x, 128)
+    assert np.array_equal(codes.astype(np.int64), c)
+    assert np.all(scales == 0x2800)                    # binary16 of 2^-5
+
+
+def test_q8_quantise_error_bound_and_edges():
+    """Every value is within half a scale step of code * d; the largest magnitude of a
+    group maps to +-127; an all-zero group has scale 0 and codes 0; a group beyond the
+    binary16 range saturates at scale 65504."""
+    rng = np.random.default_rng(7)
+    mag = 10.0 ** rng.uniform(-3, 3, (400, 4, 1))
+    x32 = (rng.standard_normal((400, 4, 32)) * mag).astype(np.float32).reshape(400, 128)
+    x = f32_to_bf16_bits(x32)
+    xv = bf16_bits_to_f32(x).astype(np.float64).reshape(400, 4, 32)
+    codes, scales = oracle.quantize_q8_rows(x, 128)
+    d = scales.view(np.float16).astype(np.float64)[..., None]
+    rec = codes.reshape(400, 4, 32).astype(np.float64) * d
+    assert np.all(np.abs(rec - xv) <= d / 2 + 1e-12 * np.abs(xv))
+    assert np.all(np.abs(codes.reshape(400, 4, 32)).max(axis=2) == 127)
+    z, zs = oracle.quantize_q8_rows(np.zeros(128, np.uint16), 128)
+    assert not z.any() and not zs.any()
+    big = f32_to_bf16_bits(np.full(128, 3e9, np.float32))
+    bc, bs = oracle.quantize_q8_rows(big, 128)
+    assert np.all(bs == 0x7BFF) and np.all(bc == 127)
+
+
+def _dequantise(pool, Hkv, D=128, B=16):
+    """numpy reading of the tile layout: [B][D] int8 codes, then [B][D/32] binary16 scales."""
+    nb = pool.shape[0]
+    codes = pool[:, :, :B * D].reshape(nb, Hkv, B, D).view(np.int8).astype(np.float64)
+    sc = np.ascontiguousarray(pool[:, :, B * D:]).view(np.float16).reshape(nb, Hkv, B, D // 32).astype(np.float64)
+    return codes * np.repeat(sc, 32, axis=3)
+
+
+def test_q8_attention_equals_dense_softmax_on_dequantised_values():
+    """Append (quantise) then attend, against a dense numpy softmax over the values the
+    codes represent, gathered through the block table."""
+    wl = synthetic.config_tiny_q8(poison=True)
+    kp, vp, res = oracle.run_workload(wl, want_f64=True)
+    K, V = _dequantise(kp, wl.num_kv_heads), _dequantise(vp, wl.num_kv_heads)
+    q = bf16_bits_to_f32(wl.q).astype(np.float64)
+    g = wl.num_q_heads // wl.num_kv_heads
+    for r in range(wl.num_reqs):
+        L = int(wl.kv_len[r])
+        blocks = wl.block_tables[r, :-(-L // 16)]
+        for h in range(wl.num_q_heads):
+            Kr = K[blocks, h // g].reshape(-1, 128)[:L]
+            Vr = V[blocks, h // g].reshape(-1, 128)[:L]
+            s = Kr @ q[r, h] * wl.scale
+            lse = np.log(np.sum(np.exp(s - s.max()))) + s.max()
+            o = np.exp(s - lse) @ Vr
+            assert abs(res["lse_f64"][r, h] - lse) < 1e-12
+            assert np.max(np.abs(res["out_f64"][r, h] - o)) < 1e-12
+
+
+def test_q8_append_writes_exactly_the_quantised_rows():
+    wl = synthetic.config_tiny_q8(poison=True)
+    kp, vp = oracle.append_q8(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads, 128, 16,
+                              wl.num_blocks)
+    for pool0, pool1, new in ((wl.k_pool, kp, wl.k_new), (wl.v_pool, vp, wl.v_new)):
+        codes, scales = oracle.quantize_q8_rows(new, 128)
+        want = pool0.copy()
+        for t, s in enumerate(wl.slot_mapping):
+            blk, off = divmod(int(s), 16)
+            want[blk, :, off * 128:(off + 1) * 128] = codes[t].view(np.uint8)
+            want[blk, :, 2048 + off * 8:2048 + off * 8 + 8] = scales[t].view(np.uint8).reshape(wl.num_kv_heads, 8)
+        assert np.array_equal(pool1, want)
