@@ -16,6 +16,13 @@ constexpr int kMaxSplitBlocks = 64 * kDecodeWaves;   // one block id per lane of
 constexpr int kPrefillQ = 32;   // new tokens per prefill tile (x kGroup heads = 128 MFMA rows)
 constexpr int kPrefillKeys = 128;     // keys per prefill step (eight blocks)
 constexpr int kMaxPrefillSplits = 64; // most key splits of one prefill tile
+// q8_0 pool: 32 values of a token's head row share one binary16 scale.  A (block, KV
+// head) tile is [kBlock][kHeadDim] int8 codes followed by [kBlock][kHeadDim / 32] scales.
+constexpr int kQ8Group = 32;
+constexpr int kQ8CodeBytes = kBlock * kHeadDim;
+constexpr int kQ8TileBytes = kQ8CodeBytes + kBlock * (kHeadDim / kQ8Group) * 2;
+static_assert(kQ8TileBytes % 16 == 0, "q8_0 tiles stay 16-byte aligned");
+static_assert(kQ8TileBytes == PA_Q8_TILE_BYTES, "header and kernels agree on the q8_0 tile");
 
 inline bool geometry_supported(const pa_geometry* g)
 {

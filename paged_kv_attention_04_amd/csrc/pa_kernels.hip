@@ -5,13 +5,16 @@
 //                       gather with several blocks of loads in flight, QK^T with bf16
 //                       dot2, online softmax in FP32, PV accumulation in FP32, and the
 //                       log-sum-exp merge of the splits done by the last split to finish
-//   pa_prefill_tile     chunked-prefill rows: one workgroup per (row, KV head, 16 new
+//   pa_prefill_tile     chunked-prefill rows: one workgroup per (row, KV head, 32 new
 //                       tokens x 4 query heads); K / V copied straight into LDS,
 //                       S^T = K Q^T and O^T = V^T P^T on BF16 MFMA with FP32
 //                       accumulation, causal mask, online softmax
+//   pa_append_q8_scatter, pa_decode_split<true>
+//                       the same append and decode over a q8_0 pool
 //
 // Pool layout: [block][kv_head][token-in-block][dim] (head-major inside a block), so one
-// (block, KV head) tile is 16 x 128 bf16 = 4 KiB of contiguous memory.
+// (block, KV head) tile is 16 x 128 bf16 = 4 KiB of contiguous memory.  A q8_0 tile is
+// the 16 x 128 int8 codes followed by the 16 x 4 binary16 scales: 2176 bytes.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <math.h>
@@ -121,6 +124,37 @@ __device__ inline float readlane_f(float x, int lane)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline float half_bits_to_float(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+// Two floats -> binary16 pair (toward zero), low half first.
+__device__ inline uint32_t pack_half_rtz(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+__device__ inline float dot2_f16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+
+// Value held by lane `src` of this wavefront (any lane may name any source).
+__device__ inline uint32_t lane_value(uint32_t v, int src)
+{
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+
+// q8_0 codes as exact binary16 numbers: the int8 code c becomes 1152 + c (= 1024 + (c + 128),
+// whose bit pattern is 0x64 : (c ^ 0x80)).  The products then carry a bias of 1152 times
+// the other operand, which the callers take off once.  `sel` picks, through v_perm, the
+// two code bytes that go to the low and high halves (byte slots 0 and 2).
+constexpr float kQ8Bias = 1152.0f;
+__device__ inline uint32_t q8_to_half2(uint32_t hi_src, uint32_t lo_src, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi_src, lo_src, sel) ^ 0x64806480u;
+}
+
 // ------------------------------------------------------------------------------ append
 
 // One thread moves one 16-byte chunk of K and the matching chunk of V.
@@ -148,29 +182,93 @@ __global__ __launch_bounds__(256) void pa_append_scatter(uint16_t* __restrict__ 
     reinterpret_cast<u32x4*>(v_pool)[dst] = reinterpret_cast<const u32x4*>(v_new)[src];
 }
 
+// One thread quantises one 32-value group of one (token, KV head) row, K and V: scale
+// d = binary16(min(amax / 127, 65504)), codes rint(x / d) clamped to +-127 (0 when d = 0),
+// the divisions in binary32 rounded to nearest.
+__global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                            const uint16_t* __restrict__ k_new,
+                                                            const uint16_t* __restrict__ v_new,
+                                                            const int32_t* __restrict__ slot_mapping,
+                                                            int32_t n_tokens, int32_t num_kv_heads, int64_t num_slots)
+{
+    constexpr int kGroups = kHeadDim / pa::kQ8Group;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_token = (int64_t)num_kv_heads * kGroups;
+    if (idx >= (int64_t)n_tokens * per_token)
+        return;
+    const int32_t t = (int32_t)(idx / per_token);
+    const int32_t rem = (int32_t)(idx - (int64_t)t * per_token);
+    const int32_t h = rem / kGroups, grp = rem % kGroups;
+    const int32_t slot = slot_mapping[t];
+    if (slot < 0 || (int64_t)slot >= num_slots)
+        return;
+    const int64_t blk = slot / kBlock, off = slot % kBlock;
+    const int64_t src = (((int64_t)t * num_kv_heads + h) * kHeadDim + grp * pa::kQ8Group) / 8;   // 16-byte units
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const u32x4* in = reinterpret_cast<const u32x4*>(which ? v_new : k_new) + src;
+        float x[pa::kQ8Group];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 w = in[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[8 * i + 2 * j] = bf16_lo(w[j]);
+                x[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+            }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < pa::kQ8Group; ++i)
+            amax = fmaxf(amax, fabsf(x[i]));
+        float d = amax / 127.0f;
+        if (d > 65504.0f)
+            d = 65504.0f;
+        const _Float16 dh = (_Float16)d;
+        const float dw = (float)dh;
+        uint32_t packed[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float c = 0.f;
+                if (dw != 0.f)
+                    c = fminf(fmaxf(rintf(x[4 * i + j] / dw), -127.f), 127.f);
+                word |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
+            }
+            packed[i] = word;
+        }
+        uint8_t* tile = (which ? v_pool : k_pool) + (blk * num_kv_heads + h) * pa::kQ8TileBytes;
+        u32x4* codes = reinterpret_cast<u32x4*>(tile + off * kHeadDim + grp * pa::kQ8Group);
+        codes[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        codes[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+        reinterpret_cast<uint16_t*>(tile + pa::kQ8CodeBytes)[off * kGroups + grp] = __builtin_bit_cast(uint16_t, dh);
+    }
+}
+
 // ------------------------------------------------------------------------------ block copy
 
-// One thread per 16 bytes of a (pair, pool, KV head) tile: pairs x 2 pools x Hkv x 256
-// threads; each 256 consecutive threads move one contiguous 4 KiB tile.
-__global__ __launch_bounds__(256) void pa_copy_scatter(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+// One thread per 16 bytes of a (pair, pool, KV head) tile: pairs x 2 pools x Hkv x
+// tile_chunks threads (tile_chunks = 16-byte chunks per tile: 256 for bf16, 136 for
+// q8_0); consecutive threads move one contiguous tile.
+__global__ __launch_bounds__(256) void pa_copy_scatter(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
                                                        const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
-                                                       int32_t n, int32_t num_kv_heads, int32_t num_blocks)
+                                                       int32_t n, int32_t num_kv_heads, int32_t num_blocks,
+                                                       int32_t tile_chunks)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t per_pair = (int64_t)2 * num_kv_heads * 256;
-    const int64_t pair = t / per_pair;
+    const int64_t blk_chunks = (int64_t)num_kv_heads * tile_chunks;   // 16-byte chunks per block (all KV heads)
+    const int64_t pair = t / (2 * blk_chunks);
     if (pair >= n)
         return;
     const int32_t s = src[pair], d = dst[pair];
     if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
         return;
-    const int64_t rem = t - pair * per_pair;
-    uint16_t* pool = (rem / ((int64_t)num_kv_heads * 256)) ? v_pool : k_pool;
-    const int64_t within = rem % ((int64_t)num_kv_heads * 256);    // chunk within one block's Hkv tiles
-    const int64_t blk_chunks = (int64_t)num_kv_heads * 256;         // 16-byte chunks per block (all KV heads)
-    const u32x4* from = reinterpret_cast<const u32x4*>(pool) + (int64_t)s * blk_chunks + within;
-    u32x4* to = reinterpret_cast<u32x4*>(pool) + (int64_t)d * blk_chunks + within;
-    *to = *from;
+    const int64_t rem = t - pair * 2 * blk_chunks;
+    u32x4* pool = rem >= blk_chunks ? v_pool : k_pool;
+    const int64_t within = rem % blk_chunks;
+    pool[(int64_t)d * blk_chunks + within] = pool[(int64_t)s * blk_chunks + within];
 }
 
 // ------------------------------------------------------------------------------ decode
@@ -212,6 +310,10 @@ struct DecodeParams {
 #endif
 // KV blocks whose loads are in flight while a block is being processed.
 constexpr int kDecodeDepth = PA_DECODE_DEPTH;
+#ifndef PA_DECODE_DEPTH_Q8
+#define PA_DECODE_DEPTH_Q8 2
+#endif
+constexpr int kDecodeDepthQ8 = PA_DECODE_DEPTH_Q8;   // a q8_0 stage is half the bytes
 constexpr int kDecodeWaves = pa::kDecodeWaves;
 
 // One (block, KV head) tile is 16 tokens x 256 bytes, read by four 16-byte loads per lane.
@@ -235,6 +337,31 @@ __device__ inline void load_stage(KvStage& s, const uint16_t* ktile, const uint1
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         s.v[i] = vp[64 * i];
+}
+
+// q8_0 tile: codes [16][128] int8, then scales [16][4] binary16.
+// K: lane = 8 * t8 + c8 reads the 16 codes of dims 16 c8 .. 16 c8 + 15 (one scale group,
+//    c8 / 2) of tokens t8 and t8 + 8; each load covers 1 KiB, eight whole 128-byte rows.
+// V: lane = 16 * tg + c16 reads the 8 codes of dims 8 c16 .. 8 c16 + 7 (group c16 / 4) of
+//    tokens tg + 4 i, i = 0..3: 512 contiguous bytes per load.
+// Scales: lane i reads scale i, (token i / 4, group i % 4); the others fetch theirs from
+//    that lane.
+struct KvStageQ8 {
+    u32x4 k[2];
+    u32x2 v[4];
+    uint32_t ks, vs;
+};
+
+__device__ inline void load_stage_q8(KvStageQ8& s, const uint8_t* ktile, const uint8_t* vtile, int lane)
+{
+    const int t8 = lane >> 3, c8 = lane & 7, tg = lane >> 4, c16 = lane & 15;
+    s.k[0] = *reinterpret_cast<const u32x4*>(ktile + t8 * kHeadDim + 16 * c8);
+    s.k[1] = *reinterpret_cast<const u32x4*>(ktile + (t8 + 8) * kHeadDim + 16 * c8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s.v[i] = *reinterpret_cast<const u32x2*>(vtile + (tg + 4 * i) * kHeadDim + 8 * c16);
+    s.ks = reinterpret_cast<const uint16_t*>(ktile + pa::kQ8CodeBytes)[lane];
+    s.vs = reinterpret_cast<const uint16_t*>(vtile + pa::kQ8CodeBytes)[lane];
 }
 
 __device__ inline float dot16(const u32x4& q, const u32x4& k, float acc)
@@ -299,8 +426,18 @@ __device__ inline void wave_lds_sync()
 // With one split per row the workgroup writes the final output.  Otherwise it writes a
 // partial, and the last split of the (row, KV head) to finish -- found with an agent-scope
 // counter that it then resets -- merges the partials by the same rule.
+//
+// With a q8_0 pool (kQ8) the loads are half as large and the codes enter the products as
+// binary16 numbers 1152 + code (see q8_to_half2): each score starts from -1152 times the
+// sum of its 16 query values and is then scaled by its group's scale; each PV weight is
+// the softmax weight times the value's scale, and -1152 times the weights' sum is taken
+// off the accumulators at the end.  Q is widened to binary16, which holds every bf16
+// value of magnitude in [2^-14, 65504] exactly.
+template <bool kQ8>
 __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParams p)
 {
+    constexpr int kDepth = kQ8 ? kDecodeDepthQ8 : kDecodeDepth;
+    using Stage = std::conditional_t<kQ8, KvStageQ8, KvStage>;
     __shared__ float p_lds[kDecodeWaves][kBlock * kGroup];
     __shared__ float o_lds[kDecodeWaves][kGroup * kHeadDim];
     __shared__ float l_lds[kDecodeWaves][kGroup];
@@ -316,7 +453,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     const float nan = __builtin_nanf("");
 
     // Wavefront w takes blocks g0 + w, g0 + w + 8, ... of the split.  Their table entries
-    // (lane i holds entry i) and the first kDecodeDepth blocks' K / V are requested before
+    // (lane i holds entry i) and the first kDepth blocks' K / V are requested before
     // the row's lengths arrive, so the start-up waits for one memory round trip less.  The
     // early requests are bounded by the table row and the pool; entries past the row's
     // last block are never used.
@@ -337,18 +474,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     const int ts = t8 + 8 * (c8 >> 2), hs = c8 & 3;   // softmax role: token ts, head hs
     const int c16 = lane & 15, tg = lane >> 4;        // PV role
 
-    const int64_t tile_elems = (int64_t)kBlock * kHeadDim;
-    const int64_t kvh_off = (int64_t)kvh * tile_elems;
-    const int64_t blk_stride = (int64_t)p.num_kv_heads * tile_elems;
-    auto issue = [&](KvStage& st, int j) {
+    auto issue = [&](Stage& st, int j) __attribute__((always_inline)) {
         int id = __builtin_amdgcn_readlane(my_blk, j);
         id = (id >= 0 && id < p.num_blocks) ? id : 0;
-        const int64_t off = (int64_t)id * blk_stride + kvh_off;
-        load_stage(st, p.k_pool + off, p.v_pool + off, lane);
+        if constexpr (kQ8) {
+            const int64_t off = ((int64_t)id * p.num_kv_heads + kvh) * pa::kQ8TileBytes;
+            load_stage_q8(st, reinterpret_cast<const uint8_t*>(p.k_pool) + off,
+                          reinterpret_cast<const uint8_t*>(p.v_pool) + off, lane);
+        } else {
+            const int64_t off = ((int64_t)id * p.num_kv_heads + kvh) * kBlock * kHeadDim;
+            load_stage(st, p.k_pool + off, p.v_pool + off, lane);
+        }
     };
-    KvStage st[kDecodeDepth + 1];
+    Stage st[kDepth + 1];
 #pragma unroll
-    for (int d = 0; d < kDecodeDepth; ++d)
+    for (int d = 0; d < kDepth; ++d)
         issue(st[d], d);
 
     if (q_end - q_row != 1)
@@ -372,37 +512,77 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     bool bad = lane < nb && (my_blk < 0 || my_blk >= p.num_blocks);
     bad = __syncthreads_or(bad);                      // a block id outside the pool: its data is not used
 
-    u32x4 qv[kGroup][2];
+    u32x4 qv[kGroup][2];       // bf16 pool: bf16 pairs of dims 8 c8 .. and 64 + 8 c8 ..
+    uint32_t qh[kGroup][8];    // q8_0 pool: binary16 pairs of dims 16 c8 + 2 j, + 1
+    float qbias[kGroup];       // q8_0 pool: -1152 times the sum of those 16 values
     {
         const u32x4* qb = reinterpret_cast<const u32x4*>(p.q + ((int64_t)q_row * p.num_q_heads + head0) * kHeadDim);
 #pragma unroll
         for (int h = 0; h < kGroup; ++h) {
-            qv[h][0] = qb[h * 16 + c8];
-            qv[h][1] = qb[h * 16 + c8 + 8];
+            if constexpr (kQ8) {
+                const u32x4 a = qb[h * 16 + 2 * c8], b = qb[h * 16 + 2 * c8 + 1];
+                const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                float sum = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+                    qh[h][j] = pack_half_rtz(lo, hi);
+                    sum += half_bits_to_float(qh[h][j] & 0xffffu) + half_bits_to_float(qh[h][j] >> 16);
+                }
+                qbias[h] = -kQ8Bias * sum;
+            } else {
+                qv[h][0] = qb[h * 16 + c8];
+                qv[h][1] = qb[h * 16 + c8 + 8];
+            }
         }
     }
 
     float m = -INFINITY;   // running max (base 2) of head hs, equal in every lane of that head
     float lsum = 0.f;      // this lane's share of head hs's softmax denominator
     float acc[kGroup][8];
+    float wsum[kGroup];        // q8_0 pool: sum of this lane's PV weights per head
 #pragma unroll
-    for (int h = 0; h < kGroup; ++h)
+    for (int h = 0; h < kGroup; ++h) {
+        wsum[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             acc[h][e] = 0.f;
+    }
 
     float* pw = p_lds[wave];
 
-    auto process = [&](const KvStage& st, int j) {
+    auto process = [&](const Stage& st, int j) __attribute__((always_inline)) {
         // scores of tokens t8 + 8 tt for the four heads, partial over this lane's 16 dims,
         // index 4 tt + h; the reduce-scatter leaves lane c8 with the full score of token
         // ts = t8 + 8 (c8 / 4), head hs = c8 % 4
         float sc[2 * kGroup];
+        if constexpr (kQ8) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+            for (int tt = 0; tt < 2; ++tt) {
+                const float dk = half_bits_to_float(lane_value(st.ks, (t8 + 8 * tt) * 4 + (c8 >> 1)));
+                const u32x4 w = st.k[tt];
+                uint32_t kc[8];
 #pragma unroll
-            for (int h = 0; h < kGroup; ++h)
-                sc[tt * kGroup + h] = dot16(qv[h][1], st.k[2 * tt + 1], dot16(qv[h][0], st.k[2 * tt], 0.f));
+                for (int i = 0; i < 4; ++i) {
+                    kc[2 * i] = q8_to_half2(w[i], w[i], 0x0c010c00u);       // codes 4i, 4i + 1
+                    kc[2 * i + 1] = q8_to_half2(w[i], w[i], 0x0c030c02u);   // codes 4i + 2, 4i + 3
+                }
+#pragma unroll
+                for (int h = 0; h < kGroup; ++h) {
+                    float a = qbias[h];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        a = dot2_f16(qh[h][i], kc[i], a);
+                    sc[tt * kGroup + h] = a * dk;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int h = 0; h < kGroup; ++h)
+                    sc[tt * kGroup + h] = dot16(qv[h][1], st.k[2 * tt + 1], dot16(qv[h][0], st.k[2 * tt], 0.f));
+        }
         float x = reduce_scatter8(sc, c8);
         x *= p.scale_log2;
         const int pos0 = (g0 + wave + kDecodeWaves * j) * kBlock;
@@ -423,6 +603,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     acc[h][e] *= a;
+                if constexpr (kQ8)
+                    wsum[h] *= a;
             }
         }
         // The softmax statistics stay FP32; the weights enter PV as bf16, as in the MFMA
@@ -431,6 +613,39 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
         lsum += pr;
         pw[ts * kGroup + hs] = pr;                    // [token][head]
         wave_lds_sync();
+        const int valid = kvlen - pos0;               // tokens of this block that exist
+        if constexpr (kQ8) {
+            // PV on binary16 dot2 over token pairs (tg + 8 pair, tg + 8 pair + 4); the weight
+            // of a token is its softmax weight times its scale for this lane's dims (group
+            // c16 / 4); a slot past kv_len gets weight 0 whatever its scale holds.
+            float dv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dv[i] = half_bits_to_float(lane_value(st.vs, (tg + 4 * i) * 4 + (c16 >> 2)));
+                if (tg + 4 * i >= valid)
+                    dv[i] = 0.f;
+            }
+#pragma unroll
+            for (int pair = 0; pair < 2; ++pair) {
+                const f32x4 pa = *reinterpret_cast<const f32x4*>(&pw[(tg + 8 * pair) * kGroup]);
+                const f32x4 pb = *reinterpret_cast<const f32x4*>(&pw[(tg + 8 * pair + 4) * kGroup]);
+                const float da = dv[2 * pair], db = dv[2 * pair + 1];
+                const uint32_t wk[kGroup] = {pack_half_rtz(pa.x * da, pb.x * db), pack_half_rtz(pa.y * da, pb.y * db),
+                                             pack_half_rtz(pa.z * da, pb.z * db), pack_half_rtz(pa.w * da, pb.w * db)};
+#pragma unroll
+                for (int h = 0; h < kGroup; ++h)
+                    wsum[h] = dot2_f16(wk[h], 0x3c003c00u, wsum[h]);   // (1, 1)
+                const u32x2 va = st.v[2 * pair], vb = st.v[2 * pair + 1];
+#pragma unroll
+                for (int d = 0; d < 8; ++d) {
+                    const uint32_t b = d & 3;
+                    const uint32_t cp = q8_to_half2(vb[d >> 2], va[d >> 2], 0x0c000c00u | ((4u + b) << 16) | b);
+#pragma unroll
+                    for (int h = 0; h < kGroup; ++h)
+                        acc[h][d] = dot2_f16(wk[h], cp, acc[h][d]);
+                }
+            }
+        } else {
         // PV on bf16 dot2: tokens are taken in pairs (tg, tg + 4) and (tg + 8, tg + 12);
         // a pair's V values for one dim and the pair's weights for one head are packed
         // into bf16x2 operands.
@@ -438,7 +653,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             v[i] = st.v[i];
-        const int valid = kvlen - pos0;               // tokens of this block that exist
         if (valid < kBlock) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -466,30 +680,38 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
                 }
             }
         }
+        }
         wave_lds_sync();
     };
 
     if (!bad && nb > 0) {
-        // Loads for block j + kDecodeDepth are issued before block j is processed (the first
-        // kDecodeDepth were issued above).  Past the end of the run the last block is
+        // Loads for block j + kDepth are issued before block j is processed (the first
+        // kDepth were issued above).  Past the end of the run the last block is
         // fetched again (an L2 hit), so every iteration issues the same loads, and the stages
         // in flight at the top of the steady-state loop are the same on entry and on every
         // trip: the compiler can then wait for exactly the oldest stage.
         int j0 = 0;
-        for (; j0 + kDecodeDepth + 1 <= nb; j0 += kDecodeDepth + 1) {
+        for (; j0 + kDepth + 1 <= nb; j0 += kDepth + 1) {
 #pragma unroll
-            for (int u = 0; u <= kDecodeDepth; ++u) {
-                issue(st[(u + kDecodeDepth) % (kDecodeDepth + 1)], min(j0 + u + kDecodeDepth, nb - 1));
+            for (int u = 0; u <= kDepth; ++u) {
+                issue(st[(u + kDepth) % (kDepth + 1)], min(j0 + u + kDepth, nb - 1));
                 process(st[u], j0 + u);
             }
         }
-        // the last nb - j0 < kDecodeDepth + 1 blocks are already in flight
+        // the last nb - j0 < kDepth + 1 blocks are already in flight
 #pragma unroll
-        for (int u = 0; u < kDecodeDepth; ++u)
+        for (int u = 0; u < kDepth; ++u)
             if (j0 + u < nb)
                 process(st[u], j0 + u);
     }
 
+    if constexpr (kQ8) {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc[h][e] = fmaf(-kQ8Bias, wsum[h], acc[h][e]);   // the codes' 1152 offset
+    }
     // this wavefront's totals: denominators over its 16 token slots, numerators over its
     // four token groups
     float ltot = lsum;
@@ -1210,24 +1432,28 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         // lanes hold 32 output values of the row block: merge each with its own running
-        // weights (the lse is the same for all of a row's values)
+        // weights (the lse is the same for all of a row's values).  The splits are taken in
+        // index order whichever of them finished last, so the result does not depend on
+        // the order in which they finished.
         LseMerge mg[8][4];
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                mg[db][e].add(lse2[rb], oacc[rb][db][e]);
         for (int sp = 0; sp < p.splits; ++sp) {
-            if (sp == split)
-                continue;
-            const float ls = load_agent(part_lse_at(sp) + rb * 64 + lane);
-            const float* po = part_o_at(sp);
+            float ls = lse2[rb];
             float os[8][4];
+            if (sp == split) {
 #pragma unroll
-            for (int db = 0; db < 8; ++db)
+                for (int db = 0; db < 8; ++db)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    os[db][e] = load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
+                    for (int e = 0; e < 4; ++e)
+                        os[db][e] = oacc[rb][db][e];
+            } else {
+                ls = load_agent(part_lse_at(sp) + rb * 64 + lane);
+                const float* po = part_o_at(sp);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        os[db][e] = load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
+            }
 #pragma unroll
             for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -1276,8 +1502,32 @@ extern "C" pa_status pa_append_kv(const pa_geometry* g, void* k_pool, void* v_po
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-extern "C" pa_status pa_copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
-                                    const int32_t* dst_blocks, int32_t n, void* stream)
+extern "C" pa_status pa_append_kv_q8(const pa_geometry* g, void* k_pool_q8, void* v_pool_q8, const void* k_new,
+                                     const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, void* stream)
+{
+    if (!g)
+        return PA_ERR_NULL;
+    if (!pa::geometry_supported(g))
+        return PA_ERR_UNSUPPORTED;
+    if (n_tokens < 0)
+        return PA_ERR_SHAPE;
+    if (n_tokens == 0)
+        return PA_OK;
+    if (!k_pool_q8 || !v_pool_q8 || !k_new || !v_new || !slot_mapping)
+        return PA_ERR_NULL;
+    const int64_t threads = (int64_t)n_tokens * g->num_kv_heads * (kHeadDim / pa::kQ8Group);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX)
+        return PA_ERR_SHAPE;
+    hipLaunchKernelGGL(pa_append_q8_scatter, dim3((uint32_t)blocks), dim3(256), 0, as_stream(stream),
+                       static_cast<uint8_t*>(k_pool_q8), static_cast<uint8_t*>(v_pool_q8),
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
+                       n_tokens, g->num_kv_heads, (int64_t)g->num_blocks * kBlock);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+static pa_status copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
+                             const int32_t* dst_blocks, int32_t n, void* stream, int32_t tile_bytes)
 {
     if (!g)
         return PA_ERR_NULL;
@@ -1289,25 +1539,40 @@ extern "C" pa_status pa_copy_blocks(const pa_geometry* g, void* k_pool, void* v_
         return PA_OK;
     if (!k_pool || !v_pool || !src_blocks || !dst_blocks)
         return PA_ERR_NULL;
-    const int64_t threads = (int64_t)n * 2 * g->num_kv_heads * 256;
+    const int32_t tile_chunks = tile_bytes / 16;
+    const int64_t threads = (int64_t)n * 2 * g->num_kv_heads * tile_chunks;
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > INT32_MAX)
         return PA_ERR_SHAPE;
     hipLaunchKernelGGL(pa_copy_scatter, dim3((uint32_t)blocks), dim3(256), 0, as_stream(stream),
-                       static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), src_blocks, dst_blocks, n,
-                       g->num_kv_heads, g->num_blocks);
+                       static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), src_blocks, dst_blocks, n,
+                       g->num_kv_heads, g->num_blocks, tile_chunks);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* plan, const void* q,
-                                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                                        int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
-                                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+extern "C" pa_status pa_copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
+                                    const int32_t* dst_blocks, int32_t n, void* stream)
+{
+    return copy_blocks(g, k_pool, v_pool, src_blocks, dst_blocks, n, stream, kBlock * kHeadDim * 2);
+}
+
+extern "C" pa_status pa_copy_blocks_q8(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
+                                       const int32_t* dst_blocks, int32_t n, void* stream)
+{
+    return copy_blocks(g, k_pool, v_pool, src_blocks, dst_blocks, n, stream, pa::kQ8TileBytes);
+}
+
+static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t* plan, const void* q,
+                                 const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!g || !plan)
         return PA_ERR_NULL;
     if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
         return PA_ERR_UNSUPPORTED;
+    if (q8 && (plan->num_prefill_rows > 0 || plan->prefill_tiles > 0 || plan->num_prefix_groups > 0))
+        return PA_ERR_UNSUPPORTED;            // a q8_0 pool serves decode rows only
     if (plan->num_reqs == 0 || plan->total_q == 0)
         return PA_OK;
     if (!q || !k_pool || !v_pool || !block_tables || !qo_indptr || !kv_len || !out || !lse)
@@ -1437,11 +1702,33 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
         const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * g->num_kv_heads;
         if (grid > INT32_MAX)
             return PA_ERR_SHAPE;
-        hipLaunchKernelGGL(pa_decode_split, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
+        if (q8)
+            hipLaunchKernelGGL(pa_decode_split<true>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
+        else
+            hipLaunchKernelGGL(pa_decode_split<false>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
     return PA_OK;
+}
+
+extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* plan, const void* q,
+                                        const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                        int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                        void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return attention_batch(false, g, plan, q, k_pool, v_pool, block_tables, max_blocks_per_req, qo_indptr, kv_len,
+                           out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_attention_batch_q8(const pa_geometry* g, const pa_plan_t* plan, const void* q,
+                                           const void* k_pool_q8, const void* v_pool_q8, const int32_t* block_tables,
+                                           int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                           void* stream)
+{
+    return attention_batch(true, g, plan, q, k_pool_q8, v_pool_q8, block_tables, max_blocks_per_req, qo_indptr,
+                           kv_len, out, lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" pa_status pa_query_num_cus(int32_t device, int32_t* num_cus)

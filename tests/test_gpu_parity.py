@@ -361,3 +361,71 @@ def test_copy_on_write_fork_step(cascade):
     # the rows' outputs differ: each attended to its own newest token
     o = bf16_bits_to_f32(out.cpu().numpy().view(np.uint16))
     assert all(not np.array_equal(o[0], o[r]) for r in range(1, wl.num_reqs))
+
+
+# ------------------------------------------------------------------ q8_0 pool
+
+def test_q8_tiny_decode():
+    """Append quantises the new rows bit-exactly as the oracle does (whole pools compared,
+    poisoned slots included); attention over the represented values within the bars."""
+    check(synthetic.config_tiny_q8(), label="q8_0")
+
+
+def test_q8_tiny_decode_q_times_8():
+    check(synthetic.config_tiny_q8(seed=13, q_scale=8.0), label="q8_0 q*8")
+
+
+def test_q8_qwen3_decode_step():
+    check(synthetic.config_decode_q8(), label="q8_0")
+
+
+@pytest.mark.parametrize("split", [1, 2, 7, 64])
+def test_q8_split_sweep(split):
+    wl = synthetic.build_q8("q8_split", 14, 32, 8, qo_len=[1] * 6, kv_len=[1, 16, 17, 300, 1000, 2500],
+                            num_blocks=400)
+    check(wl, split_blocks=split, label=f"q8_0 split {split}")
+
+
+@pytest.mark.parametrize("kv", [[1], [15], [16], [33], [4096]])
+def test_q8_edge_lengths(kv):
+    wl = synthetic.build_q8("q8_edge", 15, 32, 8, qo_len=[1] * len(kv), kv_len=kv, num_blocks=300)
+    check(wl, label=f"q8_0 kv {kv}")
+
+
+def test_q8_rejects_prefill_rows():
+    import paged_kv_attention_04_amd as pa
+    wl = synthetic.build_q8("q8_prefill", 16, 8, 2, qo_len=[1, 40], kv_len=[20, 100], num_blocks=32)
+    with pytest.raises(pa.PaError, match="UNSUPPORTED"):
+        pa.run_workload(wl)
+
+
+def test_q8_copy_blocks_bit_exact():
+    import torch
+    import paged_kv_attention_04_amd as pa
+    rng = np.random.default_rng(17)
+    nb, Hkv = 300, 8
+    kp = rng.integers(0, 256, (nb, Hkv, pa.PA_Q8_TILE_BYTES), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nb, Hkv, pa.PA_Q8_TILE_BYTES), dtype=np.uint8)
+    perm = rng.permutation(nb)
+    src, dst = perm[:40].astype(np.int32), perm[40:80].astype(np.int32)
+    g = pa.Geometry.make(32, Hkv, nb)
+    dk, dv = pa.to_device(kp), pa.to_device(vp)
+    pa.pa_copy_blocks_q8(g, dk, dv, pa.to_device(src), pa.to_device(dst))
+    torch.cuda.synchronize()
+    ek, ev = kp.copy(), vp.copy()
+    ek[dst], ev[dst] = kp[src], vp[src]
+    assert np.array_equal(dk.cpu().numpy(), ek) and np.array_equal(dv.cpu().numpy(), ev)
+
+
+@pytest.mark.parametrize("prefill_splits,split_blocks", [(3, 7), (64, 2)])
+def test_split_results_are_bitwise_reproducible(prefill_splits, split_blocks):
+    """Split partials are merged in split order, not in the order the splits finish, so
+    repeated runs of one batch give identical bits."""
+    import paged_kv_attention_04_amd as pa
+    wl = synthetic.build("repro", 82, 32, 8, qo_len=[1, 96, 1], kv_len=[700, 1500, 1300], num_blocks=300,
+                         poison=False)
+    print(f"[gpu] reproducibility prefill_splits={prefill_splits} split_blocks={split_blocks}", flush=True)
+    first = pa.run_workload(wl, split_blocks=split_blocks, prefill_splits=prefill_splits)
+    for _ in range(5):
+        again = pa.run_workload(wl, split_blocks=split_blocks, prefill_splits=prefill_splits)
+        assert np.array_equal(again[2], first[2]) and np.array_equal(again[3], first[3])
