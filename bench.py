@@ -12,7 +12,7 @@ Each step reads a different copy of the KV pools (the copies stand for different
 layers), so no step finds the previous step's KV in the 256 MB last-level cache.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --kernel-only decode|mixed|prefill   # attention launches only, for rocprofv3
+    python bench.py --kernel-only decode|decode_q8|mixed|shared|prefill   # attention launches only, for rocprofv3
     python bench.py --summarize DIR [--title T]          # rocprofv3 CSV output -> profile text
 """
 from __future__ import annotations
@@ -51,14 +51,18 @@ def algorithmic_bytes(wl) -> dict:
             blk = int(wl.block_tables[r, b])
             n = min(B, int(wl.kv_len[r]) - b * B)
             slots[blk] = max(slots.get(blk, 0), n)
-    per_tok = 2 * wl.num_kv_heads * wl.head_dim * 2
+    new_tok = 2 * wl.num_kv_heads * wl.head_dim * 2          # one token's bf16 K and V rows
+    if getattr(wl, "kv_format", "bf16") == "q8_0":            # codes plus a 2-byte scale per 32 values
+        per_tok = 2 * wl.num_kv_heads * (wl.head_dim + 2 * (wl.head_dim // 32))
+    else:
+        per_tok = new_tok
     kv_unique = sum(slots.values()) * per_tok
     kv_logical = int(wl.kv_len.sum()) * per_tok
     q = wl.total_q * wl.num_q_heads * wl.head_dim * 2
     o = q
     lse = wl.total_q * wl.num_q_heads * 4
     meta = table + 8 * wl.num_reqs
-    append = wl.total_q * per_tok * 2 + wl.total_q * 4
+    append = wl.total_q * (new_tok + per_tok) + wl.total_q * 4
     return dict(kv_unique=kv_unique, kv_logical=kv_logical, attention=kv_unique + q + o + lse + meta,
                 append=append, step=kv_unique + q + o + lse + meta + append)
 
@@ -102,6 +106,7 @@ class Stepper:
         self.out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device=device)
         self.lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=device)
         self.cascade = cascade
+        self.q8 = getattr(wl, "kv_format", "bf16") == "q8_0"
         self.plan = self.make_plan()
         self.ws = pa.workspace_for(self.plan, device)
         self.i = 0
@@ -117,11 +122,12 @@ class Stepper:
         pa, wl = self.pa, self.wl
         kp, vp = self.pools[self.i % len(self.pools)]
         self.i += 1
+        append = pa.pa_append_kv_q8 if self.q8 else pa.pa_append_kv
+        attend = pa.pa_attention_batch_q8 if self.q8 else pa.pa_attention_batch
         if not attention_only:
             self.plan = self.make_plan()
-            pa.pa_append_kv(self.g, kp, vp, self.kn, self.vn, self.sm)
-        pa.pa_attention_batch(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
-                              self.lse, self.ws)
+            append(self.g, kp, vp, self.kn, self.vn, self.sm)
+        attend(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out, self.lse, self.ws)
 
 
 def time_steps(stepper, steps: int, warmup: int, attention_only: bool = False) -> float:
@@ -314,6 +320,7 @@ def kernel_only(which: str, reps: int):
     torch.cuda.set_device(0)
     pa.lib()
     wl = {"decode": lambda: synthetic.config_decode(poison=False),
+          "decode_q8": lambda: synthetic.config_decode_q8(poison=False),
           "mixed": lambda: synthetic.config_mixed(poison=False),
           "shared": lambda: synthetic.config_shared_prefix(poison=False),
           "prefill": prefill_only_workload}[which]()
@@ -394,7 +401,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 36-layer sweep")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--kernel-only", choices=["decode", "mixed", "shared", "prefill"])
+    ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "shared", "prefill"])
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--summarize")
     ap.add_argument("--title", default="rocprofv3 summary")
@@ -452,6 +459,27 @@ def main(argv=None):
             "prefix_groups": s3.plan.num_prefix_groups, "prefix_splits": s3.plan.prefix_splits}
         del s3
 
+    # the same decode step on a q8_0 pool (same lengths and tables): the saving against
+    # the pages' model, saving = fewer bytes / bandwidth - conversion time
+    wq = synthetic.config_decode_q8(poison=False)
+    abq = algorithmic_bytes(wq)
+    sq = Stepper(wq, args.copies)
+    sec_q = time_steps(sq, args.steps, args.warmup)
+    t_q = event_time(sq, max(args.steps, 50))
+    del sq
+    fewer = ab["attention"] - abq["attention"]
+    predicted = fewer / (achieved * 1e9)
+    q8 = {"workload": "qwen3_8b_decode_step on a q8_0 pool (32-value groups, int8 codes, binary16 scales), "
+                      "same lengths and block tables",
+          "attention_us": round(t_q * 1e6, 3), "bytes_per_launch": abq["attention"],
+          "gbs": round(abq["attention"] / t_q / 1e9, 1),
+          "frac_of_hbm_peak": round(abq["attention"] / t_q / 1e9 / HBM_PEAK_GBS, 4),
+          "step_ms": round(sec_q * 1e3, 5), "bf16_attention_us": round(t_attn * 1e6, 3),
+          "fewer_bytes": fewer, "bf16_gbs": round(achieved, 1),
+          "predicted_saving_us": round(predicted * 1e6, 3),
+          "measured_saving_us": round((t_attn - t_q) * 1e6, 3),
+          "implied_conversion_us": round((predicted - (t_attn - t_q)) * 1e6, 3)}
+
     # the prefill chunk alone, against the bf16 matrix peak
     wp = prefill_only_workload()
     sp = Stepper(wp, 2)
@@ -488,6 +516,7 @@ def main(argv=None):
                         "tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
                         "attention_us": round(t_m * 1e6, 3)},
         "shared_prefix": shared,
+        "q8_0_decode": q8,
         "prefill_chunk": {"workload": "512 new tokens at kv offset 4096, 32 q / 8 kv heads, causal",
                           "us": round(t_p * 1e6, 3), "tflops": round(pflops / t_p / 1e12, 1),
                           "frac_of_bf16_mfma_peak": round(pflops / t_p / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},

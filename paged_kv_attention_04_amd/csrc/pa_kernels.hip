@@ -1431,43 +1431,51 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        // lanes hold 32 output values of the row block: merge each with its own running
-        // weights (the lse is the same for all of a row's values).  The splits are taken in
-        // index order whichever of them finished last, so the result does not depend on
-        // the order in which they finished.
-        LseMerge mg[8][4];
+        // All 32 values a lane holds belong to one row and share its log2-sum-exp, so the
+        // merge weights are found once per split: L = max_s l_s, c_s = 2^(l_s - L), then
+        // O = sum_s c_s O_s / sum_s c_s and LSE = L + log2 sum_s c_s.  The splits are taken
+        // in index order whichever finished last, so the bits do not depend on timing.
+        auto lse_of = [&](int sp) __attribute__((always_inline)) {
+            return sp == split ? lse2[rb] : load_agent(part_lse_at(sp) + rb * 64 + lane);
+        };
+        float L = -INFINITY;
+        bool any_nan = false;
         for (int sp = 0; sp < p.splits; ++sp) {
-            float ls = lse2[rb];
-            float os[8][4];
+            const float ls = lse_of(sp);
+            any_nan |= ls != ls;
+            L = fmaxf(L, ls);
+        }
+        float wsum = 0.f;
+        f32x4 o[8];
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < p.splits; ++sp) {
+            const float ls = lse_of(sp);
+            const float c = (ls > -INFINITY) ? fast_exp2(ls - L) : 0.f;
+            wsum += c;
             if (sp == split) {
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        os[db][e] = oacc[rb][db][e];
+                    o[db] += c * oacc[rb][db];
             } else {
-                ls = load_agent(part_lse_at(sp) + rb * 64 + lane);
                 const float* po = part_o_at(sp);
+                f32x4 os[8];
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         os[db][e] = load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    o[db] += c * os[db];
             }
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    mg[db][e].add(ls, os[db][e]);
         }
-        const LseMerge& m0 = mg[0][0];
-        const float inv = m0.wsum > 0.f ? 1.f / m0.wsum : 0.f;
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                oacc[rb][db][e] = mg[db][e].o * inv;
-        lse2[rb] = m0.nan ? nan : (m0.wsum > 0.f ? m0.lmax + fast_log2(m0.wsum) : -INFINITY);
+            oacc[rb][db] = o[db] * inv;
+        lse2[rb] = any_nan ? nan : (wsum > 0.f ? L + fast_log2(wsum) : -INFINITY);
     }
     write_out(oacc, lse2);
 }
