@@ -240,37 +240,39 @@ pa_status pa_validate_copy(const pa_geometry* geometry, const int32_t* src_block
 /*
  * q8_0 KV pool (book section 8.4.2 and fig. 8-23: 32 values share one 2-byte scale and
  * are stored as 8-bit codes, 34 bytes in place of 64).  A group is 32 consecutive dims
- * of one token's row for one KV head.  Pool layout: [num_blocks][num_kv_heads] tiles of
+ * of one token's row for one KV head.  A K (or V) tile of one (block, KV head) is
  * PA_Q8_TILE_BYTES bytes: the block's [block_size][head_dim] int8 codes, then its
- * [block_size][head_dim / 32] IEEE binary16 scales.  A code c with scale d stands for
- * c * d.  Q, the outputs and the new K/V rows stay bf16.
+ * [block_size][head_dim / 32] IEEE binary16 scales; a code c with scale d stands for
+ * c * d.  One pool holds both: uint8 [num_blocks][num_kv_heads][2][PA_Q8_TILE_BYTES],
+ * each (block, KV head) its K tile, then its V tile, so a block's K and V for one head
+ * are read as one contiguous 4352-byte piece.  Q, the outputs and the new rows stay bf16.
  */
 #define PA_Q8_TILE_BYTES (16 * 128 + 16 * (128 / 32) * 2)
 
 /*
- * pa_append_kv into q8_0 pools: each new bf16 row is quantised per 32-value group with
+ * pa_append_kv into a q8_0 pool: each new bf16 row is quantised per 32-value group with
  * scale d = binary16(min(max|x| / 127, 65504)) (binary32 division, conversion to
  * nearest even) and codes rint(x / d) in binary32 (ties to even) clamped to [-127, 127],
- * 0 where d = 0.  New rows must be finite.  Arguments, slot rules and errors as for
- * pa_append_kv; k_pool_q8 / v_pool_q8 are uint8 [num_blocks][num_kv_heads][PA_Q8_TILE_BYTES].
+ * 0 where d = 0.  New rows must be finite.  Device pointers: kv_pool_q8 (written in
+ * place), k_new, v_new, slot_mapping; slot rules and errors as for pa_append_kv.
  */
-pa_status pa_append_kv_q8(const pa_geometry* geometry, void* k_pool_q8, void* v_pool_q8, const void* k_new,
-                          const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, void* stream);
+pa_status pa_append_kv_q8(const pa_geometry* geometry, void* kv_pool_q8, const void* k_new, const void* v_new,
+                          const int32_t* slot_mapping, int32_t n_tokens, void* stream);
 
 /*
- * pa_attention_batch over q8_0 pools, for batches of decode rows: the values are the
+ * pa_attention_batch over a q8_0 pool, for batches of decode rows: the values are the
  * codes times their scales, and everything else (outputs, splits, workspace) is as for
  * pa_attention_batch.  Q is read as binary16, which holds every bf16 value of magnitude
  * in [2^-14, 65504] exactly.  Returns PA_ERR_UNSUPPORTED for a plan with rows of
  * qo_len > 1 or shared-prefix groups.
  */
 pa_status pa_attention_batch_q8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q,
-                                const void* k_pool_q8, const void* v_pool_q8, const int32_t* block_tables,
-                                int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
-                                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+                                const void* kv_pool_q8, const int32_t* block_tables, int32_t max_blocks_per_req,
+                                const int32_t* qo_indptr, const int32_t* kv_len, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* pa_copy_blocks for q8_0 pools (tiles of PA_Q8_TILE_BYTES bytes); same rules and errors. */
-pa_status pa_copy_blocks_q8(const pa_geometry* geometry, void* k_pool_q8, void* v_pool_q8, const int32_t* src_blocks,
+/* pa_copy_blocks for a q8_0 pool (all of a block's tiles); same rules and errors. */
+pa_status pa_copy_blocks_q8(const pa_geometry* geometry, void* kv_pool_q8, const int32_t* src_blocks,
                             const int32_t* dst_blocks, int32_t n, void* stream);
 
 /* Compute-unit count of a HIP device (for pa_plan).  PA_ERR_HIP on failure. */

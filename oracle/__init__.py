@@ -55,9 +55,9 @@ def _load():
     lib.oracle_round_bf16_array.restype = None
     lib.oracle_slot.argtypes = [P, i64, i32]
     lib.oracle_slot.restype = i64
-    lib.oracle_attention_q8.argtypes = lib.oracle_attention.argtypes
+    lib.oracle_attention_q8.argtypes = lib.oracle_attention.argtypes[:1] + lib.oracle_attention.argtypes[2:]
     lib.oracle_attention_q8.restype = ctypes.c_int
-    lib.oracle_append_q8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32]
+    lib.oracle_append_q8.argtypes = [P, P, P, P, i32, i32, i32, i32, i32]
     lib.oracle_append_q8.restype = ctypes.c_int
     lib.oracle_quantize_q8_rows.argtypes = [P, i64, i32, P, P]
     lib.oracle_quantize_q8_rows.restype = ctypes.c_int
@@ -153,29 +153,32 @@ def quantize_q8_rows(x, head_dim: int):
     return codes, scales
 
 
-def append_q8(k_pool, v_pool, k_new, v_new, slot_mapping, num_kv_heads, head_dim, block_size, num_blocks):
-    """Quantise new bf16 K/V rows into copies of q8_0 pools [num_blocks][Hkv][tile bytes]."""
-    kp = np.array(k_pool, dtype=np.uint8, copy=True)
-    vp = np.array(v_pool, dtype=np.uint8, copy=True)
+def append_q8(kv_pool, k_new, v_new, slot_mapping, num_kv_heads, head_dim, block_size, num_blocks):
+    """Quantise new bf16 K/V rows into a copy of a q8_0 pool [num_blocks][Hkv][2][tile bytes]
+    (each (block, KV head) holds its K tile, then its V tile)."""
+    p = np.array(kv_pool, dtype=np.uint8, copy=True)
     kn, vn = _c(k_new, np.uint16), _c(v_new, np.uint16)
     sm = _c(slot_mapping, np.int32)
-    rc = _load().oracle_append_q8(_ptr(kp), _ptr(vp), _ptr(kn), _ptr(vn), _ptr(sm), int(sm.size),
-                                  int(num_kv_heads), int(head_dim), int(block_size), int(num_blocks))
+    rc = _load().oracle_append_q8(_ptr(p), _ptr(kn), _ptr(vn), _ptr(sm), int(sm.size), int(num_kv_heads),
+                                  int(head_dim), int(block_size), int(num_blocks))
     if rc != 0:
         raise ValueError(f"oracle_append_q8 failed with code {rc}")
-    return kp, vp
+    return p
 
 
 def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_kv_heads, head_dim,
               block_size, num_blocks, scale, row_select=None, want_f64: bool = False, kv_format: str = "bf16"):
     """Returns dict(out=bf16 bits [total_q][Hq][D], lse=float32 [total_q][Hq], pairs=int,
     and out_f64 / lse_f64 when ``want_f64``).  Rows not in ``row_select`` are left as zero.
-    ``kv_format`` "q8_0" reads q8_0 pools [num_blocks][Hkv][tile bytes] (uint8)."""
+    ``kv_format`` "q8_0" reads the q8_0 pool [num_blocks][Hkv][2][tile bytes] (uint8) passed as
+    ``k_pool`` (``v_pool`` is unused)."""
     qa = _c(q, np.uint16)
     if kv_format == "q8_0":
-        kp, vp, fn = _c(k_pool, np.uint8), _c(v_pool, np.uint8), _load().oracle_attention_q8
+        kp, fn = _c(k_pool, np.uint8), _load().oracle_attention_q8
+        pools = (_ptr(kp),)
     elif kv_format == "bf16":
         kp, vp, fn = _c(k_pool, np.uint16), _c(v_pool, np.uint16), _load().oracle_attention
+        pools = (_ptr(kp), _ptr(vp))
     else:
         raise ValueError(f"unknown kv_format {kv_format}")
     bt = _c(block_tables, np.int32)
@@ -188,7 +191,7 @@ def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_
     lse64 = np.zeros((total_q, num_q_heads), np.float64) if want_f64 else None
     sel = None if row_select is None else _c(row_select, np.uint8)
     pairs = ctypes.c_int64(0)
-    rc = fn(_ptr(qa), _ptr(kp), _ptr(vp), _ptr(bt), int(bt.shape[1]), _ptr(qo), _ptr(kv),
+    rc = fn(_ptr(qa), *pools, _ptr(bt), int(bt.shape[1]), _ptr(qo), _ptr(kv),
                                   R, int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
                                   int(num_blocks), float(scale), _ptr(sel), _ptr(out), _ptr(lse),
                                   _ptr(out64), _ptr(lse64), ctypes.cast(ctypes.pointer(pairs), ctypes.c_void_p))
@@ -204,9 +207,13 @@ def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_
 def run_workload(wl, row_select=None, want_f64: bool = False):
     """Append the workload's new tokens, then attend; returns (k_pool, v_pool, result)."""
     fmt = getattr(wl, "kv_format", "bf16")
-    put = append_q8 if fmt == "q8_0" else append
-    kp, vp = put(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
-                 wl.head_dim, wl.block_size, wl.num_blocks)
+    if fmt == "q8_0":
+        kp = append_q8(wl.kv_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads, wl.head_dim,
+                       wl.block_size, wl.num_blocks)
+        vp = None
+    else:
+        kp, vp = append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
+                        wl.head_dim, wl.block_size, wl.num_blocks)
     res = attention(wl.q, kp, vp, wl.block_tables, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
                     wl.head_dim, wl.block_size, wl.num_blocks, wl.scale, row_select=row_select,
                     want_f64=want_f64, kv_format=fmt)

@@ -33,9 +33,11 @@
  *
  *   q8_0 pool  (book section 8.4.2 and fig. 8-23: every 32 values share one 2-byte
  *              scale and are stored as 8-bit codes, 34 bytes instead of 64.)  A group
- *              is 32 consecutive dims of one token's row for one KV head.  One
- *              (block, KV head) tile holds the codes of its B tokens, [B][D] int8,
- *              followed by their scales, [B][D / 32] IEEE binary16.  The pages fix
+ *              is 32 consecutive dims of one token's row for one KV head.  The K (or
+ *              V) tile of one (block, KV head) holds the codes of its B tokens, [B][D]
+ *              int8, followed by their scales, [B][D / 32] IEEE binary16; the pool
+ *              keeps each (block, KV head)'s K tile and V tile side by side,
+ *              [num_blocks][Hkv][2][tile bytes].  The pages fix
  *              neither the scale's type nor the rounding; the readings taken here:
  *                d    = binary16(min(amax / 127, 65504)), amax = max |x| of the group,
  *                       the division in binary32, the conversion to nearest (ties even)
@@ -197,13 +199,12 @@ int64_t oracle_q8_tile_bytes(int32_t head_dim, int32_t block_size)
     return (int64_t)block_size * head_dim + (int64_t)block_size * (head_dim / 32) * 2;
 }
 
-/* append into q8_0 pools [num_blocks][Hkv][tile bytes]; k_new / v_new are bf16 [n][Hkv][D]. */
-int oracle_append_q8(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_new, const uint16_t* v_new,
-                     const int32_t* slot_mapping, int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim,
-                     int32_t block_size, int32_t num_blocks)
+/* append into a q8_0 pool [num_blocks][Hkv][2][tile bytes] (K tile, then V tile);
+ * k_new / v_new are bf16 [n][Hkv][D]. */
+int oracle_append_q8(uint8_t* kv_pool, const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
+                     int32_t n_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks)
 {
-    if (!k_pool || !v_pool || !k_new || !v_new || (!slot_mapping && n_tokens > 0) || n_tokens < 0 ||
-        head_dim % 32 != 0)
+    if (!kv_pool || !k_new || !v_new || (!slot_mapping && n_tokens > 0) || n_tokens < 0 || head_dim % 32 != 0)
         return ORACLE_BAD_ARG;
     const int64_t tile = oracle_q8_tile_bytes(head_dim, block_size);
     const int32_t groups = head_dim / 32;
@@ -217,7 +218,7 @@ int oracle_append_q8(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_new, co
         for (int32_t h = 0; h < num_kv_heads; ++h) {
             size_t src = ((size_t)t * num_kv_heads + h) * head_dim;
             for (int which = 0; which < 2; ++which) {
-                uint8_t* base = (which ? v_pool : k_pool) + ((size_t)blk * num_kv_heads + h) * tile;
+                uint8_t* base = kv_pool + (((size_t)blk * num_kv_heads + h) * 2 + which) * tile;
                 const uint16_t* row = (which ? v_new : k_new) + src;
                 for (int32_t g = 0; g < groups; ++g) {
                     uint16_t sc;
@@ -288,7 +289,9 @@ int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, c
  */
 enum { FMT_BF16 = 0, FMT_Q8_0 = 1 };
 
-/* The values of token `tok` of physical block `phys`, KV head kvh, as doubles. */
+/* The values of token `tok` of physical block `phys`, KV head kvh, as doubles.  q8_0:
+ * `pool` points at the K or the V tile of (block 0, KV head 0), and the tiles of
+ * consecutive (block, KV head) pairs lie two tiles apart. */
 static void load_row(int fmt, const void* pool, int32_t phys, int32_t kvh, int32_t tok, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, double* dst)
 {
@@ -299,7 +302,7 @@ static void load_row(int fmt, const void* pool, int32_t phys, int32_t kvh, int32
             dst[c] = bf16_to_double(src[c]);
     } else {
         const uint8_t* tile = (const uint8_t*)pool +
-                              ((size_t)phys * num_kv_heads + kvh) * (size_t)oracle_q8_tile_bytes(head_dim, block_size);
+                              ((size_t)phys * num_kv_heads + kvh) * 2 * (size_t)oracle_q8_tile_bytes(head_dim, block_size);
         const int8_t* codes = (const int8_t*)tile + (size_t)tok * head_dim;
         const uint8_t* sc = tile + (size_t)block_size * head_dim + (size_t)tok * (head_dim / 32) * 2;
         for (int32_t c = 0; c < head_dim; ++c) {
@@ -445,15 +448,17 @@ int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
                           out_f64, lse_f64, pair_count);
 }
 
-/* attention over q8_0 pools [num_blocks][Hkv][tile bytes]; everything else as above. */
-int oracle_attention_q8(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
-                        const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
+/* attention over a q8_0 pool [num_blocks][Hkv][2][tile bytes]; everything else as above. */
+int oracle_attention_q8(const uint16_t* q, const uint8_t* kv_pool, const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
                         const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale,
                         const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
                         double* lse_f64, int64_t* pair_count)
 {
-    return attention_impl(FMT_Q8_0, q, k_pool, v_pool, block_tables, max_blocks, qo_len, kv_len, num_reqs,
+    if (!kv_pool || head_dim <= 0 || block_size <= 0)
+        return ORACLE_BAD_ARG;
+    return attention_impl(FMT_Q8_0, q, kv_pool, kv_pool + oracle_q8_tile_bytes(head_dim, block_size), block_tables,
+                          max_blocks, qo_len, kv_len, num_reqs,
                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, row_select, out, lse,
                           out_f64, lse_f64, pair_count);
 }

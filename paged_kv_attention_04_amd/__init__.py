@@ -82,9 +82,9 @@ def lib():
     L.pa_validate_batch.argtypes = [G, i32, P, P, P, i32, P]
     L.pa_validate_append.argtypes = [G, P, i32, P]
     L.pa_copy_blocks.argtypes = [G, P, P, P, P, i32, P]
-    L.pa_append_kv_q8.argtypes = [G, P, P, P, P, P, i32, P]
-    L.pa_attention_batch_q8.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
-    L.pa_copy_blocks_q8.argtypes = [G, P, P, P, P, i32, P]
+    L.pa_append_kv_q8.argtypes = [G, P, P, P, P, i32, P]
+    L.pa_attention_batch_q8.argtypes = [G, PL, P, P, P, i32, P, P, P, P, P, sz, P]
+    L.pa_copy_blocks_q8.argtypes = [G, P, P, P, i32, P]
     L.pa_validate_copy.argtypes = [G, P, P, i32, P]
     L.pa_query_num_cus.argtypes = [i32, P]
     for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
@@ -189,34 +189,39 @@ def pa_append_kv(geometry: Geometry, k_pool, v_pool, k_new, v_new, slot_mapping,
 PA_Q8_TILE_BYTES = 16 * 128 + 16 * (128 // 32) * 2
 
 
-def pa_append_kv_q8(geometry: Geometry, k_pool_q8, v_pool_q8, k_new, v_new, slot_mapping, stream=None) -> None:
-    """Quantise new bf16 K/V rows into q8_0 pools (uint8 [num_blocks][Hkv][PA_Q8_TILE_BYTES])."""
+def q8_pool_shape(num_blocks: int, num_kv_heads: int):
+    """Shape of a q8_0 pool (uint8): each (block, KV head) holds its K tile, then its V tile."""
+    return (num_blocks, num_kv_heads, 2, PA_Q8_TILE_BYTES)
+
+
+def pa_append_kv_q8(geometry: Geometry, kv_pool_q8, k_new, v_new, slot_mapping, stream=None) -> None:
+    """Quantise new bf16 K/V rows into a q8_0 pool."""
     import torch
     n = int(slot_mapping.numel())
     if n == 0:
         return
     bf, u8 = _bf16_types(), (torch.uint8,)
     _check("pa_append_kv_q8", lib().pa_append_kv_q8(
-        ctypes.byref(geometry), _dev_ptr(k_pool_q8, u8, "k_pool_q8"), _dev_ptr(v_pool_q8, u8, "v_pool_q8"),
-        _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"),
-        _dev_ptr(slot_mapping, (torch.int32,), "slot_mapping"), n, _stream_handle(stream)))
+        ctypes.byref(geometry), _dev_ptr(kv_pool_q8, u8, "kv_pool_q8"), _dev_ptr(k_new, bf, "k_new"),
+        _dev_ptr(v_new, bf, "v_new"), _dev_ptr(slot_mapping, (torch.int32,), "slot_mapping"), n,
+        _stream_handle(stream)))
 
 
-def pa_attention_batch_q8(geometry: Geometry, plan: Plan, q, k_pool_q8, v_pool_q8, block_tables, qo_indptr, kv_len,
-                          out, lse, workspace=None, stream=None) -> None:
-    """Decode attention over q8_0 pools; the rest as pa_attention_batch."""
+def pa_attention_batch_q8(geometry: Geometry, plan: Plan, q, kv_pool_q8, block_tables, qo_indptr, kv_len, out, lse,
+                          workspace=None, stream=None) -> None:
+    """Decode attention over a q8_0 pool; the rest as pa_attention_batch."""
     import torch
     bf, i32, u8 = _bf16_types(), (torch.int32,), (torch.uint8,)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_attention_batch_q8", lib().pa_attention_batch_q8(
-        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(k_pool_q8, u8, "k_pool_q8"),
-        _dev_ptr(v_pool_q8, u8, "v_pool_q8"), _dev_ptr(block_tables, i32, "block_tables"),
-        int(block_tables.shape[1]), _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"),
-        _dev_ptr(out, bf, "out"), _dev_ptr(lse, (torch.float32,), "lse"), _dev_ptr(workspace, name="workspace"),
-        ws_bytes, _stream_handle(stream)))
+        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(kv_pool_q8, u8, "kv_pool_q8"),
+        _dev_ptr(block_tables, i32, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"), _dev_ptr(out, bf, "out"),
+        _dev_ptr(lse, (torch.float32,), "lse"), _dev_ptr(workspace, name="workspace"), ws_bytes,
+        _stream_handle(stream)))
 
 
-def pa_copy_blocks_q8(geometry: Geometry, k_pool_q8, v_pool_q8, src_blocks, dst_blocks, stream=None) -> None:
+def pa_copy_blocks_q8(geometry: Geometry, kv_pool_q8, src_blocks, dst_blocks, stream=None) -> None:
     import torch
     n = int(src_blocks.numel())
     if int(dst_blocks.numel()) != n:
@@ -225,9 +230,8 @@ def pa_copy_blocks_q8(geometry: Geometry, k_pool_q8, v_pool_q8, src_blocks, dst_
         return
     u8, i32 = (torch.uint8,), (torch.int32,)
     _check("pa_copy_blocks_q8", lib().pa_copy_blocks_q8(
-        ctypes.byref(geometry), _dev_ptr(k_pool_q8, u8, "k_pool_q8"), _dev_ptr(v_pool_q8, u8, "v_pool_q8"),
-        _dev_ptr(src_blocks, i32, "src_blocks"), _dev_ptr(dst_blocks, i32, "dst_blocks"), n,
-        _stream_handle(stream)))
+        ctypes.byref(geometry), _dev_ptr(kv_pool_q8, u8, "kv_pool_q8"), _dev_ptr(src_blocks, i32, "src_blocks"),
+        _dev_ptr(dst_blocks, i32, "dst_blocks"), n, _stream_handle(stream)))
 
 
 def pa_attention_batch(geometry: Geometry, plan: Plan, q, k_pool, v_pool, block_tables, qo_indptr, kv_len, out, lse,
@@ -314,7 +318,8 @@ def to_device(arr, device="cuda"):
 def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", validate: bool = True,
                  prefill_splits: int = 0, cascade: bool = False, min_shared_blocks: int = 0):
     """Upload a workload (see synthetic.Workload for the fields), append its new tokens,
-    plan and run attention; returns host numpy (k_pool, v_pool, out, lse)."""
+    plan and run attention; returns host numpy (k_pool, v_pool, out, lse), or
+    (kv_pool, None, out, lse) for a q8_0 workload."""
     import numpy as np
     import torch
     g = Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale, wl.head_dim, wl.block_size)
@@ -329,7 +334,10 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
     plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks, prefill_splits)
     if cascade:
         pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, num_cus, min_shared_blocks)
-    kp, vp = to_device(wl.k_pool, device), to_device(wl.v_pool, device)
+    if q8:
+        kp, vp = to_device(wl.kv_pool, device), None
+    else:
+        kp, vp = to_device(wl.k_pool, device), to_device(wl.v_pool, device)
     q = to_device(wl.q, device)
     bt = to_device(wl.block_tables, device)
     qo_indptr = to_device(wl.qo_indptr, device)
@@ -340,12 +348,14 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
     lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device=device)
     ws = workspace_for(plan, device)
     if q8:
-        pa_append_kv_q8(g, kp, vp, kn, vn, sm)
-        pa_attention_batch_q8(g, plan, q, kp, vp, bt, qo_indptr, kv, out, lse, ws)
+        pa_append_kv_q8(g, kp, kn, vn, sm)
+        pa_attention_batch_q8(g, plan, q, kp, bt, qo_indptr, kv, out, lse, ws)
     else:
         pa_append_kv(g, kp, vp, kn, vn, sm)
         pa_attention_batch(g, plan, q, kp, vp, bt, qo_indptr, kv, out, lse, ws)
     torch.cuda.synchronize()
-    pool_view = np.uint8 if q8 else np.uint16
-    return (kp.cpu().numpy().view(pool_view), vp.cpu().numpy().view(pool_view),
-            out.cpu().numpy().view(np.uint16), lse.cpu().numpy())
+    if q8:
+        pools = (kp.cpu().numpy(), None)
+    else:
+        pools = (kp.cpu().numpy().view(np.uint16), vp.cpu().numpy().view(np.uint16))
+    return pools + (out.cpu().numpy().view(np.uint16), lse.cpu().numpy())

@@ -14,7 +14,9 @@
 //
 // Pool layout: [block][kv_head][token-in-block][dim] (head-major inside a block), so one
 // (block, KV head) tile is 16 x 128 bf16 = 4 KiB of contiguous memory.  A q8_0 tile is
-// the 16 x 128 int8 codes followed by the 16 x 4 binary16 scales: 2176 bytes.
+// the 16 x 128 int8 codes followed by the 16 x 4 binary16 scales, 2176 bytes, and the
+// q8_0 pool keeps each (block, KV head)'s K tile and V tile side by side (4352 bytes):
+// half-size tiles read as separate 2 KiB pieces stream markedly slower from HBM.
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <math.h>
@@ -139,12 +141,6 @@ __device__ inline float dot2_f16(uint32_t a, uint32_t b, float c)
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
 }
 
-// Value held by lane `src` of this wavefront (any lane may name any source).
-__device__ inline uint32_t lane_value(uint32_t v, int src)
-{
-    return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
-}
-
 // q8_0 codes as exact binary16 numbers: the int8 code c becomes 1152 + c (= 1024 + (c + 128),
 // whose bit pattern is 0x64 : (c ^ 0x80)).  The products then carry a bias of 1152 times
 // the other operand, which the callers take off once.  `sel` picks, through v_perm, the
@@ -185,7 +181,7 @@ __global__ __launch_bounds__(256) void pa_append_scatter(uint16_t* __restrict__ 
 // One thread quantises one 32-value group of one (token, KV head) row, K and V: scale
 // d = binary16(min(amax / 127, 65504)), codes rint(x / d) clamped to +-127 (0 when d = 0),
 // the divisions in binary32 rounded to nearest.
-__global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+__global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict__ kv_pool,
                                                             const uint16_t* __restrict__ k_new,
                                                             const uint16_t* __restrict__ v_new,
                                                             const int32_t* __restrict__ slot_mapping,
@@ -239,7 +235,7 @@ __global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict_
             }
             packed[i] = word;
         }
-        uint8_t* tile = (which ? v_pool : k_pool) + (blk * num_kv_heads + h) * pa::kQ8TileBytes;
+        uint8_t* tile = kv_pool + ((blk * num_kv_heads + h) * 2 + which) * pa::kQ8TileBytes;
         u32x4* codes = reinterpret_cast<u32x4*>(tile + off * kHeadDim + grp * pa::kQ8Group);
         codes[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
         codes[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
@@ -249,23 +245,21 @@ __global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict_
 
 // ------------------------------------------------------------------------------ block copy
 
-// One thread per 16 bytes of a (pair, pool, KV head) tile: pairs x 2 pools x Hkv x
-// tile_chunks threads (tile_chunks = 16-byte chunks per tile: 256 for bf16, 136 for
-// q8_0); consecutive threads move one contiguous tile.
+// One thread per 16 bytes of a block: pairs x npools x blk_chunks threads, where a block
+// of one pool is blk_chunks 16-byte chunks (bf16: two pools, Hkv x 256 chunks each; q8_0:
+// one pool, Hkv x 272 chunks); consecutive threads move contiguous memory.
 __global__ __launch_bounds__(256) void pa_copy_scatter(u32x4* __restrict__ k_pool, u32x4* __restrict__ v_pool,
                                                        const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
-                                                       int32_t n, int32_t num_kv_heads, int32_t num_blocks,
-                                                       int32_t tile_chunks)
+                                                       int32_t n, int32_t num_blocks, int64_t blk_chunks, int32_t npools)
 {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk_chunks = (int64_t)num_kv_heads * tile_chunks;   // 16-byte chunks per block (all KV heads)
-    const int64_t pair = t / (2 * blk_chunks);
+    const int64_t pair = t / (npools * blk_chunks);
     if (pair >= n)
         return;
     const int32_t s = src[pair], d = dst[pair];
     if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
         return;
-    const int64_t rem = t - pair * 2 * blk_chunks;
+    const int64_t rem = t - pair * npools * blk_chunks;
     u32x4* pool = rem >= blk_chunks ? v_pool : k_pool;
     const int64_t within = rem % blk_chunks;
     pool[(int64_t)d * blk_chunks + within] = pool[(int64_t)s * blk_chunks + within];
@@ -311,9 +305,9 @@ struct DecodeParams {
 // KV blocks whose loads are in flight while a block is being processed.
 constexpr int kDecodeDepth = PA_DECODE_DEPTH;
 #ifndef PA_DECODE_DEPTH_Q8
-#define PA_DECODE_DEPTH_Q8 2
+#define PA_DECODE_DEPTH_Q8 1
 #endif
-constexpr int kDecodeDepthQ8 = PA_DECODE_DEPTH_Q8;   // a q8_0 stage is half the bytes
+constexpr int kDecodeDepthQ8 = PA_DECODE_DEPTH_Q8;   // deeper was measured slower
 constexpr int kDecodeWaves = pa::kDecodeWaves;
 
 // One (block, KV head) tile is 16 tokens x 256 bytes, read by four 16-byte loads per lane.
@@ -344,12 +338,11 @@ __device__ inline void load_stage(KvStage& s, const uint16_t* ktile, const uint1
 //    c8 / 2) of tokens t8 and t8 + 8; each load covers 1 KiB, eight whole 128-byte rows.
 // V: lane = 16 * tg + c16 reads the 8 codes of dims 8 c16 .. 8 c16 + 7 (group c16 / 4) of
 //    tokens tg + 4 i, i = 0..3: 512 contiguous bytes per load.
-// Scales: lane i reads scale i, (token i / 4, group i % 4); the others fetch theirs from
-//    that lane.
+// Scales: each lane reads the scales of its own tokens and group (2 for K, 4 for V).
 struct KvStageQ8 {
     u32x4 k[2];
     u32x2 v[4];
-    uint32_t ks, vs;
+    uint32_t ks[2], vs[4];
 };
 
 __device__ inline void load_stage_q8(KvStageQ8& s, const uint8_t* ktile, const uint8_t* vtile, int lane)
@@ -360,8 +353,13 @@ __device__ inline void load_stage_q8(KvStageQ8& s, const uint8_t* ktile, const u
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         s.v[i] = *reinterpret_cast<const u32x2*>(vtile + (tg + 4 * i) * kHeadDim + 8 * c16);
-    s.ks = reinterpret_cast<const uint16_t*>(ktile + pa::kQ8CodeBytes)[lane];
-    s.vs = reinterpret_cast<const uint16_t*>(vtile + pa::kQ8CodeBytes)[lane];
+    const uint16_t* ksc = reinterpret_cast<const uint16_t*>(ktile + pa::kQ8CodeBytes);
+    const uint16_t* vsc = reinterpret_cast<const uint16_t*>(vtile + pa::kQ8CodeBytes);
+    s.ks[0] = ksc[t8 * 4 + (c8 >> 1)];
+    s.ks[1] = ksc[(t8 + 8) * 4 + (c8 >> 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s.vs[i] = vsc[(tg + 4 * i) * 4 + (c16 >> 2)];
 }
 
 __device__ inline float dot16(const u32x4& q, const u32x4& k, float acc)
@@ -478,9 +476,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
         int id = __builtin_amdgcn_readlane(my_blk, j);
         id = (id >= 0 && id < p.num_blocks) ? id : 0;
         if constexpr (kQ8) {
-            const int64_t off = ((int64_t)id * p.num_kv_heads + kvh) * pa::kQ8TileBytes;
-            load_stage_q8(st, reinterpret_cast<const uint8_t*>(p.k_pool) + off,
-                          reinterpret_cast<const uint8_t*>(p.v_pool) + off, lane);
+            const uint8_t* kt = reinterpret_cast<const uint8_t*>(p.k_pool) +
+                                ((int64_t)id * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);
+            load_stage_q8(st, kt, kt + pa::kQ8TileBytes, lane);
         } else {
             const int64_t off = ((int64_t)id * p.num_kv_heads + kvh) * kBlock * kHeadDim;
             load_stage(st, p.k_pool + off, p.v_pool + off, lane);
@@ -559,7 +557,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
         if constexpr (kQ8) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const float dk = half_bits_to_float(lane_value(st.ks, (t8 + 8 * tt) * 4 + (c8 >> 1)));
+                const float dk = half_bits_to_float(st.ks[tt]);
                 const u32x4 w = st.k[tt];
                 uint32_t kc[8];
 #pragma unroll
@@ -621,7 +619,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
             float dv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                dv[i] = half_bits_to_float(lane_value(st.vs, (tg + 4 * i) * 4 + (c16 >> 2)));
+                dv[i] = half_bits_to_float(st.vs[i]);
                 if (tg + 4 * i >= valid)
                     dv[i] = 0.f;
             }
@@ -1510,8 +1508,8 @@ extern "C" pa_status pa_append_kv(const pa_geometry* g, void* k_pool, void* v_po
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-extern "C" pa_status pa_append_kv_q8(const pa_geometry* g, void* k_pool_q8, void* v_pool_q8, const void* k_new,
-                                     const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, void* stream)
+extern "C" pa_status pa_append_kv_q8(const pa_geometry* g, void* kv_pool_q8, const void* k_new, const void* v_new,
+                                     const int32_t* slot_mapping, int32_t n_tokens, void* stream)
 {
     if (!g)
         return PA_ERR_NULL;
@@ -1521,21 +1519,21 @@ extern "C" pa_status pa_append_kv_q8(const pa_geometry* g, void* k_pool_q8, void
         return PA_ERR_SHAPE;
     if (n_tokens == 0)
         return PA_OK;
-    if (!k_pool_q8 || !v_pool_q8 || !k_new || !v_new || !slot_mapping)
+    if (!kv_pool_q8 || !k_new || !v_new || !slot_mapping)
         return PA_ERR_NULL;
     const int64_t threads = (int64_t)n_tokens * g->num_kv_heads * (kHeadDim / pa::kQ8Group);
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > INT32_MAX)
         return PA_ERR_SHAPE;
     hipLaunchKernelGGL(pa_append_q8_scatter, dim3((uint32_t)blocks), dim3(256), 0, as_stream(stream),
-                       static_cast<uint8_t*>(k_pool_q8), static_cast<uint8_t*>(v_pool_q8),
-                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping,
-                       n_tokens, g->num_kv_heads, (int64_t)g->num_blocks * kBlock);
+                       static_cast<uint8_t*>(kv_pool_q8), static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), slot_mapping, n_tokens, g->num_kv_heads,
+                       (int64_t)g->num_blocks * kBlock);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 static pa_status copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
-                             const int32_t* dst_blocks, int32_t n, void* stream, int32_t tile_bytes)
+                             const int32_t* dst_blocks, int32_t n, void* stream, int64_t head_bytes, int32_t npools)
 {
     if (!g)
         return PA_ERR_NULL;
@@ -1547,27 +1545,27 @@ static pa_status copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, c
         return PA_OK;
     if (!k_pool || !v_pool || !src_blocks || !dst_blocks)
         return PA_ERR_NULL;
-    const int32_t tile_chunks = tile_bytes / 16;
-    const int64_t threads = (int64_t)n * 2 * g->num_kv_heads * tile_chunks;
+    const int64_t blk_chunks = (int64_t)g->num_kv_heads * head_bytes / 16;   // one pool's block, all KV heads
+    const int64_t threads = (int64_t)n * npools * blk_chunks;
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > INT32_MAX)
         return PA_ERR_SHAPE;
     hipLaunchKernelGGL(pa_copy_scatter, dim3((uint32_t)blocks), dim3(256), 0, as_stream(stream),
                        static_cast<u32x4*>(k_pool), static_cast<u32x4*>(v_pool), src_blocks, dst_blocks, n,
-                       g->num_kv_heads, g->num_blocks, tile_chunks);
+                       g->num_blocks, blk_chunks, npools);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 extern "C" pa_status pa_copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
                                     const int32_t* dst_blocks, int32_t n, void* stream)
 {
-    return copy_blocks(g, k_pool, v_pool, src_blocks, dst_blocks, n, stream, kBlock * kHeadDim * 2);
+    return copy_blocks(g, k_pool, v_pool, src_blocks, dst_blocks, n, stream, kBlock * kHeadDim * 2, 2);
 }
 
-extern "C" pa_status pa_copy_blocks_q8(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
+extern "C" pa_status pa_copy_blocks_q8(const pa_geometry* g, void* kv_pool_q8, const int32_t* src_blocks,
                                        const int32_t* dst_blocks, int32_t n, void* stream)
 {
-    return copy_blocks(g, k_pool, v_pool, src_blocks, dst_blocks, n, stream, pa::kQ8TileBytes);
+    return copy_blocks(g, kv_pool_q8, kv_pool_q8, src_blocks, dst_blocks, n, stream, 2 * pa::kQ8TileBytes, 1);
 }
 
 static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t* plan, const void* q,
@@ -1730,12 +1728,12 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
 }
 
 extern "C" pa_status pa_attention_batch_q8(const pa_geometry* g, const pa_plan_t* plan, const void* q,
-                                           const void* k_pool_q8, const void* v_pool_q8, const int32_t* block_tables,
+                                           const void* kv_pool_q8, const int32_t* block_tables,
                                            int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
                                            void* out, float* lse, void* workspace, size_t workspace_bytes,
                                            void* stream)
 {
-    return attention_batch(true, g, plan, q, k_pool_q8, v_pool_q8, block_tables, max_blocks_per_req, qo_indptr,
+    return attention_batch(true, g, plan, q, kv_pool_q8, kv_pool_q8, block_tables, max_blocks_per_req, qo_indptr,
                            kv_len, out, lse, workspace, workspace_bytes, stream);
 }
 

@@ -84,7 +84,10 @@ class Workload:
     slot_mapping: np.ndarray
     shared_prefix_blocks: int = 0
     notes: dict = field(default_factory=dict)
-    kv_format: str = "bf16"      # "q8_0": pools are uint8 [num_blocks][num_kv_heads][q8_tile_bytes]
+    kv_format: str = "bf16"
+    # q8_0 only (k_pool / v_pool are then None): uint8 [num_blocks][num_kv_heads][2][q8_tile_bytes],
+    # each (block, KV head) holding its K tile, then its V tile
+    kv_pool: Optional[np.ndarray] = None
 
     @property
     def num_reqs(self) -> int:
@@ -223,14 +226,11 @@ def build_q8(name: str, seed: int, num_q_heads: int, num_kv_heads: int, qo_len, 
     nb = [-(-int(L) // B) for L in kv_len]
     bt = place_blocks(s_place, num_blocks, nb, shared_prefix_blocks, None)
     tile = q8_tile_bytes(D, B)
-    pools = []
-    for s_x in (s_k, s_v):
-        pool = np.zeros((num_blocks, Hkv, tile), np.uint8)
-        if poison:
-            pool[:, :, :B * D] = s_x.integers(0, 256, (num_blocks, Hkv, B * D), dtype=np.uint8)
-            pool[:, :, B * D:].view(np.uint16)[...] = HALF_NAN
-        pools.append(pool)
-    k_pool, v_pool = pools
+    kv_pool = np.zeros((num_blocks, Hkv, 2, tile), np.uint8)
+    if poison:
+        for which, s_x in ((0, s_k), (1, s_v)):
+            kv_pool[:, :, which, :B * D] = s_x.integers(0, 256, (num_blocks, Hkv, B * D), dtype=np.uint8)
+        kv_pool[:, :, :, B * D:].view(np.uint16)[...] = HALF_NAN
     filled = set()
     for r in range(R):
         ctx = int(kv_len[r] - qo_len[r])
@@ -239,13 +239,12 @@ def build_q8(name: str, seed: int, num_q_heads: int, num_kv_heads: int, qo_len, 
             n = min(B, ctx - b * B)
             if phys in filled:
                 continue
-            for pool, s_x in ((k_pool, s_k), (v_pool, s_v)):
+            for which, s_x in ((0, s_k), (1, s_v)):
                 codes = np.clip(np.rint(s_x.standard_normal((Hkv, n, D)) * 42.0), -127, 127).astype(np.int8)
                 scales = s_x.uniform(0.018, 0.03, (Hkv, n, G)).astype(np.float16).view(np.uint16)
-                cv = pool[phys, :, :B * D].reshape(Hkv, B, D).view(np.int8)
-                cv[:, :n, :] = codes
-                sv = pool[phys, :, B * D:].reshape(Hkv, B * G * 2).view(np.uint16).reshape(Hkv, B, G)
-                sv[:, :n, :] = scales
+                t = kv_pool[phys, :, which]                       # [Hkv][tile bytes], a view
+                t[:, :B * D].reshape(Hkv, B, D)[:, :n, :] = codes.view(np.uint8)
+                t[:, B * D:].reshape(Hkv, B, G * 2)[:, :n, :] = scales.view(np.uint8).reshape(Hkv, n, G * 2)
             if n == B:
                 filled.add(phys)
     n_new = int(qo_len.sum())
@@ -260,8 +259,9 @@ def build_q8(name: str, seed: int, num_q_heads: int, num_kv_heads: int, qo_len, 
     q = f32_to_bf16_bits(s_q.standard_normal((n_new, Hq, D), dtype=np.float32) * np.float32(q_scale))
     return Workload(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
                     num_blocks=num_blocks, scale=1.0 / np.sqrt(D), qo_len=qo_len, kv_len=kv_len,
-                    block_tables=bt, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
-                    slot_mapping=slots, shared_prefix_blocks=shared_prefix_blocks, kv_format="q8_0")
+                    block_tables=bt, q=q, k_pool=None, v_pool=None, k_new=k_new, v_new=v_new,
+                    slot_mapping=slots, shared_prefix_blocks=shared_prefix_blocks, kv_format="q8_0",
+                    kv_pool=kv_pool)
 
 
 def config_tiny_q8(seed: int = 11, poison: bool = True, q_scale: float = 1.0) -> Workload:

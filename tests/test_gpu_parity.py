@@ -404,17 +404,18 @@ def test_q8_copy_blocks_bit_exact():
     import paged_kv_attention_04_amd as pa
     rng = np.random.default_rng(17)
     nb, Hkv = 300, 8
-    kp = rng.integers(0, 256, (nb, Hkv, pa.PA_Q8_TILE_BYTES), dtype=np.uint8)
-    vp = rng.integers(0, 256, (nb, Hkv, pa.PA_Q8_TILE_BYTES), dtype=np.uint8)
+    pool = rng.integers(0, 256, pa.q8_pool_shape(nb, Hkv), dtype=np.uint8)
     perm = rng.permutation(nb)
     src, dst = perm[:40].astype(np.int32), perm[40:80].astype(np.int32)
+    src = np.concatenate([src, [-1, 3]]).astype(np.int32)
+    dst = np.concatenate([dst, [5, nb]]).astype(np.int32)
     g = pa.Geometry.make(32, Hkv, nb)
-    dk, dv = pa.to_device(kp), pa.to_device(vp)
-    pa.pa_copy_blocks_q8(g, dk, dv, pa.to_device(src), pa.to_device(dst))
+    dp = pa.to_device(pool)
+    pa.pa_copy_blocks_q8(g, dp, pa.to_device(src), pa.to_device(dst))
     torch.cuda.synchronize()
-    ek, ev = kp.copy(), vp.copy()
-    ek[dst], ev[dst] = kp[src], vp[src]
-    assert np.array_equal(dk.cpu().numpy(), ek) and np.array_equal(dv.cpu().numpy(), ev)
+    want = pool.copy()
+    want[dst[:40]] = pool[src[:40]]
+    assert np.array_equal(dp.cpu().numpy(), want)
 
 
 @pytest.mark.parametrize("prefill_splits,split_blocks", [(3, 7), (64, 2)])

@@ -566,11 +566,13 @@ def test_q8_quantise_error_bound_and_edges():
     assert np.all(bs == 0x7BFF) and np.all(bc == 127)
 
 
-def _dequantise(pool, Hkv, D=128, B=16):
-    """numpy reading of the tile layout: [B][D] int8 codes, then [B][D/32] binary16 scales."""
+def _dequantise(pool, which, Hkv, D=128, B=16):
+    """numpy reading of the layout: pool [nb][Hkv][2][tile], `which` 0 = K, 1 = V; a tile is
+    [B][D] int8 codes, then [B][D/32] binary16 scales."""
     nb = pool.shape[0]
-    codes = pool[:, :, :B * D].reshape(nb, Hkv, B, D).view(np.int8).astype(np.float64)
-    sc = np.ascontiguousarray(pool[:, :, B * D:]).view(np.float16).reshape(nb, Hkv, B, D // 32).astype(np.float64)
+    t = np.ascontiguousarray(pool.reshape(nb, Hkv, 2, -1)[:, :, which])
+    codes = t[:, :, :B * D].reshape(nb, Hkv, B, D).view(np.int8).astype(np.float64)
+    sc = np.ascontiguousarray(t[:, :, B * D:]).view(np.float16).reshape(nb, Hkv, B, D // 32).astype(np.float64)
     return codes * np.repeat(sc, 32, axis=3)
 
 
@@ -578,8 +580,8 @@ def test_q8_attention_equals_dense_softmax_on_dequantised_values():
     """Append (quantise) then attend, against a dense numpy softmax over the values the
     codes represent, gathered through the block table."""
     wl = synthetic.config_tiny_q8(poison=True)
-    kp, vp, res = oracle.run_workload(wl, want_f64=True)
-    K, V = _dequantise(kp, wl.num_kv_heads), _dequantise(vp, wl.num_kv_heads)
+    pool, _, res = oracle.run_workload(wl, want_f64=True)
+    K, V = _dequantise(pool, 0, wl.num_kv_heads), _dequantise(pool, 1, wl.num_kv_heads)
     q = bf16_bits_to_f32(wl.q).astype(np.float64)
     g = wl.num_q_heads // wl.num_kv_heads
     for r in range(wl.num_reqs):
@@ -597,13 +599,12 @@ def test_q8_attention_equals_dense_softmax_on_dequantised_values():
 
 def test_q8_append_writes_exactly_the_quantised_rows():
     wl = synthetic.config_tiny_q8(poison=True)
-    kp, vp = oracle.append_q8(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads, 128, 16,
-                              wl.num_blocks)
-    for pool0, pool1, new in ((wl.k_pool, kp, wl.k_new), (wl.v_pool, vp, wl.v_new)):
+    got = oracle.append_q8(wl.kv_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads, 128, 16, wl.num_blocks)
+    want = wl.kv_pool.copy()
+    for which, new in ((0, wl.k_new), (1, wl.v_new)):
         codes, scales = oracle.quantize_q8_rows(new, 128)
-        want = pool0.copy()
         for t, s in enumerate(wl.slot_mapping):
             blk, off = divmod(int(s), 16)
-            want[blk, :, off * 128:(off + 1) * 128] = codes[t].view(np.uint8)
-            want[blk, :, 2048 + off * 8:2048 + off * 8 + 8] = scales[t].view(np.uint8).reshape(wl.num_kv_heads, 8)
-        assert np.array_equal(pool1, want)
+            want[blk, :, which, off * 128:(off + 1) * 128] = codes[t].view(np.uint8)
+            want[blk, :, which, 2048 + off * 8:2048 + off * 8 + 8] = scales[t].view(np.uint8).reshape(wl.num_kv_heads, 8)
+    assert np.array_equal(got, want)
