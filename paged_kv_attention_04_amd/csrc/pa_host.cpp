@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <unordered_set>
+#include <map>
 #include <vector>
 
 #include "pa_internal.h"
@@ -82,6 +83,65 @@ void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t*
     }
     plan->max_splits = max_splits;
     plan->decode_items = (int32_t)std::min<int64_t>(items, INT32_MAX);
+}
+
+// Shared-prefix workgroups and decode workgroups run in one launch: the prefix ones first
+// in the grid, then the decode ones split-major, each dispatched to the first CU that
+// frees up (one workgroup per CU).  Makespan of that launch in decode block-times, from a
+// greedy list-scheduling simulation over batches of identical workgroups (a map from
+// free time to the number of CUs free then).  Costs, fitted to measurements on MI355X
+// (rms error ~2 us over 20 split choices of the 16-request, 6144-token-prefix case): a
+// decode workgroup streams its blocks at 1 each plus 13.3 of fixed cost, and the last
+// split of a row also merges its partials, 6.67 per eight; a prefix workgroup costs 33.3
+// plus 6.67 per 128-key step.
+constexpr double kFusedDecodeFixed = 13.3;
+constexpr double kFusedPrefixFixed = 33.3;
+constexpr double kFusedPrefixStep = 6.67;
+constexpr double kFusedMergePer8 = 6.67;
+constexpr int32_t kPrefixStepsPerSplit = 6;
+
+double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_blocks, const int32_t* qo_len,
+                      int32_t num_kv_heads, int32_t num_cus, int32_t prefix_splits, int32_t split_blocks)
+{
+    std::map<double, int64_t> free_at;     // time -> CUs that become free then
+    free_at[0.0] = std::max(num_cus, 1);
+    double end = 0.0;
+    auto run = [&](int64_t count, double d) {
+        while (count > 0) {
+            auto it = free_at.begin();
+            const double t = it->first;
+            const int64_t n = std::min(count, it->second);
+            if ((it->second -= n) == 0)
+                free_at.erase(it);
+            free_at[t + d] += n;
+            end = std::max(end, t + d);
+            count -= n;
+        }
+    };
+    for (int32_t gi = 0; gi < plan.num_prefix_groups; ++gi) {
+        const int32_t steps = ceil_div((int64_t)plan.prefix_blocks[gi] * pa::kBlock, pa::kPrefillKeys);
+        for (int32_t sp = 0; sp < prefix_splits; ++sp) {
+            const int32_t n = (sp + 1) * steps / prefix_splits - sp * steps / prefix_splits;
+            run(num_kv_heads, kFusedPrefixFixed + kFusedPrefixStep * n);
+        }
+    }
+    int32_t max_splits = 0;
+    for (size_t r = 0; r < suffix_blocks.size(); ++r)
+        if (qo_len[r] == 1)
+            max_splits = std::max(max_splits, ceil_div(suffix_blocks[r], split_blocks));
+    for (int32_t sp = 0; sp < max_splits; ++sp)
+        for (size_t r = 0; r < suffix_blocks.size(); ++r) {
+            if (qo_len[r] != 1)
+                continue;
+            const int32_t ns = ceil_div(suffix_blocks[r], split_blocks);
+            const int32_t n = std::min(split_blocks, suffix_blocks[r] - sp * split_blocks);
+            if (n <= 0)
+                continue;
+            const double merge =
+                sp == ns - 1 ? kFusedMergePer8 * (ceil_div(ns, 8) + ceil_div(prefix_splits, 8)) : 0.0;
+            run(num_kv_heads, kFusedDecodeFixed + n + merge);
+        }
+    return end;
 }
 
 pa_status finish_workspace(const pa_geometry* g, pa_plan_t* plan)
@@ -233,20 +293,42 @@ extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* 
     if (out.num_prefix_groups == 0)
         return PA_OK;
 
-    // Key splits of the shared blocks: enough (group, KV head, split) workgroups to fill
-    // the CUs, each at least two 128-key steps long.
-    const int32_t steps = ceil_div((int64_t)max_prefix_blocks * pa::kBlock, pa::kPrefillKeys);
-    const int64_t base = (int64_t)out.num_prefix_groups * g->num_kv_heads;
-    int32_t ps = (int32_t)std::max<int64_t>(1, std::max(num_cus, 1) / base);
-    ps = std::min(ps, std::max(1, steps / 2));
-    out.prefix_splits = std::min(ps, pa::kMaxPrefillSplits);
-
-    // Decode splits over the private suffixes.
-    std::vector<int32_t> skip(R, 0);
+    // Key splits of the shared blocks: at most kPrefixStepsPerSplit 128-key steps per
+    // prefix workgroup, so that the prefix pass ends before the decode splits it shares
+    // the launch with (measured on the 6144-token prefix: 6 steps per split ran in 42 us,
+    // 8 and more in 63-100 us, a prefix workgroup then finishing last and merging its
+    // group's rows).  Then the decode split length over the private suffixes with the
+    // smallest simulated makespan of the fused launch (ties to the longer split).
+    std::vector<int32_t> skip(R, 0), suffix(R, 0);
     for (int32_t i = 0; i < out.num_prefix_groups; ++i)
         for (int32_t k = 0; k < out.prefix_num_reqs[i]; ++k)
             skip[out.prefix_first_req[i] + k] = out.prefix_blocks[i];
-    choose_decode_splits(g, R, qo_len, kv_len, skip.data(), num_cus, 0, &out);
+    int32_t longest = 1;
+    for (int32_t r = 0; r < R; ++r) {
+        suffix[r] = decode_blocks(kv_len, skip.data(), r);
+        if (qo_len[r] == 1)
+            longest = std::max(longest, suffix[r]);
+    }
+    const int32_t steps = ceil_div((int64_t)max_prefix_blocks * pa::kBlock, pa::kPrefillKeys);
+    const int32_t best_ps = std::min(std::max(1, ceil_div(steps, kPrefixStepsPerSplit)), pa::kMaxPrefillSplits);
+    double best = 0.0;
+    int32_t best_sb = std::min(longest, pa::kMaxSplitBlocks);
+    bool have = false;
+    for (int32_t parts = 1; parts <= 16; ++parts) {
+        const int32_t sb = ceil_div(longest, parts);
+        if (sb > pa::kMaxSplitBlocks)
+            continue;
+        if (sb < kMinAutoSplitBlocks && parts > 1)
+            break;
+        const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, best_ps, sb);
+        if (!have || t < best - 1e-9) {
+            have = true;
+            best = t;
+            best_sb = sb;
+        }
+    }
+    out.prefix_splits = best_ps;
+    choose_decode_splits(g, R, qo_len, kv_len, skip.data(), num_cus, best_sb, &out);
     const pa_status st = finish_workspace(g, &out);
     if (st != PA_OK)
         return st;

@@ -37,6 +37,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 //                 prefill (tile, KV head) pairs after them at num_reqs * Hkv + tile * Hkv + kvh;
 //                 zero before the first use of the buffer, and every call leaves them zero
 //   part_o        normalised FP32 decode split outputs [num_reqs][max_splits][Hq][head_dim]
+//                 (also present with one split per row when there are shared-prefix groups)
 //   part_lse      per-split log2-sum-exp [num_reqs][max_splits][Hq]
 //   pf_part_o     normalised FP32 prefill split outputs, 128 x 128 floats per (tile, KV head,
 //                 split), in the order the prefill kernel's lanes hold them
@@ -64,7 +65,9 @@ inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, in
                                         int32_t prefix_splits = 0)
 {
     WorkspaceLayout w;
-    const bool decode = max_splits > 1 && num_reqs > 0;
+    // decode partials: split rows, and every row of a shared-prefix group (its decode
+    // result waits there for the group's prefix partials)
+    const bool decode = (max_splits > 1 || prefix_splits > 0) && num_reqs > 0;
     const bool prefill = prefill_splits > 1 && prefill_tiles > 0;
     const bool prefix = prefix_splits > 0 && num_reqs > 0;
     if (!decode && !prefill && !prefix)

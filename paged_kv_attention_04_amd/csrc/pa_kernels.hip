@@ -406,6 +406,96 @@ __device__ inline void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Decode splits of row r whose first `skip` blocks a shared-prefix pass covers, or -1 when
+// the row is not a decode row or its lengths disagree with the plan.  The decode kernel and
+// the shared-prefix pass both count into a (row, KV head) counter and use this one test, so
+// they agree on how many arrivals complete it.
+__device__ inline int decode_splits_of(const DecodeParams& p, int r, int skip)
+{
+    if (p.qo_indptr[r + 1] - p.qo_indptr[r] != 1)
+        return -1;
+    const int kvlen = p.kv_len[r];
+    const int nblk = (kvlen + kBlock - 1) / kBlock;
+    if (kvlen < 1 || nblk > p.max_blocks || nblk <= skip || p.split_blocks < 1 ||
+        p.split_blocks > pa::kMaxSplitBlocks)
+        return -1;
+    const int nsplit = (nblk - skip + p.split_blocks - 1) / p.split_blocks;
+    return nsplit > p.max_splits ? -1 : nsplit;
+}
+
+// Shared-prefix blocks of row r under the plan's groups (0 outside every group).
+__device__ inline int prefix_skip_of(const DecodeParams& p, int r)
+{
+    int skip = 0;
+    for (int gi = 0; gi < p.num_prefix_groups; ++gi)
+        if (r >= p.prefix_first[gi] && r < p.prefix_first[gi] + p.prefix_count[gi])
+            skip = p.prefix_blocks[gi];
+    return skip;
+}
+
+// Final outputs of rows rows[0 .. nrows - 1] for KV head kvh: each row's decode partials
+// (as many as decode_splits_of gives), then its nprefix shared-prefix partials, merged by
+// the log-sum-exp rule in that fixed order, whichever workgroup arrived last.  Each thread
+// owns one (head, dim) value of every row.  kChunk rows are merged together, eight
+// partials of each loaded before any is used, so a workgroup finishing several rows pays
+// about one row's load latency per kChunk rows.  All partials were written with agent-scope stores that completed
+// before their writer counted in, so agent-scope loads see them.
+static_assert(kGroup * kHeadDim == 64 * kDecodeWaves, "one output value per thread");
+template <int kChunk>
+__device__ inline void merge_rows_results(const DecodeParams& p, const int* rows, int nrows, int kvh, int nprefix)
+{
+    const int head0 = kvh * kGroup;
+    const int idx = threadIdx.x, h = idx / kHeadDim, d = idx & (kHeadDim - 1);
+    const float nan = __builtin_nanf("");
+    for (int c0 = 0; c0 < nrows; c0 += kChunk) {
+        int rr[kChunk], ns[kChunk], tot[kChunk];
+        int most = 0;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const bool valid = c0 + j < nrows;
+            rr[j] = rows[valid ? c0 + j : c0];
+            ns[j] = valid ? max(0, decode_splits_of(p, rr[j], prefix_skip_of(p, rr[j]))) : 0;
+            tot[j] = valid ? ns[j] + nprefix : 0;
+            most = max(most, tot[j]);
+        }
+        LseMerge mg[kChunk];
+        for (int s0 = 0; s0 < most; s0 += 8) {
+            float ls[kChunk][8], os[kChunk][8];
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int sidx = min(s0 + u, max(tot[j], 1) - 1);
+                    const int64_t pi = sidx < ns[j]
+                                           ? ((int64_t)rr[j] * p.max_splits + sidx) * p.num_q_heads + head0 + h
+                                           : ((int64_t)rr[j] * p.prefix_splits + (sidx - ns[j])) * p.num_q_heads +
+                                                 head0 + h;
+                    const float* lsrc = sidx < ns[j] ? p.part_lse : p.px_part_lse;
+                    const float* osrc = sidx < ns[j] ? p.part_o : p.px_part_o;
+                    ls[j][u] = tot[j] > 0 ? load_agent(lsrc + pi) : 0.f;
+                    os[j][u] = tot[j] > 0 ? load_agent(osrc + pi * kHeadDim + d) : 0.f;
+                }
+#pragma unroll
+            for (int j = 0; j < kChunk; ++j)
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < tot[j])
+                        mg[j].add(ls[j][u], os[j][u]);
+        }
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            if (c0 + j >= nrows)
+                continue;
+            const int q_row = p.qo_indptr[rr[j]];
+            p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + idx] =
+                __builtin_bit_cast(uint16_t, (__bf16)(mg[j].nan ? nan : mg[j].o / mg[j].wsum));
+            if (d == 0)
+                p.lse[(int64_t)q_row * p.num_q_heads + head0 + h] =
+                    mg[j].nan ? nan : (mg[j].lmax + fast_log2(mg[j].wsum)) * kLn2;
+        }
+    }
+}
+
 // Grid: max_splits * num_reqs * num_kv_heads workgroups of kDecodeWaves wavefronts, KV
 // head fastest: workgroups go round-robin to the eight XCDs, so with eight KV heads each
 // XCD serves one KV head of every row and reads that head's shared-prefix blocks from
@@ -432,7 +522,7 @@ __device__ inline void wave_lds_sync()
 // off the accumulators at the end.  Q is widened to binary16, which holds every bf16
 // value of magnitude in [2^-14, 65504] exactly.
 template <bool kQ8>
-__global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParams p)
+__device__ __attribute__((always_inline)) inline void decode_body(const DecodeParams& p, int bid)
 {
     constexpr int kDepth = kQ8 ? kDecodeDepthQ8 : kDecodeDepth;
     using Stage = std::conditional_t<kQ8, KvStageQ8, KvStage>;
@@ -443,8 +533,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int kvh = blockIdx.x % p.num_kv_heads;
-    const int rest = blockIdx.x / p.num_kv_heads;
+    const int kvh = bid % p.num_kv_heads;
+    const int rest = bid / p.num_kv_heads;
     const int r = rest % p.num_reqs;
     const int split = rest / p.num_reqs;
     const int head0 = kvh * kGroup;
@@ -455,10 +545,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     // the row's lengths arrive, so the start-up waits for one memory round trip less.  The
     // early requests are bounded by the table row and the pool; entries past the row's
     // last block are never used.
-    int skip = 0;                                     // blocks a shared-prefix group reads for this row
-    for (int gi = 0; gi < p.num_prefix_groups; ++gi)
-        if (r >= p.prefix_first[gi] && r < p.prefix_first[gi] + p.prefix_count[gi])
-            skip = p.prefix_blocks[gi];
+    const int skip = prefix_skip_of(p, r);            // blocks a shared-prefix group reads for this row
     const int g0 = skip + split * p.split_blocks;
     const int bidx = g0 + wave + kDecodeWaves * lane;
     int my_blk = 0;
@@ -492,9 +579,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
     if (q_end - q_row != 1)
         return;                                       // not a decode row
     const int nblk = (kvlen + kBlock - 1) / kBlock;
-    const int nsplit = (nblk - skip + p.split_blocks - 1) / p.split_blocks;
-    if (kvlen < 1 || nblk > p.max_blocks || nblk <= skip || nsplit > p.max_splits ||
-        p.split_blocks > pa::kMaxSplitBlocks) {       // lengths disagree with the plan
+    const int nsplit = decode_splits_of(p, r, skip);
+    if (nsplit < 0) {                                 // lengths disagree with the plan
         if (split == 0)
             for (int i = tid; i < kGroup * kHeadDim; i += 64 * kDecodeWaves) {
                 p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + i] = 0x7FC0;
@@ -776,57 +862,38 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParam
 
     // Partials are written with agent-scope stores (coherent across the XCDs' separate L2
     // caches) and every thread waits until its stores have completed before the
-    // workgroup counts itself in; the last split reads them with agent-scope loads.  This
-    // needs no L2 writeback or invalidation, which a device fence would do for every split.
-    const int64_t split_stride = p.num_q_heads;                        // partial index step per split
-    const int64_t base = (int64_t)r * p.max_splits * p.num_q_heads + head0;
-    if (nsplit > 1) {
-        const int64_t mine = base + (int64_t)split * split_stride;
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-            const int idx = tid + k * 64 * kDecodeWaves;
-            store_agent(p.part_o + mine * kHeadDim + idx, res[k]);
-            if ((idx & (kHeadDim - 1)) == 0)
-                store_agent(p.part_lse + mine + idx / kHeadDim, res_lse[k]);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        uint32_t* counter = p.counters + (int64_t)r * p.num_kv_heads + kvh;
-        if (tid == 0) {
-            const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool last = done == (uint32_t)(nsplit - 1);
-            if (last)
-                __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
-            last_lds = last;
-        }
-        __syncthreads();
-        if (!last_lds)
-            return;
-    }
-
-    // Merge the decode splits (this workgroup's own result when it is the only one) and,
-    // for a row of a shared-prefix group, the partials over its shared blocks, which an
-    // earlier launch wrote: plain loads see them.
-    const int64_t pbase = (int64_t)r * p.prefix_splits * p.num_q_heads + head0;
-    const int nprefix = prefix ? p.prefix_splits : 0;
+    // workgroup counts itself in; the last arrival reads them with agent-scope loads.
+    // This needs no L2 writeback or invalidation, which a device fence would do for every
+    // split.  A row of a shared-prefix group also waits for its group's prefix splits,
+    // which count into the same counter from the same launch.
+    const int64_t mine = (int64_t)r * p.max_splits * p.num_q_heads + head0 + (int64_t)split * p.num_q_heads;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int idx = tid + k * 64 * kDecodeWaves;
-        const int h = idx / kHeadDim, d = idx & (kHeadDim - 1);
-        LseMerge mg;
-        if (nsplit == 1)
-            mg.add(res_lse[k], res[k]);
-        else
-            merge_partials(
-                mg, nsplit, [&](int s) { return load_agent(p.part_lse + base + s * split_stride + h); },
-                [&](int s) { return load_agent(p.part_o + (base + s * split_stride + h) * kHeadDim + d); });
-        merge_partials(
-            mg, nprefix, [&](int s) { return p.px_part_lse[pbase + s * p.num_q_heads + h]; },
-            [&](int s) { return p.px_part_o[(pbase + s * p.num_q_heads + h) * kHeadDim + d]; });
-        p.out[out_base + idx] = __builtin_bit_cast(uint16_t, (__bf16)(mg.nan ? nan : mg.o / mg.wsum));
-        if (d == 0)
-            p.lse[(int64_t)q_row * p.num_q_heads + head0 + h] = mg.nan ? nan : (mg.lmax + fast_log2(mg.wsum)) * kLn2;
+        store_agent(p.part_o + mine * kHeadDim + idx, res[k]);
+        if ((idx & (kHeadDim - 1)) == 0)
+            store_agent(p.part_lse + mine + idx / kHeadDim, res_lse[k]);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int nprefix = prefix ? p.prefix_splits : 0;
+    uint32_t* counter = p.counters + (int64_t)r * p.num_kv_heads + kvh;
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = done == (uint32_t)(nsplit + nprefix - 1);
+        if (last)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+        last_lds = last;
+    }
+    __syncthreads();
+    if (last_lds)
+        merge_rows_results<1>(p, &r, 1, kvh, nprefix);
+}
+
+template <bool kQ8>
+__global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParams p)
+{
+    decode_body<kQ8>(p, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------ prefill
@@ -1087,7 +1154,8 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* v
 // exactly S^T values it holds; the V^T operand is read with the same key order by two
 // transposed LDS reads, and a contraction does not care how its index is permuted.
 template <bool kCascade>
-__global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
+__device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
+                                                                   int bid)
 {
     __shared__ __attribute__((aligned(1024))) u32x4 k_tile0[kTileChunks];
     __shared__ __attribute__((aligned(1024))) u32x4 v_tile0[kTileChunks];
@@ -1100,8 +1168,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int rg = wave & 3, kh = wave >> 2;
-    const int kvh = blockIdx.x % p.num_kv_heads;
-    const int rest = blockIdx.x / p.num_kv_heads;
+    const int kvh = bid % p.num_kv_heads;
+    const int rest = bid / p.num_kv_heads;
     const int split = rest % p.splits;
     const int tile = rest / p.splits;
     const int head0 = kvh * kGroup;
@@ -1349,7 +1417,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
 
     if constexpr (kCascade) {
         // this split's normalised partial and log2-sum-exp per (request, query head), in
-        // the decode kernel's partial layout; a later launch merges them
+        // the decode kernel's partial layout, with agent-scope stores: the decode
+        // workgroups of the same launch merge them
         if (kh == 0) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
@@ -1361,11 +1430,40 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
                 float* dst = p.px_part_o + pi * kHeadDim + 4 * kslice;
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
-                    *reinterpret_cast<f32x4*>(dst + 16 * db) = oacc[rb][db];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        store_agent(dst + 16 * db + e, oacc[rb][db][e]);
                 if (kslice == 0)
-                    p.px_part_lse[pi] = lse2[rb];
+                    store_agent(p.px_part_lse + pi, lse2[rb]);
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // count in for every request of the group, one lane per request so that the
+        // atomics travel together; the last arrival of a (request, KV head) -- decode split
+        // or prefix split -- merges its result
+        if (tid == 0)
+            last_lds = 0;
+        __syncthreads();
+        if (tid < grp_count) {
+            const int rr = grp_first + tid;
+            const int nsplit = decode_splits_of(dp, rr, prefix_skip_of(dp, rr));
+            if (nsplit >= 0) {                  // else the decode side does not count this row either
+                uint32_t* counter = dp.counters + (int64_t)rr * dp.num_kv_heads + kvh;
+                const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (done == (uint32_t)(nsplit + p.splits - 1)) {
+                    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    atomicOr(reinterpret_cast<unsigned int*>(&last_lds), 1u << tid);
+                }
+            }
+        }
+        __syncthreads();
+        int rows[PA_MAX_PREFIX_GROUP_REQS];
+        int nrows = 0;
+        for (uint32_t mine = (uint32_t)last_lds; mine; mine &= mine - 1)
+            rows[nrows++] = grp_first + __builtin_ctz(mine);
+        if (nrows > 0)
+            merge_rows_results<4>(dp, rows, nrows, kvh, p.splits);
         return;
     }
 
@@ -1477,6 +1575,27 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     }
     write_out(oacc, lse2);
 }
+__global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
+{
+    prefill_body<false>(p, DecodeParams{}, blockIdx.x);
+}
+
+static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
+
+// A batch with shared-prefix groups in one launch: workgroups 0 .. num_prefix_wgs - 1 read
+// each group's shared blocks once per KV head (the prefill body in its shared-prefix
+// form), the rest are the decode workgroups.  The prefix workgroups come first in the
+// grid and wait for nothing; a (row, KV head) is finished by whichever of its decode
+// splits and prefix splits arrives last, so no workgroup ever waits for another.
+__global__ __launch_bounds__(64 * kPfWaves) void pa_cascade_decode(PrefillParams pp, DecodeParams dp,
+                                                                 int32_t num_prefix_wgs)
+{
+    if ((int32_t)blockIdx.x < num_prefix_wgs)
+        prefill_body<true>(pp, dp, blockIdx.x);
+    else
+        decode_body<false>(dp, blockIdx.x - num_prefix_wgs);
+}
+
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -1591,6 +1710,13 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
     if (ngroups < 0 || ngroups > PA_MAX_PREFIX_GROUPS ||
         (ngroups > 0 && (plan->prefix_splits < 1 || plan->prefix_splits > pa::kMaxPrefillSplits)))
         return PA_ERR_SHAPE;
+    if (ngroups > 0 && (plan->num_decode_rows < 1 || plan->max_splits < 1))
+        return PA_ERR_SHAPE;
+    for (int i = 0; i < ngroups; ++i)
+        for (int j = 0; j < i; ++j)          // a row belongs to at most one group
+            if (plan->prefix_first_req[i] < plan->prefix_first_req[j] + plan->prefix_num_reqs[j] &&
+                plan->prefix_first_req[j] < plan->prefix_first_req[i] + plan->prefix_num_reqs[i])
+                return PA_ERR_SHAPE;
     for (int i = 0; i < ngroups; ++i)
         if (plan->prefix_first_req[i] < 0 || plan->prefix_num_reqs[i] < 1 ||
             plan->prefix_num_reqs[i] > PA_MAX_PREFIX_GROUP_REQS ||
@@ -1654,23 +1780,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads * plan->prefill_splits;
         if (grid > INT32_MAX)
             return PA_ERR_SHAPE;
-        hipLaunchKernelGGL(pa_prefill_tile<false>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
-        if (hipGetLastError() != hipSuccess)
-            return PA_ERR_HIP;
-    }
-    if (ngroups > 0) {
-        // each group's shared blocks, once per KV head, for all of its query rows
-        PrefillParams pp = prefill_params();
-        pp.splits = plan->prefix_splits;
-        for (int i = 0; i < ngroups; ++i) {
-            pp.group_first[i] = plan->prefix_first_req[i];
-            pp.group_count[i] = plan->prefix_num_reqs[i];
-            pp.group_blocks[i] = plan->prefix_blocks[i];
-        }
-        pp.px_part_o = reinterpret_cast<float*>(wsp + ws.px_part_o);
-        pp.px_part_lse = reinterpret_cast<float*>(wsp + ws.px_part_lse);
-        const int64_t grid = (int64_t)ngroups * g->num_kv_heads * plan->prefix_splits;
-        hipLaunchKernelGGL(pa_prefill_tile<true>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        hipLaunchKernelGGL(pa_prefill_tile, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
@@ -1684,10 +1794,10 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         dp.kv_len = kv_len;
         dp.out = static_cast<uint16_t*>(out);
         dp.lse = lse;
-        const bool split = plan->max_splits > 1;
-        dp.counters = split ? reinterpret_cast<uint32_t*>(wsp + ws.counters) : nullptr;
-        dp.part_o = split ? reinterpret_cast<float*>(wsp + ws.part_o) : nullptr;
-        dp.part_lse = split ? reinterpret_cast<float*>(wsp + ws.part_lse) : nullptr;
+        const bool partials = plan->max_splits > 1 || ngroups > 0;
+        dp.counters = partials ? reinterpret_cast<uint32_t*>(wsp + ws.counters) : nullptr;
+        dp.part_o = partials ? reinterpret_cast<float*>(wsp + ws.part_o) : nullptr;
+        dp.part_lse = partials ? reinterpret_cast<float*>(wsp + ws.part_lse) : nullptr;
         dp.max_blocks = max_blocks_per_req;
         dp.num_reqs = plan->num_reqs;
         dp.num_q_heads = g->num_q_heads;
@@ -1703,15 +1813,34 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             dp.prefix_count[i] = i < ngroups ? plan->prefix_num_reqs[i] : 0;
             dp.prefix_blocks[i] = i < ngroups ? plan->prefix_blocks[i] : 0;
         }
-        dp.px_part_o = ngroups > 0 ? reinterpret_cast<const float*>(wsp + ws.px_part_o) : nullptr;
-        dp.px_part_lse = ngroups > 0 ? reinterpret_cast<const float*>(wsp + ws.px_part_lse) : nullptr;
+        dp.px_part_o = ngroups > 0 ? reinterpret_cast<float*>(wsp + ws.px_part_o) : nullptr;
+        dp.px_part_lse = ngroups > 0 ? reinterpret_cast<float*>(wsp + ws.px_part_lse) : nullptr;
         const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * g->num_kv_heads;
-        if (grid > INT32_MAX)
-            return PA_ERR_SHAPE;
-        if (q8)
-            hipLaunchKernelGGL(pa_decode_split<true>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
-        else
-            hipLaunchKernelGGL(pa_decode_split<false>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
+        if (ngroups > 0) {
+            // each group's shared blocks, once per KV head, for all of its query rows, in
+            // the same launch as the decode workgroups
+            PrefillParams pp = prefill_params();
+            pp.splits = plan->prefix_splits;
+            for (int i = 0; i < ngroups; ++i) {
+                pp.group_first[i] = plan->prefix_first_req[i];
+                pp.group_count[i] = plan->prefix_num_reqs[i];
+                pp.group_blocks[i] = plan->prefix_blocks[i];
+            }
+            pp.px_part_o = reinterpret_cast<float*>(wsp + ws.px_part_o);
+            pp.px_part_lse = reinterpret_cast<float*>(wsp + ws.px_part_lse);
+            const int64_t nprefix = (int64_t)ngroups * g->num_kv_heads * plan->prefix_splits;
+            if (grid + nprefix > INT32_MAX)
+                return PA_ERR_SHAPE;
+            hipLaunchKernelGGL(pa_cascade_decode, dim3((uint32_t)(grid + nprefix)), dim3(64 * kPfWaves), 0, st, pp, dp,
+                               (int32_t)nprefix);
+        } else {
+            if (grid > INT32_MAX)
+                return PA_ERR_SHAPE;
+            if (q8)
+                hipLaunchKernelGGL(pa_decode_split<true>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
+            else
+                hipLaunchKernelGGL(pa_decode_split<false>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
+        }
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
