@@ -148,8 +148,11 @@ pa_status pa_plan(const pa_geometry* geometry, int32_t num_reqs, const int32_t* 
  * common prefix, referenced from every request's table (book section 8.3.2, shared
  * blocks with reference counts; Hugging Face continuous-batching page, prefix caching).
  * pa_attention_batch then reads each group's shared blocks once per KV head, for all
- * of the group's query rows together, and merges that partial result with each row's
- * private suffix by the log-sum-exp rule.  Only whole blocks that precede every row's
+ * of the group's query rows together, in the same launch as the decode rows, and
+ * merges that partial result with each row's private suffix by the log-sum-exp rule.
+ * The prefix key splits and the decode split length are chosen together for that
+ * launch.  Groups never overlap (pa_attention_batch returns PA_ERR_SHAPE for a plan
+ * whose groups share a row).  Only whole blocks that precede every row's
  * last block are shared, and a run needs at least min_shared_blocks of them (0 picks
  * 16).  block_tables_host: host int32 [num_reqs][max_blocks_per_req], the tables the
  * batch will use (a device table that differs gives wrong results).  Runs longer than
