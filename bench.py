@@ -450,7 +450,7 @@ def main(argv=None):
     # mixed continuous batch: tokens per second of a whole step
     wm = synthetic.config_mixed(poison=False)
     sm = Stepper(wm, args.copies)
-    sec_m = time_steps(sm, args.steps, args.warmup)
+    sec_m = float(np.median([time_steps(sm, args.steps, args.warmup) for _ in range(3)]))   # median of 3 runs
     t_m = event_time(sm, max(args.steps, 50))
     del sm
 
