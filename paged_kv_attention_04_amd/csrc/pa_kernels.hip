@@ -1525,53 +1525,82 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     if (!last_lds || kh != 0)
         return;
 
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        // All 32 values a lane holds belong to one row and share its log2-sum-exp, so the
-        // merge weights are found once per split: L = max_s l_s, c_s = 2^(l_s - L), then
-        // O = sum_s c_s O_s / sum_s c_s and LSE = L + log2 sum_s c_s.  The splits are taken
-        // in index order whichever finished last, so the bits do not depend on timing.
-        auto lse_of = [&](int sp) __attribute__((always_inline)) {
+    {
+        // Each row block's 32 values in a lane belong to one row and share its log2-sum-exp,
+        // so the merge weights are found once per split: L = max_s l_s, c_s = 2^(l_s - L),
+        // then O = sum_s c_s O_s / sum_s c_s and LSE = L + log2 sum_s c_s.  Both row blocks
+        // are merged together, the log2-sum-exps loaded eight splits at a time and each
+        // split's 64 values at once, so the merge costs about one memory round trip per
+        // split.  The splits are taken in index order whichever finished last, so the bits
+        // do not depend on timing.
+        auto lse_of = [&](int sp, int rb) __attribute__((always_inline)) {
             return sp == split ? lse2[rb] : load_agent(part_lse_at(sp) + rb * 64 + lane);
         };
-        float L = -INFINITY;
+        float L[2] = {-INFINITY, -INFINITY};
         bool any_nan = false;
-        for (int sp = 0; sp < p.splits; ++sp) {
-            const float ls = lse_of(sp);
-            any_nan |= ls != ls;
-            L = fmaxf(L, ls);
-        }
-        float wsum = 0.f;
-        f32x4 o[8];
+        for (int s0 = 0; s0 < p.splits; s0 += 8) {
+            float ls[8][2];
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-            o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    ls[u][rb] = lse_of(min(s0 + u, p.splits - 1), rb);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    if (s0 + u < p.splits) {
+                        any_nan |= ls[u][rb] != ls[u][rb];
+                        L[rb] = fmaxf(L[rb], ls[u][rb]);
+                    }
+        }
+        float wsum[2] = {0.f, 0.f};
+        f32x4 o[2][8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int sp = 0; sp < p.splits; ++sp) {
-            const float ls = lse_of(sp);
-            const float c = (ls > -INFINITY) ? fast_exp2(ls - L) : 0.f;
-            wsum += c;
+            float c[2];
+            f32x4 os[2][8];
             if (sp == split) {
 #pragma unroll
-                for (int db = 0; db < 8; ++db)
-                    o[db] += c * oacc[rb][db];
+                for (int rb = 0; rb < 2; ++rb) {
+                    c[rb] = lse2[rb];
+#pragma unroll
+                    for (int db = 0; db < 8; ++db)
+                        os[rb][db] = oacc[rb][db];
+                }
             } else {
                 const float* po = part_o_at(sp);
-                f32x4 os[8];
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    c[rb] = load_agent(part_lse_at(sp) + rb * 64 + lane);
+#pragma unroll
+                    for (int db = 0; db < 8; ++db)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            os[rb][db][e] = load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const float w = (c[rb] > -INFINITY) ? fast_exp2(c[rb] - L[rb]) : 0.f;
+                wsum[rb] += w;
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        os[db][e] = load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
-#pragma unroll
-                for (int db = 0; db < 8; ++db)
-                    o[db] += c * os[db];
+                    o[rb][db] += w * os[rb][db];
             }
         }
-        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
-            oacc[rb][db] = o[db] * inv;
-        lse2[rb] = any_nan ? nan : (wsum > 0.f ? L + fast_log2(wsum) : -INFINITY);
+        for (int rb = 0; rb < 2; ++rb) {
+            const float inv = wsum[rb] > 0.f ? 1.f / wsum[rb] : 0.f;
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                oacc[rb][db] = o[rb][db] * inv;
+            lse2[rb] = any_nan ? nan : (wsum[rb] > 0.f ? L[rb] + fast_log2(wsum[rb]) : -INFINITY);
+        }
     }
     write_out(oacc, lse2);
 }
