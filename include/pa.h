@@ -76,7 +76,8 @@ typedef enum pa_status {
     PA_ERR_RANGE = -3,       /* a block id or slot outside the pool, a repeated slot */
     PA_ERR_WORKSPACE = -4,   /* workspace too small for the plan                   */
     PA_ERR_UNSUPPORTED = -5, /* geometry the kernels are not built for             */
-    PA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed         */
+    PA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed         */
+    PA_ERR_NO_BLOCKS = -7    /* the block allocator has too few free blocks         */
 } pa_status;
 
 /* One layer's attention geometry and pool size. */
@@ -277,6 +278,65 @@ pa_status pa_attention_batch_q8(const pa_geometry* geometry, const pa_plan_t* pl
 /* pa_copy_blocks for a q8_0 pool (all of a block's tiles); same rules and errors. */
 pa_status pa_copy_blocks_q8(const pa_geometry* geometry, void* kv_pool_q8, const int32_t* src_blocks,
                             const int32_t* dst_blocks, int32_t n, void* stream);
+
+/*
+ * Reference-counted block allocator with stream-deferred release (host side; book
+ * section 8.3.2 and figs. 8-14 / 8-15): a physical block carries one reference per block
+ * table that points at it, so a shared prefix is a set of blocks with counts above one;
+ * a request about to write into a shared block first gets a private copy; and a block
+ * returns to the free pool only when its last reference is gone and the device has
+ * finished the work that reads it.  The allocator hands out block ids of one pool (the
+ * same ids serve every layer's pools); the caller fills block tables with them.  It owns
+ * no device memory; an allocator is not thread-safe (one per host thread, or a lock).
+ */
+typedef struct pa_block_allocator pa_block_allocator;
+
+/* A pool of num_blocks free blocks.  Errors: PA_ERR_NULL, PA_ERR_SHAPE (num_blocks < 1). */
+pa_status pa_allocator_create(int32_t num_blocks, pa_block_allocator** allocator);
+
+/* Frees the allocator (pending releases are dropped).  NULL is ignored. */
+void pa_allocator_destroy(pa_block_allocator* allocator);
+
+/*
+ * n free blocks, each with one reference, into blocks_out (host int32 [n]).  Deferred
+ * releases whose stream work has completed are reclaimed first.  All or nothing:
+ * PA_ERR_NO_BLOCKS when fewer than n are free.
+ */
+pa_status pa_allocator_alloc(pa_block_allocator* allocator, int32_t n, int32_t* blocks_out);
+
+/* One more reference to each listed block (a table that starts sharing them).
+ * PA_ERR_RANGE (nothing changed) if a block is not allocated. */
+pa_status pa_allocator_retain(pa_block_allocator* allocator, const int32_t* blocks, int32_t n);
+
+/*
+ * Drops one reference per list entry (a block may be listed more than once).  A block
+ * whose count reaches zero becomes free: at once when deferred is 0 (the caller knows
+ * no queued device work reads it), else once the work queued on `stream` at this call
+ * has completed (an event recorded now; not allowed while the stream is being captured
+ * into a graph: PA_ERR_UNSUPPORTED).  PA_ERR_RANGE (nothing changed) if a block is not
+ * allocated or would drop below zero; PA_ERR_HIP if the event cannot be recorded.
+ */
+pa_status pa_allocator_release(pa_block_allocator* allocator, const int32_t* blocks, int32_t n, void* stream,
+                               int32_t deferred);
+
+/*
+ * Copy-on-write before a request writes into `block`: if the block has one reference
+ * it is returned as is (write in place); otherwise a fresh block is allocated and
+ * returned, and the shared block loses this request's reference.  The caller then
+ * copies the data (pa_copy_blocks or pa_copy_blocks_q8, on the stream of the write) and
+ * points its table at the returned block.  PA_ERR_RANGE, PA_ERR_NO_BLOCKS.
+ */
+pa_status pa_allocator_cow(pa_block_allocator* allocator, int32_t block, int32_t* block_out);
+
+/* Current reference count of a block (0 when free or awaiting a deferred release). */
+pa_status pa_allocator_refcount(const pa_block_allocator* allocator, int32_t block, int32_t* count);
+
+/* Free blocks after reclaiming completed deferred releases, and blocks still waiting
+ * (either pointer may be NULL). */
+pa_status pa_allocator_num_free(pa_block_allocator* allocator, int32_t* free_blocks, int32_t* pending_blocks);
+
+/* Waits for every deferred release's stream work, then reclaims.  PA_ERR_HIP on failure. */
+pa_status pa_allocator_sync(pa_block_allocator* allocator);
 
 /* Compute-unit count of a HIP device (for pa_plan).  PA_ERR_HIP on failure. */
 pa_status pa_query_num_cus(int32_t device, int32_t* num_cus);

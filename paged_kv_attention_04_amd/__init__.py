@@ -25,7 +25,7 @@ HEAD_DIM = 128
 BLOCK_SIZE = 16
 
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_RANGE", -4: "PA_ERR_WORKSPACE",
-          -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_HIP"}
+          -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_HIP", -7: "PA_ERR_NO_BLOCKS"}
 
 
 class PaError(RuntimeError):
@@ -87,9 +87,21 @@ def lib():
     L.pa_copy_blocks_q8.argtypes = [G, P, P, P, i32, P]
     L.pa_validate_copy.argtypes = [G, P, P, i32, P]
     L.pa_query_num_cus.argtypes = [i32, P]
+    L.pa_allocator_create.argtypes = [i32, P]
+    L.pa_allocator_destroy.argtypes = [P]
+    L.pa_allocator_destroy.restype = None
+    L.pa_allocator_alloc.argtypes = [P, i32, P]
+    L.pa_allocator_retain.argtypes = [P, P, i32]
+    L.pa_allocator_release.argtypes = [P, P, i32, P, i32]
+    L.pa_allocator_cow.argtypes = [P, i32, P]
+    L.pa_allocator_refcount.argtypes = [P, i32, P]
+    L.pa_allocator_num_free.argtypes = [P, P, P]
+    L.pa_allocator_sync.argtypes = [P]
     for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
                "pa_validate_append", "pa_copy_blocks", "pa_validate_copy", "pa_append_kv_q8",
-               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_query_num_cus"):
+               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_query_num_cus", "pa_allocator_create",
+               "pa_allocator_alloc", "pa_allocator_retain", "pa_allocator_release", "pa_allocator_cow",
+               "pa_allocator_refcount", "pa_allocator_num_free", "pa_allocator_sync"):
         getattr(L, fn).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -294,6 +306,69 @@ def pa_validate_copy(geometry: Geometry, src_blocks, dst_blocks):
     bad = ctypes.c_int32(-1)
     rc = lib().pa_validate_copy(ctypes.byref(geometry), _np_ptr(s), _np_ptr(d), int(s.size), ctypes.byref(bad))
     return rc, int(bad.value)
+
+
+class BlockAllocator:
+    """Reference-counted block ids of one pool, with stream-deferred release (the C
+    allocator: host bookkeeping, no device memory)."""
+
+    def __init__(self, num_blocks: int):
+        h = ctypes.c_void_p()
+        _check("pa_allocator_create", lib().pa_allocator_create(int(num_blocks), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().pa_allocator_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _ids(blocks):
+        import numpy as np
+        return np.ascontiguousarray(np.atleast_1d(np.asarray(blocks, dtype=np.int32)))
+
+    def alloc(self, n: int):
+        import numpy as np
+        out = np.empty(int(n), np.int32)
+        _check("pa_allocator_alloc", lib().pa_allocator_alloc(self._h, int(n), _np_ptr(out)))
+        return out
+
+    def retain(self, blocks):
+        b = self._ids(blocks)
+        _check("pa_allocator_retain", lib().pa_allocator_retain(self._h, _np_ptr(b), int(b.size)))
+
+    def release(self, blocks, stream=None, deferred: bool = True):
+        """Drop one reference per entry; freed blocks wait for the work queued on `stream`
+        (the current stream when None) unless deferred is False."""
+        b = self._ids(blocks)
+        s = _stream_handle(stream) if deferred else None
+        _check("pa_allocator_release", lib().pa_allocator_release(self._h, _np_ptr(b), int(b.size), s,
+                                                                  1 if deferred else 0))
+
+    def cow(self, block: int) -> int:
+        out = ctypes.c_int32(-1)
+        _check("pa_allocator_cow", lib().pa_allocator_cow(self._h, int(block), ctypes.byref(out)))
+        return int(out.value)
+
+    def refcount(self, block: int) -> int:
+        out = ctypes.c_int32(0)
+        _check("pa_allocator_refcount", lib().pa_allocator_refcount(self._h, int(block), ctypes.byref(out)))
+        return int(out.value)
+
+    def num_free(self):
+        """(free blocks, blocks still waiting for their stream work)."""
+        f, w = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check("pa_allocator_num_free", lib().pa_allocator_num_free(self._h, ctypes.byref(f), ctypes.byref(w)))
+        return int(f.value), int(w.value)
+
+    def sync(self):
+        _check("pa_allocator_sync", lib().pa_allocator_sync(self._h))
 
 
 def workspace_for(plan: Plan, device="cuda"):

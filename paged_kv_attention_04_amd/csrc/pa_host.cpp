@@ -424,6 +424,7 @@ extern "C" const char* pa_status_string(pa_status s)
     case PA_ERR_WORKSPACE: return "workspace smaller than the plan needs";
     case PA_ERR_UNSUPPORTED: return "unsupported geometry (need head_dim 128, block_size 16, 4 query heads per KV head)";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     }
     return "unknown status";
 }

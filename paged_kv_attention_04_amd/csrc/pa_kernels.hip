@@ -436,12 +436,13 @@ __device__ inline int prefix_skip_of(const DecodeParams& p, int r)
 // Final outputs of rows rows[0 .. nrows - 1] for KV head kvh: each row's decode partials
 // (as many as decode_splits_of gives), then its nprefix shared-prefix partials, merged by
 // the log-sum-exp rule in that fixed order, whichever workgroup arrived last.  Each thread
-// owns one (head, dim) value of every row.  kChunk rows are merged together, eight
+// owns one (head, dim) value of every row.  kChunk rows are merged together, kBatch
 // partials of each loaded before any is used, so a workgroup finishing several rows pays
-// about one row's load latency per kChunk rows.  All partials were written with agent-scope stores that completed
+// about one row's load latency per kChunk rows (and one row with up to kBatch partials,
+// one round trip).  All partials were written with agent-scope stores that completed
 // before their writer counted in, so agent-scope loads see them.
 static_assert(kGroup * kHeadDim == 64 * kDecodeWaves, "one output value per thread");
-template <int kChunk>
+template <int kChunk, int kBatch>
 __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows, int nrows, int kvh, int nprefix)
 {
     const int head0 = kvh * kGroup;
@@ -459,12 +460,12 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
             most = max(most, tot[j]);
         }
         LseMerge mg[kChunk];
-        for (int s0 = 0; s0 < most; s0 += 8) {
-            float ls[kChunk][8], os[kChunk][8];
+        for (int s0 = 0; s0 < most; s0 += kBatch) {
+            float ls[kChunk][kBatch], os[kChunk][kBatch];
 #pragma unroll
             for (int j = 0; j < kChunk; ++j)
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < kBatch; ++u) {
                     const int sidx = min(s0 + u, max(tot[j], 1) - 1);
                     const int64_t pi = sidx < ns[j]
                                            ? ((int64_t)rr[j] * p.max_splits + sidx) * p.num_q_heads + head0 + h
@@ -478,7 +479,7 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
 #pragma unroll
             for (int j = 0; j < kChunk; ++j)
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                for (int u = 0; u < kBatch; ++u)
                     if (s0 + u < tot[j])
                         mg[j].add(ls[j][u], os[j][u]);
         }
@@ -887,7 +888,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     }
     __syncthreads();
     if (last_lds)
-        merge_rows_results<1>(p, &r, 1, kvh, nprefix);
+        merge_rows_results<1, 32>(p, &r, 1, kvh, nprefix);
 }
 
 template <bool kQ8>
@@ -1463,7 +1464,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         for (uint32_t mine = (uint32_t)last_lds; mine; mine &= mine - 1)
             rows[nrows++] = grp_first + __builtin_ctz(mine);
         if (nrows > 0)
-            merge_rows_results<4>(dp, rows, nrows, kvh, p.splits);
+            merge_rows_results<4, 8>(dp, rows, nrows, kvh, p.splits);
         return;
     }
 

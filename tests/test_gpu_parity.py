@@ -430,3 +430,81 @@ def test_split_results_are_bitwise_reproducible(prefill_splits, split_blocks):
     for _ in range(5):
         again = pa.run_workload(wl, split_blocks=split_blocks, prefill_splits=prefill_splits)
         assert np.array_equal(again[2], first[2]) and np.array_equal(again[3], first[3])
+
+
+# ------------------------------------------------------------------ block allocator
+
+def test_deferred_release_waits_for_the_stream():
+    """A block whose last reference goes while queued device work may still read it
+    returns to the free pool only after that work: here a bounded sleep kernel."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    a = pa.BlockAllocator(16)
+    b = a.alloc(4)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)                    # a few tens of ms of queued work
+    a.release(b, stream=torch.cuda.current_stream())
+    free, waiting = a.num_free()
+    assert (free, waiting) == (12, 4)
+    with pytest.raises(pa.PaError):
+        a.alloc(13)                                   # the four are not reusable yet
+    torch.cuda.synchronize()
+    assert a.num_free() == (16, 0)
+    c = a.alloc(2)
+    torch.cuda._sleep(200_000_000)
+    a.release(c, stream=torch.cuda.current_stream())
+    a.sync()                                          # waits for that work
+    assert a.num_free() == (16, 0)
+
+
+def test_allocator_drives_fork_copy_on_write():
+    """The forked decode step with its copy-on-write decisions taken by the allocator:
+    every row holds a reference to the shared blocks; each writer but the last to ask
+    gets a fresh tail (the last one finds the tail unshared and writes in place).  The
+    pools and outputs equal the oracle's for the same tables."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    wl = _forked_workload(43, 6, 16 * 20 + 9)
+    nb = wl.num_blocks
+    alloc = pa.BlockAllocator(nb)
+    ids = alloc.alloc(nb)                             # take every block, give back the unused ones
+    used = sorted(set(wl.block_tables[wl.block_tables >= 0].ravel().tolist()))
+    alloc.release([x for x in ids if x not in used], deferred=False)
+    shared = wl.block_tables[0, :21]
+    for _ in range(wl.num_reqs - 1):
+        alloc.retain(shared)                          # every forked row references the prompt
+    bt = wl.block_tables.copy()
+    src, dst = [], []
+    for r in range(1, wl.num_reqs):                   # rows 1.. ask first; row 0 asks last
+        t = alloc.cow(int(bt[r, 20]))
+        if t != bt[r, 20]:
+            src.append(int(bt[r, 20]))
+            dst.append(t)
+            bt[r, 20] = t
+    assert alloc.cow(int(bt[0, 20])) == bt[0, 20]     # the last holder writes in place
+    assert all(alloc.refcount(int(x)) == wl.num_reqs for x in shared[:20])
+    src, dst = np.array(src, np.int32), np.array(dst, np.int32)
+    slots = np.array([synthetic.slot_of(bt[r], int(wl.kv_len[r]) - 1, 16) for r in range(wl.num_reqs)], np.int32)
+    g = _geometry(wl)
+    assert pa.pa_validate_copy(g, src, dst) == (0, -1) and pa.pa_validate_append(g, slots) == (0, -1)
+    okp, ovp = oracle.copy_blocks(wl.k_pool, wl.v_pool, src, dst, wl.num_kv_heads, 128, 16, nb)
+    okp, ovp = oracle.append(okp, ovp, wl.k_new, wl.v_new, slots, wl.num_kv_heads, 128, 16, nb)
+    ref = oracle.attention(wl.q, okp, ovp, bt, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads, 128, 16, nb,
+                           wl.scale)
+    dk, dv = pa.to_device(wl.k_pool), pa.to_device(wl.v_pool)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len)
+    out = torch.empty((wl.total_q, wl.num_q_heads, 128), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    pa.pa_copy_blocks(g, dk, dv, pa.to_device(src), pa.to_device(dst))
+    pa.pa_append_kv(g, dk, dv, pa.to_device(wl.k_new), pa.to_device(wl.v_new), pa.to_device(slots))
+    pa.pa_attention_batch(g, plan, pa.to_device(wl.q), dk, dv, pa.to_device(bt), pa.to_device(wl.qo_indptr),
+                          pa.to_device(wl.kv_len), out, lse, pa.workspace_for(plan))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy().view(np.uint16), okp)
+    assert np.array_equal(dv.cpu().numpy().view(np.uint16), ovp)
+    eo, el = _errors(out.cpu().numpy().view(np.uint16), lse.cpu().numpy(), ref)
+    assert eo <= TOL_O and el <= TOL_LSE
+    for r in range(wl.num_reqs):                      # every request ends
+        alloc.release(bt[r, :21], stream=torch.cuda.current_stream())
+    alloc.sync()
+    assert alloc.num_free() == (nb, 0)
