@@ -57,7 +57,11 @@
  * pa_validate_batch / pa_validate_append.  The kernels bound-check what they read
  * and write: a block id outside the pool or a row whose lengths disagree with the
  * plan is not read and that row's output is set to NaN; an out-of-range slot is
- * not written.  A failed launch maps to PA_ERR_HIP.
+ * not written.  A failed launch maps to PA_ERR_HIP.  With PA_VALIDATE=1 in the
+ * environment, pa_append_kv(_q8) and pa_attention_batch(_q8) also copy their index
+ * arrays to the host in stream order (waiting for the stream; PA_ERR_UNSUPPORTED under
+ * graph capture) and run the validators' checks first, returning their status with
+ * nothing launched.
  */
 #ifndef PA_H
 #define PA_H

@@ -22,7 +22,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <stdlib.h>
+
 #include <type_traits>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -1633,6 +1636,39 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // ------------------------------------------------------------------------------ C entry points
 
+// With PA_VALIDATE=1 in the environment the entry points also run the content checks of
+// pa_validate_batch / pa_validate_append before launching anything: a debugging mode in
+// which the index arrays are copied to the host in stream order (so the call waits for
+// the stream) and a failed check returns its status with nothing launched.
+static bool validate_requested()
+{
+    const char* v = getenv("PA_VALIDATE");
+    return v && v[0] == '1';
+}
+
+template <typename T>
+static pa_status copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t st)
+{
+    dst.resize(n);
+    if (n == 0)
+        return PA_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess)
+        return PA_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone)
+        return PA_ERR_UNSUPPORTED;             // the check cannot wait inside a graph capture
+    if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return PA_ERR_HIP;
+    return hipStreamSynchronize(st) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+static pa_status validate_slots(const pa_geometry* g, const int32_t* slot_mapping, int32_t n_tokens, void* stream)
+{
+    std::vector<int32_t> slots;
+    const pa_status st = copy_to_host(slots, slot_mapping, (size_t)n_tokens, as_stream(stream));
+    return st != PA_OK ? st : pa_validate_append(g, slots.data(), n_tokens, nullptr);
+}
+
 extern "C" pa_status pa_append_kv(const pa_geometry* g, void* k_pool, void* v_pool, const void* k_new,
                                   const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, void* stream)
 {
@@ -1646,6 +1682,11 @@ extern "C" pa_status pa_append_kv(const pa_geometry* g, void* k_pool, void* v_po
         return PA_OK;
     if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
         return PA_ERR_NULL;
+    if (validate_requested()) {
+        const pa_status st = validate_slots(g, slot_mapping, n_tokens, stream);
+        if (st != PA_OK)
+            return st;
+    }
     const int64_t threads = (int64_t)n_tokens * g->num_kv_heads * (kHeadDim * 2 / 16);
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > INT32_MAX)
@@ -1670,6 +1711,11 @@ extern "C" pa_status pa_append_kv_q8(const pa_geometry* g, void* kv_pool_q8, con
         return PA_OK;
     if (!kv_pool_q8 || !k_new || !v_new || !slot_mapping)
         return PA_ERR_NULL;
+    if (validate_requested()) {
+        const pa_status st = validate_slots(g, slot_mapping, n_tokens, stream);
+        if (st != PA_OK)
+            return st;
+    }
     const int64_t threads = (int64_t)n_tokens * g->num_kv_heads * (kHeadDim / pa::kQ8Group);
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > INT32_MAX)
@@ -1762,6 +1808,25 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         return PA_ERR_UNSUPPORTED;
     char* wsp = static_cast<char*>(workspace);
     hipStream_t st = as_stream(stream);
+    if (validate_requested()) {
+        const int32_t R = plan->num_reqs;
+        std::vector<int32_t> indptr, kvl, bt;
+        pa_status vs = copy_to_host(indptr, qo_indptr, (size_t)R + 1, st);
+        if (vs == PA_OK)
+            vs = copy_to_host(kvl, kv_len, (size_t)R, st);
+        if (vs == PA_OK)
+            vs = copy_to_host(bt, block_tables, (size_t)R * max_blocks_per_req, st);
+        if (vs != PA_OK)
+            return vs;
+        if (indptr[0] != 0 || indptr[R] != plan->total_q)
+            return PA_ERR_SHAPE;
+        std::vector<int32_t> qo(R);
+        for (int32_t r = 0; r < R; ++r)
+            qo[r] = indptr[r + 1] - indptr[r];
+        vs = pa_validate_batch(g, R, qo.data(), kvl.data(), bt.data(), max_blocks_per_req, nullptr);
+        if (vs != PA_OK)
+            return vs;
+    }
     const float scale_log2 = g->scale * kLog2e;
 
     auto prefill_params = [&]() {

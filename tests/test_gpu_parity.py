@@ -508,3 +508,41 @@ def test_allocator_drives_fork_copy_on_write():
         alloc.release(bt[r, :21], stream=torch.cuda.current_stream())
     alloc.sync()
     assert alloc.num_free() == (nb, 0)
+
+
+# ------------------------------------------------------------------ PA_VALIDATE=1
+
+def test_validate_mode_rejects_bad_content_before_launch(monkeypatch):
+    """With PA_VALIDATE=1 the entry points copy the index arrays to the host and run the
+    validators first: a table entry outside the pool, a repeated slot or lengths that
+    disagree return an error with nothing launched; a valid batch gives the same result
+    as without the checks."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    wl = synthetic.config_tiny(poison=False)
+    ref = pa.run_workload(wl, validate=False)
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    got = pa.run_workload(wl, validate=False)
+    assert all(np.array_equal(a, b) for a, b in zip(ref, got))
+    g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len)
+    kp, vp = pa.to_device(wl.k_pool), pa.to_device(wl.v_pool)
+    out = torch.zeros((wl.total_q, wl.num_q_heads, 128), dtype=torch.int16, device="cuda")
+    lse = torch.zeros((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    bad_bt = wl.block_tables.copy()
+    bad_bt[2, 1] = wl.num_blocks + 5
+    with pytest.raises(pa.PaError, match="RANGE"):
+        pa.pa_attention_batch(g, plan, pa.to_device(wl.q), kp, vp, pa.to_device(bad_bt), pa.to_device(wl.qo_indptr),
+                              pa.to_device(wl.kv_len), out, lse, pa.workspace_for(plan))
+    bad_kv = wl.kv_len.copy()
+    bad_kv[0] = 0                                      # kv_len < qo_len
+    with pytest.raises(pa.PaError, match="SHAPE"):
+        pa.pa_attention_batch(g, plan, pa.to_device(wl.q), kp, vp, pa.to_device(wl.block_tables),
+                              pa.to_device(wl.qo_indptr), pa.to_device(bad_kv), out, lse, pa.workspace_for(plan))
+    slots = wl.slot_mapping.copy()
+    slots[1] = slots[0]
+    before = kp.clone()
+    with pytest.raises(pa.PaError, match="RANGE"):
+        pa.pa_append_kv(g, kp, vp, pa.to_device(wl.k_new), pa.to_device(wl.v_new), pa.to_device(slots))
+    torch.cuda.synchronize()
+    assert torch.equal(kp, before) and not out.any()   # nothing was launched
