@@ -246,12 +246,17 @@ class LayerStack:
             self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus)
         return plan
 
-    def step(self, replan: bool = True):
-        """One model step: the plan once, then per layer the append and the attention."""
+    def step(self, replan: bool = True, fused: bool = False):
+        """One model step: the plan once, then per layer the append and the attention
+        (one launch per layer with `fused`: pa_decode_step, decode-only batches)."""
         pa = self.pa
         if replan:
             self.plan = self.make_plan()
         for kp, vp in self.pools:
+            if fused:
+                pa.pa_decode_step(self.g, self.plan, self.q, kp, vp, self.kn, self.vn, self.bt, self.qo_indptr,
+                                  self.kv, self.out, self.lse, self.ws)
+                continue
             pa.pa_append_kv(self.g, kp, vp, self.kn, self.vn, self.sm)
             pa.pa_attention_batch(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
                                   self.lse, self.ws)
@@ -295,15 +300,20 @@ def sweep36(steps: int = 20, warmup: int = 5) -> dict:
         with torch.cuda.graph(graph):
             stack.step(replan=False)
         tg = median_step_seconds(graph.replay, steps, warmup)
+        graph_f = torch.cuda.CUDAGraph()             # append fused into the attention launch
+        with torch.cuda.graph(graph_f):
+            stack.step(replan=False, fused=True)
+        tf = median_step_seconds(graph_f.replay, steps, warmup)
         unique = ab["step"] * SWEEP_LAYERS
         logical = (ab["kv_logical"] - ab["kv_unique"] + ab["step"]) * SWEEP_LAYERS
         res["decode"].append({
             "batch": batch, "context": "8192 (6144 shared)" if long_only else ("2048" if batch == 1 else "half 2048, half 8192 sharing 6144"),
             "step_ms": round(t * 1e3, 4), "graph_step_ms": round(tg * 1e3, 4),
+            "graph_fused_step_ms": round(tf * 1e3, 4),
             "unique_gb_per_step": round(unique / 1e9, 4), "unique_gbs": round(unique / tg / 1e9, 1),
             "logical_gbs": round(logical / tg / 1e9, 1), "frac_of_hbm_peak": round(unique / tg / 1e9 / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(batch / tg, 1), "prefix_groups": stack.plan.num_prefix_groups})
-        del stack, graph
+        del stack, graph, graph_f
         torch.cuda.empty_cache()
     # 2048-token prompt, four 512-token chunks, 36 layers each
     _, chunks = synthetic.prompt_chunks(seed=5, prompt_len=2048, chunk=512, num_blocks=256, poison=False)

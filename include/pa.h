@@ -204,6 +204,24 @@ pa_status pa_attention_batch(const pa_geometry* geometry, const pa_plan_t* plan,
                              void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step of a layer with the append fused into the attention launch: for a
+ * batch of decode rows only (qo_len = 1), row r's new K / V (k_new / v_new row
+ * qo_indptr[r], bf16 [total_q][num_kv_heads][head_dim]) is written to the slot of its
+ * position kv_len[r] - 1 -- block_tables[r][(kv_len[r] - 1) / block_size], offset
+ * (kv_len[r] - 1) % block_size -- and attention reads it from k_new / v_new directly.
+ * The result equals pa_append_kv (with those slots) followed by pa_attention_batch, in
+ * one launch: the per-layer append is the step's other kernel (book section 8.3.1; the
+ * Perplexity blog orders the per-layer append before attention).  Shared-prefix groups
+ * are supported; a row's last block must be its own (the planner never shares it).
+ * PA_ERR_UNSUPPORTED for a plan with rows of qo_len > 1; other arguments and errors as
+ * for pa_attention_batch (PA_VALIDATE=1 also checks that no two rows write one slot).
+ */
+pa_status pa_decode_step(const pa_geometry* geometry, const pa_plan_t* plan, const void* q, void* k_pool,
+                         void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
+                         int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Host-side content checks on host copies of a batch's arguments: 1 <= qo_len <=
  * kv_len, ceil(kv_len / block_size) <= max_blocks_per_req, and every table entry
  * a row reads names a block in [0, num_blocks).  Returns PA_OK, PA_ERR_NULL,

@@ -79,6 +79,7 @@ def lib():
     L.pa_plan_shared_prefix.argtypes = [G, P, P, P, i32, i32, i32, PL]
     L.pa_append_kv.argtypes = [G, P, P, P, P, P, i32, P]
     L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
+    L.pa_decode_step.argtypes = [G, PL, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_validate_batch.argtypes = [G, i32, P, P, P, i32, P]
     L.pa_validate_append.argtypes = [G, P, i32, P]
     L.pa_copy_blocks.argtypes = [G, P, P, P, P, i32, P]
@@ -99,7 +100,7 @@ def lib():
     L.pa_allocator_sync.argtypes = [P]
     for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
                "pa_validate_append", "pa_copy_blocks", "pa_validate_copy", "pa_append_kv_q8",
-               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_query_num_cus", "pa_allocator_create",
+               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
                "pa_allocator_alloc", "pa_allocator_retain", "pa_allocator_release", "pa_allocator_cow",
                "pa_allocator_refcount", "pa_allocator_num_free", "pa_allocator_sync"):
         getattr(L, fn).restype = ctypes.c_int
@@ -196,6 +197,21 @@ def pa_append_kv(geometry: Geometry, k_pool, v_pool, k_new, v_new, slot_mapping,
         ctypes.byref(geometry), _dev_ptr(k_pool, bf, "k_pool"), _dev_ptr(v_pool, bf, "v_pool"),
         _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"),
         _dev_ptr(slot_mapping, (torch.int32,), "slot_mapping"), n, _stream_handle(stream)))
+
+
+def pa_decode_step(geometry: Geometry, plan: Plan, q, k_pool, v_pool, k_new, v_new, block_tables, qo_indptr, kv_len,
+                   out, lse, workspace=None, stream=None) -> None:
+    """A decode-only batch: append each row's new K/V (at position kv_len - 1) and attend,
+    in one launch."""
+    import torch
+    bf, i32 = _bf16_types(), (torch.int32,)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_step", lib().pa_decode_step(
+        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(k_pool, bf, "k_pool"),
+        _dev_ptr(v_pool, bf, "v_pool"), _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"),
+        _dev_ptr(block_tables, i32, "block_tables"), int(block_tables.shape[1]), _dev_ptr(qo_indptr, i32, "qo_indptr"),
+        _dev_ptr(kv_len, i32, "kv_len"), _dev_ptr(out, bf, "out"), _dev_ptr(lse, (torch.float32,), "lse"),
+        _dev_ptr(workspace, name="workspace"), ws_bytes, _stream_handle(stream)))
 
 
 PA_Q8_TILE_BYTES = 16 * 128 + 16 * (128 // 32) * 2

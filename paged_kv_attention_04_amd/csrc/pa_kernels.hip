@@ -300,6 +300,10 @@ struct DecodeParams {
     int32_t prefix_blocks[PA_MAX_PREFIX_GROUPS];
     const float* px_part_o;
     const float* px_part_lse;
+    // fused append (decode steps): row r's new token, k_new / v_new row qo_indptr[r], is
+    // written to the slot of position kv_len - 1 and read from these rows directly
+    const uint16_t* k_new;
+    const uint16_t* v_new;
 };
 
 #ifndef PA_DECODE_DEPTH
@@ -525,7 +529,7 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
 // the softmax weight times the value's scale, and -1152 times the weights' sum is taken
 // off the accumulators at the end.  Q is widened to binary16, which holds every bf16
 // value of magnitude in [2^-14, 65504] exactly.
-template <bool kQ8>
+template <bool kQ8, bool kFused>
 __device__ __attribute__((always_inline)) inline void decode_body(const DecodeParams& p, int bid)
 {
     constexpr int kDepth = kQ8 ? kDecodeDepthQ8 : kDecodeDepth;
@@ -600,6 +604,27 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     bool bad = lane < nb && (my_blk < 0 || my_blk >= p.num_blocks);
     bad = __syncthreads_or(bad);                      // a block id outside the pool: its data is not used
 
+    // Fused append: the workgroup whose blocks include the new token's block writes the
+    // token's K / V row into the pool and uses the new values for that block directly
+    // (no other workgroup of the launch reads that block).
+    const int new_blk = (kvlen - 1) / kBlock, new_off = (kvlen - 1) % kBlock;
+    u32x4 kn0 = u32x4{0u, 0u, 0u, 0u}, kn1 = kn0, vn = kn0;
+    if constexpr (kFused) {
+        if (new_blk >= g0 && new_blk < g_end) {
+            const u32x4* kr = reinterpret_cast<const u32x4*>(p.k_new + ((int64_t)q_row * p.num_kv_heads + kvh) * kHeadDim);
+            const u32x4* vr = reinterpret_cast<const u32x4*>(p.v_new + ((int64_t)q_row * p.num_kv_heads + kvh) * kHeadDim);
+            kn0 = kr[c8];
+            kn1 = kr[c8 + 8];
+            vn = vr[c16];
+            const int phys = p.block_tables[(int64_t)r * p.max_blocks + new_blk];
+            if (tid < 16 && phys >= 0 && phys < p.num_blocks) {
+                const int64_t row = (((int64_t)phys * p.num_kv_heads + kvh) * kBlock + new_off) * (kHeadDim / 8);
+                reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool))[row + tid] = kr[tid];
+                reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool))[row + tid] = vr[tid];
+            }
+        }
+    }
+
     u32x4 qv[kGroup][2];       // bf16 pool: bf16 pairs of dims 8 c8 .. and 64 + 8 c8 ..
     uint32_t qh[kGroup][8];    // q8_0 pool: binary16 pairs of dims 16 c8 + 2 j, + 1
     float qbias[kGroup];       // q8_0 pool: -1152 times the sum of those 16 values
@@ -639,7 +664,24 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
 
     float* pw = p_lds[wave];
 
-    auto process = [&](const Stage& st, int j) __attribute__((always_inline)) {
+    auto process = [&](const Stage& st_in, int j) __attribute__((always_inline)) {
+        Stage st = st_in;
+        if constexpr (kFused) {
+            if (g0 + wave + kDecodeWaves * j == new_blk) {   // the block that holds the new token
+                if (t8 == new_off) {
+                    st.k[0] = kn0;
+                    st.k[1] = kn1;
+                }
+                if (t8 + 8 == new_off) {
+                    st.k[2] = kn0;
+                    st.k[3] = kn1;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (tg + 4 * i == new_off)
+                        st.v[i] = vn;
+            }
+        }
         // scores of tokens t8 + 8 tt for the four heads, partial over this lane's 16 dims,
         // index 4 tt + h; the reduce-scatter leaves lane c8 with the full score of token
         // ts = t8 + 8 (c8 / 4), head hs = c8 % 4
@@ -894,10 +936,10 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
         merge_rows_results<1, 32>(p, &r, 1, kvh, nprefix);
 }
 
-template <bool kQ8>
+template <bool kQ8, bool kFused>
 __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParams p)
 {
-    decode_body<kQ8>(p, blockIdx.x);
+    decode_body<kQ8, kFused>(p, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------ prefill
@@ -1620,13 +1662,14 @@ static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs bot
 // form), the rest are the decode workgroups.  The prefix workgroups come first in the
 // grid and wait for nothing; a (row, KV head) is finished by whichever of its decode
 // splits and prefix splits arrives last, so no workgroup ever waits for another.
+template <bool kFused>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_cascade_decode(PrefillParams pp, DecodeParams dp,
                                                                  int32_t num_prefix_wgs)
 {
     if ((int32_t)blockIdx.x < num_prefix_wgs)
         prefill_body<true>(pp, dp, blockIdx.x);
     else
-        decode_body<false>(dp, blockIdx.x - num_prefix_wgs);
+        decode_body<false, kFused>(dp, blockIdx.x - num_prefix_wgs);
 }
 
 
@@ -1766,8 +1809,10 @@ extern "C" pa_status pa_copy_blocks_q8(const pa_geometry* g, void* kv_pool_q8, c
 static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t* plan, const void* q,
                                  const void* k_pool, const void* v_pool, const int32_t* block_tables,
                                  int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
-                                 float* lse, void* workspace, size_t workspace_bytes, void* stream)
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                                 const void* k_new = nullptr, const void* v_new = nullptr)
 {
+    const bool fused = k_new != nullptr;
     if (!g || !plan)
         return PA_ERR_NULL;
     if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
@@ -1826,6 +1871,16 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         vs = pa_validate_batch(g, R, qo.data(), kvl.data(), bt.data(), max_blocks_per_req, nullptr);
         if (vs != PA_OK)
             return vs;
+        if (fused) {            // the slots the fused append writes: position kv_len - 1 of each row
+            std::vector<int32_t> slots(R);
+            for (int32_t r = 0; r < R; ++r) {
+                const int32_t pos = kvl[r] - 1;
+                slots[r] = bt[(size_t)r * max_blocks_per_req + pos / kBlock] * kBlock + pos % kBlock;
+            }
+            vs = pa_validate_append(g, slots.data(), R, nullptr);
+            if (vs != PA_OK)
+                return vs;
+        }
     }
     const float scale_log2 = g->scale * kLog2e;
 
@@ -1910,6 +1965,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         }
         dp.px_part_o = ngroups > 0 ? reinterpret_cast<float*>(wsp + ws.px_part_o) : nullptr;
         dp.px_part_lse = ngroups > 0 ? reinterpret_cast<float*>(wsp + ws.px_part_lse) : nullptr;
+        dp.k_new = static_cast<const uint16_t*>(k_new);
+        dp.v_new = static_cast<const uint16_t*>(v_new);
         const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * g->num_kv_heads;
         if (ngroups > 0) {
             // each group's shared blocks, once per KV head, for all of its query rows, in
@@ -1926,15 +1983,24 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             const int64_t nprefix = (int64_t)ngroups * g->num_kv_heads * plan->prefix_splits;
             if (grid + nprefix > INT32_MAX)
                 return PA_ERR_SHAPE;
-            hipLaunchKernelGGL(pa_cascade_decode, dim3((uint32_t)(grid + nprefix)), dim3(64 * kPfWaves), 0, st, pp, dp,
-                               (int32_t)nprefix);
+            if (fused)
+                hipLaunchKernelGGL(pa_cascade_decode<true>, dim3((uint32_t)(grid + nprefix)), dim3(64 * kPfWaves), 0,
+                                   st, pp, dp, (int32_t)nprefix);
+            else
+                hipLaunchKernelGGL(pa_cascade_decode<false>, dim3((uint32_t)(grid + nprefix)), dim3(64 * kPfWaves), 0,
+                                   st, pp, dp, (int32_t)nprefix);
         } else {
             if (grid > INT32_MAX)
                 return PA_ERR_SHAPE;
             if (q8)
-                hipLaunchKernelGGL(pa_decode_split<true>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
+                hipLaunchKernelGGL((pa_decode_split<true, false>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
+                                   dp);
+            else if (fused)
+                hipLaunchKernelGGL((pa_decode_split<false, true>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
+                                   dp);
             else
-                hipLaunchKernelGGL(pa_decode_split<false>, dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
+                hipLaunchKernelGGL((pa_decode_split<false, false>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
+                                   dp);
         }
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
@@ -1949,6 +2015,21 @@ extern "C" pa_status pa_attention_batch(const pa_geometry* g, const pa_plan_t* p
 {
     return attention_batch(false, g, plan, q, k_pool, v_pool, block_tables, max_blocks_per_req, qo_indptr, kv_len,
                            out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_step(const pa_geometry* g, const pa_plan_t* plan, const void* q, void* k_pool,
+                                    void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
+                                    int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                    void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    if (plan->num_prefill_rows > 0 || plan->prefill_tiles > 0)
+        return PA_ERR_UNSUPPORTED;                 // decode rows only
+    if (plan->num_reqs > 0 && plan->total_q > 0 && (!k_new || !v_new))
+        return PA_ERR_NULL;
+    return attention_batch(false, g, plan, q, k_pool, v_pool, block_tables, max_blocks_per_req, qo_indptr, kv_len,
+                           out, lse, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 extern "C" pa_status pa_attention_batch_q8(const pa_geometry* g, const pa_plan_t* plan, const void* q,

@@ -546,3 +546,56 @@ def test_validate_mode_rejects_bad_content_before_launch(monkeypatch):
         pa.pa_append_kv(g, kp, vp, pa.to_device(wl.k_new), pa.to_device(wl.v_new), pa.to_device(slots))
     torch.cuda.synchronize()
     assert torch.equal(kp, before) and not out.any()   # nothing was launched
+
+
+# ------------------------------------------------------------------ fused decode step
+
+def _decode_step_gpu(wl, split_blocks=0, cascade=False):
+    """pa_decode_step on device copies of the workload; returns host (k_pool, v_pool, out, lse)."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256, split_blocks)
+    if cascade:
+        pa.pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables)
+    kp, vp = pa.to_device(wl.k_pool), pa.to_device(wl.v_pool)
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    pa.pa_decode_step(g, plan, pa.to_device(wl.q), kp, vp, pa.to_device(wl.k_new), pa.to_device(wl.v_new),
+                      pa.to_device(wl.block_tables), pa.to_device(wl.qo_indptr), pa.to_device(wl.kv_len), out, lse,
+                      pa.workspace_for(plan))
+    torch.cuda.synchronize()
+    return (kp.cpu().numpy().view(np.uint16), vp.cpu().numpy().view(np.uint16), out.cpu().numpy().view(np.uint16),
+            lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", ["tiny", "qwen3", "split7", "split1", "cascade"])
+def test_fused_decode_step_matches_append_then_attention(case):
+    """Writing each row's new token inside the attention launch gives the pools the
+    oracle's append gives, and the same output bits as pa_append_kv followed by
+    pa_attention_batch on the GPU."""
+    split = {"split7": 7, "split1": 1}.get(case, 0)
+    cascade = case == "cascade"
+    wl = {"tiny": lambda: synthetic.config_tiny(),
+          "qwen3": lambda: synthetic.config_decode(num_reqs=12, num_blocks=2000),
+          "split7": lambda: synthetic.config_tiny(seed=45),
+          "split1": lambda: synthetic.build("fused_split1", 46, 32, 8, qo_len=[1] * 3, kv_len=[1, 17, 300],
+                                            num_blocks=40),
+          "cascade": lambda: synthetic.build("fused_cascade", 47, 32, 8, qo_len=[1] * 5, kv_len=[700, 820, 990, 640, 777],
+                                             num_blocks=400, shared_prefix_blocks=30)}[case]()
+    print(f"[gpu] fused decode step {case}", flush=True)
+    kp, vp, out, lse = _decode_step_gpu(wl, split, cascade)
+    okp, ovp, ref = oracle.run_workload(wl)
+    assert np.array_equal(kp, okp) and np.array_equal(vp, ovp)
+    eo, el = _errors(out, lse, ref)
+    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+    _, _, out2, lse2 = _run_gpu(wl, split, cascade=cascade)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_fused_decode_step_rejects_chunk_rows():
+    import paged_kv_attention_04_amd as pa
+    wl = synthetic.build("fused_mixed", 48, 8, 2, qo_len=[1, 40], kv_len=[20, 100], num_blocks=32)
+    with pytest.raises(pa.PaError, match="UNSUPPORTED"):
+        _decode_step_gpu(wl)
