@@ -208,6 +208,35 @@ def test_plan_shared_prefix_runs_and_limits():
     assert e.value.code == -2 and bytes(plan) == before
 
 
+def test_plan_shared_prefix_fused_launch_choices():
+    """The prefix key splits give each prefix workgroup at most six 128-key steps; the
+    decode split length is one of the even cuts of the longest suffix (48 blocks for the
+    16-request, 6144-token case, the measured best); the workspace holds a decode partial
+    for every group row (its result waits there for the prefix partials) and the prefix
+    partials."""
+    g = qwen(num_blocks=100000)
+    sp = synthetic.config_shared_prefix(poison=False)
+    plan = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
+    pa.pa_plan_shared_prefix(g, plan, sp.qo_len, sp.kv_len, sp.block_tables, 256)
+    assert plan.prefix_splits == 8 and plan.split_blocks == 48 and plan.max_splits == 3
+    longest = max(-(-int(L) // 16) - 384 for L in sp.kv_len)
+    assert plan.split_blocks in {-(-longest // k) for k in range(1, 17)}
+    R, S, Hq = 16, plan.max_splits, 32
+    need = 65536 + R * S * Hq * 128 * 4 + R * S * Hq * 4 + R * plan.prefix_splits * Hq * 129 * 4
+    assert plan.workspace_bytes >= need
+    again = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
+    pa.pa_plan_shared_prefix(g, again, sp.qo_len, sp.kv_len, sp.block_tables, 256)
+    assert bytes(again) == bytes(plan)                 # a pure function of its inputs
+    for shared, want in ((20, 1), (100, 3), (200, 5)):
+        qo = [1] * 6
+        kv = [16 * (shared + 30) + r for r in range(6)]
+        bt = _shared_tables(6, shared, [31] * 6, shared + 40)
+        p2 = pa.pa_plan(g, qo, kv, 256)
+        pa.pa_plan_shared_prefix(g, p2, qo, kv, bt, 256)
+        steps = -(-shared * 16 // 128)
+        assert p2.num_prefix_groups == 1 and p2.prefix_splits == want == -(-steps // 6)
+
+
 def test_plan_errors():
     g = qwen()
     with pytest.raises(pa.PaError) as e:
