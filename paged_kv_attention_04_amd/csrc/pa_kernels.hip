@@ -977,6 +977,7 @@ struct PrefillParams {
 constexpr int kPfKeys = pa::kPrefillKeys;  // keys per step: eight 16-token blocks
 constexpr int kPfWaves = 8;                // 4 row groups x 2 key halves
 constexpr int kPfRows = pa::kPrefillQ * kGroup;   // 128 MFMA rows: (token, head) pairs
+static_assert(kPfRows * kHeadDim == pa::kPrefillPartFloats, "a prefill split partial holds every row of its tile");
 constexpr int kPfAcc = 16;                 // f32x4 O^T accumulators per lane: 2 row blocks x 8 dim blocks
 constexpr int kTileChunks = kPfKeys * kHeadDim * 2 / 16;   // 16-byte chunks in one K or V tile
 

@@ -569,7 +569,7 @@ def _decode_step_gpu(wl, split_blocks=0, cascade=False):
             lse.cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["tiny", "qwen3", "split7", "split1", "cascade"])
+@pytest.mark.parametrize("case", ["tiny", "qwen3", "qwen3_full", "split7", "split1", "cascade"])
 def test_fused_decode_step_matches_append_then_attention(case):
     """Writing each row's new token inside the attention launch gives the pools the
     oracle's append gives, and the same output bits as pa_append_kv followed by
@@ -578,6 +578,7 @@ def test_fused_decode_step_matches_append_then_attention(case):
     cascade = case == "cascade"
     wl = {"tiny": lambda: synthetic.config_tiny(),
           "qwen3": lambda: synthetic.config_decode(num_reqs=12, num_blocks=2000),
+          "qwen3_full": lambda: synthetic.config_decode(),        # the bench's step, full size
           "split7": lambda: synthetic.config_tiny(seed=45),
           "split1": lambda: synthetic.build("fused_split1", 46, 32, 8, qo_len=[1] * 3, kv_len=[1, 17, 300],
                                             num_blocks=40),
