@@ -522,6 +522,21 @@ def main(argv=None):
           "measured_saving_us": round((t_plain - t_q) * 1e6, 3),
           "implied_conversion_us": round((predicted - (t_plain - t_q)) * 1e6, 3)}
 
+    # speculative verification: 16 requests, 8 new tokens each at 8192 tokens of context
+    # (small qo_len rows, served by the chunked-prefill path; K / V streaming dominates)
+    wv = synthetic.build("spec_verify", 91, 32, 8, qo_len=[8] * 16, kv_len=[8192 + 8] * 16,
+                         num_blocks=16 * (8192 // 16 + 2) + 64, poison=False)
+    abv = algorithmic_bytes(wv)
+    sv = Stepper(wv, 2)
+    time_steps(sv, 10, 5, attention_only=True)
+    t_v = event_time(sv, max(args.steps // 4, 30))
+    spec = {"workload": "16 requests x 8 new tokens (causal) at kv_len 8200, 32 q / 8 kv heads",
+            "attention_us": round(t_v * 1e6, 3), "bytes_per_launch": abv["attention"],
+            "gbs": round(abv["attention"] / t_v / 1e9, 1),
+            "frac_of_hbm_peak": round(abv["attention"] / t_v / 1e9 / HBM_PEAK_GBS, 4),
+            "prefill_splits": sv.plan.prefill_splits}
+    del sv
+
     # the prefill chunk alone, against the bf16 matrix peak
     wp = prefill_only_workload()
     sp = Stepper(wp, 2)
@@ -558,6 +573,7 @@ def main(argv=None):
                         "attention_us": round(t_m * 1e6, 3)},
         "shared_prefix": shared,
         "q8_0_decode": q8,
+        "spec_verify": spec,
         "prefill_chunk": {"workload": "512 new tokens at kv offset 4096, 32 q / 8 kv heads, causal",
                           "us": round(t_p * 1e6, 3), "tflops": round(pflops / t_p / 1e12, 1),
                           "frac_of_bf16_mfma_peak": round(pflops / t_p / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
