@@ -600,3 +600,11 @@ def test_fused_decode_step_rejects_chunk_rows():
     wl = synthetic.build("fused_mixed", 48, 8, 2, qo_len=[1, 40], kv_len=[20, 100], num_blocks=32)
     with pytest.raises(pa.PaError, match="UNSUPPORTED"):
         _decode_step_gpu(wl)
+
+
+def test_spec_verify_rows():
+    """Speculative verification (small qo_len rows): 16 requests x 8 new tokens, causal,
+    at 2056 tokens of context, through the chunked-prefill path."""
+    wl = synthetic.build("spec_verify_2k", 92, 32, 8, qo_len=[8] * 16, kv_len=[2048 + 8] * 16,
+                         num_blocks=16 * 130 + 32)
+    check(wl, label="spec verify")
