@@ -608,3 +608,40 @@ def test_spec_verify_rows():
     wl = synthetic.build("spec_verify_2k", 92, 32, 8, qo_len=[8] * 16, kv_len=[2048 + 8] * 16,
                          num_blocks=16 * 130 + 32)
     check(wl, label="spec verify")
+
+
+# ------------------------------------------------------------------ randomised batches
+
+def _random_batch(seed):
+    """A seeded random batch: 1-24 rows, a mix of decode rows and chunk rows (2-100 new
+    tokens), contexts up to ~2600 tokens, sometimes a shared prefix, random split
+    overrides, and which path runs it."""
+    rng = np.random.default_rng(1000 + seed)
+    R = int(rng.integers(1, 25))
+    decode_only = rng.random() < 0.5
+    qo = [1 if (decode_only or rng.random() < 0.6) else int(rng.integers(2, 101)) for _ in range(R)]
+    shared = int(rng.choice([0, 0, 17, 40])) if R > 1 else 0
+    kv = [int(max(q, shared * 16 + 1 + rng.integers(0, 2600 - shared * 16))) for q in qo]
+    kv = [max(k, q + shared * 16) for k, q in zip(kv, qo)]     # new tokens never land in shared blocks
+    nb = sum(-(-k // 16) for k in kv) + 16
+    wl = synthetic.build(f"random{seed}", 2000 + seed, 32, 8, qo_len=qo, kv_len=kv, num_blocks=nb,
+                         shared_prefix_blocks=shared, poison=True)
+    split = int(rng.choice([0, 0, 1, 3, 16]))
+    psplit = int(rng.choice([0, 0, 1, 2, 5]))
+    cascade = bool(shared and decode_only and rng.random() < 0.7)
+    return wl, split, psplit, cascade, decode_only, rng
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_batches(seed):
+    wl, split, psplit, cascade, decode_only, rng = _random_batch(seed)
+    print(f"[gpu] random batch {seed}: R={wl.num_reqs} qo={list(wl.qo_len)[:6]}.. kv_max={int(wl.kv_len.max())} "
+          f"shared={wl.shared_prefix_blocks} split={split} psplit={psplit} cascade={cascade}", flush=True)
+    check(wl, split_blocks=split, prefill_splits=psplit, cascade=cascade, label=f"random {seed}")
+    if decode_only:
+        kp, vp, out, lse = _decode_step_gpu(wl, split, cascade)          # the fused step, same bits
+        _, _, out2, lse2 = _run_gpu(wl, split, cascade=cascade)
+        assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+        q8 = synthetic.build_q8(f"random{seed}_q8", 3000 + seed, 32, 8, qo_len=list(wl.qo_len),
+                                kv_len=list(wl.kv_len), num_blocks=wl.num_blocks)
+        check(q8, split_blocks=split, label=f"random {seed} q8_0")
