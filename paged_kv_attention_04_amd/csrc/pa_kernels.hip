@@ -334,10 +334,10 @@ __device__ inline void load_stage(KvStage& s, const uint16_t* ktile, const uint1
     const int t8 = lane >> 3, c8 = lane & 7;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        s.k[i] = kp[(t8 + 8 * (i >> 1)) * 16 + c8 + 8 * (i & 1)];
+        s.k[i] = __builtin_nontemporal_load(kp + (t8 + 8 * (i >> 1)) * 16 + c8 + 8 * (i & 1));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        s.v[i] = vp[64 * i];
+        s.v[i] = __builtin_nontemporal_load(vp + 64 * i);
 }
 
 // q8_0 tile: codes [16][128] int8, then scales [16][4] binary16.
@@ -355,18 +355,18 @@ struct KvStageQ8 {
 __device__ inline void load_stage_q8(KvStageQ8& s, const uint8_t* ktile, const uint8_t* vtile, int lane)
 {
     const int t8 = lane >> 3, c8 = lane & 7, tg = lane >> 4, c16 = lane & 15;
-    s.k[0] = *reinterpret_cast<const u32x4*>(ktile + t8 * kHeadDim + 16 * c8);
-    s.k[1] = *reinterpret_cast<const u32x4*>(ktile + (t8 + 8) * kHeadDim + 16 * c8);
+    s.k[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ktile + t8 * kHeadDim + 16 * c8));
+    s.k[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ktile + (t8 + 8) * kHeadDim + 16 * c8));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        s.v[i] = *reinterpret_cast<const u32x2*>(vtile + (tg + 4 * i) * kHeadDim + 8 * c16);
+        s.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vtile + (tg + 4 * i) * kHeadDim + 8 * c16));
     const uint16_t* ksc = reinterpret_cast<const uint16_t*>(ktile + pa::kQ8CodeBytes);
     const uint16_t* vsc = reinterpret_cast<const uint16_t*>(vtile + pa::kQ8CodeBytes);
-    s.ks[0] = ksc[t8 * 4 + (c8 >> 1)];
-    s.ks[1] = ksc[(t8 + 8) * 4 + (c8 >> 1)];
+    s.ks[0] = __builtin_nontemporal_load(ksc + t8 * 4 + (c8 >> 1));
+    s.ks[1] = __builtin_nontemporal_load(ksc + (t8 + 8) * 4 + (c8 >> 1));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        s.vs[i] = vsc[(tg + 4 * i) * 4 + (c16 >> 2)];
+        s.vs[i] = __builtin_nontemporal_load(vsc + (tg + 4 * i) * 4 + (c16 >> 2));
 }
 
 __device__ inline float dot16(const u32x4& q, const u32x4& k, float acc)
@@ -567,9 +567,12 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     const int ts = t8 + 8 * (c8 >> 2), hs = c8 & 3;   // softmax role: token ts, head hs
     const int c16 = lane & 15, tg = lane >> 4;        // PV role
 
+    // j < 0: a spare load whose data is never used; it reads pool block 0, which the
+    // other spare loads keep in L2 (a re-read of the run's own last block would often
+    // miss, the K / V loads being nontemporal)
     auto issue = [&](Stage& st, int j) __attribute__((always_inline)) {
-        int id = __builtin_amdgcn_readlane(my_blk, j);
-        id = (id >= 0 && id < p.num_blocks) ? id : 0;
+        int id = __builtin_amdgcn_readlane(my_blk, j < 0 ? 0 : j);
+        id = (j >= 0 && id >= 0 && id < p.num_blocks) ? id : 0;
         if constexpr (kQ8) {
             const uint8_t* kt = reinterpret_cast<const uint8_t*>(p.k_pool) +
                                 ((int64_t)id * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);
@@ -816,15 +819,15 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
 
     if (!bad && nb > 0) {
         // Loads for block j + kDepth are issued before block j is processed (the first
-        // kDepth were issued above).  Past the end of the run the last block is
-        // fetched again (an L2 hit), so every iteration issues the same loads, and the stages
-        // in flight at the top of the steady-state loop are the same on entry and on every
-        // trip: the compiler can then wait for exactly the oldest stage.
+        // kDepth were issued above).  Past the end of the run a spare load is issued
+        // instead, so every iteration issues the same loads, and the stages in flight at
+        // the top of the steady-state loop are the same on entry and on every trip: the
+        // compiler can then wait for exactly the oldest stage.
         int j0 = 0;
         for (; j0 + kDepth + 1 <= nb; j0 += kDepth + 1) {
 #pragma unroll
             for (int u = 0; u <= kDepth; ++u) {
-                issue(st[(u + kDepth) % (kDepth + 1)], min(j0 + u + kDepth, nb - 1));
+                issue(st[(u + kDepth) % (kDepth + 1)], j0 + u + kDepth < nb ? j0 + u + kDepth : -1);
                 process(st[u], j0 + u);
             }
         }
