@@ -163,13 +163,18 @@ pa_status pa_plan(const pa_geometry* geometry, int32_t num_reqs, const int32_t* 
  * batch will use (a device table that differs gives wrong results).  Runs longer than
  * PA_MAX_PREFIX_GROUP_REQS are cut; at most PA_MAX_PREFIX_GROUPS groups are kept.
  * Recomputes the decode splits over the private suffixes and the workspace size; a
- * plan with no group found is left as it was.  Errors: PA_ERR_NULL, PA_ERR_SHAPE
- * (lengths differ from the plan's), PA_ERR_UNSUPPORTED (completion counters, as for
- * pa_plan).
+ * plan with no group found is left as it was.  prefix_splits: 0 lets the planner
+ * choose how many key ranges each group's shared blocks are cut into (one workgroup
+ * per range and KV head); > 0 forces that count (1 .. 64).  split_blocks: 0 lets the
+ * planner choose the decode split length over the private suffixes; > 0 forces it
+ * (clamped to 1 .. 512).  Errors: PA_ERR_NULL, PA_ERR_SHAPE (lengths differ from
+ * the plan's, prefix_splits or split_blocks out of range), PA_ERR_UNSUPPORTED
+ * (completion counters, as for pa_plan).
  */
 pa_status pa_plan_shared_prefix(const pa_geometry* geometry, const int32_t* qo_len_host, const int32_t* kv_len_host,
                                 const int32_t* block_tables_host, int32_t max_blocks_per_req, int32_t num_cus,
-                                int32_t min_shared_blocks, pa_plan_t* plan);
+                                int32_t min_shared_blocks, int32_t prefix_splits, int32_t split_blocks,
+                                pa_plan_t* plan);
 
 /*
  * Write this step's new K/V rows into the pools through the slot mapping

@@ -76,7 +76,7 @@ def lib():
     P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     G, PL = ctypes.POINTER(Geometry), ctypes.POINTER(Plan)
     L.pa_plan.argtypes = [G, i32, P, P, i32, i32, i32, PL]
-    L.pa_plan_shared_prefix.argtypes = [G, P, P, P, i32, i32, i32, PL]
+    L.pa_plan_shared_prefix.argtypes = [G, P, P, P, i32, i32, i32, i32, i32, PL]
     L.pa_append_kv.argtypes = [G, P, P, P, P, P, i32, P]
     L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_decode_step.argtypes = [G, PL, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
@@ -167,9 +167,10 @@ def pa_plan(geometry: Geometry, qo_len, kv_len, num_cus: int = 256, split_blocks
 
 
 def pa_plan_shared_prefix(geometry: Geometry, plan: Plan, qo_len, kv_len, block_tables, num_cus: int = 256,
-                          min_shared_blocks: int = 0) -> Plan:
+                          min_shared_blocks: int = 0, prefix_splits: int = 0, split_blocks: int = 0) -> Plan:
     """Add shared-prefix groups found in the host block tables to `plan` (in place; also
-    returned).  block_tables: host int32 [num_reqs][max_blocks]."""
+    returned).  block_tables: host int32 [num_reqs][max_blocks].  prefix_splits /
+    split_blocks: 0 lets the planner choose; > 0 forces the value."""
     import numpy as np
     qo = np.ascontiguousarray(qo_len, dtype=np.int32)
     kv = np.ascontiguousarray(kv_len, dtype=np.int32)
@@ -178,7 +179,8 @@ def pa_plan_shared_prefix(geometry: Geometry, plan: Plan, qo_len, kv_len, block_
         raise ValueError("block_tables must be [num_reqs][max_blocks] and match the lengths")
     _check("pa_plan_shared_prefix", lib().pa_plan_shared_prefix(ctypes.byref(geometry), _np_ptr(qo), _np_ptr(kv),
                                                                 _np_ptr(bt), int(bt.shape[1]), int(num_cus),
-                                                                int(min_shared_blocks), ctypes.byref(plan)))
+                                                                int(min_shared_blocks), int(prefix_splits),
+                                                                int(split_blocks), ctypes.byref(plan)))
     return plan
 
 

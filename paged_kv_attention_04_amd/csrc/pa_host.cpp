@@ -89,19 +89,28 @@ void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t*
 // in the grid, then the decode ones split-major, each dispatched to the first CU that
 // frees up (one workgroup per CU).  Makespan of that launch in decode block-times, from a
 // greedy list-scheduling simulation over batches of identical workgroups (a map from
-// free time to the number of CUs free then).  Costs, fitted to measurements on MI355X
-// (rms error ~2 us over 20 split choices of the 16-request, 6144-token-prefix case): a
-// decode workgroup streams its blocks at 1 each plus 13.3 of fixed cost, and the last
-// split of a row also merges its partials, 6.67 per eight; a prefix workgroup costs 33.3
-// plus 6.67 per 128-key step.
-constexpr double kFusedDecodeFixed = 13.3;
-constexpr double kFusedPrefixFixed = 33.3;
-constexpr double kFusedPrefixStep = 6.67;
-constexpr double kFusedMergePer8 = 6.67;
-constexpr int32_t kPrefixStepsPerSplit = 6;
+// free time to the number of CUs free then).  A decode workgroup costs its blocks plus a
+// fixed cost, and the last split of a row also merges its partials (a cost per eight);
+// a prefix workgroup costs a fixed amount, an amount per 128-key step and one per
+// request of its group.
+struct MakespanCosts {
+    double decode_fixed, merge_per8, prefix_fixed, prefix_step, prefix_per_req;
+};
+// Fitted to the 16-request, 6144-token-prefix case on MI355X (rms error ~2 us over 20
+// split choices); used to pick the decode split length for a given prefix split count.
+constexpr MakespanCosts kSplitCosts = {13.3, 6.67, 33.3, 6.67, 0.0};
+// Fitted to 320 measured (prefix splits, split length) pairs over five batches (4 to 32
+// requests sharing a 6144-token prefix, 2048-token suffixes; rms log error 0.11); it
+// weighs the prefix pass, whose 128-key steps stream their blocks from memory once, more
+// heavily and is used to choose between prefix split counts.
+constexpr MakespanCosts kPrefixCosts = {23.0, 5.57, 43.9, 11.6, 3.30};
+// Candidate prefix split counts: this many 128-key steps per prefix workgroup (the
+// measured optimum over those five batches was always at 4 or 6 steps, or within 2% of it).
+constexpr int32_t kPrefixStepsPerSplit[] = {6, 4};
 
 double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_blocks, const int32_t* qo_len,
-                      int32_t num_kv_heads, int32_t num_cus, int32_t prefix_splits, int32_t split_blocks)
+                      int32_t num_kv_heads, int32_t num_cus, int32_t prefix_splits, int32_t split_blocks,
+                      const MakespanCosts& c)
 {
     std::map<double, int64_t> free_at;     // time -> CUs that become free then
     free_at[0.0] = std::max(num_cus, 1);
@@ -122,7 +131,7 @@ double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_
         const int32_t steps = ceil_div((int64_t)plan.prefix_blocks[gi] * pa::kBlock, pa::kPrefillKeys);
         for (int32_t sp = 0; sp < prefix_splits; ++sp) {
             const int32_t n = (sp + 1) * steps / prefix_splits - sp * steps / prefix_splits;
-            run(num_kv_heads, kFusedPrefixFixed + kFusedPrefixStep * n);
+            run(num_kv_heads, c.prefix_fixed + c.prefix_step * n + c.prefix_per_req * plan.prefix_num_reqs[gi]);
         }
     }
     int32_t max_splits = 0;
@@ -137,9 +146,8 @@ double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_
             const int32_t n = std::min(split_blocks, suffix_blocks[r] - sp * split_blocks);
             if (n <= 0)
                 continue;
-            const double merge =
-                sp == ns - 1 ? kFusedMergePer8 * (ceil_div(ns, 8) + ceil_div(prefix_splits, 8)) : 0.0;
-            run(num_kv_heads, kFusedDecodeFixed + n + merge);
+            const double merge = sp == ns - 1 ? c.merge_per8 * (ceil_div(ns, 8) + ceil_div(prefix_splits, 8)) : 0.0;
+            run(num_kv_heads, c.decode_fixed + n + merge);
         }
     return end;
 }
@@ -233,7 +241,8 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
 
 extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* qo_len, const int32_t* kv_len,
                                            const int32_t* bt, int32_t max_blocks, int32_t num_cus,
-                                           int32_t min_shared_blocks, pa_plan_t* plan)
+                                           int32_t min_shared_blocks, int32_t prefix_splits, int32_t split_blocks,
+                                           pa_plan_t* plan)
 {
     if (!g || !plan)
         return PA_ERR_NULL;
@@ -243,6 +252,8 @@ extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* 
     if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
         return PA_ERR_UNSUPPORTED;
     if (max_blocks < 1 && R > 0)
+        return PA_ERR_SHAPE;
+    if (prefix_splits < 0 || prefix_splits > pa::kMaxPrefillSplits || split_blocks < 0)
         return PA_ERR_SHAPE;
     int64_t total_q = 0;
     for (int32_t r = 0; r < R; ++r) {
@@ -293,12 +304,15 @@ extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* 
     if (out.num_prefix_groups == 0)
         return PA_OK;
 
-    // Key splits of the shared blocks: at most kPrefixStepsPerSplit 128-key steps per
-    // prefix workgroup, so that the prefix pass ends before the decode splits it shares
-    // the launch with (measured on the 6144-token prefix: 6 steps per split ran in 42 us,
-    // 8 and more in 63-100 us, a prefix workgroup then finishing last and merging its
-    // group's rows).  Then the decode split length over the private suffixes with the
-    // smallest simulated makespan of the fused launch (ties to the longer split).
+    // Key splits of the shared blocks and the decode split length over the private
+    // suffixes, chosen together for the one launch.  For each candidate prefix split
+    // count (kPrefixStepsPerSplit 128-key steps per prefix workgroup) the split length
+    // with the smallest simulated makespan under kSplitCosts (ties to the longer split);
+    // then the candidate whose plan has the smaller makespan under kPrefixCosts (ties to
+    // the first).  Measured on the 6144-token prefix: 8 and more steps per prefix
+    // workgroup ran in 63-100 us against 42 us at 6 (a prefix workgroup then finishing
+    // last and merging its group's rows), and with 4 requests per group 4 steps ran in
+    // 30 us against 39 us at 6 (the prefix pass is then the critical path).
     std::vector<int32_t> skip(R, 0), suffix(R, 0);
     for (int32_t i = 0; i < out.num_prefix_groups; ++i)
         for (int32_t k = 0; k < out.prefix_num_reqs[i]; ++k)
@@ -310,21 +324,42 @@ extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* 
             longest = std::max(longest, suffix[r]);
     }
     const int32_t steps = ceil_div((int64_t)max_prefix_blocks * pa::kBlock, pa::kPrefillKeys);
-    const int32_t best_ps = std::min(std::max(1, ceil_div(steps, kPrefixStepsPerSplit)), pa::kMaxPrefillSplits);
-    double best = 0.0;
-    int32_t best_sb = std::min(longest, pa::kMaxSplitBlocks);
-    bool have = false;
-    for (int32_t parts = 1; parts <= 16; ++parts) {
-        const int32_t sb = ceil_div(longest, parts);
-        if (sb > pa::kMaxSplitBlocks)
-            continue;
-        if (sb < kMinAutoSplitBlocks && parts > 1)
-            break;
-        const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, best_ps, sb);
-        if (!have || t < best - 1e-9) {
-            have = true;
-            best = t;
-            best_sb = sb;
+    auto best_split_length = [&](int32_t ps) {
+        if (split_blocks > 0)
+            return split_blocks;
+        double best = 0.0;
+        int32_t best_sb = std::min(longest, pa::kMaxSplitBlocks);
+        bool have = false;
+        for (int32_t parts = 1; parts <= 16; ++parts) {
+            const int32_t sb = ceil_div(longest, parts);
+            if (sb > pa::kMaxSplitBlocks)
+                continue;
+            if (sb < kMinAutoSplitBlocks && parts > 1)
+                break;
+            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb, kSplitCosts);
+            if (!have || t < best - 1e-9) {
+                have = true;
+                best = t;
+                best_sb = sb;
+            }
+        }
+        return best_sb;
+    };
+    int32_t best_ps = 0, best_sb = 0;
+    if (prefix_splits > 0) {
+        best_ps = prefix_splits;
+        best_sb = best_split_length(best_ps);
+    } else {
+        double best = 0.0;
+        for (const int32_t per : kPrefixStepsPerSplit) {
+            const int32_t ps = std::min(std::max(1, ceil_div(steps, per)), pa::kMaxPrefillSplits);
+            const int32_t sb = best_split_length(ps);
+            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb, kPrefixCosts);
+            if (best_ps == 0 || t < best - 1e-9) {
+                best = t;
+                best_ps = ps;
+                best_sb = sb;
+            }
         }
     }
     out.prefix_splits = best_ps;

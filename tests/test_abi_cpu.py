@@ -209,11 +209,13 @@ def test_plan_shared_prefix_runs_and_limits():
 
 
 def test_plan_shared_prefix_fused_launch_choices():
-    """The prefix key splits give each prefix workgroup at most six 128-key steps; the
-    decode split length is one of the even cuts of the longest suffix (48 blocks for the
-    16-request, 6144-token case, the measured best); the workspace holds a decode partial
-    for every group row (its result waits there for the prefix partials) and the prefix
-    partials."""
+    """The prefix key splits give each prefix workgroup six or four 128-key steps (the two
+    candidates the planner weighs); the decode split length is one of the even cuts of
+    the longest suffix.  Pinned choices, each the measured best or within 2% of it on
+    MI355X: 16 requests at 8192 + U sharing 6144 tokens -> (8 splits, 48 blocks); the
+    36-layer sweep's batch 8 (4 of the rows share the prefix) -> (12, 65) and batch 32
+    -> (12, 129).  The workspace holds a decode partial for every group row (its result
+    waits there for the prefix partials) and the prefix partials."""
     g = qwen(num_blocks=100000)
     sp = synthetic.config_shared_prefix(poison=False)
     plan = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
@@ -227,14 +229,45 @@ def test_plan_shared_prefix_fused_launch_choices():
     again = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
     pa.pa_plan_shared_prefix(g, again, sp.qo_len, sp.kv_len, sp.block_tables, 256)
     assert bytes(again) == bytes(plan)                 # a pure function of its inputs
-    for shared, want in ((20, 1), (100, 3), (200, 5)):
+    for batch, want in ((8, (12, 65)), (32, (12, 129))):
+        wl = synthetic.config_sweep_decode(batch, 0, poison=False, fill_pools=False)
+        gs = pa.Geometry.make(32, 8, wl.num_blocks)
+        p = pa.pa_plan(gs, wl.qo_len, wl.kv_len, 256)
+        pa.pa_plan_shared_prefix(gs, p, wl.qo_len, wl.kv_len, wl.block_tables, 256)
+        assert (p.prefix_splits, p.split_blocks) == want, batch
+    for shared in (20, 100, 200):
         qo = [1] * 6
         kv = [16 * (shared + 30) + r for r in range(6)]
         bt = _shared_tables(6, shared, [31] * 6, shared + 40)
         p2 = pa.pa_plan(g, qo, kv, 256)
         pa.pa_plan_shared_prefix(g, p2, qo, kv, bt, 256)
         steps = -(-shared * 16 // 128)
-        assert p2.num_prefix_groups == 1 and p2.prefix_splits == want == -(-steps // 6)
+        assert p2.num_prefix_groups == 1 and p2.prefix_splits in {-(-steps // 6), -(-steps // 4)}
+
+
+def test_plan_shared_prefix_overrides():
+    """Forced prefix split counts and split lengths are used as given (the split length
+    clamped to 512 blocks); out-of-range values are PA_ERR_SHAPE and leave the plan as
+    it was."""
+    g = qwen(num_blocks=100000)
+    sp = synthetic.config_shared_prefix(poison=False)
+    for ps, sb in ((3, 0), (0, 36), (24, 18), (1, 1000)):
+        plan = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
+        pa.pa_plan_shared_prefix(g, plan, sp.qo_len, sp.kv_len, sp.block_tables, 256, prefix_splits=ps,
+                                 split_blocks=sb)
+        if ps:
+            assert plan.prefix_splits == ps
+        if sb:
+            assert plan.split_blocks == min(sb, 512)
+            longest = max(-(-int(L) // 16) - 384 for L in sp.kv_len)
+            assert plan.max_splits == -(-longest // plan.split_blocks)
+    for ps, sb in ((-1, 0), (65, 0), (0, -3)):
+        plan = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
+        before = bytes(plan)
+        with pytest.raises(pa.PaError) as e:
+            pa.pa_plan_shared_prefix(g, plan, sp.qo_len, sp.kv_len, sp.block_tables, 256, prefix_splits=ps,
+                                     split_blocks=sb)
+        assert e.value.code == -2 and bytes(plan) == before
 
 
 def test_plan_errors():

@@ -112,6 +112,13 @@ def test_sweep_decode_layer(batch, long_only):
     check(synthetic.config_sweep_decode(batch, layer=batch % 36, long_only=long_only))
 
 
+@pytest.mark.parametrize("batch", [8, 16, 32, 64])
+def test_sweep_decode_layer_cascade(batch):
+    """The sweep's layers with half the rows sharing a 6144-token prefix, on the
+    one-launch cascade with the planner's choice of prefix splits and split length."""
+    check(synthetic.config_sweep_decode(batch, layer=(batch + 1) % 36), cascade=True, label="cascade")
+
+
 def test_prompt_chunks_match_oracle_and_one_shot():
     one, chunks = synthetic.prompt_chunks(seed=5, prompt_len=2048, chunk=512, num_blocks=256)
     o_one, l_one = check(one, label="one-shot")
