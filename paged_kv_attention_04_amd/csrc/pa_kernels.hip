@@ -1255,6 +1255,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         // keys any token of this tile can see: 0 .. ctx + last token of the tile
         kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * pa::kPrefillQ));
     }
+    // Row groups with no valid row skip the products (their wavefronts still copy their
+    // block of every step and meet every barrier).
+    const int valid_rows = kCascade ? 4 * grp_count : min(kPfRows, 4 * (qlen - qt * pa::kPrefillQ));
+    const bool active = 32 * rg < valid_rows;
     const int nsteps_tile = (kv_hi + kPfKeys - 1) / kPfKeys;
     const int s_begin = split * nsteps_tile / p.splits;
     const int nsteps = (split + 1) * nsteps_tile / p.splits - s_begin;
@@ -1392,6 +1396,13 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         // the compiler from moving any memory access across; register-only work of the
         // previous step may still drift past it.
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (!active) {
+            int id = next_id;
+            asm volatile("" : "+v"(id));
+            stage(BufSel<B ^ 1>{}, step_at(it + 1), checked(__builtin_amdgcn_readfirstlane(id)));
+            next_id = table_entry(step_at(it + 2));
+            return;
+        }
         bf16x8 kop[4][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -1468,24 +1479,37 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     if constexpr (kCascade) {
         // this split's normalised partial and log2-sum-exp per (request, query head), in
         // the decode kernel's partial layout, with agent-scope stores: the decode
-        // workgroups of the same launch merge them
+        // workgroups of the same launch merge them.  The kh = 0 wavefronts first stage
+        // their rows in LDS ([row][dim], rows 0..63 in k_tile0, 64..127 in v_tile0, each
+        // row's 16-byte chunks XOR-swizzled by the row), so that the workgroup then writes
+        // every row as contiguous 256-byte pieces; written straight from the MFMA layout,
+        // each store instruction would scatter 16-byte pieces over 16 rows.
+        const int nrows_valid = 4 * grp_count;
+        auto stage_at = [&](int row, int chunk) __attribute__((always_inline)) {
+            u32x4* base = row < 64 ? k_tile0 : v_tile0;
+            return base + (row & 63) * (kHeadDim / 4) + (chunk ^ (row & 31));
+        };
+        __syncthreads();                        // the key-half exchange above is done with k_tile0 / v_tile0
         if (kh == 0) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 const int rho = 32 * rg + 16 * rb + row16;
-                if ((rho >> 2) >= grp_count)
-                    continue;
-                const int64_t pi =
-                    ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * p.num_q_heads + head0 + (rho & 3);
-                float* dst = p.px_part_o + pi * kHeadDim + 4 * kslice;
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        store_agent(dst + 16 * db + e, oacc[rb][db][e]);
-                if (kslice == 0)
+                    *stage_at(rho, 4 * db + kslice) = __builtin_bit_cast(u32x4, oacc[rb][db]);
+                if (kslice == 0 && rho < nrows_valid) {
+                    const int64_t pi =
+                        ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * p.num_q_heads + head0 + (rho & 3);
                     store_agent(p.px_part_lse + pi, lse2[rb]);
+                }
             }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nrows_valid * kHeadDim; idx += 64 * kPfWaves) {
+            const int rho = idx / kHeadDim, d = idx % kHeadDim;
+            const int64_t pi = ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * p.num_q_heads + head0 + (rho & 3);
+            const float v = reinterpret_cast<const float*>(stage_at(rho, d >> 2))[d & 3];
+            store_agent(p.px_part_o + pi * kHeadDim + d, v);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
