@@ -368,6 +368,9 @@ pa_status pa_allocator_sync(pa_block_allocator* allocator);
 /* Compute-unit count of a HIP device (for pa_plan).  PA_ERR_HIP on failure. */
 pa_status pa_query_num_cus(int32_t device, int32_t* num_cus);
 
+/* sizeof(pa_plan_t) as this library was compiled, for bindings that mirror the struct. */
+size_t pa_plan_struct_bytes(void);
+
 /* Static text for a status code. */
 const char* pa_status_string(pa_status status);
 

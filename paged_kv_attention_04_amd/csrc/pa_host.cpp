@@ -463,3 +463,5 @@ extern "C" const char* pa_status_string(pa_status s)
     }
     return "unknown status";
 }
+
+extern "C" size_t pa_plan_struct_bytes(void) { return sizeof(pa_plan_t); }
