@@ -1,7 +1,9 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
-A step is one pass of the path over one layer's batch: pa_plan (host) ->
-pa_append_kv -> pa_attention_batch.  The headline workload is the Qwen3-8B
+A step is one pass of the path over one layer's batch: pa_plan (host), then the
+append of the new K/V and attention -- pa_append_kv -> pa_attention_batch, or in the
+fused form the bench times, pa_decode_step (decode rows) / pa_attention_step (any
+batch), which do the append inside the attention launches.  The headline workload is the Qwen3-8B
 single-layer decode step (32 requests, kv_len = 2048 + U[0,255], 32 query / 8 KV
 heads, head_dim 128, 16-token blocks, bf16); its value is algorithmic HBM bytes per
 second of the whole step.  The mixed continuous batch (one 512-token prefill chunk at
@@ -130,8 +132,9 @@ class Stepper:
         if self.fused:
             if not attention_only:
                 self.plan = self.make_plan()
-            pa.pa_decode_step(self.g, self.plan, self.q, kp, vp, self.kn, self.vn, self.bt, self.qo_indptr, self.kv,
-                              self.out, self.lse, self.ws)
+            step = pa.pa_attention_step if self.plan.num_prefill_rows > 0 else pa.pa_decode_step
+            step(self.g, self.plan, self.q, kp, vp, self.kn, self.vn, self.bt, self.qo_indptr, self.kv,
+                 self.out, self.lse, self.ws)
             return
         if not attention_only:
             self.plan = self.make_plan()
@@ -269,8 +272,9 @@ class LayerStack:
             self.plan = self.make_plan()
         for kp, vp in self.pools:
             if fused:
-                pa.pa_decode_step(self.g, self.plan, self.q, kp, vp, self.kn, self.vn, self.bt, self.qo_indptr,
-                                  self.kv, self.out, self.lse, self.ws)
+                step = pa.pa_attention_step if self.plan.num_prefill_rows > 0 else pa.pa_decode_step
+                step(self.g, self.plan, self.q, kp, vp, self.kn, self.vn, self.bt, self.qo_indptr, self.kv, self.out,
+                     self.lse, self.ws)
                 continue
             pa.pa_append_kv(self.g, kp, vp, self.kn, self.vn, self.sm)
             pa.pa_attention_batch(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
@@ -335,13 +339,16 @@ def sweep36(steps: int = 20, warmup: int = 5) -> dict:
     stacks = [LayerStack(c) for c in chunks]
     flops = sum(prefill_flops(c) for c in chunks) * SWEEP_LAYERS
 
-    def prompt():
+    def prompt(fused):
         for st in stacks:
-            st.step(replan=True)
-    t = median_step_seconds(prompt, max(steps // 2, 5), 2)
+            st.step(replan=True, fused=fused)
+    t_sep = median_step_seconds(lambda: prompt(False), max(steps // 2, 5), 2)
+    t = median_step_seconds(lambda: prompt(True), max(steps // 2, 5), 2)
     res["prefill_2k_in_4x512"] = {"ms": round(t * 1e3, 4), "tflops": round(flops / t / 1e12, 1),
                                   "frac_of_bf16_mfma_peak": round(flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                                  "tokens_per_s": round(2048 / t, 1)}
+                                  "tokens_per_s": round(2048 / t, 1),
+                                  "step": "per chunk and layer: pa_plan + pa_attention_step (append fused)",
+                                  "ms_append_then_attention": round(t_sep * 1e3, 4)}
     return res
 
 
@@ -474,10 +481,13 @@ def main(argv=None):
 
     # mixed continuous batch: tokens per second of a whole step
     wm = synthetic.config_mixed(poison=False)
-    sm = Stepper(wm, args.copies)
+    sm = Stepper(wm, args.copies, fused=True)
     sec_m = float(np.median([time_steps(sm, args.steps, args.warmup) for _ in range(3)]))   # median of 3 runs
     t_m = event_time(sm, max(args.steps, 50))
     del sm
+    sm2 = Stepper(wm, args.copies)                 # the same step as pa_append_kv + pa_attention_batch
+    sec_m2 = float(np.median([time_steps(sm2, args.steps, args.warmup) for _ in range(3)]))
+    del sm2
 
     # shared-prefix decode (16 requests share 6144 tokens), plain and with the cascade plan
     ws3 = synthetic.config_shared_prefix(poison=False)
@@ -569,8 +579,10 @@ def main(argv=None):
                      "kernel": "pa_decode_split<bf16, fused append> (the one launch of the step)",
                      "avg_us": round(t_attn * 1e6, 3), "bytes_per_launch": ab["step"]},
         "mixed_batch": {"workload": "1 prefill row (512 tokens at offset 4096) + 31 decode rows, 543 new tokens",
+                        "step": "pa_plan + pa_attention_step (append fused into the prefill and decode launches)",
                         "tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
-                        "attention_us": round(t_m * 1e6, 3)},
+                        "launches_us": round(t_m * 1e6, 3),
+                        "append_then_attention_ms_per_step": round(sec_m2 * 1e3, 5)},
         "shared_prefix": shared,
         "q8_0_decode": q8,
         "spec_verify": spec,

@@ -227,6 +227,25 @@ pa_status pa_decode_step(const pa_geometry* geometry, const pa_plan_t* plan, con
                          float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One step of a layer for any batch (decode rows and chunked-prefill rows) with the
+ * append fused into the attention launches: row r's qo_len new K / V rows (k_new /
+ * v_new rows qo_indptr[r] .. qo_indptr[r + 1] - 1, bf16 [total_q][num_kv_heads]
+ * [head_dim]) are written to the slots of positions kv_len[r] - qo_len .. kv_len[r] - 1
+ * through block_tables, and attention reads them from k_new / v_new directly.  The
+ * result equals pa_append_kv (with those slots) followed by pa_attention_batch, in the
+ * launches of pa_attention_batch alone (book section 8.3.1: a token's KV goes to a slot
+ * of the block its table names; the Perplexity blog orders the per-layer append before
+ * attention).  The slots a step writes must be distinct and in blocks no other row of the
+ * batch reads (copy-on-write of shared blocks is the caller's, as for pa_append_kv).
+ * Arguments and errors as for pa_attention_batch; PA_ERR_NULL for missing k_new / v_new;
+ * PA_VALIDATE=1 also checks that no two new tokens share a slot.
+ */
+pa_status pa_attention_step(const pa_geometry* geometry, const pa_plan_t* plan, const void* q, void* k_pool,
+                            void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
+                            int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Host-side content checks on host copies of a batch's arguments: 1 <= qo_len <=
  * kv_len, ceil(kv_len / block_size) <= max_blocks_per_req, and every table entry
  * a row reads names a block in [0, num_blocks).  Returns PA_OK, PA_ERR_NULL,

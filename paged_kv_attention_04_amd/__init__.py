@@ -80,6 +80,7 @@ def lib():
     L.pa_append_kv.argtypes = [G, P, P, P, P, P, i32, P]
     L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_decode_step.argtypes = [G, PL, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
+    L.pa_attention_step.argtypes = [G, PL, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_validate_batch.argtypes = [G, i32, P, P, P, i32, P]
     L.pa_validate_append.argtypes = [G, P, i32, P]
     L.pa_copy_blocks.argtypes = [G, P, P, P, P, i32, P]
@@ -209,6 +210,21 @@ def pa_decode_step(geometry: Geometry, plan: Plan, q, k_pool, v_pool, k_new, v_n
     bf, i32 = _bf16_types(), (torch.int32,)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_decode_step", lib().pa_decode_step(
+        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(k_pool, bf, "k_pool"),
+        _dev_ptr(v_pool, bf, "v_pool"), _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"),
+        _dev_ptr(block_tables, i32, "block_tables"), int(block_tables.shape[1]), _dev_ptr(qo_indptr, i32, "qo_indptr"),
+        _dev_ptr(kv_len, i32, "kv_len"), _dev_ptr(out, bf, "out"), _dev_ptr(lse, (torch.float32,), "lse"),
+        _dev_ptr(workspace, name="workspace"), ws_bytes, _stream_handle(stream)))
+
+
+def pa_attention_step(geometry: Geometry, plan: Plan, q, k_pool, v_pool, k_new, v_new, block_tables, qo_indptr,
+                      kv_len, out, lse, workspace=None, stream=None) -> None:
+    """Any batch (decode and chunked-prefill rows): append each row's new K/V (positions
+    kv_len - qo_len .. kv_len - 1) and attend, in the attention launches alone."""
+    import torch
+    bf, i32 = _bf16_types(), (torch.int32,)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_attention_step", lib().pa_attention_step(
         ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(k_pool, bf, "k_pool"),
         _dev_ptr(v_pool, bf, "v_pool"), _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"),
         _dev_ptr(block_tables, i32, "block_tables"), int(block_tables.shape[1]), _dev_ptr(qo_indptr, i32, "qo_indptr"),

@@ -975,6 +975,11 @@ struct PrefillParams {
     int32_t group_blocks[PA_MAX_PREFIX_GROUPS];
     float* px_part_o;           // [num_reqs][splits][Hq][head_dim]
     float* px_part_lse;         // [num_reqs][splits][Hq]
+    // fused append (chunked-prefill rows of a step): row r's new tokens, k_new / v_new
+    // rows qo_indptr[r] .., are written to the slots of positions kv_len - qo_len .. and
+    // read from these rows directly
+    const uint16_t* k_new;
+    const uint16_t* v_new;
 };
 
 constexpr int kPfKeys = pa::kPrefillKeys;  // keys per step: eight 16-token blocks
@@ -1203,7 +1208,7 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* v
 // eight keys of chunk c are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of the chunk:
 // exactly S^T values it holds; the V^T operand is read with the same key order by two
 // transposed LDS reads, and a contraction does not care how its index is permuted.
-template <bool kCascade>
+template <bool kCascade, bool kFused = false>
 __device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
                                                                    int bid)
 {
@@ -1264,6 +1269,26 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     const int nsteps = (split + 1) * nsteps_tile / p.splits - s_begin;
 
     const int row16 = lane & 15, kslice = lane >> 4;
+    if constexpr (kFused) {
+        // Fused append: split 0 of each (tile, KV head) writes the tile's new tokens of this
+        // KV head into their slots.  Every workgroup of the launch reads new positions from
+        // k_new / v_new (see `stage`), so nothing here waits for these stores.
+        if (split == 0 && !bad_row) {
+            const int tl = qt * pa::kPrefillQ + (tid >> 4), c = tid & 15;      // 32 tokens x 16 chunks
+            if (tl < qlen) {
+                const int pos = ctx + tl;
+                const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
+                if (phys >= 0 && phys < p.num_blocks) {
+                    const int64_t dst = (((int64_t)phys * p.num_kv_heads + kvh) * kBlock + pos % kBlock) * kHeadDim + c * 8;
+                    const int64_t src = ((int64_t)(q0 + tl) * p.num_kv_heads + kvh) * kHeadDim + c * 8;
+                    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + dst) =
+                        *reinterpret_cast<const u32x4*>(p.k_new + src);
+                    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + dst) =
+                        *reinterpret_cast<const u32x4*>(p.v_new + src);
+                }
+            }
+        }
+    }
     // this lane's two rows (row blocks rb = 0, 1)
     int qpos[2];
     bf16x8 qop[2][4];
@@ -1332,11 +1357,23 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-            __builtin_amdgcn_global_load_lds(p.k_pool + base + off,
-                                             (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16],
+            const uint16_t* ks = p.k_pool + base + off;
+            const uint16_t* vs = p.v_pool + base + off;
+            if constexpr (kFused) {
+                // a position of this chunk (past kv_len: the chunk's last token, so that
+                // every staged value is finite) comes from the new rows; only blocks that
+                // reach the chunk look
+                const int pos = s * kPfKeys + 16 * wave + 4 * i + (lane >> 4);
+                if (s * kPfKeys + 16 * wave + kBlock > ctx && pos >= ctx) {
+                    const int64_t src = ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
+                                        (cp_off[i] & (kHeadDim - 1));
+                    ks = p.k_new + src;
+                    vs = p.v_new + src;
+                }
+            }
+            __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16],
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds(p.v_pool + base + off,
-                                             (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16],
+            __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16],
                                              16, 0, 0);
         }
     };
@@ -1678,9 +1715,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     }
     write_out(oacc, lse2);
 }
+template <bool kFused>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
 {
-    prefill_body<false>(p, DecodeParams{}, blockIdx.x);
+    prefill_body<false, kFused>(p, DecodeParams{}, blockIdx.x);
 }
 
 static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
@@ -1899,13 +1937,13 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         vs = pa_validate_batch(g, R, qo.data(), kvl.data(), bt.data(), max_blocks_per_req, nullptr);
         if (vs != PA_OK)
             return vs;
-        if (fused) {            // the slots the fused append writes: position kv_len - 1 of each row
-            std::vector<int32_t> slots(R);
-            for (int32_t r = 0; r < R; ++r) {
-                const int32_t pos = kvl[r] - 1;
-                slots[r] = bt[(size_t)r * max_blocks_per_req + pos / kBlock] * kBlock + pos % kBlock;
-            }
-            vs = pa_validate_append(g, slots.data(), R, nullptr);
+        if (fused) {            // the slots the fused append writes: positions kv_len - qo_len .. kv_len - 1
+            std::vector<int32_t> slots;
+            slots.reserve((size_t)plan->total_q);
+            for (int32_t r = 0; r < R; ++r)
+                for (int32_t pos = kvl[r] - qo[r]; pos < kvl[r]; ++pos)
+                    slots.push_back(bt[(size_t)r * max_blocks_per_req + pos / kBlock] * kBlock + pos % kBlock);
+            vs = pa_validate_append(g, slots.data(), (int32_t)slots.size(), nullptr);
             if (vs != PA_OK)
                 return vs;
         }
@@ -1958,7 +1996,12 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads * plan->prefill_splits;
         if (grid > INT32_MAX)
             return PA_ERR_SHAPE;
-        hipLaunchKernelGGL(pa_prefill_tile, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        pp.k_new = static_cast<const uint16_t*>(k_new);
+        pp.v_new = static_cast<const uint16_t*>(v_new);
+        if (fused)
+            hipLaunchKernelGGL(pa_prefill_tile<true>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        else
+            hipLaunchKernelGGL(pa_prefill_tile<false>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
@@ -2054,6 +2097,19 @@ extern "C" pa_status pa_decode_step(const pa_geometry* g, const pa_plan_t* plan,
         return PA_ERR_NULL;
     if (plan->num_prefill_rows > 0 || plan->prefill_tiles > 0)
         return PA_ERR_UNSUPPORTED;                 // decode rows only
+    if (plan->num_reqs > 0 && plan->total_q > 0 && (!k_new || !v_new))
+        return PA_ERR_NULL;
+    return attention_batch(false, g, plan, q, k_pool, v_pool, block_tables, max_blocks_per_req, qo_indptr, kv_len,
+                           out, lse, workspace, workspace_bytes, stream, k_new, v_new);
+}
+
+extern "C" pa_status pa_attention_step(const pa_geometry* g, const pa_plan_t* plan, const void* q, void* k_pool,
+                                       void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
+                                       int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                       void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
     if (plan->num_reqs > 0 && plan->total_q > 0 && (!k_new || !v_new))
         return PA_ERR_NULL;
     return attention_batch(false, g, plan, q, k_pool, v_pool, block_tables, max_blocks_per_req, qo_indptr, kv_len,

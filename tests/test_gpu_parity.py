@@ -602,6 +602,61 @@ def test_fused_decode_step_matches_append_then_attention(case):
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
 
+def _attention_step_gpu(wl, prefill_splits=0, cascade=False):
+    """pa_attention_step on device copies of the workload; returns host (k_pool, v_pool, out, lse)."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256, 0, prefill_splits)
+    if cascade:
+        pa.pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables)
+        assert plan.num_prefix_groups >= 1
+    kp, vp = pa.to_device(wl.k_pool), pa.to_device(wl.v_pool)
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    pa.pa_attention_step(g, plan, pa.to_device(wl.q), kp, vp, pa.to_device(wl.k_new), pa.to_device(wl.v_new),
+                         pa.to_device(wl.block_tables), pa.to_device(wl.qo_indptr), pa.to_device(wl.kv_len), out, lse,
+                         pa.workspace_for(plan))
+    torch.cuda.synchronize()
+    return (kp.cpu().numpy().view(np.uint16), vp.cpu().numpy().view(np.uint16), out.cpu().numpy().view(np.uint16),
+            lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", ["tiny_mixed", "mixed", "chunk_at_0", "chunk_at_1536", "spec", "psplit3",
+                                  "cascade_mixed"])
+def test_fused_attention_step_matches_append_then_attention(case):
+    """Any batch with the append fused into the attention launches (chunk rows read their
+    new tokens from the new rows, one workgroup per tile and KV head writes them): the
+    pools the oracle's append gives, outputs within tolerance of the oracle, and the same
+    output bits as pa_append_kv followed by pa_attention_batch on the GPU."""
+    psplit = 3 if case == "psplit3" else 0
+    cascade = case == "cascade_mixed"
+    chunks = None
+    if case.startswith("chunk_at"):
+        _, chunks = synthetic.prompt_chunks(seed=5, prompt_len=2048, chunk=512, num_blocks=256)
+    wl = {"tiny_mixed": lambda: synthetic.build("fused_mixed", 48, 8, 2, qo_len=[1, 40], kv_len=[20, 100],
+                                                num_blocks=32),
+          "mixed": lambda: synthetic.config_mixed(),
+          "chunk_at_0": lambda: chunks[0],
+          "chunk_at_1536": lambda: chunks[3],
+          "spec": lambda: synthetic.build("spec_verify_fused", 93, 32, 8, qo_len=[8] * 16, kv_len=[2048 + 8] * 16,
+                                          num_blocks=16 * 130 + 32),
+          "psplit3": lambda: synthetic.build("fused_psplit", 49, 32, 8, qo_len=[1, 40, 1, 70, 2], kv_len=[300, 500, 17, 70, 33],
+                                             num_blocks=200),
+          "cascade_mixed": lambda: synthetic.build("fused_cascade_mixed", 50, 32, 8, qo_len=[1, 1, 1, 1, 33],
+                                                   kv_len=[700, 820, 990, 640, 900], num_blocks=400,
+                                                   shared_prefix_blocks=30)}[case]()
+    print(f"[gpu] fused attention step {case} R={wl.num_reqs} total_q={wl.total_q}", flush=True)
+    kp, vp, out, lse = _attention_step_gpu(wl, psplit, cascade)
+    okp, ovp, ref = oracle.run_workload(wl)
+    assert np.array_equal(kp, okp) and np.array_equal(vp, ovp)
+    eo, el = _errors(out, lse, ref)
+    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+    _, _, out2, lse2 = _run_gpu(wl, 0, psplit, cascade=cascade)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
 def test_fused_decode_step_rejects_chunk_rows():
     import paged_kv_attention_04_amd as pa
     wl = synthetic.build("fused_mixed", 48, 8, 2, qo_len=[1, 40], kv_len=[20, 100], num_blocks=32)
