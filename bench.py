@@ -14,7 +14,7 @@ Each step reads a different copy of the KV pools (the copies stand for different
 layers), so no step finds the previous step's KV in the 256 MB last-level cache.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --kernel-only decode|decode_q8|mixed|shared|prefill   # attention launches only, for rocprofv3
+    python bench.py --kernel-only decode|decode_q8|mixed|mixed_fused|shared|prefill   # attention launches only, for rocprofv3
     python bench.py --summarize DIR [--title T]          # rocprofv3 CSV output -> profile text
 """
 from __future__ import annotations
@@ -364,9 +364,10 @@ def kernel_only(which: str, reps: int):
     wl = {"decode": lambda: synthetic.config_decode(poison=False),
           "decode_q8": lambda: synthetic.config_decode_q8(poison=False),
           "mixed": lambda: synthetic.config_mixed(poison=False),
+          "mixed_fused": lambda: synthetic.config_mixed(poison=False),
           "shared": lambda: synthetic.config_shared_prefix(poison=False),
           "prefill": prefill_only_workload}[which]()
-    st = Stepper(wl, 4, cascade=which == "shared", fused=which == "decode")
+    st = Stepper(wl, 4, cascade=which == "shared", fused=which in ("decode", "mixed_fused"))
     src = torch.empty(CALIBRATION_COPY_BYTES // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)                                           # calibration: reads and writes 256 MiB
@@ -443,7 +444,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 36-layer sweep")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "shared", "prefill"])
+    ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "mixed_fused", "shared", "prefill"])
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--summarize")
     ap.add_argument("--title", default="rocprofv3 summary")

@@ -1269,26 +1269,6 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     const int nsteps = (split + 1) * nsteps_tile / p.splits - s_begin;
 
     const int row16 = lane & 15, kslice = lane >> 4;
-    if constexpr (kFused) {
-        // Fused append: split 0 of each (tile, KV head) writes the tile's new tokens of this
-        // KV head into their slots.  Every workgroup of the launch reads new positions from
-        // k_new / v_new (see `stage`), so nothing here waits for these stores.
-        if (split == 0 && !bad_row) {
-            const int tl = qt * pa::kPrefillQ + (tid >> 4), c = tid & 15;      // 32 tokens x 16 chunks
-            if (tl < qlen) {
-                const int pos = ctx + tl;
-                const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
-                if (phys >= 0 && phys < p.num_blocks) {
-                    const int64_t dst = (((int64_t)phys * p.num_kv_heads + kvh) * kBlock + pos % kBlock) * kHeadDim + c * 8;
-                    const int64_t src = ((int64_t)(q0 + tl) * p.num_kv_heads + kvh) * kHeadDim + c * 8;
-                    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + dst) =
-                        *reinterpret_cast<const u32x4*>(p.k_new + src);
-                    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + dst) =
-                        *reinterpret_cast<const u32x4*>(p.v_new + src);
-                }
-            }
-        }
-    }
     // this lane's two rows (row blocks rb = 0, 1)
     int qpos[2];
     bf16x8 qop[2][4];
@@ -1354,26 +1334,36 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         u32x4* vd = decltype(sel)::value == 0 ? v_tile0 : v_tile1;
         const int64_t base = (int64_t)id * blk_stride + kvh_off;
         const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
+        if constexpr (kFused) {
+            // A block that reaches this chunk takes the chunk's positions from the new rows
+            // (past kv_len: the chunk's last token, so that every staged value is finite).
+            // The test is the same for the whole wavefront, and other blocks take the plain
+            // copies below.
+            if (s * kPfKeys + 16 * wave + kBlock > ctx) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = s * kPfKeys + 16 * wave + 4 * i + (lane >> 4);
+                    const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
+                    const int64_t src = ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
+                                        (cp_off[i] & (kHeadDim - 1));
+                    const uint16_t* ks = pos >= ctx ? p.k_new + src : p.k_pool + base + off;
+                    const uint16_t* vs = pos >= ctx ? p.v_new + src : p.v_pool + base + off;
+                    __builtin_amdgcn_global_load_lds(
+                        ks, (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16], 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(
+                        vs, (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16], 16, 0, 0);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-            const uint16_t* ks = p.k_pool + base + off;
-            const uint16_t* vs = p.v_pool + base + off;
-            if constexpr (kFused) {
-                // a position of this chunk (past kv_len: the chunk's last token, so that
-                // every staged value is finite) comes from the new rows; only blocks that
-                // reach the chunk look
-                const int pos = s * kPfKeys + 16 * wave + 4 * i + (lane >> 4);
-                if (s * kPfKeys + 16 * wave + kBlock > ctx && pos >= ctx) {
-                    const int64_t src = ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
-                                        (cp_off[i] & (kHeadDim - 1));
-                    ks = p.k_new + src;
-                    vs = p.v_new + src;
-                }
-            }
-            __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16],
+            __builtin_amdgcn_global_load_lds(p.k_pool + base + off,
+                                             (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16],
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16],
+            __builtin_amdgcn_global_load_lds(p.v_pool + base + off,
+                                             (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16],
                                              16, 0, 0);
         }
     };
@@ -1478,6 +1468,26 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     run(std::integral_constant<bool, true>{}, n_plain, nsteps);
     wait_vmcnt<0>();                           // the last step's spare copy
 
+    // Fused append: split 0 of each (tile, KV head) writes the tile's new tokens of this KV
+    // head into their slots (every workgroup of the launch reads new positions from k_new /
+    // v_new, see `stage`).  The rows are loaded here and stored after the key-half merge,
+    // so that their load latency hides behind it.
+    u32x4 new_k = u32x4{0u, 0u, 0u, 0u}, new_v = new_k;
+    int64_t new_dst = -1;
+    if constexpr (kFused) {
+        const int tl = qt * pa::kPrefillQ + (tid >> 4), c = tid & 15;          // 32 tokens x 16 chunks
+        if (split == 0 && !bad_row && tl < qlen) {
+            const int pos = ctx + tl;
+            const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
+            if (phys >= 0 && phys < p.num_blocks) {
+                new_dst = (((int64_t)phys * p.num_kv_heads + kvh) * kBlock + pos % kBlock) * kHeadDim + c * 8;
+                const int64_t src = ((int64_t)(q0 + tl) * p.num_kv_heads + kvh) * kHeadDim + c * 8;
+                new_k = *reinterpret_cast<const u32x4*>(p.k_new + src);
+                new_v = *reinterpret_cast<const u32x4*>(p.v_new + src);
+            }
+        }
+    }
+
     // merge the two key halves: the kh = 1 wavefronts hand (m, lane-partial l, O^T) to the
     // kh = 0 wavefront with the same rows, in the lanes' own layout
     __syncthreads();
@@ -1493,6 +1503,12 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         }
     }
     bad = __syncthreads_or(bad);
+    if constexpr (kFused) {
+        if (new_dst >= 0) {
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + new_dst) = new_k;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + new_dst) = new_v;
+        }
+    }
     const float nan = __builtin_nanf("");
     float lse2[2] = {-INFINITY, -INFINITY};     // log2-sum-exp of this workgroup's keys per row
     if (kh == 0) {
