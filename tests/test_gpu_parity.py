@@ -657,6 +657,35 @@ def test_fused_attention_step_matches_append_then_attention(case):
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
 
+def test_validate_mode_attention_step(monkeypatch):
+    """With PA_VALIDATE=1 pa_attention_step checks the slots its fused append writes,
+    chunk rows included: a valid mixed batch gives the same bytes as without the checks,
+    and tables that send a chunk token and another row's new token to one slot return
+    PA_ERR_RANGE with nothing launched."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    wl = synthetic.build("validate_step", 51, 8, 2, qo_len=[1, 40, 3], kv_len=[20, 100, 35], num_blocks=40,
+                         poison=False)
+    plain = _attention_step_gpu(wl)
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    checked = _attention_step_gpu(wl)
+    assert all(np.array_equal(a, b) for a, b in zip(plain, checked))
+    g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len)
+    bad_bt = wl.block_tables.copy()
+    bad_bt[2, 2] = bad_bt[1, 6]          # row 2's new positions 32..34 land on row 1's positions 96..98
+    kp, vp = pa.to_device(wl.k_pool), pa.to_device(wl.v_pool)
+    before = kp.clone()
+    out = torch.zeros((wl.total_q, wl.num_q_heads, 128), dtype=torch.int16, device="cuda")
+    lse = torch.zeros((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    with pytest.raises(pa.PaError, match="RANGE"):
+        pa.pa_attention_step(g, plan, pa.to_device(wl.q), kp, vp, pa.to_device(wl.k_new), pa.to_device(wl.v_new),
+                             pa.to_device(bad_bt), pa.to_device(wl.qo_indptr), pa.to_device(wl.kv_len), out, lse,
+                             pa.workspace_for(plan))
+    torch.cuda.synchronize()
+    assert torch.equal(kp, before) and not out.any()   # nothing was launched
+
+
 def test_fused_decode_step_rejects_chunk_rows():
     import paged_kv_attention_04_amd as pa
     wl = synthetic.build("fused_mixed", 48, 8, 2, qo_len=[1, 40], kv_len=[20, 100], num_blocks=32)
