@@ -14,7 +14,8 @@ Each step reads a different copy of the KV pools (the copies stand for different
 layers), so no step finds the previous step's KV in the 256 MB last-level cache.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --kernel-only decode|decode_q8|mixed|mixed_fused|shared|prefill   # attention launches only, for rocprofv3
+    python bench.py --kernel-only decode|decode_q8|mixed|mixed_fused|mixed_q8|shared|shared_q8|prefill
+                                                   # attention launches only, for rocprofv3
     python bench.py --summarize DIR [--title T]          # rocprofv3 CSV output -> profile text
 """
 from __future__ import annotations
@@ -365,9 +366,11 @@ def kernel_only(which: str, reps: int):
           "decode_q8": lambda: synthetic.config_decode_q8(poison=False),
           "mixed": lambda: synthetic.config_mixed(poison=False),
           "mixed_fused": lambda: synthetic.config_mixed(poison=False),
+          "mixed_q8": lambda: synthetic.config_mixed_q8(poison=False),
+          "shared_q8": lambda: synthetic.config_shared_prefix_q8(poison=False),
           "shared": lambda: synthetic.config_shared_prefix(poison=False),
           "prefill": prefill_only_workload}[which]()
-    st = Stepper(wl, 4, cascade=which == "shared", fused=which in ("decode", "mixed_fused"))
+    st = Stepper(wl, 4, cascade=which in ("shared", "shared_q8"), fused=which in ("decode", "mixed_fused"))
     src = torch.empty(CALIBRATION_COPY_BYTES // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)                                           # calibration: reads and writes 256 MiB
@@ -444,7 +447,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 36-layer sweep")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "mixed_fused", "shared", "prefill"])
+    ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "mixed_fused", "mixed_q8", "shared",
+                                              "shared_q8", "prefill"])
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--summarize")
     ap.add_argument("--title", default="rocprofv3 summary")
@@ -532,6 +536,24 @@ def main(argv=None):
           "predicted_saving_us": round(predicted * 1e6, 3),
           "measured_saving_us": round((t_plain - t_q) * 1e6, 3),
           "implied_conversion_us": round((predicted - (t_plain - t_q)) * 1e6, 3)}
+    # the mixed batch on a q8_0 pool: the append quantises in its own launch, then the chunk
+    # row runs the matrix-unit tile over codes and the decode rows the q8_0 decode kernel
+    wmq = synthetic.config_mixed_q8(poison=False)
+    smq = Stepper(wmq, args.copies)
+    sec_mq = time_steps(smq, args.steps, args.warmup)
+    t_mq = event_time(smq, max(args.steps // 2, 50))
+    del smq
+    q8["mixed_batch"] = {"workload": "1 prefill row (512 tokens at offset 4096) + 31 decode rows on a q8_0 pool",
+                         "step": "pa_plan + pa_append_kv_q8 + pa_attention_batch_q8",
+                         "tokens_per_s": round(wmq.total_q / sec_mq, 1), "ms_per_step": round(sec_mq * 1e3, 5),
+                         "attention_launches_us": round(t_mq * 1e6, 3)}
+    wsq = synthetic.config_shared_prefix_q8(poison=False)
+    ssq = Stepper(wsq, 2, cascade=True)
+    time_steps(ssq, 10, 5, attention_only=True)
+    t_sq = event_time(ssq, max(args.steps // 2, 50))
+    q8["shared_prefix_cascade"] = {"workload": "the shared-prefix decode (16 rows, 384 shared blocks) on a q8_0 pool",
+                                   "attention_us": round(t_sq * 1e6, 3), "prefix_splits": ssq.plan.prefix_splits}
+    del ssq
 
     # speculative verification: 16 requests, 8 new tokens each at 8192 tokens of context
     # (small qo_len rows, served by the chunked-prefill path; K / V streaming dominates)

@@ -310,11 +310,16 @@ pa_status pa_append_kv_q8(const pa_geometry* geometry, void* kv_pool_q8, const v
                           const int32_t* slot_mapping, int32_t n_tokens, void* stream);
 
 /*
- * pa_attention_batch over a q8_0 pool, for batches of decode rows: the values are the
- * codes times their scales, and everything else (outputs, splits, workspace) is as for
- * pa_attention_batch.  Q is read as binary16, which holds every bf16 value of magnitude
- * in [2^-14, 65504] exactly.  Returns PA_ERR_UNSUPPORTED for a plan with rows of
- * qo_len > 1 or shared-prefix groups.
+ * pa_attention_batch over a q8_0 pool, for any batch pa_attention_batch takes (decode
+ * rows, chunked-prefill rows, shared-prefix groups from pa_plan_shared_prefix): the values
+ * are the codes times their scales, and everything else (outputs, splits, workspace) is
+ * as for pa_attention_batch.  Q is read as binary16, which holds every bf16 value of
+ * magnitude in [2^-14, 65504] exactly.  Decode rows take the codes and scales as they
+ * are; chunked-prefill rows and the shared blocks of a prefix group run on the matrix
+ * units with each value rounded once to binary16 (relative error at most 2^-11 of the
+ * value, so |code x scale| must stay within 65504) and the softmax weights rounded to
+ * binary16.  The append into a q8_0 pool is always its own launch (pa_append_kv_q8
+ * first).
  */
 pa_status pa_attention_batch_q8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q,
                                 const void* kv_pool_q8, const int32_t* block_tables, int32_t max_blocks_per_req,

@@ -455,6 +455,14 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
     const int head0 = kvh * kGroup;
     const int idx = threadIdx.x, h = idx / kHeadDim, d = idx & (kHeadDim - 1);
     const float nan = __builtin_nanf("");
+    // The partial buffers, held in vector registers so that picking a partial's buffer is
+    // a select; left to the compiler, each pick reloads the pointer from the kernel
+    // arguments and waits for that scalar load before the partial's loads can go out.
+    const float* dec_lse = p.part_lse;
+    const float* dec_o = p.part_o;
+    const float* pfx_lse = p.px_part_lse;
+    const float* pfx_o = p.px_part_o;
+    asm volatile("" : "+v"(dec_lse), "+v"(dec_o), "+v"(pfx_lse), "+v"(pfx_o));
     for (int c0 = 0; c0 < nrows; c0 += kChunk) {
         int rr[kChunk], ns[kChunk], tot[kChunk];
         int most = 0;
@@ -478,8 +486,8 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
                                            ? ((int64_t)rr[j] * p.max_splits + sidx) * p.num_q_heads + head0 + h
                                            : ((int64_t)rr[j] * p.prefix_splits + (sidx - ns[j])) * p.num_q_heads +
                                                  head0 + h;
-                    const float* lsrc = sidx < ns[j] ? p.part_lse : p.px_part_lse;
-                    const float* osrc = sidx < ns[j] ? p.part_o : p.px_part_o;
+                    const float* lsrc = sidx < ns[j] ? dec_lse : pfx_lse;
+                    const float* osrc = sidx < ns[j] ? dec_o : pfx_o;
                     ls[j][u] = tot[j] > 0 ? load_agent(lsrc + pi) : 0.f;
                     os[j][u] = tot[j] > 0 ? load_agent(osrc + pi * kHeadDim + d) : 0.f;
                 }
@@ -1187,6 +1195,129 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* v
 // hold the same rows.  Their two key halves are merged through LDS at the end, lane by
 // lane, by the log-sum-exp rule.
 //
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Round two floats to binary16 (nearest even) and pack them, low half first.
+__device__ inline uint32_t pack_f16(float a, float b)
+{
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(const bf16x8& a, const bf16x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+}
+
+// pf_step over a q8_0 pool.  The staged K and V tiles hold the codes as binary16 integers
+// (exact), Q is binary16, and the scales of the step's keys sit in LDS as floats,
+// [group][key] (ksc for K, vsc for V).  S^T is formed one 32-dim group (one k-slice of
+// the product) at a time: the group's codes times Q, exact products summed in fp32,
+// then weighted by each key's scale of that group, so the scores carry no rounding of
+// the stored values.  In PV the weights of the output dims of group g are the softmax
+// weights times the keys' V scales of group g, rounded to binary16.  The softmax
+// statistics are those of pf_step (same lazy rescaling; the denominators are summed
+// from the unrounded weights).
+template <bool kMask>
+__device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char* vt, const int (&v_addr)[8],
+                                           const float* ksc, const float* vsc, const bf16x8 (&qop)[2][4],
+                                           f32x4 (&oacc)[2][8], float (&m)[2], float (&lsum)[2], int key0, int kh,
+                                           int kslice, const int (&qpos)[2], int kv_hi, float scale_log2)
+{
+    const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+    // x[rb][4 kb + e] is the score of key key0 + 16 kb + 4 kslice + e for this lane's row
+    float x[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        f32x4 dk[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            dk[g] = *reinterpret_cast<const f32x4*>(ksc + g * kPfKeys + 64 * kh + 16 * kb + 4 * kslice);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            f32x4 acc = zero;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 part = mfma_f16(kop[kb][g], qop[rb][g], zero);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = fmaf(part[e], dk[g][e], acc[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[rb][4 * kb + e] = acc[e];
+        }
+    }
+    if constexpr (kMask) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + 16 * (i >> 2) + 4 * kslice + (i & 3);
+                x[rb][i] = (key > qpos[rb] || key >= kv_hi) ? -INFINITY : x[rb][i];
+            }
+    }
+    float lmax[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        float t = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            t = fmaxf(t, x[rb][i]);
+        lmax[rb] = t * scale_log2;
+    }
+    const bool raise = lmax[0] > m[0] + kRescaleSlack || lmax[1] > m[1] + kRescaleSlack;
+    if (__any(raise)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float t = fmaxf(lmax[rb], shfl_xor(lmax[rb], 16));
+            t = fmaxf(t, shfl_xor(t, 32));
+            if (t > m[rb] + kRescaleSlack) {
+                const float alpha = (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - t);
+                m[rb] = t;
+                lsum[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    oacc[rb][db] *= alpha;
+            }
+        }
+    }
+    const float nm[2] = {(m[0] == -INFINITY) ? 0.f : -m[0], (m[1] == -INFINITY) ? 0.f : -m[1]};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        bf16x8 vop[8];
+        pf_read_v(vt, v_addr, c, vop);
+        // this lane's keys of chunk c: 32 c + 4 kslice + 0..3, then 32 c + 16 + 4 kslice + 0..3
+        float pe[2][8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                pe[rb][i] = fast_exp2(fmaf(x[rb][8 * c + i], scale_log2, nm[rb]));
+                sum += pe[rb][i];
+            }
+            lsum[rb] += sum;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float* vs = vsc + g * kPfKeys + 64 * kh + 32 * c + 4 * kslice;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(vs);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(vs + 16);
+            const float dv[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const bf16x8 pg = __builtin_bit_cast(
+                    bf16x8, u32x4{pack_f16(pe[rb][0] * dv[0], pe[rb][1] * dv[1]), pack_f16(pe[rb][2] * dv[2], pe[rb][3] * dv[3]),
+                                  pack_f16(pe[rb][4] * dv[4], pe[rb][5] * dv[5]), pack_f16(pe[rb][6] * dv[6], pe[rb][7] * dv[7])});
+                oacc[rb][2 * g] = mfma_f16(vop[2 * g], pg, oacc[rb][2 * g]);
+                oacc[rb][2 * g + 1] = mfma_f16(vop[2 * g + 1], pg, oacc[rb][2 * g + 1]);
+            }
+        }
+    }
+}
+
 // Key splits: the tile's causal key range, ceil(kv_hi / 128) steps, is cut into `splits`
 // contiguous step ranges, one workgroup each.  With one split the workgroup writes the
 // output; otherwise each writes its normalised partial and log2-sum-exp to the workspace
@@ -1208,7 +1339,14 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* v
 // eight keys of chunk c are {4j..4j+3} and {16+4j..16+4j+3} (j = l/16) of the chunk:
 // exactly S^T values it holds; the V^T operand is read with the same key order by two
 // transposed LDS reads, and a contraction does not care how its index is permuted.
-template <bool kCascade, bool kFused = false>
+//
+// q8_0 pool (kQ8): the copies go through registers instead.  Lane l of wavefront w loads
+// the 32 codes and the scale of group l % 4 of token l / 4 of its block (K and V) when the
+// step is staged; right before the next barrier it writes the codes as binary16 integers
+// (exact) to the same LDS places the bf16 copies use and the two scales as floats to a
+// [group][key] table beside the tiles.  The products then run on binary16 operands (Q
+// converted once, exact for bf16 values inside the binary16 range), see pf_step_q8.
+template <bool kCascade, bool kFused = false, bool kQ8 = false>
 __device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
                                                                    int bid)
 {
@@ -1219,6 +1357,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     __shared__ float x_m[4][2][64];     // key-half merge: running maxima of the kh = 1 wavefronts
     __shared__ float x_l[4][2][64];     // and their lane-partial denominators
     __shared__ int last_lds;
+    // q8_0: scales of the staged keys, [buffer pair][K, V][group][key]
+    __shared__ __attribute__((aligned(16))) float q8_sc[kQ8 ? 2 * 2 * 4 * kPfKeys : 4];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -1294,6 +1434,11 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             if (ok)
                 v = *reinterpret_cast<const u32x4*>(
                     p.q + ((int64_t)qidx * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + ks * 32 + kslice * 8);
+            if constexpr (kQ8) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = pack_f16(bf16_lo(v[j]), bf16_hi(v[j]));
+            }
             qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
@@ -1329,11 +1474,32 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         const int chunk = (lane & 15) ^ pf_swz(tok);      // pf_swz sees only the key's low four bits
         cp_off[i] = tok * kHeadDim + chunk * 8;            // token 0's offset is cp_off[i] % kHeadDim
     }
+    // q8_0 copies in flight: this lane's 32 K and 32 V codes (token q8_tok, group q8_grp of
+    // the wavefront's block) and the two scales
+    const int q8_tok = lane >> 2, q8_grp = lane & 3;
+    u32x4 q8k[2], q8v[2];
+    uint32_t q8ks = 0, q8vs = 0;
     auto stage = [&](auto sel, int s, int id) __attribute__((always_inline)) {
+        const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
+        if constexpr (kQ8) {
+            // slots past kv_len read token 0 of the block, so that every staged value is finite
+            const int t = q8_tok < valid ? q8_tok : 0;
+            const uint8_t* kt = reinterpret_cast<const uint8_t*>(p.k_pool) +
+                                ((int64_t)id * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);
+            const uint8_t* vt = kt + pa::kQ8TileBytes;
+            const int co = t * kHeadDim + q8_grp * pa::kQ8Group;
+            q8k[0] = *reinterpret_cast<const u32x4*>(kt + co);
+            q8k[1] = *reinterpret_cast<const u32x4*>(kt + co + 16);
+            q8v[0] = *reinterpret_cast<const u32x4*>(vt + co);
+            q8v[1] = *reinterpret_cast<const u32x4*>(vt + co + 16);
+            const int so = pa::kQ8CodeBytes + 2 * (t * (kHeadDim / pa::kQ8Group) + q8_grp);
+            q8ks = *reinterpret_cast<const uint16_t*>(kt + so);
+            q8vs = *reinterpret_cast<const uint16_t*>(vt + so);
+            return;
+        }
         u32x4* kd = decltype(sel)::value == 0 ? k_tile0 : k_tile1;
         u32x4* vd = decltype(sel)::value == 0 ? v_tile0 : v_tile1;
         const int64_t base = (int64_t)id * blk_stride + kvh_off;
-        const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
         if constexpr (kFused) {
             // A block that reaches this chunk takes the chunk's positions from the new rows
             // (past kv_len: the chunk's last token, so that every staged value is finite).
@@ -1365,6 +1531,34 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             __builtin_amdgcn_global_load_lds(p.v_pool + base + off,
                                              (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16],
                                              16, 0, 0);
+        }
+    };
+    // q8_0: the copies staged one step ago into buffer pair `sel` (whose previous contents
+    // every wavefront finished reading before the last barrier)
+    auto finish_q8 = [&](auto sel) __attribute__((always_inline)) {
+        if constexpr (kQ8) {
+            constexpr int B = decltype(sel)::value;
+            u32x4* kd = B == 0 ? k_tile0 : k_tile1;
+            u32x4* vd = B == 0 ? v_tile0 : v_tile1;
+            wait_vmcnt<0>();
+            const f16x2 bias = {(_Float16)kQ8Bias, (_Float16)kQ8Bias};
+            // codes 2 i, 2 i + 1 of word w as binary16 integers: (1152 + code) - 1152, exact
+            auto code2 = [&](uint32_t w, int i) __attribute__((always_inline)) {
+                const uint32_t c = q8_to_half2(w, w, i ? 0x0c030c02u : 0x0c010c00u);
+                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, c) - bias);
+            };
+            const int row = (16 * wave + q8_tok) * 16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {                  // chunk 4 q8_grp + j: dims 8 j .. 8 j + 7 of the group
+                const uint32_t k0 = q8k[j >> 1][2 * (j & 1)], k1 = q8k[j >> 1][2 * (j & 1) + 1];
+                const uint32_t v0 = q8v[j >> 1][2 * (j & 1)], v1 = q8v[j >> 1][2 * (j & 1) + 1];
+                const int slot = (4 * q8_grp + j) ^ pf_swz(q8_tok);
+                kd[row + slot] = u32x4{code2(k0, 0), code2(k0, 1), code2(k1, 0), code2(k1, 1)};
+                vd[row + slot] = u32x4{code2(v0, 0), code2(v0, 1), code2(v1, 0), code2(v1, 1)};
+            }
+            float* sc = q8_sc + B * (2 * 4 * kPfKeys) + q8_grp * kPfKeys + 16 * wave + q8_tok;
+            sc[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)q8ks);
+            sc[4 * kPfKeys] = (float)__builtin_bit_cast(_Float16, (uint16_t)q8vs);
         }
     };
     // LDS byte offsets of this lane's operand reads within a K or V tile.  K: key
@@ -1418,6 +1612,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         const char* kt = reinterpret_cast<const char*>(B == 0 ? k_tile0 : k_tile1);
         const char* vt = reinterpret_cast<const char*>(B == 0 ? v_tile0 : v_tile1);
         const int s = step_at(it);
+        finish_q8(sel);
         // This wavefront's copies of this step have landed and its LDS reads of the previous
         // step have returned; after the barrier everyone's have.  The memory clobber keeps
         // the compiler from moving any memory access across; register-only work of the
@@ -1447,8 +1642,14 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             stage(BufSel<B ^ 1>{}, step_at(it + 1), checked(__builtin_amdgcn_readfirstlane(id)));
             next_id = table_entry(step_at(it + 2));
         }
-        pf_step<decltype(msk)::value>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + 64 * kh, kslice, qpos, kv_hi,
-                                      p.scale_log2);
+        if constexpr (kQ8) {
+            const float* ksc = q8_sc + B * (2 * 4 * kPfKeys);
+            pf_step_q8<decltype(msk)::value>(kop, vt, v_addr, ksc, ksc + 4 * kPfKeys, qop, oacc, m, lsum,
+                                             s * kPfKeys + 64 * kh, kh, kslice, qpos, kv_hi, p.scale_log2);
+        } else {
+            pf_step<decltype(msk)::value>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + 64 * kh, kslice, qpos,
+                                          kv_hi, p.scale_log2);
+        }
     };
     // Steps alternate between the two buffer pairs; each loop is unrolled by two so that
     // every LDS access names its buffer statically.
@@ -1731,10 +1932,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     }
     write_out(oacc, lse2);
 }
-template <bool kFused>
+template <bool kFused, bool kQ8>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
 {
-    prefill_body<false, kFused>(p, DecodeParams{}, blockIdx.x);
+    prefill_body<false, kFused, kQ8>(p, DecodeParams{}, blockIdx.x);
 }
 
 static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
@@ -1744,14 +1945,14 @@ static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs bot
 // form), the rest are the decode workgroups.  The prefix workgroups come first in the
 // grid and wait for nothing; a (row, KV head) is finished by whichever of its decode
 // splits and prefix splits arrives last, so no workgroup ever waits for another.
-template <bool kFused>
+template <bool kQ8, bool kFused>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_cascade_decode(PrefillParams pp, DecodeParams dp,
                                                                  int32_t num_prefix_wgs)
 {
     if ((int32_t)blockIdx.x < num_prefix_wgs)
-        prefill_body<true>(pp, dp, blockIdx.x);
+        prefill_body<true, false, kQ8>(pp, dp, blockIdx.x);
     else
-        decode_body<false, kFused>(dp, blockIdx.x - num_prefix_wgs);
+        decode_body<kQ8, kFused>(dp, blockIdx.x - num_prefix_wgs);
 }
 
 
@@ -1899,8 +2100,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         return PA_ERR_NULL;
     if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
         return PA_ERR_UNSUPPORTED;
-    if (q8 && (plan->num_prefill_rows > 0 || plan->prefill_tiles > 0 || plan->num_prefix_groups > 0))
-        return PA_ERR_UNSUPPORTED;            // a q8_0 pool serves decode rows only
+    if (q8 && fused)
+        return PA_ERR_UNSUPPORTED;            // the append into a q8_0 pool is its own launch
     if (plan->num_reqs == 0 || plan->total_q == 0)
         return PA_OK;
     if (!q || !k_pool || !v_pool || !block_tables || !qo_indptr || !kv_len || !out || !lse)
@@ -2014,10 +2215,12 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             return PA_ERR_SHAPE;
         pp.k_new = static_cast<const uint16_t*>(k_new);
         pp.v_new = static_cast<const uint16_t*>(v_new);
-        if (fused)
-            hipLaunchKernelGGL(pa_prefill_tile<true>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        if (q8)
+            hipLaunchKernelGGL((pa_prefill_tile<false, true>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        else if (fused)
+            hipLaunchKernelGGL((pa_prefill_tile<true, false>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         else
-            hipLaunchKernelGGL(pa_prefill_tile<false>, dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+            hipLaunchKernelGGL((pa_prefill_tile<false, false>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         if (hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
@@ -2070,12 +2273,15 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             const int64_t nprefix = (int64_t)ngroups * g->num_kv_heads * plan->prefix_splits;
             if (grid + nprefix > INT32_MAX)
                 return PA_ERR_SHAPE;
-            if (fused)
-                hipLaunchKernelGGL(pa_cascade_decode<true>, dim3((uint32_t)(grid + nprefix)), dim3(64 * kPfWaves), 0,
-                                   st, pp, dp, (int32_t)nprefix);
+            if (q8)
+                hipLaunchKernelGGL((pa_cascade_decode<true, false>), dim3((uint32_t)(grid + nprefix)),
+                                   dim3(64 * kPfWaves), 0, st, pp, dp, (int32_t)nprefix);
+            else if (fused)
+                hipLaunchKernelGGL((pa_cascade_decode<false, true>), dim3((uint32_t)(grid + nprefix)),
+                                   dim3(64 * kPfWaves), 0, st, pp, dp, (int32_t)nprefix);
             else
-                hipLaunchKernelGGL(pa_cascade_decode<false>, dim3((uint32_t)(grid + nprefix)), dim3(64 * kPfWaves), 0,
-                                   st, pp, dp, (int32_t)nprefix);
+                hipLaunchKernelGGL((pa_cascade_decode<false, false>), dim3((uint32_t)(grid + nprefix)),
+                                   dim3(64 * kPfWaves), 0, st, pp, dp, (int32_t)nprefix);
         } else {
             if (grid > INT32_MAX)
                 return PA_ERR_SHAPE;

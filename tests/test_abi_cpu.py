@@ -365,10 +365,10 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.pa_append_kv(ctypes.byref(g), one, one, one, one, one, -1, None) == -2
     assert lib.pa_append_kv(ctypes.byref(g), None, one, one, one, one, 1, None) == -1
     assert lib.pa_append_kv(ctypes.byref(g), None, None, None, None, None, 0, None) == 0
-    # q8_0 pool: decode batches only; the same argument checks
+    # q8_0 pool: the same argument checks
     mixed = pa.pa_plan(g, [1, 64], [100, 200])
-    rc = lib.pa_attention_batch_q8(ctypes.byref(g), ctypes.byref(mixed), one, one, one, 16, one, one, one, one,
-                                   None, 0, None)
+    rc = lib.pa_attention_batch_q8(ctypes.byref(pa.Geometry.make(32, 8, 10, head_dim=64)), ctypes.byref(mixed), one,
+                                   one, one, 16, one, one, one, one, None, 0, None)
     assert rc == -5
     rc = lib.pa_attention_batch_q8(ctypes.byref(g), ctypes.byref(plan), None, None, None, 7, None, None, None,
                                    None, None, 0, None)

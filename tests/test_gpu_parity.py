@@ -399,11 +399,45 @@ def test_q8_edge_lengths(kv):
     check(wl, label=f"q8_0 kv {kv}")
 
 
-def test_q8_rejects_prefill_rows():
-    import paged_kv_attention_04_amd as pa
+def test_q8_chunk_row_small():
+    """A 40-token chunk at offset 60 beside a decode row (8 q / 2 kv heads) on a q8_0 pool:
+    the chunk's new rows are quantised by the append and read back as codes."""
     wl = synthetic.build_q8("q8_prefill", 16, 8, 2, qo_len=[1, 40], kv_len=[20, 100], num_blocks=32)
-    with pytest.raises(pa.PaError, match="UNSUPPORTED"):
-        pa.run_workload(wl)
+    check(wl, label="q8_0 chunk")
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+@pytest.mark.parametrize("psplit", [0, 1, 3, 16])
+def test_q8_chunk_rows(psplit, q_scale):
+    """Chunk rows on a q8_0 pool: chunks at position 0 (2 and 129 tokens), ragged tails,
+    a 77-token chunk at 2036 spanning three 32-token tiles, decode rows beside them, with
+    the planner's or 1 / 3 / 16 key splits; q*8 makes the softmax peaked, so the LSE
+    follows single scores (their K scales are applied in fp32, not rounded)."""
+    wl = synthetic.build_q8("q8_chunks", 17, 32, 8, qo_len=[2, 31, 129, 1, 77, 16],
+                            kv_len=[2, 1000, 129, 500, 2113, 300], num_blocks=300, q_scale=q_scale)
+    check(wl, prefill_splits=psplit, label=f"q8_0 chunks psplit {psplit} q*{q_scale:g}")
+
+
+def test_q8_mixed_batch():
+    """The mixed batch (512-token chunk at 4096 + 31 decode rows) on a q8_0 pool."""
+    check(synthetic.config_mixed_q8(), label="q8_0")
+
+
+def test_q8_shared_prefix_cascade():
+    """The shared-prefix decode on a q8_0 pool through the one-launch cascade: the shared
+    blocks' codes read once per KV head by the matrix-unit tile."""
+    check(synthetic.config_shared_prefix_q8(), cascade=True, label="q8_0 cascade")
+
+
+@pytest.mark.parametrize("num_cus", [8, 256])
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_q8_cascade_groups(num_cus, q_scale):
+    """test_cascade_groups' batch (two groups split by a chunk row, a shared range ending
+    inside a step, a one-token suffix) on a q8_0 pool."""
+    wl = synthetic.build_q8("q8_cascade_groups", 72, 32, 8, qo_len=[1, 1, 1, 1, 1, 20, 1, 1, 1],
+                            kv_len=[1125, 1300, 1500, 1121, 1700, 1250, 1136, 1400, 2000], num_blocks=700,
+                            shared_prefix_blocks=70, q_scale=q_scale)
+    check(wl, cascade=True, num_cus=num_cus, label=f"q8_0 cascade q*{q_scale:g}")
 
 
 def test_q8_copy_blocks_bit_exact():
@@ -733,6 +767,6 @@ def test_random_batches(seed):
         kp, vp, out, lse = _decode_step_gpu(wl, split, cascade)          # the fused step, same bits
         _, _, out2, lse2 = _run_gpu(wl, split, cascade=cascade)
         assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
-        q8 = synthetic.build_q8(f"random{seed}_q8", 3000 + seed, 32, 8, qo_len=list(wl.qo_len),
-                                kv_len=list(wl.kv_len), num_blocks=wl.num_blocks)
-        check(q8, split_blocks=split, label=f"random {seed} q8_0")
+    q8 = synthetic.build_q8(f"random{seed}_q8", 3000 + seed, 32, 8, qo_len=list(wl.qo_len), kv_len=list(wl.kv_len),
+                            num_blocks=wl.num_blocks, shared_prefix_blocks=wl.shared_prefix_blocks)
+    check(q8, split_blocks=split, prefill_splits=psplit, cascade=cascade, label=f"random {seed} q8_0")
