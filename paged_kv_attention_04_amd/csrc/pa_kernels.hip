@@ -512,6 +512,61 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
     }
 }
 
+// merge_rows_results for the many rows a prefix-group workgroup can finish: four rows at
+// a time, two wavefronts per row, each lane merging four consecutive dims of one head, so
+// a row's partials (up to kBatch at once) are all requested before any is used.
+__device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, int nrows, int kvh, int nprefix)
+{
+    constexpr int kBatch = 12;
+    const int head0 = kvh * kGroup;
+    const int t = threadIdx.x, slot = t >> 7, h = (t >> 5) & 3, d4 = (t & 31) * 4;
+    const float nan = __builtin_nanf("");
+    const float* dec_lse = p.part_lse;            // in vector registers: see merge_rows_results
+    const float* dec_o = p.part_o;
+    const float* pfx_lse = p.px_part_lse;
+    const float* pfx_o = p.px_part_o;
+    asm volatile("" : "+v"(dec_lse), "+v"(dec_o), "+v"(pfx_lse), "+v"(pfx_o));
+    for (int c0 = 0; c0 < nrows; c0 += 4) {
+        const int j = c0 + slot;                  // the same for both wavefronts of a row
+        if (j >= nrows)
+            continue;
+        const int rr = rows[j];
+        const int ns = max(0, decode_splits_of(p, rr, prefix_skip_of(p, rr)));
+        const int tot = ns + nprefix;
+        LseMerge mg[4];
+        for (int s0 = 0; s0 < tot; s0 += kBatch) {
+            float ls[kBatch], os[kBatch][4];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int sidx = min(s0 + u, tot - 1);
+                const int64_t pi = sidx < ns ? ((int64_t)rr * p.max_splits + sidx) * p.num_q_heads + head0 + h
+                                             : ((int64_t)rr * p.prefix_splits + (sidx - ns)) * p.num_q_heads + head0 + h;
+                const float* lsrc = sidx < ns ? dec_lse : pfx_lse;
+                const float* osrc = (sidx < ns ? dec_o : pfx_o) + pi * kHeadDim + d4;
+                ls[u] = load_agent(lsrc + pi);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    os[u][k] = load_agent(osrc + k);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (s0 + u < tot)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        mg[k].add(ls[u], os[u][k]);
+        }
+        const int q_row = p.qo_indptr[rr];
+        const int64_t orow = (int64_t)q_row * p.num_q_heads + head0 + h;
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[k] = mg[k].nan ? nan : mg[k].o / mg[k].wsum;
+        *reinterpret_cast<u32x2*>(p.out + orow * kHeadDim + d4) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+        if (d4 == 0)
+            p.lse[orow] = mg[0].nan ? nan : (mg[0].lmax + fast_log2(mg[0].wsum)) * kLn2;
+    }
+}
+
 // Grid: max_splits * num_reqs * num_kv_heads workgroups of kDecodeWaves wavefronts, KV
 // head fastest: workgroups go round-robin to the eight XCDs, so with eight KV heads each
 // XCD serves one KV head of every row and reads that head's shared-prefix blocks from
@@ -1791,7 +1846,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         for (uint32_t mine = (uint32_t)last_lds; mine; mine &= mine - 1)
             rows[nrows++] = grp_first + __builtin_ctz(mine);
         if (nrows > 0)
-            merge_rows_results<4, 8>(dp, rows, nrows, kvh, p.splits);
+            merge_group_rows(dp, rows, nrows, kvh, p.splits);
         return;
     }
 
