@@ -425,7 +425,7 @@ def to_device(arr, device="cuda"):
 
 
 def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", validate: bool = True,
-                 prefill_splits: int = 0, cascade: bool = False, min_shared_blocks: int = 0):
+                 prefill_splits: int = 0, cascade: bool = False, min_shared_blocks: int = 0, prefix_splits: int = 0):
     """Upload a workload (see synthetic.Workload for the fields), append its new tokens,
     plan and run attention; returns host numpy (k_pool, v_pool, out, lse), or
     (kv_pool, None, out, lse) for a q8_0 workload."""
@@ -442,7 +442,8 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
     q8 = getattr(wl, "kv_format", "bf16") == "q8_0"
     plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks, prefill_splits)
     if cascade:
-        pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, num_cus, min_shared_blocks)
+        pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, num_cus, min_shared_blocks,
+                              prefix_splits=prefix_splits)
     if q8:
         kp, vp = to_device(wl.kv_pool, device), None
     else:

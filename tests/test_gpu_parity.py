@@ -29,10 +29,10 @@ def _gpu():
     yield
 
 
-def _run_gpu(wl, split_blocks=0, prefill_splits=0, cascade=False, num_cus=256):
+def _run_gpu(wl, split_blocks=0, prefill_splits=0, cascade=False, num_cus=256, prefix_splits=0):
     import paged_kv_attention_04_amd as pa
     return pa.run_workload(wl, split_blocks=split_blocks, prefill_splits=prefill_splits, cascade=cascade,
-                           num_cus=num_cus)
+                           num_cus=num_cus, prefix_splits=prefix_splits)
 
 
 def _errors(out, lse, ref, rows=None):
@@ -44,10 +44,11 @@ def _errors(out, lse, ref, rows=None):
     return float(np.max(np.abs(got - want))), float(np.max(np.abs(l_got - l_want)))
 
 
-def check(wl, split_blocks=0, label="", prefill_splits=0, cascade=False, num_cus=256):
+def check(wl, split_blocks=0, label="", prefill_splits=0, cascade=False, num_cus=256, prefix_splits=0):
     print(f"[gpu] {wl.name} {label} R={wl.num_reqs} total_q={wl.total_q} split={split_blocks} "
-          f"prefill_splits={prefill_splits} cascade={cascade} num_cus={num_cus}", flush=True)
-    kp, vp, out, lse = _run_gpu(wl, split_blocks, prefill_splits, cascade, num_cus)
+          f"prefill_splits={prefill_splits} cascade={cascade} num_cus={num_cus} prefix_splits={prefix_splits}",
+          flush=True)
+    kp, vp, out, lse = _run_gpu(wl, split_blocks, prefill_splits, cascade, num_cus, prefix_splits)
     okp, ovp, ref = oracle.run_workload(wl)
     assert np.array_equal(kp, okp) and np.array_equal(vp, ovp), "append is not bit-exact"
     eo, el = _errors(out, lse, ref)
@@ -110,6 +111,19 @@ def test_mixed_batch():
 @pytest.mark.parametrize("batch,long_only", [(1, False), (1, True), (8, False), (32, False), (64, False)])
 def test_sweep_decode_layer(batch, long_only):
     check(synthetic.config_sweep_decode(batch, layer=batch % 36, long_only=long_only))
+
+
+@pytest.mark.parametrize("q8", [False, True])
+def test_cascade_prefix_workgroups_merge(q8):
+    """32 rows share 125 blocks (2000 tokens) and have 1-20-token suffixes; with 20 prefix
+    splits the decode workgroups are done long before the prefix ones, so the prefix
+    workgroups are the last arrivals and merge the group's rows: eight passes of four rows,
+    21-22 partials per row in two batches."""
+    kv = [2001 + (i * 7) % 20 for i in range(32)]
+    build = synthetic.build_q8 if q8 else synthetic.build
+    wl = build("prefix_last", 73, 32, 8, qo_len=[1] * 32, kv_len=kv, num_blocks=125 + 2 * 32 + 16,
+               shared_prefix_blocks=125)
+    check(wl, cascade=True, prefix_splits=20, label="q8_0 prefix last" if q8 else "prefix last")
 
 
 @pytest.mark.parametrize("batch", [8, 16, 32, 64])
