@@ -123,7 +123,8 @@ class Stepper:
         wl = self.wl
         plan = self.pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
         if self.cascade:
-            self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus)
+            self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus,
+                                          q8=getattr(wl, "kv_format", "bf16") == "q8_0")
         return plan
 
     def step(self, attention_only: bool = False):
@@ -262,7 +263,8 @@ class LayerStack:
         wl = self.wl
         plan = self.pa.pa_plan(self.g, wl.qo_len, wl.kv_len, self.num_cus)
         if self.cascade:
-            self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus)
+            self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus,
+                                          q8=getattr(wl, "kv_format", "bf16") == "q8_0")
         return plan
 
     def step(self, replan: bool = True, fused: bool = False):

@@ -177,6 +177,17 @@ pa_status pa_plan_shared_prefix(const pa_geometry* geometry, const int32_t* qo_l
                                 pa_plan_t* plan);
 
 /*
+ * pa_plan_shared_prefix for a batch that runs on a q8_0 pool (pa_attention_batch_q8):
+ * the same groups, arguments, overrides and errors; the automatic choice of prefix splits
+ * and split length uses the q8_0 kernels' costs (prefix steps dearer, decode blocks
+ * cheaper than on bf16), which favours more, shorter prefix splits.
+ */
+pa_status pa_plan_shared_prefix_q8(const pa_geometry* geometry, const int32_t* qo_len_host,
+                                   const int32_t* kv_len_host, const int32_t* block_tables_host,
+                                   int32_t max_blocks_per_req, int32_t num_cus, int32_t min_shared_blocks,
+                                   int32_t prefix_splits, int32_t split_blocks, pa_plan_t* plan);
+
+/*
  * Write this step's new K/V rows into the pools through the slot mapping
  * (book section 8.3.1: a token's KV goes to a slot of the block its table
  * names; Perplexity blog: the per-layer append happens before attention).

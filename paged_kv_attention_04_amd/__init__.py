@@ -77,6 +77,7 @@ def lib():
     G, PL = ctypes.POINTER(Geometry), ctypes.POINTER(Plan)
     L.pa_plan.argtypes = [G, i32, P, P, i32, i32, i32, PL]
     L.pa_plan_shared_prefix.argtypes = [G, P, P, P, i32, i32, i32, i32, i32, PL]
+    L.pa_plan_shared_prefix_q8.argtypes = [G, P, P, P, i32, i32, i32, i32, i32, PL]
     L.pa_append_kv.argtypes = [G, P, P, P, P, P, i32, P]
     L.pa_attention_batch.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_decode_step.argtypes = [G, PL, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
@@ -99,7 +100,7 @@ def lib():
     L.pa_allocator_refcount.argtypes = [P, i32, P]
     L.pa_allocator_num_free.argtypes = [P, P, P]
     L.pa_allocator_sync.argtypes = [P]
-    for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
+    for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_plan_shared_prefix_q8", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
                "pa_validate_append", "pa_copy_blocks", "pa_validate_copy", "pa_append_kv_q8",
                "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
                "pa_allocator_alloc", "pa_allocator_retain", "pa_allocator_release", "pa_allocator_cow",
@@ -168,20 +169,22 @@ def pa_plan(geometry: Geometry, qo_len, kv_len, num_cus: int = 256, split_blocks
 
 
 def pa_plan_shared_prefix(geometry: Geometry, plan: Plan, qo_len, kv_len, block_tables, num_cus: int = 256,
-                          min_shared_blocks: int = 0, prefix_splits: int = 0, split_blocks: int = 0) -> Plan:
+                          min_shared_blocks: int = 0, prefix_splits: int = 0, split_blocks: int = 0,
+                          q8: bool = False) -> Plan:
     """Add shared-prefix groups found in the host block tables to `plan` (in place; also
     returned).  block_tables: host int32 [num_reqs][max_blocks].  prefix_splits /
-    split_blocks: 0 lets the planner choose; > 0 forces the value."""
+    split_blocks: 0 lets the planner choose; > 0 forces the value.  q8: the batch runs on a
+    q8_0 pool (pa_plan_shared_prefix_q8)."""
     import numpy as np
     qo = np.ascontiguousarray(qo_len, dtype=np.int32)
     kv = np.ascontiguousarray(kv_len, dtype=np.int32)
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     if bt.ndim != 2 or bt.shape[0] != qo.size or qo.shape != kv.shape:
         raise ValueError("block_tables must be [num_reqs][max_blocks] and match the lengths")
-    _check("pa_plan_shared_prefix", lib().pa_plan_shared_prefix(ctypes.byref(geometry), _np_ptr(qo), _np_ptr(kv),
-                                                                _np_ptr(bt), int(bt.shape[1]), int(num_cus),
-                                                                int(min_shared_blocks), int(prefix_splits),
-                                                                int(split_blocks), ctypes.byref(plan)))
+    name = "pa_plan_shared_prefix_q8" if q8 else "pa_plan_shared_prefix"
+    _check(name, getattr(lib(), name)(ctypes.byref(geometry), _np_ptr(qo), _np_ptr(kv), _np_ptr(bt), int(bt.shape[1]),
+                                      int(num_cus), int(min_shared_blocks), int(prefix_splits), int(split_blocks),
+                                      ctypes.byref(plan)))
     return plan
 
 
@@ -443,7 +446,7 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
     plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks, prefill_splits)
     if cascade:
         pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, num_cus, min_shared_blocks,
-                              prefix_splits=prefix_splits)
+                              prefix_splits=prefix_splits, q8=q8)
     if q8:
         kp, vp = to_device(wl.kv_pool, device), None
     else:

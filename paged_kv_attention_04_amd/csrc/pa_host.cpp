@@ -107,6 +107,19 @@ constexpr MakespanCosts kPrefixCosts = {23.0, 5.57, 43.9, 11.6, 3.30};
 // Candidate prefix split counts: this many 128-key steps per prefix workgroup (the
 // measured optimum over those five batches was always at 4 or 6 steps, or within 2% of it).
 constexpr int32_t kPrefixStepsPerSplit[] = {6, 4};
+// The same planner for a q8_0 pool.  Not fitted: the bf16 constants rescaled by two
+// measured ratios (per-workgroup timestamps on the 16-request, 6144-token-prefix batch):
+// a q8_0 prefix step costs 1.5 bf16 steps (the matrix-unit tile also applies the scales),
+// and a q8_0 decode block 0.85 bf16 blocks (half the bytes, plus the conversion); costs
+// are in q8_0 decode block-times.  The candidates keep the prefix workgroups as long as
+// the bf16 ones in time (4 and 3 steps); with 6 steps the prefix workgroups finished last
+// and merged their groups' rows (64.7 us on that batch against 44.9 us with 3).
+constexpr double kQ8StepRatio = 1.5, kQ8BlockRatio = 0.85;
+constexpr MakespanCosts kSplitCostsQ8 = {13.3 / kQ8BlockRatio, 6.67 / kQ8BlockRatio, 33.3 / kQ8BlockRatio,
+                                         6.67 * kQ8StepRatio / kQ8BlockRatio, 0.0};
+constexpr MakespanCosts kPrefixCostsQ8 = {23.0 / kQ8BlockRatio, 5.57 / kQ8BlockRatio, 43.9 / kQ8BlockRatio,
+                                          11.6 * kQ8StepRatio / kQ8BlockRatio, 3.30 / kQ8BlockRatio};
+constexpr int32_t kPrefixStepsPerSplitQ8[] = {4, 3};
 
 double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_blocks, const int32_t* qo_len,
                       int32_t num_kv_heads, int32_t num_cus, int32_t prefix_splits, int32_t split_blocks,
@@ -239,10 +252,9 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
     return finish_workspace(g, plan);
 }
 
-extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* qo_len, const int32_t* kv_len,
-                                           const int32_t* bt, int32_t max_blocks, int32_t num_cus,
-                                           int32_t min_shared_blocks, int32_t prefix_splits, int32_t split_blocks,
-                                           pa_plan_t* plan)
+static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t* qo_len, const int32_t* kv_len,
+                                    const int32_t* bt, int32_t max_blocks, int32_t num_cus, int32_t min_shared_blocks,
+                                    int32_t prefix_splits, int32_t split_blocks, pa_plan_t* plan)
 {
     if (!g || !plan)
         return PA_ERR_NULL;
@@ -336,7 +348,8 @@ extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* 
                 continue;
             if (sb < kMinAutoSplitBlocks && parts > 1)
                 break;
-            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb, kSplitCosts);
+            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb,
+                                            q8 ? kSplitCostsQ8 : kSplitCosts);
             if (!have || t < best - 1e-9) {
                 have = true;
                 best = t;
@@ -351,10 +364,11 @@ extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* 
         best_sb = best_split_length(best_ps);
     } else {
         double best = 0.0;
-        for (const int32_t per : kPrefixStepsPerSplit) {
+        for (const int32_t per : q8 ? kPrefixStepsPerSplitQ8 : kPrefixStepsPerSplit) {
             const int32_t ps = std::min(std::max(1, ceil_div(steps, per)), pa::kMaxPrefillSplits);
             const int32_t sb = best_split_length(ps);
-            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb, kPrefixCosts);
+            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb,
+                                            q8 ? kPrefixCostsQ8 : kPrefixCosts);
             if (best_ps == 0 || t < best - 1e-9) {
                 best = t;
                 best_ps = ps;
@@ -369,6 +383,24 @@ extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* 
         return st;
     *plan = out;
     return PA_OK;
+}
+
+extern "C" pa_status pa_plan_shared_prefix(const pa_geometry* g, const int32_t* qo_len, const int32_t* kv_len,
+                                           const int32_t* bt, int32_t max_blocks, int32_t num_cus,
+                                           int32_t min_shared_blocks, int32_t prefix_splits, int32_t split_blocks,
+                                           pa_plan_t* plan)
+{
+    return plan_shared_prefix(false, g, qo_len, kv_len, bt, max_blocks, num_cus, min_shared_blocks, prefix_splits,
+                              split_blocks, plan);
+}
+
+extern "C" pa_status pa_plan_shared_prefix_q8(const pa_geometry* g, const int32_t* qo_len, const int32_t* kv_len,
+                                              const int32_t* bt, int32_t max_blocks, int32_t num_cus,
+                                              int32_t min_shared_blocks, int32_t prefix_splits,
+                                              int32_t split_blocks, pa_plan_t* plan)
+{
+    return plan_shared_prefix(true, g, qo_len, kv_len, bt, max_blocks, num_cus, min_shared_blocks, prefix_splits,
+                              split_blocks, plan);
 }
 
 extern "C" pa_status pa_validate_batch(const pa_geometry* g, int32_t num_reqs, const int32_t* qo_len,
