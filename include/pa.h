@@ -400,6 +400,27 @@ pa_status pa_allocator_num_free(pa_block_allocator* allocator, int32_t* free_blo
 /* Waits for every deferred release's stream work, then reclaims.  PA_ERR_HIP on failure. */
 pa_status pa_allocator_sync(pa_block_allocator* allocator);
 
+/*
+ * pa_attention_batch for callers that cannot allocate device memory or pass a workspace:
+ * code being captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: the split partials and completion counters live in a
+ * fixed scratch array of PA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every
+ * device it runs on until the process ends.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).  Arguments, layouts and results are those of
+ * pa_attention_batch; the stream must belong to the current device (PA_ERR_UNSUPPORTED
+ * otherwise).  PA_ERR_WORKSPACE, with nothing launched, when plan->workspace_bytes exceeds
+ * PA_NOALLOC_SCRATCH_BYTES.  The first call on a device looks the scratch array up and
+ * zeroes its counters on `stream`; every call leaves them zero again.  All calls on one
+ * device share that device's array: two calls whose work overlaps in time on one device
+ * (different streams, or different host threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+pa_status pa_attention_batch_noalloc(const pa_geometry* geometry, const pa_plan_t* plan, const void* q,
+                                     const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                     int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                     void* out, float* lse, void* stream);
+
 /* Compute-unit count of a HIP device (for pa_plan).  PA_ERR_HIP on failure. */
 pa_status pa_query_num_cus(int32_t device, int32_t* num_cus);
 

@@ -21,6 +21,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "pa.h")
 PA_MAX_PREFILL_ROWS = 128
 PA_MAX_PREFIX_GROUPS = 16
 PA_MAX_PREFIX_GROUP_REQS = 32
+PA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 HEAD_DIM = 128
 BLOCK_SIZE = 16
 
@@ -87,6 +88,7 @@ def lib():
     L.pa_copy_blocks.argtypes = [G, P, P, P, P, i32, P]
     L.pa_append_kv_q8.argtypes = [G, P, P, P, P, i32, P]
     L.pa_attention_batch_q8.argtypes = [G, PL, P, P, P, i32, P, P, P, P, P, sz, P]
+    L.pa_attention_batch_noalloc.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P]
     L.pa_copy_blocks_q8.argtypes = [G, P, P, P, i32, P]
     L.pa_validate_copy.argtypes = [G, P, P, i32, P]
     L.pa_query_num_cus.argtypes = [i32, P]
@@ -102,7 +104,7 @@ def lib():
     L.pa_allocator_sync.argtypes = [P]
     for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_plan_shared_prefix_q8", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
                "pa_validate_append", "pa_copy_blocks", "pa_validate_copy", "pa_append_kv_q8",
-               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
+               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_attention_batch_noalloc", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
                "pa_allocator_alloc", "pa_allocator_retain", "pa_allocator_release", "pa_allocator_cow",
                "pa_allocator_refcount", "pa_allocator_num_free", "pa_allocator_sync"):
         getattr(L, fn).restype = ctypes.c_int
@@ -295,6 +297,19 @@ def pa_attention_batch(geometry: Geometry, plan: Plan, q, k_pool, v_pool, block_
         _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"), _dev_ptr(out, bf, "out"),
         _dev_ptr(lse, (torch.float32,), "lse"), _dev_ptr(workspace, None, "workspace"), ws_bytes,
         _stream_handle(stream)))
+
+
+def pa_attention_batch_noalloc(geometry: Geometry, plan: Plan, q, k_pool, v_pool, block_tables, qo_indptr, kv_len, out,
+                               lse, stream=None) -> None:
+    """pa_attention_batch without a workspace: split partials and counters live in the
+    library's fixed per-device scratch array (PA_NOALLOC_SCRATCH_BYTES); nothing is allocated."""
+    import torch
+    bf, i32 = _bf16_types(), (torch.int32,)
+    _check("pa_attention_batch_noalloc", lib().pa_attention_batch_noalloc(
+        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(k_pool, bf, "k_pool"),
+        _dev_ptr(v_pool, bf, "v_pool"), _dev_ptr(block_tables, i32, "block_tables"), int(block_tables.shape[1]),
+        _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"), _dev_ptr(out, bf, "out"),
+        _dev_ptr(lse, (torch.float32,), "lse"), _stream_handle(stream)))
 
 
 def pa_validate_batch(geometry: Geometry, qo_len, kv_len, block_tables):

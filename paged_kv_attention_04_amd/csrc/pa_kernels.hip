@@ -24,6 +24,7 @@
 
 #include <stdlib.h>
 
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -2011,6 +2012,15 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_cascade_decode(PrefillParams
 }
 
 
+// Sets n 32-bit words to zero (a kernel rather than a memset, so that a stream capture
+// records an ordinary kernel node).
+__global__ __launch_bounds__(256) void pa_zero_words(uint32_t* __restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -2412,4 +2422,73 @@ extern "C" pa_status pa_query_num_cus(int32_t device, int32_t* num_cus)
         return PA_ERR_HIP;
     *num_cus = v;
     return PA_OK;
+}
+
+// ------------------------------------------------------------------------------ allocation-free entry
+
+// Scratch memory of pa_attention_batch_noalloc: the completion counters and split
+// partials that pa_attention_batch keeps in the caller's workspace, in a fixed array that
+// every device holds from the moment the library's code is loaded on it until the process
+// ends.  Host code must never use the array's name as an address (it names a host-side
+// stand-in); it uses the device address that hipGetSymbolAddress returns for the current
+// device, kept in g_scratch below.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxScratchDevices] = {};
+
+// This device's copy of `scratch`, looked up once per device.  The first call on a device
+// also zeroes the completion counters on `stream` (the array starts zeroed when it is
+// loaded; every call leaves the counters zero again).
+pa_status scratch_for_device(int device, hipStream_t stream, void** out)
+{
+    if (device < 0 || device >= kMaxScratchDevices)
+        return PA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[device]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return PA_ERR_HIP;
+        constexpr int64_t words = pa::kCounterBytes / sizeof(uint32_t);
+        hipLaunchKernelGGL(pa_zero_words, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(ptr), words);
+        if (hipGetLastError() != hipSuccess)
+            return PA_ERR_HIP;
+        g_scratch[device] = ptr;
+    }
+    *out = g_scratch[device];
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_attention_batch_noalloc(const pa_geometry* g, const pa_plan_t* plan, const void* q,
+                                                const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                                int32_t max_blocks_per_req, const int32_t* qo_indptr,
+                                                const int32_t* kv_len, void* out, float* lse, void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    if (plan->workspace_bytes > PA_NOALLOC_SCRATCH_BYTES)
+        return PA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (plan->workspace_bytes > 0) {
+        // the scratch copy must be that of the device the stream runs on
+        int current = -1;
+        hipDevice_t stream_device = -1;
+        if (hipGetDevice(&current) != hipSuccess)
+            return PA_ERR_HIP;
+        if (stream && hipStreamGetDevice(as_stream(stream), &stream_device) != hipSuccess)
+            return PA_ERR_HIP;
+        if (stream && stream_device != current)
+            return PA_ERR_UNSUPPORTED;
+        const pa_status st = scratch_for_device(current, as_stream(stream), &ws);
+        if (st != PA_OK)
+            return st;
+    }
+    return attention_batch(false, g, plan, q, k_pool, v_pool, block_tables, max_blocks_per_req, qo_indptr, kv_len,
+                           out, lse, ws, ws ? (size_t)PA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
