@@ -27,6 +27,7 @@ import json
 import os
 import sys
 import time
+from typing import Optional
 
 import numpy as np
 
@@ -39,6 +40,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_attention_04_amd", "csrc", "pa_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.json")
 CALIBRATION_COPY_BYTES = 256 << 20
+KERNEL_AVG_LAUNCHES = 200       # back-to-back launches behind the roofline's average duration
 
 
 def algorithmic_bytes(wl) -> dict:
@@ -152,40 +154,63 @@ class Stepper:
                                   self.lse, self.ws)
 
 
-def time_steps(stepper, steps: int, warmup: int, attention_only: bool = False) -> float:
-    """Seconds per step over exactly `steps` steps, bracketed by synchronisations (Python's
-    garbage collector is run before and paused during the timed steps)."""
+def time_steps(stepper, steps: int, warmup: int, attention_only: bool = False, events: bool = False):
+    """Seconds per step over exactly `steps` steps, bracketed by synchronisations.  Python's
+    garbage collector runs before the warmup steps and is paused until the timed steps
+    end, so the device goes from the warmup straight into the timed steps.  With
+    `events`, also the device time per step from HIP events recorded on the current
+    stream (the one the library launches on) before the first and after the last timed
+    step: returns (wall seconds per step, event seconds per step)."""
     import gc
 
     import torch
-    for _ in range(warmup):
-        stepper.step(attention_only)
     gc.collect()
     gc.disable()
     try:
+        for _ in range(warmup):
+            stepper.step(attention_only)
+        stream = torch.cuda.current_stream()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if events else None
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        if ev:
+            ev[0].record(stream)
         for _ in range(steps):
             stepper.step(attention_only)
+        if ev:
+            ev[1].record(stream)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        wall = (time.perf_counter() - t0) / steps
     finally:
         gc.enable()
+    if ev:
+        return wall, ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+    return wall
 
 
 def event_time(stepper, reps: int) -> float:
-    """Average device time of one pa_attention_batch call, from HIP events recorded on
-    the stream its kernels are launched on (the current stream)."""
+    """Average device time of one attention call (the plan fixed): HIP events on the
+    current stream -- the stream the library launches on -- around `reps` back-to-back
+    calls, divided by `reps`."""
+    import gc
+
     import torch
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        starts[i].record(stream)
-        stepper.step(attention_only=True)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    return float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
+    gc.collect()
+    gc.disable()
+    try:
+        for _ in range(5):
+            stepper.step(attention_only=True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            stepper.step(attention_only=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
+    return a.elapsed_time(b) * 1e-3 / reps
 
 
 def kernel_source_hash() -> str:
@@ -204,27 +229,110 @@ def measured_traffic():
     return t.get("bytes_per_launch", {}).get("total")
 
 
-def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
-    """The oracle, as it stands, on the host cores: whole attention passes over the
-    decode-step workload repeated until `min_seconds` have passed; same unit as value."""
-    import oracle
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    kp, vp = oracle.append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
-                           wl.head_dim, wl.block_size, wl.num_blocks)
+
+def _sampled_rows(wl, every: int):
+    """Every `every`-th query row of a workload as its own one-token row at the same
+    position: the same keys through the same table row, so the oracle does exactly that
+    row's share of the work.  Returns (q, block_tables, qo_len, kv_len)."""
+    rows, bts, kvs = [], [], []
+    for r in range(wl.num_reqs):
+        q0, ql, kv = int(wl.qo_indptr[r]), int(wl.qo_len[r]), int(wl.kv_len[r])
+        for i in range(ql):
+            if (q0 + i) % every == 0:
+                rows.append(q0 + i)
+                bts.append(r)
+                kvs.append(kv - ql + i + 1)
+    n = len(rows)
+    return (np.ascontiguousarray(wl.q[rows]), np.ascontiguousarray(wl.block_tables[bts]), np.ones(n, np.int32),
+            np.asarray(kvs, np.int32))
+
+
+def _oracle_rate(wl, kp, vp, every: int, min_seconds: float) -> dict:
+    """Attention passes of the oracle over a workload (every `every`-th query row when
+    every > 1) until `min_seconds` have passed, at least one: seconds per pass and
+    (query, key) pairs per second, pairs counted per query head as the oracle counts them."""
+    import oracle
+    fmt = getattr(wl, "kv_format", "bf16")
+    q, bt, qo, kv = (wl.q, wl.block_tables, wl.qo_len, wl.kv_len) if every == 1 else _sampled_rows(wl, every)
+    reps, pairs = 0, 0
     t0 = time.perf_counter()
-    reps = 0
     while True:
-        oracle.attention(wl.q, kp, vp, wl.block_tables, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
-                         wl.head_dim, wl.block_size, wl.num_blocks, wl.scale)
+        res = oracle.attention(q, kp, vp, bt, qo, kv, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
+                               wl.num_blocks, wl.scale, kv_format=fmt)
         reps += 1
+        pairs += res["pairs"]
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
+    return {"pass_s": el / reps, "pairs_per_s": pairs / el, "passes": reps}
+
+
+def _full_pairs(wl) -> int:
+    """Visible (query, key) pairs of a whole workload (per query head)."""
+    return int(sum(int(q) * (int(kv) - int(q)) + int(q) * (int(q) + 1) // 2 for q, kv in zip(wl.qo_len, wl.kv_len)))
+
+
+def cpu_baseline(min_seconds: float = 0.5, pair_budget: int = 40_000, built: Optional[dict] = None) -> dict:
+    """The oracle as it stands (fp64 C, OpenMP over rows and heads), timed on the host on
+    every workload, with all host threads and with one thread.  Each timing covers at
+    most about `pair_budget` (query, key) pairs per thread: a workload with more is timed
+    on every k-th query row and its whole pass extrapolated from the pairs per second
+    (the oracle's cost is linear in the pairs).  The 36-layer workload is timed for one
+    layer and multiplied by 36, and says so.  The headline value is the decode-step
+    workload at all threads, in the headline's unit.  `built` may hold workloads the caller
+    already made ("decode", "shared", "mixed"; unpoisoned)."""
+    import oracle
+    import synthetic
+
+    built = built or {}
+    nproc = oracle.num_threads()
+    out = {"cpu_model": cpu_model(), "threads_all": nproc, "configs": []}
+    _, chunks = synthetic.prompt_chunks(seed=5, prompt_len=2048, chunk=512, num_blocks=256, poison=False)
+    cases = [("tiny: 4 decode rows, kv_len 17/64/100/250, 8 q / 2 kv heads", synthetic.config_tiny(poison=False), 1),
+             ("qwen3_8b_decode_step: 32 x (2048 + U[0,255])",
+              built.get("decode") or synthetic.config_decode(poison=False), 1),
+             ("shared_prefix: 16 x (8192 + U[0,255]), 6144 shared",
+              built.get("shared") or synthetic.config_shared_prefix(poison=False), 1),
+             ("mixed: 512-token chunk at 4096 + 31 decode rows", built.get("mixed") or synthetic.config_mixed(poison=False), 1),
+             ("36-layer sweep, batch-32 decode layer (x 36 layers)",
+              synthetic.config_sweep_decode(32, 0, poison=False), 36)]
+    cases += [(f"36-layer sweep, 2048-token prompt, chunk {i} of 4 x 512 (x 36 layers)", c, 36)
+              for i, c in enumerate(chunks)]
+    head = None
+    for name, wl, layers in cases:
+        kp, vp = oracle.append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
+                               wl.head_dim, wl.block_size, wl.num_blocks)
+        full = _full_pairs(wl)
+        for threads in (nproc, 1):
+            oracle.set_num_threads(threads)
+            every = max(1, -(-full // (pair_budget * threads)))
+            rate = _oracle_rate(wl, kp, vp, every, min_seconds if every == 1 else 0.0)
+            pass_s = full / rate["pairs_per_s"] if every > 1 else rate["pass_s"]
+            sample = (f"every {every}th query row, whole pass extrapolated from pairs/s" if every > 1
+                      else f"{rate['passes']} whole passes")
+            out["configs"].append({
+                "workload": name, "threads": threads, "pass_s": round(pass_s * layers, 5),
+                "new_tokens_per_s": round(wl.total_q / pass_s, 2), "pairs_per_s": round(rate["pairs_per_s"], 1),
+                "sample": sample + (f"; one layer timed, pass_s x {layers} layers" if layers > 1 else "")})
+            if name.startswith("qwen3_8b_decode_step") and threads == nproc:
+                head = (wl, pass_s, sample)
+    oracle.set_num_threads(nproc)
+    wl, pass_s, sample = head
     ab = algorithmic_bytes(wl)
-    return {"value": round(ab["attention"] * reps / el / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} full attention passes of the decode-step workload (32 requests, "
-                      f"{int(wl.kv_len.sum())} KV tokens), fp64 C oracle, {el:.1f} s"}
+    out.update({"value": round(ab["attention"] / pass_s / 1e9, 4), "unit": "GB/s", "cores": nproc,
+                "kind": "oracle",
+                "sample": f"decode-step workload (32 requests, {int(wl.kv_len.sum())} KV tokens): {sample}, fp64 C "
+                          f"oracle, {nproc} threads; every workload at {nproc} threads and at 1 thread under configs"})
+    return out
 
 
 SWEEP_LAYERS = 36
@@ -395,6 +503,17 @@ def summarize(directory: str, title: str):
             lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
                          f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['TotalDurationNs']) / 1e3:.1f} |")
         lines.append("")
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)):
+        per = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+            wg = int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", 1)) or 1)
+            per[(name, grid // max(wg, 1))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["| kernel | workgroups | calls | avg us | median us | min us |", "|---|---|---|---|---|---|"]
+        for (name, wgs), d in sorted(per.items()):
+            lines.append(f"| {name} | {wgs} | {len(d)} | {np.mean(d):.3f} | {np.median(d):.3f} | {min(d):.3f} |")
+        lines.append("")
     for f in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
         agg = defaultdict(list)
         for r in csv.DictReader(open(f)):
@@ -448,7 +567,8 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=8, help="KV pool replicas rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 36-layer sweep")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=0.5, help="least seconds per whole-pass CPU timing")
+    ap.add_argument("--only", choices=["headline"], help="run the headline step only (for rocprofv3)")
     ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "mixed_fused", "mixed_q8", "shared",
                                               "shared_q8", "prefill"])
     ap.add_argument("--reps", type=int, default=20)
@@ -481,10 +601,30 @@ def main(argv=None):
     wl = synthetic.config_decode(poison=False)
     ab = algorithmic_bytes(wl)
     st = Stepper(wl, args.copies, fused=True)      # plan + pa_decode_step (append fused into attention)
-    sec = time_steps(st, args.steps, args.warmup)
-    t_attn = event_time(st, max(args.steps, 50))   # the one launch of a step
+    sec, sec_ev = time_steps(st, args.steps, args.warmup, events=True)
+    t_attn = event_time(st, KERNEL_AVG_LAUNCHES)   # the one launch of a step, back to back
     value = ab["step"] / sec / 1e9
     achieved = ab["step"] / t_attn / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "kernel": "pa_decode_split<false, true> (bf16 pool, append fused: the one launch of a step)",
+                "avg_us": round(t_attn * 1e6, 3),
+                "avg_us_from": f"HIP events on the launch stream around {KERNEL_AVG_LAUNCHES} back-to-back launches",
+                "avg_us_timed_region": round(sec_ev * 1e6, 3),
+                "bytes_per_launch": ab["step"]}
+    config = {"workload": "qwen3_8b_decode_step: 32 requests, kv_len 2048+U[0,255], 32 q / 8 kv heads, "
+                          "head_dim 128, 16-token blocks, bf16 KV pool of 5461 blocks, 1 layer; "
+                          "step = pa_plan + pa_decode_step (the append fused into the attention launch)",
+              "kv_bytes_unique": ab["kv_unique"], "step_bytes": ab["step"],
+              "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+              "plan": {"split_blocks": st.plan.split_blocks, "max_splits": st.plan.max_splits,
+                       "decode_workgroups": st.plan.decode_items}}
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config, "roofline": roofline}
+    if args.only == "headline":
+        print(json.dumps(line), flush=True)
+        return
 
     # mixed continuous batch: tokens per second of a whole step
     wm = synthetic.config_mixed(poison=False)
@@ -513,8 +653,6 @@ def main(argv=None):
 
     # the same decode step on a q8_0 pool (same lengths and tables): the saving against
     # the pages' model, saving = fewer bytes / bandwidth - conversion time
-    plan_info = {"split_blocks": st.plan.split_blocks, "max_splits": st.plan.max_splits,
-                 "decode_workgroups": st.plan.decode_items}
     del st
     st_plain = Stepper(wl, args.copies)            # bf16 attention alone, the q8_0 line's reference
     time_steps(st_plain, 10, 5, attention_only=True)
@@ -580,29 +718,7 @@ def main(argv=None):
     del sp
     pflops = prefill_flops(wp)
 
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(sec * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "qwen3_8b_decode_step: 32 requests, kv_len 2048+U[0,255], 32 q / 8 kv heads, "
-                               "head_dim 128, 16-token blocks, bf16 KV pool of 5461 blocks, 1 layer; "
-                               "step = pa_plan + pa_decode_step (the append fused into the attention launch)",
-                   "kv_bytes_unique": ab["kv_unique"], "step_bytes": ab["step"],
-                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "plan": plan_info},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "pa_decode_split<bf16, fused append> (the one launch of the step)",
-                     "avg_us": round(t_attn * 1e6, 3), "bytes_per_launch": ab["step"]},
+    line.update({
         "mixed_batch": {"workload": "1 prefill row (512 tokens at offset 4096) + 31 decode rows, 543 new tokens",
                         "step": "pa_plan + pa_attention_step (append fused into the prefill and decode launches)",
                         "tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
@@ -614,11 +730,11 @@ def main(argv=None):
         "prefill_chunk": {"workload": "512 new tokens at kv offset 4096, 32 q / 8 kv heads, causal",
                           "us": round(t_p * 1e6, 3), "tflops": round(pflops / t_p / 1e12, 1),
                           "frac_of_bf16_mfma_peak": round(pflops / t_p / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
-    }
+    })
     if not args.no_sweep:
         line["sweep_36_layers"] = sweep36()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(synthetic.config_decode(poison=False), args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds, built={"decode": wl, "shared": ws3, "mixed": wm})
     print(json.dumps(line), flush=True)
 
 

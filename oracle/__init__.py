@@ -69,6 +69,8 @@ def _load():
     lib.oracle_half_to_double.restype = f64
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -83,6 +85,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads later attention calls may use (timing only; results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def round_bf16(x) -> np.ndarray:

@@ -470,10 +470,13 @@ void oracle_round_bf16_array(const double* x, uint16_t* out, int64_t n)
         out[i] = oracle_double_to_bf16(x[i]);
 }
 
-/* Threads the attention loop may use (OpenMP's current maximum; 1 without OpenMP). */
+/* Threads the attention loop may use (OpenMP's current maximum; 1 without OpenMP), and
+ * a setter for it (timing runs on one thread and on all host threads). */
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif

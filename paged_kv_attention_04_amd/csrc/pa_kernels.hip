@@ -1491,9 +1491,11 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 v = *reinterpret_cast<const u32x4*>(
                     p.q + ((int64_t)qidx * p.num_q_heads + head0 + (rho & 3)) * kHeadDim + ks * 32 + kslice * 8);
             if constexpr (kQ8) {
+                // toward zero, as the decode rows convert Q: exact inside the binary16
+                // range, and a magnitude past 65504 saturates instead of becoming inf
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    v[j] = pack_f16(bf16_lo(v[j]), bf16_hi(v[j]));
+                    v[j] = pack_half_rtz(bf16_lo(v[j]), bf16_hi(v[j]));
             }
             qop[rb][ks] = __builtin_bit_cast(bf16x8, v);
         }
@@ -2154,6 +2156,37 @@ extern "C" pa_status pa_copy_blocks_q8(const pa_geometry* g, void* kv_pool_q8, c
     return copy_blocks(g, kv_pool_q8, kv_pool_q8, src_blocks, dst_blocks, n, stream, 2 * pa::kQ8TileBytes, 1);
 }
 
+// The plan's view of the rows must be that of the device lengths: the same rows with
+// qo_len > 1, in order and with their tile counts, every other row a decode row whose
+// splits fit max_splits, and shared-prefix groups made of decode rows with blocks past
+// the shared ones.  A row the plan classifies wrongly would otherwise be left unwritten.
+static pa_status check_plan_matches(const pa_plan_t* plan, const std::vector<int32_t>& qo,
+                                    const std::vector<int32_t>& kvl)
+{
+    const int32_t R = plan->num_reqs;
+    std::vector<int32_t> skip((size_t)R, 0);
+    for (int gi = 0; gi < plan->num_prefix_groups; ++gi)
+        for (int k = 0; k < plan->prefix_num_reqs[gi]; ++k)
+            skip[(size_t)(plan->prefix_first_req[gi] + k)] = plan->prefix_blocks[gi];
+    int32_t nd = 0, np = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        if (qo[r] == 1) {
+            ++nd;
+            const int32_t nblk = (kvl[r] + kBlock - 1) / kBlock;
+            if (plan->split_blocks < 1 || nblk <= skip[r] ||
+                (nblk - skip[r] + plan->split_blocks - 1) / plan->split_blocks > plan->max_splits)
+                return PA_ERR_SHAPE;
+        } else {
+            if (np >= plan->num_prefill_rows || plan->prefill_req[np] != r || skip[r] != 0 ||
+                plan->prefill_tile_start[np + 1] - plan->prefill_tile_start[np] !=
+                    (qo[r] + pa::kPrefillQ - 1) / pa::kPrefillQ)
+                return PA_ERR_SHAPE;
+            ++np;
+        }
+    }
+    return nd == plan->num_decode_rows && np == plan->num_prefill_rows ? PA_OK : PA_ERR_SHAPE;
+}
+
 static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t* plan, const void* q,
                                  const void* k_pool, const void* v_pool, const int32_t* block_tables,
                                  int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
@@ -2217,6 +2250,9 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         for (int32_t r = 0; r < R; ++r)
             qo[r] = indptr[r + 1] - indptr[r];
         vs = pa_validate_batch(g, R, qo.data(), kvl.data(), bt.data(), max_blocks_per_req, nullptr);
+        if (vs != PA_OK)
+            return vs;
+        vs = check_plan_matches(plan, qo, kvl);
         if (vs != PA_OK)
             return vs;
         if (fused) {            // the slots the fused append writes: positions kv_len - qo_len .. kv_len - 1

@@ -44,12 +44,29 @@ def _errors(out, lse, ref, rows=None):
     return float(np.max(np.abs(got - want))), float(np.max(np.abs(l_got - l_want)))
 
 
+def exact_error_report(out, lse, ref) -> str:
+    """Error of the GPU result against the oracle's unrounded (fp64) values: the largest
+    error in bf16 units in the last place of the exact value, the largest normwise
+    relative error of a (row, head) output vector, and the largest LSE error.  Printed
+    beside the bars, so that a regression that stays inside the absolute bar still shows."""
+    got = bf16_bits_to_f32(out).astype(np.float64)
+    exact = ref["out_f64"]
+    mag = np.maximum(np.abs(exact), 2.0 ** -126)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - 7)              # bf16 keeps 8 significant bits
+    ulps = np.abs(got - exact) / ulp
+    norm = np.maximum(np.max(np.abs(exact), axis=-1), 1e-30)
+    rel = np.max(np.abs(got - exact), axis=-1) / norm
+    dl = np.abs(lse.astype(np.float64) - ref["lse_f64"])
+    return (f"ulp max {ulps.max():.2f} p99.9 {np.quantile(ulps, 0.999):.2f}; normwise rel max {rel.max():.2e}; "
+            f"|dLSE| vs fp64 {dl.max():.2e}")
+
+
 def check(wl, split_blocks=0, label="", prefill_splits=0, cascade=False, num_cus=256, prefix_splits=0):
     print(f"[gpu] {wl.name} {label} R={wl.num_reqs} total_q={wl.total_q} split={split_blocks} "
           f"prefill_splits={prefill_splits} cascade={cascade} num_cus={num_cus} prefix_splits={prefix_splits}",
           flush=True)
     kp, vp, out, lse = _run_gpu(wl, split_blocks, prefill_splits, cascade, num_cus, prefix_splits)
-    okp, ovp, ref = oracle.run_workload(wl)
+    okp, ovp, ref = oracle.run_workload(wl, want_f64=True)
     assert np.array_equal(kp, okp) and np.array_equal(vp, ovp), "append is not bit-exact"
     eo, el = _errors(out, lse, ref)
     dec = np.concatenate([np.arange(a, b) for a, b, q in zip(wl.qo_indptr[:-1], wl.qo_indptr[1:], wl.qo_len) if q == 1]
@@ -60,7 +77,8 @@ def check(wl, split_blocks=0, label="", prefill_splits=0, cascade=False, num_cus
         parts.append("decode %.2e/%.2e" % _errors(out, lse, ref, dec))
     if pre.size:
         parts.append("prefill %.2e/%.2e" % _errors(out, lse, ref, pre))
-    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e} ({', '.join(parts)})", flush=True)
+    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e} ({', '.join(parts)}); {exact_error_report(out, lse, ref)}",
+          flush=True)
     assert eo <= TOL_O, f"output error {eo}"
     assert el <= TOL_LSE, f"LSE error {el}"
     return out, lse
@@ -278,6 +296,86 @@ def test_graph_replay_matches_eager():
         step()                                   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+
+
+def _layer_workloads(num_layers, batch=8, seed=97):
+    """``num_layers`` layers of the 36-layer sweep's batch shape (half the rows at 2048
+    tokens, half at 8192 sharing a 6144-token prefix): one set of block tables and lengths
+    for every layer (a block id names one page in each layer's pool), and per layer its
+    own pool values, Q and new K / V.  Unused slots stay NaN in every layer."""
+    import dataclasses
+    base = synthetic.config_sweep_decode(batch, layer=0, num_blocks=1600)
+    rng = np.random.default_rng(seed)
+    layers = []
+    for li in range(num_layers):
+        def fresh(a):
+            vals = synthetic.f32_to_bf16_bits(rng.standard_normal(a.shape, dtype=np.float32))
+            return np.where(np.isnan(bf16_bits_to_f32(a)), a, vals).astype(np.uint16)
+        layers.append(dataclasses.replace(
+            base, name=f"sweep_b{batch}_stack_layer{li}", k_pool=fresh(base.k_pool), v_pool=fresh(base.v_pool),
+            q=synthetic.f32_to_bf16_bits(rng.standard_normal(base.q.shape, dtype=np.float32)),
+            k_new=synthetic.f32_to_bf16_bits(rng.standard_normal(base.k_new.shape, dtype=np.float32)),
+            v_new=synthetic.f32_to_bf16_bits(rng.standard_normal(base.v_new.shape, dtype=np.float32))))
+    return layers
+
+
+def test_graph_captured_layer_stack_matches_oracle():
+    """The form the 36-layer sweep times: one plan per step with shared-prefix groups, then
+    per layer one pa_decode_step (append fused into the attention launch), all layers
+    captured into one graph.  Four layers of the batch-8 shape; every replay (eager work and
+    synchronisations between replays) is checked layer by layer against the oracle --
+    pools bit-exact after the append, outputs within the bars -- and bit for bit against
+    the first replay."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    layers = _layer_workloads(4)
+    wl0 = layers[0]
+    g = pa.Geometry.make(wl0.num_q_heads, wl0.num_kv_heads, wl0.num_blocks, wl0.scale)
+    plan = pa.pa_plan(g, wl0.qo_len, wl0.kv_len, 256)
+    pa.pa_plan_shared_prefix(g, plan, wl0.qo_len, wl0.kv_len, wl0.block_tables, 256)
+    assert plan.num_prefix_groups == 1
+    ws = pa.workspace_for(plan)
+    bt, indptr, kv = (pa.to_device(getattr(wl0, k)) for k in ("block_tables", "qo_indptr", "kv_len"))
+    dev = [{k: pa.to_device(getattr(wl, k)) for k in ("k_pool", "v_pool", "q", "k_new", "v_new")} for wl in layers]
+    outs = [torch.empty((wl0.total_q, wl0.num_q_heads, wl0.head_dim), dtype=torch.int16, device="cuda")
+            for _ in layers]
+    lses = [torch.empty((wl0.total_q, wl0.num_q_heads), dtype=torch.float32, device="cuda") for _ in layers]
+
+    def step():
+        for d, o, l in zip(dev, outs, lses):
+            pa.pa_decode_step(g, plan, d["q"], d["k_pool"], d["v_pool"], d["k_new"], d["v_new"], bt, indptr, kv, o, l,
+                              ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                    # the append is idempotent: the same token to the same slot
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    refs = [oracle.run_workload(wl, want_f64=True) for wl in layers]
+    first = None
+    for rep in range(3):
+        for o, l in zip(outs, lses):
+            o.fill_(-1)
+            l.fill_(-7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [(o.cpu().numpy().view(np.uint16), l.cpu().numpy()) for o, l in zip(outs, lses)]
+        for li, ((out, lse), (okp, ovp, ref), d) in enumerate(zip(got, refs, dev)):
+            assert np.array_equal(d["k_pool"].cpu().numpy().view(np.uint16), okp)
+            assert np.array_equal(d["v_pool"].cpu().numpy().view(np.uint16), ovp)
+            eo, el = _errors(out, lse, ref)
+            print(f"[gpu] graph stack replay {rep} layer {li}: max|dO|={eo:.3e} max|dLSE|={el:.3e}; "
+                  f"{exact_error_report(out, lse, ref)}", flush=True)
+            assert eo <= TOL_O and el <= TOL_LSE
+        if first is None:
+            first = got
+        assert all(np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) for a, b in zip(got, first))
+        step()                                    # eager work between replays
+        torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------------ block copy (copy-on-write)
@@ -594,6 +692,21 @@ def test_validate_mode_rejects_bad_content_before_launch(monkeypatch):
     with pytest.raises(pa.PaError, match="SHAPE"):
         pa.pa_attention_batch(g, plan, pa.to_device(wl.q), kp, vp, pa.to_device(wl.block_tables),
                               pa.to_device(wl.qo_indptr), pa.to_device(bad_kv), out, lse, pa.workspace_for(plan))
+    # lengths that keep the total but move the 2-token row: the plan's row classes no
+    # longer match the device's (a row the plan takes for a decode row would be left
+    # unwritten), so validation rejects the call
+    wl2 = synthetic.build("validate_classes", 19, 8, 2, qo_len=[2, 1, 1], kv_len=[40, 50, 60], num_blocks=32,
+                          poison=False)
+    g2 = pa.Geometry.make(wl2.num_q_heads, wl2.num_kv_heads, wl2.num_blocks, wl2.scale)
+    plan2 = pa.pa_plan(g2, [1, 2, 1], wl2.kv_len)
+    out2 = torch.zeros((wl2.total_q, wl2.num_q_heads, 128), dtype=torch.int16, device="cuda")
+    lse2 = torch.zeros((wl2.total_q, wl2.num_q_heads), dtype=torch.float32, device="cuda")
+    with pytest.raises(pa.PaError, match="SHAPE"):
+        pa.pa_attention_batch(g2, plan2, pa.to_device(wl2.q), pa.to_device(wl2.k_pool), pa.to_device(wl2.v_pool),
+                              pa.to_device(wl2.block_tables), pa.to_device(wl2.qo_indptr), pa.to_device(wl2.kv_len),
+                              out2, lse2, pa.workspace_for(plan2))
+    torch.cuda.synchronize()
+    assert not out2.any()
     slots = wl.slot_mapping.copy()
     slots[1] = slots[0]
     before = kp.clone()
