@@ -92,7 +92,8 @@ def prefill_only_workload(poison=False):
 class Stepper:
     """Device copies of a workload, with `copies` KV-pool replicas rotated per step."""
 
-    def __init__(self, wl, copies: int, device="cuda", cascade: bool = False, fused: bool = False):
+    def __init__(self, wl, copies: int, device="cuda", cascade: bool = False, fused: bool = False,
+                 one_launch: Optional[int] = None):
         import torch
 
         import paged_kv_attention_04_amd as pa
@@ -117,6 +118,7 @@ class Stepper:
         self.cascade = cascade
         self.fused = fused               # decode-only batches: append fused into the attention launch
         self.q8 = getattr(wl, "kv_format", "bf16") == "q8_0"
+        self.one_launch = one_launch     # None: the planner's choice of one or two launches
         self.plan = self.make_plan()
         self.ws = pa.workspace_for(self.plan, device)
         self.i = 0
@@ -127,6 +129,8 @@ class Stepper:
         if self.cascade:
             self.pa.pa_plan_shared_prefix(self.g, plan, wl.qo_len, wl.kv_len, wl.block_tables, self.num_cus,
                                           q8=getattr(wl, "kv_format", "bf16") == "q8_0")
+        if self.one_launch is not None:
+            plan.one_launch = self.one_launch
         return plan
 
     def step(self, attention_only: bool = False):

@@ -123,6 +123,13 @@ typedef struct pa_plan_t {
     int32_t prefix_first_req[PA_MAX_PREFIX_GROUPS]; /* first request of each group            */
     int32_t prefix_num_reqs[PA_MAX_PREFIX_GROUPS];  /* consecutive decode requests in it      */
     int32_t prefix_blocks[PA_MAX_PREFIX_GROUPS];    /* leading blocks all of them share       */
+    int32_t one_launch;                  /* a batch with chunk tiles and decode rows (and no
+                                            shared-prefix group, bf16 pool): 0 launches the
+                                            chunk tiles, then the decode rows; 1 runs both in
+                                            one launch, chunk tiles first in the grid; 2 the
+                                            same with the two kinds interleaved.  Results are
+                                            bit-identical.  pa_plan sets 0 (measured fastest
+                                            on a one-GPU MI355X); the caller may override   */
     uint64_t workspace_bytes;            /* device workspace pa_attention_batch needs         */
 } pa_plan_t;
 

@@ -59,6 +59,7 @@ class Plan(ctypes.Structure):
                 ("prefix_first_req", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
                 ("prefix_num_reqs", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
                 ("prefix_blocks", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
+                ("one_launch", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
@@ -443,10 +444,12 @@ def to_device(arr, device="cuda"):
 
 
 def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", validate: bool = True,
-                 prefill_splits: int = 0, cascade: bool = False, min_shared_blocks: int = 0, prefix_splits: int = 0):
+                 prefill_splits: int = 0, cascade: bool = False, min_shared_blocks: int = 0, prefix_splits: int = 0,
+                 one_launch: Optional[int] = None):
     """Upload a workload (see synthetic.Workload for the fields), append its new tokens,
     plan and run attention; returns host numpy (k_pool, v_pool, out, lse), or
-    (kv_pool, None, out, lse) for a q8_0 workload."""
+    (kv_pool, None, out, lse) for a q8_0 workload.  one_launch overrides the plan's choice
+    of one or two launches for a batch with chunk tiles and decode rows."""
     import numpy as np
     import torch
     g = Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale, wl.head_dim, wl.block_size)
@@ -462,6 +465,8 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
     if cascade:
         pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, num_cus, min_shared_blocks,
                               prefix_splits=prefix_splits, q8=q8)
+    if one_launch is not None:
+        plan.one_launch = int(one_launch)
     if q8:
         kp, vp = to_device(wl.kv_pool, device), None
     else:

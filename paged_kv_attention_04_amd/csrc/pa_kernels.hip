@@ -2023,6 +2023,41 @@ __global__ __launch_bounds__(256) void pa_zero_words(uint32_t* __restrict__ p, i
         p[i] = 0u;
 }
 
+// A mixed batch (chunk tiles and decode rows) in one launch.  With `interleave` 0 the grid
+// holds the chunk-tile workgroups first, then the decode workgroups (which fill CUs as the
+// chunk tiles drain).  Otherwise both kinds come in groups of num_kv_heads, one per KV
+// head, and the grid alternates a group of chunk-tile workgroups with a group of decode
+// workgroups while both last, then runs the rest of the longer kind; workgroups are dealt
+// round-robin to the XCDs, so each KV head keeps one XCD (and its L2) for both kinds.
+// Nothing waits for anything else: the two kinds share no outputs, and their split
+// counters and partials sit in separate parts of the workspace.
+template <bool kFused>
+__global__ __launch_bounds__(64 * kPfWaves) void pa_mixed_batch(PrefillParams pp, DecodeParams dp,
+                                                                int32_t num_prefill_wgs, int32_t num_decode_wgs,
+                                                                int32_t interleave)
+{
+    const int H = dp.num_kv_heads;
+    const int b = blockIdx.x, grp = b / H, lane = b - grp * H;
+    const int pf_groups = num_prefill_wgs / H, dc_groups = num_decode_wgs / H;
+    const int both = interleave ? min(pf_groups, dc_groups) : 0;
+    bool prefill;
+    int idx;
+    if (!interleave) {
+        prefill = b < num_prefill_wgs;
+        idx = prefill ? b : b - num_prefill_wgs;
+    } else if (grp < 2 * both) {
+        prefill = (grp & 1) == 0;
+        idx = (grp >> 1) * H + lane;
+    } else {
+        prefill = pf_groups > both;
+        idx = (grp - both) * H + lane;
+    }
+    if (prefill)
+        prefill_body<false, kFused, false>(pp, dp, idx);
+    else
+        decode_body<false, kFused>(dp, idx);
+}
+
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -2286,6 +2321,11 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         return pp;
     };
 
+    // chunk tiles and decode rows in one launch (bf16 pool, no shared-prefix group)
+    const bool one_launch = plan->one_launch >= 1 && !q8 && ngroups == 0 && plan->num_prefill_rows > 0 &&
+                            plan->prefill_tiles > 0 && plan->num_decode_rows > 0 && plan->max_splits > 0;
+    PrefillParams mixed_pp = {};
+    int64_t mixed_prefill_wgs = 0;
     if (plan->num_prefill_rows > 0 && plan->prefill_tiles > 0) {
         PrefillParams pp = prefill_params();
         pp.q = static_cast<const uint16_t*>(q);
@@ -2316,13 +2356,16 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             return PA_ERR_SHAPE;
         pp.k_new = static_cast<const uint16_t*>(k_new);
         pp.v_new = static_cast<const uint16_t*>(v_new);
-        if (q8)
+        if (one_launch) {
+            mixed_pp = pp;
+            mixed_prefill_wgs = grid;
+        } else if (q8)
             hipLaunchKernelGGL((pa_prefill_tile<false, true>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         else if (fused)
             hipLaunchKernelGGL((pa_prefill_tile<true, false>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
         else
             hipLaunchKernelGGL((pa_prefill_tile<false, false>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
-        if (hipGetLastError() != hipSuccess)
+        if (!one_launch && hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
     if (plan->num_decode_rows > 0 && plan->max_splits > 0) {
@@ -2383,6 +2426,16 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             else
                 hipLaunchKernelGGL((pa_cascade_decode<false, false>), dim3((uint32_t)(grid + nprefix)),
                                    dim3(64 * kPfWaves), 0, st, pp, dp, (int32_t)nprefix);
+        } else if (one_launch) {
+            if (grid + mixed_prefill_wgs > INT32_MAX)
+                return PA_ERR_SHAPE;
+            const dim3 blocks((uint32_t)(grid + mixed_prefill_wgs));
+            if (fused)
+                hipLaunchKernelGGL((pa_mixed_batch<true>), blocks, dim3(64 * kPfWaves), 0, st, mixed_pp, dp,
+                                   (int32_t)mixed_prefill_wgs, (int32_t)grid, (int32_t)(plan->one_launch == 2));
+            else
+                hipLaunchKernelGGL((pa_mixed_batch<false>), blocks, dim3(64 * kPfWaves), 0, st, mixed_pp, dp,
+                                   (int32_t)mixed_prefill_wgs, (int32_t)grid, (int32_t)(plan->one_launch == 2));
         } else {
             if (grid > INT32_MAX)
                 return PA_ERR_SHAPE;

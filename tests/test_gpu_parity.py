@@ -763,15 +763,17 @@ def test_fused_decode_step_matches_append_then_attention(case):
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
 
 
-def _attention_step_gpu(wl, prefill_splits=0, cascade=False):
+def _attention_step_gpu(wl, prefill_splits=0, cascade=False, one_launch=None, split_blocks=0):
     """pa_attention_step on device copies of the workload; returns host (k_pool, v_pool, out, lse)."""
     import torch
     import paged_kv_attention_04_amd as pa
     g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
-    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256, 0, prefill_splits)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256, split_blocks, prefill_splits)
     if cascade:
         pa.pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables)
         assert plan.num_prefix_groups >= 1
+    if one_launch is not None:
+        plan.one_launch = one_launch
     kp, vp = pa.to_device(wl.k_pool), pa.to_device(wl.v_pool)
     out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device="cuda")
     lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
@@ -845,6 +847,41 @@ def test_validate_mode_attention_step(monkeypatch):
                              pa.workspace_for(plan))
     torch.cuda.synchronize()
     assert torch.equal(kp, before) and not out.any()   # nothing was launched
+
+
+@pytest.mark.parametrize("case", ["mixed", "tiny_mixed", "psplit3_split5", "chunks_only_one_decode", "many_decode"])
+def test_one_launch_mixed_batch(case):
+    """Chunk tiles and decode workgroups interleaved in one launch: the same output bits as
+    the two launches (prefill, then decode), with and without the fused append, pools
+    bit-exact against the oracle's append, outputs within the bars of the oracle."""
+    wl, psplit, split = {
+        "mixed": lambda: (synthetic.config_mixed(), 0, 0),
+        "tiny_mixed": lambda: (synthetic.build("one_launch_tiny", 52, 8, 2, qo_len=[1, 40, 1], kv_len=[20, 100, 7],
+                                               num_blocks=40), 0, 0),
+        "psplit3_split5": lambda: (synthetic.build("one_launch_splits", 53, 32, 8, qo_len=[1, 40, 1, 70, 2, 1],
+                                                   kv_len=[300, 500, 17, 700, 33, 900], num_blocks=300), 3, 5),
+        "chunks_only_one_decode": lambda: (synthetic.build("one_launch_more_tiles", 54, 32, 8, qo_len=[200, 1, 130],
+                                                           kv_len=[1200, 64, 900], num_blocks=200), 0, 0),
+        "many_decode": lambda: (synthetic.build("one_launch_many_decode", 55, 32, 8, qo_len=[33] + [1] * 40,
+                                                kv_len=[40] + [300 + 13 * i for i in range(40)],
+                                                num_blocks=3 + sum(-(-(300 + 13 * i) // 16) for i in range(40)) + 8),
+                           0, 0),
+    }[case]()
+    print(f"[gpu] one-launch mixed {case} R={wl.num_reqs} total_q={wl.total_q}", flush=True)
+    two = _run_gpu(wl, split, psplit)
+    import paged_kv_attention_04_amd as pa
+    one = pa.run_workload(wl, split_blocks=split, prefill_splits=psplit, one_launch=1)
+    assert np.array_equal(one[2], two[2]) and np.array_equal(one[3], two[3]), "one launch differs from two"
+    mix = pa.run_workload(wl, split_blocks=split, prefill_splits=psplit, one_launch=2)      # interleaved order
+    assert np.array_equal(mix[2], two[2]) and np.array_equal(mix[3], two[3]), "interleaved launch differs"
+    okp, ovp, ref = oracle.run_workload(wl, want_f64=True)
+    assert np.array_equal(one[0], okp) and np.array_equal(one[1], ovp)
+    eo, el = _errors(one[2], one[3], ref)
+    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e}; {exact_error_report(one[2], one[3], ref)}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+    fk, fv, fo, fl = _attention_step_gpu(wl, psplit, one_launch=1, split_blocks=split)      # the fused append too
+    assert np.array_equal(fk, okp) and np.array_equal(fv, ovp)
+    assert np.array_equal(fo, two[2]) and np.array_equal(fl, two[3])
 
 
 def test_fused_decode_step_rejects_chunk_rows():
