@@ -114,7 +114,7 @@ typedef struct pa_plan_t {
     int32_t split_blocks;                /* KV blocks per decode split (one workgroup each)   */
     int32_t max_splits;                  /* largest split count of any decode row             */
     int32_t decode_items;                /* (row, KV head, split) decode workgroups           */
-    int32_t prefill_tiles;               /* 32-token query tiles over all prefill rows        */
+    int32_t prefill_tiles;               /* query tiles over all prefill rows                 */
     int32_t prefill_splits;              /* key splits per prefill tile (one workgroup each)  */
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];       /* request index of each prefill row      */
     int32_t prefill_tile_start[PA_MAX_PREFILL_ROWS + 1]; /* prefix sums of tiles per row      */
@@ -123,6 +123,12 @@ typedef struct pa_plan_t {
     int32_t prefix_first_req[PA_MAX_PREFIX_GROUPS]; /* first request of each group            */
     int32_t prefix_num_reqs[PA_MAX_PREFIX_GROUPS];  /* consecutive decode requests in it      */
     int32_t prefix_blocks[PA_MAX_PREFIX_GROUPS];    /* leading blocks all of them share       */
+    int32_t prefill_tile_tokens;         /* new tokens per query tile: 32, or 16 / 8 when every
+                                            row with qo_len > 1 fits one such tile (the tile's
+                                            MFMA rows are then all busy, spread over all four
+                                            SIMDs of a CU); a q8_0 pool always runs 32      */
+    int32_t prefix_tile_rows;            /* MFMA rows of a shared-prefix group's tile: 128, or
+                                            64 / 32 when every group has at most 16 / 8 rows */
     int32_t one_launch;                  /* a batch with chunk tiles and decode rows (and no
                                             shared-prefix group, bf16 pool): 0 launches the
                                             chunk tiles, then the decode rows; 1 runs both in

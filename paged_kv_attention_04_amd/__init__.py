@@ -59,6 +59,7 @@ class Plan(ctypes.Structure):
                 ("prefix_first_req", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
                 ("prefix_num_reqs", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
                 ("prefix_blocks", ctypes.c_int32 * PA_MAX_PREFIX_GROUPS),
+                ("prefill_tile_tokens", ctypes.c_int32), ("prefix_tile_rows", ctypes.c_int32),
                 ("one_launch", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64)]
 

@@ -194,11 +194,20 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
     plan->num_reqs = num_reqs;
 
     int64_t total_q = 0;
-    int32_t max_prefill_steps = 0;
+    int32_t max_prefill_steps = 0, max_prefill_q = 0;
     for (int32_t r = 0; r < num_reqs; ++r) {
         if (qo_len[r] < 1 || kv_len[r] < qo_len[r])
             return PA_ERR_SHAPE;
         total_q += qo_len[r];
+        if (qo_len[r] > 1)
+            max_prefill_q = std::max(max_prefill_q, qo_len[r]);
+    }
+    // Query tile: 32 new tokens x 4 query heads = 128 MFMA rows; when every chunk row fits
+    // a tile of 8 or 16 tokens, that smaller tile, whose rows keep all wavefronts (and all
+    // four SIMDs of the CU) busy, where a 32-token tile would leave row groups idle.
+    plan->prefill_tile_tokens = max_prefill_q <= 8 ? 8 : max_prefill_q <= 16 ? 16 : pa::kPrefillQ;
+    plan->prefix_tile_rows = pa::kPrefillQ * pa::kGroup;
+    for (int32_t r = 0; r < num_reqs; ++r) {
         if (qo_len[r] == 1) {
             plan->num_decode_rows++;
         } else {
@@ -206,7 +215,8 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
                 return PA_ERR_UNSUPPORTED;
             int32_t i = plan->num_prefill_rows++;
             plan->prefill_req[i] = r;
-            plan->prefill_tile_start[i + 1] = plan->prefill_tile_start[i] + ceil_div(qo_len[r], pa::kPrefillQ);
+            plan->prefill_tile_start[i + 1] =
+                plan->prefill_tile_start[i] + ceil_div(qo_len[r], plan->prefill_tile_tokens);
             max_prefill_steps = std::max(max_prefill_steps, ceil_div(kv_len[r], pa::kPrefillKeys));
         }
     }
@@ -377,6 +387,11 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
         }
     }
     out.prefix_splits = best_ps;
+    // the prefix tile: 4 rows per request of the largest group; a q8_0 pool runs the full tile
+    int32_t most_reqs = 0;
+    for (int32_t i = 0; i < out.num_prefix_groups; ++i)
+        most_reqs = std::max(most_reqs, out.prefix_num_reqs[i]);
+    out.prefix_tile_rows = q8 ? 128 : most_reqs <= 8 ? 32 : most_reqs <= 16 ? 64 : 128;
     choose_decode_splits(g, R, qo_len, kv_len, skip.data(), num_cus, best_sb, &out);
     const pa_status st = finish_workspace(g, &out);
     if (st != PA_OK)

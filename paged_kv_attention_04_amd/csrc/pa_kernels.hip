@@ -1138,12 +1138,85 @@ __device__ __forceinline__ void pf_read_v(const char* vt, const int (&v_addr)[8]
 // exponentials, and the second chunk's PV products with the denominator sums.
 // The matrix unit thus stays busy while the wavefront works through the softmax.
 // kMask: the step holds keys past some row's position or past kv_hi.
-template <bool kMask>
-__device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* vt, const int (&v_addr)[8],
-                                        const bf16x8 (&qop)[2][4], f32x4 (&oacc)[2][8], float (&m)[2],
-                                        float (&lsum)[2], int key0, int kslice, const int (&qpos)[2], int kv_hi,
+//
+// Tile shapes: kRB row blocks of 16 rows per wavefront and kKB key blocks of 16 keys per
+// wavefront and step.  The full tile (kRB 2, kKB 4) runs the instruction order above; the
+// smaller tiles (kKB 2: one 32-key chunk per wavefront and step) run the same arithmetic
+// in program order.
+template <int kRB, int kKB, bool kMask>
+__device__ __forceinline__ void pf_step(const bf16x8 (&kop)[kKB][4], const char* vt, const int (&v_addr)[8],
+                                        const bf16x8 (&qop)[kRB][4], f32x4 (&oacc)[kRB][8], float (&m)[kRB],
+                                        float (&lsum)[kRB], int key0, int kslice, const int (&qpos)[kRB], int kv_hi,
                                         float scale_log2)
 {
+    if constexpr (kKB == 2) {
+        bf16x8 v0[8];
+        pf_read_v(vt, v_addr, 0, v0);
+        f32x4 sacc[kRB][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) {
+                sacc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    sacc[rb][kb] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb][ks], qop[rb][ks], sacc[rb][kb], 0, 0, 0);
+            }
+        // x[rb][4 kb + e] is the score of key key0 + 16 kb + 4 kslice + e for this lane's row
+        float x[kRB][8];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[rb][4 * kb + e] = sacc[rb][kb][e];
+        if constexpr (kMask) {
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int key = key0 + 16 * (i >> 2) + 4 * kslice + (i & 3);
+                    x[rb][i] = (key > qpos[rb] || key >= kv_hi) ? -INFINITY : x[rb][i];
+                }
+        }
+        float lmax[kRB];
+        bool raise = false;
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            const float a = max3f(x[rb][0], x[rb][1], x[rb][2]);
+            const float b = max3f(x[rb][3], x[rb][4], x[rb][5]);
+            lmax[rb] = max3f(max3f(a, b, x[rb][6]), x[rb][7], -INFINITY) * scale_log2;
+            raise = raise || lmax[rb] > m[rb] + kRescaleSlack;
+        }
+        if (__any(raise)) {
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb) {
+                float t = fmaxf(lmax[rb], shfl_xor(lmax[rb], 16));
+                t = fmaxf(t, shfl_xor(t, 32));
+                if (t > m[rb] + kRescaleSlack) {
+                    const float alpha = (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - t);
+                    m[rb] = t;
+                    lsum[rb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db)
+                        oacc[rb][db] *= alpha;
+                }
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            const float nm = (m[rb] == -INFINITY) ? 0.f : -m[rb];
+            bf16x8 pb;
+            lsum[rb] += pf_exp8(&x[rb][0], nm, scale_log2, pb);
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                oacc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0[db], pb, oacc[rb][db], 0, 0, 0);
+        }
+        return;
+    } else {
+    static_assert(kRB == 2 && kKB == 4, "the full tile: two row blocks and four key blocks per wavefront");
     bf16x8 v0[8];
     pf_read_v(vt, v_addr, 0, v0);
     // key block by key block, so that each K operand is dead once both row blocks used it
@@ -1241,6 +1314,7 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[4][4], const char* v
     for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedValu, 1, 0);
+    }
     }
 }
 
@@ -1402,23 +1476,30 @@ __device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char
 // (exact) to the same LDS places the bf16 copies use and the two scales as floats to a
 // [group][key] table beside the tiles.  The products then run on binary16 operands (Q
 // converted once, exact for bf16 values inside the binary16 range), see pf_step_q8.
-template <bool kCascade, bool kFused = false, bool kQ8 = false>
+template <bool kCascade, bool kFused = false, bool kQ8 = false, int kRG = 4, int kRB = 2>
 __device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
                                                                    int bid)
 {
+    // Tile shape: kRG row groups of kRB row blocks (16 MFMA rows each) and kNKP = 8 / kRG
+    // key parts of kKPW keys of every 128-key step, one wavefront per (row group, key part).
+    static_assert((kRG == 4 && kRB == 2) || (kRG == 2 && (kRB == 2 || kRB == 1)), "tile shapes: 4 x 2, 2 x 2, 2 x 1");
+    static_assert(!kQ8 || (kRG == 4 && kRB == 2), "q8_0 pools run the full tile");
+    constexpr int kNKP = kPfWaves / kRG;              // key parts
+    constexpr int kKPW = kPfKeys / kNKP;              // keys per wavefront and step (64 or 32)
+    constexpr int kKB = kKPW / 16;                    // 16-key blocks per wavefront and step
+    constexpr int kRows = kRG * 16 * kRB;             // MFMA rows of the tile: 128, 64 or 32
+    constexpr int kTileTok = kRows / kGroup;          // chunk tokens of the tile: 32, 16 or 8
     __shared__ __attribute__((aligned(1024))) u32x4 k_tile0[kTileChunks];
     __shared__ __attribute__((aligned(1024))) u32x4 v_tile0[kTileChunks];
     __shared__ __attribute__((aligned(1024))) u32x4 k_tile1[kTileChunks];
     __shared__ __attribute__((aligned(1024))) u32x4 v_tile1[kTileChunks];
-    __shared__ float x_m[4][2][64];     // key-half merge: running maxima of the kh = 1 wavefronts
-    __shared__ float x_l[4][2][64];     // and their lane-partial denominators
     __shared__ int last_lds;
     // q8_0: scales of the staged keys, [buffer pair][K, V][group][key]
     __shared__ __attribute__((aligned(16))) float q8_sc[kQ8 ? 2 * 2 * 4 * kPfKeys : 4];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int rg = wave & 3, kh = wave >> 2;
+    const int rg = wave % kRG, kh = wave / kRG;     // row group, key part
     const int kvh = bid % p.num_kv_heads;
     const int rest = bid / p.num_kv_heads;
     const int split = rest % p.splits;
@@ -1448,29 +1529,29 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         q0 = p.qo_indptr[r];
         qlen = p.qo_indptr[r + 1] - q0;
         kvlen = p.kv_len[r];
-        if (qt * pa::kPrefillQ >= qlen)         // the same for every split of the tile
+        if (qt * kTileTok >= qlen)              // the same for every split of the tile
             return;
         ctx = kvlen - qlen;                     // tokens before this chunk
         nblk_row = (kvlen + kBlock - 1) / kBlock;
         bad_row = qlen < 2 || ctx < 0 || nblk_row > p.max_blocks;
         // keys any token of this tile can see: 0 .. ctx + last token of the tile
-        kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * pa::kPrefillQ));
+        kv_hi = bad_row ? 0 : min(kvlen, ctx + min(qlen, (qt + 1) * kTileTok));
     }
     // Row groups with no valid row skip the products (their wavefronts still copy their
     // block of every step and meet every barrier).
-    const int valid_rows = kCascade ? 4 * grp_count : min(kPfRows, 4 * (qlen - qt * pa::kPrefillQ));
-    const bool active = 32 * rg < valid_rows;
+    const int valid_rows = kCascade ? 4 * grp_count : min(kRows, 4 * (qlen - qt * kTileTok));
+    const bool active = 16 * kRB * rg < valid_rows;
     const int nsteps_tile = (kv_hi + kPfKeys - 1) / kPfKeys;
     const int s_begin = split * nsteps_tile / p.splits;
     const int nsteps = (split + 1) * nsteps_tile / p.splits - s_begin;
 
     const int row16 = lane & 15, kslice = lane >> 4;
-    // this lane's two rows (row blocks rb = 0, 1)
-    int qpos[2];
-    bf16x8 qop[2][4];
+    // this lane's rows (row blocks rb = 0 .. kRB - 1)
+    int qpos[kRB];
+    bf16x8 qop[kRB][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int rho = 32 * rg + 16 * rb + row16;
+    for (int rb = 0; rb < kRB; ++rb) {
+        const int rho = 16 * kRB * rg + 16 * rb + row16;
         int qidx;
         bool ok;
         if constexpr (kCascade) {
@@ -1479,7 +1560,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             qidx = ok ? p.qo_indptr[grp_first + slot] : 0;
             qpos[rb] = INT_MAX;                 // every shared key precedes the query
         } else {
-            const int tl = qt * pa::kPrefillQ + (rho >> 2);
+            const int tl = qt * kTileTok + (rho >> 2);
             qpos[rb] = ctx + tl;
             ok = tl < qlen;
             qidx = q0 + tl;
@@ -1620,17 +1701,18 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         }
     };
     // LDS byte offsets of this lane's operand reads within a K or V tile.  K: key
-    // 64 kh + 16 kb + row16, chunk 4 ks + kslice (kb adds 4 KiB).  V: source lane i16 of
+    // kKPW kh + 16 kb + row16, chunk 4 ks + kslice (kb adds 4 KiB).  V: source lane i16 of
     // group kslice points at key 4 kslice + i16/4 (+16) of chunk c, dims 16 db + 4 (i16 % 4)
     // .. +4, and lane (kslice, i16) receives dim 16 db + i16 of keys 4 kslice + 0..3 (+16)
-    // (c adds 8 KiB, +16 keys 4 KiB).
+    // (c adds 8 KiB, +16 keys 4 KiB).  kKPW kh is a multiple of 32, so the swizzle, which
+    // sees a key's low four bits, is the same for every key part.
     int k_addr[4], v_addr[8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-        k_addr[ks] = (64 * kh + row16) * 256 + (((ks * 4 + kslice) ^ pf_swz(row16)) << 4);
+        k_addr[ks] = (kKPW * kh + row16) * 256 + (((ks * 4 + kslice) ^ pf_swz(row16)) << 4);
     {
         const int i16 = lane & 15;
-        const int k_lo = 64 * kh + 4 * kslice + (i16 >> 2);
+        const int k_lo = kKPW * kh + 4 * kslice + (i16 >> 2);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const int cc = 2 * db + ((i16 & 3) >> 1);
@@ -1638,20 +1720,23 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         }
     }
 
-    f32x4 oacc[2][8];
+    f32x4 oacc[kRB][8];
+    float m[kRB], lsum[kRB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < kRB; ++rb) {
+        m[rb] = -INFINITY;
+        lsum[rb] = 0.f;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
             oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+    }
 
     // Step order: the steps no row of the tile needs masked first, rotated so that
     // workgroups of neighbouring query tiles start one step apart (at any time each K / V
     // step is then fetched from memory by one workgroup and found in the XCD's L2 by the
     // others: all tiles of one KV head run on one XCD), then the diagonal and tail steps.
     // smallest query position of the tile (a shared prefix masks only past its end)
-    const int qmin = kCascade ? kv_hi - 1 : ctx + qt * pa::kPrefillQ;
+    const int qmin = kCascade ? kv_hi - 1 : ctx + qt * kTileTok;
     const int s_masked = max(s_begin, min(s_begin + nsteps, (qmin + 1) / kPfKeys));
     const int n_plain = s_masked - s_begin;
     const int rot = (!kCascade && n_plain > 0) ? qt % n_plain : 0;
@@ -1683,9 +1768,9 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             next_id = table_entry(step_at(it + 2));
             return;
         }
-        bf16x8 kop[4][4];
+        bf16x8 kop[kKB][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 kop[kb][ks] = *reinterpret_cast<const bf16x8*>(kt + k_addr[ks] + kb * 4096);
@@ -1705,8 +1790,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             pf_step_q8<decltype(msk)::value>(kop, vt, v_addr, ksc, ksc + 4 * kPfKeys, qop, oacc, m, lsum,
                                              s * kPfKeys + 64 * kh, kh, kslice, qpos, kv_hi, p.scale_log2);
         } else {
-            pf_step<decltype(msk)::value>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + 64 * kh, kslice, qpos,
-                                          kv_hi, p.scale_log2);
+            pf_step<kRB, kKB, decltype(msk)::value>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + kKPW * kh,
+                                                    kslice, qpos, kv_hi, p.scale_log2);
         }
     };
     // Steps alternate between the two buffer pairs; each loop is unrolled by two so that
@@ -1729,13 +1814,13 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
 
     // Fused append: split 0 of each (tile, KV head) writes the tile's new tokens of this KV
     // head into their slots (every workgroup of the launch reads new positions from k_new /
-    // v_new, see `stage`).  The rows are loaded here and stored after the key-half merge,
+    // v_new, see `stage`).  The rows are loaded here and stored after the key-part merge,
     // so that their load latency hides behind it.
     u32x4 new_k = u32x4{0u, 0u, 0u, 0u}, new_v = new_k;
     int64_t new_dst = -1;
     if constexpr (kFused) {
-        const int tl = qt * pa::kPrefillQ + (tid >> 4), c = tid & 15;          // 32 tokens x 16 chunks
-        if (split == 0 && !bad_row && tl < qlen) {
+        const int tl = qt * kTileTok + (tid >> 4), c = tid & 15;          // kTileTok tokens x 16 chunks
+        if (split == 0 && !bad_row && (tid >> 4) < kTileTok && tl < qlen) {
             const int pos = ctx + tl;
             const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
             if (phys >= 0 && phys < p.num_blocks) {
@@ -1747,18 +1832,32 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         }
     }
 
-    // merge the two key halves: the kh = 1 wavefronts hand (m, lane-partial l, O^T) to the
-    // kh = 0 wavefront with the same rows, in the lanes' own layout
+    // Merge the key parts: the wavefronts of key parts 1 .. kNKP - 1 hand (m, lane-partial l,
+    // O^T) to the key-part-0 wavefront with the same rows, in the lanes' own layout.  The
+    // O^T blocks (kRB x 8 KiB per wavefront) fill the first three tile buffers in (key part,
+    // row group) order, the maxima and sums sit in the fourth; every wavefront is past its
+    // last LDS read of the tiles and its last copy has landed.
     __syncthreads();
-    u32x4* xo = (rg < 2 ? k_tile0 : v_tile0) + (rg & 1) * (kPfAcc * 64);
-    if (kh == 1) {
+    auto xo_at = [&](int kp) __attribute__((always_inline)) {
+        const int e = ((kp - 1) * kRG + rg) * (kRB * 8 * 64);     // 16-byte units
+        const int bi = e / kTileChunks;
+        u32x4* base = bi == 0 ? k_tile0 : (bi == 1 ? v_tile0 : k_tile1);
+        return base + (e - bi * kTileChunks);
+    };
+    static_assert((kNKP - 1) * kRG * kRB * 8 * 64 <= 3 * kTileChunks, "key-part partials fit three tile buffers");
+    float* const xm = reinterpret_cast<float*>(v_tile1);              // [kNKP - 1][kRG][kRB][64]
+    float* const xl = xm + 1024;
+    static_assert((kNKP - 1) * kRG * kRB * 64 <= 1024, "key-part maxima fit");
+    if (kh > 0) {
+        u32x4* xo = xo_at(kh);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
 #pragma unroll
             for (int db = 0; db < 8; ++db)
                 xo[(rb * 8 + db) * 64 + lane] = __builtin_bit_cast(u32x4, oacc[rb][db]);
-            x_m[rg][rb][lane] = m[rb];
-            x_l[rg][rb][lane] = lsum[rb];
+            const int mi = (((kh - 1) * kRG + rg) * kRB + rb) * 64 + lane;
+            xm[mi] = m[rb];
+            xl[mi] = lsum[rb];
         }
     }
     bad = __syncthreads_or(bad);
@@ -1769,21 +1868,42 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         }
     }
     const float nan = __builtin_nanf("");
-    float lse2[2] = {-INFINITY, -INFINITY};     // log2-sum-exp of this workgroup's keys per row
+    float lse2[kRB];                            // log2-sum-exp of this workgroup's keys per row
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+        lse2[rb] = -INFINITY;
     if (kh == 0) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const float m1 = x_m[rg][rb][lane], l1 = x_l[rg][rb][lane];
-            const float M = fmaxf(m[rb], m1);
-            const float w0 = (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - M);
-            const float w1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - M);
-            float l = w0 * lsum[rb] + w1 * l1;
+        for (int rb = 0; rb < kRB; ++rb) {
+            float mk[kNKP], lk[kNKP], w[kNKP];
+            mk[0] = m[rb];
+            lk[0] = lsum[rb];
+            float M = m[rb];
+#pragma unroll
+            for (int kp = 1; kp < kNKP; ++kp) {
+                const int mi = (((kp - 1) * kRG + rg) * kRB + rb) * 64 + lane;
+                mk[kp] = xm[mi];
+                lk[kp] = xl[mi];
+                M = fmaxf(M, mk[kp]);
+            }
+#pragma unroll
+            for (int kp = 0; kp < kNKP; ++kp)
+                w[kp] = (mk[kp] == -INFINITY) ? 0.f : fast_exp2(mk[kp] - M);
+            float l = w[0] * lk[0] + w[1] * lk[1];
+#pragma unroll
+            for (int kp = 2; kp < kNKP; ++kp)
+                l += w[kp] * lk[kp];
             l += shfl_xor(l, 16);
             l += shfl_xor(l, 32);
             const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-            for (int db = 0; db < 8; ++db)
-                oacc[rb][db] = (w0 * oacc[rb][db] + w1 * __builtin_bit_cast(f32x4, xo[(rb * 8 + db) * 64 + lane])) * inv;
+            for (int db = 0; db < 8; ++db) {
+                f32x4 o = w[0] * oacc[rb][db] + w[1] * __builtin_bit_cast(f32x4, xo_at(1)[(rb * 8 + db) * 64 + lane]);
+#pragma unroll
+                for (int kp = 2; kp < kNKP; ++kp)
+                    o += w[kp] * __builtin_bit_cast(f32x4, xo_at(kp)[(rb * 8 + db) * 64 + lane]);
+                oacc[rb][db] = o * inv;
+            }
             lse2[rb] = bad ? nan : (l > 0.f ? M + fast_log2(l) : -INFINITY);
         }
     }
@@ -1804,8 +1924,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         __syncthreads();                        // the key-half exchange above is done with k_tile0 / v_tile0
         if (kh == 0) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int rho = 32 * rg + 16 * rb + row16;
+            for (int rb = 0; rb < kRB; ++rb) {
+                const int rho = 16 * kRB * rg + 16 * rb + row16;
 #pragma unroll
                 for (int db = 0; db < 8; ++db)
                     *stage_at(rho, 4 * db + kslice) = __builtin_bit_cast(u32x4, oacc[rb][db]);
@@ -1854,11 +1974,11 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     }
 
     // output: lane l holds O^T[16 db + 4 kslice + e][row row16] of row block rb
-    auto write_out = [&](const f32x4 (&o)[2][8], const float (&lse_row)[2]) __attribute__((always_inline)) {
+    auto write_out = [&](const f32x4 (&o)[kRB][8], const float (&lse_row)[kRB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const int rho = 32 * rg + 16 * rb + row16;
-            const int tl = qt * pa::kPrefillQ + (rho >> 2);
+        for (int rb = 0; rb < kRB; ++rb) {
+            const int rho = 16 * kRB * rg + 16 * rb + row16;
+            const int tl = qt * kTileTok + (rho >> 2);
             if (tl >= qlen)
                 continue;
             const bool nan_row = lse_row[rb] != lse_row[rb];
@@ -1884,17 +2004,19 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     // caches) and every thread waits until its stores have completed before the
     // workgroup counts itself in; the last split reads them with agent-scope loads.
     const int64_t item0 = ((int64_t)tile * p.num_kv_heads + kvh) * p.splits;   // split 0 of this (tile, KV head)
-    auto part_o_at = [&](int sp) __attribute__((always_inline)) { return p.part_o + ((item0 + sp) * 4 + rg) * (kPfAcc * 4 * 64); };
-    auto part_lse_at = [&](int sp) __attribute__((always_inline)) { return p.part_lse + ((item0 + sp) * 4 + rg) * 128; };   // 2 x 64 per row group
+    // per (tile, KV head, split): kRG row groups of kRB x 8 f32x4 per lane, and kRB x 64
+    // log2-sum-exps per row group, in lane order
+    auto part_o_at = [&](int sp) __attribute__((always_inline)) { return p.part_o + ((item0 + sp) * kRG + rg) * (kRB * 8 * 4 * 64); };
+    auto part_lse_at = [&](int sp) __attribute__((always_inline)) { return p.part_lse + ((item0 + sp) * kRG + rg) * (kRB * 64); };
     if (kh == 0) {
         float* po = part_o_at(split);
 #pragma unroll
-        for (int i = 0; i < kPfAcc; ++i)
+        for (int i = 0; i < kRB * 8; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 store_agent(po + (i * 4 + e) * 64 + lane, oacc[i >> 3][i & 7][e]);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < kRB; ++rb)
             store_agent(part_lse_at(split) + rb * 64 + lane, lse2[rb]);
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -1922,37 +2044,42 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         auto lse_of = [&](int sp, int rb) __attribute__((always_inline)) {
             return sp == split ? lse2[rb] : load_agent(part_lse_at(sp) + rb * 64 + lane);
         };
-        float L[2] = {-INFINITY, -INFINITY};
+        float L[kRB];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+            L[rb] = -INFINITY;
         bool any_nan = false;
         for (int s0 = 0; s0 < p.splits; s0 += 8) {
-            float ls[8][2];
+            float ls[8][kRB];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < kRB; ++rb)
                     ls[u][rb] = lse_of(min(s0 + u, p.splits - 1), rb);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
+                for (int rb = 0; rb < kRB; ++rb)
                     if (s0 + u < p.splits) {
                         any_nan |= ls[u][rb] != ls[u][rb];
                         L[rb] = fmaxf(L[rb], ls[u][rb]);
                     }
         }
-        float wsum[2] = {0.f, 0.f};
-        f32x4 o[2][8];
+        float wsum[kRB];
+        f32x4 o[kRB][8];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < kRB; ++rb) {
+            wsum[rb] = 0.f;
 #pragma unroll
             for (int db = 0; db < 8; ++db)
                 o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         for (int sp = 0; sp < p.splits; ++sp) {
-            float c[2];
-            f32x4 os[2][8];
+            float c[kRB];
+            f32x4 os[kRB][8];
             if (sp == split) {
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
+                for (int rb = 0; rb < kRB; ++rb) {
                     c[rb] = lse2[rb];
 #pragma unroll
                     for (int db = 0; db < 8; ++db)
@@ -1961,7 +2088,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             } else {
                 const float* po = part_o_at(sp);
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
+                for (int rb = 0; rb < kRB; ++rb) {
                     c[rb] = load_agent(part_lse_at(sp) + rb * 64 + lane);
 #pragma unroll
                     for (int db = 0; db < 8; ++db)
@@ -1971,7 +2098,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 }
             }
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < kRB; ++rb) {
                 const float w = (c[rb] > -INFINITY) ? fast_exp2(c[rb] - L[rb]) : 0.f;
                 wsum[rb] += w;
 #pragma unroll
@@ -1980,7 +2107,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             }
         }
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < kRB; ++rb) {
             const float inv = wsum[rb] > 0.f ? 1.f / wsum[rb] : 0.f;
 #pragma unroll
             for (int db = 0; db < 8; ++db)
@@ -1990,10 +2117,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     }
     write_out(oacc, lse2);
 }
-template <bool kFused, bool kQ8>
+template <bool kFused, bool kQ8, int kRG, int kRB>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
 {
-    prefill_body<false, kFused, kQ8>(p, DecodeParams{}, blockIdx.x);
+    prefill_body<false, kFused, kQ8, kRG, kRB>(p, DecodeParams{}, blockIdx.x);
 }
 
 static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
@@ -2003,12 +2130,12 @@ static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs bot
 // form), the rest are the decode workgroups.  The prefix workgroups come first in the
 // grid and wait for nothing; a (row, KV head) is finished by whichever of its decode
 // splits and prefix splits arrives last, so no workgroup ever waits for another.
-template <bool kQ8, bool kFused>
+template <bool kQ8, bool kFused, int kRG, int kRB>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_cascade_decode(PrefillParams pp, DecodeParams dp,
                                                                  int32_t num_prefix_wgs)
 {
     if ((int32_t)blockIdx.x < num_prefix_wgs)
-        prefill_body<true, false, kQ8>(pp, dp, blockIdx.x);
+        prefill_body<true, false, kQ8, kRG, kRB>(pp, dp, blockIdx.x);
     else
         decode_body<kQ8, kFused>(dp, blockIdx.x - num_prefix_wgs);
 }
@@ -2191,6 +2318,43 @@ extern "C" pa_status pa_copy_blocks_q8(const pa_geometry* g, void* kv_pool_q8, c
     return copy_blocks(g, kv_pool_q8, kv_pool_q8, src_blocks, dst_blocks, n, stream, 2 * pa::kQ8TileBytes, 1);
 }
 
+// Tile shape (row groups, row blocks per wavefront) of a tile of `rows` MFMA rows.
+static bool tile_rows_supported(int rows) { return rows == 32 || rows == 64 || rows == 128; }
+
+template <typename... Args>
+static void launch(void (*kernel)(Args...), uint32_t grid, hipStream_t st, Args... args)
+{
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kPfWaves), 0, st, args...);
+}
+
+static void launch_prefill_tiles(bool q8, bool fused, int rows, uint32_t grid, hipStream_t st, const PrefillParams& pp)
+{
+    if (q8)
+        launch(pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
+    else if (rows == 32)
+        launch(fused ? pa_prefill_tile<true, false, 2, 1> : pa_prefill_tile<false, false, 2, 1>, grid, st, pp);
+    else if (rows == 64)
+        launch(fused ? pa_prefill_tile<true, false, 2, 2> : pa_prefill_tile<false, false, 2, 2>, grid, st, pp);
+    else
+        launch(fused ? pa_prefill_tile<true, false, 4, 2> : pa_prefill_tile<false, false, 4, 2>, grid, st, pp);
+}
+
+static void launch_cascade(bool q8, bool fused, int rows, uint32_t grid, hipStream_t st, const PrefillParams& pp,
+                           const DecodeParams& dp, int32_t nprefix)
+{
+    if (q8)
+        launch(pa_cascade_decode<true, false, 4, 2>, grid, st, pp, dp, nprefix);
+    else if (rows == 32)
+        launch(fused ? pa_cascade_decode<false, true, 2, 1> : pa_cascade_decode<false, false, 2, 1>, grid, st, pp, dp,
+               nprefix);
+    else if (rows == 64)
+        launch(fused ? pa_cascade_decode<false, true, 2, 2> : pa_cascade_decode<false, false, 2, 2>, grid, st, pp, dp,
+               nprefix);
+    else
+        launch(fused ? pa_cascade_decode<false, true, 4, 2> : pa_cascade_decode<false, false, 4, 2>, grid, st, pp, dp,
+               nprefix);
+}
+
 // The plan's view of the rows must be that of the device lengths: the same rows with
 // qo_len > 1, in order and with their tile counts, every other row a decode row whose
 // splits fit max_splits, and shared-prefix groups made of decode rows with blocks past
@@ -2214,7 +2378,7 @@ static pa_status check_plan_matches(const pa_plan_t* plan, const std::vector<int
         } else {
             if (np >= plan->num_prefill_rows || plan->prefill_req[np] != r || skip[r] != 0 ||
                 plan->prefill_tile_start[np + 1] - plan->prefill_tile_start[np] !=
-                    (qo[r] + pa::kPrefillQ - 1) / pa::kPrefillQ)
+                    (qo[r] + plan->prefill_tile_tokens - 1) / plan->prefill_tile_tokens)
                 return PA_ERR_SHAPE;
             ++np;
         }
@@ -2241,13 +2405,14 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         return PA_ERR_NULL;
     if (max_blocks_per_req < 1 || plan->num_prefill_rows > PA_MAX_PREFILL_ROWS)
         return PA_ERR_SHAPE;
-    if (plan->prefill_tiles > 0 && (plan->prefill_splits < 1 || plan->prefill_splits > pa::kMaxPrefillSplits))
+    if (plan->prefill_tiles > 0 && (plan->prefill_splits < 1 || plan->prefill_splits > pa::kMaxPrefillSplits ||
+                                    !tile_rows_supported(kGroup * plan->prefill_tile_tokens)))
         return PA_ERR_SHAPE;
     const int ngroups = plan->num_prefix_groups;
     if (ngroups < 0 || ngroups > PA_MAX_PREFIX_GROUPS ||
         (ngroups > 0 && (plan->prefix_splits < 1 || plan->prefix_splits > pa::kMaxPrefillSplits)))
         return PA_ERR_SHAPE;
-    if (ngroups > 0 && (plan->num_decode_rows < 1 || plan->max_splits < 1))
+    if (ngroups > 0 && (plan->num_decode_rows < 1 || plan->max_splits < 1 || !tile_rows_supported(plan->prefix_tile_rows)))
         return PA_ERR_SHAPE;
     for (int i = 0; i < ngroups; ++i)
         for (int j = 0; j < i; ++j)          // a row belongs to at most one group
@@ -2257,6 +2422,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
     for (int i = 0; i < ngroups; ++i)
         if (plan->prefix_first_req[i] < 0 || plan->prefix_num_reqs[i] < 1 ||
             plan->prefix_num_reqs[i] > PA_MAX_PREFIX_GROUP_REQS ||
+            (!q8 && kGroup * plan->prefix_num_reqs[i] > plan->prefix_tile_rows) ||
             plan->prefix_first_req[i] + plan->prefix_num_reqs[i] > plan->num_reqs || plan->prefix_blocks[i] < 1 ||
             plan->prefix_blocks[i] > max_blocks_per_req)
             return PA_ERR_SHAPE;
@@ -2322,7 +2488,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
     };
 
     // chunk tiles and decode rows in one launch (bf16 pool, no shared-prefix group)
-    const bool one_launch = plan->one_launch >= 1 && !q8 && ngroups == 0 && plan->num_prefill_rows > 0 &&
+    const bool one_launch = plan->one_launch >= 1 && !q8 && ngroups == 0 && plan->prefill_tile_tokens == 32 &&
+                            plan->num_prefill_rows > 0 &&
                             plan->prefill_tiles > 0 && plan->num_decode_rows > 0 && plan->max_splits > 0;
     PrefillParams mixed_pp = {};
     int64_t mixed_prefill_wgs = 0;
@@ -2359,12 +2526,9 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         if (one_launch) {
             mixed_pp = pp;
             mixed_prefill_wgs = grid;
-        } else if (q8)
-            hipLaunchKernelGGL((pa_prefill_tile<false, true>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
-        else if (fused)
-            hipLaunchKernelGGL((pa_prefill_tile<true, false>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
-        else
-            hipLaunchKernelGGL((pa_prefill_tile<false, false>), dim3((uint32_t)grid), dim3(64 * kPfWaves), 0, st, pp);
+        } else {
+            launch_prefill_tiles(q8, fused, q8 ? 128 : kGroup * plan->prefill_tile_tokens, (uint32_t)grid, st, pp);
+        }
         if (!one_launch && hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
     }
@@ -2417,15 +2581,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             const int64_t nprefix = (int64_t)ngroups * g->num_kv_heads * plan->prefix_splits;
             if (grid + nprefix > INT32_MAX)
                 return PA_ERR_SHAPE;
-            if (q8)
-                hipLaunchKernelGGL((pa_cascade_decode<true, false>), dim3((uint32_t)(grid + nprefix)),
-                                   dim3(64 * kPfWaves), 0, st, pp, dp, (int32_t)nprefix);
-            else if (fused)
-                hipLaunchKernelGGL((pa_cascade_decode<false, true>), dim3((uint32_t)(grid + nprefix)),
-                                   dim3(64 * kPfWaves), 0, st, pp, dp, (int32_t)nprefix);
-            else
-                hipLaunchKernelGGL((pa_cascade_decode<false, false>), dim3((uint32_t)(grid + nprefix)),
-                                   dim3(64 * kPfWaves), 0, st, pp, dp, (int32_t)nprefix);
+            launch_cascade(q8, fused, q8 ? 128 : plan->prefix_tile_rows, (uint32_t)(grid + nprefix), st, pp, dp,
+                           (int32_t)nprefix);
         } else if (one_launch) {
             if (grid + mixed_prefill_wgs > INT32_MAX)
                 return PA_ERR_SHAPE;

@@ -31,7 +31,7 @@ def test_struct_sizes_match_header(lib):
     # int32 x 11 + 128 + 129, then 2 + 3 x 16 int32 of the prefix groups, then a uint64 at
     # an 8-byte boundary; the library reports the size its own compiler gives the struct
     assert ctypes.sizeof(pa.Geometry) == 24
-    assert ctypes.sizeof(pa.Plan) == 8 * ((4 * (11 + 128 + 129 + 2 + 3 * 16 + 1) + 7) // 8) + 8
+    assert ctypes.sizeof(pa.Plan) == 8 * ((4 * (11 + 128 + 129 + 2 + 3 * 16 + 3) + 7) // 8) + 8
     lib.pa_plan_struct_bytes.restype = ctypes.c_size_t
     assert lib.pa_plan_struct_bytes() == ctypes.sizeof(pa.Plan)
 
