@@ -53,11 +53,12 @@ def _run_both(wl, split_blocks, prefill_splits, cascade):
 
 
 def _check_against_oracle(wl, out, lse):
-    _, _, ref = oracle.run_workload(wl)
-    got, want = bf16_bits_to_f32(out), bf16_bits_to_f32(ref["out"])
+    """The bars against the oracle's exact (fp64) outputs and LSE."""
+    _, _, ref = oracle.run_workload(wl, want_f64=True)
+    got = bf16_bits_to_f32(out).astype(np.float64)
     assert not np.isnan(got).any()
-    eo = float(np.max(np.abs(got - want)))
-    el = float(np.max(np.abs(lse - ref["lse"])))
+    eo = float(np.max(np.abs(got - ref["out_f64"])))
+    el = float(np.max(np.abs(lse.astype(np.float64) - ref["lse_f64"])))
     print(f"[gpu]   vs oracle max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
     assert eo <= TOL_O and el <= TOL_LSE
 
