@@ -40,6 +40,11 @@
  * kv_len counts the tokens after this step's append, so a row sees its own new
  * token: call pa_append_kv before pa_attention_batch on the same stream.
  *
+ * Work is cut per "virtual KV head": a workgroup serves four query heads of one KV
+ * head, so a KV head with G = num_q_heads / num_kv_heads query heads takes
+ * ceil(G / 4) virtual heads (G < 4 leaves head slots idle).  Counts of
+ * (row, KV head) or (tile, KV head) pairs below are over virtual KV heads.
+ *
  * Ownership and ordering: the caller allocates and owns every buffer (device
  * memory for everything the kernels touch, host memory for plans and the
  * validators' inputs).  The library allocates no device memory and keeps no
@@ -87,7 +92,7 @@ typedef enum pa_status {
 /* One layer's attention geometry and pool size. */
 typedef struct pa_geometry {
     int32_t num_q_heads;   /* query heads (32 for Qwen3-8B)                                   */
-    int32_t num_kv_heads;  /* KV heads (8 for Qwen3-8B); num_q_heads / num_kv_heads must be 4  */
+    int32_t num_kv_heads;  /* KV heads (8 for Qwen3-8B); must divide num_q_heads               */
     int32_t head_dim;      /* must be 128                                                      */
     int32_t block_size;    /* tokens per block; must be 16                                     */
     int32_t num_blocks;    /* physical blocks in each of the K and V pools                     */
@@ -113,7 +118,7 @@ typedef struct pa_plan_t {
     int32_t num_prefill_rows;            /* rows with qo_len > 1                              */
     int32_t split_blocks;                /* KV blocks per decode split (one workgroup each)   */
     int32_t max_splits;                  /* largest split count of any decode row             */
-    int32_t decode_items;                /* (row, KV head, split) decode workgroups           */
+    int32_t decode_items;                /* (row, virtual KV head, split) decode workgroups   */
     int32_t prefill_tiles;               /* query tiles over all prefill rows                 */
     int32_t prefill_splits;              /* key splits per prefill tile (one workgroup each)  */
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];       /* request index of each prefill row      */

@@ -43,6 +43,7 @@ int32_t decode_blocks(const int32_t* kv_len, const int32_t* skip, int32_t r)
 void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t* qo_len, const int32_t* kv_len,
                           const int32_t* skip, int32_t num_cus, int32_t split_blocks, pa_plan_t* plan)
 {
+    const int32_t vheads = pa::num_vheads(g->num_q_heads, g->num_kv_heads);   // workgroups per split of a row
     int32_t longest = 1;
     for (int32_t r = 0; r < num_reqs; ++r)
         if (qo_len[r] == 1)
@@ -63,7 +64,7 @@ void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t*
             int64_t wgs = 0;
             for (int32_t r = 0; r < num_reqs; ++r)
                 if (qo_len[r] == 1)
-                    wgs += (int64_t)ceil_div(decode_blocks(kv_len, skip, r), cand) * g->num_kv_heads;
+                    wgs += (int64_t)ceil_div(decode_blocks(kv_len, skip, r), cand) * vheads;
             const int64_t cost = (wgs + target - 1) / target * (cand + kWorkgroupOverheadBlocks);
             if (cost < best_cost) {
                 best_cost = cost;
@@ -79,7 +80,7 @@ void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t*
             continue;
         const int32_t s = ceil_div(decode_blocks(kv_len, skip, r), sb);
         max_splits = std::max(max_splits, s);
-        items += (int64_t)s * g->num_kv_heads;
+        items += (int64_t)s * vheads;
     }
     plan->max_splits = max_splits;
     plan->decode_items = (int32_t)std::min<int64_t>(items, INT32_MAX);
@@ -122,7 +123,7 @@ constexpr MakespanCosts kPrefixCostsQ8 = {23.0 / kQ8BlockRatio, 5.57 / kQ8BlockR
 constexpr int32_t kPrefixStepsPerSplitQ8[] = {4, 3};
 
 double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_blocks, const int32_t* qo_len,
-                      int32_t num_kv_heads, int32_t num_cus, int32_t prefix_splits, int32_t split_blocks,
+                      int32_t num_vheads, int32_t num_cus, int32_t prefix_splits, int32_t split_blocks,
                       const MakespanCosts& c)
 {
     std::map<double, int64_t> free_at;     // time -> CUs that become free then
@@ -144,7 +145,7 @@ double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_
         const int32_t steps = ceil_div((int64_t)plan.prefix_blocks[gi] * pa::kBlock, pa::kPrefillKeys);
         for (int32_t sp = 0; sp < prefix_splits; ++sp) {
             const int32_t n = (sp + 1) * steps / prefix_splits - sp * steps / prefix_splits;
-            run(num_kv_heads, c.prefix_fixed + c.prefix_step * n + c.prefix_per_req * plan.prefix_num_reqs[gi]);
+            run(num_vheads, c.prefix_fixed + c.prefix_step * n + c.prefix_per_req * plan.prefix_num_reqs[gi]);
         }
     }
     int32_t max_splits = 0;
@@ -160,7 +161,7 @@ double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_
             if (n <= 0)
                 continue;
             const double merge = sp == ns - 1 ? c.merge_per8 * (ceil_div(ns, 8) + ceil_div(prefix_splits, 8)) : 0.0;
-            run(num_kv_heads, c.decode_fixed + n + merge);
+            run(num_vheads, c.decode_fixed + n + merge);
         }
     return end;
 }
@@ -238,7 +239,8 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
         if (prefill_splits > 0) {
             ps = prefill_splits;
         } else {
-            const int64_t base = (int64_t)plan->prefill_tiles * g->num_kv_heads;
+            const int32_t vheads = pa::num_vheads(g->num_q_heads, g->num_kv_heads);
+            const int64_t base = (int64_t)plan->prefill_tiles * vheads;
             const int64_t cus = std::max(num_cus, 1);
             int64_t best_cost = INT64_MAX;
             for (int32_t cand = 1; cand <= pa::kMaxPrefillSplits; ++cand) {
@@ -254,7 +256,7 @@ extern "C" pa_status pa_plan(const pa_geometry* g, int32_t num_reqs, const int32
                 }
             }
             // fall back to unsplit tiles when the counters would not fit
-            if (ps > 1 && (int64_t)num_reqs * g->num_kv_heads + base > pa::kMaxCounters)
+            if (ps > 1 && (int64_t)num_reqs * vheads + base > pa::kMaxCounters)
                 ps = 1;
         }
     }
@@ -294,6 +296,7 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
     pa_plan_t out = *plan;
     out.num_prefix_groups = 0;
     int32_t max_prefix_blocks = 0;
+    const int32_t vheads = pa::num_vheads(g->num_q_heads, g->num_kv_heads);
     for (int32_t r = 0; r < R && out.num_prefix_groups < PA_MAX_PREFIX_GROUPS;) {
         if (qo_len[r] != 1 || shareable(r) < min_shared) {
             ++r;
@@ -358,7 +361,7 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
                 continue;
             if (sb < kMinAutoSplitBlocks && parts > 1)
                 break;
-            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb,
+            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb,
                                             q8 ? kSplitCostsQ8 : kSplitCosts);
             if (!have || t < best - 1e-9) {
                 have = true;
@@ -377,7 +380,7 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
         for (const int32_t per : q8 ? kPrefixStepsPerSplitQ8 : kPrefixStepsPerSplit) {
             const int32_t ps = std::min(std::max(1, ceil_div(steps, per)), pa::kMaxPrefillSplits);
             const int32_t sb = best_split_length(ps);
-            const double t = fused_makespan(out, suffix, qo_len, g->num_kv_heads, num_cus, ps, sb,
+            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb,
                                             q8 ? kPrefixCostsQ8 : kPrefixCosts);
             if (best_ps == 0 || t < best - 1e-9) {
                 best = t;
@@ -504,7 +507,7 @@ extern "C" const char* pa_status_string(pa_status s)
     case PA_ERR_SHAPE: return "inconsistent lengths (need 1 <= qo_len <= kv_len and enough table entries)";
     case PA_ERR_RANGE: return "block id or slot outside the pool, or a repeated slot";
     case PA_ERR_WORKSPACE: return "workspace smaller than the plan needs";
-    case PA_ERR_UNSUPPORTED: return "unsupported geometry (need head_dim 128, block_size 16, 4 query heads per KV head)";
+    case PA_ERR_UNSUPPORTED: return "unsupported geometry (need head_dim 128, block_size 16, query heads a multiple of KV heads)";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_NO_BLOCKS: return "not enough free blocks";
     }

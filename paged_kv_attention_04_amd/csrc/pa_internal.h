@@ -26,25 +26,37 @@ static_assert(kQ8TileBytes == PA_Q8_TILE_BYTES, "header and kernels agree on the
 
 inline bool geometry_supported(const pa_geometry* g)
 {
-    return g->head_dim == kHeadDim && g->block_size == kBlock && g->num_kv_heads > 0 &&
-           g->num_q_heads == g->num_kv_heads * kGroup && g->num_blocks > 0;
+    return g->head_dim == kHeadDim && g->block_size == kBlock && g->num_kv_heads > 0 && g->num_q_heads > 0 &&
+           g->num_q_heads % g->num_kv_heads == 0 && g->num_blocks > 0;
+}
+
+// Workgroups serve kGroup query heads of one KV head.  A KV head with G = Hq / Hkv query
+// heads is served in ceil(G / kGroup) slices ("virtual KV heads"); slice s holds its query
+// heads kGroup s .. kGroup s + kGroup - 1, of which min(kGroup, G - kGroup s) exist (G < 4
+// leaves head slots empty).  Virtual head v = s * Hkv + kvh, so that the slices of one KV
+// head land on the same XCD when workgroups go round-robin to the eight XCDs.
+inline int32_t num_vheads(int32_t num_q_heads, int32_t num_kv_heads)
+{
+    const int32_t g = num_q_heads / num_kv_heads;
+    return num_kv_heads * ((g + kGroup - 1) / kGroup);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace of a batch whose decode rows or prefill tiles are split:
-//   [0, 64 KiB)   uint32 completion counters: decode (row, KV head) pairs at r * Hkv + kvh,
-//                 prefill (tile, KV head) pairs after them at num_reqs * Hkv + tile * Hkv + kvh;
+//   [0, 64 KiB)   uint32 completion counters: decode (row, virtual KV head) pairs at r * V + v,
+//                 prefill (tile, virtual KV head) pairs after them at num_reqs * V + tile * V + v;
 //                 zero before the first use of the buffer, and every call leaves them zero
-//   part_o        normalised FP32 decode split outputs [num_reqs][max_splits][Hq][head_dim]
+//   part_o        normalised FP32 decode split outputs [num_reqs][max_splits][V * 4][head_dim]
+//                 (V virtual KV heads of 4 head slots each; V * 4 = Hq when Hq / Hkv is a multiple of 4)
 //                 (also present with one split per row when there are shared-prefix groups)
-//   part_lse      per-split log2-sum-exp [num_reqs][max_splits][Hq]
+//   part_lse      per-split log2-sum-exp [num_reqs][max_splits][V * 4]
 //   pf_part_o     normalised FP32 prefill split outputs, 128 x 128 floats per (tile, KV head,
 //                 split), in the order the prefill kernel's lanes hold them
 //   pf_part_lse   their log2-sum-exp, 512 floats per (tile, KV head, split), also in lane order
 //   px_part_o     normalised FP32 outputs over a row's shared-prefix blocks, per (request,
-//                 prefix split, query head): [num_reqs][prefix_splits][Hq][head_dim]
-//   px_part_lse   their log2-sum-exp [num_reqs][prefix_splits][Hq]
+//                 prefix split, head slot): [num_reqs][prefix_splits][V * 4][head_dim]
+//   px_part_lse   their log2-sum-exp [num_reqs][prefix_splits][V * 4]
 // The counters sit at a fixed place so that no call's partials ever land on them.
 constexpr size_t kCounterBytes = 64 * 1024;
 constexpr int64_t kMaxCounters = kCounterBytes / sizeof(uint32_t);
@@ -65,6 +77,9 @@ inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, in
                                         int32_t prefix_splits = 0)
 {
     WorkspaceLayout w;
+    // partials are indexed by head slot (kGroup per virtual KV head), counters by virtual head
+    const int32_t vheads = num_vheads(num_q_heads, num_kv_heads);
+    const int32_t slots = vheads * kGroup;
     // decode partials: split rows, and every row of a shared-prefix group (its decode
     // result waits there for the group's prefix partials)
     const bool decode = (max_splits > 1 || prefix_splits > 0) && num_reqs > 0;
@@ -72,24 +87,24 @@ inline WorkspaceLayout workspace_layout(int32_t num_reqs, int32_t max_splits, in
     const bool prefix = prefix_splits > 0 && num_reqs > 0;
     if (!decode && !prefill && !prefix)
         return w;
-    w.pf_counter_base = (int64_t)num_reqs * num_kv_heads;
-    w.counters_used = prefill ? w.pf_counter_base + (int64_t)prefill_tiles * num_kv_heads
-                              : decode ? (int64_t)num_reqs * num_kv_heads : 0;
+    w.pf_counter_base = (int64_t)num_reqs * vheads;
+    w.counters_used = prefill ? w.pf_counter_base + (int64_t)prefill_tiles * vheads
+                              : decode ? (int64_t)num_reqs * vheads : 0;
     size_t at = kCounterBytes;
     if (decode) {
-        const size_t n = (size_t)num_reqs * (size_t)max_splits * (size_t)num_q_heads;
+        const size_t n = (size_t)num_reqs * (size_t)max_splits * (size_t)slots;
         w.part_o = at;
         w.part_lse = align256(w.part_o + n * kHeadDim * sizeof(float));
         at = align256(w.part_lse + n * sizeof(float));
     }
     if (prefill) {
-        const size_t n = (size_t)prefill_tiles * (size_t)num_kv_heads * (size_t)prefill_splits;
+        const size_t n = (size_t)prefill_tiles * (size_t)vheads * (size_t)prefill_splits;
         w.pf_part_o = at;
         w.pf_part_lse = align256(w.pf_part_o + n * (size_t)kPrefillPartFloats * sizeof(float));
         at = align256(w.pf_part_lse + n * (size_t)kPrefillPartLseFloats * sizeof(float));
     }
     if (prefix) {
-        const size_t n = (size_t)num_reqs * (size_t)prefix_splits * (size_t)num_q_heads;
+        const size_t n = (size_t)num_reqs * (size_t)prefix_splits * (size_t)slots;
         w.px_part_o = at;
         w.px_part_lse = align256(w.px_part_o + n * kHeadDim * sizeof(float));
         at = align256(w.px_part_lse + n * sizeof(float));

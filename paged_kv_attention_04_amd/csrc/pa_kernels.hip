@@ -132,6 +132,25 @@ __device__ inline float readlane_f(float x, int lane)
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// The query heads one workgroup serves: virtual KV head vkv = slice * Hkv + kvh holds query
+// heads head0 .. head0 + 3 of KV head kvh, head0 = kvh * G + 4 * slice (G = Hq / Hkv), of
+// which `heads` = min(4, G - 4 * slice) exist; the others are empty slots (zero queries,
+// nothing written).  Partials are indexed by head slot, vkv * 4 + h.
+struct HeadSlice {
+    int kvh, slice, head0, heads, slot0;
+};
+__device__ inline HeadSlice head_slice(int vkv, int num_q_heads, int num_kv_heads)
+{
+    HeadSlice hs;
+    const int g = num_q_heads / num_kv_heads;
+    hs.kvh = vkv % num_kv_heads;
+    hs.slice = vkv / num_kv_heads;
+    hs.head0 = hs.kvh * g + kGroup * hs.slice;
+    hs.heads = min(kGroup, g - kGroup * hs.slice);
+    hs.slot0 = vkv * kGroup;
+    return hs;
+}
+
 __device__ inline float half_bits_to_float(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
 // Two floats -> binary16 pair (toward zero), low half first.
@@ -287,6 +306,7 @@ struct DecodeParams {
     int32_t num_reqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
+    int32_t num_vheads;    // workgroups per (row, split): virtual KV heads of four head slots
     int32_t num_blocks;
     int32_t split_blocks;
     int32_t max_splits;
@@ -441,7 +461,7 @@ __device__ inline int prefix_skip_of(const DecodeParams& p, int r)
     return skip;
 }
 
-// Final outputs of rows rows[0 .. nrows - 1] for KV head kvh: each row's decode partials
+// Final outputs of rows rows[0 .. nrows - 1] for virtual KV head vkv: each row's decode partials
 // (as many as decode_splits_of gives), then its nprefix shared-prefix partials, merged by
 // the log-sum-exp rule in that fixed order, whichever workgroup arrived last.  Each thread
 // owns one (head, dim) value of every row.  kChunk rows are merged together, kBatch
@@ -451,9 +471,10 @@ __device__ inline int prefix_skip_of(const DecodeParams& p, int r)
 // before their writer counted in, so agent-scope loads see them.
 static_assert(kGroup * kHeadDim == 64 * kDecodeWaves, "one output value per thread");
 template <int kChunk, int kBatch>
-__device__ inline void merge_rows_results(const DecodeParams& p, const int* rows, int nrows, int kvh, int nprefix)
+__device__ inline void merge_rows_results(const DecodeParams& p, const int* rows, int nrows, int vkv, int nprefix)
 {
-    const int head0 = kvh * kGroup;
+    const HeadSlice hs = head_slice(vkv, p.num_q_heads, p.num_kv_heads);
+    const int head0 = hs.head0, slots = p.num_vheads * kGroup;
     const int idx = threadIdx.x, h = idx / kHeadDim, d = idx & (kHeadDim - 1);
     const float nan = __builtin_nanf("");
     // The partial buffers, held in vector registers so that picking a partial's buffer is
@@ -484,9 +505,9 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
                 for (int u = 0; u < kBatch; ++u) {
                     const int sidx = min(s0 + u, max(tot[j], 1) - 1);
                     const int64_t pi = sidx < ns[j]
-                                           ? ((int64_t)rr[j] * p.max_splits + sidx) * p.num_q_heads + head0 + h
-                                           : ((int64_t)rr[j] * p.prefix_splits + (sidx - ns[j])) * p.num_q_heads +
-                                                 head0 + h;
+                                           ? ((int64_t)rr[j] * p.max_splits + sidx) * slots + hs.slot0 + h
+                                           : ((int64_t)rr[j] * p.prefix_splits + (sidx - ns[j])) * slots +
+                                                 hs.slot0 + h;
                     const float* lsrc = sidx < ns[j] ? dec_lse : pfx_lse;
                     const float* osrc = sidx < ns[j] ? dec_o : pfx_o;
                     ls[j][u] = tot[j] > 0 ? load_agent(lsrc + pi) : 0.f;
@@ -501,7 +522,7 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
         }
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) {
-            if (c0 + j >= nrows)
+            if (c0 + j >= nrows || h >= hs.heads)
                 continue;
             const int q_row = p.qo_indptr[rr[j]];
             p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + idx] =
@@ -516,10 +537,11 @@ __device__ inline void merge_rows_results(const DecodeParams& p, const int* rows
 // merge_rows_results for the many rows a prefix-group workgroup can finish: four rows at
 // a time, two wavefronts per row, each lane merging four consecutive dims of one head, so
 // a row's partials (up to kBatch at once) are all requested before any is used.
-__device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, int nrows, int kvh, int nprefix)
+__device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, int nrows, int vkv, int nprefix)
 {
     constexpr int kBatch = 12;
-    const int head0 = kvh * kGroup;
+    const HeadSlice hs = head_slice(vkv, p.num_q_heads, p.num_kv_heads);
+    const int head0 = hs.head0, slots = p.num_vheads * kGroup;
     const int t = threadIdx.x, slot = t >> 7, h = (t >> 5) & 3, d4 = (t & 31) * 4;
     const float nan = __builtin_nanf("");
     const float* dec_lse = p.part_lse;            // in vector registers: see merge_rows_results
@@ -540,8 +562,8 @@ __device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, 
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int sidx = min(s0 + u, tot - 1);
-                const int64_t pi = sidx < ns ? ((int64_t)rr * p.max_splits + sidx) * p.num_q_heads + head0 + h
-                                             : ((int64_t)rr * p.prefix_splits + (sidx - ns)) * p.num_q_heads + head0 + h;
+                const int64_t pi = sidx < ns ? ((int64_t)rr * p.max_splits + sidx) * slots + hs.slot0 + h
+                                             : ((int64_t)rr * p.prefix_splits + (sidx - ns)) * slots + hs.slot0 + h;
                 const float* lsrc = sidx < ns ? dec_lse : pfx_lse;
                 const float* osrc = (sidx < ns ? dec_o : pfx_o) + pi * kHeadDim + d4;
                 ls[u] = load_agent(lsrc + pi);
@@ -556,6 +578,8 @@ __device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, 
                     for (int k = 0; k < 4; ++k)
                         mg[k].add(ls[u], os[u][k]);
         }
+        if (h >= hs.heads)
+            continue;
         const int q_row = p.qo_indptr[rr];
         const int64_t orow = (int64_t)q_row * p.num_q_heads + head0 + h;
         float v[4];
@@ -568,12 +592,13 @@ __device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, 
     }
 }
 
-// Grid: max_splits * num_reqs * num_kv_heads workgroups of kDecodeWaves wavefronts, KV
-// head fastest: workgroups go round-robin to the eight XCDs, so with eight KV heads each
-// XCD serves one KV head of every row and reads that head's shared-prefix blocks from
-// one L2.
+// Grid: max_splits * num_reqs * V workgroups of kDecodeWaves wavefronts (V virtual KV
+// heads of four query-head slots each: one per KV head when it serves four query heads),
+// virtual head fastest: workgroups go round-robin to the eight XCDs, so with eight KV
+// heads each XCD serves one KV head of every row and reads that head's shared-prefix
+// blocks from one L2.
 //
-// A workgroup owns one (row, KV head, split); its blocks are cut into kDecodeWaves
+// A workgroup owns one (row, virtual KV head, split); its blocks are cut into kDecodeWaves
 // contiguous runs, one per wavefront.  Each wavefront streams its run with kDecodeDepth
 // blocks of loads in flight.  Per block: scores of 16 tokens x 4 heads (bf16 dot2, FP32
 // accumulation, reduced over 8 lanes), the online softmax with one (token, head) pair per
@@ -605,11 +630,12 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int kvh = bid % p.num_kv_heads;
-    const int rest = bid / p.num_kv_heads;
+    const int vkv = bid % p.num_vheads;
+    const int rest = bid / p.num_vheads;
     const int r = rest % p.num_reqs;
     const int split = rest / p.num_reqs;
-    const int head0 = kvh * kGroup;
+    const HeadSlice hsl = head_slice(vkv, p.num_q_heads, p.num_kv_heads);
+    const int kvh = hsl.kvh, head0 = hsl.head0;
     const float nan = __builtin_nanf("");
 
     // Wavefront w takes blocks g0 + w, g0 + w + 8, ... of the split.  Their table entries
@@ -657,9 +683,9 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     const int nsplit = decode_splits_of(p, r, skip);
     if (nsplit < 0) {                                 // lengths disagree with the plan
         if (split == 0)
-            for (int i = tid; i < kGroup * kHeadDim; i += 64 * kDecodeWaves) {
+            for (int i = tid; i < hsl.heads * kHeadDim; i += 64 * kDecodeWaves) {
                 p.out[((int64_t)q_row * p.num_q_heads + head0) * kHeadDim + i] = 0x7FC0;
-                if (i < kGroup)
+                if (i < hsl.heads)
                     p.lse[(int64_t)q_row * p.num_q_heads + head0 + i] = nan;
             }
         return;
@@ -684,7 +710,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
             kn1 = kr[c8 + 8];
             vn = vr[c16];
             const int phys = p.block_tables[(int64_t)r * p.max_blocks + new_blk];
-            if (tid < 16 && phys >= 0 && phys < p.num_blocks) {
+            if (tid < 16 && hsl.slice == 0 && phys >= 0 && phys < p.num_blocks) {   // one slice writes
                 const int64_t row = (((int64_t)phys * p.num_kv_heads + kvh) * kBlock + new_off) * (kHeadDim / 8);
                 reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool))[row + tid] = kr[tid];
                 reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool))[row + tid] = vr[tid];
@@ -699,8 +725,10 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
         const u32x4* qb = reinterpret_cast<const u32x4*>(p.q + ((int64_t)q_row * p.num_q_heads + head0) * kHeadDim);
 #pragma unroll
         for (int h = 0; h < kGroup; ++h) {
+            const bool has = h < hsl.heads;             // empty head slots hold zero queries
             if constexpr (kQ8) {
-                const u32x4 a = qb[h * 16 + 2 * c8], b = qb[h * 16 + 2 * c8 + 1];
+                const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+                const u32x4 a = has ? qb[h * 16 + 2 * c8] : z, b = has ? qb[h * 16 + 2 * c8 + 1] : z;
                 const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
                 float sum = 0.f;
 #pragma unroll
@@ -711,8 +739,8 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
                 }
                 qbias[h] = -kQ8Bias * sum;
             } else {
-                qv[h][0] = qb[h * 16 + c8];
-                qv[h][1] = qb[h * 16 + c8 + 8];
+                qv[h][0] = has ? qb[h * 16 + c8] : u32x4{0u, 0u, 0u, 0u};
+                qv[h][1] = has ? qb[h * 16 + c8 + 8] : u32x4{0u, 0u, 0u, 0u};
             }
         }
     }
@@ -966,6 +994,8 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
             const int idx = tid + k * 64 * kDecodeWaves;
+            if (idx / kHeadDim >= hsl.heads)
+                continue;
             p.out[out_base + idx] = __builtin_bit_cast(uint16_t, (__bf16)res[k]);
             if ((idx & (kHeadDim - 1)) == 0)
                 p.lse[(int64_t)q_row * p.num_q_heads + head0 + idx / kHeadDim] = res_lse[k] * kLn2;
@@ -979,7 +1009,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     // This needs no L2 writeback or invalidation, which a device fence would do for every
     // split.  A row of a shared-prefix group also waits for its group's prefix splits,
     // which count into the same counter from the same launch.
-    const int64_t mine = (int64_t)r * p.max_splits * p.num_q_heads + head0 + (int64_t)split * p.num_q_heads;
+    const int64_t mine = ((int64_t)r * p.max_splits + split) * (p.num_vheads * kGroup) + hsl.slot0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int idx = tid + k * 64 * kDecodeWaves;
@@ -990,7 +1020,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int nprefix = prefix ? p.prefix_splits : 0;
-    uint32_t* counter = p.counters + (int64_t)r * p.num_kv_heads + kvh;
+    uint32_t* counter = p.counters + (int64_t)r * p.num_vheads + vkv;
     if (tid == 0) {
         const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = done == (uint32_t)(nsplit + nprefix - 1);
@@ -1000,7 +1030,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     }
     __syncthreads();
     if (last_lds)
-        merge_rows_results<1, 32>(p, &r, 1, kvh, nprefix);
+        merge_rows_results<1, 32>(p, &r, 1, vkv, nprefix);
 }
 
 template <bool kQ8, bool kFused>
@@ -1026,6 +1056,7 @@ struct PrefillParams {
     int32_t max_blocks;
     int32_t num_q_heads;
     int32_t num_kv_heads;
+    int32_t num_vheads;         // virtual KV heads (see HeadSlice)
     int32_t num_blocks;
     int32_t num_prefill_rows;
     int32_t splits;             // key splits per tile
@@ -1500,11 +1531,12 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int rg = wave % kRG, kh = wave / kRG;     // row group, key part
-    const int kvh = bid % p.num_kv_heads;
-    const int rest = bid / p.num_kv_heads;
+    const int vkv = bid % p.num_vheads;
+    const int rest = bid / p.num_vheads;
     const int split = rest % p.splits;
     const int tile = rest / p.splits;
-    const int head0 = kvh * kGroup;
+    const HeadSlice hs = head_slice(vkv, p.num_q_heads, p.num_kv_heads);
+    const int kvh = hs.kvh, head0 = hs.head0;
     int r, qt, q0, qlen, kvlen, ctx, nblk_row, kv_hi;
     bool bad_row;
     int grp_first = 0, grp_count = 0;
@@ -1565,6 +1597,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             ok = tl < qlen;
             qidx = q0 + tl;
         }
+        ok = ok && (rho & 3) < hs.heads;       // empty head slots hold zero queries
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -1820,7 +1853,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     int64_t new_dst = -1;
     if constexpr (kFused) {
         const int tl = qt * kTileTok + (tid >> 4), c = tid & 15;          // kTileTok tokens x 16 chunks
-        if (split == 0 && !bad_row && (tid >> 4) < kTileTok && tl < qlen) {
+        if (split == 0 && hs.slice == 0 && !bad_row && (tid >> 4) < kTileTok && tl < qlen) {
             const int pos = ctx + tl;
             const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
             if (phys >= 0 && phys < p.num_blocks) {
@@ -1931,7 +1964,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                     *stage_at(rho, 4 * db + kslice) = __builtin_bit_cast(u32x4, oacc[rb][db]);
                 if (kslice == 0 && rho < nrows_valid) {
                     const int64_t pi =
-                        ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * p.num_q_heads + head0 + (rho & 3);
+                        ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * (p.num_vheads * kGroup) + hs.slot0 +
+                        (rho & 3);
                     store_agent(p.px_part_lse + pi, lse2[rb]);
                 }
             }
@@ -1939,7 +1973,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         __syncthreads();
         for (int idx = tid; idx < nrows_valid * kHeadDim; idx += 64 * kPfWaves) {
             const int rho = idx / kHeadDim, d = idx % kHeadDim;
-            const int64_t pi = ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * p.num_q_heads + head0 + (rho & 3);
+            const int64_t pi =
+                ((int64_t)(grp_first + (rho >> 2)) * p.splits + split) * (p.num_vheads * kGroup) + hs.slot0 + (rho & 3);
             const float v = reinterpret_cast<const float*>(stage_at(rho, d >> 2))[d & 3];
             store_agent(p.px_part_o + pi * kHeadDim + d, v);
         }
@@ -1955,7 +1990,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             const int rr = grp_first + tid;
             const int nsplit = decode_splits_of(dp, rr, prefix_skip_of(dp, rr));
             if (nsplit >= 0) {                  // else the decode side does not count this row either
-                uint32_t* counter = dp.counters + (int64_t)rr * dp.num_kv_heads + kvh;
+                uint32_t* counter = dp.counters + (int64_t)rr * dp.num_vheads + vkv;
                 const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (done == (uint32_t)(nsplit + p.splits - 1)) {
                     __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1969,7 +2004,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         for (uint32_t mine = (uint32_t)last_lds; mine; mine &= mine - 1)
             rows[nrows++] = grp_first + __builtin_ctz(mine);
         if (nrows > 0)
-            merge_group_rows(dp, rows, nrows, kvh, p.splits);
+            merge_group_rows(dp, rows, nrows, vkv, p.splits);
         return;
     }
 
@@ -1979,7 +2014,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         for (int rb = 0; rb < kRB; ++rb) {
             const int rho = 16 * kRB * rg + 16 * rb + row16;
             const int tl = qt * kTileTok + (rho >> 2);
-            if (tl >= qlen)
+            if (tl >= qlen || (rho & 3) >= hs.heads)
                 continue;
             const bool nan_row = lse_row[rb] != lse_row[rb];
             const int64_t orow = ((int64_t)(q0 + tl) * p.num_q_heads + head0 + (rho & 3));
@@ -2003,7 +2038,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     // Partials are written with agent-scope stores (coherent across the XCDs' separate L2
     // caches) and every thread waits until its stores have completed before the
     // workgroup counts itself in; the last split reads them with agent-scope loads.
-    const int64_t item0 = ((int64_t)tile * p.num_kv_heads + kvh) * p.splits;   // split 0 of this (tile, KV head)
+    const int64_t item0 = ((int64_t)tile * p.num_vheads + vkv) * p.splits;   // split 0 of this (tile, virtual KV head)
     // per (tile, KV head, split): kRG row groups of kRB x 8 f32x4 per lane, and kRB x 64
     // log2-sum-exps per row group, in lane order
     auto part_o_at = [&](int sp) __attribute__((always_inline)) { return p.part_o + ((item0 + sp) * kRG + rg) * (kRB * 8 * 4 * 64); };
@@ -2021,7 +2056,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    uint32_t* counter = p.counters + (int64_t)tile * p.num_kv_heads + kvh;
+    uint32_t* counter = p.counters + (int64_t)tile * p.num_vheads + vkv;
     if (tid == 0) {
         const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = done == (uint32_t)(p.splits - 1);
@@ -2152,8 +2187,8 @@ __global__ __launch_bounds__(256) void pa_zero_words(uint32_t* __restrict__ p, i
 
 // A mixed batch (chunk tiles and decode rows) in one launch.  With `interleave` 0 the grid
 // holds the chunk-tile workgroups first, then the decode workgroups (which fill CUs as the
-// chunk tiles drain).  Otherwise both kinds come in groups of num_kv_heads, one per KV
-// head, and the grid alternates a group of chunk-tile workgroups with a group of decode
+// chunk tiles drain).  Otherwise both kinds come in groups of num_vheads, one per virtual
+// KV head, and the grid alternates a group of chunk-tile workgroups with a group of decode
 // workgroups while both last, then runs the rest of the longer kind; workgroups are dealt
 // round-robin to the XCDs, so each KV head keeps one XCD (and its L2) for both kinds.
 // Nothing waits for anything else: the two kinds share no outputs, and their split
@@ -2163,7 +2198,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_mixed_batch(PrefillParams pp
                                                                 int32_t num_prefill_wgs, int32_t num_decode_wgs,
                                                                 int32_t interleave)
 {
-    const int H = dp.num_kv_heads;
+    const int H = dp.num_vheads;
     const int b = blockIdx.x, grp = b / H, lane = b - grp * H;
     const int pf_groups = num_prefill_wgs / H, dc_groups = num_decode_wgs / H;
     const int both = interleave ? min(pf_groups, dc_groups) : 0;
@@ -2468,6 +2503,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         }
     }
     const float scale_log2 = g->scale * kLog2e;
+    const int32_t vheads = pa::num_vheads(g->num_q_heads, g->num_kv_heads);
 
     auto prefill_params = [&]() {
         PrefillParams pp = {};
@@ -2482,6 +2518,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         pp.max_blocks = max_blocks_per_req;
         pp.num_q_heads = g->num_q_heads;
         pp.num_kv_heads = g->num_kv_heads;
+        pp.num_vheads = vheads;
         pp.num_blocks = g->num_blocks;
         pp.scale_log2 = scale_log2;
         return pp;
@@ -2506,6 +2543,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         pp.max_blocks = max_blocks_per_req;
         pp.num_q_heads = g->num_q_heads;
         pp.num_kv_heads = g->num_kv_heads;
+        pp.num_vheads = vheads;
         pp.num_blocks = g->num_blocks;
         pp.num_prefill_rows = plan->num_prefill_rows;
         pp.splits = plan->prefill_splits;
@@ -2518,7 +2556,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             pp.prefill_req[i] = i < plan->num_prefill_rows ? plan->prefill_req[i] : 0;
         for (int i = 0; i <= PA_MAX_PREFILL_ROWS; ++i)
             pp.tile_start[i] = i <= plan->num_prefill_rows ? plan->prefill_tile_start[i] : plan->prefill_tiles;
-        const int64_t grid = (int64_t)plan->prefill_tiles * g->num_kv_heads * plan->prefill_splits;
+        const int64_t grid = (int64_t)plan->prefill_tiles * vheads * plan->prefill_splits;
         if (grid > INT32_MAX)
             return PA_ERR_SHAPE;
         pp.k_new = static_cast<const uint16_t*>(k_new);
@@ -2550,6 +2588,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         dp.num_reqs = plan->num_reqs;
         dp.num_q_heads = g->num_q_heads;
         dp.num_kv_heads = g->num_kv_heads;
+        dp.num_vheads = vheads;
         dp.num_blocks = g->num_blocks;
         dp.split_blocks = plan->split_blocks;
         dp.max_splits = plan->max_splits;
@@ -2565,7 +2604,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         dp.px_part_lse = ngroups > 0 ? reinterpret_cast<float*>(wsp + ws.px_part_lse) : nullptr;
         dp.k_new = static_cast<const uint16_t*>(k_new);
         dp.v_new = static_cast<const uint16_t*>(v_new);
-        const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * g->num_kv_heads;
+        const int64_t grid = (int64_t)plan->max_splits * plan->num_reqs * vheads;
         if (ngroups > 0) {
             // each group's shared blocks, once per KV head, for all of its query rows, in
             // the same launch as the decode workgroups
@@ -2578,7 +2617,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             }
             pp.px_part_o = reinterpret_cast<float*>(wsp + ws.px_part_o);
             pp.px_part_lse = reinterpret_cast<float*>(wsp + ws.px_part_lse);
-            const int64_t nprefix = (int64_t)ngroups * g->num_kv_heads * plan->prefix_splits;
+            const int64_t nprefix = (int64_t)ngroups * vheads * plan->prefix_splits;
             if (grid + nprefix > INT32_MAX)
                 return PA_ERR_SHAPE;
             launch_cascade(q8, fused, q8 ? 128 : plan->prefix_tile_rows, (uint32_t)(grid + nprefix), st, pp, dp,

@@ -277,6 +277,23 @@ def test_plan_shared_prefix_overrides():
         assert e.value.code == -2 and bytes(plan) == before
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 32), (32, 16), (24, 8), (48, 8), (64, 8), (8, 1)])
+def test_plan_counts_virtual_kv_heads(hq, hkv):
+    """Grouped-query ratios other than four: a KV head with G query heads is served by
+    ceil(G / 4) workgroups of four head slots, so the decode workgroup count and the
+    partials scale with that count of virtual KV heads, not with num_kv_heads."""
+    vheads = hkv * -(-(hq // hkv) // 4)
+    g = pa.Geometry.make(hq, hkv, 4096)
+    kv = [700, 33, 1, 2048]
+    plan = pa.pa_plan(g, [1] * 4, kv, split_blocks=8)
+    splits = [-(-(-(-k // 16)) // 8) for k in kv]
+    assert plan.max_splits == max(splits)
+    assert plan.decode_items == sum(splits) * vheads
+    # decode partials hold four head slots per virtual KV head: o and lse per (row, split, slot)
+    n = 4 * plan.max_splits * vheads * 4
+    assert plan.workspace_bytes >= 64 * 1024 + n * 128 * 4 + n * 4
+
+
 def test_plan_errors():
     g = qwen()
     with pytest.raises(pa.PaError) as e:
@@ -286,7 +303,7 @@ def test_plan_errors():
         pa.pa_plan(g, [0], [5])
     assert e.value.code == -2
     with pytest.raises(pa.PaError) as e:
-        pa.pa_plan(pa.Geometry.make(32, 16, 10), [1], [5])              # 2 query heads per KV head
+        pa.pa_plan(pa.Geometry.make(32, 12, 10), [1], [5])              # KV heads do not divide query heads
     assert e.value.code == -5
     with pytest.raises(pa.PaError) as e:
         pa.pa_plan(pa.Geometry.make(32, 8, 10, head_dim=64), [1], [5])

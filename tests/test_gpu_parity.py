@@ -909,6 +909,68 @@ def test_spec_verify_rows():
     check(wl, label="spec verify")
 
 
+# ------------------------------------------------------------------ grouped-query ratios
+
+# (query heads, KV heads): G = 1, 2, 3, 5, 6, 8 query heads per KV head, and one KV head
+# for all query heads.  Workgroups serve four head slots of one KV head, so G = 1, 2, 3
+# leave slots empty, 5 and 6 take two slices with the second partly empty, 8 two full ones.
+GQA_RATIOS = [(8, 8), (16, 8), (24, 8), (40, 8), (48, 8), (64, 8), (8, 1)]
+
+
+def _gqa(case, hq, hkv, q8=False):
+    seed = 4000 + 17 * hq + hkv + (500 if q8 else 0)
+    make = synthetic.build_q8 if q8 else synthetic.build
+    name = f"gqa{hq}x{hkv}_{case}" + ("_q8" if q8 else "")
+    if case == "mixed":        # split decode rows, a one-token row, 32-token chunk tiles
+        return make(name, seed, hq, hkv, qo_len=[1, 70, 1, 1, 33], kv_len=[900, 300, 17, 1, 33], num_blocks=100)
+    if case == "chunks8":      # rows of at most 8 tokens: 32-row tiles
+        return make(name, seed, hq, hkv, qo_len=[8] * 5 + [3], kv_len=[520] * 5 + [40], num_blocks=180)
+    if case == "chunks16":     # rows of at most 16 tokens: 64-row tiles
+        return make(name, seed, hq, hkv, qo_len=[16, 12, 1, 16], kv_len=[700, 90, 300, 16], num_blocks=90)
+    if case == "cascade":      # decode rows sharing 30 blocks
+        return make(name, seed, hq, hkv, qo_len=[1] * 6, kv_len=[700, 820, 990, 640, 777, 1000], num_blocks=200,
+                    shared_prefix_blocks=30)
+    raise ValueError(case)
+
+
+@pytest.mark.parametrize("hq,hkv", GQA_RATIOS)
+@pytest.mark.parametrize("case", ["mixed", "chunks8", "chunks16", "cascade"])
+def test_gqa_ratios(hq, hkv, case):
+    """Other query-head-per-KV-head ratios through every path: decode rows (split and not),
+    chunk tiles of 128 / 64 / 32 rows with and without key splits, the shared-prefix
+    cascade, the fused append (both steps) and the one-launch mixed batch, each within the
+    bars of the oracle, and the fused and one-launch forms bit-identical to the plain ones."""
+    wl = _gqa(case, hq, hkv)
+    if case == "cascade":
+        check(wl, cascade=True, label=f"G={hq // hkv} cascade")
+        check(wl, split_blocks=3, label=f"G={hq // hkv} split 3")
+        kp, vp, out, lse = _decode_step_gpu(wl, cascade=True)
+        _, _, out2, lse2 = _run_gpu(wl, cascade=True)
+        assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+        okp, ovp, _ = oracle.run_workload(wl)
+        assert np.array_equal(kp, okp) and np.array_equal(vp, ovp)
+        return
+    out, lse = check(wl, split_blocks=5, label=f"G={hq // hkv} split 5")
+    check(wl, prefill_splits=3, label=f"G={hq // hkv} psplit 3")
+    kp, vp, fo, fl = _attention_step_gpu(wl, split_blocks=5)
+    assert np.array_equal(fo, out) and np.array_equal(fl, lse), "fused step differs"
+    okp, ovp, _ = oracle.run_workload(wl)
+    assert np.array_equal(kp, okp) and np.array_equal(vp, ovp)
+    if case == "mixed":
+        import paged_kv_attention_04_amd as pa
+        for mode in (1, 2):
+            one = pa.run_workload(wl, split_blocks=5, one_launch=mode)
+            assert np.array_equal(one[2], out) and np.array_equal(one[3], lse), f"one launch {mode} differs"
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (24, 8), (48, 8), (8, 1)])
+@pytest.mark.parametrize("case", ["mixed", "cascade"])
+def test_gqa_ratios_q8(hq, hkv, case):
+    """The q8_0 pool at other grouped-query ratios: decode rows, chunk rows, cascade."""
+    wl = _gqa(case, hq, hkv, q8=True)
+    check(wl, split_blocks=5, cascade=case == "cascade", label=f"G={hq // hkv} q8_0")
+
+
 # ------------------------------------------------------------------ randomised batches
 
 def _random_batch(seed):
