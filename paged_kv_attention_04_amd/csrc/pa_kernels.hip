@@ -1349,6 +1349,122 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[kKB][4], const char*
     }
 }
 
+// The full tile's step in two halves, for the alternating schedule of prefill_body: the
+// matrix half (PV of the previous step with its weights pw, then S^T = K Q^T of this step)
+// and the vector half (masking, maxima, lazy rescale, exponentials and denominators, which
+// leave the next PV's weights in pw).  Per output value the arithmetic and its order are
+// those of pf_step: the same products accumulate in the same order and the softmax takes
+// the same steps, so both schedules give the same bits.
+__device__ __forceinline__ void pf_pv_full(const char* vt, const int (&v_addr)[8], const bf16x8 (&pw)[2][2],
+                                           f32x4 (&oacc)[2][8])
+{
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        bf16x8 v[8];
+        pf_read_v(vt, v_addr, c, v);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[db], pw[0][c], oacc[0][db], 0, 0, 0);
+            oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[db], pw[1][c], oacc[1][db], 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void pf_qk_full(const char* kt, const int (&k_addr)[4], const bf16x8 (&qop)[2][4],
+                                           f32x4 (&sacc)[2][4])
+{
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        bf16x8 kop[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            kop[ks] = *reinterpret_cast<const bf16x8*>(kt + k_addr[ks] + kb * 4096);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            sacc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                sacc[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[ks], qop[rb][ks], sacc[rb][kb], 0, 0, 0);
+        }
+    }
+}
+
+// Both products of the matrix half in one instruction stream: the 48 LDS operand reads
+// (V's two 32-key chunks, then K's four 16-key blocks) go out eight ahead of the 64
+// products that use them, one per product, so that few operands are live at a time.
+__device__ __forceinline__ void pf_matrix_full(const char* vt, const int (&v_addr)[8], const bf16x8 (&pw)[2][2],
+                                               f32x4 (&oacc)[2][8], const char* kt, const int (&k_addr)[4],
+                                               const bf16x8 (&qop)[2][4], f32x4 (&sacc)[2][4])
+{
+    pf_pv_full(vt, v_addr, pw, oacc);
+    pf_qk_full(kt, k_addr, qop, sacc);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 40; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 24, 0);
+}
+
+template <bool kMask>
+__device__ __forceinline__ void pf_softmax_full(const f32x4 (&sacc)[2][4], f32x4 (&oacc)[2][8], float (&m)[2],
+                                                float (&lsum)[2], bf16x8 (&pw)[2][2], int key0, int kslice,
+                                                const int (&qpos)[2], int kv_hi, float scale_log2)
+{
+    float x[2][16];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[rb][4 * kb + e] = sacc[rb][kb][e];
+    if constexpr (kMask) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + 16 * (i >> 2) + 4 * kslice + (i & 3);
+                x[rb][i] = (key > qpos[rb] || key >= kv_hi) ? -INFINITY : x[rb][i];
+            }
+    }
+    float lmax[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float a = max3f(x[rb][0], x[rb][1], x[rb][2]);
+        const float b = max3f(x[rb][3], x[rb][4], x[rb][5]);
+        const float c = max3f(x[rb][6], x[rb][7], x[rb][8]);
+        const float d = max3f(x[rb][9], x[rb][10], x[rb][11]);
+        const float e = max3f(x[rb][12], x[rb][13], x[rb][14]);
+        lmax[rb] = max3f(max3f(a, b, c), max3f(d, e, x[rb][15]), -INFINITY) * scale_log2;
+    }
+    const bool raise = lmax[0] > m[0] + kRescaleSlack || lmax[1] > m[1] + kRescaleSlack;
+    if (__any(raise)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float t = fmaxf(lmax[rb], shfl_xor(lmax[rb], 16));
+            t = fmaxf(t, shfl_xor(t, 32));
+            if (t > m[rb] + kRescaleSlack) {
+                const float alpha = (m[rb] == -INFINITY) ? 0.f : fast_exp2(m[rb] - t);
+                m[rb] = t;
+                lsum[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    oacc[rb][db] *= alpha;
+            }
+        }
+    }
+    const float nm0 = (m[0] == -INFINITY) ? 0.f : -m[0];
+    const float nm1 = (m[1] == -INFINITY) ? 0.f : -m[1];
+    float s0 = pf_exp8(&x[0][0], nm0, scale_log2, pw[0][0]);
+    float s1 = pf_exp8(&x[1][0], nm1, scale_log2, pw[1][0]);
+    s0 += pf_exp8(&x[0][8], nm0, scale_log2, pw[0][1]);
+    s1 += pf_exp8(&x[1][8], nm1, scale_log2, pw[1][1]);
+    lsum[0] += s0;
+    lsum[1] += s1;
+}
+
 // Workgroup of eight wavefronts per (prefill row, 32-token query tile, KV head, key split).
 // The tile's 128 MFMA rows are (token, head) pairs, row = 4 * token + head, so the four
 // query heads of a group share every K / V tile.  Wavefront w owns rows 32 (w % 4) .. +32
@@ -1705,6 +1821,39 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                                              16, 0, 0);
         }
     };
+    // The copies of one pool (K or V) of step s into buffer `sel` of that pool, as `stage`
+    // makes them for both; the alternating schedule stages K one step ahead of V.
+    auto stage_pool = [&](auto which, auto sel, int s, int id) __attribute__((always_inline)) {
+        constexpr bool kV = decltype(which)::value;
+        u32x4* dst = kV ? (decltype(sel)::value == 0 ? v_tile0 : v_tile1)
+                        : (decltype(sel)::value == 0 ? k_tile0 : k_tile1);
+        const uint16_t* pool = kV ? p.v_pool : p.k_pool;
+        const int valid = kvlen - (s * kPfKeys + 16 * wave);
+        const int64_t base = (int64_t)id * blk_stride + kvh_off;
+        if constexpr (kFused) {
+            if (s * kPfKeys + 16 * wave + kBlock > ctx) {
+                const uint16_t* fresh = kV ? p.v_new : p.k_new;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = s * kPfKeys + 16 * wave + 4 * i + (lane >> 4);
+                    const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
+                    const int64_t src = ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
+                                        (cp_off[i] & (kHeadDim - 1));
+                    __builtin_amdgcn_global_load_lds(pos >= ctx ? fresh + src : pool + base + off,
+                                                     (__attribute__((address_space(3))) void*)&dst[(16 * wave + 4 * i) * 16],
+                                                     16, 0, 0);
+                }
+                return;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
+            __builtin_amdgcn_global_load_lds(pool + base + off,
+                                             (__attribute__((address_space(3))) void*)&dst[(16 * wave + 4 * i) * 16],
+                                             16, 0, 0);
+        }
+    };
     // q8_0: the copies staged one step ago into buffer pair `sel` (whose previous contents
     // every wavefront finished reading before the last barrier)
     auto finish_q8 = [&](auto sel) __attribute__((always_inline)) {
@@ -1777,9 +1926,16 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         i = min(i, nsteps - 1);
         return i >= n_plain ? s_begin + i : s_begin + (i + rot < n_plain ? i + rot : i + rot - n_plain);
     };
-    int next_id = 0;
+    // The full bf16 tile runs the alternating schedule (see below); the other shapes and
+    // the q8_0 pool run one step at a time.
+    constexpr bool kAlternate = !kQ8 && kRG == 4 && kRB == 2;
+    int next_id = 0, cur_id = 0;
     if (nsteps > 0) {
-        stage(BufSel<0>{}, step_at(0), checked(table_entry(step_at(0))));
+        cur_id = checked(table_entry(step_at(0)));
+        if constexpr (kAlternate)
+            stage_pool(std::false_type{}, BufSel<0>{}, step_at(0), cur_id);
+        else
+            stage(BufSel<0>{}, step_at(0), cur_id);
         next_id = table_entry(step_at(1));
     }
 
@@ -1841,9 +1997,137 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         if (it < it_end)
             do_step(BufSel<0>{}, msk, it);
     };
-    run(std::integral_constant<bool, false>{}, 0, n_plain);
-    run(std::integral_constant<bool, true>{}, n_plain, nsteps);
-    wait_vmcnt<0>();                           // the last step's spare copy
+    if constexpr (kAlternate) {
+        // Alternating schedule.  The two wavefronts of a SIMD (row group rg, key parts 0
+        // and 1) take the two halves of each step in opposite order, so that one issues
+        // matrix products while the other runs the softmax:
+        //   iteration t, first half:   part 0: PV(t - 1), S(t)     part 1: softmax(t - 1)
+        //   iteration t, second half:  part 0: softmax(t)          part 1: PV(t - 1), S(t)
+        // for t = 0 .. nsteps (PV(-1), S(nsteps) and softmax(-1) are empty).  K of step t
+        // sits in K buffer t & 1 and V of step t in V buffer t & 1: iteration t copies
+        // K(t + 1) and V(t), which land before its closing barrier, while it reads K(t) and
+        // V(t - 1), so V is staged one step after K and no buffer is written while read.
+        f32x4 sacc[2][4];
+        bf16x8 pw[2][2];
+        auto ktile = [&](auto sel) __attribute__((always_inline)) {
+            return reinterpret_cast<const char*>(decltype(sel)::value == 0 ? k_tile0 : k_tile1);
+        };
+        auto vtile = [&](auto sel) __attribute__((always_inline)) {
+            return reinterpret_cast<const char*>(decltype(sel)::value == 0 ? v_tile0 : v_tile1);
+        };
+        // iteration t's copies: K(t + 1) (past the last step a spare copy of it, which
+        // nothing reads) and V(t)
+        auto copies = [&](auto sel, int t) __attribute__((always_inline)) {
+            constexpr int B = decltype(sel)::value;
+            int id = next_id;
+            asm volatile("" : "+v"(id));
+            const int id1 = checked(__builtin_amdgcn_readfirstlane(id));
+            stage_pool(std::false_type{}, BufSel<B ^ 1>{}, step_at(t + 1), id1);
+            stage_pool(std::true_type{}, BufSel<B>{}, step_at(t), cur_id);
+            cur_id = id1;
+            next_id = table_entry(step_at(t + 2));
+        };
+        auto softmax = [&](auto msk, int t) __attribute__((always_inline)) {
+            pf_softmax_full<decltype(msk)::value>(sacc, oacc, m, lsum, pw, step_at(t) * kPfKeys + kKPW * kh, kslice,
+                                                  qpos, kv_hi, p.scale_log2);
+        };
+        auto softmax_any = [&](int t) __attribute__((always_inline)) {
+            if (t >= n_plain)
+                softmax(std::true_type{}, t);
+            else
+                softmax(std::false_type{}, t);
+        };
+        auto sync = [&]() __attribute__((always_inline)) {
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        };
+        // keeps the two halves of the key parts aligned (no data passes here)
+        auto half_sync = [&]() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+        // iterations t0 .. t1 - 1 of the steady state (both products, one softmax), with the
+        // softmax's step masked or not throughout
+        auto steady = [&](auto part, auto msk, int t0, int t1) __attribute__((always_inline)) {
+            auto body = [&](auto sel, int t) __attribute__((always_inline)) {
+                constexpr int B = decltype(sel)::value;
+                copies(sel, t);
+                if constexpr (decltype(part)::value == 0) {
+                    if (active)
+                        pf_matrix_full(vtile(BufSel<B ^ 1>{}), v_addr, pw, oacc, ktile(sel), k_addr, qop, sacc);
+                    half_sync();
+                    if (active)
+                        softmax(msk, t);
+                } else {
+                    if (active)
+                        softmax(msk, t - 1);
+                    half_sync();
+                    if (active)
+                        pf_matrix_full(vtile(BufSel<B ^ 1>{}), v_addr, pw, oacc, ktile(sel), k_addr, qop, sacc);
+                }
+                sync();
+            };
+            int t = t0;
+            if (t < t1 && (t & 1)) {
+                body(BufSel<1>{}, t);
+                ++t;
+            }
+            for (; t + 1 < t1; t += 2) {
+                body(BufSel<0>{}, t);
+                body(BufSel<1>{}, t + 1);
+            }
+            if (t < t1)
+                body(BufSel<0>{}, t);
+        };
+        auto loop = [&](auto part) __attribute__((always_inline)) {
+            constexpr int kPart = decltype(part)::value;
+            // t = 0: S(0) (and part 0's softmax of it)
+            copies(BufSel<0>{}, 0);
+            if constexpr (kPart == 0) {
+                if (active)
+                    pf_qk_full(ktile(BufSel<0>{}), k_addr, qop, sacc);
+                half_sync();
+                if (active)
+                    softmax_any(0);
+            } else {
+                half_sync();
+                if (active)
+                    pf_qk_full(ktile(BufSel<0>{}), k_addr, qop, sacc);
+            }
+            sync();
+            // t = 1 .. nsteps - 1; the softmax of step t (part 0) or t - 1 (part 1) is
+            // masked from step n_plain on
+            const int edge = min(max(n_plain + kPart, 1), nsteps);
+            steady(part, std::false_type{}, 1, edge);
+            steady(part, std::true_type{}, edge, nsteps);
+            // t = nsteps: the last PV (after part 1's last softmax)
+            auto last_pv = [&]() __attribute__((always_inline)) {
+                if ((nsteps - 1) & 1)
+                    pf_pv_full(vtile(BufSel<1>{}), v_addr, pw, oacc);
+                else
+                    pf_pv_full(vtile(BufSel<0>{}), v_addr, pw, oacc);
+            };
+            if constexpr (kPart == 0) {
+                if (active)
+                    last_pv();
+                half_sync();
+            } else {
+                if (active)
+                    softmax_any(nsteps - 1);
+                half_sync();
+                if (active)
+                    last_pv();
+            }
+            sync();
+        };
+        if (nsteps > 0) {
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");   // K(0)
+            if (kh == 0)
+                loop(std::integral_constant<int, 0>{});
+            else
+                loop(std::integral_constant<int, 1>{});
+        }
+    } else {
+        run(std::integral_constant<bool, false>{}, 0, n_plain);
+        run(std::integral_constant<bool, true>{}, n_plain, nsteps);
+        wait_vmcnt<0>();                       // the last step's spare copy
+    }
 
     // Fused append: split 0 of each (tile, KV head) writes the tile's new tokens of this KV
     // head into their slots (every workgroup of the launch reads new positions from k_new /
