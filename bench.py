@@ -89,6 +89,13 @@ def prefill_only_workload(poison=False):
                            num_blocks=synthetic.POOL_BLOCKS_12GIB, poison=poison)
 
 
+def spec_verify_workload(poison=False):
+    """Speculative verification rows: 16 requests x 8 new tokens (causal) at 8192 tokens of context."""
+    import synthetic
+    return synthetic.build("spec_verify", 91, 32, 8, qo_len=[8] * 16, kv_len=[8192 + 8] * 16,
+                           num_blocks=16 * (8192 // 16 + 2) + 64, poison=poison)
+
+
 class Stepper:
     """Device copies of a workload, with `copies` KV-pool replicas rotated per step."""
 
@@ -483,7 +490,8 @@ def kernel_only(which: str, reps: int):
           "mixed_q8": lambda: synthetic.config_mixed_q8(poison=False),
           "shared_q8": lambda: synthetic.config_shared_prefix_q8(poison=False),
           "shared": lambda: synthetic.config_shared_prefix(poison=False),
-          "prefill": prefill_only_workload}[which]()
+          "prefill": prefill_only_workload,
+          "spec": spec_verify_workload}[which]()
     st = Stepper(wl, 4, cascade=which in ("shared", "shared_q8"), fused=which in ("decode", "mixed_fused"))
     src = torch.empty(CALIBRATION_COPY_BYTES // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
@@ -574,7 +582,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=0.5, help="least seconds per whole-pass CPU timing")
     ap.add_argument("--only", choices=["headline"], help="run the headline step only (for rocprofv3)")
     ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "mixed_fused", "mixed_q8", "shared",
-                                              "shared_q8", "prefill"])
+                                              "shared_q8", "prefill", "spec"])
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--summarize")
     ap.add_argument("--title", default="rocprofv3 summary")
@@ -701,8 +709,7 @@ def main(argv=None):
 
     # speculative verification: 16 requests, 8 new tokens each at 8192 tokens of context
     # (small qo_len rows, served by the chunked-prefill path; K / V streaming dominates)
-    wv = synthetic.build("spec_verify", 91, 32, 8, qo_len=[8] * 16, kv_len=[8192 + 8] * 16,
-                         num_blocks=16 * (8192 // 16 + 2) + 64, poison=False)
+    wv = spec_verify_workload()
     abv = algorithmic_bytes(wv)
     sv = Stepper(wv, 2)
     time_steps(sv, 10, 5, attention_only=True)
