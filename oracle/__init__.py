@@ -67,6 +67,17 @@ def _load():
     lib.oracle_float_to_half.restype = ctypes.c_uint16
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = f64
+    lib.oracle_append_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, ctypes.c_float]
+    lib.oracle_append_fp8.restype = ctypes.c_int
+    lib.oracle_copy_blocks_fp8.argtypes = [P, P, P, P, i32, i32, i32, i32, i32]
+    lib.oracle_copy_blocks_fp8.restype = ctypes.c_int
+    lib.oracle_attention_fp8.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f64, f64, f64,
+                                         P, P, P, P, P, P]
+    lib.oracle_attention_fp8.restype = ctypes.c_int
+    lib.oracle_encode_e4m3_array.argtypes = [P, P, i64]
+    lib.oracle_encode_e4m3_array.restype = None
+    lib.oracle_decode_e4m3_array.argtypes = [P, P, i64]
+    lib.oracle_decode_e4m3_array.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -173,16 +184,67 @@ def append_q8(kv_pool, k_new, v_new, slot_mapping, num_kv_heads, head_dim, block
     return p
 
 
+def encode_e4m3(x) -> np.ndarray:
+    """Doubles -> OCP FP8 E4M3 codes, to nearest with ties to even, saturating at 448."""
+    xa = _c(np.atleast_1d(x), np.float64)
+    out = np.empty(xa.shape, np.uint8)
+    _load().oracle_encode_e4m3_array(_ptr(xa), _ptr(out), xa.size)
+    return out
+
+
+def decode_e4m3(c) -> np.ndarray:
+    """OCP FP8 E4M3 codes -> doubles (NaN for S.1111.111)."""
+    ca = _c(np.atleast_1d(c), np.uint8)
+    out = np.empty(ca.shape, np.float64)
+    _load().oracle_decode_e4m3_array(_ptr(ca), _ptr(out), ca.size)
+    return out
+
+
+def append_fp8(k_pool, v_pool, k_new, v_new, slot_mapping, num_kv_heads, head_dim, block_size, num_blocks,
+               k_scale: float = 1.0, v_scale: float = 1.0):
+    """Store new bf16 K/V rows as E4M3 codes of x / scale into copies of FP8 pools
+    [num_blocks][Hkv][B][D] (uint8); returns (k_pool, v_pool)."""
+    kp = np.array(k_pool, dtype=np.uint8, copy=True)
+    vp = np.array(v_pool, dtype=np.uint8, copy=True)
+    kn, vn = _c(k_new, np.uint16), _c(v_new, np.uint16)
+    sm = _c(slot_mapping, np.int32)
+    rc = _load().oracle_append_fp8(_ptr(kp), _ptr(vp), _ptr(kn), _ptr(vn), _ptr(sm), int(sm.size), int(num_kv_heads),
+                                   int(head_dim), int(block_size), int(num_blocks), float(k_scale), float(v_scale))
+    if rc != 0:
+        raise ValueError(f"oracle_append_fp8 failed with code {rc}")
+    return kp, vp
+
+
+def copy_blocks_fp8(k_pool, v_pool, src, dst, num_kv_heads, head_dim, block_size, num_blocks):
+    """copy_blocks for FP8 pools (uint8, one byte per value)."""
+    kp = np.array(k_pool, dtype=np.uint8, copy=True)
+    vp = np.array(v_pool, dtype=np.uint8, copy=True)
+    s, d = _c(src, np.int32), _c(dst, np.int32)
+    if s.shape != d.shape:
+        raise ValueError("src and dst differ in length")
+    rc = _load().oracle_copy_blocks_fp8(_ptr(kp), _ptr(vp), _ptr(s), _ptr(d), int(s.size), int(num_kv_heads),
+                                        int(head_dim), int(block_size), int(num_blocks))
+    if rc != 0:
+        raise ValueError(f"oracle_copy_blocks_fp8 failed with code {rc}")
+    return kp, vp
+
+
 def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_kv_heads, head_dim,
-              block_size, num_blocks, scale, row_select=None, want_f64: bool = False, kv_format: str = "bf16"):
+              block_size, num_blocks, scale, row_select=None, want_f64: bool = False, kv_format: str = "bf16",
+              k_scale: float = 1.0, v_scale: float = 1.0):
     """Returns dict(out=bf16 bits [total_q][Hq][D], lse=float32 [total_q][Hq], pairs=int,
     and out_f64 / lse_f64 when ``want_f64``).  Rows not in ``row_select`` are left as zero.
     ``kv_format`` "q8_0" reads the q8_0 pool [num_blocks][Hkv][2][tile bytes] (uint8) passed as
-    ``k_pool`` (``v_pool`` is unused)."""
+    ``k_pool`` (``v_pool`` is unused); "fp8" reads E4M3 pools (uint8) with ``k_scale`` / ``v_scale``."""
     qa = _c(q, np.uint16)
+    extra = ()
     if kv_format == "q8_0":
         kp, fn = _c(k_pool, np.uint8), _load().oracle_attention_q8
         pools = (_ptr(kp),)
+    elif kv_format == "fp8":
+        kp, vp, fn = _c(k_pool, np.uint8), _c(v_pool, np.uint8), _load().oracle_attention_fp8
+        pools = (_ptr(kp), _ptr(vp))
+        extra = (float(k_scale), float(v_scale))
     elif kv_format == "bf16":
         kp, vp, fn = _c(k_pool, np.uint16), _c(v_pool, np.uint16), _load().oracle_attention
         pools = (_ptr(kp), _ptr(vp))
@@ -200,7 +262,7 @@ def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_
     pairs = ctypes.c_int64(0)
     rc = fn(_ptr(qa), *pools, _ptr(bt), int(bt.shape[1]), _ptr(qo), _ptr(kv),
                                   R, int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
-                                  int(num_blocks), float(scale), _ptr(sel), _ptr(out), _ptr(lse),
+                                  int(num_blocks), float(scale), *extra, _ptr(sel), _ptr(out), _ptr(lse),
                                   _ptr(out64), _ptr(lse64), ctypes.cast(ctypes.pointer(pairs), ctypes.c_void_p))
     if rc != 0:
         raise ValueError(f"oracle_attention failed with code {rc}")
@@ -214,14 +276,18 @@ def attention(q, k_pool, v_pool, block_tables, qo_len, kv_len, num_q_heads, num_
 def run_workload(wl, row_select=None, want_f64: bool = False):
     """Append the workload's new tokens, then attend; returns (k_pool, v_pool, result)."""
     fmt = getattr(wl, "kv_format", "bf16")
+    ks, vs = getattr(wl, "k_scale", 1.0), getattr(wl, "v_scale", 1.0)
     if fmt == "q8_0":
         kp = append_q8(wl.kv_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads, wl.head_dim,
                        wl.block_size, wl.num_blocks)
         vp = None
+    elif fmt == "fp8":
+        kp, vp = append_fp8(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
+                            wl.head_dim, wl.block_size, wl.num_blocks, ks, vs)
     else:
         kp, vp = append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, wl.num_kv_heads,
                         wl.head_dim, wl.block_size, wl.num_blocks)
     res = attention(wl.q, kp, vp, wl.block_tables, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
                     wl.head_dim, wl.block_size, wl.num_blocks, wl.scale, row_select=row_select,
-                    want_f64=want_f64, kv_format=fmt)
+                    want_f64=want_f64, kv_format=fmt, k_scale=ks, v_scale=vs)
     return kp, vp, res

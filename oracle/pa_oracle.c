@@ -46,6 +46,19 @@
  *                value represented = code * d
  *              Append quantises each new row this way; attention is the definition
  *              above applied to the represented values.
+ *
+ *   FP8 pool   (book section 8.4.4: KV stored in FP8 while Q stays BF16, figs. 8-27 and
+ *              8-28; section 8.4.2's cost model ΔT = ΔD/β − T_c with the H100 BF16 and FP8
+ *              slopes.)  The pages fix neither the FP8 encoding nor the scale's
+ *              granularity; the readings taken here: OCP FP8 E4M3 (1 sign bit, 4
+ *              exponent bits with bias 7, 3 fraction bits, no infinities, S.1111.111 =
+ *              NaN, largest magnitude 448), one binary32 scale per pool (k_scale for K,
+ *              v_scale for V), the bf16 pool's layout with one byte per value, and
+ *                code = e4m3(y), y = x / scale in binary32, to nearest with ties to
+ *                       even, magnitudes above 448 saturating to 448
+ *                value represented = decode(code) * scale
+ *              Append stores each new value this way; attention is the definition
+ *              above applied to the represented values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -154,6 +167,45 @@ uint16_t oracle_float_to_half(float x)
     return sign | (uint16_t)((Er + 15) << 10) | frac;
 }
 
+/* OCP FP8 E4M3 code -> double: (-1)^s * 2^(e-7) * (1 + f/8) for e >= 1, (-1)^s * 2^-6 *
+ * (f/8) for e = 0, NaN for e = 15 and f = 7 (the format has no infinities). */
+static double e4m3_to_double(uint8_t c)
+{
+    const double sign = (c & 0x80) ? -1.0 : 1.0;
+    const int e = (c >> 3) & 15, f = c & 7;
+    if (e == 15 && f == 7)
+        return NAN;
+    if (e == 0)
+        return sign * ldexp((double)f, -9);
+    return sign * ldexp(8.0 + f, e - 10);
+}
+
+double oracle_e4m3_to_double(uint8_t c) { return e4m3_to_double(c); }
+
+/* double -> E4M3 code, to nearest with ties to even; magnitudes above 448 become 448.
+ * Below 2^-6 the quantum is 2^-9 (subnormal codes 0..7; a rounded count of 8 is the
+ * smallest normal, code 8); in [2^E, 2^(E+1)) it is 2^(E-3). */
+uint8_t oracle_double_to_e4m3(double x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (a > 448.0)
+        a = 448.0;
+    if (a < 0.015625) {
+        const double k = nearbyint(ldexp(a, 9));          /* 0 .. 8, ties to even */
+        return (uint8_t)(sign | (uint8_t)k);
+    }
+    int E;
+    const double m = frexp(a, &E);                         /* a = m * 2^E, m in [0.5, 1) */
+    int e = E - 1;                                         /* a in [2^e, 2^(e+1)) */
+    double f = nearbyint(ldexp(m, 4) - 8.0);               /* (a / 2^e - 1) * 8, ties to even */
+    if (f == 8.0) {
+        f = 0.0;
+        ++e;
+    }
+    return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | (int)f));
+}
+
 /* One q8_0 group of 32 bf16 values -> 32 codes and the scale's binary16 bits. */
 static void quantize_q8_group(const uint16_t* x, int8_t* codes, uint16_t* scale)
 {
@@ -255,26 +307,69 @@ int oracle_append(uint16_t* k_pool, uint16_t* v_pool, const uint16_t* k_new, con
     return ORACLE_OK;
 }
 
+/* append into FP8 pools [num_blocks][Hkv][B][D] (one E4M3 code per value): each new bf16
+ * value x is stored as e4m3(x / scale), the division in binary32 (k_scale for K rows,
+ * v_scale for V rows); k_new / v_new are bf16 [n][Hkv][D]. */
+int oracle_append_fp8(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_new, const uint16_t* v_new,
+                      const int32_t* slot_mapping, int32_t n, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, float k_scale, float v_scale)
+{
+    if (!k_pool || !v_pool || (n > 0 && (!k_new || !v_new || !slot_mapping)) || n < 0 || !(k_scale > 0.0f) ||
+        !(v_scale > 0.0f))
+        return ORACLE_BAD_ARG;
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    for (int32_t t = 0; t < n; ++t) {
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0)
+            continue;
+        if (slot >= num_slots)
+            return ORACLE_BAD_BLOCK;
+        const int64_t blk = slot / block_size, off = slot % block_size;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            const size_t dst = (((size_t)blk * num_kv_heads + h) * block_size + (size_t)off) * head_dim;
+            const size_t src = ((size_t)t * num_kv_heads + h) * head_dim;
+            for (int32_t c = 0; c < head_dim; ++c) {
+                const float ky = (float)bf16_to_double(k_new[src + c]) / k_scale;
+                const float vy = (float)bf16_to_double(v_new[src + c]) / v_scale;
+                k_pool[dst + c] = oracle_double_to_e4m3((double)ky);
+                v_pool[dst + c] = oracle_double_to_e4m3((double)vy);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
 /*
  * block copy (book section 8.3.2, copy-on-write: the writer gets a private copy of a
  * shared block): block src[i]'s tiles of every KV head, K and V, become block dst[i]'s.
  * The pairs are applied in order; a valid list never writes a block it later reads.
  */
-int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
-                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks)
+static int copy_blocks_bytes(uint8_t* k_pool, uint8_t* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
+                             size_t block_bytes, int32_t num_blocks)
 {
     if (!k_pool || !v_pool || (n > 0 && (!src || !dst)) || n < 0)
         return ORACLE_BAD_ARG;
-    const size_t block_elems = (size_t)num_kv_heads * block_size * head_dim;
     for (int32_t i = 0; i < n; ++i) {
         if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
             continue;                      /* out-of-range pair: skipped */
-        memcpy(k_pool + (size_t)dst[i] * block_elems, k_pool + (size_t)src[i] * block_elems,
-               sizeof(uint16_t) * block_elems);
-        memcpy(v_pool + (size_t)dst[i] * block_elems, v_pool + (size_t)src[i] * block_elems,
-               sizeof(uint16_t) * block_elems);
+        memcpy(k_pool + (size_t)dst[i] * block_bytes, k_pool + (size_t)src[i] * block_bytes, block_bytes);
+        memcpy(v_pool + (size_t)dst[i] * block_bytes, v_pool + (size_t)src[i] * block_bytes, block_bytes);
     }
     return ORACLE_OK;
+}
+
+int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks)
+{
+    return copy_blocks_bytes((uint8_t*)k_pool, (uint8_t*)v_pool, src, dst, n,
+                             sizeof(uint16_t) * (size_t)num_kv_heads * block_size * head_dim, num_blocks);
+}
+
+/* block copy for FP8 pools (one byte per value). */
+int oracle_copy_blocks_fp8(uint8_t* k_pool, uint8_t* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks)
+{
+    return copy_blocks_bytes(k_pool, v_pool, src, dst, n, (size_t)num_kv_heads * block_size * head_dim, num_blocks);
 }
 
 /*
@@ -287,15 +382,20 @@ int oracle_copy_blocks(uint16_t* k_pool, uint16_t* v_pool, const int32_t* src, c
  * (query, key) pairs visited for one head, summed over the computed rows: an
  * instrument for the causal mask.
  */
-enum { FMT_BF16 = 0, FMT_Q8_0 = 1 };
+enum { FMT_BF16 = 0, FMT_Q8_0 = 1, FMT_FP8 = 2 };
 
 /* The values of token `tok` of physical block `phys`, KV head kvh, as doubles.  q8_0:
  * `pool` points at the K or the V tile of (block 0, KV head 0), and the tiles of
  * consecutive (block, KV head) pairs lie two tiles apart. */
 static void load_row(int fmt, const void* pool, int32_t phys, int32_t kvh, int32_t tok, int32_t num_kv_heads,
-                     int32_t head_dim, int32_t block_size, double* dst)
+                     int32_t head_dim, int32_t block_size, double pool_scale, double* dst)
 {
-    if (fmt == FMT_BF16) {
+    if (fmt == FMT_FP8) {
+        const uint8_t* src = (const uint8_t*)pool +
+                             (((size_t)phys * num_kv_heads + kvh) * block_size + (size_t)tok) * head_dim;
+        for (int32_t c = 0; c < head_dim; ++c)
+            dst[c] = e4m3_to_double(src[c]) * pool_scale;
+    } else if (fmt == FMT_BF16) {
         const uint16_t* src = (const uint16_t*)pool +
                               (((size_t)phys * num_kv_heads + kvh) * block_size + (size_t)tok) * head_dim;
         for (int32_t c = 0; c < head_dim; ++c)
@@ -317,8 +417,8 @@ static int attention_impl(int fmt, const uint16_t* q, const void* k_pool, const 
                           const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
                           const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale,
-                          const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
-                          double* lse_f64, int64_t* pair_count)
+                          double k_scale, double v_scale, const uint8_t* row_select, uint16_t* out, float* lse,
+                          double* out_f64, double* lse_f64, int64_t* pair_count)
 {
     if (!q || !k_pool || !v_pool || !block_tables || !qo_len || !kv_len)
         return ORACLE_BAD_ARG;
@@ -391,7 +491,7 @@ static int attention_impl(int fmt, const uint16_t* q, const void* k_pool, const 
                 double m = -INFINITY;
                 for (int64_t j = 0; j <= p; ++j) {
                     load_row(fmt, k_pool, bt[j / block_size], kvh, (int32_t)(j % block_size), num_kv_heads,
-                             head_dim, block_size, kvrow);
+                             head_dim, block_size, k_scale, kvrow);
                     double dot = 0.0;
                     for (int32_t c = 0; c < head_dim; ++c)
                         dot += qd[c] * kvrow[c];
@@ -408,7 +508,7 @@ static int attention_impl(int fmt, const uint16_t* q, const void* k_pool, const 
                     double e = exp(s[j] - m);
                     l += e;
                     load_row(fmt, v_pool, bt[j / block_size], kvh, (int32_t)(j % block_size), num_kv_heads,
-                             head_dim, block_size, kvrow);
+                             head_dim, block_size, v_scale, kvrow);
                     for (int32_t c = 0; c < head_dim; ++c)
                         acc[c] += e * kvrow[c];
                 }
@@ -444,8 +544,21 @@ int oracle_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
                      double* lse_f64, int64_t* pair_count)
 {
     return attention_impl(FMT_BF16, q, k_pool, v_pool, block_tables, max_blocks, qo_len, kv_len, num_reqs,
-                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, row_select, out, lse,
-                          out_f64, lse_f64, pair_count);
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, 1.0, 1.0, row_select,
+                          out, lse, out_f64, lse_f64, pair_count);
+}
+
+/* attention over FP8 pools [num_blocks][Hkv][B][D] (E4M3 codes) with scales k_scale / v_scale. */
+int oracle_attention_fp8(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                         const int32_t* block_tables, int32_t max_blocks, const int32_t* qo_len,
+                         const int32_t* kv_len, int32_t num_reqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, double scale, double k_scale,
+                         double v_scale, const uint8_t* row_select, uint16_t* out, float* lse, double* out_f64,
+                         double* lse_f64, int64_t* pair_count)
+{
+    return attention_impl(FMT_FP8, q, k_pool, v_pool, block_tables, max_blocks, qo_len, kv_len, num_reqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, k_scale, v_scale,
+                          row_select, out, lse, out_f64, lse_f64, pair_count);
 }
 
 /* attention over a q8_0 pool [num_blocks][Hkv][2][tile bytes]; everything else as above. */
@@ -459,8 +572,21 @@ int oracle_attention_q8(const uint16_t* q, const uint8_t* kv_pool, const int32_t
         return ORACLE_BAD_ARG;
     return attention_impl(FMT_Q8_0, q, kv_pool, kv_pool + oracle_q8_tile_bytes(head_dim, block_size), block_tables,
                           max_blocks, qo_len, kv_len, num_reqs,
-                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, row_select, out, lse,
-                          out_f64, lse_f64, pair_count);
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, 1.0, 1.0, row_select,
+                          out, lse, out_f64, lse_f64, pair_count);
+}
+
+/* Element-wise E4M3 encode / decode over arrays (for the format tests). */
+void oracle_encode_e4m3_array(const double* x, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_double_to_e4m3(x[i]);
+}
+
+void oracle_decode_e4m3_array(const uint8_t* c, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = e4m3_to_double(c[i]);
 }
 
 /* Element-wise oracle_double_to_bf16 over an array (for the rounding tests). */

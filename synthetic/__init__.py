@@ -88,6 +88,9 @@ class Workload:
     # q8_0 only (k_pool / v_pool are then None): uint8 [num_blocks][num_kv_heads][2][q8_tile_bytes],
     # each (block, KV head) holding its K tile, then its V tile
     kv_pool: Optional[np.ndarray] = None
+    # fp8 only: k_pool / v_pool are uint8 E4M3 codes in the bf16 layout; a value is code * scale
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_reqs(self) -> int:
@@ -262,6 +265,76 @@ def build_q8(name: str, seed: int, num_q_heads: int, num_kv_heads: int, qo_len, 
                     block_tables=bt, q=q, k_pool=None, v_pool=None, k_new=k_new, v_new=v_new,
                     slot_mapping=slots, shared_prefix_blocks=shared_prefix_blocks, kv_format="q8_0",
                     kv_pool=kv_pool)
+
+
+FP8_NAN = np.uint8(0x7F)
+
+
+def build_fp8(name: str, seed: int, num_q_heads: int, num_kv_heads: int, qo_len, kv_len, num_blocks: int,
+              head_dim: int = 128, block_size: int = 16, shared_prefix_blocks: int = 0, poison: bool = True,
+              q_scale: float = 1.0, k_scale: float = 0.375, v_scale: float = 0.3125) -> Workload:
+    """Like ``build`` with FP8 pools (OCP E4M3 codes, one byte per value, the bf16 layout)
+    and per-pool scales.  Context tokens already in the cache are drawn in the storage
+    format itself: a random sign, exponent field 3..8 (magnitudes 2^-4 .. 3.75) and fraction
+    field 0..7, so every code is finite.  Slots that hold no context token keep the NaN
+    code when ``poison`` is set.  The new tokens' K/V are bf16 N(0,1), stored by the append."""
+    qo_len = np.asarray(qo_len, dtype=np.int32)
+    kv_len = np.asarray(kv_len, dtype=np.int32)
+    R = qo_len.shape[0]
+    if np.any(qo_len < 1) or np.any(kv_len < qo_len):
+        raise ValueError("need 1 <= qo_len <= kv_len")
+    s_len, s_place, s_k, s_v, s_new, s_q = _streams(seed)
+    B, D, Hkv, Hq = block_size, head_dim, num_kv_heads, num_q_heads
+    nb = [-(-int(L) // B) for L in kv_len]
+    bt = place_blocks(s_place, num_blocks, nb, shared_prefix_blocks, None)
+    fill = FP8_NAN if poison else np.uint8(0)
+    k_pool = np.full((num_blocks, Hkv, B, D), fill, dtype=np.uint8)
+    v_pool = np.full((num_blocks, Hkv, B, D), fill, dtype=np.uint8)
+    filled = set()
+    for r in range(R):
+        ctx = int(kv_len[r] - qo_len[r])
+        for b in range(-(-ctx // B)):
+            phys = int(bt[r, b])
+            n = min(B, ctx - b * B)
+            if phys in filled:
+                continue
+            for pool, s_x in ((k_pool, s_k), (v_pool, s_v)):
+                sign = s_x.integers(0, 2, (Hkv, n, D), dtype=np.uint8) << 7
+                expo = s_x.integers(3, 9, (Hkv, n, D), dtype=np.uint8) << 3
+                frac = s_x.integers(0, 8, (Hkv, n, D), dtype=np.uint8)
+                pool[phys, :, :n, :] = sign | expo | frac
+            if n == B:
+                filled.add(phys)
+    n_new = int(qo_len.sum())
+    k_new = f32_to_bf16_bits(s_new.standard_normal((n_new, Hkv, D), dtype=np.float32))
+    v_new = f32_to_bf16_bits(s_new.standard_normal((n_new, Hkv, D), dtype=np.float32))
+    slots = np.empty(n_new, dtype=np.int32)
+    t = 0
+    for r in range(R):
+        for pos in range(int(kv_len[r] - qo_len[r]), int(kv_len[r])):
+            slots[t] = slot_of(bt[r], pos, B)
+            t += 1
+    q = f32_to_bf16_bits(s_q.standard_normal((n_new, Hq, D), dtype=np.float32) * np.float32(q_scale))
+    wl = Workload(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
+                  num_blocks=num_blocks, scale=1.0 / np.sqrt(D), qo_len=qo_len, kv_len=kv_len,
+                  block_tables=bt, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
+                  slot_mapping=slots, shared_prefix_blocks=shared_prefix_blocks, kv_format="fp8",
+                  k_scale=float(k_scale), v_scale=float(v_scale))
+    return wl
+
+
+def config_tiny_fp8(seed: int = 12, poison: bool = True, q_scale: float = 1.0) -> Workload:
+    """config_tiny's shape (4 decode rows, 8 q / 2 kv heads) on FP8 pools."""
+    return build_fp8("tiny_fp8", seed, 8, 2, qo_len=[1] * 4, kv_len=[17, 64, 100, 250], num_blocks=64,
+                     poison=poison, q_scale=q_scale)
+
+
+def config_decode_fp8(seed: int = 2, num_reqs: int = 32, poison: bool = True) -> Workload:
+    """The Qwen3-8B decode step (32 rows, kv_len 2048 + U[0,255]) on FP8 pools of as many
+    blocks as the bf16 one; the default seed gives config_decode's lengths and tables."""
+    kv = 2048 + _uniform_extra(seed, num_reqs)
+    return build_fp8("qwen3_8b_decode_step_fp8", seed, 32, 8, qo_len=[1] * num_reqs, kv_len=kv,
+                     num_blocks=POOL_BLOCKS_12GIB, poison=poison)
 
 
 def config_tiny_q8(seed: int = 11, poison: bool = True, q_scale: float = 1.0) -> Workload:

@@ -608,3 +608,82 @@ def test_q8_append_writes_exactly_the_quantised_rows():
             want[blk, :, which, off * 128:(off + 1) * 128] = codes[t].view(np.uint8)
             want[blk, :, which, 2048 + off * 8:2048 + off * 8 + 8] = scales[t].view(np.uint8).reshape(wl.num_kv_heads, 8)
     assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ FP8 (E4M3) pool
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    """All 256 codes against torch's float8_e4m3fn (the OCP E4M3 format): 448 at 0x7E, NaN at
+    S.1111.111, subnormals k * 2^-9."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode_e4m3(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0**-9 and got[0x08] == 2.0**-6 and got[0x38] == 1.0
+
+
+def test_e4m3_encode_matches_torch_and_saturates():
+    """Encoding rounds to nearest with ties to even (torch's float -> float8_e4m3fn on every
+    value up to 464, where torch's result is still finite, including every midpoint between
+    neighbouring codes); magnitudes above 448 saturate to 448 (torch gives NaN past 464)."""
+    rng = np.random.default_rng(21)
+    vals = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.uniform(-4, 2.4, 20000),
+                           np.linspace(-464, 464, 4001)])
+    finite = oracle.decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (finite[:-1] + finite[1:]) / 2
+    vals = np.concatenate([vals, mids, -mids, [0.0, -0.0, 448.0, -448.0, 2.0**-10, 3 * 2.0**-11]])
+    vals = vals[np.abs(vals) <= 464]
+    got = oracle.encode_e4m3(vals)
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    big = oracle.encode_e4m3([464.5, 500.0, 1e6, -1e30])
+    assert list(big) == [0x7E, 0x7E, 0x7E, 0xFE]
+
+
+def test_fp8_bytes_are_half_of_bf16():
+    """Book section 8.4.2: one byte per value against two; per token and layer of Qwen3-8B
+    (8 KV heads x 128 dims, K and V) 4096 bytes against 8192, the byte ratio behind the
+    pages' smaller per-token slope of the FP8 fit (2.37e-5 against 4.37e-5 ms per token)."""
+    wl = synthetic.config_decode_fp8(poison=False)
+    assert wl.k_pool.dtype == np.uint8 and wl.k_pool.shape == (synthetic.POOL_BLOCKS_12GIB, 8, 16, 128)
+    per_token = 2 * 8 * 128
+    assert per_token * 2 == QWEN_KV_BYTES_PER_TOKEN_BF16 // 36
+
+
+def test_fp8_attention_equals_bf16_attention_on_the_represented_values():
+    """With power-of-two scales every represented value code * scale is a bf16 value, so
+    attention over the FP8 pools must equal the (pinned) bf16 definition over pools that hold
+    those values, to the last bit of the fp64 result."""
+    wl = synthetic.build_fp8("fp8_pin", 31, 8, 2, qo_len=[1, 5, 1], kv_len=[40, 70, 129], num_blocks=40,
+                             poison=False, k_scale=0.5, v_scale=0.25)
+    kp, vp, res = oracle.run_workload(wl, want_f64=True)
+    kb = f32_to_bf16_bits((oracle.decode_e4m3(kp) * 0.5).astype(np.float32)).reshape(kp.shape)
+    vb = f32_to_bf16_bits((oracle.decode_e4m3(vp) * 0.25).astype(np.float32)).reshape(vp.shape)
+    ref = oracle.attention(wl.q, kb, vb, wl.block_tables, wl.qo_len, wl.kv_len, wl.num_q_heads, wl.num_kv_heads,
+                           128, 16, wl.num_blocks, wl.scale, want_f64=True)
+    assert np.array_equal(res["out_f64"], ref["out_f64"]) and np.array_equal(res["lse_f64"], ref["lse_f64"])
+
+
+def test_fp8_append_stores_the_encoded_quotients():
+    """Each new value x lands as encode(float32(x / scale)) at its slot; every other byte of
+    the pools is unchanged; a value that is already code * scale round-trips exactly."""
+    wl = synthetic.build_fp8("fp8_append", 32, 8, 2, qo_len=[1, 3], kv_len=[30, 50], num_blocks=12,
+                             poison=True, k_scale=0.375, v_scale=3.0)
+    kp, vp = oracle.append_fp8(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.slot_mapping, 2, 128, 16, 12,
+                               wl.k_scale, wl.v_scale)
+    wk, wv = wl.k_pool.copy(), wl.v_pool.copy()
+    for t, s in enumerate(wl.slot_mapping):
+        blk, off = divmod(int(s), 16)
+        for new, want, sc in ((wl.k_new, wk, wl.k_scale), (wl.v_new, wv, wl.v_scale)):
+            q = (bf16_bits_to_f32(new[t]) / np.float32(sc)).astype(np.float32)
+            want[blk, :, off] = oracle.encode_e4m3(q.astype(np.float64).ravel()).reshape(2, 128)
+    assert np.array_equal(kp, wk) and np.array_equal(vp, wv)
+    # round trip of representable values (scale a power of two keeps them in bf16)
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    x = f32_to_bf16_bits((oracle.decode_e4m3(codes) * 2.0).astype(np.float32))
+    x = np.concatenate([x, np.zeros(128 - x.size, np.uint16)])[None, None, :].repeat(2, axis=1)
+    kp2, _ = oracle.append_fp8(np.zeros((1, 2, 16, 128), np.uint8), np.zeros((1, 2, 16, 128), np.uint8), x, x,
+                               [0], 2, 128, 16, 1, 2.0, 2.0)
+    assert np.array_equal(kp2[0, 0, 0, :codes.size], codes)
