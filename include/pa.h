@@ -365,6 +365,41 @@ pa_status pa_copy_blocks_q8(const pa_geometry* geometry, void* kv_pool_q8, const
                             const int32_t* dst_blocks, int32_t n, void* stream);
 
 /*
+ * FP8 KV pools (book section 8.4.4: KV stored in FP8 while Q stays BF16, figs. 8-27 and
+ * 8-28; section 8.4.2's cost model ΔT = ΔD/β − T_c).  Two pools with the bf16 pools'
+ * layout, uint8 [num_blocks][num_kv_heads][block_size][head_dim], one OCP FP8 E4M3 code
+ * per value (1 sign bit, 4 exponent bits with bias 7, 3 fraction bits; largest magnitude
+ * 448; S.1111.111 is NaN), and one binary32 scale per pool: a code c stands for
+ * decode(c) * k_scale in the K pool and decode(c) * v_scale in the V pool.  Scales must be
+ * finite and > 0 (else PA_ERR_SHAPE).
+ *
+ * pa_append_kv_fp8: each new bf16 value x is stored as the code of x / scale (binary32
+ * division), to nearest with ties to even, magnitudes above 448 saturating to 448.  New
+ * rows must be finite.  Slot rules and errors as for pa_append_kv.
+ */
+pa_status pa_append_kv_fp8(const pa_geometry* geometry, void* k_pool_fp8, void* v_pool_fp8, const void* k_new,
+                           const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, float k_scale,
+                           float v_scale, void* stream);
+
+/*
+ * pa_attention_batch over FP8 pools, for any batch pa_attention_batch takes (decode rows,
+ * chunked-prefill rows, shared-prefix groups); outputs, splits, workspace and errors as for
+ * pa_attention_batch.  Every E4M3 value is a bf16 value, so the codes are widened to bf16
+ * exactly and the bf16 arithmetic runs on them; k_scale multiplies the scores (folded
+ * into the score scale in binary32) and v_scale each normalised output.  The append into
+ * FP8 pools is always its own launch (pa_append_kv_fp8 first).
+ */
+pa_status pa_attention_batch_fp8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q,
+                                 const void* k_pool_fp8, const void* v_pool_fp8, const int32_t* block_tables,
+                                 int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes, float k_scale,
+                                 float v_scale, void* stream);
+
+/* pa_copy_blocks for FP8 pools (one byte per value); same rules and errors. */
+pa_status pa_copy_blocks_fp8(const pa_geometry* geometry, void* k_pool_fp8, void* v_pool_fp8,
+                             const int32_t* src_blocks, const int32_t* dst_blocks, int32_t n, void* stream);
+
+/*
  * Reference-counted block allocator with stream-deferred release (host side; book
  * section 8.3.2 and figs. 8-14 / 8-15): a physical block carries one reference per block
  * table that points at it, so a shared prefix is a set of blocks with counts above one;

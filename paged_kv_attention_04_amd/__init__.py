@@ -92,6 +92,10 @@ def lib():
     L.pa_attention_batch_q8.argtypes = [G, PL, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_attention_batch_noalloc.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P]
     L.pa_copy_blocks_q8.argtypes = [G, P, P, P, i32, P]
+    f32 = ctypes.c_float
+    L.pa_append_kv_fp8.argtypes = [G, P, P, P, P, P, i32, f32, f32, P]
+    L.pa_attention_batch_fp8.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, f32, f32, P]
+    L.pa_copy_blocks_fp8.argtypes = [G, P, P, P, P, i32, P]
     L.pa_validate_copy.argtypes = [G, P, P, i32, P]
     L.pa_query_num_cus.argtypes = [i32, P]
     L.pa_allocator_create.argtypes = [i32, P]
@@ -106,7 +110,8 @@ def lib():
     L.pa_allocator_sync.argtypes = [P]
     for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_plan_shared_prefix_q8", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
                "pa_validate_append", "pa_copy_blocks", "pa_validate_copy", "pa_append_kv_q8",
-               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_attention_batch_noalloc", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
+               "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_append_kv_fp8", "pa_attention_batch_fp8",
+               "pa_copy_blocks_fp8", "pa_attention_batch_noalloc", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
                "pa_allocator_alloc", "pa_allocator_retain", "pa_allocator_release", "pa_allocator_cow",
                "pa_allocator_refcount", "pa_allocator_num_free", "pa_allocator_sync"):
         getattr(L, fn).restype = ctypes.c_int
@@ -287,6 +292,49 @@ def pa_copy_blocks_q8(geometry: Geometry, kv_pool_q8, src_blocks, dst_blocks, st
         _dev_ptr(dst_blocks, i32, "dst_blocks"), n, _stream_handle(stream)))
 
 
+def pa_append_kv_fp8(geometry: Geometry, k_pool_fp8, v_pool_fp8, k_new, v_new, slot_mapping, k_scale: float = 1.0,
+                     v_scale: float = 1.0, stream=None) -> None:
+    """Store new bf16 K/V rows as E4M3 codes of x / scale in FP8 pools (uint8, the bf16 layout)."""
+    import torch
+    n = int(slot_mapping.numel())
+    if n == 0:
+        return
+    bf, u8 = _bf16_types(), (torch.uint8,)
+    _check("pa_append_kv_fp8", lib().pa_append_kv_fp8(
+        ctypes.byref(geometry), _dev_ptr(k_pool_fp8, u8, "k_pool_fp8"), _dev_ptr(v_pool_fp8, u8, "v_pool_fp8"),
+        _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"),
+        _dev_ptr(slot_mapping, (torch.int32,), "slot_mapping"), n, float(k_scale), float(v_scale),
+        _stream_handle(stream)))
+
+
+def pa_attention_batch_fp8(geometry: Geometry, plan: Plan, q, k_pool_fp8, v_pool_fp8, block_tables, qo_indptr, kv_len,
+                           out, lse, workspace=None, k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """Attention over FP8 pools with per-pool scales; the rest as pa_attention_batch."""
+    import torch
+    bf, i32, u8 = _bf16_types(), (torch.int32,), (torch.uint8,)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_attention_batch_fp8", lib().pa_attention_batch_fp8(
+        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(k_pool_fp8, u8, "k_pool_fp8"),
+        _dev_ptr(v_pool_fp8, u8, "v_pool_fp8"), _dev_ptr(block_tables, i32, "block_tables"),
+        int(block_tables.shape[1]), _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"),
+        _dev_ptr(out, bf, "out"), _dev_ptr(lse, (torch.float32,), "lse"), _dev_ptr(workspace, name="workspace"),
+        ws_bytes, float(k_scale), float(v_scale), _stream_handle(stream)))
+
+
+def pa_copy_blocks_fp8(geometry: Geometry, k_pool_fp8, v_pool_fp8, src_blocks, dst_blocks, stream=None) -> None:
+    import torch
+    n = int(src_blocks.numel())
+    if int(dst_blocks.numel()) != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    if n == 0:
+        return
+    u8, i32 = (torch.uint8,), (torch.int32,)
+    _check("pa_copy_blocks_fp8", lib().pa_copy_blocks_fp8(
+        ctypes.byref(geometry), _dev_ptr(k_pool_fp8, u8, "k_pool_fp8"), _dev_ptr(v_pool_fp8, u8, "v_pool_fp8"),
+        _dev_ptr(src_blocks, i32, "src_blocks"), _dev_ptr(dst_blocks, i32, "dst_blocks"), n,
+        _stream_handle(stream)))
+
+
 def pa_attention_batch(geometry: Geometry, plan: Plan, q, k_pool, v_pool, block_tables, qo_indptr, kv_len, out, lse,
                        workspace=None, stream=None) -> None:
     import torch
@@ -462,6 +510,7 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
         if rc:
             raise PaError("pa_validate_append", rc, f" at token {bad}")
     q8 = getattr(wl, "kv_format", "bf16") == "q8_0"
+    fp8 = getattr(wl, "kv_format", "bf16") == "fp8"
     plan = pa_plan(g, wl.qo_len, wl.kv_len, num_cus, split_blocks, prefill_splits)
     if cascade:
         pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, num_cus, min_shared_blocks,
@@ -484,12 +533,17 @@ def run_workload(wl, split_blocks: int = 0, num_cus: int = 256, device="cuda", v
     if q8:
         pa_append_kv_q8(g, kp, kn, vn, sm)
         pa_attention_batch_q8(g, plan, q, kp, bt, qo_indptr, kv, out, lse, ws)
+    elif fp8:
+        pa_append_kv_fp8(g, kp, vp, kn, vn, sm, wl.k_scale, wl.v_scale)
+        pa_attention_batch_fp8(g, plan, q, kp, vp, bt, qo_indptr, kv, out, lse, ws, wl.k_scale, wl.v_scale)
     else:
         pa_append_kv(g, kp, vp, kn, vn, sm)
         pa_attention_batch(g, plan, q, kp, vp, bt, qo_indptr, kv, out, lse, ws)
     torch.cuda.synchronize()
     if q8:
         pools = (kp.cpu().numpy(), None)
+    elif fp8:
+        pools = (kp.cpu().numpy(), vp.cpu().numpy())
     else:
         pools = (kp.cpu().numpy().view(np.uint16), vp.cpu().numpy().view(np.uint16))
     return pools + (out.cpu().numpy().view(np.uint16), lse.cpu().numpy())

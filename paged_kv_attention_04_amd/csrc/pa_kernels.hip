@@ -18,6 +18,8 @@
 // q8_0 pool keeps each (block, KV head)'s K tile and V tile side by side (4352 bytes):
 // half-size tiles read as separate 2 KiB pieces stream markedly slower from HBM.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
@@ -266,6 +268,56 @@ __global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict_
     }
 }
 
+// Append into FP8 pools (the bf16 layout, one E4M3 code per value): one thread per 16 values
+// of one (new token, KV head) row, K and V.  Each value x is stored as the E4M3 code of
+// x / scale (binary32 division), clamped to +-448 first so that the conversion, which
+// rounds to nearest with ties to even, saturates instead of producing NaN.
+__global__ __launch_bounds__(256) void pa_append_fp8_scatter(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                             const uint16_t* __restrict__ k_new,
+                                                             const uint16_t* __restrict__ v_new,
+                                                             const int32_t* __restrict__ slot_mapping, int32_t n_tokens,
+                                                             int32_t num_kv_heads, int64_t num_slots, float k_scale,
+                                                             float v_scale)
+{
+    constexpr int kChunks = kHeadDim / 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_token = (int64_t)num_kv_heads * kChunks;
+    if (idx >= (int64_t)n_tokens * per_token)
+        return;
+    const int32_t t = (int32_t)(idx / per_token);
+    const int32_t rem = (int32_t)(idx - (int64_t)t * per_token);
+    const int32_t h = rem / kChunks, c = rem % kChunks;
+    const int32_t slot = slot_mapping[t];
+    if (slot < 0 || (int64_t)slot >= num_slots)
+        return;
+    const int64_t blk = slot / kBlock, off = slot % kBlock;
+    const int64_t src = ((int64_t)t * num_kv_heads + h) * kHeadDim + 16 * c;                 // elements
+    const int64_t dst = ((blk * num_kv_heads + h) * kBlock + off) * kHeadDim + 16 * c;      // bytes
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const u32x4* in = reinterpret_cast<const u32x4*>((which ? v_new : k_new) + src);
+        const float sc = which ? v_scale : k_scale;
+        uint32_t packed[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 w = in[i];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    y[2 * e] = fminf(fmaxf(bf16_lo(w[2 * j + e]) / sc, -448.0f), 448.0f);
+                    y[2 * e + 1] = fminf(fmaxf(bf16_hi(w[2 * j + e]) / sc, -448.0f), 448.0f);
+                }
+                uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
+                word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+                packed[2 * i + j] = word;
+            }
+        }
+        *reinterpret_cast<u32x4*>((which ? v_pool : k_pool) + dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    }
+}
+
 // ------------------------------------------------------------------------------ block copy
 
 // One thread per 16 bytes of a block: pairs x npools x blk_chunks threads, where a block
@@ -310,7 +362,8 @@ struct DecodeParams {
     int32_t num_blocks;
     int32_t split_blocks;
     int32_t max_splits;
-    float scale_log2;   // score scale times log2(e): softmax runs in base 2
+    float scale_log2;   // score scale times log2(e): softmax runs in base 2 (times the K scale of an FP8 pool)
+    float v_scale;      // FP8 pool: the V scale, applied to each normalised output (1 otherwise)
     // shared-prefix groups: rows first .. first + count - 1 skip their first `blocks`
     // blocks, whose partial results (prefix_splits of them per row and head) an earlier
     // launch left in px_part_o / px_part_lse
@@ -360,6 +413,49 @@ __device__ inline void load_stage(KvStage& s, const uint16_t* ktile, const uint1
     for (int i = 0; i < 4; ++i)
         s.v[i] = __builtin_nontemporal_load(vp + 64 * i);
 }
+
+// FP8 pool: the bf16 tile's layout with one E4M3 code per value, read at the same element
+// positions as load_stage (8 bytes where it reads 16) and widened to bf16 before use:
+// every E4M3 value is a bf16 value, so the widening is exact and the bf16 arithmetic runs
+// unchanged (the K scale is folded into the score scale, the V scale into the output).
+struct KvStageFp8 {
+    u32x2 k[4];
+    u32x2 v[4];
+};
+
+__device__ inline void load_stage_fp8(KvStageFp8& s, const uint8_t* ktile, const uint8_t* vtile, int lane)
+{
+    const u32x2* kp = reinterpret_cast<const u32x2*>(ktile);
+    const u32x2* vp = reinterpret_cast<const u32x2*>(vtile) + lane;
+    const int t8 = lane >> 3, c8 = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s.k[i] = __builtin_nontemporal_load(kp + (t8 + 8 * (i >> 1)) * 16 + c8 + 8 * (i & 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s.v[i] = __builtin_nontemporal_load(vp + 64 * i);
+}
+
+// Eight E4M3 codes -> eight bf16 values (four bf16 pairs, first code in the low half).
+__device__ inline u32x4 e4m3x8_to_bf16(const u32x2 w)
+{
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
+}
+
+__device__ inline KvStage widen(const KvStageFp8& s)
+{
+    KvStage o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o.k[i] = e4m3x8_to_bf16(s.k[i]);
+        o.v[i] = e4m3x8_to_bf16(s.v[i]);
+    }
+    return o;
+}
+__device__ inline KvStage widen(const KvStage& s) { return s; }
 
 // q8_0 tile: codes [16][128] int8, then scales [16][4] binary16.
 // K: lane = 8 * t8 + c8 reads the 16 codes of dims 16 c8 .. 16 c8 + 15 (one scale group,
@@ -618,11 +714,12 @@ __device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, 
 // the softmax weight times the value's scale, and -1152 times the weights' sum is taken
 // off the accumulators at the end.  Q is widened to binary16, which holds every bf16
 // value of magnitude in [2^-14, 65504] exactly.
-template <bool kQ8, bool kFused>
+template <bool kQ8, bool kFused, bool kFp8 = false>
 __device__ __attribute__((always_inline)) inline void decode_body(const DecodeParams& p, int bid)
 {
+    static_assert(!(kFp8 && (kQ8 || kFused)), "FP8 pools: own format, append in its own launch");
     constexpr int kDepth = kQ8 ? kDecodeDepthQ8 : kDecodeDepth;
-    using Stage = std::conditional_t<kQ8, KvStageQ8, KvStage>;
+    using Stage = std::conditional_t<kQ8, KvStageQ8, std::conditional_t<kFp8, KvStageFp8, KvStage>>;
     __shared__ float p_lds[kDecodeWaves][kBlock * kGroup];
     __shared__ float o_lds[kDecodeWaves][kGroup * kHeadDim];
     __shared__ float l_lds[kDecodeWaves][kGroup];
@@ -667,6 +764,10 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
             const uint8_t* kt = reinterpret_cast<const uint8_t*>(p.k_pool) +
                                 ((int64_t)id * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);
             load_stage_q8(st, kt, kt + pa::kQ8TileBytes, lane);
+        } else if constexpr (kFp8) {
+            const int64_t off = ((int64_t)id * p.num_kv_heads + kvh) * kBlock * kHeadDim;   // one byte per value
+            load_stage_fp8(st, reinterpret_cast<const uint8_t*>(p.k_pool) + off,
+                           reinterpret_cast<const uint8_t*>(p.v_pool) + off, lane);
         } else {
             const int64_t off = ((int64_t)id * p.num_kv_heads + kvh) * kBlock * kHeadDim;
             load_stage(st, p.k_pool + off, p.v_pool + off, lane);
@@ -760,7 +861,12 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     float* pw = p_lds[wave];
 
     auto process = [&](const Stage& st_in, int j) __attribute__((always_inline)) {
-        Stage st = st_in;
+        auto st = [&]() {
+            if constexpr (kQ8)
+                return st_in;
+            else
+                return widen(st_in);                  // FP8 codes -> bf16 (exact); bf16 as is
+        }();
         if constexpr (kFused) {
             if (g0 + wave + kDecodeWaves * j == new_blk) {   // the block that holds the new token
                 if (t8 == new_off) {
@@ -955,7 +1061,7 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     if (lane < 16) {
 #pragma unroll
         for (int h = 0; h < kGroup; ++h) {
-            const float inv = empty ? 0.f : 1.f / readlane_f(ltot, h);
+            const float inv = empty ? 0.f : p.v_scale / readlane_f(ltot, h);
             f32x4* dst = reinterpret_cast<f32x4*>(&o_lds[wave][h * kHeadDim + c16 * 8]);
             dst[0] = f32x4{acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
             dst[1] = f32x4{acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
@@ -1033,10 +1139,10 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
         merge_rows_results<1, 32>(p, &r, 1, vkv, nprefix);
 }
 
-template <bool kQ8, bool kFused>
+template <bool kQ8, bool kFused, bool kFp8 = false>
 __global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split(DecodeParams p)
 {
-    decode_body<kQ8, kFused>(p, blockIdx.x);
+    decode_body<kQ8, kFused, kFp8>(p, blockIdx.x);
 }
 
 // ------------------------------------------------------------------------------ prefill
@@ -1061,6 +1167,7 @@ struct PrefillParams {
     int32_t num_prefill_rows;
     int32_t splits;             // key splits per tile
     float scale_log2;
+    float v_scale;      // FP8 pool: the V scale, applied to each normalised output (1 otherwise)
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];
     int32_t tile_start[PA_MAX_PREFILL_ROWS + 1];
     // shared-prefix mode: one tile per group, its rows (request, head) of the group's
@@ -1623,10 +1730,11 @@ __device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char
 // (exact) to the same LDS places the bf16 copies use and the two scales as floats to a
 // [group][key] table beside the tiles.  The products then run on binary16 operands (Q
 // converted once, exact for bf16 values inside the binary16 range), see pf_step_q8.
-template <bool kCascade, bool kFused = false, bool kQ8 = false, int kRG = 4, int kRB = 2>
+template <bool kCascade, bool kFused = false, bool kQ8 = false, int kRG = 4, int kRB = 2, bool kFp8 = false>
 __device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
                                                                    int bid)
 {
+    static_assert(!(kFp8 && (kQ8 || kFused)), "FP8 pools: own format, append in its own launch");
     // Tile shape: kRG row groups of kRB row blocks (16 MFMA rows each) and kNKP = 8 / kRG
     // key parts of kKPW keys of every 128-key step, one wavefront per (row group, key part).
     static_assert((kRG == 4 && kRB == 2) || (kRG == 2 && (kRB == 2 || kRB == 1)), "tile shapes: 4 x 2, 2 x 2, 2 x 1");
@@ -1767,6 +1875,9 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     const int q8_tok = lane >> 2, q8_grp = lane & 3;
     u32x4 q8k[2], q8v[2];
     uint32_t q8ks = 0, q8vs = 0;
+    // FP8 copies in flight: the E4M3 codes of this lane's four copies (the chunks the bf16
+    // copies would move, 8 bytes each instead of 16), widened to bf16 when written to LDS
+    u32x2 f8k[4], f8v[4];
     auto stage = [&](auto sel, int s, int id) __attribute__((always_inline)) {
         const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
         if constexpr (kQ8) {
@@ -1783,6 +1894,19 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             const int so = pa::kQ8CodeBytes + 2 * (t * (kHeadDim / pa::kQ8Group) + q8_grp);
             q8ks = *reinterpret_cast<const uint16_t*>(kt + so);
             q8vs = *reinterpret_cast<const uint16_t*>(vt + so);
+            return;
+        }
+        if constexpr (kFp8) {
+            // element offsets are byte offsets in an FP8 pool; slots past kv_len read token 0
+            const int64_t base = (int64_t)id * blk_stride + kvh_off;
+            const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.k_pool) + base;
+            const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.v_pool) + base;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
+                f8k[i] = *reinterpret_cast<const u32x2*>(kb + off);
+                f8v[i] = *reinterpret_cast<const u32x2*>(vb + off);
+            }
             return;
         }
         u32x4* kd = decltype(sel)::value == 0 ? k_tile0 : k_tile1;
@@ -1880,6 +2004,17 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             float* sc = q8_sc + B * (2 * 4 * kPfKeys) + q8_grp * kPfKeys + 16 * wave + q8_tok;
             sc[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)q8ks);
             sc[4 * kPfKeys] = (float)__builtin_bit_cast(_Float16, (uint16_t)q8vs);
+        } else if constexpr (kFp8) {
+            // the widened codes go where the bf16 copies would have put them
+            constexpr int B = decltype(sel)::value;
+            u32x4* kd = B == 0 ? k_tile0 : k_tile1;
+            u32x4* vd = B == 0 ? v_tile0 : v_tile1;
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kd[(16 * wave + 4 * i) * 16 + lane] = e4m3x8_to_bf16(f8k[i]);
+                vd[(16 * wave + 4 * i) * 16 + lane] = e4m3x8_to_bf16(f8v[i]);
+            }
         }
     };
     // LDS byte offsets of this lane's operand reads within a K or V tile.  K: key
@@ -1928,7 +2063,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     };
     // The full bf16 tile runs the alternating schedule (see below); the other shapes and
     // the q8_0 pool run one step at a time.
-    constexpr bool kAlternate = !kQ8 && kRG == 4 && kRB == 2;
+    constexpr bool kAlternate = !kQ8 && !kFp8 && kRG == 4 && kRB == 2;
     int next_id = 0, cur_id = 0;
     if (nsteps > 0) {
         cur_id = checked(table_entry(step_at(0)));
@@ -2212,7 +2347,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 l += w[kp] * lk[kp];
             l += shfl_xor(l, 16);
             l += shfl_xor(l, 32);
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float inv = l > 0.f ? p.v_scale / l : 0.f;
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 f32x4 o = w[0] * oacc[rb][db] + w[1] * __builtin_bit_cast(f32x4, xo_at(1)[(rb * 8 + db) * 64 + lane]);
@@ -2436,10 +2571,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     }
     write_out(oacc, lse2);
 }
-template <bool kFused, bool kQ8, int kRG, int kRB>
+template <bool kFused, bool kQ8, int kRG, int kRB, bool kFp8 = false>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p)
 {
-    prefill_body<false, kFused, kQ8, kRG, kRB>(p, DecodeParams{}, blockIdx.x);
+    prefill_body<false, kFused, kQ8, kRG, kRB, kFp8>(p, DecodeParams{}, blockIdx.x);
 }
 
 static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
@@ -2449,14 +2584,14 @@ static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs bot
 // form), the rest are the decode workgroups.  The prefix workgroups come first in the
 // grid and wait for nothing; a (row, KV head) is finished by whichever of its decode
 // splits and prefix splits arrives last, so no workgroup ever waits for another.
-template <bool kQ8, bool kFused, int kRG, int kRB>
+template <bool kQ8, bool kFused, int kRG, int kRB, bool kFp8 = false>
 __global__ __launch_bounds__(64 * kPfWaves) void pa_cascade_decode(PrefillParams pp, DecodeParams dp,
                                                                  int32_t num_prefix_wgs)
 {
     if ((int32_t)blockIdx.x < num_prefix_wgs)
-        prefill_body<true, false, kQ8, kRG, kRB>(pp, dp, blockIdx.x);
+        prefill_body<true, false, kQ8, kRG, kRB, kFp8>(pp, dp, blockIdx.x);
     else
-        decode_body<kQ8, kFused>(dp, blockIdx.x - num_prefix_wgs);
+        decode_body<kQ8, kFused, kFp8>(dp, blockIdx.x - num_prefix_wgs);
 }
 
 
@@ -2601,6 +2736,36 @@ extern "C" pa_status pa_append_kv_q8(const pa_geometry* g, void* kv_pool_q8, con
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+extern "C" pa_status pa_append_kv_fp8(const pa_geometry* g, void* k_pool_fp8, void* v_pool_fp8, const void* k_new,
+                                      const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, float k_scale,
+                                      float v_scale, void* stream)
+{
+    if (!g)
+        return PA_ERR_NULL;
+    if (!pa::geometry_supported(g))
+        return PA_ERR_UNSUPPORTED;
+    if (n_tokens < 0 || !(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return PA_ERR_SHAPE;
+    if (n_tokens == 0)
+        return PA_OK;
+    if (!k_pool_fp8 || !v_pool_fp8 || !k_new || !v_new || !slot_mapping)
+        return PA_ERR_NULL;
+    if (validate_requested()) {
+        const pa_status st = validate_slots(g, slot_mapping, n_tokens, stream);
+        if (st != PA_OK)
+            return st;
+    }
+    const int64_t threads = (int64_t)n_tokens * g->num_kv_heads * (kHeadDim / 16);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX)
+        return PA_ERR_SHAPE;
+    hipLaunchKernelGGL(pa_append_fp8_scatter, dim3((uint32_t)blocks), dim3(256), 0, as_stream(stream),
+                       static_cast<uint8_t*>(k_pool_fp8), static_cast<uint8_t*>(v_pool_fp8),
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slot_mapping, n_tokens,
+                       g->num_kv_heads, (int64_t)g->num_blocks * kBlock, k_scale, v_scale);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 static pa_status copy_blocks(const pa_geometry* g, void* k_pool, void* v_pool, const int32_t* src_blocks,
                              const int32_t* dst_blocks, int32_t n, void* stream, int64_t head_bytes, int32_t npools)
 {
@@ -2631,6 +2796,12 @@ extern "C" pa_status pa_copy_blocks(const pa_geometry* g, void* k_pool, void* v_
     return copy_blocks(g, k_pool, v_pool, src_blocks, dst_blocks, n, stream, kBlock * kHeadDim * 2, 2);
 }
 
+extern "C" pa_status pa_copy_blocks_fp8(const pa_geometry* g, void* k_pool_fp8, void* v_pool_fp8,
+                                        const int32_t* src_blocks, const int32_t* dst_blocks, int32_t n, void* stream)
+{
+    return copy_blocks(g, k_pool_fp8, v_pool_fp8, src_blocks, dst_blocks, n, stream, kBlock * kHeadDim, 2);
+}
+
 extern "C" pa_status pa_copy_blocks_q8(const pa_geometry* g, void* kv_pool_q8, const int32_t* src_blocks,
                                        const int32_t* dst_blocks, int32_t n, void* stream)
 {
@@ -2646,10 +2817,16 @@ static void launch(void (*kernel)(Args...), uint32_t grid, hipStream_t st, Args.
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kPfWaves), 0, st, args...);
 }
 
-static void launch_prefill_tiles(bool q8, bool fused, int rows, uint32_t grid, hipStream_t st, const PrefillParams& pp)
+static void launch_prefill_tiles(bool q8, bool fused, bool fp8, int rows, uint32_t grid, hipStream_t st,
+                                 const PrefillParams& pp)
 {
     if (q8)
         launch(pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
+    else if (fp8)
+        launch(rows == 32   ? pa_prefill_tile<false, false, 2, 1, true>
+               : rows == 64 ? pa_prefill_tile<false, false, 2, 2, true>
+                            : pa_prefill_tile<false, false, 4, 2, true>,
+               grid, st, pp);
     else if (rows == 32)
         launch(fused ? pa_prefill_tile<true, false, 2, 1> : pa_prefill_tile<false, false, 2, 1>, grid, st, pp);
     else if (rows == 64)
@@ -2658,11 +2835,16 @@ static void launch_prefill_tiles(bool q8, bool fused, int rows, uint32_t grid, h
         launch(fused ? pa_prefill_tile<true, false, 4, 2> : pa_prefill_tile<false, false, 4, 2>, grid, st, pp);
 }
 
-static void launch_cascade(bool q8, bool fused, int rows, uint32_t grid, hipStream_t st, const PrefillParams& pp,
-                           const DecodeParams& dp, int32_t nprefix)
+static void launch_cascade(bool q8, bool fused, bool fp8, int rows, uint32_t grid, hipStream_t st,
+                           const PrefillParams& pp, const DecodeParams& dp, int32_t nprefix)
 {
     if (q8)
         launch(pa_cascade_decode<true, false, 4, 2>, grid, st, pp, dp, nprefix);
+    else if (fp8)
+        launch(rows == 32   ? pa_cascade_decode<false, false, 2, 1, true>
+               : rows == 64 ? pa_cascade_decode<false, false, 2, 2, true>
+                            : pa_cascade_decode<false, false, 4, 2, true>,
+               grid, st, pp, dp, nprefix);
     else if (rows == 32)
         launch(fused ? pa_cascade_decode<false, true, 2, 1> : pa_cascade_decode<false, false, 2, 1>, grid, st, pp, dp,
                nprefix);
@@ -2705,15 +2887,19 @@ static pa_status check_plan_matches(const pa_plan_t* plan, const std::vector<int
     return nd == plan->num_decode_rows && np == plan->num_prefill_rows ? PA_OK : PA_ERR_SHAPE;
 }
 
+// FP8 pools pass fp8 = true and their scales (k_scale, v_scale); other pools leave them at 1.
 static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t* plan, const void* q,
                                  const void* k_pool, const void* v_pool, const int32_t* block_tables,
                                  int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
                                  float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                                 const void* k_new = nullptr, const void* v_new = nullptr)
+                                 const void* k_new = nullptr, const void* v_new = nullptr, bool fp8 = false,
+                                 float k_scale = 1.0f, float v_scale = 1.0f)
 {
     const bool fused = k_new != nullptr;
     if (!g || !plan)
         return PA_ERR_NULL;
+    if (fp8 && (fused || !(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) || !std::isfinite(v_scale)))
+        return fused ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
     if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
         return PA_ERR_UNSUPPORTED;
     if (q8 && fused)
@@ -2786,7 +2972,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
                 return vs;
         }
     }
-    const float scale_log2 = g->scale * kLog2e;
+    const float scale_log2 = g->scale * kLog2e * (fp8 ? k_scale : 1.0f);   // an FP8 pool's K scale folds in
+    const float out_v_scale = fp8 ? v_scale : 1.0f;
     const int32_t vheads = pa::num_vheads(g->num_q_heads, g->num_kv_heads);
 
     auto prefill_params = [&]() {
@@ -2805,11 +2992,12 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         pp.num_vheads = vheads;
         pp.num_blocks = g->num_blocks;
         pp.scale_log2 = scale_log2;
+        pp.v_scale = out_v_scale;
         return pp;
     };
 
     // chunk tiles and decode rows in one launch (bf16 pool, no shared-prefix group)
-    const bool one_launch = plan->one_launch >= 1 && !q8 && ngroups == 0 && plan->prefill_tile_tokens == 32 &&
+    const bool one_launch = plan->one_launch >= 1 && !q8 && !fp8 && ngroups == 0 && plan->prefill_tile_tokens == 32 &&
                             plan->num_prefill_rows > 0 &&
                             plan->prefill_tiles > 0 && plan->num_decode_rows > 0 && plan->max_splits > 0;
     PrefillParams mixed_pp = {};
@@ -2836,6 +3024,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         pp.part_o = split ? reinterpret_cast<float*>(wsp + ws.pf_part_o) : nullptr;
         pp.part_lse = split ? reinterpret_cast<float*>(wsp + ws.pf_part_lse) : nullptr;
         pp.scale_log2 = scale_log2;
+        pp.v_scale = out_v_scale;
         for (int i = 0; i < PA_MAX_PREFILL_ROWS; ++i)
             pp.prefill_req[i] = i < plan->num_prefill_rows ? plan->prefill_req[i] : 0;
         for (int i = 0; i <= PA_MAX_PREFILL_ROWS; ++i)
@@ -2849,7 +3038,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             mixed_pp = pp;
             mixed_prefill_wgs = grid;
         } else {
-            launch_prefill_tiles(q8, fused, q8 ? 128 : kGroup * plan->prefill_tile_tokens, (uint32_t)grid, st, pp);
+            launch_prefill_tiles(q8, fused, fp8, q8 ? 128 : kGroup * plan->prefill_tile_tokens, (uint32_t)grid, st, pp);
         }
         if (!one_launch && hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
@@ -2877,6 +3066,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         dp.split_blocks = plan->split_blocks;
         dp.max_splits = plan->max_splits;
         dp.scale_log2 = scale_log2;
+        dp.v_scale = out_v_scale;
         dp.num_prefix_groups = ngroups;
         dp.prefix_splits = ngroups > 0 ? plan->prefix_splits : 0;
         for (int i = 0; i < PA_MAX_PREFIX_GROUPS; ++i) {
@@ -2904,7 +3094,7 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             const int64_t nprefix = (int64_t)ngroups * vheads * plan->prefix_splits;
             if (grid + nprefix > INT32_MAX)
                 return PA_ERR_SHAPE;
-            launch_cascade(q8, fused, q8 ? 128 : plan->prefix_tile_rows, (uint32_t)(grid + nprefix), st, pp, dp,
+            launch_cascade(q8, fused, fp8, q8 ? 128 : plan->prefix_tile_rows, (uint32_t)(grid + nprefix), st, pp, dp,
                            (int32_t)nprefix);
         } else if (one_launch) {
             if (grid + mixed_prefill_wgs > INT32_MAX)
@@ -2922,6 +3112,9 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             if (q8)
                 hipLaunchKernelGGL((pa_decode_split<true, false>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
                                    dp);
+            else if (fp8)
+                hipLaunchKernelGGL((pa_decode_split<false, false, true>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves),
+                                   0, st, dp);
             else if (fused)
                 hipLaunchKernelGGL((pa_decode_split<false, true>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
                                    dp);
@@ -2980,6 +3173,17 @@ extern "C" pa_status pa_attention_batch_q8(const pa_geometry* g, const pa_plan_t
 {
     return attention_batch(true, g, plan, q, kv_pool_q8, kv_pool_q8, block_tables, max_blocks_per_req, qo_indptr,
                            kv_len, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_attention_batch_fp8(const pa_geometry* g, const pa_plan_t* plan, const void* q,
+                                            const void* k_pool_fp8, const void* v_pool_fp8, const int32_t* block_tables,
+                                            int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                            float k_scale, float v_scale, void* stream)
+{
+    return attention_batch(false, g, plan, q, k_pool_fp8, v_pool_fp8, block_tables, max_blocks_per_req, qo_indptr,
+                           kv_len, out, lse, workspace, workspace_bytes, stream, nullptr, nullptr, true, k_scale,
+                           v_scale);
 }
 
 extern "C" pa_status pa_query_num_cus(int32_t device, int32_t* num_cus)

@@ -409,6 +409,21 @@ def config_shared_prefix_q8(seed: int = 3, num_reqs: int = 16, poison: bool = Tr
                     num_blocks=num_blocks, shared_prefix_blocks=384, poison=poison)
 
 
+def config_mixed_fp8(seed: int = 4, poison: bool = True, num_blocks: int = POOL_BLOCKS_12GIB) -> Workload:
+    """config_mixed's rows (one 512-token chunk at kv offset 4096, 31 decode rows) on FP8 pools."""
+    kv = np.concatenate([[4608], 2048 + _uniform_extra(seed, 31)]).astype(np.int32)
+    qo = np.concatenate([[512], np.ones(31, np.int32)]).astype(np.int32)
+    return build_fp8("mixed_batch_fp8", seed, 32, 8, qo_len=qo, kv_len=kv, num_blocks=num_blocks, poison=poison)
+
+
+def config_shared_prefix_fp8(seed: int = 3, num_reqs: int = 16, poison: bool = True,
+                             num_blocks: int = POOL_BLOCKS_12GIB) -> Workload:
+    """config_shared_prefix's rows (kv_len 8192 + U[0,255], 384 shared blocks) on FP8 pools."""
+    kv = 8192 + _uniform_extra(seed, num_reqs)
+    return build_fp8("shared_prefix_decode_fp8", seed, 32, 8, qo_len=np.ones(num_reqs, np.int32), kv_len=kv,
+                     num_blocks=num_blocks, shared_prefix_blocks=384, poison=poison)
+
+
 def config_sweep_decode(batch: int, layer: int, seed: int = 5, poison: bool = True,
                         num_blocks: Optional[int] = None, long_only: bool = False,
                         fill_pools: bool = True) -> Workload:

@@ -402,6 +402,22 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.pa_copy_blocks_q8(ctypes.byref(g), one, one, one, -1, None) == -2
     assert lib.pa_copy_blocks_q8(None, one, one, one, 1, None) == -1
     assert lib.pa_append_kv_q8(None, one, one, one, one, 1, None) == -1
+    # FP8 pools: the same checks, and scales that are not finite and > 0
+    f = ctypes.c_float
+    assert lib.pa_append_kv_fp8(ctypes.byref(g), None, one, one, one, one, 1, f(1), f(1), None) == -1
+    assert lib.pa_append_kv_fp8(ctypes.byref(g), one, one, one, one, one, -1, f(1), f(1), None) == -2
+    assert lib.pa_append_kv_fp8(ctypes.byref(g), one, one, one, one, one, 1, f(0), f(1), None) == -2
+    assert lib.pa_append_kv_fp8(ctypes.byref(g), one, one, one, one, one, 1, f(1), f(float("nan")), None) == -2
+    assert lib.pa_append_kv_fp8(ctypes.byref(g), None, None, None, None, None, 0, f(1), f(1), None) == 0
+    assert lib.pa_append_kv_fp8(None, one, one, one, one, one, 1, f(1), f(1), None) == -1
+    rc = lib.pa_attention_batch_fp8(ctypes.byref(g), ctypes.byref(plan), one, one, one, one, 7, one, one, one, one,
+                                    None, 0, f(-1), f(1), None)
+    assert rc == -2
+    rc = lib.pa_attention_batch_fp8(ctypes.byref(g), ctypes.byref(plan), None, None, None, None, 7, None, None, None,
+                                    None, None, 0, f(1), f(1), None)
+    assert rc == -1
+    assert lib.pa_copy_blocks_fp8(ctypes.byref(g), one, None, one, one, 1, None) == -1
+    assert lib.pa_copy_blocks_fp8(ctypes.byref(g), one, one, one, one, -1, None) == -2
     # block copy: the same checks
     rc = lib.pa_copy_blocks(ctypes.byref(pa.Geometry.make(32, 8, 10, head_dim=64)), one, one, one, one, 1, None)
     assert rc == -5

@@ -917,10 +917,10 @@ def test_spec_verify_rows():
 GQA_RATIOS = [(8, 8), (16, 8), (24, 8), (40, 8), (48, 8), (64, 8), (8, 1)]
 
 
-def _gqa(case, hq, hkv, q8=False):
-    seed = 4000 + 17 * hq + hkv + (500 if q8 else 0)
-    make = synthetic.build_q8 if q8 else synthetic.build
-    name = f"gqa{hq}x{hkv}_{case}" + ("_q8" if q8 else "")
+def _gqa(case, hq, hkv, q8=False, fp8=False):
+    seed = 4000 + 17 * hq + hkv + (500 if q8 else 0) + (900 if fp8 else 0)
+    make = synthetic.build_q8 if q8 else synthetic.build_fp8 if fp8 else synthetic.build
+    name = f"gqa{hq}x{hkv}_{case}" + ("_q8" if q8 else "") + ("_fp8" if fp8 else "")
     if case == "mixed":        # split decode rows, a one-token row, 32-token chunk tiles
         return make(name, seed, hq, hkv, qo_len=[1, 70, 1, 1, 33], kv_len=[900, 300, 17, 1, 33], num_blocks=100)
     if case == "chunks8":      # rows of at most 8 tokens: 32-row tiles
@@ -971,6 +971,157 @@ def test_gqa_ratios_q8(hq, hkv, case):
     check(wl, split_blocks=5, cascade=case == "cascade", label=f"G={hq // hkv} q8_0")
 
 
+# ------------------------------------------------------------------ FP8 pools
+
+def test_fp8_tiny_decode():
+    """Append encodes the new rows bit-exactly as the oracle does (both whole pools compared,
+    NaN-coded poison slots included); attention over the represented values within the bars."""
+    check(synthetic.config_tiny_fp8(), label="fp8")
+
+
+def test_fp8_tiny_decode_q_times_8():
+    check(synthetic.config_tiny_fp8(seed=23, q_scale=8.0), label="fp8 q*8")
+
+
+def test_fp8_qwen3_decode_step():
+    check(synthetic.config_decode_fp8(), label="fp8")
+
+
+@pytest.mark.parametrize("split", [1, 2, 7, 64])
+def test_fp8_split_sweep(split):
+    wl = synthetic.build_fp8("fp8_split", 24, 32, 8, qo_len=[1] * 6, kv_len=[1, 16, 17, 300, 1000, 2500],
+                             num_blocks=400)
+    check(wl, split_blocks=split, label=f"fp8 split {split}")
+
+
+@pytest.mark.parametrize("kv", [[1], [15], [16], [33], [4096]])
+def test_fp8_edge_lengths(kv):
+    wl = synthetic.build_fp8("fp8_edge", 25, 32, 8, qo_len=[1] * len(kv), kv_len=kv, num_blocks=300)
+    check(wl, label=f"fp8 kv {kv}")
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+@pytest.mark.parametrize("psplit", [0, 1, 3, 16])
+def test_fp8_chunk_rows(psplit, q_scale):
+    """Chunk rows on FP8 pools (128-row tiles): chunks at position 0 (2 and 129 tokens),
+    ragged tails, a 77-token chunk at 2036 spanning three 32-token tiles, decode rows beside
+    them, with the planner's or 1 / 3 / 16 key splits."""
+    wl = synthetic.build_fp8("fp8_chunks", 27, 32, 8, qo_len=[2, 31, 129, 1, 77, 16],
+                             kv_len=[2, 1000, 129, 500, 2113, 300], num_blocks=300, q_scale=q_scale)
+    check(wl, prefill_splits=psplit, label=f"fp8 chunks psplit {psplit} q*{q_scale:g}")
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(2.0 ** -8, 2.0 ** -7), (7.3, 0.0173), (1.0, 1.0)])
+def test_fp8_scales(k_scale, v_scale):
+    """Scales that make the append saturate (|x| / scale beyond 448 for most new values),
+    that make it produce subnormal codes (x / 7.3), and the unit scale, through decode,
+    split decode and chunk rows."""
+    wl = synthetic.build_fp8("fp8_scales", 28, 32, 8, qo_len=[1, 40, 1, 9], kv_len=[700, 300, 33, 1200],
+                             num_blocks=200, k_scale=k_scale, v_scale=v_scale)
+    check(wl, label=f"fp8 scales {k_scale:g}/{v_scale:g}")
+    check(wl, split_blocks=3, prefill_splits=2, label=f"fp8 scales {k_scale:g}/{v_scale:g} split")
+
+
+def test_fp8_mixed_batch():
+    """The mixed batch (512-token chunk at 4096 + 31 decode rows) on FP8 pools."""
+    check(synthetic.config_mixed_fp8(), label="fp8")
+
+
+def test_fp8_shared_prefix_cascade():
+    """The shared-prefix decode on FP8 pools through the one-launch cascade."""
+    check(synthetic.config_shared_prefix_fp8(), cascade=True, label="fp8 cascade")
+
+
+@pytest.mark.parametrize("num_cus", [8, 256])
+@pytest.mark.parametrize("q_scale", [1.0, 8.0])
+def test_fp8_cascade_groups(num_cus, q_scale):
+    """test_cascade_groups' batch (two groups split by a chunk row, a shared range ending
+    inside a step, a one-token suffix) on FP8 pools."""
+    wl = synthetic.build_fp8("fp8_cascade_groups", 73, 32, 8, qo_len=[1, 1, 1, 1, 1, 20, 1, 1, 1],
+                             kv_len=[1125, 1300, 1500, 1121, 1700, 1250, 1136, 1400, 2000], num_blocks=700,
+                             shared_prefix_blocks=70, q_scale=q_scale)
+    check(wl, cascade=True, num_cus=num_cus, label=f"fp8 cascade q*{q_scale:g}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (24, 8), (48, 8), (8, 1)])
+@pytest.mark.parametrize("case", ["mixed", "chunks8", "chunks16", "cascade"])
+def test_gqa_ratios_fp8(hq, hkv, case):
+    """FP8 pools at other grouped-query ratios: decode rows, chunk tiles of 128 / 64 / 32
+    rows, the cascade with its 32 / 64-row prefix tiles."""
+    wl = _gqa(case, hq, hkv, fp8=True)
+    check(wl, split_blocks=5, cascade=case == "cascade", label=f"G={hq // hkv} fp8")
+    if case != "cascade":
+        check(wl, prefill_splits=3, label=f"G={hq // hkv} fp8 psplit 3")
+
+
+def _represented_bf16(wl, kp8, vp8):
+    """The bf16 workload that holds what FP8 pools kp8 / vp8 (after the append) represent:
+    pools of code * scale, and new rows equal to the represented values at their slots, so
+    that its own append leaves exactly those pools."""
+    import dataclasses
+    from synthetic import f32_to_bf16_bits
+    kb = f32_to_bf16_bits((oracle.decode_e4m3(kp8) * wl.k_scale).astype(np.float32)).reshape(kp8.shape)
+    vb = f32_to_bf16_bits((oracle.decode_e4m3(vp8) * wl.v_scale).astype(np.float32)).reshape(vp8.shape)
+    blk, off = wl.slot_mapping // wl.block_size, wl.slot_mapping % wl.block_size
+    return dataclasses.replace(wl, name=wl.name + "_as_bf16", kv_format="bf16", k_pool=kb, v_pool=vb,
+                               k_new=np.ascontiguousarray(kb[blk, :, off]),
+                               v_new=np.ascontiguousarray(vb[blk, :, off]), k_scale=1.0, v_scale=1.0)
+
+
+@pytest.mark.parametrize("case", ["decode", "chunks8", "chunks16", "chunks128", "cascade"])
+def test_fp8_equals_bf16_on_represented_values_bit_exact(case):
+    """With power-of-two scales every represented value is a bf16 number and scaling by the
+    scale is exact, so the FP8 path (codes widened to bf16, K scale folded into the score
+    scale, V scale into the normalisation) must give the bf16 path's bits over pools of the
+    represented values: decode rows split and not, chunk tiles of 32 / 64 / 128 rows with
+    and without key splits, the cascade."""
+    kw = dict(num_blocks=300, k_scale=0.5, v_scale=0.125)
+    chunk_runs = [dict(), dict(prefill_splits=3, split_blocks=2)]
+    if case == "decode":
+        wl = synthetic.build_fp8("fp8_eq", 41, 32, 8, qo_len=[1] * 5, kv_len=[1, 17, 300, 1000, 2500], **kw)
+        runs = [dict(), dict(split_blocks=3)]
+    elif case == "chunks8":
+        wl = synthetic.build_fp8("fp8_eq", 42, 32, 8, qo_len=[1, 8, 5, 8], kv_len=[500, 800, 100, 8], **kw)
+        runs = chunk_runs
+    elif case == "chunks16":
+        wl = synthetic.build_fp8("fp8_eq", 43, 32, 8, qo_len=[16, 1, 11], kv_len=[700, 90, 1100], **kw)
+        runs = chunk_runs
+    elif case == "chunks128":
+        wl = synthetic.build_fp8("fp8_eq", 44, 32, 8, qo_len=[1, 100, 3, 40], kv_len=[500, 900, 3, 1300], **kw)
+        runs = chunk_runs
+    else:
+        wl = synthetic.build_fp8("fp8_eq", 45, 32, 8, qo_len=[1] * 6, kv_len=[700, 820, 990, 640, 777, 1000],
+                                 num_blocks=200, shared_prefix_blocks=30, k_scale=2.0, v_scale=0.25)
+        runs = [dict(cascade=True), dict(cascade=True, num_cus=8)]
+    for kw_run in runs:
+        print(f"[gpu] fp8 == bf16 {case} {kw_run}", flush=True)
+        kp8, vp8, out8, lse8 = _run_gpu(wl, **kw_run)
+        okp, ovp, _ = oracle.run_workload(wl)
+        assert np.array_equal(kp8, okp) and np.array_equal(vp8, ovp), "append is not bit-exact"
+        bw = _represented_bf16(wl, kp8, vp8)
+        kpb, vpb, outb, lseb = _run_gpu(bw, **kw_run)
+        assert np.array_equal(outb, out8), f"outputs differ in {np.count_nonzero(outb != out8)} places"
+        assert np.array_equal(lseb.view(np.uint32), lse8.view(np.uint32))
+
+
+def test_fp8_copy_blocks_bit_exact():
+    import torch
+    import paged_kv_attention_04_amd as pa
+    rng = np.random.default_rng(19)
+    nb, Hkv, B, D = 300, 8, 16, 128
+    kp = rng.integers(0, 256, (nb, Hkv, B, D), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nb, Hkv, B, D), dtype=np.uint8)
+    perm = rng.permutation(nb)
+    src = np.concatenate([perm[:40], [-1, 3]]).astype(np.int32)
+    dst = np.concatenate([perm[40:80], [5, nb]]).astype(np.int32)
+    g = pa.Geometry.make(32, Hkv, nb)
+    okp, ovp = oracle.copy_blocks_fp8(kp, vp, src, dst, Hkv, D, B, nb)
+    dk, dv = pa.to_device(kp), pa.to_device(vp)
+    pa.pa_copy_blocks_fp8(g, dk, dv, pa.to_device(src), pa.to_device(dst))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy(), okp) and np.array_equal(dv.cpu().numpy(), ovp)
+
+
 # ------------------------------------------------------------------ randomised batches
 
 def _random_batch(seed):
@@ -1006,3 +1157,7 @@ def test_random_batches(seed):
     q8 = synthetic.build_q8(f"random{seed}_q8", 3000 + seed, 32, 8, qo_len=list(wl.qo_len), kv_len=list(wl.kv_len),
                             num_blocks=wl.num_blocks, shared_prefix_blocks=wl.shared_prefix_blocks)
     check(q8, split_blocks=split, prefill_splits=psplit, cascade=cascade, label=f"random {seed} q8_0")
+    f8 = synthetic.build_fp8(f"random{seed}_fp8", 5000 + seed, 32, 8, qo_len=list(wl.qo_len), kv_len=list(wl.kv_len),
+                             num_blocks=wl.num_blocks, shared_prefix_blocks=wl.shared_prefix_blocks,
+                             k_scale=float(rng.choice([0.03, 0.375, 2.5])), v_scale=float(rng.choice([0.05, 0.5])))
+    check(f8, split_blocks=split, prefill_splits=psplit, cascade=cascade, label=f"random {seed} fp8")
