@@ -389,6 +389,10 @@ constexpr int kDecodeDepth = PA_DECODE_DEPTH;
 #define PA_DECODE_DEPTH_Q8 1
 #endif
 constexpr int kDecodeDepthQ8 = PA_DECODE_DEPTH_Q8;   // deeper was measured slower
+#ifndef PA_DECODE_DEPTH_FP8
+#define PA_DECODE_DEPTH_FP8 1
+#endif
+constexpr int kDecodeDepthFp8 = PA_DECODE_DEPTH_FP8;
 constexpr int kDecodeWaves = pa::kDecodeWaves;
 
 // One (block, KV head) tile is 16 tokens x 256 bytes, read by four 16-byte loads per lane.
@@ -718,7 +722,7 @@ template <bool kQ8, bool kFused, bool kFp8 = false>
 __device__ __attribute__((always_inline)) inline void decode_body(const DecodeParams& p, int bid)
 {
     static_assert(!(kFp8 && (kQ8 || kFused)), "FP8 pools: own format, append in its own launch");
-    constexpr int kDepth = kQ8 ? kDecodeDepthQ8 : kDecodeDepth;
+    constexpr int kDepth = kQ8 ? kDecodeDepthQ8 : kFp8 ? kDecodeDepthFp8 : kDecodeDepth;
     using Stage = std::conditional_t<kQ8, KvStageQ8, std::conditional_t<kFp8, KvStageFp8, KvStage>>;
     __shared__ float p_lds[kDecodeWaves][kBlock * kGroup];
     __shared__ float o_lds[kDecodeWaves][kGroup * kHeadDim];
@@ -1225,6 +1229,26 @@ __device__ inline float max3f(float a, float b, float c)
 
 static_assert(4 * kPfAcc * 4 * 64 == pa::kPrefillPartFloats, "prefill partial size differs from the workspace's");
 static_assert(4 * 2 * 64 == pa::kPrefillPartLseFloats, "prefill partial LSE size differs from the workspace's");
+
+// Cache-policy bits of a tile kernel's K / V copies: nt (2) for the 64- / 32-row chunk
+// tiles, whose copies no other workgroup reads again.
+template <bool kCascade, int kRG>
+constexpr int kPfCopyAux = (!kCascade && kRG == 2) ? 2 : 0;
+
+template <bool kCascade, int kRG>
+using PfCopy = std::integral_constant<int, kPfCopyAux<kCascade, kRG>>;
+
+// One 16-byte-per-lane LDS-DMA copy (global_load_lds_dwordx4) with cache-policy bits aux.
+using CopyDefault = std::integral_constant<int, 0>;
+using CopyStream = std::integral_constant<int, 2>;
+__device__ inline void lds_copy16(const void* src, void* lds, CopyDefault)
+{
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ inline void lds_copy16(const void* src, void* lds, CopyStream)
+{
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 2);
+}
 
 template <int N>
 struct BufSel {
@@ -1878,6 +1902,20 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     // FP8 copies in flight: the E4M3 codes of this lane's four copies (the chunks the bf16
     // copies would move, 8 bytes each instead of 16), widened to bf16 when written to LDS
     u32x2 f8k[4], f8v[4];
+    // The copies of a 64- / 32-row chunk tile (chosen only when every chunk row fits one
+    // tile, so each row's keys are read by its own workgroups and nobody else) carry the
+    // nontemporal hint, as the decode kernel's loads do: 16 rows x 8 new tokens at 8,200
+    // context took 91 against 102 us with it.  The 128-row tiles of a long chunk share
+    // every K / V step with the chunk's other query tiles through L2 and keep the default
+    // policy (with the hint the 512-token chunk at 4096 took 60 against 55 us); so do the
+    // shared-prefix tiles, read once per KV head as well, which measured slower with the
+    // hint for small groups (16 rows sharing 96 blocks: 44 against 30 us).
+    auto copy_load = [&](const auto* ptr) __attribute__((always_inline)) {
+        if constexpr (kPfCopyAux<kCascade, kRG> != 0)
+            return __builtin_nontemporal_load(ptr);
+        else
+            return *ptr;
+    };
     auto stage = [&](auto sel, int s, int id) __attribute__((always_inline)) {
         const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
         if constexpr (kQ8) {
@@ -1887,10 +1925,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                                 ((int64_t)id * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);
             const uint8_t* vt = kt + pa::kQ8TileBytes;
             const int co = t * kHeadDim + q8_grp * pa::kQ8Group;
-            q8k[0] = *reinterpret_cast<const u32x4*>(kt + co);
-            q8k[1] = *reinterpret_cast<const u32x4*>(kt + co + 16);
-            q8v[0] = *reinterpret_cast<const u32x4*>(vt + co);
-            q8v[1] = *reinterpret_cast<const u32x4*>(vt + co + 16);
+            q8k[0] = copy_load(reinterpret_cast<const u32x4*>(kt + co));
+            q8k[1] = copy_load(reinterpret_cast<const u32x4*>(kt + co + 16));
+            q8v[0] = copy_load(reinterpret_cast<const u32x4*>(vt + co));
+            q8v[1] = copy_load(reinterpret_cast<const u32x4*>(vt + co + 16));
             const int so = pa::kQ8CodeBytes + 2 * (t * (kHeadDim / pa::kQ8Group) + q8_grp);
             q8ks = *reinterpret_cast<const uint16_t*>(kt + so);
             q8vs = *reinterpret_cast<const uint16_t*>(vt + so);
@@ -1904,8 +1942,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-                f8k[i] = *reinterpret_cast<const u32x2*>(kb + off);
-                f8v[i] = *reinterpret_cast<const u32x2*>(vb + off);
+                f8k[i] = copy_load(reinterpret_cast<const u32x2*>(kb + off));
+                f8v[i] = copy_load(reinterpret_cast<const u32x2*>(vb + off));
             }
             return;
         }
@@ -1926,10 +1964,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                                         (cp_off[i] & (kHeadDim - 1));
                     const uint16_t* ks = pos >= ctx ? p.k_new + src : p.k_pool + base + off;
                     const uint16_t* vs = pos >= ctx ? p.v_new + src : p.v_pool + base + off;
-                    __builtin_amdgcn_global_load_lds(
-                        ks, (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16], 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(
-                        vs, (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16], 16, 0, 0);
+                    lds_copy16(ks, &kd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
+                    lds_copy16(vs, &vd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
                 }
                 return;
             }
@@ -1937,12 +1973,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-            __builtin_amdgcn_global_load_lds(p.k_pool + base + off,
-                                             (__attribute__((address_space(3))) void*)&kd[(16 * wave + 4 * i) * 16],
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(p.v_pool + base + off,
-                                             (__attribute__((address_space(3))) void*)&vd[(16 * wave + 4 * i) * 16],
-                                             16, 0, 0);
+            lds_copy16(p.k_pool + base + off, &kd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
+            lds_copy16(p.v_pool + base + off, &vd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
         }
     };
     // The copies of one pool (K or V) of step s into buffer `sel` of that pool, as `stage`
@@ -1963,9 +1995,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                     const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
                     const int64_t src = ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
                                         (cp_off[i] & (kHeadDim - 1));
-                    __builtin_amdgcn_global_load_lds(pos >= ctx ? fresh + src : pool + base + off,
-                                                     (__attribute__((address_space(3))) void*)&dst[(16 * wave + 4 * i) * 16],
-                                                     16, 0, 0);
+                    lds_copy16(pos >= ctx ? fresh + src : pool + base + off, &dst[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
                 }
                 return;
             }
@@ -1973,9 +2003,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-            __builtin_amdgcn_global_load_lds(pool + base + off,
-                                             (__attribute__((address_space(3))) void*)&dst[(16 * wave + 4 * i) * 16],
-                                             16, 0, 0);
+            lds_copy16(pool + base + off, &dst[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
         }
     };
     // q8_0: the copies staged one step ago into buffer pair `sel` (whose previous contents
