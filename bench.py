@@ -14,7 +14,8 @@ Each step reads a different copy of the KV pools (the copies stand for different
 layers), so no step finds the previous step's KV in the 256 MB last-level cache.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --kernel-only decode|decode_q8|mixed|mixed_fused|mixed_q8|shared|shared_q8|prefill
+    python bench.py --kernel-only decode|decode_q8|decode_fp8|mixed|mixed_fused|mixed_q8|mixed_fp8|shared|
+                                  shared_q8|shared_fp8|prefill|spec
                                                    # attention launches only, for rocprofv3
     python bench.py --summarize DIR [--title T]          # rocprofv3 CSV output -> profile text
 """
@@ -59,6 +60,8 @@ def algorithmic_bytes(wl) -> dict:
     new_tok = 2 * wl.num_kv_heads * wl.head_dim * 2          # one token's bf16 K and V rows
     if getattr(wl, "kv_format", "bf16") == "q8_0":            # codes plus a 2-byte scale per 32 values
         per_tok = 2 * wl.num_kv_heads * (wl.head_dim + 2 * (wl.head_dim // 32))
+    elif getattr(wl, "kv_format", "bf16") == "fp8":           # one E4M3 code per value
+        per_tok = 2 * wl.num_kv_heads * wl.head_dim
     else:
         per_tok = new_tok
     kv_unique = sum(slots.values()) * per_tok
@@ -125,6 +128,7 @@ class Stepper:
         self.cascade = cascade
         self.fused = fused               # decode-only batches: append fused into the attention launch
         self.q8 = getattr(wl, "kv_format", "bf16") == "q8_0"
+        self.fp8 = getattr(wl, "kv_format", "bf16") == "fp8"
         self.one_launch = one_launch     # None: the planner's choice of one or two launches
         self.plan = self.make_plan()
         self.ws = pa.workspace_for(self.plan, device)
@@ -155,11 +159,16 @@ class Stepper:
             self.plan = self.make_plan()
             if self.q8:
                 pa.pa_append_kv_q8(self.g, kp, self.kn, self.vn, self.sm)
+            elif self.fp8:
+                pa.pa_append_kv_fp8(self.g, kp, vp, self.kn, self.vn, self.sm, wl.k_scale, wl.v_scale)
             else:
                 pa.pa_append_kv(self.g, kp, vp, self.kn, self.vn, self.sm)
         if self.q8:
             pa.pa_attention_batch_q8(self.g, self.plan, self.q, kp, self.bt, self.qo_indptr, self.kv, self.out,
                                      self.lse, self.ws)
+        elif self.fp8:
+            pa.pa_attention_batch_fp8(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
+                                      self.lse, self.ws, wl.k_scale, wl.v_scale)
         else:
             pa.pa_attention_batch(self.g, self.plan, self.q, kp, vp, self.bt, self.qo_indptr, self.kv, self.out,
                                   self.lse, self.ws)
@@ -485,6 +494,9 @@ def kernel_only(which: str, reps: int):
     pa.lib()
     wl = {"decode": lambda: synthetic.config_decode(poison=False),
           "decode_q8": lambda: synthetic.config_decode_q8(poison=False),
+          "decode_fp8": lambda: synthetic.config_decode_fp8(poison=False),
+          "mixed_fp8": lambda: synthetic.config_mixed_fp8(poison=False),
+          "shared_fp8": lambda: synthetic.config_shared_prefix_fp8(poison=False),
           "mixed": lambda: synthetic.config_mixed(poison=False),
           "mixed_fused": lambda: synthetic.config_mixed(poison=False),
           "mixed_q8": lambda: synthetic.config_mixed_q8(poison=False),
@@ -492,7 +504,7 @@ def kernel_only(which: str, reps: int):
           "shared": lambda: synthetic.config_shared_prefix(poison=False),
           "prefill": prefill_only_workload,
           "spec": spec_verify_workload}[which]()
-    st = Stepper(wl, 4, cascade=which in ("shared", "shared_q8"), fused=which in ("decode", "mixed_fused"))
+    st = Stepper(wl, 4, cascade=which in ("shared", "shared_q8", "shared_fp8"), fused=which in ("decode", "mixed_fused"))
     src = torch.empty(CALIBRATION_COPY_BYTES // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)                                           # calibration: reads and writes 256 MiB
@@ -581,8 +593,8 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true", help="skip the 36-layer sweep")
     ap.add_argument("--cpu-seconds", type=float, default=0.5, help="least seconds per whole-pass CPU timing")
     ap.add_argument("--only", choices=["headline"], help="run the headline step only (for rocprofv3)")
-    ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "mixed", "mixed_fused", "mixed_q8", "shared",
-                                              "shared_q8", "prefill", "spec"])
+    ap.add_argument("--kernel-only", choices=["decode", "decode_q8", "decode_fp8", "mixed", "mixed_fused", "mixed_q8",
+                                              "mixed_fp8", "shared", "shared_q8", "shared_fp8", "prefill", "spec"])
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--summarize")
     ap.add_argument("--title", default="rocprofv3 summary")
@@ -707,6 +719,43 @@ def main(argv=None):
                                    "attention_us": round(t_sq * 1e6, 3), "prefix_splits": ssq.plan.prefix_splits}
     del ssq
 
+    # the same three on FP8 pools (E4M3 codes, per-pool scales): half the KV bytes of bf16,
+    # the codes widened to bf16 in registers (decode) or on their way into LDS (tiles)
+    wf = synthetic.config_decode_fp8(poison=False)
+    abf = algorithmic_bytes(wf)
+    sf = Stepper(wf, args.copies)
+    sec_f = time_steps(sf, args.steps, args.warmup)
+    t_f = event_time(sf, max(args.steps, 50))
+    del sf
+    fewer_f = ab["attention"] - abf["attention"]
+    predicted_f = fewer_f / (ab["attention"] / t_plain)
+    fp8 = {"workload": "qwen3_8b_decode_step on FP8 pools (OCP E4M3 codes, one K and one V scale, the bf16 "
+                       "layout), same lengths and block tables",
+           "attention_us": round(t_f * 1e6, 3), "bytes_per_launch": abf["attention"],
+           "gbs": round(abf["attention"] / t_f / 1e9, 1),
+           "frac_of_hbm_peak": round(abf["attention"] / t_f / 1e9 / HBM_PEAK_GBS, 4),
+           "step_ms": round(sec_f * 1e3, 5), "step": "pa_plan + pa_append_kv_fp8 + pa_attention_batch_fp8",
+           "bf16_attention_us": round(t_plain * 1e6, 3), "fewer_bytes": fewer_f,
+           "predicted_saving_us": round(predicted_f * 1e6, 3),
+           "measured_saving_us": round((t_plain - t_f) * 1e6, 3),
+           "implied_conversion_us": round((predicted_f - (t_plain - t_f)) * 1e6, 3)}
+    wmf = synthetic.config_mixed_fp8(poison=False)
+    smf = Stepper(wmf, args.copies)
+    sec_mf = time_steps(smf, args.steps, args.warmup)
+    t_mf = event_time(smf, max(args.steps // 2, 50))
+    del smf
+    fp8["mixed_batch"] = {"workload": "1 prefill row (512 tokens at offset 4096) + 31 decode rows on FP8 pools",
+                          "step": "pa_plan + pa_append_kv_fp8 + pa_attention_batch_fp8",
+                          "tokens_per_s": round(wmf.total_q / sec_mf, 1), "ms_per_step": round(sec_mf * 1e3, 5),
+                          "attention_launches_us": round(t_mf * 1e6, 3)}
+    wsf = synthetic.config_shared_prefix_fp8(poison=False)
+    ssf = Stepper(wsf, 2, cascade=True)
+    time_steps(ssf, 10, 5, attention_only=True)
+    t_sf = event_time(ssf, max(args.steps // 2, 50))
+    fp8["shared_prefix_cascade"] = {"workload": "the shared-prefix decode (16 rows, 384 shared blocks) on FP8 pools",
+                                    "attention_us": round(t_sf * 1e6, 3), "prefix_splits": ssf.plan.prefix_splits}
+    del ssf
+
     # speculative verification: 16 requests, 8 new tokens each at 8192 tokens of context
     # (small qo_len rows, served by the chunked-prefill path; K / V streaming dominates)
     wv = spec_verify_workload()
@@ -737,6 +786,7 @@ def main(argv=None):
                         "append_then_attention_ms_per_step": round(sec_m2 * 1e3, 5)},
         "shared_prefix": shared,
         "q8_0_decode": q8,
+        "fp8_decode": fp8,
         "spec_verify": spec,
         "prefill_chunk": {"workload": "512 new tokens at kv offset 4096, 32 q / 8 kv heads, causal",
                           "us": round(t_p * 1e6, 3), "tflops": round(pflops / t_p / 1e12, 1),
