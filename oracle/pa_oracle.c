@@ -55,7 +55,8 @@
  *              NaN, largest magnitude 448), one binary32 scale per pool (k_scale for K,
  *              v_scale for V), the bf16 pool's layout with one byte per value, and
  *                code = e4m3(y), y = x / scale in binary32, to nearest with ties to
- *                       even, magnitudes above 448 saturating to 448
+ *                       even, magnitudes above 448 (infinities too) saturating to 448,
+ *                       and a NaN stored as the NaN code 0x7F
  *                value represented = decode(code) * scale
  *              Append stores each new value this way; attention is the definition
  *              above applied to the represented values.
@@ -182,11 +183,13 @@ static double e4m3_to_double(uint8_t c)
 
 double oracle_e4m3_to_double(uint8_t c) { return e4m3_to_double(c); }
 
-/* double -> E4M3 code, to nearest with ties to even; magnitudes above 448 become 448.
- * Below 2^-6 the quantum is 2^-9 (subnormal codes 0..7; a rounded count of 8 is the
- * smallest normal, code 8); in [2^E, 2^(E+1)) it is 2^(E-3). */
+/* double -> E4M3 code, to nearest with ties to even; magnitudes above 448 become 448,
+ * a NaN becomes 0x7F.  Below 2^-6 the quantum is 2^-9 (subnormal codes 0..7; a rounded
+ * count of 8 is the smallest normal, code 8); in [2^E, 2^(E+1)) it is 2^(E-3). */
 uint8_t oracle_double_to_e4m3(double x)
 {
+    if (isnan(x))
+        return 0x7F;
     const uint8_t sign = signbit(x) ? 0x80 : 0x00;
     double a = fabs(x);
     if (a > 448.0)

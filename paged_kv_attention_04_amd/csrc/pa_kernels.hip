@@ -271,7 +271,8 @@ __global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict_
 // Append into FP8 pools (the bf16 layout, one E4M3 code per value): one thread per 16 values
 // of one (new token, KV head) row, K and V.  Each value x is stored as the E4M3 code of
 // x / scale (binary32 division), clamped to +-448 first so that the conversion, which
-// rounds to nearest with ties to even, saturates instead of producing NaN.
+// rounds to nearest with ties to even, saturates instead of producing NaN; a NaN quotient
+// is stored as the NaN code 0x7F.
 __global__ __launch_bounds__(256) void pa_append_fp8_scatter(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                              const uint16_t* __restrict__ k_new,
                                                              const uint16_t* __restrict__ v_new,
@@ -306,12 +307,18 @@ __global__ __launch_bounds__(256) void pa_append_fp8_scatter(uint8_t* __restrict
                 float y[4];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    y[2 * e] = fminf(fmaxf(bf16_lo(w[2 * j + e]) / sc, -448.0f), 448.0f);
-                    y[2 * e + 1] = fminf(fmaxf(bf16_hi(w[2 * j + e]) / sc, -448.0f), 448.0f);
+                    y[2 * e] = bf16_lo(w[2 * j + e]) / sc;
+                    y[2 * e + 1] = bf16_hi(w[2 * j + e]) / sc;
+                }
+                uint32_t nan_bytes = 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    nan_bytes |= y[e] != y[e] ? 0xFFu << (8 * e) : 0u;
+                    y[e] = fminf(fmaxf(y[e], -448.0f), 448.0f);
                 }
                 uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
                 word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
-                packed[2 * i + j] = word;
+                packed[2 * i + j] = (word & ~nan_bytes) | (0x7F7F7F7Fu & nan_bytes);
             }
         }
         *reinterpret_cast<u32x4*>((which ? v_pool : k_pool) + dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};

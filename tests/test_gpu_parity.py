@@ -1104,6 +1104,34 @@ def test_fp8_equals_bf16_on_represented_values_bit_exact(case):
         assert np.array_equal(lseb.view(np.uint32), lse8.view(np.uint32))
 
 
+def test_fp8_append_special_values_bit_exact():
+    """The append on special inputs: NaN (stored as the NaN code 0x7F), +-inf and values
+    far past 448 * scale (saturated to +-448), +-0, values in the subnormal range and
+    exact midpoints between codes (ties to even), both pools compared whole."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    from synthetic import f32_to_bf16_bits
+    rng = np.random.default_rng(23)
+    nb, Hkv, B, D, n = 40, 2, 16, 128, 37
+    kp = rng.integers(0, 256, (nb, Hkv, B, D), dtype=np.uint8)
+    vp = rng.integers(0, 256, (nb, Hkv, B, D), dtype=np.uint8)
+    special = np.array([np.nan, -np.nan, np.inf, -np.inf, 1e30, -1e30, 0.0, -0.0, 2.0**-12, -2.0**-10,
+                        3 * 2.0**-11, 2.5, 2.75, 448.0, 480.0], np.float32)
+    vals = rng.standard_normal((n, Hkv, D)).astype(np.float32) * 50.0
+    vals.reshape(-1)[rng.choice(vals.size, 800, replace=False)] = np.resize(special, 800)
+    k_new = f32_to_bf16_bits(vals)
+    v_new = f32_to_bf16_bits(vals[::-1].copy())
+    slots = rng.choice(nb * B, n, replace=False).astype(np.int32)
+    slots[3] = -1                                         # skipped
+    g = pa.Geometry.make(8, Hkv, nb)
+    for k_scale, v_scale in ((1.0, 1.0), (0.25, 3.0)):
+        okp, ovp = oracle.append_fp8(kp, vp, k_new, v_new, slots, Hkv, D, B, nb, k_scale, v_scale)
+        dk, dv = pa.to_device(kp), pa.to_device(vp)
+        pa.pa_append_kv_fp8(g, dk, dv, pa.to_device(k_new), pa.to_device(v_new), pa.to_device(slots), k_scale, v_scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(dk.cpu().numpy(), okp) and np.array_equal(dv.cpu().numpy(), ovp)
+
+
 def test_fp8_copy_blocks_bit_exact():
     import torch
     import paged_kv_attention_04_amd as pa

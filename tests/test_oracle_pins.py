@@ -638,8 +638,12 @@ def test_e4m3_encode_matches_torch_and_saturates():
     got = oracle.encode_e4m3(vals)
     want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(got, want)
-    big = oracle.encode_e4m3([464.5, 500.0, 1e6, -1e30])
-    assert list(big) == [0x7E, 0x7E, 0x7E, 0xFE]
+    big = oracle.encode_e4m3([464.5, 500.0, 1e6, -1e30, np.inf, -np.inf])
+    assert list(big) == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE]
+    # a NaN (either sign) is stored as the NaN code 0x7F, which decodes to NaN
+    nan_codes = oracle.encode_e4m3([np.nan, -np.nan, np.copysign(np.nan, -1.0)])
+    assert list(nan_codes) == [0x7F, 0x7F, 0x7F]
+    assert np.isnan(oracle.decode_e4m3(nan_codes)).all()
 
 
 def test_fp8_bytes_are_half_of_bf16():
