@@ -374,8 +374,9 @@ pa_status pa_copy_blocks_q8(const pa_geometry* geometry, void* kv_pool_q8, const
  * finite and > 0 (else PA_ERR_SHAPE).
  *
  * pa_append_kv_fp8: each new bf16 value x is stored as the code of x / scale (binary32
- * division), to nearest with ties to even, magnitudes above 448 saturating to 448.  New
- * rows must be finite.  Slot rules and errors as for pa_append_kv.
+ * division), to nearest with ties to even, magnitudes above 448 (infinities too)
+ * saturating to 448, a NaN as the NaN code 0x7F.  Slot rules and errors as for
+ * pa_append_kv.
  */
 pa_status pa_append_kv_fp8(const pa_geometry* geometry, void* k_pool_fp8, void* v_pool_fp8, const void* k_new,
                            const void* v_new, const int32_t* slot_mapping, int32_t n_tokens, float k_scale,
@@ -386,14 +387,33 @@ pa_status pa_append_kv_fp8(const pa_geometry* geometry, void* k_pool_fp8, void* 
  * chunked-prefill rows, shared-prefix groups); outputs, splits, workspace and errors as for
  * pa_attention_batch.  Every E4M3 value is a bf16 value, so the codes are widened to bf16
  * exactly and the bf16 arithmetic runs on them; k_scale multiplies the scores (folded
- * into the score scale in binary32) and v_scale each normalised output.  The append into
- * FP8 pools is always its own launch (pa_append_kv_fp8 first).
+ * into the score scale in binary32) and v_scale each normalised output.  The new rows must
+ * already be in the pools (pa_append_kv_fp8 first), or use the fused steps below.
  */
 pa_status pa_attention_batch_fp8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q,
                                  const void* k_pool_fp8, const void* v_pool_fp8, const int32_t* block_tables,
                                  int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
                                  void* out, float* lse, void* workspace, size_t workspace_bytes, float k_scale,
                                  float v_scale, void* stream);
+
+/*
+ * pa_decode_step / pa_attention_step over FP8 pools: the append of the new rows fused into
+ * the attention launches, as the bf16 steps do.  Each new value is encoded exactly as
+ * pa_append_kv_fp8 encodes it (the same binary32 quotient, saturation and NaN rule) and
+ * written to the slot of its position; the attention uses the value its code represents,
+ * so outputs, LSEs and pools are bit-identical to pa_append_kv_fp8 + pa_attention_batch_fp8.
+ * Arguments, rules and errors as for pa_decode_step / pa_attention_step, plus the scales.
+ */
+pa_status pa_decode_step_fp8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q, void* k_pool_fp8,
+                             void* v_pool_fp8, const void* k_new, const void* v_new, const int32_t* block_tables,
+                             int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
+                             float* lse, void* workspace, size_t workspace_bytes, float k_scale, float v_scale,
+                             void* stream);
+pa_status pa_attention_step_fp8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q, void* k_pool_fp8,
+                                void* v_pool_fp8, const void* k_new, const void* v_new, const int32_t* block_tables,
+                                int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes, float k_scale,
+                                float v_scale, void* stream);
 
 /* pa_copy_blocks for FP8 pools (one byte per value); same rules and errors. */
 pa_status pa_copy_blocks_fp8(const pa_geometry* geometry, void* k_pool_fp8, void* v_pool_fp8,

@@ -268,11 +268,42 @@ __global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict_
     }
 }
 
-// Append into FP8 pools (the bf16 layout, one E4M3 code per value): one thread per 16 values
-// of one (new token, KV head) row, K and V.  Each value x is stored as the E4M3 code of
-// x / scale (binary32 division), clamped to +-448 first so that the conversion, which
+// E4M3 codes of eight bf16 values x (four bf16 pairs, first value in the low half): the code
+// of x / scale (binary32 division), clamped to +-448 first so that the conversion, which
 // rounds to nearest with ties to even, saturates instead of producing NaN; a NaN quotient
-// is stored as the NaN code 0x7F.
+// becomes the NaN code 0x7F.  The append and the fused steps share it, so the codes they
+// store agree bit for bit.
+__device__ inline u32x2 e4m3x8_from_bf16(const u32x4 w, float scale)
+{
+    uint32_t out[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float y[4] = {bf16_lo(w[2 * j]) / scale, bf16_hi(w[2 * j]) / scale, bf16_lo(w[2 * j + 1]) / scale,
+                      bf16_hi(w[2 * j + 1]) / scale};
+        uint32_t nan_bytes = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            nan_bytes |= y[e] != y[e] ? 0xFFu << (8 * e) : 0u;
+            y[e] = fminf(fmaxf(y[e], -448.0f), 448.0f);
+        }
+        uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+        out[j] = (word & ~nan_bytes) | (0x7F7F7F7Fu & nan_bytes);
+    }
+    return u32x2{out[0], out[1]};
+}
+
+// Eight E4M3 codes -> eight bf16 values (four bf16 pairs, first code in the low half).
+__device__ inline u32x4 e4m3x8_to_bf16(const u32x2 w)
+{
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
+}
+
+// Append into FP8 pools (the bf16 layout, one E4M3 code per value): one thread per 16 values
+// of one (new token, KV head) row, K and V, each value stored as e4m3x8_from_bf16 encodes it.
 __global__ __launch_bounds__(256) void pa_append_fp8_scatter(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                              const uint16_t* __restrict__ k_new,
                                                              const uint16_t* __restrict__ v_new,
@@ -298,30 +329,8 @@ __global__ __launch_bounds__(256) void pa_append_fp8_scatter(uint8_t* __restrict
     for (int which = 0; which < 2; ++which) {
         const u32x4* in = reinterpret_cast<const u32x4*>((which ? v_new : k_new) + src);
         const float sc = which ? v_scale : k_scale;
-        uint32_t packed[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const u32x4 w = in[i];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float y[4];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    y[2 * e] = bf16_lo(w[2 * j + e]) / sc;
-                    y[2 * e + 1] = bf16_hi(w[2 * j + e]) / sc;
-                }
-                uint32_t nan_bytes = 0u;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    nan_bytes |= y[e] != y[e] ? 0xFFu << (8 * e) : 0u;
-                    y[e] = fminf(fmaxf(y[e], -448.0f), 448.0f);
-                }
-                uint32_t word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0u, false);
-                word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
-                packed[2 * i + j] = (word & ~nan_bytes) | (0x7F7F7F7Fu & nan_bytes);
-            }
-        }
-        *reinterpret_cast<u32x4*>((which ? v_pool : k_pool) + dst) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+        const u32x2 lo = e4m3x8_from_bf16(in[0], sc), hi = e4m3x8_from_bf16(in[1], sc);
+        *reinterpret_cast<u32x4*>((which ? v_pool : k_pool) + dst) = u32x4{lo.x, lo.y, hi.x, hi.y};
     }
 }
 
@@ -371,6 +380,7 @@ struct DecodeParams {
     int32_t max_splits;
     float scale_log2;   // score scale times log2(e): softmax runs in base 2 (times the K scale of an FP8 pool)
     float v_scale;      // FP8 pool: the V scale, applied to each normalised output (1 otherwise)
+    float k_div, v_div; // FP8 pool with the append fused: the scales new K / V values are divided by
     // shared-prefix groups: rows first .. first + count - 1 skip their first `blocks`
     // blocks, whose partial results (prefix_splits of them per row and head) an earlier
     // launch left in px_part_o / px_part_lse
@@ -447,14 +457,6 @@ __device__ inline void load_stage_fp8(KvStageFp8& s, const uint8_t* ktile, const
         s.v[i] = __builtin_nontemporal_load(vp + 64 * i);
 }
 
-// Eight E4M3 codes -> eight bf16 values (four bf16 pairs, first code in the low half).
-__device__ inline u32x4 e4m3x8_to_bf16(const u32x2 w)
-{
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
-}
 
 __device__ inline KvStage widen(const KvStageFp8& s)
 {
@@ -728,7 +730,7 @@ __device__ inline void merge_group_rows(const DecodeParams& p, const int* rows, 
 template <bool kQ8, bool kFused, bool kFp8 = false>
 __device__ __attribute__((always_inline)) inline void decode_body(const DecodeParams& p, int bid)
 {
-    static_assert(!(kFp8 && (kQ8 || kFused)), "FP8 pools: own format, append in its own launch");
+    static_assert(!(kFp8 && kQ8), "one pool format");
     constexpr int kDepth = kQ8 ? kDecodeDepthQ8 : kFp8 ? kDecodeDepthFp8 : kDecodeDepth;
     using Stage = std::conditional_t<kQ8, KvStageQ8, std::conditional_t<kFp8, KvStageFp8, KvStage>>;
     __shared__ float p_lds[kDecodeWaves][kBlock * kGroup];
@@ -821,11 +823,22 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
             kn0 = kr[c8];
             kn1 = kr[c8 + 8];
             vn = vr[c16];
+            if constexpr (kFp8) {
+                // the new row as its codes represent it (the stage holds widened codes)
+                kn0 = e4m3x8_to_bf16(e4m3x8_from_bf16(kn0, p.k_div));
+                kn1 = e4m3x8_to_bf16(e4m3x8_from_bf16(kn1, p.k_div));
+                vn = e4m3x8_to_bf16(e4m3x8_from_bf16(vn, p.v_div));
+            }
             const int phys = p.block_tables[(int64_t)r * p.max_blocks + new_blk];
             if (tid < 16 && hsl.slice == 0 && phys >= 0 && phys < p.num_blocks) {   // one slice writes
                 const int64_t row = (((int64_t)phys * p.num_kv_heads + kvh) * kBlock + new_off) * (kHeadDim / 8);
-                reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool))[row + tid] = kr[tid];
-                reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool))[row + tid] = vr[tid];
+                if constexpr (kFp8) {
+                    reinterpret_cast<u32x2*>(const_cast<uint16_t*>(p.k_pool))[row + tid] = e4m3x8_from_bf16(kr[tid], p.k_div);
+                    reinterpret_cast<u32x2*>(const_cast<uint16_t*>(p.v_pool))[row + tid] = e4m3x8_from_bf16(vr[tid], p.v_div);
+                } else {
+                    reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool))[row + tid] = kr[tid];
+                    reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool))[row + tid] = vr[tid];
+                }
             }
         }
     }
@@ -1179,6 +1192,7 @@ struct PrefillParams {
     int32_t splits;             // key splits per tile
     float scale_log2;
     float v_scale;      // FP8 pool: the V scale, applied to each normalised output (1 otherwise)
+    float k_div, v_div; // FP8 pool with the append fused: the scales new K / V values are divided by
     int32_t prefill_req[PA_MAX_PREFILL_ROWS];
     int32_t tile_start[PA_MAX_PREFILL_ROWS + 1];
     // shared-prefix mode: one tile per group, its rows (request, head) of the group's
@@ -1765,7 +1779,7 @@ template <bool kCascade, bool kFused = false, bool kQ8 = false, int kRG = 4, int
 __device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
                                                                    int bid)
 {
-    static_assert(!(kFp8 && (kQ8 || kFused)), "FP8 pools: own format, append in its own launch");
+    static_assert(!(kFp8 && kQ8), "one pool format");
     // Tile shape: kRG row groups of kRB row blocks (16 MFMA rows each) and kNKP = 8 / kRG
     // key parts of kKPW keys of every 128-key step, one wavefront per (row group, key part).
     static_assert((kRG == 4 && kRB == 2) || (kRG == 2 && (kRB == 2 || kRB == 1)), "tile shapes: 4 x 2, 2 x 2, 2 x 1");
@@ -1946,6 +1960,27 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             const int64_t base = (int64_t)id * blk_stride + kvh_off;
             const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.k_pool) + base;
             const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.v_pool) + base;
+            if constexpr (kFused) {
+                // positions from ctx on come from the new rows, encoded as the append would
+                // store them (past kv_len: the chunk's last token, so that every value is finite)
+                if (s * kPfKeys + 16 * wave + kBlock > ctx) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int pos = s * kPfKeys + 16 * wave + 4 * i + (lane >> 4);
+                        const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
+                        if (pos >= ctx) {
+                            const int64_t src = ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) *
+                                                    kHeadDim + (cp_off[i] & (kHeadDim - 1));
+                            f8k[i] = e4m3x8_from_bf16(*reinterpret_cast<const u32x4*>(p.k_new + src), p.k_div);
+                            f8v[i] = e4m3x8_from_bf16(*reinterpret_cast<const u32x4*>(p.v_new + src), p.v_div);
+                        } else {
+                            f8k[i] = *reinterpret_cast<const u32x2*>(kb + off);
+                            f8v[i] = *reinterpret_cast<const u32x2*>(vb + off);
+                        }
+                    }
+                    return;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
@@ -2350,8 +2385,15 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     bad = __syncthreads_or(bad);
     if constexpr (kFused) {
         if (new_dst >= 0) {
-            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + new_dst) = new_k;
-            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + new_dst) = new_v;
+            if constexpr (kFp8) {           // new_dst counts values: bytes of an FP8 pool
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool)) + new_dst) =
+                    e4m3x8_from_bf16(new_k, p.k_div);
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.v_pool)) + new_dst) =
+                    e4m3x8_from_bf16(new_v, p.v_div);
+            } else {
+                *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + new_dst) = new_k;
+                *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + new_dst) = new_v;
+            }
         }
     }
     const float nan = __builtin_nanf("");
@@ -2857,6 +2899,11 @@ static void launch_prefill_tiles(bool q8, bool fused, bool fp8, int rows, uint32
 {
     if (q8)
         launch(pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
+    else if (fp8 && fused)
+        launch(rows == 32   ? pa_prefill_tile<true, false, 2, 1, true>
+               : rows == 64 ? pa_prefill_tile<true, false, 2, 2, true>
+                            : pa_prefill_tile<true, false, 4, 2, true>,
+               grid, st, pp);
     else if (fp8)
         launch(rows == 32   ? pa_prefill_tile<false, false, 2, 1, true>
                : rows == 64 ? pa_prefill_tile<false, false, 2, 2, true>
@@ -2875,6 +2922,11 @@ static void launch_cascade(bool q8, bool fused, bool fp8, int rows, uint32_t gri
 {
     if (q8)
         launch(pa_cascade_decode<true, false, 4, 2>, grid, st, pp, dp, nprefix);
+    else if (fp8 && fused)
+        launch(rows == 32   ? pa_cascade_decode<false, true, 2, 1, true>
+               : rows == 64 ? pa_cascade_decode<false, true, 2, 2, true>
+                            : pa_cascade_decode<false, true, 4, 2, true>,
+               grid, st, pp, dp, nprefix);
     else if (fp8)
         launch(rows == 32   ? pa_cascade_decode<false, false, 2, 1, true>
                : rows == 64 ? pa_cascade_decode<false, false, 2, 2, true>
@@ -2933,8 +2985,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
     const bool fused = k_new != nullptr;
     if (!g || !plan)
         return PA_ERR_NULL;
-    if (fp8 && (fused || !(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) || !std::isfinite(v_scale)))
-        return fused ? PA_ERR_UNSUPPORTED : PA_ERR_SHAPE;
+    if (fp8 && (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !std::isfinite(k_scale) || !std::isfinite(v_scale)))
+        return PA_ERR_SHAPE;
     if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
         return PA_ERR_UNSUPPORTED;
     if (q8 && fused)
@@ -3028,6 +3080,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         pp.num_blocks = g->num_blocks;
         pp.scale_log2 = scale_log2;
         pp.v_scale = out_v_scale;
+        pp.k_div = k_scale;
+        pp.v_div = v_scale;
         return pp;
     };
 
@@ -3060,6 +3114,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         pp.part_lse = split ? reinterpret_cast<float*>(wsp + ws.pf_part_lse) : nullptr;
         pp.scale_log2 = scale_log2;
         pp.v_scale = out_v_scale;
+        pp.k_div = k_scale;
+        pp.v_div = v_scale;
         for (int i = 0; i < PA_MAX_PREFILL_ROWS; ++i)
             pp.prefill_req[i] = i < plan->num_prefill_rows ? plan->prefill_req[i] : 0;
         for (int i = 0; i <= PA_MAX_PREFILL_ROWS; ++i)
@@ -3102,6 +3158,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         dp.max_splits = plan->max_splits;
         dp.scale_log2 = scale_log2;
         dp.v_scale = out_v_scale;
+        dp.k_div = k_scale;
+        dp.v_div = v_scale;
         dp.num_prefix_groups = ngroups;
         dp.prefix_splits = ngroups > 0 ? plan->prefix_splits : 0;
         for (int i = 0; i < PA_MAX_PREFIX_GROUPS; ++i) {
@@ -3148,8 +3206,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
                 hipLaunchKernelGGL((pa_decode_split<true, false>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
                                    dp);
             else if (fp8)
-                hipLaunchKernelGGL((pa_decode_split<false, false, true>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves),
-                                   0, st, dp);
+                hipLaunchKernelGGL((fused ? pa_decode_split<false, true, true> : pa_decode_split<false, false, true>),
+                                   dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
             else if (fused)
                 hipLaunchKernelGGL((pa_decode_split<false, true>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
                                    dp);
@@ -3219,6 +3277,38 @@ extern "C" pa_status pa_attention_batch_fp8(const pa_geometry* g, const pa_plan_
     return attention_batch(false, g, plan, q, k_pool_fp8, v_pool_fp8, block_tables, max_blocks_per_req, qo_indptr,
                            kv_len, out, lse, workspace, workspace_bytes, stream, nullptr, nullptr, true, k_scale,
                            v_scale);
+}
+
+extern "C" pa_status pa_decode_step_fp8(const pa_geometry* g, const pa_plan_t* plan, const void* q, void* k_pool_fp8,
+                                        void* v_pool_fp8, const void* k_new, const void* v_new,
+                                        const int32_t* block_tables, int32_t max_blocks_per_req,
+                                        const int32_t* qo_indptr, const int32_t* kv_len, void* out, float* lse,
+                                        void* workspace, size_t workspace_bytes, float k_scale, float v_scale,
+                                        void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    if (plan->num_prefill_rows > 0 || plan->prefill_tiles > 0)
+        return PA_ERR_UNSUPPORTED;                 // decode rows only
+    if (plan->num_reqs > 0 && plan->total_q > 0 && (!k_new || !v_new))
+        return PA_ERR_NULL;
+    return attention_batch(false, g, plan, q, k_pool_fp8, v_pool_fp8, block_tables, max_blocks_per_req, qo_indptr,
+                           kv_len, out, lse, workspace, workspace_bytes, stream, k_new, v_new, true, k_scale, v_scale);
+}
+
+extern "C" pa_status pa_attention_step_fp8(const pa_geometry* g, const pa_plan_t* plan, const void* q,
+                                           void* k_pool_fp8, void* v_pool_fp8, const void* k_new, const void* v_new,
+                                           const int32_t* block_tables, int32_t max_blocks_per_req,
+                                           const int32_t* qo_indptr, const int32_t* kv_len, void* out, float* lse,
+                                           void* workspace, size_t workspace_bytes, float k_scale, float v_scale,
+                                           void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    if (plan->num_reqs > 0 && plan->total_q > 0 && (!k_new || !v_new))
+        return PA_ERR_NULL;
+    return attention_batch(false, g, plan, q, k_pool_fp8, v_pool_fp8, block_tables, max_blocks_per_req, qo_indptr,
+                           kv_len, out, lse, workspace, workspace_bytes, stream, k_new, v_new, true, k_scale, v_scale);
 }
 
 extern "C" pa_status pa_query_num_cus(int32_t device, int32_t* num_cus)
