@@ -360,6 +360,24 @@ pa_status pa_attention_batch_q8(const pa_geometry* geometry, const pa_plan_t* pl
                                 const int32_t* qo_indptr, const int32_t* kv_len, void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_step / pa_attention_step over a q8_0 pool: the append of the new rows fused
+ * into the attention launches.  Each new 32-value group is quantised exactly as
+ * pa_append_kv_q8 quantises it (the same scale and codes: a group's largest magnitude is
+ * gathered from the lanes that hold its pieces) and written to the slot of its position;
+ * the attention uses the stored codes and scales, so outputs, LSEs and the pool are
+ * bit-identical to pa_append_kv_q8 + pa_attention_batch_q8.  Arguments, rules and errors as
+ * for pa_decode_step / pa_attention_step, with the one q8_0 pool in place of k_pool / v_pool.
+ */
+pa_status pa_decode_step_q8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q, void* kv_pool_q8,
+                            const void* k_new, const void* v_new, const int32_t* block_tables,
+                            int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_attention_step_q8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q, void* kv_pool_q8,
+                               const void* k_new, const void* v_new, const int32_t* block_tables,
+                               int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* pa_copy_blocks for a q8_0 pool (all of a block's tiles); same rules and errors. */
 pa_status pa_copy_blocks_q8(const pa_geometry* geometry, void* kv_pool_q8, const int32_t* src_blocks,
                             const int32_t* dst_blocks, int32_t n, void* stream);

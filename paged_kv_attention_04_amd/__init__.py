@@ -92,6 +92,8 @@ def lib():
     L.pa_attention_batch_q8.argtypes = [G, PL, P, P, P, i32, P, P, P, P, P, sz, P]
     L.pa_attention_batch_noalloc.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P]
     L.pa_copy_blocks_q8.argtypes = [G, P, P, P, i32, P]
+    L.pa_decode_step_q8.argtypes = [G, PL, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
+    L.pa_attention_step_q8.argtypes = [G, PL, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
     f32 = ctypes.c_float
     L.pa_append_kv_fp8.argtypes = [G, P, P, P, P, P, i32, f32, f32, P]
     L.pa_attention_batch_fp8.argtypes = [G, PL, P, P, P, P, i32, P, P, P, P, P, sz, f32, f32, P]
@@ -113,7 +115,8 @@ def lib():
     for fn in ("pa_plan", "pa_plan_shared_prefix", "pa_plan_shared_prefix_q8", "pa_append_kv", "pa_attention_batch", "pa_validate_batch",
                "pa_validate_append", "pa_copy_blocks", "pa_validate_copy", "pa_append_kv_q8",
                "pa_attention_batch_q8", "pa_copy_blocks_q8", "pa_append_kv_fp8", "pa_attention_batch_fp8",
-               "pa_copy_blocks_fp8", "pa_decode_step_fp8", "pa_attention_step_fp8", "pa_attention_batch_noalloc", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
+               "pa_copy_blocks_fp8", "pa_decode_step_fp8", "pa_attention_step_fp8", "pa_decode_step_q8",
+               "pa_attention_step_q8", "pa_attention_batch_noalloc", "pa_query_num_cus", "pa_decode_step", "pa_allocator_create",
                "pa_allocator_alloc", "pa_allocator_retain", "pa_allocator_release", "pa_allocator_cow",
                "pa_allocator_refcount", "pa_allocator_num_free", "pa_allocator_sync"):
         getattr(L, fn).restype = ctypes.c_int
@@ -279,6 +282,33 @@ def pa_attention_batch_q8(geometry: Geometry, plan: Plan, q, kv_pool_q8, block_t
         _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"), _dev_ptr(out, bf, "out"),
         _dev_ptr(lse, (torch.float32,), "lse"), _dev_ptr(workspace, name="workspace"), ws_bytes,
         _stream_handle(stream)))
+
+
+def _step_q8(name, geometry, plan, q, kv_pool_q8, k_new, v_new, block_tables, qo_indptr, kv_len, out, lse,
+             workspace, stream):
+    import torch
+    bf, i32, u8 = _bf16_types(), (torch.int32,), (torch.uint8,)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(name, getattr(lib(), name)(
+        ctypes.byref(geometry), ctypes.byref(plan), _dev_ptr(q, bf, "q"), _dev_ptr(kv_pool_q8, u8, "kv_pool_q8"),
+        _dev_ptr(k_new, bf, "k_new"), _dev_ptr(v_new, bf, "v_new"), _dev_ptr(block_tables, i32, "block_tables"),
+        int(block_tables.shape[1]), _dev_ptr(qo_indptr, i32, "qo_indptr"), _dev_ptr(kv_len, i32, "kv_len"),
+        _dev_ptr(out, bf, "out"), _dev_ptr(lse, (torch.float32,), "lse"), _dev_ptr(workspace, name="workspace"),
+        ws_bytes, _stream_handle(stream)))
+
+
+def pa_decode_step_q8(geometry: Geometry, plan: Plan, q, kv_pool_q8, k_new, v_new, block_tables, qo_indptr, kv_len,
+                      out, lse, workspace=None, stream=None) -> None:
+    """pa_decode_step over a q8_0 pool: the new rows quantised and appended inside the launch."""
+    _step_q8("pa_decode_step_q8", geometry, plan, q, kv_pool_q8, k_new, v_new, block_tables, qo_indptr, kv_len, out,
+             lse, workspace, stream)
+
+
+def pa_attention_step_q8(geometry: Geometry, plan: Plan, q, kv_pool_q8, k_new, v_new, block_tables, qo_indptr,
+                         kv_len, out, lse, workspace=None, stream=None) -> None:
+    """pa_attention_step over a q8_0 pool: the new rows quantised and appended inside the launches."""
+    _step_q8("pa_attention_step_q8", geometry, plan, q, kv_pool_q8, k_new, v_new, block_tables, qo_indptr, kv_len,
+             out, lse, workspace, stream)
 
 
 def pa_copy_blocks_q8(geometry: Geometry, kv_pool_q8, src_blocks, dst_blocks, stream=None) -> None:

@@ -203,6 +203,54 @@ __global__ __launch_bounds__(256) void pa_append_scatter(uint16_t* __restrict__ 
     reinterpret_cast<u32x4*>(v_pool)[dst] = reinterpret_cast<const u32x4*>(v_new)[src];
 }
 
+// q8_0 quantisation shared by the append and the fused steps (so that the codes they
+// store agree bit for bit).  Scale of a 32-value group from its largest magnitude:
+// binary16(min(amax / 127, 65504)), the division in binary32 rounded to nearest; returns
+// the scale as a float and its binary16 bits in `bits`.
+__device__ inline float q8_group_scale(float amax, uint32_t& bits)
+{
+    float d = amax / 127.0f;
+    if (d > 65504.0f)
+        d = 65504.0f;
+    const _Float16 dh = (_Float16)d;
+    bits = __builtin_bit_cast(uint16_t, dh);
+    return (float)dh;
+}
+
+// Codes of four values with scale dw: rint(x / dw) clamped to +-127 (0 when dw = 0), as
+// int8 bytes, first value in the low byte.
+__device__ inline uint32_t q8_codes4(float x0, float x1, float x2, float x3, float dw)
+{
+    const float x[4] = {x0, x1, x2, x3};
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float c = 0.f;
+        if (dw != 0.f)
+            c = fminf(fmaxf(rintf(x[j] / dw), -127.f), 127.f);
+        word |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
+    }
+    return word;
+}
+
+// Largest magnitude of eight bf16 values (four pairs), from 0: the append's amax over a
+// group is the largest of these over the group's pieces.
+__device__ inline float bf16x8_amax(const u32x4 w)
+{
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+    return a;
+}
+
+// Codes of eight bf16 values (four pairs) with scale dw.
+__device__ inline u32x2 q8_codes8(const u32x4 w, float dw)
+{
+    return u32x2{q8_codes4(bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]), dw),
+                 q8_codes4(bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3]), dw)};
+}
+
 // One thread quantises one 32-value group of one (token, KV head) row, K and V: scale
 // d = binary16(min(amax / 127, 65504)), codes rint(x / d) clamped to +-127 (0 when d = 0),
 // the divisions in binary32 rounded to nearest.
@@ -228,43 +276,24 @@ __global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict_
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const u32x4* in = reinterpret_cast<const u32x4*>(which ? v_new : k_new) + src;
-        float x[pa::kQ8Group];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 w = in[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x[8 * i + 2 * j] = bf16_lo(w[j]);
-                x[8 * i + 2 * j + 1] = bf16_hi(w[j]);
-            }
-        }
+        u32x4 w[4];
         float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < pa::kQ8Group; ++i)
-            amax = fmaxf(amax, fabsf(x[i]));
-        float d = amax / 127.0f;
-        if (d > 65504.0f)
-            d = 65504.0f;
-        const _Float16 dh = (_Float16)d;
-        const float dw = (float)dh;
-        uint32_t packed[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float c = 0.f;
-                if (dw != 0.f)
-                    c = fminf(fmaxf(rintf(x[4 * i + j] / dw), -127.f), 127.f);
-                word |= ((uint32_t)(int32_t)c & 0xffu) << (8 * j);
-            }
-            packed[i] = word;
+        for (int i = 0; i < 4; ++i) {
+            w[i] = in[i];
+            amax = fmaxf(amax, bf16x8_amax(w[i]));
         }
+        uint32_t bits;
+        const float dw = q8_group_scale(amax, bits);
+        u32x2 c[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            c[i] = q8_codes8(w[i], dw);
         uint8_t* tile = kv_pool + ((blk * num_kv_heads + h) * 2 + which) * pa::kQ8TileBytes;
         u32x4* codes = reinterpret_cast<u32x4*>(tile + off * kHeadDim + grp * pa::kQ8Group);
-        codes[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
-        codes[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
-        reinterpret_cast<uint16_t*>(tile + pa::kQ8CodeBytes)[off * kGroups + grp] = __builtin_bit_cast(uint16_t, dh);
+        codes[0] = u32x4{c[0].x, c[0].y, c[1].x, c[1].y};
+        codes[1] = u32x4{c[2].x, c[2].y, c[3].x, c[3].y};
+        reinterpret_cast<uint16_t*>(tile + pa::kQ8CodeBytes)[off * kGroups + grp] = (uint16_t)bits;
     }
 }
 
@@ -816,7 +845,44 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
     // (no other workgroup of the launch reads that block).
     const int new_blk = (kvlen - 1) / kBlock, new_off = (kvlen - 1) % kBlock;
     u32x4 kn0 = u32x4{0u, 0u, 0u, 0u}, kn1 = kn0, vn = kn0;
-    if constexpr (kFused) {
+    // q8_0 pool: the new row quantised as the append quantises it -- this lane's K codes
+    // (dims 16 c8 .., group c8 / 2) and V codes (dims 8 c16 .., group c16 / 4) with their
+    // groups' scale bits; a group's largest magnitude is gathered from the lanes holding it
+    u32x4 kq = u32x4{0u, 0u, 0u, 0u};
+    u32x2 vq = u32x2{0u, 0u};
+    uint32_t kqs = 0u, vqs = 0u;
+    if constexpr (kFused && kQ8) {
+        if (new_blk >= g0 && new_blk < g_end) {
+            const u32x4* kr = reinterpret_cast<const u32x4*>(p.k_new + ((int64_t)q_row * p.num_kv_heads + kvh) * kHeadDim);
+            const u32x4* vr = reinterpret_cast<const u32x4*>(p.v_new + ((int64_t)q_row * p.num_kv_heads + kvh) * kHeadDim);
+            const u32x4 ka = kr[2 * c8], kb = kr[2 * c8 + 1], vv = vr[c16];
+            float am = fmaxf(bf16x8_amax(ka), bf16x8_amax(kb));
+            am = fmaxf(am, shfl_xor(am, 1));                    // the other half of the group
+            const float kdw = q8_group_scale(am, kqs);
+            const u32x2 k0 = q8_codes8(ka, kdw), k1 = q8_codes8(kb, kdw);
+            kq = u32x4{k0.x, k0.y, k1.x, k1.y};
+            float av = bf16x8_amax(vv);
+            av = fmaxf(av, shfl_xor(av, 1));
+            av = fmaxf(av, shfl_xor(av, 2));                    // the four lanes of the group
+            vq = q8_codes8(vv, q8_group_scale(av, vqs));
+            const int phys = p.block_tables[(int64_t)r * p.max_blocks + new_blk];
+            if (hsl.slice == 0 && phys >= 0 && phys < p.num_blocks) {   // one slice writes
+                uint8_t* kt = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool)) +
+                              ((int64_t)phys * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);
+                uint8_t* vt = kt + pa::kQ8TileBytes;
+                if (wave == 0 && t8 == 0) {
+                    *reinterpret_cast<u32x4*>(kt + new_off * kHeadDim + 16 * c8) = kq;
+                    if ((c8 & 1) == 0)
+                        reinterpret_cast<uint16_t*>(kt + pa::kQ8CodeBytes)[new_off * 4 + (c8 >> 1)] = (uint16_t)kqs;
+                }
+                if (wave == 0 && tg == 0) {
+                    *reinterpret_cast<u32x2*>(vt + new_off * kHeadDim + 8 * c16) = vq;
+                    if ((c16 & 3) == 0)
+                        reinterpret_cast<uint16_t*>(vt + pa::kQ8CodeBytes)[new_off * 4 + (c16 >> 2)] = (uint16_t)vqs;
+                }
+            }
+        }
+    } else if constexpr (kFused) {
         if (new_blk >= g0 && new_blk < g_end) {
             const u32x4* kr = reinterpret_cast<const u32x4*>(p.k_new + ((int64_t)q_row * p.num_kv_heads + kvh) * kHeadDim);
             const u32x4* vr = reinterpret_cast<const u32x4*>(p.v_new + ((int64_t)q_row * p.num_kv_heads + kvh) * kHeadDim);
@@ -891,7 +957,24 @@ __device__ __attribute__((always_inline)) inline void decode_body(const DecodePa
             else
                 return widen(st_in);                  // FP8 codes -> bf16 (exact); bf16 as is
         }();
-        if constexpr (kFused) {
+        if constexpr (kFused && kQ8) {
+            if (g0 + wave + kDecodeWaves * j == new_blk) {   // the block that holds the new token
+                if (t8 == new_off) {
+                    st.k[0] = kq;
+                    st.ks[0] = kqs;
+                }
+                if (t8 + 8 == new_off) {
+                    st.k[1] = kq;
+                    st.ks[1] = kqs;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (tg + 4 * i == new_off) {
+                        st.v[i] = vq;
+                        st.vs[i] = vqs;
+                    }
+            }
+        } else if constexpr (kFused) {
             if (g0 + wave + kDecodeWaves * j == new_blk) {   // the block that holds the new token
                 if (t8 == new_off) {
                     st.k[0] = kn0;
@@ -1940,6 +2023,40 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     auto stage = [&](auto sel, int s, int id) __attribute__((always_inline)) {
         const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
         if constexpr (kQ8) {
+            if constexpr (kFused) {
+                // positions from ctx on come from the new rows, quantised as the append
+                // quantises them (this lane's whole group; past kv_len the chunk's last token)
+                const int pos = s * kPfKeys + 16 * wave + q8_tok;
+                if (pos >= ctx) {
+                    const u32x4* kr = reinterpret_cast<const u32x4*>(
+                        p.k_new + ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
+                        q8_grp * pa::kQ8Group);
+                    const u32x4* vr = reinterpret_cast<const u32x4*>(
+                        p.v_new + ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
+                        q8_grp * pa::kQ8Group);
+                    u32x4 kw[4], vw[4];
+                    float ka = 0.f, va = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        kw[i] = kr[i];
+                        vw[i] = vr[i];
+                        ka = fmaxf(ka, bf16x8_amax(kw[i]));
+                        va = fmaxf(va, bf16x8_amax(vw[i]));
+                    }
+                    const float kdw = q8_group_scale(ka, q8ks), vdw = q8_group_scale(va, q8vs);
+                    u32x2 kc[4], vc[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        kc[i] = q8_codes8(kw[i], kdw);
+                        vc[i] = q8_codes8(vw[i], vdw);
+                    }
+                    q8k[0] = u32x4{kc[0].x, kc[0].y, kc[1].x, kc[1].y};
+                    q8k[1] = u32x4{kc[2].x, kc[2].y, kc[3].x, kc[3].y};
+                    q8v[0] = u32x4{vc[0].x, vc[0].y, vc[1].x, vc[1].y};
+                    q8v[1] = u32x4{vc[2].x, vc[2].y, vc[3].x, vc[3].y};
+                    return;
+                }
+            }
             // slots past kv_len read token 0 of the block, so that every staged value is finite
             const int t = q8_tok < valid ? q8_tok : 0;
             const uint8_t* kt = reinterpret_cast<const uint8_t*>(p.k_pool) +
@@ -2340,7 +2457,41 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     // so that their load latency hides behind it.
     u32x4 new_k = u32x4{0u, 0u, 0u, 0u}, new_v = new_k;
     int64_t new_dst = -1;
-    if constexpr (kFused) {
+    // q8_0 pool: thread (token, group) quantises one group of K and of V (as the append does)
+    u32x4 nq[4] = {};
+    uint32_t nq_ks = 0u, nq_vs = 0u;
+    int nq_at = 0;                              // token * 4 + group inside the (block, KV head) tiles
+    if constexpr (kFused && kQ8) {
+        const int tl = qt * kTileTok + (tid >> 2), grp = tid & 3;          // kTileTok tokens x 4 groups
+        if (split == 0 && hs.slice == 0 && !bad_row && (tid >> 2) < kTileTok && tl < qlen) {
+            const int pos = ctx + tl;
+            const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
+            if (phys >= 0 && phys < p.num_blocks) {
+                new_dst = ((int64_t)phys * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);   // the K tile's byte offset
+                nq_at = (pos % kBlock) * 4 + grp;
+                const int64_t src = ((int64_t)(q0 + tl) * p.num_kv_heads + kvh) * kHeadDim + grp * pa::kQ8Group;
+                const u32x4* kr = reinterpret_cast<const u32x4*>(p.k_new + src);
+                const u32x4* vr = reinterpret_cast<const u32x4*>(p.v_new + src);
+                u32x4 kw[4], vw[4];
+                float ka = 0.f, va = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kw[i] = kr[i];
+                    vw[i] = vr[i];
+                    ka = fmaxf(ka, bf16x8_amax(kw[i]));
+                    va = fmaxf(va, bf16x8_amax(vw[i]));
+                }
+                const float kdw = q8_group_scale(ka, nq_ks), vdw = q8_group_scale(va, nq_vs);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const u32x2 a0 = q8_codes8(kw[2 * i], kdw), a1 = q8_codes8(kw[2 * i + 1], kdw);
+                    const u32x2 b0 = q8_codes8(vw[2 * i], vdw), b1 = q8_codes8(vw[2 * i + 1], vdw);
+                    nq[i] = u32x4{a0.x, a0.y, a1.x, a1.y};
+                    nq[2 + i] = u32x4{b0.x, b0.y, b1.x, b1.y};
+                }
+            }
+        }
+    } else if constexpr (kFused) {
         const int tl = qt * kTileTok + (tid >> 4), c = tid & 15;          // kTileTok tokens x 16 chunks
         if (split == 0 && hs.slice == 0 && !bad_row && (tid >> 4) < kTileTok && tl < qlen) {
             const int pos = ctx + tl;
@@ -2383,7 +2534,24 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         }
     }
     bad = __syncthreads_or(bad);
-    if constexpr (kFused) {
+    if constexpr (kFused && kQ8) {
+        if (new_dst >= 0) {
+            // codes at token * 128 + 32 group, the scale at kQ8CodeBytes + 2 (token * 4 + group),
+            // in the K tile and in the V tile after it
+            uint8_t* kt = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool)) + new_dst;
+            const int tg4 = nq_at;
+            const int tok = tg4 >> 2, grp = tg4 & 3;
+            uint8_t* vt = kt + pa::kQ8TileBytes;
+            u32x4* kc = reinterpret_cast<u32x4*>(kt + tok * kHeadDim + grp * pa::kQ8Group);
+            u32x4* vc = reinterpret_cast<u32x4*>(vt + tok * kHeadDim + grp * pa::kQ8Group);
+            kc[0] = nq[0];
+            kc[1] = nq[1];
+            vc[0] = nq[2];
+            vc[1] = nq[3];
+            reinterpret_cast<uint16_t*>(kt + pa::kQ8CodeBytes)[tg4] = (uint16_t)nq_ks;
+            reinterpret_cast<uint16_t*>(vt + pa::kQ8CodeBytes)[tg4] = (uint16_t)nq_vs;
+        }
+    } else if constexpr (kFused) {
         if (new_dst >= 0) {
             if constexpr (kFp8) {           // new_dst counts values: bytes of an FP8 pool
                 *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool)) + new_dst) =
@@ -2898,7 +3066,7 @@ static void launch_prefill_tiles(bool q8, bool fused, bool fp8, int rows, uint32
                                  const PrefillParams& pp)
 {
     if (q8)
-        launch(pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
+        launch(fused ? pa_prefill_tile<true, true, 4, 2> : pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
     else if (fp8 && fused)
         launch(rows == 32   ? pa_prefill_tile<true, false, 2, 1, true>
                : rows == 64 ? pa_prefill_tile<true, false, 2, 2, true>
@@ -2921,7 +3089,8 @@ static void launch_cascade(bool q8, bool fused, bool fp8, int rows, uint32_t gri
                            const PrefillParams& pp, const DecodeParams& dp, int32_t nprefix)
 {
     if (q8)
-        launch(pa_cascade_decode<true, false, 4, 2>, grid, st, pp, dp, nprefix);
+        launch(fused ? pa_cascade_decode<true, true, 4, 2> : pa_cascade_decode<true, false, 4, 2>, grid, st, pp, dp,
+               nprefix);
     else if (fp8 && fused)
         launch(rows == 32   ? pa_cascade_decode<false, true, 2, 1, true>
                : rows == 64 ? pa_cascade_decode<false, true, 2, 2, true>
@@ -2989,8 +3158,6 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         return PA_ERR_SHAPE;
     if (!pa::geometry_supported(g) || plan->num_q_heads != g->num_q_heads || plan->num_kv_heads != g->num_kv_heads)
         return PA_ERR_UNSUPPORTED;
-    if (q8 && fused)
-        return PA_ERR_UNSUPPORTED;            // the append into a q8_0 pool is its own launch
     if (plan->num_reqs == 0 || plan->total_q == 0)
         return PA_OK;
     if (!q || !k_pool || !v_pool || !block_tables || !qo_indptr || !kv_len || !out || !lse)
@@ -3203,8 +3370,8 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             if (grid > INT32_MAX)
                 return PA_ERR_SHAPE;
             if (q8)
-                hipLaunchKernelGGL((pa_decode_split<true, false>), dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st,
-                                   dp);
+                hipLaunchKernelGGL((fused ? pa_decode_split<true, true> : pa_decode_split<true, false>),
+                                   dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
             else if (fp8)
                 hipLaunchKernelGGL((fused ? pa_decode_split<false, true, true> : pa_decode_split<false, false, true>),
                                    dim3((uint32_t)grid), dim3(64 * kDecodeWaves), 0, st, dp);
@@ -3277,6 +3444,35 @@ extern "C" pa_status pa_attention_batch_fp8(const pa_geometry* g, const pa_plan_
     return attention_batch(false, g, plan, q, k_pool_fp8, v_pool_fp8, block_tables, max_blocks_per_req, qo_indptr,
                            kv_len, out, lse, workspace, workspace_bytes, stream, nullptr, nullptr, true, k_scale,
                            v_scale);
+}
+
+extern "C" pa_status pa_decode_step_q8(const pa_geometry* g, const pa_plan_t* plan, const void* q, void* kv_pool_q8,
+                                       const void* k_new, const void* v_new, const int32_t* block_tables,
+                                       int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                       void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    if (plan->num_prefill_rows > 0 || plan->prefill_tiles > 0)
+        return PA_ERR_UNSUPPORTED;                 // decode rows only
+    if (plan->num_reqs > 0 && plan->total_q > 0 && (!k_new || !v_new))
+        return PA_ERR_NULL;
+    return attention_batch(true, g, plan, q, kv_pool_q8, kv_pool_q8, block_tables, max_blocks_per_req, qo_indptr,
+                           kv_len, out, lse, workspace, workspace_bytes, stream, k_new, v_new);
+}
+
+extern "C" pa_status pa_attention_step_q8(const pa_geometry* g, const pa_plan_t* plan, const void* q, void* kv_pool_q8,
+                                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                                          int32_t max_blocks_per_req, const int32_t* qo_indptr, const int32_t* kv_len,
+                                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                          void* stream)
+{
+    if (!g || !plan)
+        return PA_ERR_NULL;
+    if (plan->num_reqs > 0 && plan->total_q > 0 && (!k_new || !v_new))
+        return PA_ERR_NULL;
+    return attention_batch(true, g, plan, q, kv_pool_q8, kv_pool_q8, block_tables, max_blocks_per_req, qo_indptr,
+                           kv_len, out, lse, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 extern "C" pa_status pa_decode_step_fp8(const pa_geometry* g, const pa_plan_t* plan, const void* q, void* k_pool_fp8,

@@ -1194,6 +1194,66 @@ def test_fp8_fused_steps_match_append_then_attention(case):
     assert np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
 
 
+def _q8_step_gpu(wl, split_blocks=0, prefill_splits=0, cascade=False):
+    """pa_decode_step_q8 (decode-only batches) or pa_attention_step_q8 on a device copy of
+    a q8_0 workload; returns host (kv_pool, out, lse)."""
+    import torch
+    import paged_kv_attention_04_amd as pa
+    g = pa.Geometry.make(wl.num_q_heads, wl.num_kv_heads, wl.num_blocks, wl.scale)
+    plan = pa.pa_plan(g, wl.qo_len, wl.kv_len, 256, split_blocks, prefill_splits)
+    if cascade:
+        pa.pa_plan_shared_prefix(g, plan, wl.qo_len, wl.kv_len, wl.block_tables, q8=True)
+        assert plan.num_prefix_groups >= 1
+    kvp = pa.to_device(wl.kv_pool)
+    out = torch.empty((wl.total_q, wl.num_q_heads, wl.head_dim), dtype=torch.int16, device="cuda")
+    lse = torch.empty((wl.total_q, wl.num_q_heads), dtype=torch.float32, device="cuda")
+    step = pa.pa_decode_step_q8 if plan.num_prefill_rows == 0 else pa.pa_attention_step_q8
+    step(g, plan, pa.to_device(wl.q), kvp, pa.to_device(wl.k_new), pa.to_device(wl.v_new),
+         pa.to_device(wl.block_tables), pa.to_device(wl.qo_indptr), pa.to_device(wl.kv_len), out, lse,
+         pa.workspace_for(plan))
+    torch.cuda.synchronize()
+    return kvp.cpu().numpy(), out.cpu().numpy().view(np.uint16), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["tiny", "qwen3", "split7", "split1", "cascade", "mixed", "chunks", "psplit3",
+                                  "cascade_mixed", "gqa"])
+def test_q8_fused_steps_match_append_then_attention(case):
+    """The q8_0 steps with the append fused into the attention launches: the pool the
+    oracle's append gives (codes and scales, bit for bit, poisoned slots included) and the
+    same output and LSE bits as pa_append_kv_q8 followed by pa_attention_batch_q8, on
+    decode rows (split and not, the cascade) and chunk rows (key splits, a shared-prefix
+    group beside them, other query-head ratios)."""
+    split = {"split7": 7, "split1": 1}.get(case, 0)
+    psplit = 3 if case == "psplit3" else 0
+    cascade = case in ("cascade", "cascade_mixed")
+    b = synthetic.build_q8
+    wl = {"tiny": lambda: synthetic.config_tiny_q8(seed=81),
+          "qwen3": lambda: synthetic.config_decode_q8(num_reqs=12),
+          "split7": lambda: synthetic.config_tiny_q8(seed=82),
+          "split1": lambda: b("q8_fused_split1", 83, 32, 8, qo_len=[1] * 3, kv_len=[1, 17, 300], num_blocks=40),
+          "cascade": lambda: b("q8_fused_cascade", 84, 32, 8, qo_len=[1] * 5, kv_len=[700, 820, 990, 640, 777],
+                               num_blocks=400, shared_prefix_blocks=30),
+          "mixed": lambda: b("q8_fused_mixed", 85, 32, 8, qo_len=[1, 77, 1, 33], kv_len=[300, 2113, 17, 33],
+                             num_blocks=300),
+          "chunks": lambda: b("q8_fused_chunks", 86, 32, 8, qo_len=[8, 3, 1, 16, 2], kv_len=[520, 40, 100, 700, 2],
+                              num_blocks=120),
+          "psplit3": lambda: b("q8_fused_psplit", 87, 32, 8, qo_len=[1, 40, 1, 70, 2], kv_len=[300, 500, 17, 70, 33],
+                               num_blocks=200),
+          "cascade_mixed": lambda: b("q8_fused_cascade_mixed", 88, 32, 8, qo_len=[1, 1, 1, 1, 33],
+                                     kv_len=[700, 820, 990, 640, 900], num_blocks=400, shared_prefix_blocks=30),
+          "gqa": lambda: b("q8_fused_gqa", 89, 24, 8, qo_len=[1, 20, 1], kv_len=[300, 400, 50], num_blocks=80)}[case]()
+    print(f"[gpu] q8_0 fused step {case} R={wl.num_reqs} total_q={wl.total_q}", flush=True)
+    kvp, out, lse = _q8_step_gpu(wl, split, psplit, cascade)
+    okvp, _, ref = oracle.run_workload(wl, want_f64=True)
+    assert np.array_equal(kvp, okvp), "fused append is not bit-exact"
+    eo, el = _errors(out, lse, ref)
+    print(f"[gpu]   max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= TOL_O and el <= TOL_LSE
+    _, _, out2, lse2 = _run_gpu(wl, split, psplit, cascade=cascade)
+    assert np.array_equal(out, out2), f"outputs differ in {np.count_nonzero(out != out2)} places"
+    assert np.array_equal(lse.view(np.uint32), lse2.view(np.uint32))
+
+
 def test_fp8_copy_blocks_bit_exact():
     import torch
     import paged_kv_attention_04_amd as pa
