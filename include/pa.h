@@ -362,7 +362,8 @@ pa_status pa_attention_batch_q8(const pa_geometry* geometry, const pa_plan_t* pl
 
 /*
  * pa_decode_step / pa_attention_step over a q8_0 pool: the append of the new rows fused
- * into the attention launches.  Each new 32-value group is quantised exactly as
+ * into the step (into the decode launch for decode rows; chunk rows' new tokens go into the
+ * pool in a short launch before the tiles).  Each new 32-value group is quantised exactly as
  * pa_append_kv_q8 quantises it (the same scale and codes: a group's largest magnitude is
  * gathered from the lanes that hold its pieces) and written to the slot of its position;
  * the attention uses the stored codes and scales, so outputs, LSEs and the pool are
@@ -416,7 +417,8 @@ pa_status pa_attention_batch_fp8(const pa_geometry* geometry, const pa_plan_t* p
 
 /*
  * pa_decode_step / pa_attention_step over FP8 pools: the append of the new rows fused into
- * the attention launches, as the bf16 steps do.  Each new value is encoded exactly as
+ * the step (into the decode launch for decode rows; chunk rows' new tokens go into the
+ * pools in a short launch before the tiles).  Each new value is encoded exactly as
  * pa_append_kv_fp8 encodes it (the same binary32 quotient, saturation and NaN rule) and
  * written to the slot of its position; the attention uses the value its code represents,
  * so outputs, LSEs and pools are bit-identical to pa_append_kv_fp8 + pa_attention_batch_fp8.

@@ -254,28 +254,15 @@ __device__ inline u32x2 q8_codes8(const u32x4 w, float dw)
 // One thread quantises one 32-value group of one (token, KV head) row, K and V: scale
 // d = binary16(min(amax / 127, 65504)), codes rint(x / d) clamped to +-127 (0 when d = 0),
 // the divisions in binary32 rounded to nearest.
-__global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict__ kv_pool,
-                                                            const uint16_t* __restrict__ k_new,
-                                                            const uint16_t* __restrict__ v_new,
-                                                            const int32_t* __restrict__ slot_mapping,
-                                                            int32_t n_tokens, int32_t num_kv_heads, int64_t num_slots)
+// Group grp of new row src (element offset (token * Hkv + h) * head_dim) of K and of V,
+// quantised into slot off of block blk, KV head h.
+__device__ inline void q8_append_group(uint8_t* kv_pool, const uint16_t* k_new, const uint16_t* v_new, int64_t src,
+                                       int grp, int64_t blk, int off, int h, int num_kv_heads)
 {
     constexpr int kGroups = kHeadDim / pa::kQ8Group;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t per_token = (int64_t)num_kv_heads * kGroups;
-    if (idx >= (int64_t)n_tokens * per_token)
-        return;
-    const int32_t t = (int32_t)(idx / per_token);
-    const int32_t rem = (int32_t)(idx - (int64_t)t * per_token);
-    const int32_t h = rem / kGroups, grp = rem % kGroups;
-    const int32_t slot = slot_mapping[t];
-    if (slot < 0 || (int64_t)slot >= num_slots)
-        return;
-    const int64_t blk = slot / kBlock, off = slot % kBlock;
-    const int64_t src = (((int64_t)t * num_kv_heads + h) * kHeadDim + grp * pa::kQ8Group) / 8;   // 16-byte units
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-        const u32x4* in = reinterpret_cast<const u32x4*>(which ? v_new : k_new) + src;
+        const u32x4* in = reinterpret_cast<const u32x4*>((which ? v_new : k_new) + src + grp * pa::kQ8Group);
         u32x4 w[4];
         float amax = 0.f;
 #pragma unroll
@@ -295,6 +282,27 @@ __global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict_
         codes[1] = u32x4{c[2].x, c[2].y, c[3].x, c[3].y};
         reinterpret_cast<uint16_t*>(tile + pa::kQ8CodeBytes)[off * kGroups + grp] = (uint16_t)bits;
     }
+}
+
+__global__ __launch_bounds__(256) void pa_append_q8_scatter(uint8_t* __restrict__ kv_pool,
+                                                            const uint16_t* __restrict__ k_new,
+                                                            const uint16_t* __restrict__ v_new,
+                                                            const int32_t* __restrict__ slot_mapping,
+                                                            int32_t n_tokens, int32_t num_kv_heads, int64_t num_slots)
+{
+    constexpr int kGroups = kHeadDim / pa::kQ8Group;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_token = (int64_t)num_kv_heads * kGroups;
+    if (idx >= (int64_t)n_tokens * per_token)
+        return;
+    const int32_t t = (int32_t)(idx / per_token);
+    const int32_t rem = (int32_t)(idx - (int64_t)t * per_token);
+    const int32_t h = rem / kGroups, grp = rem % kGroups;
+    const int32_t slot = slot_mapping[t];
+    if (slot < 0 || (int64_t)slot >= num_slots)
+        return;
+    q8_append_group(kv_pool, k_new, v_new, ((int64_t)t * num_kv_heads + h) * kHeadDim, grp, slot / kBlock,
+                    slot % kBlock, h, num_kv_heads);
 }
 
 // E4M3 codes of eight bf16 values x (four bf16 pairs, first value in the low half): the code
@@ -333,6 +341,20 @@ __device__ inline u32x4 e4m3x8_to_bf16(const u32x2 w)
 
 // Append into FP8 pools (the bf16 layout, one E4M3 code per value): one thread per 16 values
 // of one (new token, KV head) row, K and V, each value stored as e4m3x8_from_bf16 encodes it.
+// 16 values (chunk c) of new row src (element offset (token * Hkv + h) * head_dim) of K and
+// of V, encoded into the slot row at byte offset dst (of the (block, KV head) tile's row).
+__device__ inline void fp8_append_chunk(uint8_t* k_pool, uint8_t* v_pool, const uint16_t* k_new, const uint16_t* v_new,
+                                        int64_t src, int c, int64_t dst, float k_scale, float v_scale)
+{
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const u32x4* in = reinterpret_cast<const u32x4*>((which ? v_new : k_new) + src + 16 * c);
+        const float sc = which ? v_scale : k_scale;
+        const u32x2 lo = e4m3x8_from_bf16(in[0], sc), hi = e4m3x8_from_bf16(in[1], sc);
+        *reinterpret_cast<u32x4*>((which ? v_pool : k_pool) + dst + 16 * c) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+}
+
 __global__ __launch_bounds__(256) void pa_append_fp8_scatter(uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                              const uint16_t* __restrict__ k_new,
                                                              const uint16_t* __restrict__ v_new,
@@ -352,15 +374,8 @@ __global__ __launch_bounds__(256) void pa_append_fp8_scatter(uint8_t* __restrict
     if (slot < 0 || (int64_t)slot >= num_slots)
         return;
     const int64_t blk = slot / kBlock, off = slot % kBlock;
-    const int64_t src = ((int64_t)t * num_kv_heads + h) * kHeadDim + 16 * c;                 // elements
-    const int64_t dst = ((blk * num_kv_heads + h) * kBlock + off) * kHeadDim + 16 * c;      // bytes
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const u32x4* in = reinterpret_cast<const u32x4*>((which ? v_new : k_new) + src);
-        const float sc = which ? v_scale : k_scale;
-        const u32x2 lo = e4m3x8_from_bf16(in[0], sc), hi = e4m3x8_from_bf16(in[1], sc);
-        *reinterpret_cast<u32x4*>((which ? v_pool : k_pool) + dst) = u32x4{lo.x, lo.y, hi.x, hi.y};
-    }
+    fp8_append_chunk(k_pool, v_pool, k_new, v_new, ((int64_t)t * num_kv_heads + h) * kHeadDim, c,
+                     ((blk * num_kv_heads + h) * kBlock + off) * kHeadDim, k_scale, v_scale);
 }
 
 // ------------------------------------------------------------------------------ block copy
@@ -1863,6 +1878,9 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                                                                    int bid)
 {
     static_assert(!(kFp8 && kQ8), "one pool format");
+    // Quantised pools: a step's chunk rows are encoded into the pool by a launch of their own
+    // first (encoding inside the tile raised its register spills in the step loop).
+    static_assert(!(kFused && (kQ8 || kFp8)), "quantised pools: chunk rows are appended before the tiles");
     // Tile shape: kRG row groups of kRB row blocks (16 MFMA rows each) and kNKP = 8 / kRG
     // key parts of kKPW keys of every 128-key step, one wavefront per (row group, key part).
     static_assert((kRG == 4 && kRB == 2) || (kRG == 2 && (kRB == 2 || kRB == 1)), "tile shapes: 4 x 2, 2 x 2, 2 x 1");
@@ -2023,40 +2041,6 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     auto stage = [&](auto sel, int s, int id) __attribute__((always_inline)) {
         const int valid = kvlen - (s * kPfKeys + 16 * wave);   // tokens of this block inside the row
         if constexpr (kQ8) {
-            if constexpr (kFused) {
-                // positions from ctx on come from the new rows, quantised as the append
-                // quantises them (this lane's whole group; past kv_len the chunk's last token)
-                const int pos = s * kPfKeys + 16 * wave + q8_tok;
-                if (pos >= ctx) {
-                    const u32x4* kr = reinterpret_cast<const u32x4*>(
-                        p.k_new + ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
-                        q8_grp * pa::kQ8Group);
-                    const u32x4* vr = reinterpret_cast<const u32x4*>(
-                        p.v_new + ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) * kHeadDim +
-                        q8_grp * pa::kQ8Group);
-                    u32x4 kw[4], vw[4];
-                    float ka = 0.f, va = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        kw[i] = kr[i];
-                        vw[i] = vr[i];
-                        ka = fmaxf(ka, bf16x8_amax(kw[i]));
-                        va = fmaxf(va, bf16x8_amax(vw[i]));
-                    }
-                    const float kdw = q8_group_scale(ka, q8ks), vdw = q8_group_scale(va, q8vs);
-                    u32x2 kc[4], vc[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        kc[i] = q8_codes8(kw[i], kdw);
-                        vc[i] = q8_codes8(vw[i], vdw);
-                    }
-                    q8k[0] = u32x4{kc[0].x, kc[0].y, kc[1].x, kc[1].y};
-                    q8k[1] = u32x4{kc[2].x, kc[2].y, kc[3].x, kc[3].y};
-                    q8v[0] = u32x4{vc[0].x, vc[0].y, vc[1].x, vc[1].y};
-                    q8v[1] = u32x4{vc[2].x, vc[2].y, vc[3].x, vc[3].y};
-                    return;
-                }
-            }
             // slots past kv_len read token 0 of the block, so that every staged value is finite
             const int t = q8_tok < valid ? q8_tok : 0;
             const uint8_t* kt = reinterpret_cast<const uint8_t*>(p.k_pool) +
@@ -2077,27 +2061,6 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             const int64_t base = (int64_t)id * blk_stride + kvh_off;
             const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.k_pool) + base;
             const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.v_pool) + base;
-            if constexpr (kFused) {
-                // positions from ctx on come from the new rows, encoded as the append would
-                // store them (past kv_len: the chunk's last token, so that every value is finite)
-                if (s * kPfKeys + 16 * wave + kBlock > ctx) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int pos = s * kPfKeys + 16 * wave + 4 * i + (lane >> 4);
-                        const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-                        if (pos >= ctx) {
-                            const int64_t src = ((int64_t)(q0 + min(pos, kvlen - 1) - ctx) * p.num_kv_heads + kvh) *
-                                                    kHeadDim + (cp_off[i] & (kHeadDim - 1));
-                            f8k[i] = e4m3x8_from_bf16(*reinterpret_cast<const u32x4*>(p.k_new + src), p.k_div);
-                            f8v[i] = e4m3x8_from_bf16(*reinterpret_cast<const u32x4*>(p.v_new + src), p.v_div);
-                        } else {
-                            f8k[i] = *reinterpret_cast<const u32x2*>(kb + off);
-                            f8v[i] = *reinterpret_cast<const u32x2*>(vb + off);
-                        }
-                    }
-                    return;
-                }
-            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
@@ -2457,41 +2420,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     // so that their load latency hides behind it.
     u32x4 new_k = u32x4{0u, 0u, 0u, 0u}, new_v = new_k;
     int64_t new_dst = -1;
-    // q8_0 pool: thread (token, group) quantises one group of K and of V (as the append does)
-    u32x4 nq[4] = {};
-    uint32_t nq_ks = 0u, nq_vs = 0u;
-    int nq_at = 0;                              // token * 4 + group inside the (block, KV head) tiles
-    if constexpr (kFused && kQ8) {
-        const int tl = qt * kTileTok + (tid >> 2), grp = tid & 3;          // kTileTok tokens x 4 groups
-        if (split == 0 && hs.slice == 0 && !bad_row && (tid >> 2) < kTileTok && tl < qlen) {
-            const int pos = ctx + tl;
-            const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
-            if (phys >= 0 && phys < p.num_blocks) {
-                new_dst = ((int64_t)phys * p.num_kv_heads + kvh) * (2 * pa::kQ8TileBytes);   // the K tile's byte offset
-                nq_at = (pos % kBlock) * 4 + grp;
-                const int64_t src = ((int64_t)(q0 + tl) * p.num_kv_heads + kvh) * kHeadDim + grp * pa::kQ8Group;
-                const u32x4* kr = reinterpret_cast<const u32x4*>(p.k_new + src);
-                const u32x4* vr = reinterpret_cast<const u32x4*>(p.v_new + src);
-                u32x4 kw[4], vw[4];
-                float ka = 0.f, va = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kw[i] = kr[i];
-                    vw[i] = vr[i];
-                    ka = fmaxf(ka, bf16x8_amax(kw[i]));
-                    va = fmaxf(va, bf16x8_amax(vw[i]));
-                }
-                const float kdw = q8_group_scale(ka, nq_ks), vdw = q8_group_scale(va, nq_vs);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const u32x2 a0 = q8_codes8(kw[2 * i], kdw), a1 = q8_codes8(kw[2 * i + 1], kdw);
-                    const u32x2 b0 = q8_codes8(vw[2 * i], vdw), b1 = q8_codes8(vw[2 * i + 1], vdw);
-                    nq[i] = u32x4{a0.x, a0.y, a1.x, a1.y};
-                    nq[2 + i] = u32x4{b0.x, b0.y, b1.x, b1.y};
-                }
-            }
-        }
-    } else if constexpr (kFused) {
+    if constexpr (kFused) {
         const int tl = qt * kTileTok + (tid >> 4), c = tid & 15;          // kTileTok tokens x 16 chunks
         if (split == 0 && hs.slice == 0 && !bad_row && (tid >> 4) < kTileTok && tl < qlen) {
             const int pos = ctx + tl;
@@ -2534,34 +2463,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         }
     }
     bad = __syncthreads_or(bad);
-    if constexpr (kFused && kQ8) {
+    if constexpr (kFused) {
         if (new_dst >= 0) {
-            // codes at token * 128 + 32 group, the scale at kQ8CodeBytes + 2 (token * 4 + group),
-            // in the K tile and in the V tile after it
-            uint8_t* kt = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool)) + new_dst;
-            const int tg4 = nq_at;
-            const int tok = tg4 >> 2, grp = tg4 & 3;
-            uint8_t* vt = kt + pa::kQ8TileBytes;
-            u32x4* kc = reinterpret_cast<u32x4*>(kt + tok * kHeadDim + grp * pa::kQ8Group);
-            u32x4* vc = reinterpret_cast<u32x4*>(vt + tok * kHeadDim + grp * pa::kQ8Group);
-            kc[0] = nq[0];
-            kc[1] = nq[1];
-            vc[0] = nq[2];
-            vc[1] = nq[3];
-            reinterpret_cast<uint16_t*>(kt + pa::kQ8CodeBytes)[tg4] = (uint16_t)nq_ks;
-            reinterpret_cast<uint16_t*>(vt + pa::kQ8CodeBytes)[tg4] = (uint16_t)nq_vs;
-        }
-    } else if constexpr (kFused) {
-        if (new_dst >= 0) {
-            if constexpr (kFp8) {           // new_dst counts values: bytes of an FP8 pool
-                *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool)) + new_dst) =
-                    e4m3x8_from_bf16(new_k, p.k_div);
-                *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.v_pool)) + new_dst) =
-                    e4m3x8_from_bf16(new_v, p.v_div);
-            } else {
-                *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + new_dst) = new_k;
-                *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + new_dst) = new_v;
-            }
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + new_dst) = new_k;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + new_dst) = new_v;
         }
     }
     const float nan = __builtin_nanf("");
@@ -2822,6 +2727,43 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     prefill_body<false, kFused, kQ8, kRG, kRB, kFp8>(p, DecodeParams{}, blockIdx.x);
 }
 
+// The chunk rows of a step over a quantised pool: each row's new K / V rows go into the
+// slots of positions kv_len - qo_len .. kv_len - 1 through its table, encoded exactly as
+// pa_append_q8_scatter / pa_append_fp8_scatter encode them, before the tiles read them.
+// One thread per (token, KV head, piece): a 32-value group (q8_0) or 16 values (FP8);
+// blockIdx.y is the prefill row.
+template <bool kQ8>
+__global__ __launch_bounds__(256) void pa_append_chunk_rows(PrefillParams p)
+{
+    constexpr int kPieces = kQ8 ? kHeadDim / pa::kQ8Group : kHeadDim / 16;
+    const int r = p.prefill_req[blockIdx.y];
+    const int q0 = p.qo_indptr[r];
+    const int qlen = p.qo_indptr[r + 1] - q0;
+    const int kvlen = p.kv_len[r];
+    const int ctx = kvlen - qlen;
+    const int64_t per_token = (int64_t)p.num_kv_heads * kPieces;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (qlen < 1 || ctx < 0 || idx >= (int64_t)qlen * per_token)
+        return;
+    const int t = (int)(idx / per_token);
+    const int rem = (int)(idx - (int64_t)t * per_token);
+    const int h = rem / kPieces, c = rem % kPieces;
+    const int pos = ctx + t;
+    if (pos / kBlock >= p.max_blocks)
+        return;
+    const int phys = p.block_tables[(int64_t)r * p.max_blocks + pos / kBlock];
+    if (phys < 0 || phys >= p.num_blocks)
+        return;
+    const int64_t src = ((int64_t)(q0 + t) * p.num_kv_heads + h) * kHeadDim;
+    uint8_t* kpool = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool));
+    uint8_t* vpool = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.v_pool));
+    if constexpr (kQ8)
+        q8_append_group(kpool, p.k_new, p.v_new, src, c, phys, pos % kBlock, h, p.num_kv_heads);
+    else
+        fp8_append_chunk(kpool, vpool, p.k_new, p.v_new, src, c,
+                         (((int64_t)phys * p.num_kv_heads + h) * kBlock + pos % kBlock) * kHeadDim, p.k_div, p.v_div);
+}
+
 static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
 
 // A batch with shared-prefix groups in one launch: workgroups 0 .. num_prefix_wgs - 1 read
@@ -3066,12 +3008,7 @@ static void launch_prefill_tiles(bool q8, bool fused, bool fp8, int rows, uint32
                                  const PrefillParams& pp)
 {
     if (q8)
-        launch(fused ? pa_prefill_tile<true, true, 4, 2> : pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
-    else if (fp8 && fused)
-        launch(rows == 32   ? pa_prefill_tile<true, false, 2, 1, true>
-               : rows == 64 ? pa_prefill_tile<true, false, 2, 2, true>
-                            : pa_prefill_tile<true, false, 4, 2, true>,
-               grid, st, pp);
+        launch(pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
     else if (fp8)
         launch(rows == 32   ? pa_prefill_tile<false, false, 2, 1, true>
                : rows == 64 ? pa_prefill_tile<false, false, 2, 2, true>
@@ -3296,7 +3233,25 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             mixed_pp = pp;
             mixed_prefill_wgs = grid;
         } else {
-            launch_prefill_tiles(q8, fused, fp8, q8 ? 128 : kGroup * plan->prefill_tile_tokens, (uint32_t)grid, st, pp);
+            if (fused && (q8 || fp8)) {
+                // quantised pools: the chunk rows' new tokens are encoded into the pool first,
+                // then the tiles read them there (the decode rows keep the fused append)
+                int32_t most_tiles = 0;
+                for (int i = 0; i < plan->num_prefill_rows; ++i)
+                    most_tiles = std::max(most_tiles, plan->prefill_tile_start[i + 1] - plan->prefill_tile_start[i]);
+                const int64_t pieces = (int64_t)most_tiles * plan->prefill_tile_tokens * g->num_kv_heads *
+                                       (q8 ? kHeadDim / pa::kQ8Group : kHeadDim / 16);
+                const int64_t bx = (pieces + 255) / 256;
+                if (bx > INT32_MAX)
+                    return PA_ERR_SHAPE;
+                const dim3 agrid((uint32_t)std::max<int64_t>(bx, 1), (uint32_t)plan->num_prefill_rows);
+                if (q8)
+                    hipLaunchKernelGGL(pa_append_chunk_rows<true>, agrid, dim3(256), 0, st, pp);
+                else
+                    hipLaunchKernelGGL(pa_append_chunk_rows<false>, agrid, dim3(256), 0, st, pp);
+            }
+            launch_prefill_tiles(q8, fused && !(q8 || fp8), fp8, q8 ? 128 : kGroup * plan->prefill_tile_tokens,
+                                 (uint32_t)grid, st, pp);
         }
         if (!one_launch && hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
