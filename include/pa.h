@@ -344,16 +344,17 @@ pa_status pa_append_kv_q8(const pa_geometry* geometry, void* kv_pool_q8, const v
  * are the codes times their scales, and everything else (outputs, splits, workspace) is
  * as for pa_attention_batch.  Q is converted to binary16 toward zero (exact for bf16
  * values of magnitude in [2^-14, 65504]; larger ones saturate at 65504).  Every path
- * takes the codes as exact binary16 integers and applies the K scales to the scores in
- * binary32; each V scale d is folded into its token's softmax weight p (p <= 2^8, as the
- * running maximum is raised lazily), and the product p * d is rounded to binary16
- * (toward zero on decode rows, to nearest on chunk rows and prefix groups).  Limits that
- * follow: (1) a V group with scale d below 2^-14 (largest |value| below about 0.008)
- * gives weights in binary16's subnormal range, so the output's relative error grows
- * as the V values shrink (about 0.4% of |O| at |V| ~ 1e-3, several percent at 1e-4);
- * (2) p * d must stay below 65504, which holds for d <= 255 (largest |V| <= 32,000).
- * K scales have no such limit.  The append into a q8_0 pool is always its own launch
- * (pa_append_kv_q8 first).
+ * takes the K codes as exact binary16 integers and applies the K scales to the scores in
+ * binary32.  V: on decode rows each V scale d is folded into its token's softmax weight p
+ * (p <= 2^8, as the running maximum is raised lazily) and p * d is rounded to binary16
+ * toward zero; on chunk rows and prefix groups each V value code * d is rounded to
+ * binary16 (nearest) and the weights p to binary16 (nearest).  Limits that follow: (1) a
+ * V group with scale d below 2^-14 (largest |value| below about 0.008) gives decode
+ * weights, or chunk-row values, in binary16's subnormal range, so the output's relative
+ * error grows as the V values shrink (about 0.4% of |O| at |V| ~ 1e-3, several percent at
+ * 1e-4); (2) p * d and code * d must stay below 65504, which holds for d <= 255 (largest
+ * |V| <= 32,000).  K scales have no such limit.  The new rows must already be in the pool
+ * (pa_append_kv_q8 first), or use the fused steps below.
  */
 pa_status pa_attention_batch_q8(const pa_geometry* geometry, const pa_plan_t* plan, const void* q,
                                 const void* kv_pool_q8, const int32_t* block_tables, int32_t max_blocks_per_req,

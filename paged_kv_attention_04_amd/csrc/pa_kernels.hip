@@ -1737,18 +1737,18 @@ __device__ __forceinline__ f32x4 mfma_f16(const bf16x8& a, const bf16x8& b, cons
                                                   0);
 }
 
-// pf_step over a q8_0 pool.  The staged K and V tiles hold the codes as binary16 integers
-// (exact), Q is binary16, and the scales of the step's keys sit in LDS as floats,
-// [group][key] (ksc for K, vsc for V).  S^T is formed one 32-dim group (one k-slice of
-// the product) at a time: the group's codes times Q, exact products summed in fp32,
-// then weighted by each key's scale of that group, so the scores carry no rounding of
-// the stored values.  In PV the weights of the output dims of group g are the softmax
-// weights times the keys' V scales of group g, rounded to binary16.  The softmax
-// statistics are those of pf_step (same lazy rescaling; the denominators are summed
-// from the unrounded weights).
+// pf_step over a q8_0 pool.  The staged K tile holds the codes as binary16 integers
+// (exact), the staged V tile the values code x scale rounded to binary16, Q is binary16,
+// and the K scales of the step's keys sit in LDS as floats, [group][key] (ksc).  S^T is
+// formed one 32-dim group (one k-slice of the product) at a time: the group's codes times
+// Q, exact products summed in fp32, then weighted by each key's scale of that group, so
+// the scores carry no rounding of the stored values.  PV takes the softmax weights rounded
+// to binary16 against the staged V values, as the bf16 tile takes them in bf16.  The
+// softmax statistics are those of pf_step (same lazy rescaling; the denominators are
+// summed from the unrounded weights).
 template <bool kMask>
 __device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char* vt, const int (&v_addr)[8],
-                                           const float* ksc, const float* vsc, const bf16x8 (&qop)[2][4],
+                                           const float* ksc, const bf16x8 (&qop)[2][4],
                                            f32x4 (&oacc)[2][8], float (&m)[2], float (&lsum)[2], int key0, int kh,
                                            int kslice, const int (&qpos)[2], int kv_hi, float scale_log2)
 {
@@ -1816,31 +1816,21 @@ __device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char
         bf16x8 vop[8];
         pf_read_v(vt, v_addr, c, vop);
         // this lane's keys of chunk c: 32 c + 4 kslice + 0..3, then 32 c + 16 + 4 kslice + 0..3
-        float pe[2][8];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
+            float pe[8];
             float sum = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                pe[rb][i] = fast_exp2(fmaf(x[rb][8 * c + i], scale_log2, nm[rb]));
-                sum += pe[rb][i];
+                pe[i] = fast_exp2(fmaf(x[rb][8 * c + i], scale_log2, nm[rb]));
+                sum += pe[i];
             }
             lsum[rb] += sum;
-        }
+            const bf16x8 pg = __builtin_bit_cast(bf16x8, u32x4{pack_f16(pe[0], pe[1]), pack_f16(pe[2], pe[3]),
+                                                               pack_f16(pe[4], pe[5]), pack_f16(pe[6], pe[7])});
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float* vs = vsc + g * kPfKeys + 64 * kh + 32 * c + 4 * kslice;
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(vs);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(vs + 16);
-            const float dv[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const bf16x8 pg = __builtin_bit_cast(
-                    bf16x8, u32x4{pack_f16(pe[rb][0] * dv[0], pe[rb][1] * dv[1]), pack_f16(pe[rb][2] * dv[2], pe[rb][3] * dv[3]),
-                                  pack_f16(pe[rb][4] * dv[4], pe[rb][5] * dv[5]), pack_f16(pe[rb][6] * dv[6], pe[rb][7] * dv[7])});
-                oacc[rb][2 * g] = mfma_f16(vop[2 * g], pg, oacc[rb][2 * g]);
-                oacc[rb][2 * g + 1] = mfma_f16(vop[2 * g + 1], pg, oacc[rb][2 * g + 1]);
-            }
+            for (int db = 0; db < 8; ++db)
+                oacc[rb][db] = mfma_f16(vop[db], pg, oacc[rb][db]);
         }
     }
 }
@@ -1869,10 +1859,11 @@ __device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char
 //
 // q8_0 pool (kQ8): the copies go through registers instead.  Lane l of wavefront w loads
 // the 32 codes and the scale of group l % 4 of token l / 4 of its block (K and V) when the
-// step is staged; right before the next barrier it writes the codes as binary16 integers
-// (exact) to the same LDS places the bf16 copies use and the two scales as floats to a
-// [group][key] table beside the tiles.  The products then run on binary16 operands (Q
-// converted once, exact for bf16 values inside the binary16 range), see pf_step_q8.
+// step is staged; right before the next barrier it writes the K codes as binary16 integers
+// (exact) and the V values code x scale rounded to binary16 to the same LDS places the
+// bf16 copies use, and the K scale as a float to a [group][key] table beside the tiles.
+// The products then run on binary16 operands (Q converted once, exact for bf16 values
+// inside the binary16 range), see pf_step_q8.
 template <bool kCascade, bool kFused = false, bool kQ8 = false, int kRG = 4, int kRB = 2, bool kFp8 = false>
 __device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
                                                                    int bid)
@@ -1895,8 +1886,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     __shared__ __attribute__((aligned(1024))) u32x4 k_tile1[kTileChunks];
     __shared__ __attribute__((aligned(1024))) u32x4 v_tile1[kTileChunks];
     __shared__ int last_lds;
-    // q8_0: scales of the staged keys, [buffer pair][K, V][group][key]
-    __shared__ __attribute__((aligned(16))) float q8_sc[kQ8 ? 2 * 2 * 4 * kPfKeys : 4];
+    // q8_0: K scales of the staged keys, [buffer pair][group][key]
+    __shared__ __attribute__((aligned(16))) float q8_sc[kQ8 ? 2 * 4 * kPfKeys : 4];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -2142,6 +2133,12 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 const uint32_t c = q8_to_half2(w, w, i ? 0x0c030c02u : 0x0c010c00u);
                 return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, c) - bias);
             };
+            // V values: code x scale, one binary16 product rounded to nearest
+            const _Float16 dvh = __builtin_bit_cast(_Float16, (uint16_t)q8vs);
+            const f16x2 dv2 = {dvh, dvh};
+            auto value2 = [&](uint32_t w, int i) __attribute__((always_inline)) {
+                return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, code2(w, i)) * dv2);
+            };
             const int row = (16 * wave + q8_tok) * 16;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {                  // chunk 4 q8_grp + j: dims 8 j .. 8 j + 7 of the group
@@ -2149,11 +2146,10 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 const uint32_t v0 = q8v[j >> 1][2 * (j & 1)], v1 = q8v[j >> 1][2 * (j & 1) + 1];
                 const int slot = (4 * q8_grp + j) ^ pf_swz(q8_tok);
                 kd[row + slot] = u32x4{code2(k0, 0), code2(k0, 1), code2(k1, 0), code2(k1, 1)};
-                vd[row + slot] = u32x4{code2(v0, 0), code2(v0, 1), code2(v1, 0), code2(v1, 1)};
+                vd[row + slot] = u32x4{value2(v0, 0), value2(v0, 1), value2(v1, 0), value2(v1, 1)};
             }
-            float* sc = q8_sc + B * (2 * 4 * kPfKeys) + q8_grp * kPfKeys + 16 * wave + q8_tok;
+            float* sc = q8_sc + B * (4 * kPfKeys) + q8_grp * kPfKeys + 16 * wave + q8_tok;
             sc[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)q8ks);
-            sc[4 * kPfKeys] = (float)__builtin_bit_cast(_Float16, (uint16_t)q8vs);
         } else if constexpr (kFp8) {
             // the widened codes go where the bf16 copies would have put them
             constexpr int B = decltype(sel)::value;
@@ -2260,8 +2256,8 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             next_id = table_entry(step_at(it + 2));
         }
         if constexpr (kQ8) {
-            const float* ksc = q8_sc + B * (2 * 4 * kPfKeys);
-            pf_step_q8<decltype(msk)::value>(kop, vt, v_addr, ksc, ksc + 4 * kPfKeys, qop, oacc, m, lsum,
+            const float* ksc = q8_sc + B * (4 * kPfKeys);
+            pf_step_q8<decltype(msk)::value>(kop, vt, v_addr, ksc, qop, oacc, m, lsum,
                                              s * kPfKeys + 64 * kh, kh, kslice, qpos, kv_hi, p.scale_log2);
         } else {
             pf_step<kRB, kKB, decltype(msk)::value>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + kKPW * kh,
