@@ -418,6 +418,26 @@ def test_entry_points_reject_bad_arguments_before_launch(lib):
     assert rc == -1
     assert lib.pa_copy_blocks_fp8(ctypes.byref(g), one, None, one, one, 1, None) == -1
     assert lib.pa_copy_blocks_fp8(ctypes.byref(g), one, one, one, one, -1, None) == -2
+    # the fused steps (bf16, q8_0, FP8): NULL geometry or plan, missing new rows, a decode
+    # step given chunk rows, bad FP8 scales -- all before anything is launched
+    chunk = pa.pa_plan(g, [1, 5], [100, 40])
+    for name, q8, fp8 in (("pa_decode_step", False, False), ("pa_attention_step", False, False),
+                          ("pa_decode_step_q8", True, False), ("pa_attention_step_q8", True, False),
+                          ("pa_decode_step_fp8", False, True), ("pa_attention_step_fp8", False, True)):
+        fn = getattr(lib, name)
+        pools = (one,) if q8 else (one, one)
+        scales = (f(1), f(1)) if fp8 else ()
+
+        def call(geo, pl, k_new, v_new, scales=scales):
+            return fn(geo, pl, one, *pools, k_new, v_new, one, 7, one, one, one, one, None, 0, *scales, None)
+        assert call(None, ctypes.byref(plan), one, one) == -1, name
+        assert call(ctypes.byref(g), None, one, one) == -1, name
+        assert call(ctypes.byref(g), ctypes.byref(plan), None, one) == -1, name
+        if "decode" in name:
+            assert call(ctypes.byref(g), ctypes.byref(chunk), one, one) == -5, name
+        if fp8:
+            assert call(ctypes.byref(g), ctypes.byref(plan), one, one, (f(0), f(1))) == -2, name
+            assert call(ctypes.byref(g), ctypes.byref(plan), one, one, (f(1), f(float("inf")))) == -2, name
     # block copy: the same checks
     rc = lib.pa_copy_blocks(ctypes.byref(pa.Geometry.make(32, 8, 10, head_dim=64)), one, one, one, one, 1, None)
     assert rc == -5
