@@ -1406,6 +1406,45 @@ __device__ __forceinline__ void pf_read_v(const char* vt, const int (&v_addr)[8]
     }
 }
 
+// FP8 tiles keep the codes in LDS: one 128-byte row per key, its eight 16-byte units
+// permuted by pf_swz8(key), a bijection of the unit index that changes with key bits 1..4
+// and not with key + 32 (so a 32-key chunk's read offsets hold for every chunk).  The K
+// operand reads (16 keys of one unit) and the transposed V reads (eight keys, two units)
+// then hit distinct banks.
+__device__ inline int pf_swz8(int key) { return ((key >> 1) & 7) ^ ((key >> 4) & 1); }
+
+// Transposed 8-bit LDS read: within each group of 16 lanes, if lane m points at eight
+// consecutive bytes (row m of a 16 x 8 byte tile), lane i receives byte i % 8 of rows
+// 2 j + i / 8, j = 0..7 (measured on the chip with an in-bounds probe).
+__device__ inline u32x2 lds_read_tr8(const void* p)
+{
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(const_cast<void*>(p)));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// FP8 tile: the transposed V operand of 32-key chunk c as bf16 (the codes widened exactly).
+// v_addr[db] points lane (kslice, m) at key 4 kslice + m / 2 (m / 2 < 4) or
+// 16 + 4 kslice + m / 2 - 4 of the chunk, dims 16 db + 8 (m % 2) .. +8, so lane
+// (kslice, i) receives dim 16 db + i of the same eight keys the bf16 operand holds; a
+// chunk is 4 KiB of codes.
+__device__ __forceinline__ void pf_read_v8(const char* vt, const int (&v_addr)[8], int c, bf16x8 (&vop)[8])
+{
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+        vop[db] = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(lds_read_tr8(vt + v_addr[db] + c * 4096)));
+}
+
+template <bool kV8>
+__device__ __forceinline__ void pf_read_vx(const char* vt, const int (&v_addr)[8], int c, bf16x8 (&vop)[8])
+{
+    if constexpr (kV8)
+        pf_read_v8(vt, v_addr, c, vop);
+    else
+        pf_read_v(vt, v_addr, c, vop);
+}
+
 // One 64-key half step of a prefill wavefront (two row blocks rb of 16 rows): S^T = K Q^T,
 // the online softmax, O^T += V^T P^T.  The running maximum is raised lazily: a lane
 // compares its own scores with the row's running maximum plus kRescaleSlack, and only
@@ -1424,7 +1463,7 @@ __device__ __forceinline__ void pf_read_v(const char* vt, const int (&v_addr)[8]
 // wavefront and step.  The full tile (kRB 2, kKB 4) runs the instruction order above; the
 // smaller tiles (kKB 2: one 32-key chunk per wavefront and step) run the same arithmetic
 // in program order.
-template <int kRB, int kKB, bool kMask>
+template <int kRB, int kKB, bool kMask, bool kV8 = false>
 __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[kKB][4], const char* vt, const int (&v_addr)[8],
                                         const bf16x8 (&qop)[kRB][4], f32x4 (&oacc)[kRB][8], float (&m)[kRB],
                                         float (&lsum)[kRB], int key0, int kslice, const int (&qpos)[kRB], int kv_hi,
@@ -1432,7 +1471,7 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[kKB][4], const char*
 {
     if constexpr (kKB == 2) {
         bf16x8 v0[8];
-        pf_read_v(vt, v_addr, 0, v0);
+        pf_read_vx<kV8>(vt, v_addr, 0, v0);
         f32x4 sacc[kRB][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -1499,7 +1538,7 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[kKB][4], const char*
     } else {
     static_assert(kRB == 2 && kKB == 4, "the full tile: two row blocks and four key blocks per wavefront");
     bf16x8 v0[8];
-    pf_read_v(vt, v_addr, 0, v0);
+    pf_read_vx<kV8>(vt, v_addr, 0, v0);
     // key block by key block, so that each K operand is dead once both row blocks used it
     f32x4 sacc[2][4];
 #pragma unroll
@@ -1569,7 +1608,7 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[kKB][4], const char*
     float s0 = pf_exp8(&x[0][0], nm0, scale_log2, p00);
     float s1 = pf_exp8(&x[1][0], nm1, scale_log2, p10);
     bf16x8 v1[8];
-    pf_read_v(vt, v_addr, 1, v1);
+    pf_read_vx<kV8>(vt, v_addr, 1, v1);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
         oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0[db], p00, oacc[0][db], 0, 0, 0);
@@ -2012,9 +2051,6 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     const int q8_tok = lane >> 2, q8_grp = lane & 3;
     u32x4 q8k[2], q8v[2];
     uint32_t q8ks = 0, q8vs = 0;
-    // FP8 copies in flight: the E4M3 codes of this lane's four copies (the chunks the bf16
-    // copies would move, 8 bytes each instead of 16), widened to bf16 when written to LDS
-    u32x2 f8k[4], f8v[4];
     // The copies of a 64- / 32-row chunk tile (chosen only when every chunk row fits one
     // tile, so each row's keys are read by its own workgroups and nobody else) carry the
     // nontemporal hint, as the decode kernel's loads do: 16 rows x 8 new tokens at 8,200
@@ -2048,15 +2084,21 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             return;
         }
         if constexpr (kFp8) {
-            // element offsets are byte offsets in an FP8 pool; slots past kv_len read token 0
-            const int64_t base = (int64_t)id * blk_stride + kvh_off;
+            // the codes go to LDS as they are: wavefront w's block is keys 16 w .. 16 w + 15
+            // of the step, two 1 KiB copies per pool; lane l of copy i moves 16 bytes (unit
+            // l % 8 of LDS row 16 w + 8 i + l / 8, i.e. unit (l % 8) ^ swz8 of the token's
+            // row); slots past kv_len take token 0's bytes
+            u32x4* kd = decltype(sel)::value == 0 ? k_tile0 : k_tile1;
+            u32x4* vd = decltype(sel)::value == 0 ? v_tile0 : v_tile1;
+            const int64_t base = (int64_t)id * blk_stride + kvh_off;   // bytes in an FP8 pool
             const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.k_pool) + base;
             const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.v_pool) + base;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-                f8k[i] = copy_load(reinterpret_cast<const u32x2*>(kb + off));
-                f8v[i] = copy_load(reinterpret_cast<const u32x2*>(vb + off));
+            for (int i = 0; i < 2; ++i) {
+                const int tok = 8 * i + (lane >> 3);
+                const int off = (tok < valid ? tok : 0) * kHeadDim + (((lane & 7) ^ pf_swz8(16 * wave + tok)) << 4);
+                lds_copy16(kb + off, reinterpret_cast<char*>(kd) + (16 * wave + 8 * i) * kHeadDim, PfCopy<kCascade, kRG>{});
+                lds_copy16(vb + off, reinterpret_cast<char*>(vd) + (16 * wave + 8 * i) * kHeadDim, PfCopy<kCascade, kRG>{});
             }
             return;
         }
@@ -2150,17 +2192,6 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             }
             float* sc = q8_sc + B * (4 * kPfKeys) + q8_grp * kPfKeys + 16 * wave + q8_tok;
             sc[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)q8ks);
-        } else if constexpr (kFp8) {
-            // the widened codes go where the bf16 copies would have put them
-            constexpr int B = decltype(sel)::value;
-            u32x4* kd = B == 0 ? k_tile0 : k_tile1;
-            u32x4* vd = B == 0 ? v_tile0 : v_tile1;
-            wait_vmcnt<0>();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kd[(16 * wave + 4 * i) * 16 + lane] = e4m3x8_to_bf16(f8k[i]);
-                vd[(16 * wave + 4 * i) * 16 + lane] = e4m3x8_to_bf16(f8v[i]);
-            }
         }
     };
     // LDS byte offsets of this lane's operand reads within a K or V tile.  K: key
@@ -2170,10 +2201,25 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     // (c adds 8 KiB, +16 keys 4 KiB).  kKPW kh is a multiple of 32, so the swizzle, which
     // sees a key's low four bits, is the same for every key part.
     int k_addr[4], v_addr[8];
+    int k_addr8[2][4];          // FP8 tiles: K operand offsets for even and odd key blocks kb
+    if constexpr (kFp8) {
+        // K: key kKPW kh + 16 kb + row16, dims 32 ks + 8 kslice .. +8 = unit 2 ks + kslice / 2,
+        // half kslice % 2 of that unit (kb adds 2 KiB; its parity flips the swizzle's bit 4)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        k_addr[ks] = (kKPW * kh + row16) * 256 + (((ks * 4 + kslice) ^ pf_swz(row16)) << 4);
-    {
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                k_addr8[par][ks] = (kKPW * kh + row16) * kHeadDim +
+                                   (((2 * ks + (kslice >> 1)) ^ pf_swz8(16 * par + row16)) << 4) + ((kslice & 1) << 3);
+        const int mm = lane & 15, j = mm >> 1;
+        const int key = kKPW * kh + (j < 4 ? 4 * kslice + j : 16 + 4 * kslice + j - 4);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+            v_addr[db] = key * kHeadDim + ((db ^ pf_swz8(key)) << 4) + ((mm & 1) << 3);
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            k_addr[ks] = (kKPW * kh + row16) * 256 + (((ks * 4 + kslice) ^ pf_swz(row16)) << 4);
         const int i16 = lane & 15;
         const int k_lo = kKPW * kh + 4 * kslice + (i16 >> 2);
 #pragma unroll
@@ -2242,8 +2288,13 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                kop[kb][ks] = *reinterpret_cast<const bf16x8*>(kt + k_addr[ks] + kb * 4096);
+            for (int ks = 0; ks < 4; ++ks) {
+                if constexpr (kFp8)
+                    kop[kb][ks] = __builtin_bit_cast(
+                        bf16x8, e4m3x8_to_bf16(*reinterpret_cast<const u32x2*>(kt + k_addr8[kb & 1][ks] + kb * 2048)));
+                else
+                    kop[kb][ks] = *reinterpret_cast<const bf16x8*>(kt + k_addr[ks] + kb * 4096);
+            }
         // Next step's copy (the last step repeats its own; nothing reads that copy) into
         // the other buffer pair, which every wavefront finished reading in the previous
         // step.  Its table entry was loaded one step ago and has landed; the empty asm
@@ -2260,7 +2311,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             pf_step_q8<decltype(msk)::value>(kop, vt, v_addr, ksc, qop, oacc, m, lsum,
                                              s * kPfKeys + 64 * kh, kh, kslice, qpos, kv_hi, p.scale_log2);
         } else {
-            pf_step<kRB, kKB, decltype(msk)::value>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + kKPW * kh,
+            pf_step<kRB, kKB, decltype(msk)::value, kFp8>(kop, vt, v_addr, qop, oacc, m, lsum, s * kPfKeys + kKPW * kh,
                                                     kslice, qpos, kv_hi, p.scale_log2);
         }
     };
