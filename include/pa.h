@@ -257,12 +257,13 @@ pa_status pa_decode_step(const pa_geometry* geometry, const pa_plan_t* plan, con
 
 /*
  * One step of a layer for any batch (decode rows and chunked-prefill rows) with the
- * append fused into the attention launches: row r's qo_len new K / V rows (k_new /
- * v_new rows qo_indptr[r] .. qo_indptr[r + 1] - 1, bf16 [total_q][num_kv_heads]
- * [head_dim]) are written to the slots of positions kv_len[r] - qo_len .. kv_len[r] - 1
- * through block_tables, and attention reads them from k_new / v_new directly.  The
- * result equals pa_append_kv (with those slots) followed by pa_attention_batch, in the
- * launches of pa_attention_batch alone (book section 8.3.1: a token's KV goes to a slot
+ * append fused into the step: row r's qo_len new K / V rows (k_new / v_new rows
+ * qo_indptr[r] .. qo_indptr[r + 1] - 1, bf16 [total_q][num_kv_heads][head_dim]) are
+ * written to the slots of positions kv_len[r] - qo_len .. kv_len[r] - 1 through
+ * block_tables.  Decode rows do it inside the decode launch (attention reads the new
+ * token from k_new / v_new); chunk rows' tokens go into the pool in a short launch before
+ * the chunk tiles, which then read the pool.  The result equals pa_append_kv (with those
+ * slots) followed by pa_attention_batch (book section 8.3.1: a token's KV goes to a slot
  * of the block its table names; the Perplexity blog orders the per-layer append before
  * attention).  The slots a step writes must be distinct and in blocks no other row of the
  * batch reads (copy-on-write of shared blocks is the caller's, as for pa_append_kv).

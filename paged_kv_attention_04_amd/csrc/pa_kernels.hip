@@ -1357,16 +1357,34 @@ constexpr int kPfCopyAux = (!kCascade && kRG == 2) ? 2 : 0;
 template <bool kCascade, int kRG>
 using PfCopy = std::integral_constant<int, kPfCopyAux<kCascade, kRG>>;
 
-// One 16-byte-per-lane LDS-DMA copy (global_load_lds_dwordx4) with cache-policy bits aux.
+// One 16-byte-per-lane LDS-DMA copy (global_load_lds_dwordx4) from per-lane addresses, for
+// the one-launch mixed batch's fused chunk tiles, whose lanes may read the new rows or the
+// pool; cache-policy bits aux as the tags say.
 using CopyDefault = std::integral_constant<int, 0>;
 using CopyStream = std::integral_constant<int, 2>;
 __device__ inline void lds_copy16(const void* src, void* lds, CopyDefault)
 {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
-__device__ inline void lds_copy16(const void* src, void* lds, CopyStream)
+
+// The same copy through a buffer resource (buffer_load_dwordx4 ... lds): lane bytes
+// off .. off + 15 of the `bytes` bytes at the wavefront-uniform address of pf_rsrc (a lane
+// past them reads zeros).  The tiles stage their pool blocks this way: while a copy in the
+// global form is in flight, the compiler cannot tell its completion apart from that of the
+// LDS reads (it counts it as a flat access that may finish out of order) and waits for
+// every outstanding LDS read before each product instead of only for the operands that
+// product needs.
+__device__ inline __amdgpu_buffer_rsrc_t pf_rsrc(const void* base, uint32_t bytes)
 {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 2);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t rs, uint32_t off, void* lds, CopyDefault)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+__device__ inline void lds_copy16(__amdgpu_buffer_rsrc_t rs, uint32_t off, void* lds, CopyStream)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 2);
 }
 
 template <int N>
@@ -1911,6 +1929,9 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     // Quantised pools: a step's chunk rows are encoded into the pool by a launch of their own
     // first (encoding inside the tile raised its register spills in the step loop).
     static_assert(!(kFused && (kQ8 || kFp8)), "quantised pools: chunk rows are appended before the tiles");
+    // Only the one-launch mixed batch fuses the append into its (full) chunk tiles; the
+    // separate tile launches read rows appended by a short launch of their own.
+    static_assert(!kFused || (kRG == 4 && !kCascade), "fused append: full chunk tiles of the one-launch form");
     // Tile shape: kRG row groups of kRB row blocks (16 MFMA rows each) and kNKP = 8 / kRG
     // key parts of kKPW keys of every 128-key step, one wavefront per (row group, key part).
     static_assert((kRG == 4 && kRB == 2) || (kRG == 2 && (kRB == 2 || kRB == 1)), "tile shapes: 4 x 2, 2 x 2, 2 x 1");
@@ -2091,14 +2112,14 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             u32x4* kd = decltype(sel)::value == 0 ? k_tile0 : k_tile1;
             u32x4* vd = decltype(sel)::value == 0 ? v_tile0 : v_tile1;
             const int64_t base = (int64_t)id * blk_stride + kvh_off;   // bytes in an FP8 pool
-            const uint8_t* kb = reinterpret_cast<const uint8_t*>(p.k_pool) + base;
-            const uint8_t* vb = reinterpret_cast<const uint8_t*>(p.v_pool) + base;
+            const auto kr = pf_rsrc(reinterpret_cast<const uint8_t*>(p.k_pool) + base, kBlock * kHeadDim);
+            const auto vr = pf_rsrc(reinterpret_cast<const uint8_t*>(p.v_pool) + base, kBlock * kHeadDim);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int tok = 8 * i + (lane >> 3);
                 const int off = (tok < valid ? tok : 0) * kHeadDim + (((lane & 7) ^ pf_swz8(16 * wave + tok)) << 4);
-                lds_copy16(kb + off, reinterpret_cast<char*>(kd) + (16 * wave + 8 * i) * kHeadDim, PfCopy<kCascade, kRG>{});
-                lds_copy16(vb + off, reinterpret_cast<char*>(vd) + (16 * wave + 8 * i) * kHeadDim, PfCopy<kCascade, kRG>{});
+                lds_copy16(kr, off, reinterpret_cast<char*>(kd) + (16 * wave + 8 * i) * kHeadDim, PfCopy<kCascade, kRG>{});
+                lds_copy16(vr, off, reinterpret_cast<char*>(vd) + (16 * wave + 8 * i) * kHeadDim, PfCopy<kCascade, kRG>{});
             }
             return;
         }
@@ -2125,11 +2146,13 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 return;
             }
         }
+        const auto kr = pf_rsrc(p.k_pool + base, kBlock * kHeadDim * 2);
+        const auto vr = pf_rsrc(p.v_pool + base, kBlock * kHeadDim * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-            lds_copy16(p.k_pool + base + off, &kd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
-            lds_copy16(p.v_pool + base + off, &vd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
+            lds_copy16(kr, 2 * off, &kd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
+            lds_copy16(vr, 2 * off, &vd[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
         }
     };
     // The copies of one pool (K or V) of step s into buffer `sel` of that pool, as `stage`
@@ -2155,10 +2178,11 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 return;
             }
         }
+        const auto rs = pf_rsrc(pool + base, kBlock * kHeadDim * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int off = (4 * i + (lane >> 4)) < valid ? cp_off[i] : (cp_off[i] & (kHeadDim - 1));
-            lds_copy16(pool + base + off, &dst[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
+            lds_copy16(rs, 2 * off, &dst[(16 * wave + 4 * i) * 16], PfCopy<kCascade, kRG>{});
         }
     };
     // q8_0: the copies staged one step ago into buffer pair `sel` (whose previous contents
@@ -2774,15 +2798,17 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
     prefill_body<false, kFused, kQ8, kRG, kRB, kFp8>(p, DecodeParams{}, blockIdx.x);
 }
 
-// The chunk rows of a step over a quantised pool: each row's new K / V rows go into the
-// slots of positions kv_len - qo_len .. kv_len - 1 through its table, encoded exactly as
-// pa_append_q8_scatter / pa_append_fp8_scatter encode them, before the tiles read them.
-// One thread per (token, KV head, piece): a 32-value group (q8_0) or 16 values (FP8);
-// blockIdx.y is the prefill row.
-template <bool kQ8>
+// The chunk rows of a fused step: each row's new K / V rows go into the slots of positions
+// kv_len - qo_len .. kv_len - 1 through its table before the tiles read them, as they are
+// (bf16 pool) or encoded exactly as pa_append_q8_scatter / pa_append_fp8_scatter encode
+// them.  One thread per (token, KV head, piece): 8 values (bf16), a 32-value group (q8_0)
+// or 16 values (FP8); blockIdx.y is the prefill row.
+enum PoolFmt { kFmtBf16 = 0, kFmtQ8 = 1, kFmtFp8 = 2 };
+template <int kFmt>
 __global__ __launch_bounds__(256) void pa_append_chunk_rows(PrefillParams p)
 {
-    constexpr int kPieces = kQ8 ? kHeadDim / pa::kQ8Group : kHeadDim / 16;
+    constexpr bool kQ8 = kFmt == kFmtQ8;
+    constexpr int kPieces = kFmt == kFmtBf16 ? kHeadDim / 8 : kQ8 ? kHeadDim / pa::kQ8Group : kHeadDim / 16;
     const int r = p.prefill_req[blockIdx.y];
     const int q0 = p.qo_indptr[r];
     const int qlen = p.qo_indptr[r + 1] - q0;
@@ -2804,11 +2830,17 @@ __global__ __launch_bounds__(256) void pa_append_chunk_rows(PrefillParams p)
     const int64_t src = ((int64_t)(q0 + t) * p.num_kv_heads + h) * kHeadDim;
     uint8_t* kpool = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_pool));
     uint8_t* vpool = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.v_pool));
-    if constexpr (kQ8)
+    const int64_t dst = (((int64_t)phys * p.num_kv_heads + h) * kBlock + pos % kBlock) * kHeadDim;
+    if constexpr (kFmt == kFmtBf16) {
+        *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_pool) + dst + 8 * c) =
+            *reinterpret_cast<const u32x4*>(p.k_new + src + 8 * c);
+        *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_pool) + dst + 8 * c) =
+            *reinterpret_cast<const u32x4*>(p.v_new + src + 8 * c);
+    } else if constexpr (kQ8) {
         q8_append_group(kpool, p.k_new, p.v_new, src, c, phys, pos % kBlock, h, p.num_kv_heads);
-    else
-        fp8_append_chunk(kpool, vpool, p.k_new, p.v_new, src, c,
-                         (((int64_t)phys * p.num_kv_heads + h) * kBlock + pos % kBlock) * kHeadDim, p.k_div, p.v_div);
+    } else {
+        fp8_append_chunk(kpool, vpool, p.k_new, p.v_new, src, c, dst, p.k_div, p.v_div);
+    }
 }
 
 static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
@@ -3051,8 +3083,7 @@ static void launch(void (*kernel)(Args...), uint32_t grid, hipStream_t st, Args.
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * kPfWaves), 0, st, args...);
 }
 
-static void launch_prefill_tiles(bool q8, bool fused, bool fp8, int rows, uint32_t grid, hipStream_t st,
-                                 const PrefillParams& pp)
+static void launch_prefill_tiles(bool q8, bool fp8, int rows, uint32_t grid, hipStream_t st, const PrefillParams& pp)
 {
     if (q8)
         launch(pa_prefill_tile<false, true, 4, 2>, grid, st, pp);
@@ -3062,11 +3093,11 @@ static void launch_prefill_tiles(bool q8, bool fused, bool fp8, int rows, uint32
                             : pa_prefill_tile<false, false, 4, 2, true>,
                grid, st, pp);
     else if (rows == 32)
-        launch(fused ? pa_prefill_tile<true, false, 2, 1> : pa_prefill_tile<false, false, 2, 1>, grid, st, pp);
+        launch(pa_prefill_tile<false, false, 2, 1>, grid, st, pp);
     else if (rows == 64)
-        launch(fused ? pa_prefill_tile<true, false, 2, 2> : pa_prefill_tile<false, false, 2, 2>, grid, st, pp);
+        launch(pa_prefill_tile<false, false, 2, 2>, grid, st, pp);
     else
-        launch(fused ? pa_prefill_tile<true, false, 4, 2> : pa_prefill_tile<false, false, 4, 2>, grid, st, pp);
+        launch(pa_prefill_tile<false, false, 4, 2>, grid, st, pp);
 }
 
 static void launch_cascade(bool q8, bool fused, bool fp8, int rows, uint32_t grid, hipStream_t st,
@@ -3280,25 +3311,26 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             mixed_pp = pp;
             mixed_prefill_wgs = grid;
         } else {
-            if (fused && (q8 || fp8)) {
-                // quantised pools: the chunk rows' new tokens are encoded into the pool first,
-                // then the tiles read them there (the decode rows keep the fused append)
+            if (fused) {
+                // the chunk rows' new tokens go into the pool first (encoded on a quantised
+                // pool), then the tiles read them there; the decode rows keep the fused append
                 int32_t most_tiles = 0;
                 for (int i = 0; i < plan->num_prefill_rows; ++i)
                     most_tiles = std::max(most_tiles, plan->prefill_tile_start[i + 1] - plan->prefill_tile_start[i]);
                 const int64_t pieces = (int64_t)most_tiles * plan->prefill_tile_tokens * g->num_kv_heads *
-                                       (q8 ? kHeadDim / pa::kQ8Group : kHeadDim / 16);
+                                       (q8 ? kHeadDim / pa::kQ8Group : fp8 ? kHeadDim / 16 : kHeadDim / 8);
                 const int64_t bx = (pieces + 255) / 256;
                 if (bx > INT32_MAX)
                     return PA_ERR_SHAPE;
                 const dim3 agrid((uint32_t)std::max<int64_t>(bx, 1), (uint32_t)plan->num_prefill_rows);
                 if (q8)
-                    hipLaunchKernelGGL(pa_append_chunk_rows<true>, agrid, dim3(256), 0, st, pp);
+                    hipLaunchKernelGGL(pa_append_chunk_rows<kFmtQ8>, agrid, dim3(256), 0, st, pp);
+                else if (fp8)
+                    hipLaunchKernelGGL(pa_append_chunk_rows<kFmtFp8>, agrid, dim3(256), 0, st, pp);
                 else
-                    hipLaunchKernelGGL(pa_append_chunk_rows<false>, agrid, dim3(256), 0, st, pp);
+                    hipLaunchKernelGGL(pa_append_chunk_rows<kFmtBf16>, agrid, dim3(256), 0, st, pp);
             }
-            launch_prefill_tiles(q8, fused && !(q8 || fp8), fp8, q8 ? 128 : kGroup * plan->prefill_tile_tokens,
-                                 (uint32_t)grid, st, pp);
+            launch_prefill_tiles(q8, fp8, q8 ? 128 : kGroup * plan->prefill_tile_tokens, (uint32_t)grid, st, pp);
         }
         if (!one_launch && hipGetLastError() != hipSuccess)
             return PA_ERR_HIP;
