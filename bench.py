@@ -688,6 +688,8 @@ def main(argv=None):
     # the same decode step on a q8_0 pool (same lengths and tables): the saving against
     # the pages' model, saving = fewer bytes / bandwidth - conversion time
     del st
+    # the saving model's three attention times (bf16, q8_0, FP8: attention alone, append
+    # separate), each after a warm-up of its own
     st_plain = Stepper(wl, args.copies)            # bf16 attention alone, the q8_0 line's reference
     time_steps(st_plain, 10, 5, attention_only=True)
     t_plain = event_time(st_plain, max(args.steps, 50))
@@ -695,6 +697,7 @@ def main(argv=None):
     wq = synthetic.config_decode_q8(poison=False)
     abq = algorithmic_bytes(wq)
     sq = Stepper(wq, args.copies)                  # attention alone (append separate): the saving model
+    time_steps(sq, 10, 5, attention_only=True)
     t_q = event_time(sq, max(args.steps, 50))
     del sq
     sq = Stepper(wq, args.copies, fused=True)      # the step: plan + pa_decode_step_q8 (append fused)
@@ -737,6 +740,7 @@ def main(argv=None):
     wf = synthetic.config_decode_fp8(poison=False)
     abf = algorithmic_bytes(wf)
     sf = Stepper(wf, args.copies)                  # attention alone (append separate): the saving model
+    time_steps(sf, 10, 5, attention_only=True)
     t_f = event_time(sf, max(args.steps, 50))
     del sf
     sf = Stepper(wf, args.copies, fused=True)      # the step: plan + pa_decode_step_fp8 (append fused)
