@@ -472,7 +472,11 @@ def sweep36(steps: int = 20, warmup: int = 5) -> dict:
             "graph_fused_step_ms": round(tf * 1e3, 4),
             "unique_gb_per_step": round(unique / 1e9, 4), "unique_gbs": round(unique / tg / 1e9, 1),
             "logical_gbs": round(logical / tg / 1e9, 1), "frac_of_hbm_peak": round(unique / tg / 1e9 / HBM_PEAK_GBS, 4),
-            "tokens_per_s": round(batch / tg, 1), "prefix_groups": stack.plan.num_prefix_groups})
+            "tokens_per_s": round(batch / tg, 1), "prefix_groups": stack.plan.num_prefix_groups,
+            "pool_blocks_per_layer": wl.num_blocks,
+            "pool": ("12 GiB / 36 layers" if wl.num_blocks <= synthetic.POOL_BLOCKS_12GIB else
+                     f"enlarged past 12 GiB / 36 layers ({synthetic.POOL_BLOCKS_12GIB} blocks per layer): "
+                     f"the batch's tables need {wl.num_blocks}")})
         del stack, graph, graph_f
         torch.cuda.empty_cache()
     # 2048-token prompt, four 512-token chunks, 36 layers each
