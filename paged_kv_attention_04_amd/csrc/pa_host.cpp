@@ -97,30 +97,33 @@ void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t*
 struct MakespanCosts {
     double decode_fixed, merge_per8, prefix_fixed, prefix_step, prefix_per_req;
 };
-// Fitted to the 16-request, 6144-token-prefix case on MI355X (rms error ~2 us over 20
-// split choices); used to pick the decode split length for a given prefix split count.
-constexpr MakespanCosts kSplitCosts = {13.3, 6.67, 33.3, 6.67, 0.0};
-// Fitted to 320 measured (prefix splits, split length) pairs over five batches (4 to 32
-// requests sharing a 6144-token prefix, 2048-token suffixes; rms log error 0.11); it
-// weighs the prefix pass, whose 128-key steps stream their blocks from memory once, more
-// heavily and is used to choose between prefix split counts.
-constexpr MakespanCosts kPrefixCosts = {23.0, 5.57, 43.9, 11.6, 3.30};
-// Candidate prefix split counts: this many 128-key steps per prefix workgroup (the
-// measured optimum over those five batches was always at 4 or 6 steps, or within 2% of it).
-constexpr int32_t kPrefixStepsPerSplit[] = {6, 4};
-// The same planner for a q8_0 pool.  Not fitted: the bf16 constants rescaled by two
-// measured ratios (per-workgroup timestamps on the 16-request, 6144-token-prefix batch):
-// a q8_0 prefix step costs 1.5 bf16 steps (the matrix-unit tile also applies the scales),
-// and a q8_0 decode block 0.85 bf16 blocks (half the bytes, plus the conversion); costs
-// are in q8_0 decode block-times.  The candidates keep the prefix workgroups as long as
-// the bf16 ones in time (4 and 3 steps); with 6 steps the prefix workgroups finished last
-// and merged their groups' rows (64.7 us on that batch against 44.9 us with 3).
+// q8_0 pools: two models, rescaled from an earlier bf16 fit (decode fixed 13.3, merge
+// 6.67, prefix fixed 33.3 and step 6.67 block-times, used to pick the decode split length
+// for a given prefix split count; and 23.0, 5.57, 43.9, 11.6 plus 3.30 per group request,
+// used to choose between prefix split counts) by two measured ratios (per-workgroup
+// timestamps on the 16-request, 6144-token-prefix batch): a q8_0 prefix step costs 1.5
+// bf16 steps (the matrix-unit tile also applies the scales), and a q8_0 decode block 0.85
+// bf16 blocks (half the bytes, plus the conversion); costs are in q8_0 decode
+// block-times.  The candidates keep the prefix workgroups as long as the bf16 ones in
+// time (4 and 3 steps per prefix workgroup); with 6 steps the prefix workgroups finished
+// last and merged their groups' rows (64.7 us on that batch against 44.9 us with 3).
 constexpr double kQ8StepRatio = 1.5, kQ8BlockRatio = 0.85;
 constexpr MakespanCosts kSplitCostsQ8 = {13.3 / kQ8BlockRatio, 6.67 / kQ8BlockRatio, 33.3 / kQ8BlockRatio,
                                          6.67 * kQ8StepRatio / kQ8BlockRatio, 0.0};
 constexpr MakespanCosts kPrefixCostsQ8 = {23.0 / kQ8BlockRatio, 5.57 / kQ8BlockRatio, 43.9 / kQ8BlockRatio,
                                           11.6 * kQ8StepRatio / kQ8BlockRatio, 3.30 / kQ8BlockRatio};
 constexpr int32_t kPrefixStepsPerSplitQ8[] = {4, 3};
+// bf16 (and FP8) pools: one model for both choices, fitted to 240 measured plans (HIP
+// events) -- 4, 8, 16 and 32 requests sharing a 6144-token prefix with 2048-token
+// suffixes, and the 36-layer sweep's batches 8, 16, 32 and 64 (half the rows sharing the
+// prefix), each over prefix splits 4 .. 24 and decode split lengths of 1 .. 6 parts of
+// the longest suffix; rms log error 0.086.  The joint search over the candidates below
+// picked a plan within 1.00-1.07 of each batch's best measured one (against 1.02-1.43
+// for the two-stage search kept for q8_0 pools).  Prefix splits past 16 were slower on
+// every batch measured and are not candidates.
+constexpr MakespanCosts kCascadeCosts = {34.3, 0.0, 69.5, 7.66, 0.90};
+constexpr int32_t kPrefixSplitCandidates[] = {4, 6, 8, 12, 16};
+constexpr int32_t kMaxAutoDecodeParts = 8;
 
 double fused_makespan(const pa_plan_t& plan, const std::vector<int32_t>& suffix_blocks, const int32_t* qo_len,
                       int32_t num_vheads, int32_t num_cus, int32_t prefix_splits, int32_t split_blocks,
@@ -330,14 +333,12 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
         return PA_OK;
 
     // Key splits of the shared blocks and the decode split length over the private
-    // suffixes, chosen together for the one launch.  For each candidate prefix split
-    // count (kPrefixStepsPerSplit 128-key steps per prefix workgroup) the split length
-    // with the smallest simulated makespan under kSplitCosts (ties to the longer split);
-    // then the candidate whose plan has the smaller makespan under kPrefixCosts (ties to
-    // the first).  Measured on the 6144-token prefix: 8 and more steps per prefix
-    // workgroup ran in 63-100 us against 42 us at 6 (a prefix workgroup then finishing
-    // last and merging its group's rows), and with 4 requests per group 4 steps ran in
-    // 30 us against 39 us at 6 (the prefix pass is then the critical path).
+    // suffixes, chosen together for the one launch: on bf16 and FP8 pools the pair with
+    // the smallest simulated makespan under kCascadeCosts; on q8_0 pools, for each
+    // candidate prefix split count (kPrefixStepsPerSplitQ8 128-key steps per prefix
+    // workgroup) the split length with the smallest makespan under kSplitCostsQ8 (ties to
+    // the longer split), then the candidate whose plan has the smaller makespan under
+    // kPrefixCostsQ8 (ties to the first).
     std::vector<int32_t> skip(R, 0), suffix(R, 0);
     for (int32_t i = 0; i < out.num_prefix_groups; ++i)
         for (int32_t k = 0; k < out.prefix_num_reqs[i]; ++k)
@@ -361,8 +362,7 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
                 continue;
             if (sb < kMinAutoSplitBlocks && parts > 1)
                 break;
-            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb,
-                                            q8 ? kSplitCostsQ8 : kSplitCosts);
+            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb, kSplitCostsQ8);
             if (!have || t < best - 1e-9) {
                 have = true;
                 best = t;
@@ -372,16 +372,51 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
         return best_sb;
     };
     int32_t best_ps = 0, best_sb = 0;
-    if (prefix_splits > 0) {
+    if (!q8) {
+        // one makespan model for both choices, searched jointly (ties to fewer prefix
+        // splits, then to the longer split length)
+        double best = 0.0;
+        bool have = false;
+        auto consider = [&](int32_t ps, int32_t sb) {
+            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb, kCascadeCosts);
+            if (!have || t < best - 1e-9) {
+                have = true;
+                best = t;
+                best_ps = ps;
+                best_sb = sb;
+            }
+        };
+        auto over_lengths = [&](int32_t ps) {
+            if (split_blocks > 0) {
+                consider(ps, split_blocks);
+                return;
+            }
+            for (int32_t parts = 1; parts <= kMaxAutoDecodeParts; ++parts) {
+                const int32_t sb = ceil_div(longest, parts);
+                if (sb > pa::kMaxSplitBlocks)
+                    continue;
+                if (sb < kMinAutoSplitBlocks && parts > 1)
+                    break;
+                consider(ps, sb);
+            }
+            if (!have)                                 // every row longer than the largest split
+                consider(ps, pa::kMaxSplitBlocks);
+        };
+        if (prefix_splits > 0) {
+            over_lengths(prefix_splits);
+        } else {
+            for (const int32_t cand : kPrefixSplitCandidates)
+                over_lengths(std::max(1, std::min({cand, steps, (int32_t)pa::kMaxPrefillSplits})));
+        }
+    } else if (prefix_splits > 0) {
         best_ps = prefix_splits;
         best_sb = best_split_length(best_ps);
     } else {
         double best = 0.0;
-        for (const int32_t per : q8 ? kPrefixStepsPerSplitQ8 : kPrefixStepsPerSplit) {
+        for (const int32_t per : kPrefixStepsPerSplitQ8) {
             const int32_t ps = std::min(std::max(1, ceil_div(steps, per)), pa::kMaxPrefillSplits);
             const int32_t sb = best_split_length(ps);
-            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb,
-                                            q8 ? kPrefixCostsQ8 : kPrefixCosts);
+            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb, kPrefixCostsQ8);
             if (best_ps == 0 || t < best - 1e-9) {
                 best = t;
                 best_ps = ps;
