@@ -97,31 +97,19 @@ void choose_decode_splits(const pa_geometry* g, int32_t num_reqs, const int32_t*
 struct MakespanCosts {
     double decode_fixed, merge_per8, prefix_fixed, prefix_step, prefix_per_req;
 };
-// q8_0 pools: two models, rescaled from an earlier bf16 fit (decode fixed 13.3, merge
-// 6.67, prefix fixed 33.3 and step 6.67 block-times, used to pick the decode split length
-// for a given prefix split count; and 23.0, 5.57, 43.9, 11.6 plus 3.30 per group request,
-// used to choose between prefix split counts) by two measured ratios (per-workgroup
-// timestamps on the 16-request, 6144-token-prefix batch): a q8_0 prefix step costs 1.5
-// bf16 steps (the matrix-unit tile also applies the scales), and a q8_0 decode block 0.85
-// bf16 blocks (half the bytes, plus the conversion); costs are in q8_0 decode
-// block-times.  The candidates keep the prefix workgroups as long as the bf16 ones in
-// time (4 and 3 steps per prefix workgroup); with 6 steps the prefix workgroups finished
-// last and merged their groups' rows (64.7 us on that batch against 44.9 us with 3).
-constexpr double kQ8StepRatio = 1.5, kQ8BlockRatio = 0.85;
-constexpr MakespanCosts kSplitCostsQ8 = {13.3 / kQ8BlockRatio, 6.67 / kQ8BlockRatio, 33.3 / kQ8BlockRatio,
-                                         6.67 * kQ8StepRatio / kQ8BlockRatio, 0.0};
-constexpr MakespanCosts kPrefixCostsQ8 = {23.0 / kQ8BlockRatio, 5.57 / kQ8BlockRatio, 43.9 / kQ8BlockRatio,
-                                          11.6 * kQ8StepRatio / kQ8BlockRatio, 3.30 / kQ8BlockRatio};
-constexpr int32_t kPrefixStepsPerSplitQ8[] = {4, 3};
-// bf16 (and FP8) pools: one model for both choices, fitted to 240 measured plans (HIP
-// events) -- 4, 8, 16 and 32 requests sharing a 6144-token prefix with 2048-token
-// suffixes, and the 36-layer sweep's batches 8, 16, 32 and 64 (half the rows sharing the
-// prefix), each over prefix splits 4 .. 24 and decode split lengths of 1 .. 6 parts of
-// the longest suffix; rms log error 0.086.  The joint search over the candidates below
-// picked a plan within 1.00-1.07 of each batch's best measured one (against 1.02-1.43
-// for the two-stage search kept for q8_0 pools).  Prefix splits past 16 were slower on
+// One model for both choices per pool format, each fitted to plans measured with HIP
+// events over prefix splits 4 .. 24 and decode split lengths of 1 .. 6 parts of the
+// longest suffix.  bf16 (and FP8) pools: 240 plans -- 4, 8, 16 and 32 requests sharing a
+// 6144-token prefix with 2048-token suffixes, and the 36-layer sweep's batches 8, 16, 32
+// and 64 (half the rows sharing the prefix); rms log error 0.086; the joint search over
+// the candidates below picks a plan within 1.00-1.07 of each batch's best measured one
+// (FP8 pools, measured on the four shared-prefix batches: within 1.00-1.14).  q8_0
+// pools: 120 plans over the four shared-prefix batches, rms log error 0.12, picks within
+// 1.00-1.06 (the 128-row q8_0 prefix tile makes a prefix workgroup dearer).  Costs are
+// in decode block-times of the pool's format.  Prefix splits past 16 were slower on
 // every batch measured and are not candidates.
 constexpr MakespanCosts kCascadeCosts = {34.3, 0.0, 69.5, 7.66, 0.90};
+constexpr MakespanCosts kCascadeCostsQ8 = {28.5, 0.0, 78.8, 14.6, 3.34};
 constexpr int32_t kPrefixSplitCandidates[] = {4, 6, 8, 12, 16};
 constexpr int32_t kMaxAutoDecodeParts = 8;
 
@@ -333,12 +321,8 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
         return PA_OK;
 
     // Key splits of the shared blocks and the decode split length over the private
-    // suffixes, chosen together for the one launch: on bf16 and FP8 pools the pair with
-    // the smallest simulated makespan under kCascadeCosts; on q8_0 pools, for each
-    // candidate prefix split count (kPrefixStepsPerSplitQ8 128-key steps per prefix
-    // workgroup) the split length with the smallest makespan under kSplitCostsQ8 (ties to
-    // the longer split), then the candidate whose plan has the smaller makespan under
-    // kPrefixCostsQ8 (ties to the first).
+    // suffixes, chosen together for the one launch: the pair with the smallest simulated
+    // makespan under the pool format's costs.
     std::vector<int32_t> skip(R, 0), suffix(R, 0);
     for (int32_t i = 0; i < out.num_prefix_groups; ++i)
         for (int32_t k = 0; k < out.prefix_num_reqs[i]; ++k)
@@ -350,79 +334,44 @@ static pa_status plan_shared_prefix(bool q8, const pa_geometry* g, const int32_t
             longest = std::max(longest, suffix[r]);
     }
     const int32_t steps = ceil_div((int64_t)max_prefix_blocks * pa::kBlock, pa::kPrefillKeys);
-    auto best_split_length = [&](int32_t ps) {
-        if (split_blocks > 0)
-            return split_blocks;
-        double best = 0.0;
-        int32_t best_sb = std::min(longest, pa::kMaxSplitBlocks);
-        bool have = false;
-        for (int32_t parts = 1; parts <= 16; ++parts) {
+    // one makespan model for both choices, searched jointly (ties to fewer prefix splits,
+    // then to the longer split length)
+    const MakespanCosts& costs = q8 ? kCascadeCostsQ8 : kCascadeCosts;
+    int32_t best_ps = 0, best_sb = 0;
+    double best = 0.0;
+    bool have = false;
+    auto consider = [&](int32_t ps, int32_t sb) {
+        const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb, costs);
+        if (!have || t < best - 1e-9) {
+            have = true;
+            best = t;
+            best_ps = ps;
+            best_sb = sb;
+        }
+    };
+    auto over_lengths = [&](int32_t ps) {
+        if (split_blocks > 0) {
+            consider(ps, split_blocks);
+            return;
+        }
+        bool any = false;
+        for (int32_t parts = 1; parts <= kMaxAutoDecodeParts; ++parts) {
             const int32_t sb = ceil_div(longest, parts);
             if (sb > pa::kMaxSplitBlocks)
                 continue;
             if (sb < kMinAutoSplitBlocks && parts > 1)
                 break;
-            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb, kSplitCostsQ8);
-            if (!have || t < best - 1e-9) {
-                have = true;
-                best = t;
-                best_sb = sb;
-            }
+            consider(ps, sb);
+            any = true;
         }
-        return best_sb;
+        if (!any)                                      // every cut longer than the largest split
+            consider(ps, pa::kMaxSplitBlocks);
     };
-    int32_t best_ps = 0, best_sb = 0;
-    if (!q8) {
-        // one makespan model for both choices, searched jointly (ties to fewer prefix
-        // splits, then to the longer split length)
-        double best = 0.0;
-        bool have = false;
-        auto consider = [&](int32_t ps, int32_t sb) {
-            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb, kCascadeCosts);
-            if (!have || t < best - 1e-9) {
-                have = true;
-                best = t;
-                best_ps = ps;
-                best_sb = sb;
-            }
-        };
-        auto over_lengths = [&](int32_t ps) {
-            if (split_blocks > 0) {
-                consider(ps, split_blocks);
-                return;
-            }
-            for (int32_t parts = 1; parts <= kMaxAutoDecodeParts; ++parts) {
-                const int32_t sb = ceil_div(longest, parts);
-                if (sb > pa::kMaxSplitBlocks)
-                    continue;
-                if (sb < kMinAutoSplitBlocks && parts > 1)
-                    break;
-                consider(ps, sb);
-            }
-            if (!have)                                 // every row longer than the largest split
-                consider(ps, pa::kMaxSplitBlocks);
-        };
-        if (prefix_splits > 0) {
-            over_lengths(prefix_splits);
-        } else {
-            for (const int32_t cand : kPrefixSplitCandidates)
-                over_lengths(std::max(1, std::min({cand, steps, (int32_t)pa::kMaxPrefillSplits})));
-        }
-    } else if (prefix_splits > 0) {
-        best_ps = prefix_splits;
-        best_sb = best_split_length(best_ps);
+    if (prefix_splits > 0) {
+        over_lengths(prefix_splits);
     } else {
-        double best = 0.0;
-        for (const int32_t per : kPrefixStepsPerSplitQ8) {
-            const int32_t ps = std::min(std::max(1, ceil_div(steps, per)), pa::kMaxPrefillSplits);
-            const int32_t sb = best_split_length(ps);
-            const double t = fused_makespan(out, suffix, qo_len, vheads, num_cus, ps, sb, kPrefixCostsQ8);
-            if (best_ps == 0 || t < best - 1e-9) {
-                best = t;
-                best_ps = ps;
-                best_sb = sb;
-            }
-        }
+        for (const int32_t cand : kPrefixSplitCandidates)
+            over_lengths(std::max(1, std::min({cand, steps, (int32_t)pa::kMaxPrefillSplits})));
     }
     out.prefix_splits = best_ps;
     // the prefix tile: 4 rows per request of the largest group; a q8_0 pool runs the full tile

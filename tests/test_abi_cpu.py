@@ -233,11 +233,12 @@ def test_plan_shared_prefix_fused_launch_choices():
     again = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
     pa.pa_plan_shared_prefix(g, again, sp.qo_len, sp.kv_len, sp.block_tables, 256)
     assert bytes(again) == bytes(plan)                 # a pure function of its inputs
-    # the same batch on a q8_0 pool: prefix steps dearer, decode blocks cheaper -> four
-    # steps per prefix workgroup (45.4 us measured against 64.7 us with the bf16 choice)
+    # the same batch on a q8_0 pool, under the q8_0 costs (its 128-row prefix tile makes
+    # a prefix workgroup dearer): unsplit decode rows and 16 prefix splits, 38.5 us in
+    # the q8_0 grid (its best 37.3 us; the earlier choice (12, 48) 42.6 us)
     q8 = pa.pa_plan(g, sp.qo_len, sp.kv_len, 256)
     pa.pa_plan_shared_prefix(g, q8, sp.qo_len, sp.kv_len, sp.block_tables, 256, q8=True)
-    assert (q8.prefix_splits, q8.split_blocks) == (12, 48)
+    assert (q8.prefix_splits, q8.split_blocks) == (16, 142)
     for batch, want in ((8, (16, 65)), (32, (16, 129))):
         wl = synthetic.config_sweep_decode(batch, 0, poison=False, fill_pools=False)
         gs = pa.Geometry.make(32, 8, wl.num_blocks)
