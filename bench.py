@@ -693,16 +693,19 @@ def main(argv=None):
     # the pages' model, saving = fewer bytes / bandwidth - conversion time
     del st
     # the saving model's three attention times (bf16, q8_0, FP8: attention alone, append
-    # separate), each after a warm-up of its own
+    # separate), each after a warm-up of its own and the least of three timed runs (the
+    # shorter quantised launches are the likelier to catch a slow stretch of the box)
+    def least_time(st):
+        return min(event_time(st, max(args.steps // 2, 50)) for _ in range(3))
     st_plain = Stepper(wl, args.copies)            # bf16 attention alone, the q8_0 line's reference
     time_steps(st_plain, 10, 5, attention_only=True)
-    t_plain = event_time(st_plain, max(args.steps, 50))
+    t_plain = least_time(st_plain)
     del st_plain
     wq = synthetic.config_decode_q8(poison=False)
     abq = algorithmic_bytes(wq)
     sq = Stepper(wq, args.copies)                  # attention alone (append separate): the saving model
     time_steps(sq, 10, 5, attention_only=True)
-    t_q = event_time(sq, max(args.steps, 50))
+    t_q = least_time(sq)
     del sq
     sq = Stepper(wq, args.copies, fused=True)      # the step: plan + pa_decode_step_q8 (append fused)
     sec_q = time_steps(sq, args.steps, args.warmup)
@@ -745,7 +748,7 @@ def main(argv=None):
     abf = algorithmic_bytes(wf)
     sf = Stepper(wf, args.copies)                  # attention alone (append separate): the saving model
     time_steps(sf, 10, 5, attention_only=True)
-    t_f = event_time(sf, max(args.steps, 50))
+    t_f = least_time(sf)
     del sf
     sf = Stepper(wf, args.copies, fused=True)      # the step: plan + pa_decode_step_fp8 (append fused)
     sec_f = time_steps(sf, args.steps, args.warmup)
