@@ -806,7 +806,7 @@ def main(argv=None):
 
     line.update({
         "mixed_batch": {"workload": "1 prefill row (512 tokens at offset 4096) + 31 decode rows, 543 new tokens",
-                        "step": "pa_plan + pa_attention_step (append fused into the prefill and decode launches)",
+                        "step": "pa_plan + pa_attention_step (decode and chunk rows' appends inside the decode launch, then the chunk tiles)",
                         "tokens_per_s": round(wm.total_q / sec_m, 1), "ms_per_step": round(sec_m * 1e3, 5),
                         "launches_us": round(t_m * 1e6, 3),
                         "append_then_attention_ms_per_step": round(sec_m2 * 1e3, 5)},

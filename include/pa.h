@@ -261,8 +261,10 @@ pa_status pa_decode_step(const pa_geometry* geometry, const pa_plan_t* plan, con
  * qo_indptr[r] .. qo_indptr[r + 1] - 1, bf16 [total_q][num_kv_heads][head_dim]) are
  * written to the slots of positions kv_len[r] - qo_len .. kv_len[r] - 1 through
  * block_tables.  Decode rows do it inside the decode launch (attention reads the new
- * token from k_new / v_new); chunk rows' tokens go into the pool in a short launch before
- * the chunk tiles, which then read the pool.  The result equals pa_append_kv (with those
+ * token from k_new / v_new); chunk rows' tokens go into the pool in extra workgroups of
+ * that launch, which then runs before the chunk tiles (with no decode rows, or with
+ * shared-prefix groups, in a short launch of their own before the tiles); the tiles read
+ * the pool.  The result equals pa_append_kv (with those
  * slots) followed by pa_attention_batch (book section 8.3.1: a token's KV goes to a slot
  * of the block its table names; the Perplexity blog orders the per-layer append before
  * attention).  The slots a step writes must be distinct and in blocks no other row of the

@@ -2805,17 +2805,21 @@ __global__ __launch_bounds__(64 * kPfWaves) void pa_prefill_tile(PrefillParams p
 // or 16 values (FP8); blockIdx.y is the prefill row.
 enum PoolFmt { kFmtBf16 = 0, kFmtQ8 = 1, kFmtFp8 = 2 };
 template <int kFmt>
-__global__ __launch_bounds__(256) void pa_append_chunk_rows(PrefillParams p)
+constexpr int kAppendPieces = kFmt == kFmtBf16 ? kHeadDim / 8 : kFmt == kFmtQ8 ? kHeadDim / pa::kQ8Group : kHeadDim / 16;
+
+// Piece idx of prefill row i's new tokens (idx = (token * num_kv_heads + head) * pieces +
+// piece); indices past the row's tokens do nothing.
+template <int kFmt>
+__device__ inline void append_chunk_piece(const PrefillParams& p, int i, int64_t idx)
 {
     constexpr bool kQ8 = kFmt == kFmtQ8;
-    constexpr int kPieces = kFmt == kFmtBf16 ? kHeadDim / 8 : kQ8 ? kHeadDim / pa::kQ8Group : kHeadDim / 16;
-    const int r = p.prefill_req[blockIdx.y];
+    constexpr int kPieces = kAppendPieces<kFmt>;
+    const int r = p.prefill_req[i];
     const int q0 = p.qo_indptr[r];
     const int qlen = p.qo_indptr[r + 1] - q0;
     const int kvlen = p.kv_len[r];
     const int ctx = kvlen - qlen;
     const int64_t per_token = (int64_t)p.num_kv_heads * kPieces;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (qlen < 1 || ctx < 0 || idx >= (int64_t)qlen * per_token)
         return;
     const int t = (int)(idx / per_token);
@@ -2841,6 +2845,33 @@ __global__ __launch_bounds__(256) void pa_append_chunk_rows(PrefillParams p)
     } else {
         fp8_append_chunk(kpool, vpool, p.k_new, p.v_new, src, c, dst, p.k_div, p.v_div);
     }
+}
+
+template <int kFmt>
+__global__ __launch_bounds__(256) void pa_append_chunk_rows(PrefillParams p)
+{
+    append_chunk_piece<kFmt>(p, blockIdx.y, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// A fused step's decode rows (their append inside, as in pa_decode_split) and, in
+// workgroups past them, its chunk rows' appends (append_wgs_per_row workgroups of
+// 64 * kDecodeWaves threads per prefill row): one launch instead of an append launch
+// before the chunk tiles, which the host then launches after this one.
+template <bool kQ8, bool kFp8>
+__global__ __launch_bounds__(64 * kDecodeWaves) void pa_decode_split_append(DecodeParams dp, PrefillParams pp,
+                                                                             int32_t decode_wgs,
+                                                                             int32_t append_wgs_per_row)
+{
+    if ((int32_t)blockIdx.x < decode_wgs) {
+        decode_body<kQ8, true, kFp8>(dp, blockIdx.x);
+        return;
+    }
+    constexpr int kFmt = kQ8 ? kFmtQ8 : kFp8 ? kFmtFp8 : kFmtBf16;
+    const int e = (int)blockIdx.x - decode_wgs;
+    const int i = e / append_wgs_per_row;
+    if (i >= pp.num_prefill_rows)
+        return;
+    append_chunk_piece<kFmt>(pp, i, (int64_t)(e % append_wgs_per_row) * (64 * kDecodeWaves) + threadIdx.x);
 }
 
 static_assert(kPfWaves == kDecodeWaves, "the fused shared-prefix launch runs both bodies with one block size");
@@ -3273,6 +3304,15 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
                             plan->prefill_tiles > 0 && plan->num_decode_rows > 0 && plan->max_splits > 0;
     PrefillParams mixed_pp = {};
     int64_t mixed_prefill_wgs = 0;
+    // A fused step with decode rows and chunk rows (no shared-prefix group, two launches):
+    // the chunk rows' appends ride in extra workgroups of the decode launch, which then
+    // goes first, and the chunk tiles follow it (the two kinds share no blocks, outputs or
+    // workspace).
+    const bool append_in_decode = fused && !one_launch && ngroups == 0 && plan->num_prefill_rows > 0 &&
+                                  plan->prefill_tiles > 0 && plan->num_decode_rows > 0 && plan->max_splits > 0;
+    PrefillParams later_pp = {};
+    int64_t later_grid = 0;
+    int32_t append_wgs_per_row = 0;
     if (plan->num_prefill_rows > 0 && plan->prefill_tiles > 0) {
         PrefillParams pp = prefill_params();
         pp.q = static_cast<const uint16_t*>(q);
@@ -3310,6 +3350,18 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
         if (one_launch) {
             mixed_pp = pp;
             mixed_prefill_wgs = grid;
+        } else if (append_in_decode) {
+            int32_t most_tiles = 0;
+            for (int i = 0; i < plan->num_prefill_rows; ++i)
+                most_tiles = std::max(most_tiles, plan->prefill_tile_start[i + 1] - plan->prefill_tile_start[i]);
+            const int64_t pieces = (int64_t)most_tiles * plan->prefill_tile_tokens * g->num_kv_heads *
+                                   (q8 ? kHeadDim / pa::kQ8Group : fp8 ? kHeadDim / 16 : kHeadDim / 8);
+            const int64_t per_row = std::max<int64_t>((pieces + 64 * kDecodeWaves - 1) / (64 * kDecodeWaves), 1);
+            if (per_row * plan->num_prefill_rows > INT32_MAX / 2)
+                return PA_ERR_SHAPE;
+            append_wgs_per_row = (int32_t)per_row;
+            later_pp = pp;
+            later_grid = grid;
         } else {
             if (fused) {
                 // the chunk rows' new tokens go into the pool first (encoded on a quantised
@@ -3400,6 +3452,23 @@ static pa_status attention_batch(bool q8, const pa_geometry* g, const pa_plan_t*
             else
                 hipLaunchKernelGGL((pa_mixed_batch<false>), blocks, dim3(64 * kPfWaves), 0, st, mixed_pp, dp,
                                    (int32_t)mixed_prefill_wgs, (int32_t)grid, (int32_t)(plan->one_launch == 2));
+        } else if (append_in_decode) {
+            const int64_t total = grid + (int64_t)append_wgs_per_row * plan->num_prefill_rows;
+            if (total > INT32_MAX)
+                return PA_ERR_SHAPE;
+            if (q8)
+                hipLaunchKernelGGL((pa_decode_split_append<true, false>), dim3((uint32_t)total), dim3(64 * kDecodeWaves),
+                                   0, st, dp, later_pp, (int32_t)grid, append_wgs_per_row);
+            else if (fp8)
+                hipLaunchKernelGGL((pa_decode_split_append<false, true>), dim3((uint32_t)total), dim3(64 * kDecodeWaves),
+                                   0, st, dp, later_pp, (int32_t)grid, append_wgs_per_row);
+            else
+                hipLaunchKernelGGL((pa_decode_split_append<false, false>), dim3((uint32_t)total),
+                                   dim3(64 * kDecodeWaves), 0, st, dp, later_pp, (int32_t)grid, append_wgs_per_row);
+            if (hipGetLastError() != hipSuccess)
+                return PA_ERR_HIP;
+            launch_prefill_tiles(q8, fp8, q8 ? 128 : kGroup * plan->prefill_tile_tokens, (uint32_t)later_grid, st,
+                                 later_pp);
         } else {
             if (grid > INT32_MAX)
                 return PA_ERR_SHAPE;
