@@ -2708,7 +2708,52 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
     if (!last_lds || kh != 0)
         return;
 
-    {
+    if (p.splits == 2) {
+        // Two splits, the usual case: the other split's log2-sum-exps and values are loaded
+        // together, so that the merge waits for one round trip.  The arithmetic and its order
+        // are those of the general merge below.
+        const int other = split ^ 1;
+        const float* po = part_o_at(other);
+        float lo[kRB];
+        f32x4 oo[kRB][8];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            lo[rb] = load_agent(part_lse_at(other) + rb * 64 + lane);
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    oo[rb][db][e] = load_agent(po + ((rb * 8 + db) * 4 + e) * 64 + lane);
+        }
+        bool any_nan = false;
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            const float l0 = split == 0 ? lse2[rb] : lo[rb];
+            const float l1 = split == 0 ? lo[rb] : lse2[rb];
+            any_nan |= l0 != l0;
+            any_nan |= l1 != l1;
+            const float L = fmaxf(fmaxf(-INFINITY, l0), l1);
+            const float w0 = (l0 > -INFINITY) ? fast_exp2(l0 - L) : 0.f;
+            const float w1 = (l1 > -INFINITY) ? fast_exp2(l1 - L) : 0.f;
+            float wsum = 0.f;
+            wsum += w0;
+            wsum += w1;
+            const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+                o += w0 * (split == 0 ? oacc[rb][db] : oo[rb][db]);
+                o += w1 * (split == 0 ? oo[rb][db] : oacc[rb][db]);
+                oacc[rb][db] = o * inv;
+            }
+            lse2[rb] = wsum > 0.f ? L + fast_log2(wsum) : -INFINITY;
+        }
+        if (any_nan) {
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+                lse2[rb] = nan;
+        }
+    } else {
         // Each row block's 32 values in a lane belong to one row and share its log2-sum-exp,
         // so the merge weights are found once per split: L = max_s l_s, c_s = 2^(l_s - L),
         // then O = sum_s c_s O_s / sum_s c_s and LSE = L + log2 sum_s c_s.  Both row blocks
