@@ -1662,13 +1662,14 @@ __device__ __forceinline__ void pf_step(const bf16x8 (&kop)[kKB][4], const char*
 // leave the next PV's weights in pw).  Per output value the arithmetic and its order are
 // those of pf_step: the same products accumulate in the same order and the softmax takes
 // the same steps, so both schedules give the same bits.
+template <bool kV8 = false>
 __device__ __forceinline__ void pf_pv_full(const char* vt, const int (&v_addr)[8], const bf16x8 (&pw)[2][2],
                                            f32x4 (&oacc)[2][8])
 {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
         bf16x8 v[8];
-        pf_read_v(vt, v_addr, c, v);
+        pf_read_vx<kV8>(vt, v_addr, c, v);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[db], pw[0][c], oacc[0][db], 0, 0, 0);
@@ -1677,7 +1678,20 @@ __device__ __forceinline__ void pf_pv_full(const char* vt, const int (&v_addr)[8
     }
 }
 
-__device__ __forceinline__ void pf_qk_full(const char* kt, const int (&k_addr)[4], const bf16x8 (&qop)[2][4],
+// k_addr: this lane's K operand offsets (a bf16 tile), or, as [2][4], those of an FP8
+// tile's even and odd key blocks, whose codes are widened exactly to bf16 as they are read.
+__device__ __forceinline__ bf16x8 pf_k_op(const char* kt, const int (&k_addr)[4], int kb, int ks)
+{
+    return *reinterpret_cast<const bf16x8*>(kt + k_addr[ks] + kb * 4096);
+}
+__device__ __forceinline__ bf16x8 pf_k_op(const char* kt, const int (&k_addr8)[2][4], int kb, int ks)
+{
+    return __builtin_bit_cast(bf16x8,
+                              e4m3x8_to_bf16(*reinterpret_cast<const u32x2*>(kt + k_addr8[kb & 1][ks] + kb * 2048)));
+}
+
+template <class KAddr>
+__device__ __forceinline__ void pf_qk_full(const char* kt, const KAddr& k_addr, const bf16x8 (&qop)[2][4],
                                            f32x4 (&sacc)[2][4])
 {
 #pragma unroll
@@ -1685,7 +1699,7 @@ __device__ __forceinline__ void pf_qk_full(const char* kt, const int (&k_addr)[4
         bf16x8 kop[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            kop[ks] = *reinterpret_cast<const bf16x8*>(kt + k_addr[ks] + kb * 4096);
+            kop[ks] = pf_k_op(kt, k_addr, kb, ks);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             sacc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1699,19 +1713,32 @@ __device__ __forceinline__ void pf_qk_full(const char* kt, const int (&k_addr)[4
 // Both products of the matrix half in one instruction stream: the 48 LDS operand reads
 // (V's two 32-key chunks, then K's four 16-key blocks) go out eight ahead of the 64
 // products that use them, one per product, so that few operands are live at a time.
+// An FP8 tile (kV8, k_addr as [2][4]) reads half the bytes: 16 V and 16 K operand reads,
+// each widened by four conversions, ahead of the 64 products.
+template <bool kV8 = false, class KAddr>
 __device__ __forceinline__ void pf_matrix_full(const char* vt, const int (&v_addr)[8], const bf16x8 (&pw)[2][2],
-                                               f32x4 (&oacc)[2][8], const char* kt, const int (&k_addr)[4],
+                                               f32x4 (&oacc)[2][8], const char* kt, const KAddr& k_addr,
                                                const bf16x8 (&qop)[2][4], f32x4 (&sacc)[2][4])
 {
-    pf_pv_full(vt, v_addr, pw, oacc);
+    pf_pv_full<kV8>(vt, v_addr, pw, oacc);
     pf_qk_full(kt, k_addr, qop, sacc);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+    if constexpr (kV8) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 40; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        for (int i = 0; i < 28; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 36, 0);
+    } else {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 40; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 24, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 24, 0);
 }
 
 template <bool kMask>
@@ -1921,6 +1948,15 @@ __device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char
 // bf16 copies use, and the K scale as a float to a [group][key] table beside the tiles.
 // The products then run on binary16 operands (Q converted once, exact for bf16 values
 // inside the binary16 range), see pf_step_q8.
+template <bool kFirst, class A, class B>
+__device__ __forceinline__ constexpr const auto& pf_pick(const A& a, const B& b)
+{
+    if constexpr (kFirst)
+        return a;
+    else
+        return b;
+}
+
 template <bool kCascade, bool kFused = false, bool kQ8 = false, int kRG = 4, int kRB = 2, bool kFp8 = false>
 __device__ __attribute__((always_inline)) inline void prefill_body(const PrefillParams& p, const DecodeParams& dp,
                                                                    int bid)
@@ -2161,6 +2197,19 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         constexpr bool kV = decltype(which)::value;
         u32x4* dst = kV ? (decltype(sel)::value == 0 ? v_tile0 : v_tile1)
                         : (decltype(sel)::value == 0 ? k_tile0 : k_tile1);
+        if constexpr (kFp8) {
+            // the codes of one pool, as `stage` copies them
+            const int valid = kvlen - (s * kPfKeys + 16 * wave);
+            const int64_t base = (int64_t)id * blk_stride + kvh_off;   // bytes in an FP8 pool
+            const auto rs = pf_rsrc(reinterpret_cast<const uint8_t*>(kV ? p.v_pool : p.k_pool) + base, kBlock * kHeadDim);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int tok = 8 * i + (lane >> 3);
+                const int off = (tok < valid ? tok : 0) * kHeadDim + (((lane & 7) ^ pf_swz8(16 * wave + tok)) << 4);
+                lds_copy16(rs, off, reinterpret_cast<char*>(dst) + (16 * wave + 8 * i) * kHeadDim, PfCopy<kCascade, kRG>{});
+            }
+            return;
+        }
         const uint16_t* pool = kV ? p.v_pool : p.k_pool;
         const int valid = kvlen - (s * kPfKeys + 16 * wave);
         const int64_t base = (int64_t)id * blk_stride + kvh_off;
@@ -2277,9 +2326,9 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         i = min(i, nsteps - 1);
         return i >= n_plain ? s_begin + i : s_begin + (i + rot < n_plain ? i + rot : i + rot - n_plain);
     };
-    // The full bf16 tile runs the alternating schedule (see below); the other shapes and
-    // the q8_0 pool run one step at a time.
-    constexpr bool kAlternate = !kQ8 && !kFp8 && kRG == 4 && kRB == 2;
+    // The full tile on bf16 and FP8 pools runs the alternating schedule (see below); the
+    // other shapes and the q8_0 pool run one step at a time.
+    constexpr bool kAlternate = !kQ8 && kRG == 4 && kRB == 2;
     int next_id = 0, cur_id = 0;
     if (nsteps > 0) {
         cur_id = checked(table_entry(step_at(0)));
@@ -2365,6 +2414,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
         // V(t - 1), so V is staged one step after K and no buffer is written while read.
         f32x4 sacc[2][4];
         bf16x8 pw[2][2];
+        const auto& k_ops = pf_pick<kFp8>(k_addr8, k_addr);   // the K operand offsets of the format
         auto ktile = [&](auto sel) __attribute__((always_inline)) {
             return reinterpret_cast<const char*>(decltype(sel)::value == 0 ? k_tile0 : k_tile1);
         };
@@ -2406,7 +2456,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                 copies(sel, t);
                 if constexpr (decltype(part)::value == 0) {
                     if (active)
-                        pf_matrix_full(vtile(BufSel<B ^ 1>{}), v_addr, pw, oacc, ktile(sel), k_addr, qop, sacc);
+                        pf_matrix_full<kFp8>(vtile(BufSel<B ^ 1>{}), v_addr, pw, oacc, ktile(sel), k_ops, qop, sacc);
                     half_sync();
                     if (active)
                         softmax(msk, t);
@@ -2415,7 +2465,7 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
                         softmax(msk, t - 1);
                     half_sync();
                     if (active)
-                        pf_matrix_full(vtile(BufSel<B ^ 1>{}), v_addr, pw, oacc, ktile(sel), k_addr, qop, sacc);
+                        pf_matrix_full<kFp8>(vtile(BufSel<B ^ 1>{}), v_addr, pw, oacc, ktile(sel), k_ops, qop, sacc);
                 }
                 sync();
             };
@@ -2437,14 +2487,14 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             copies(BufSel<0>{}, 0);
             if constexpr (kPart == 0) {
                 if (active)
-                    pf_qk_full(ktile(BufSel<0>{}), k_addr, qop, sacc);
+                    pf_qk_full(ktile(BufSel<0>{}), k_ops, qop, sacc);
                 half_sync();
                 if (active)
                     softmax_any(0);
             } else {
                 half_sync();
                 if (active)
-                    pf_qk_full(ktile(BufSel<0>{}), k_addr, qop, sacc);
+                    pf_qk_full(ktile(BufSel<0>{}), k_ops, qop, sacc);
             }
             sync();
             // t = 1 .. nsteps - 1; the softmax of step t (part 0) or t - 1 (part 1) is
@@ -2455,9 +2505,9 @@ __device__ __attribute__((always_inline)) inline void prefill_body(const Prefill
             // t = nsteps: the last PV (after part 1's last softmax)
             auto last_pv = [&]() __attribute__((always_inline)) {
                 if ((nsteps - 1) & 1)
-                    pf_pv_full(vtile(BufSel<1>{}), v_addr, pw, oacc);
+                    pf_pv_full<kFp8>(vtile(BufSel<1>{}), v_addr, pw, oacc);
                 else
-                    pf_pv_full(vtile(BufSel<0>{}), v_addr, pw, oacc);
+                    pf_pv_full<kFp8>(vtile(BufSel<0>{}), v_addr, pw, oacc);
             };
             if constexpr (kPart == 0) {
                 if (active)
