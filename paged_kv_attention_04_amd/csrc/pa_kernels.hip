@@ -1948,6 +1948,7 @@ __device__ __forceinline__ void pf_step_q8(const bf16x8 (&kop)[4][4], const char
 // bf16 copies use, and the K scale as a float to a [group][key] table beside the tiles.
 // The products then run on binary16 operands (Q converted once, exact for bf16 values
 // inside the binary16 range), see pf_step_q8.
+// a or b, chosen at compile time (the two may differ in type)
 template <bool kFirst, class A, class B>
 __device__ __forceinline__ constexpr const auto& pf_pick(const A& a, const B& b)
 {
